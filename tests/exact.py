@@ -1,0 +1,124 @@
+"""Exact integer arithmetic used to pin the oracle.  Written independently of ``oracle/``.
+
+Every finite bf16 value is an integer multiple of 2**-133, so scaling by 2**133 turns
+bf16 values into Python integers; sums and products are then exact.  Rounding back to
+bf16 is done here with integer operations (round to nearest, ties to even), so a mistake
+in the oracle's float-based rounding, in its GEMM indexing, or in its chunk loop shows up
+as a mismatch against these functions.
+"""
+
+import operator
+
+import numpy as np
+
+SCALE = 133  # bf16 value * 2**133 is an integer
+
+
+def bf16_bits_to_int(b):
+    """One bf16 pattern -> integer value * 2**133 (finite patterns only)."""
+    b = int(b)
+    sign = -1 if (b >> 15) & 1 else 1
+    expf = (b >> 7) & 0xFF
+    man = b & 0x7F
+    if expf == 0xFF:
+        raise ValueError("inf/nan has no integer form")
+    if expf == 0:
+        mag = man  # subnormal: man * 2**-133
+    else:
+        mag = (128 + man) << (expf - 1)  # (128+man) * 2**(expf-127-7) * 2**133
+    return sign * mag
+
+
+def ints_of(bits):
+    flat = np.asarray(bits, dtype=np.uint16).ravel()
+    return np.array([bf16_bits_to_int(x) for x in flat], dtype=object).reshape(np.shape(bits))
+
+
+def rne_int(S, frac_bits):
+    """bf16 pattern of the exact value S / 2**frac_bits, round to nearest even."""
+    S = int(S)
+    if S == 0:
+        return 0
+    neg = S < 0
+    a = -S if neg else S
+    e = max(a.bit_length() - 1 - frac_bits, -126)  # floor(log2 value), clamped
+    shift = frac_bits + e - 7  # quantum 2**(e-7) in units of 2**-frac_bits
+    if shift > 0:
+        q, r = divmod(a, 1 << shift)
+        half = 1 << (shift - 1)
+        if r > half or (r == half and (q & 1)):
+            q += 1
+    else:
+        q = a << (-shift)
+    if q >= 256:  # carried into the next binade
+        q >>= 1
+        e += 1
+    if e > 127:
+        bits = 0x7F80
+    elif q < 128:  # subnormal (only possible at e == -126)
+        bits = q
+    else:
+        bits = ((e + 127) << 7) | (q - 128)
+    return bits | (0x8000 if neg else 0)
+
+
+def gemm_rne(a_bits, w_bits):
+    """bf16( exact A @ W ) by brute force over Python integers.  Small inputs only."""
+    A = ints_of(a_bits)
+    W = ints_of(w_bits)
+    m, k = A.shape
+    k2, n = W.shape
+    assert k == k2
+    rows = [list(A[i]) for i in range(m)]
+    cols = [list(W[:, j]) for j in range(n)]
+    out = np.zeros((m, n), dtype=np.uint16)
+    for i in range(m):
+        ar = rows[i]
+        for j in range(n):
+            out[i, j] = rne_int(sum(map(operator.mul, ar, cols[j])), 2 * SCALE)
+    return out
+
+
+def gemm_exact_ints(a_bits, w_bits):
+    """Exact A @ W as Python integers scaled by 2**266 (object array)."""
+    A = ints_of(a_bits)
+    W = ints_of(w_bits)
+    m, k = A.shape
+    _, n = W.shape
+    rows = [list(A[i]) for i in range(m)]
+    cols = [list(W[:, j]) for j in range(n)]
+    out = np.empty((m, n), dtype=object)
+    for i in range(m):
+        for j in range(n):
+            out[i, j] = sum(map(operator.mul, rows[i], cols[j]))
+    return out
+
+
+def rs_rne(a_bits, w_bits, tp):
+    """Brute-force row-parallel result: bf16 partial per K slice, exact sum, one RNE.
+
+    Returns (out bits [m, n], list of tp partial bit arrays)."""
+    a = np.asarray(a_bits)
+    w = np.asarray(w_bits)
+    k = a.shape[1]
+    ks = k // tp
+    parts = [gemm_rne(a[:, s * ks:(s + 1) * ks], w[s * ks:(s + 1) * ks, :]) for s in range(tp)]
+    P = [ints_of(p) for p in parts]
+    m, n = parts[0].shape
+    out = np.zeros((m, n), dtype=np.uint16)
+    for i in range(m):
+        for j in range(n):
+            out[i, j] = rne_int(sum(p[i, j] for p in P), SCALE)
+    return out, parts
+
+
+def int_valued_gemm_rne(a_bits, w_bits):
+    """bf16 of A @ W when A and W hold small integers (exact int64 products and sums)."""
+    A = ints_of(a_bits)
+    W = ints_of(w_bits)
+    # integer-valued bf16 -> scaled ints are v * 2**133; undo the scale exactly
+    Ai = np.array([[x >> SCALE if x >= 0 else -((-x) >> SCALE) for x in r] for r in A], dtype=np.int64)
+    Wi = np.array([[x >> SCALE if x >= 0 else -((-x) >> SCALE) for x in r] for r in W], dtype=np.int64)
+    assert np.all(Ai.astype(object) * (1 << SCALE) == A) and np.all(Wi.astype(object) * (1 << SCALE) == W)
+    S = Ai @ Wi
+    return np.vectorize(lambda s: rne_int(int(s), 0), otypes=[np.uint16])(S)
