@@ -1,0 +1,561 @@
+// C ABI of the capacity/active-shape UserBuffer and its chunked overlap GEMMs.
+//
+// Buffer manager: "[Feature Request] Support dynamic token counts in TP communication/GEMM
+// overlap" (Transformer Engine issue 3564), sections "Proposed API" and "Implementation
+// approach in the prototype": a buffer registered once at [max_tokens, hidden]; a separate
+// active shape per microbatch whose data is the buffer's contiguous prefix; views, offsets
+// and copy-size checks recomputed from the active T; no allocation, free or
+// re-registration on a shape change; the constraint list on the active shape.
+//
+// Scheduler: "How to setup TP Overlap configs" (Transformer Engine issue 1344), option
+// list: GEMM chunks on min(num_splits, num_max_streams) compute streams.  Here stream 0 of
+// a plan is the caller's stream and streams 1..S-1 are the handle's own non-blocking HIP
+// streams (default priority).  A call forks them from the caller's stream with one event
+// and joins them back with one event each, so the call as a whole is ordered on the
+// caller's stream and never synchronises the host.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "ub_internal.h"
+
+struct ub_ctx {
+  // registration
+  int64_t capacity = 0;
+  int64_t hidden = 0;
+  int32_t tp = 1;
+  uint16_t* ub = nullptr;
+  size_t ub_bytes = 0;
+  uint16_t* ws = nullptr;
+  size_t ws_bytes = 0;
+  // active shape
+  int64_t T = 0;
+  // device resources, created on the first GEMM call
+  int device = -1;
+  hipStream_t streams[UB_MAX_STREAMS] = {};  // [0] unused: the caller's stream
+  int n_streams_created = 1;
+  hipEvent_t ev_fork = nullptr;
+  hipEvent_t ev_join[UB_MAX_STREAMS] = {};
+  // kernel timing
+  bool timing = false;
+  struct TimedLaunch {
+    hipEvent_t start, stop;
+    int kind;  // 0 gemm, 1 reduce
+    double flops, bytes;
+  };
+  std::vector<hipEvent_t> free_events;
+  std::vector<TimedLaunch> pending;
+  ub_kernel_stats_t stats[2] = {};
+  // scratch for plans
+  ubx::Plan plan;
+  std::string last_error;
+};
+
+namespace {
+
+constexpr int64_t kMaxRowsPerUnit = int64_t(1) << 30;
+
+ub_status_t fail(ub_ctx* h, ub_status_t st, const char* fmt, ...) {
+  if (h) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    h->last_error = buf;
+  }
+  return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+ub_status_t check_registration(int64_t capacity, int64_t hidden, int32_t tp, ub_dtype_t dtype,
+                               std::string* err) {
+  if (dtype != UB_DTYPE_BF16) {
+    *err = "only unquantized bf16 UserBuffers are supported";
+    return UB_ERR_DTYPE;
+  }
+  if (capacity <= 0 || hidden <= 0) {
+    *err = "capacity and hidden must be > 0";
+    return UB_ERR_INVALID_ARG;
+  }
+  if (tp < 1 || tp > UB_MAX_TP) {
+    *err = "tp_size must be in [1, " + std::to_string(UB_MAX_TP) + "]";
+    return UB_ERR_INVALID_ARG;
+  }
+  if (hidden % 8 != 0) {
+    *err = "hidden must be a multiple of 8 (16-byte rows)";
+    return UB_ERR_INVALID_ARG;
+  }
+  if (capacity % tp != 0) {
+    *err = "capacity must be divisible by tp_size (the initial active shape is the capacity)";
+    return UB_ERR_TP_DIVISIBILITY;
+  }
+  if (capacity > (int64_t(1) << 40) / hidden) {
+    *err = "capacity * hidden too large";
+    return UB_ERR_INVALID_ARG;
+  }
+  return UB_OK;
+}
+
+ub_status_t hip_fail(ub_ctx* h, hipError_t e, const char* what) {
+  return fail(h, UB_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Bind the handle to the current device and create the streams/events it needs.
+ub_status_t ensure_device(ub_ctx* h, int need_streams) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(h, e, "hipGetDevice");
+  if (h->device < 0) {
+    h->device = dev;
+    e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(h, e, "hipEventCreate");
+  } else if (h->device != dev) {
+    return fail(h, UB_ERR_INVALID_ARG, "handle is bound to device %d but device %d is current",
+                h->device, dev);
+  }
+  while (h->n_streams_created < need_streams) {
+    const int i = h->n_streams_created;
+    e = hipStreamCreateWithFlags(&h->streams[i], hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(h, e, "hipStreamCreate");
+    e = hipEventCreateWithFlags(&h->ev_join[i], hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(h, e, "hipEventCreate");
+    h->n_streams_created = i + 1;
+  }
+  return UB_OK;
+}
+
+// ---- per-launch timing ----------------------------------------------------------------
+ub_status_t harvest(ub_ctx* h) {
+  for (auto& t : h->pending) {
+    hipError_t e = hipEventSynchronize(t.stop);
+    if (e != hipSuccess) return hip_fail(h, e, "hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, t.start, t.stop);
+    if (e != hipSuccess) return hip_fail(h, e, "hipEventElapsedTime");
+    ub_kernel_stats_t& s = h->stats[t.kind];
+    s.launches += 1;
+    s.total_ms += ms;
+    s.flops += t.flops;
+    s.bytes += t.bytes;
+    h->free_events.push_back(t.start);
+    h->free_events.push_back(t.stop);
+  }
+  h->pending.clear();
+  return UB_OK;
+}
+
+hipEvent_t take_event(ub_ctx* h) {
+  if (!h->free_events.empty()) {
+    hipEvent_t ev = h->free_events.back();
+    h->free_events.pop_back();
+    return ev;
+  }
+  hipEvent_t ev = nullptr;
+  if (hipEventCreate(&ev) != hipSuccess) return nullptr;
+  return ev;
+}
+
+constexpr size_t kMaxPendingTimings = 4096;
+
+template <class Launch>
+ub_status_t timed_launch(ub_ctx* h, hipStream_t s, int kind, double flops, double bytes,
+                         Launch&& launch, const char* what) {
+  if (!h->timing) {
+    hipError_t e = launch();
+    return e == hipSuccess ? UB_OK : hip_fail(h, e, what);
+  }
+  if (h->pending.size() >= kMaxPendingTimings) {
+    ub_status_t st = harvest(h);  // oldest launches finished long ago: no real stall
+    if (st != UB_OK) return st;
+  }
+  hipEvent_t a = take_event(h), b = take_event(h);
+  if (!a || !b) return fail(h, UB_ERR_HIP, "hipEventCreate failed for kernel timing");
+  hipError_t e = hipEventRecord(a, s);
+  if (e == hipSuccess) e = launch();
+  if (e == hipSuccess) e = hipEventRecord(b, s);
+  if (e != hipSuccess) return hip_fail(h, e, what);
+  h->pending.push_back({a, b, kind, flops, bytes});
+  return UB_OK;
+}
+
+// ---- fork / join ----------------------------------------------------------------------
+ub_status_t fork_streams(ub_ctx* h, hipStream_t caller, int S) {
+  if (S <= 1) return UB_OK;
+  hipError_t e = hipEventRecord(h->ev_fork, caller);
+  if (e != hipSuccess) return hip_fail(h, e, "hipEventRecord(fork)");
+  for (int i = 1; i < S; ++i) {
+    e = hipStreamWaitEvent(h->streams[i], h->ev_fork, 0);
+    if (e != hipSuccess) return hip_fail(h, e, "hipStreamWaitEvent(fork)");
+  }
+  return UB_OK;
+}
+
+ub_status_t join_streams(ub_ctx* h, hipStream_t caller, int S) {
+  for (int i = 1; i < S; ++i) {
+    hipError_t e = hipEventRecord(h->ev_join[i], h->streams[i]);
+    if (e != hipSuccess) return hip_fail(h, e, "hipEventRecord(join)");
+    e = hipStreamWaitEvent(caller, h->ev_join[i], 0);
+    if (e != hipSuccess) return hip_fail(h, e, "hipStreamWaitEvent(join)");
+  }
+  return UB_OK;
+}
+
+ub_status_t check_cfg_common(ub_ctx* h, const ub_overlap_cfg_t* cfg) {
+  if (!cfg) return fail(h, UB_ERR_INVALID_ARG, "cfg is NULL");
+  if (cfg->atomic_gemm)
+    return fail(h, UB_ERR_UNSUPPORTED, "atomic_gemm (device-side chunk loop) is not built");
+  return UB_OK;
+}
+
+ub_status_t check_ld(ub_ctx* h, const char* name, int64_t ld, int64_t cols) {
+  if (ld < cols || ld % 8 != 0)
+    return fail(h, UB_ERR_INVALID_ARG, "%s=%lld must be >= %lld and a multiple of 8", name,
+                (long long)ld, (long long)cols);
+  return UB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+UB_API void ub_overlap_cfg_default(ub_overlap_cfg_t* cfg) {
+  if (!cfg) return;
+  std::memset(cfg, 0, sizeof(*cfg));
+  cfg->method = UB_RING_EXCHANGE;
+  cfg->num_splits = 1;
+  cfg->num_max_streams = 3;
+  cfg->aggregate = 0;
+  cfg->atomic_gemm = 0;
+  cfg->rank = 0;
+  cfg->use_ce = 1;
+  cfg->num_sm = 0;
+  cfg->set_sm_margin = 0;
+}
+
+UB_API const char* ub_status_string(ub_status_t s) {
+  switch (s) {
+    case UB_OK: return "UB_OK";
+    case UB_ERR_INVALID_ARG: return "UB_ERR_INVALID_ARG";
+    case UB_ERR_NDIM: return "UB_ERR_NDIM";
+    case UB_ERR_ZERO_DIM: return "UB_ERR_ZERO_DIM";
+    case UB_ERR_CAPACITY: return "UB_ERR_CAPACITY";
+    case UB_ERR_HIDDEN_MISMATCH: return "UB_ERR_HIDDEN_MISMATCH";
+    case UB_ERR_TP_DIVISIBILITY: return "UB_ERR_TP_DIVISIBILITY";
+    case UB_ERR_DTYPE: return "UB_ERR_DTYPE";
+    case UB_ERR_UNSUPPORTED: return "UB_ERR_UNSUPPORTED";
+    case UB_ERR_BUFFER_TOO_SMALL: return "UB_ERR_BUFFER_TOO_SMALL";
+    case UB_ERR_NOT_INITIALIZED: return "UB_ERR_NOT_INITIALIZED";
+    case UB_ERR_HIP: return "UB_ERR_HIP";
+  }
+  return "UB_ERR_UNKNOWN";
+}
+
+UB_API const char* ub_last_error(ub_handle_t h) { return h ? h->last_error.c_str() : ""; }
+
+UB_API ub_status_t ub_required_bytes(int64_t capacity, int64_t hidden, int32_t tp_size,
+                                     ub_dtype_t dtype, size_t* ub_bytes,
+                                     size_t* rs_workspace_bytes) {
+  std::string err;
+  ub_status_t st = check_registration(capacity, hidden, tp_size, dtype, &err);
+  if (st != UB_OK) return st;
+  const size_t elems = static_cast<size_t>(capacity) * static_cast<size_t>(hidden);
+  if (ub_bytes) *ub_bytes = elems * 2;
+  if (rs_workspace_bytes) *rs_workspace_bytes = elems * 2 * static_cast<size_t>(tp_size);
+  return UB_OK;
+}
+
+UB_API ub_status_t ub_init(ub_handle_t* out, int64_t capacity, int64_t hidden, int32_t tp_size,
+                           ub_dtype_t dtype, void* ub_buf, size_t ub_bytes, void* rs_ws,
+                           size_t rs_ws_bytes) {
+  if (!out) return UB_ERR_INVALID_ARG;
+  *out = nullptr;
+  std::string err;
+  ub_status_t st = check_registration(capacity, hidden, tp_size, dtype, &err);
+  if (st != UB_OK) return st;
+  const size_t need = static_cast<size_t>(capacity) * static_cast<size_t>(hidden) * 2;
+  if (!ub_buf || !aligned16(ub_buf)) return UB_ERR_INVALID_ARG;
+  if (ub_bytes < need) return UB_ERR_BUFFER_TOO_SMALL;
+  if (rs_ws) {
+    if (!aligned16(rs_ws)) return UB_ERR_INVALID_ARG;
+    if (rs_ws_bytes < need * static_cast<size_t>(tp_size)) return UB_ERR_BUFFER_TOO_SMALL;
+  } else if (rs_ws_bytes != 0) {
+    return UB_ERR_INVALID_ARG;
+  }
+  ub_ctx* h = new (std::nothrow) ub_ctx();
+  if (!h) return UB_ERR_INVALID_ARG;
+  h->capacity = capacity;
+  h->hidden = hidden;
+  h->tp = tp_size;
+  h->ub = static_cast<uint16_t*>(ub_buf);
+  h->ub_bytes = ub_bytes;
+  h->ws = static_cast<uint16_t*>(rs_ws);
+  h->ws_bytes = rs_ws_bytes;
+  h->T = capacity;  // the initial active shape is the capacity shape
+  *out = h;
+  return UB_OK;
+}
+
+UB_API ub_status_t ub_set_active_shape(ub_handle_t h, const int64_t* shape, int32_t ndim) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  if (ndim != 2) return fail(h, UB_ERR_NDIM, "active shape must be 2-D, got %d dims", ndim);
+  if (!shape) return fail(h, UB_ERR_INVALID_ARG, "shape is NULL");
+  const int64_t T = shape[0], H = shape[1];
+  if (T <= 0 || H <= 0)
+    return fail(h, UB_ERR_ZERO_DIM, "active shape [%lld, %lld] has a dimension <= 0",
+                (long long)T, (long long)H);
+  if (T > h->capacity)
+    return fail(h, UB_ERR_CAPACITY, "active T=%lld exceeds capacity %lld", (long long)T,
+                (long long)h->capacity);
+  if (H != h->hidden)
+    return fail(h, UB_ERR_HIDDEN_MISMATCH, "active hidden %lld != registered %lld",
+                (long long)H, (long long)h->hidden);
+  if (T % h->tp != 0)
+    return fail(h, UB_ERR_TP_DIVISIBILITY, "active T=%lld not divisible by tp_size %d",
+                (long long)T, h->tp);
+  h->T = T;  // views and offsets are derived from T at each call; nothing else changes
+  h->last_error.clear();
+  return UB_OK;
+}
+
+UB_API ub_status_t ub_get_active_shape(ub_handle_t h, int64_t shape_out[2]) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  if (!shape_out) return fail(h, UB_ERR_INVALID_ARG, "shape_out is NULL");
+  shape_out[0] = h->T;
+  shape_out[1] = h->hidden;
+  return UB_OK;
+}
+
+UB_API ub_status_t ub_get_capacity_shape(ub_handle_t h, int64_t shape_out[2]) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  if (!shape_out) return fail(h, UB_ERR_INVALID_ARG, "shape_out is NULL");
+  shape_out[0] = h->capacity;
+  shape_out[1] = h->hidden;
+  return UB_OK;
+}
+
+UB_API ub_status_t ub_get_plan(ub_handle_t h, const ub_overlap_cfg_t* cfg, ub_op_t op,
+                               ub_plan_unit_t* out, int32_t max_units, int32_t* n_units,
+                               int32_t* n_streams) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  if (!cfg) return fail(h, UB_ERR_INVALID_ARG, "cfg is NULL");
+  if (max_units < 0 || (max_units > 0 && !out))
+    return fail(h, UB_ERR_INVALID_ARG, "bad output array");
+  ub_status_t st = ubx::build_plan(h->T, h->tp, *cfg, op, &h->plan, &h->last_error);
+  if (st != UB_OK) return st;
+  const int32_t U = static_cast<int32_t>(h->plan.units.size());
+  for (int32_t i = 0; i < std::min(U, max_units); ++i) out[i] = h->plan.units[i];
+  if (n_units) *n_units = U;
+  if (n_streams) *n_streams = h->plan.n_streams;
+  return UB_OK;
+}
+
+UB_API ub_status_t ub_copy_in(ub_handle_t h, const void* src, int64_t rows, int64_t row_offset,
+                              ub_stream_t stream) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  if (!src) return fail(h, UB_ERR_INVALID_ARG, "src is NULL");
+  if (rows < 0 || row_offset < 0 || row_offset + rows > h->T)
+    return fail(h, UB_ERR_INVALID_ARG,
+                "copy of %lld rows at row %lld does not fit the active T=%lld", (long long)rows,
+                (long long)row_offset, (long long)h->T);
+  if (rows == 0) return UB_OK;
+  ub_status_t st = ensure_device(h, 1);
+  if (st != UB_OK) return st;
+  hipError_t e = hipMemcpyAsync(h->ub + row_offset * h->hidden, src,
+                                static_cast<size_t>(rows * h->hidden) * 2,
+                                hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? UB_OK : hip_fail(h, e, "hipMemcpyAsync");
+}
+
+UB_API ub_status_t ub_gemm_ag_chunked(ub_handle_t h, const void* w, int64_t n_cols, int64_t ldw,
+                                      void* c, int64_t ldc, const ub_overlap_cfg_t* cfg,
+                                      ub_stream_t stream) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  ub_status_t st = check_cfg_common(h, cfg);
+  if (st != UB_OK) return st;
+  if (!w || !c) return fail(h, UB_ERR_INVALID_ARG, "w and c must be non-NULL");
+  if (!aligned16(w) || !aligned16(c))
+    return fail(h, UB_ERR_INVALID_ARG, "w and c must be 16-byte aligned");
+  if (n_cols <= 0 || n_cols % 8 != 0 || n_cols > INT32_MAX)
+    return fail(h, UB_ERR_INVALID_ARG, "n_cols=%lld must be > 0 and a multiple of 8",
+                (long long)n_cols);
+  if ((st = check_ld(h, "ldw", ldw, n_cols)) != UB_OK) return st;
+  if ((st = check_ld(h, "ldc", ldc, n_cols)) != UB_OK) return st;
+  if (h->hidden % ubx::kGemmKStep != 0)
+    return fail(h, UB_ERR_UNSUPPORTED, "hidden=%lld must be a multiple of %d",
+                (long long)h->hidden, ubx::kGemmKStep);
+  st = ubx::build_plan(h->T, h->tp, *cfg, UB_OP_AG, &h->plan, &h->last_error);
+  if (st != UB_OK) return st;
+  const int S = h->plan.n_streams;
+  if ((st = ensure_device(h, S)) != UB_OK) return st;
+
+  hipStream_t caller = static_cast<hipStream_t>(stream);
+  if ((st = fork_streams(h, caller, S)) != UB_OK) return st;
+  const int64_t H = h->hidden;
+  for (const ub_plan_unit_t& u : h->plan.units) {
+    const int64_t rows = u.row1 - u.row0;
+    if (rows <= 0) continue;
+    if (rows > kMaxRowsPerUnit) return fail(h, UB_ERR_UNSUPPORTED, "unit too large");
+    hipStream_t s = u.stream == 0 ? caller : h->streams[u.stream];
+    ubx::GemmArgs g{};
+    g.a = h->ub + u.row0 * H;  // byte offset row0 * hidden * 2 into the capacity buffer
+    g.lda = H;
+    g.b = static_cast<const uint16_t*>(w);
+    g.ldb = ldw;
+    g.c = static_cast<uint16_t*>(c) + u.row0 * ldc;
+    g.ldc = ldc;
+    g.m = static_cast<int32_t>(rows);
+    g.n = static_cast<int32_t>(n_cols);
+    g.k = static_cast<int32_t>(H);
+    g.batch = 1;
+    const double flops = 2.0 * rows * H * n_cols;
+    const double bytes = 2.0 * (rows * H + H * n_cols + rows * n_cols);
+    st = timed_launch(h, s, 0, flops, bytes, [&] { return ubx::launch_gemm_bf16(g, s); },
+                      "GEMM launch");
+    if (st != UB_OK) return st;
+  }
+  return join_streams(h, caller, S);
+}
+
+UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, int64_t lda,
+                                      const void* w, int64_t ldw, void* out, int64_t ldo,
+                                      const ub_overlap_cfg_t* cfg, ub_stream_t stream) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  ub_status_t st = check_cfg_common(h, cfg);
+  if (st != UB_OK) return st;
+  if (!h->ws) return fail(h, UB_ERR_NOT_INITIALIZED, "no reduce-scatter workspace registered");
+  if (!a || !w || !out) return fail(h, UB_ERR_INVALID_ARG, "a, w and out must be non-NULL");
+  if (!aligned16(a) || !aligned16(w) || !aligned16(out))
+    return fail(h, UB_ERR_INVALID_ARG, "a, w and out must be 16-byte aligned");
+  if (k <= 0 || k % h->tp != 0 || k > INT32_MAX)
+    return fail(h, UB_ERR_INVALID_ARG, "k=%lld must be > 0 and divisible by tp_size %d",
+                (long long)k, h->tp);
+  const int64_t ks = k / h->tp;
+  if (ks % ubx::kGemmKStep != 0)
+    return fail(h, UB_ERR_UNSUPPORTED, "k / tp_size = %lld must be a multiple of %d",
+                (long long)ks, ubx::kGemmKStep);
+  const int64_t H = h->hidden;
+  if ((st = check_ld(h, "lda", lda, k)) != UB_OK) return st;
+  if ((st = check_ld(h, "ldw", ldw, H)) != UB_OK) return st;
+  if ((st = check_ld(h, "ldo", ldo, H)) != UB_OK) return st;
+  st = ubx::build_plan(h->T, h->tp, *cfg, UB_OP_RS, &h->plan, &h->last_error);
+  if (st != UB_OK) return st;
+  const int S = h->plan.n_streams;
+  if ((st = ensure_device(h, S)) != UB_OK) return st;
+
+  hipStream_t caller = static_cast<hipStream_t>(stream);
+  if ((st = fork_streams(h, caller, S)) != UB_OK) return st;
+  const int64_t T = h->T;
+  const int32_t tp = h->tp;
+  for (const ub_plan_unit_t& u : h->plan.units) {
+    const int64_t rows = u.row1 - u.row0;
+    if (rows <= 0) continue;
+    if (rows > kMaxRowsPerUnit) return fail(h, UB_ERR_UNSUPPORTED, "unit too large");
+    hipStream_t s = u.stream == 0 ? caller : h->streams[u.stream];
+    // tp slice GEMMs of this chunk in one batched launch; slot s of the packed active
+    // prefix starts at workspace element s*T*H (offsets from the active T).
+    ubx::GemmArgs g{};
+    g.a = static_cast<const uint16_t*>(a) + u.row0 * lda;
+    g.lda = lda;
+    g.a_batch_stride = ks;
+    g.b = static_cast<const uint16_t*>(w);
+    g.ldb = ldw;
+    g.b_batch_stride = ks * ldw;
+    g.c = h->ws + u.row0 * H;
+    g.ldc = H;
+    g.c_batch_stride = T * H;
+    g.m = static_cast<int32_t>(rows);
+    g.n = static_cast<int32_t>(H);
+    g.k = static_cast<int32_t>(ks);
+    g.batch = tp;
+    const double flops = 2.0 * rows * k * H;
+    const double gbytes = 2.0 * (rows * k + k * H + tp * rows * H);
+    st = timed_launch(h, s, 0, flops, gbytes, [&] { return ubx::launch_gemm_bf16(g, s); },
+                      "slice GEMM launch");
+    if (st != UB_OK) return st;
+    // the reduction of this chunk follows its GEMMs on the same stream
+    ubx::ReduceArgs r{};
+    r.parts = h->ws + u.row0 * H;
+    r.slot_stride = T * H;
+    r.ldp = H;
+    r.nslots = tp;
+    r.out = static_cast<uint16_t*>(out) + u.row0 * ldo;
+    r.ldo = ldo;
+    r.rows = rows;
+    r.cols = H;
+    const double rbytes = 2.0 * (tp + 1) * rows * H;
+    st = timed_launch(h, s, 1, double(tp - 1) * rows * H, rbytes,
+                      [&] { return ubx::launch_reduce_partials(r, s); }, "reduce launch");
+    if (st != UB_OK) return st;
+  }
+  return join_streams(h, caller, S);
+}
+
+UB_API ub_status_t ub_reduce_partials(ub_handle_t h, void* out, int64_t ldo, ub_stream_t stream) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  if (!h->ws) return fail(h, UB_ERR_NOT_INITIALIZED, "no reduce-scatter workspace registered");
+  if (!out || !aligned16(out)) return fail(h, UB_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  ub_status_t st = check_ld(h, "ldo", ldo, h->hidden);
+  if (st != UB_OK) return st;
+  if ((st = ensure_device(h, 1)) != UB_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ubx::ReduceArgs r{};
+  r.parts = h->ws;
+  r.slot_stride = h->T * h->hidden;
+  r.ldp = h->hidden;
+  r.nslots = h->tp;
+  r.out = static_cast<uint16_t*>(out);
+  r.ldo = ldo;
+  r.rows = h->T;
+  r.cols = h->hidden;
+  const double rbytes = 2.0 * (h->tp + 1) * h->T * h->hidden;
+  return timed_launch(h, s, 1, double(h->tp - 1) * h->T * h->hidden, rbytes,
+                      [&] { return ubx::launch_reduce_partials(r, s); }, "reduce launch");
+}
+
+UB_API ub_status_t ub_set_kernel_timing(ub_handle_t h, int32_t enable) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  h->timing = enable != 0;
+  return UB_OK;
+}
+
+UB_API ub_status_t ub_get_kernel_timing(ub_handle_t h, ub_kernel_stats_t* gemm,
+                                        ub_kernel_stats_t* reduce) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  ub_status_t st = harvest(h);
+  if (st != UB_OK) return st;
+  if (gemm) *gemm = h->stats[0];
+  if (reduce) *reduce = h->stats[1];
+  h->stats[0] = ub_kernel_stats_t{};
+  h->stats[1] = ub_kernel_stats_t{};
+  return UB_OK;
+}
+
+UB_API ub_status_t ub_destroy(ub_handle_t h) {
+  if (!h) return UB_OK;
+  if (h->device >= 0) {
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (cur != h->device) (void)hipSetDevice(h->device);
+    harvest(h);
+    for (int i = 1; i < h->n_streams_created; ++i) {
+      (void)hipStreamSynchronize(h->streams[i]);
+      (void)hipStreamDestroy(h->streams[i]);
+      (void)hipEventDestroy(h->ev_join[i]);
+    }
+    if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+    for (hipEvent_t ev : h->free_events) (void)hipEventDestroy(ev);
+    if (cur >= 0 && cur != h->device) (void)hipSetDevice(cur);
+  }
+  delete h;
+  return UB_OK;
+}
+
+}  // extern "C"

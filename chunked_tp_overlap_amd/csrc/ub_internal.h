@@ -1,0 +1,59 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "ub.h"
+
+namespace ubx {
+
+// ---- chunk plan (host only; ub_plan.cpp) ------------------------------------------------
+struct Plan {
+  std::vector<ub_plan_unit_t> units;  // in execution order
+  int32_t n_chunks = 0;               // chunks before aggregation
+  int32_t n_streams = 0;              // compute streams used (stream 0 = caller's)
+};
+
+// Validates cfg (method, num_splits, num_max_streams, rank) and builds the plan for an
+// active T.  Returns UB_OK or UB_ERR_INVALID_ARG with a message in *err.
+ub_status_t build_plan(int64_t T, int32_t tp, const ub_overlap_cfg_t& cfg, ub_op_t op,
+                       Plan* out, std::string* err);
+
+// ---- kernels (gemm_bf16.hip, reduce_partials.hip) ----------------------------------------
+// Batched row-major bf16 GEMM, C[b] = bf16(A[b] * B[b]) with fp32 accumulation.
+// All strides in elements.  Requirements checked by the caller: k % 64 == 0,
+// n % 8 == 0, lda/ldb/ldc % 8 == 0, pointers 16-byte aligned.
+struct GemmArgs {
+  const uint16_t* a;
+  int64_t lda;
+  int64_t a_batch_stride;
+  const uint16_t* b;
+  int64_t ldb;
+  int64_t b_batch_stride;
+  uint16_t* c;
+  int64_t ldc;
+  int64_t c_batch_stride;
+  int32_t m, n, k, batch;
+};
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream);
+constexpr int kGemmKStep = 64;  // k must be a multiple of this
+
+// out[r, c] = bf16( sum_{s < nslots} float(parts[s*slot_stride + r*ldp + c]) ), ascending s.
+// cols % 8 == 0, ldp/ldo % 8 == 0, pointers 16-byte aligned.
+struct ReduceArgs {
+  const uint16_t* parts;
+  int64_t slot_stride;
+  int64_t ldp;
+  int32_t nslots;
+  uint16_t* out;
+  int64_t ldo;
+  int64_t rows;
+  int64_t cols;
+};
+hipError_t launch_reduce_partials(const ReduceArgs& r, hipStream_t stream);
+
+}  // namespace ubx

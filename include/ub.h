@@ -1,0 +1,271 @@
+/*
+ * ub.h -- C ABI of the chunked tensor-parallel overlap GEMMs over a capacity UserBuffer,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited by title:
+ *   [TE#3564] "[Feature Request] Support dynamic token counts in TP communication/GEMM
+ *             overlap" (Transformer Engine issue 3564): "Problem", "Proposed API",
+ *             "Implementation approach in the prototype".
+ *   [TE#1344] "How to setup TP Overlap configs" (Transformer Engine issue 1344): the
+ *             maintainer's option list.
+ *   [MLM#1240] "[QUESTION] Do tp overlap support thd, whose sequence length is flexible?"
+ *             (Megatron-LM discussion 1240): the QKV and MLP shape diagrams and the
+ *             "Why doesn't the hidden dimension appear" answer.
+ *
+ * What the library does.  A UserBuffer (UB) is registered once at a fixed capacity
+ * [capacity, hidden] of bf16 ([TE#3564] "Proposed API"); every microbatch then sets an
+ * active shape [T, hidden] whose data is the contiguous prefix of the buffer, and all
+ * views, chunk offsets and counts are recomputed from T without any allocation
+ * ([TE#3564] "Implementation approach in the prototype").  Two chunked bf16 GEMMs read
+ * the buffer by offset:
+ *   - the all-gather side: a column-parallel GEMM (QKV, MLP fc1; [MLM#1240] diagrams)
+ *     whose input is the gathered activation tensor held in the UB, cut into token
+ *     chunks that run in ring, pipeline or bulk order on min(num_splits, num_max_streams)
+ *     HIP streams ([TE#1344] "method", "num_splits", "num_max_streams", "aggregate");
+ *   - the reduce-scatter side: a row-parallel GEMM (MLP fc2) whose tp K-slice partial
+ *     products are written as bf16 into a workspace and summed into tp shards of
+ *     [T/tp, hidden] ([MLM#1240] MLP diagram; [TE#3564]: reduce-scatter keeps its extra
+ *     per-rank chunks inside its own allocation).
+ * One process drives one GPU; the library moves no data between GPUs.  The UB holds what
+ * a rank would have after the all-gather; the caller fills its active prefix.
+ *
+ * Conventions for every entry point.
+ *   - Tensors are row-major bf16 (2 bytes, IEEE binary32 upper half).  Device pointers
+ *     must be 16-byte aligned; leading dimensions and the hidden size are counted in
+ *     elements and must be multiples of 8 (16-byte rows).
+ *   - Every device buffer is owned by the caller (allocated by PyTorch or hipMalloc) and
+ *     must outlive the handle.  The library never allocates, frees or registers device
+ *     memory.  A handle owns only host state and its HIP streams and events.
+ *   - Functions return a ub_status_t; no C++ exception crosses the ABI.  Arguments are
+ *     checked before anything is launched; a rejected call changes no state and enqueues
+ *     nothing.  ub_last_error() returns a message for the last failure on a handle.
+ *   - GEMM calls are asynchronous on the caller's stream: their results are ordered
+ *     after work already on `stream` and before work enqueued on it afterwards.  No
+ *     host synchronisation happens inside them.  Device faults surface at the caller's
+ *     next synchronisation.
+ *   - A handle is not thread-safe.  The caller must not modify the UB prefix, the
+ *     weights or the outputs while a call that uses them is in flight.
+ *   - Rounding: products are accumulated in fp32 (MFMA) and each stored result is
+ *     rounded once to bf16, round-to-nearest-even.  An output element depends only on
+ *     its own input row and weight column: results are bit-identical for every chunk
+ *     count, stream count, order, aggregate setting, capacity and buffer offset.
+ */
+#ifndef CHUNKED_TP_OVERLAP_AMD_UB_H
+#define CHUNKED_TP_OVERLAP_AMD_UB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define UB_API __attribute__((visibility("default")))
+
+/* Largest number of compute streams a handle uses; num_max_streams above it is clamped. */
+#define UB_MAX_STREAMS 8
+/* Largest tensor-parallel size (number of K slices on the reduce-scatter side). */
+#define UB_MAX_TP 64
+
+typedef struct ub_ctx* ub_handle_t;
+/* A hipStream_t passed as an opaque pointer; NULL is the device's null stream. */
+typedef void* ub_stream_t;
+
+typedef enum {
+  UB_OK = 0,
+  UB_ERR_INVALID_ARG = 1,       /* null pointer, bad size, misalignment, bad option */
+  UB_ERR_NDIM = 2,              /* active shape is not 2-D                    [TE#3564] */
+  UB_ERR_ZERO_DIM = 3,          /* active shape has a dimension <= 0          [TE#3564] */
+  UB_ERR_CAPACITY = 4,          /* active T exceeds the registered capacity   [TE#3564] */
+  UB_ERR_HIDDEN_MISMATCH = 5,   /* active hidden differs from the registered  [TE#3564] */
+  UB_ERR_TP_DIVISIBILITY = 6,   /* T (or capacity) not divisible by tp_size   [TE#3564] */
+  UB_ERR_DTYPE = 7,             /* not bf16: quantized buffers are out of scope [TE#3564] */
+  UB_ERR_UNSUPPORTED = 8,       /* a valid request this build does not implement */
+  UB_ERR_BUFFER_TOO_SMALL = 9,  /* a registered byte size is below what the shape needs */
+  UB_ERR_NOT_INITIALIZED = 10,  /* null handle, or a reduce-scatter call without workspace */
+  UB_ERR_HIP = 11               /* a HIP runtime call failed; see ub_last_error */
+} ub_status_t;
+
+/* Element type of a UserBuffer.  Only UB_DTYPE_BF16 is accepted: the pages scope the
+ * prototype to unquantized 2-byte bf16 buffers ([TE#3564] "Implementation approach",
+ * last paragraph); the others are rejected with UB_ERR_DTYPE. */
+typedef enum {
+  UB_DTYPE_BF16 = 0,
+  UB_DTYPE_FP16 = 1,
+  UB_DTYPE_FP8_E4M3 = 2,
+  UB_DTYPE_FP8_E5M2 = 3
+} ub_dtype_t;
+
+/* Overlap method ([TE#1344] "method"). */
+typedef enum {
+  UB_RING_EXCHANGE = 0, /* chunk count forced to tp_size; ring order from `rank` */
+  UB_PIPELINE = 1,      /* num_splits chunks in natural order */
+  UB_BULK = 2           /* num_splits chunks in natural order */
+} ub_method_t;
+
+/* Which side of the overlap a plan describes. */
+typedef enum { UB_OP_AG = 0, UB_OP_RS = 1 } ub_op_t;
+
+/* Per-call overlap options: the keys of [TE#1344]'s option list.
+ *   num_splits       chunks the GEMM is cut into (>= 1); ignored for ring exchange,
+ *                    which uses tp_size chunks.
+ *   num_max_streams  compute streams = min(chunks, num_max_streams, UB_MAX_STREAMS), >= 1.
+ *                    Default 3.
+ *   aggregate        all-gather side only: chunks {2u, 2u+1} are merged into one launch.
+ *   atomic_gemm      0: one kernel launch per chunk from a host loop; 1: one kernel that
+ *                    walks the chunks on the device.  Results are identical.
+ *   rank             this rank in [0, tp_size): sets the ring order.
+ *   use_ce, num_sm, set_sm_margin  accepted for compatibility and ignored: on one GPU
+ *                    there is no send/recv to place on a copy engine and no
+ *                    communication kernel to reserve compute units for. */
+typedef struct {
+  int32_t method;
+  int32_t num_splits;
+  int32_t num_max_streams;
+  int32_t aggregate;
+  int32_t atomic_gemm;
+  int32_t rank;
+  int32_t use_ce;
+  int32_t num_sm;
+  int32_t set_sm_margin;
+} ub_overlap_cfg_t;
+
+/* One unit of an execution plan: rows [row0, row1) of the active T, at position `pos`
+ * of the execution order, on compute stream `stream` (0 = the caller's stream). */
+typedef struct {
+  int32_t pos;
+  int32_t unit;
+  int64_t row0;
+  int64_t row1;
+  int32_t stream;
+  int32_t reserved;
+} ub_plan_unit_t;
+
+/* Accumulated per-launch kernel timings (see ub_set_kernel_timing). */
+typedef struct {
+  int64_t launches;   /* kernel launches measured */
+  double total_ms;    /* sum of per-launch durations, HIP events on the launch stream */
+  double flops;       /* algorithmic floating-point operations of those launches */
+  double bytes;       /* algorithmic HBM bytes of those launches */
+} ub_kernel_stats_t;
+
+/* Fill `cfg` with the defaults of [TE#1344]: ring exchange, num_splits 1,
+ * num_max_streams 3, use_ce 1, aggregate 0, atomic_gemm 0, set_sm_margin 0, num_sm 0,
+ * rank 0. */
+UB_API void ub_overlap_cfg_default(ub_overlap_cfg_t* cfg);
+
+/* Bytes the caller must allocate for a registration of [capacity, hidden] over
+ * tp_size ranks: the UB itself (capacity * hidden * 2) and the reduce-scatter workspace
+ * of tp_size partial slots (tp_size * capacity * hidden * 2).  Same validation as
+ * ub_init.  Either output pointer may be NULL. */
+UB_API ub_status_t ub_required_bytes(int64_t capacity, int64_t hidden, int32_t tp_size,
+                                     ub_dtype_t dtype, size_t* ub_bytes,
+                                     size_t* rs_workspace_bytes);
+
+/* Register a UserBuffer at its maximum token capacity ([TE#3564] "Proposed API":
+ * initialize at [max_tokens, hidden_size] with tp_size, unquantized, bf16).
+ *   capacity, hidden  > 0; hidden % 8 == 0; capacity % tp_size == 0 (so that the initial
+ *                     active shape, which equals the capacity shape, is valid).
+ *   tp_size           1 .. UB_MAX_TP.
+ *   dtype             UB_DTYPE_BF16, else UB_ERR_DTYPE.
+ *   ub_buf, ub_bytes  device memory of at least capacity*hidden*2 bytes (16-byte
+ *                     aligned), else UB_ERR_BUFFER_TOO_SMALL / UB_ERR_INVALID_ARG.
+ *   rs_ws, rs_ws_bytes reduce-scatter workspace of at least tp_size*capacity*hidden*2
+ *                     bytes, or NULL/0 when the reduce-scatter side is not used.
+ * Records the pointers and sizes; allocates no device memory and makes no HIP call
+ * (streams and events are created on the first GEMM call, on the device current then).
+ * On success *out is a new handle whose active shape is [capacity, hidden]. */
+UB_API ub_status_t ub_init(ub_handle_t* out, int64_t capacity, int64_t hidden,
+                           int32_t tp_size, ub_dtype_t dtype, void* ub_buf, size_t ub_bytes,
+                           void* rs_ws, size_t rs_ws_bytes);
+
+/* Set the active shape for the next microbatch ([TE#3564] "Proposed API" and
+ * "Implementation approach"): shape = {T, hidden}, ndim = 2.  Checks, in the order the
+ * pages list the constraints, returning the first that fails: ndim != 2 -> NDIM; any
+ * dimension <= 0 -> ZERO_DIM; T > capacity -> CAPACITY; hidden != registered ->
+ * HIDDEN_MISMATCH; T % tp_size != 0 -> TP_DIVISIBILITY.  On success only host-side views
+ * change (T, element counts, chunk/shard/partial offsets); nothing is allocated, freed,
+ * re-registered or launched.  On failure the previous active shape is kept. */
+UB_API ub_status_t ub_set_active_shape(ub_handle_t h, const int64_t* shape, int32_t ndim);
+
+/* Active and capacity shapes ([TE#3564]: per-communicator active/capacity getters). */
+UB_API ub_status_t ub_get_active_shape(ub_handle_t h, int64_t shape_out[2]);
+UB_API ub_status_t ub_get_capacity_shape(ub_handle_t h, int64_t shape_out[2]);
+
+/* Execution plan a GEMM call with `cfg` would follow at the current active T
+ * ([TE#1344] "num_splits", "num_max_streams", "aggregate", "method").  Writes up to
+ * max_units entries to `out` (may be NULL when max_units is 0) and the unit and stream
+ * counts to *n_units / *n_streams.  Host-only. */
+UB_API ub_status_t ub_get_plan(ub_handle_t h, const ub_overlap_cfg_t* cfg, ub_op_t op,
+                               ub_plan_unit_t* out, int32_t max_units, int32_t* n_units,
+                               int32_t* n_streams);
+
+/* Copy `rows` rows of [*, hidden] bf16 from device memory `src` (row stride hidden) into
+ * active rows [row_offset, row_offset + rows) of the UB, asynchronously on `stream`
+ * (this is where a rank's own shard enters the buffer).  The copy-size check is against
+ * the active T, not the capacity ([TE#3564]: copy-size checks use the active element
+ * count): row_offset + rows > T -> UB_ERR_INVALID_ARG. */
+UB_API ub_status_t ub_copy_in(ub_handle_t h, const void* src, int64_t rows,
+                              int64_t row_offset, ub_stream_t stream);
+
+/* All-gather-side column-parallel GEMM over the active prefix ([MLM#1240] QKV / MLP fc1
+ * diagrams; [TE#1344] option list; [TE#3564] offsets from the active T):
+ *   C[t, j] = bf16( sum_k UB[t, k] * W[k, j] ),  t in [0, T), j in [0, n_cols),
+ * with UB the active [T, hidden] prefix (row stride hidden), W [hidden, n_cols] with row
+ * stride ldw >= n_cols, C [T, n_cols] with row stride ldc >= n_cols.  The rows are cut
+ * into the plan's units; unit u is one GEMM reading the UB at byte offset
+ * row0_u * hidden * 2.  Reads no UB byte beyond T*hidden elements; writes only C rows
+ * [0, T).  n_cols, ldw, ldc multiples of 8; hidden a multiple of 64 (else
+ * UB_ERR_UNSUPPORTED).  aggregate is honoured; W and C are caller memory. */
+UB_API ub_status_t ub_gemm_ag_chunked(ub_handle_t h, const void* w, int64_t n_cols,
+                                      int64_t ldw, void* c, int64_t ldc,
+                                      const ub_overlap_cfg_t* cfg, ub_stream_t stream);
+
+/* Reduce-scatter-side row-parallel GEMM ([MLM#1240] MLP diagram, RowParallelLinear;
+ * [TE#3564]: partial chunks inside the workspace's allocation, offsets from active T):
+ * with Ks = k / tp_size, for every plan unit (rows [r0, r1)) and slice s:
+ *   P_s[t, j] = bf16( sum_{k in [s Ks, (s+1) Ks)} A[t, k] * W[k, j] )
+ * written to the workspace at element (s*T + t) * hidden + j (the packed active prefix
+ * of tp_size slots), then
+ *   out[t, j] = bf16( sum_{s = 0..tp_size-1} P_s[t, j] )   (fp32 sum, ascending s)
+ * so that rank r's shard is out rows [r T/tp, (r+1) T/tp), contiguous.
+ * A is [T, k] (row stride lda >= k), W is [k, hidden] (row stride ldw >= hidden), out is
+ * [T, hidden] (row stride ldo >= hidden).  k % tp_size == 0 (else INVALID_ARG) and
+ * Ks % 64 == 0 (else UNSUPPORTED).  Requires a registered workspace (else
+ * NOT_INITIALIZED).  aggregate is ignored (it is an all-gather option).  Writes nothing
+ * beyond tp_size*T*hidden workspace elements or beyond T rows of out. */
+UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, int64_t lda,
+                                      const void* w, int64_t ldw, void* out, int64_t ldo,
+                                      const ub_overlap_cfg_t* cfg, ub_stream_t stream);
+
+/* The reduce-scatter sum alone: out[t, :] = bf16(sum_s P_s[t, :]) for all active rows
+ * t in [0, T), reading the tp_size partial slots currently in the workspace (as left by
+ * ub_gemm_rs_chunked at the same T).  One launch on `stream`.  For measuring the
+ * reduction by itself ([TE#1344] "pipeline": the reduce-scatter that the GEMM chunks
+ * feed). */
+UB_API ub_status_t ub_reduce_partials(ub_handle_t h, void* out, int64_t ldo,
+                                      ub_stream_t stream);
+
+/* Per-launch kernel timing.  While enabled, every GEMM and reduction launch is bracketed
+ * by HIP events recorded on the stream it is launched on; ub_get_kernel_timing waits for
+ * them and returns the accumulated durations with the algorithmic FLOPs and bytes of the
+ * measured launches, then clears the counters.  Disabled by default; enabling it adds two
+ * event records per launch. */
+UB_API ub_status_t ub_set_kernel_timing(ub_handle_t h, int32_t enable);
+UB_API ub_status_t ub_get_kernel_timing(ub_handle_t h, ub_kernel_stats_t* gemm,
+                                        ub_kernel_stats_t* reduce);
+
+/* Destroy a handle: waits for the handle's streams, then releases its streams and
+ * events.  Caller buffers are untouched.  NULL is accepted. */
+UB_API ub_status_t ub_destroy(ub_handle_t h);
+
+/* Static name of a status code ("UB_OK", "UB_ERR_CAPACITY", ...). */
+UB_API const char* ub_status_string(ub_status_t s);
+/* Message describing the last failure on h ("" if none); valid until the next call on h. */
+UB_API const char* ub_last_error(ub_handle_t h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CHUNKED_TP_OVERLAP_AMD_UB_H */

@@ -1,0 +1,194 @@
+"""Host-side tests of the C-ABI library (no GPU): exports, the buffer-manager state
+machine, plan tables against the oracle's independently written plan, argument errors.
+
+ub_init, ub_set_active_shape, the getters and ub_get_plan make no HIP call, and every
+argument check of the GEMM entry points runs before the first one, so all of this runs on
+the CPU with placeholder (never dereferenced) device addresses.
+"""
+
+import ctypes
+import itertools
+import os
+import re
+
+import pytest
+
+from oracle import manager, plan
+from tests.test_oracle_plan_manager import constraint_cases
+
+ub = pytest.importorskip("chunked_tp_overlap_amd.ub", reason="libub.so not built")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000  # 16-byte aligned placeholder device address (never dereferenced)
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "ub.h")).read()
+    return set(re.findall(r"UB_API\s+[\w\s\*]+?\b(ub_\w+)\s*\(", text))
+
+
+def test_every_declared_symbol_is_exported():
+    syms = header_symbols()
+    assert syms == set(ub.EXPORTS)
+    lib = ctypes.CDLL(ub.LIB_PATH)
+    for s in sorted(syms):
+        assert hasattr(lib, s), s
+
+
+def test_library_binds_to_torchs_hip_runtime():
+    maps = open("/proc/self/maps").read()
+    hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(hip) == 1, hip  # exactly one HIP runtime in the process
+
+
+def test_status_strings():
+    for code, name in ub.STATUS.items():
+        assert ub.ub_status_string(code) == name
+
+
+def _handle(capacity, hidden, tp, ws=True):
+    ub_bytes, ws_bytes = ub.ub_required_bytes(capacity, hidden, tp)
+    return ub.ub_init(capacity, hidden, tp, ub.UB_DTYPE_BF16, FAKE, ub_bytes,
+                      FAKE if ws else None, ws_bytes if ws else 0)
+
+
+def test_required_bytes_and_registration_errors():
+    assert ub.ub_required_bytes(8192, 4096, 8) == (8192 * 4096 * 2, 8 * 8192 * 4096 * 2)
+    with pytest.raises(ub.UBError) as e:
+        ub.ub_required_bytes(512, 256, 2, ub.UB_DTYPE_FP8_E4M3)
+    assert e.value.name == "UB_ERR_DTYPE"
+    with pytest.raises(ub.UBError) as e:
+        ub.ub_required_bytes(510, 256, 4)
+    assert e.value.name == "UB_ERR_TP_DIVISIBILITY"
+    with pytest.raises(ub.UBError) as e:
+        ub.ub_init(512, 256, 2, ub.UB_DTYPE_BF16, FAKE, 512 * 256 * 2 - 2)
+    assert e.value.name == "UB_ERR_BUFFER_TOO_SMALL"
+    with pytest.raises(ub.UBError) as e:
+        ub.ub_init(512, 256, 2, ub.UB_DTYPE_BF16, FAKE, 512 * 256 * 2, FAKE, 100)
+    assert e.value.name == "UB_ERR_BUFFER_TOO_SMALL"
+    with pytest.raises(ub.UBError) as e:
+        ub.ub_init(512, 256, 2, ub.UB_DTYPE_BF16, FAKE + 2, 512 * 256 * 2)
+    assert e.value.name == "UB_ERR_INVALID_ARG"
+    with pytest.raises(ub.UBError) as e:
+        ub.ub_init(512, 252, 2, ub.UB_DTYPE_BF16, FAKE, 512 * 256 * 2)
+    assert e.value.name == "UB_ERR_INVALID_ARG"
+
+
+def test_initial_shapes_are_capacity():
+    h = _handle(512, 256, 2)
+    try:
+        assert ub.ub_get_active_shape(h) == (512, 256)
+        assert ub.ub_get_capacity_shape(h) == (512, 256)
+    finally:
+        ub.ub_destroy(h)
+
+
+@pytest.mark.parametrize("cap,hid,tp,shape,expected", constraint_cases())
+def test_constraint_matrix_matches_oracle(cap, hid, tp, shape, expected):
+    h = _handle(cap, hid, tp)
+    try:
+        first = (max(tp, cap // 2 // tp * tp), hid)
+        ub.ub_set_active_shape(h, first)
+        st = ub.ub_set_active_shape(h, shape, check=False)
+        assert ub.STATUS[st] == ("UB_OK" if expected == manager.OK else "UB_ERR_" + expected)
+        if expected == manager.OK:
+            assert ub.ub_get_active_shape(h) == (shape[0], hid)
+        else:
+            assert ub.ub_get_active_shape(h) == first  # state unchanged on error
+            assert ub.ub_last_error(h) != ""
+        assert ub.ub_get_capacity_shape(h) == (cap, hid)
+    finally:
+        ub.ub_destroy(h)
+
+
+def _oracle_cfg(method, ns, nms, agg, rank):
+    return plan.OverlapCfg(method=method, num_splits=ns, num_max_streams=nms, aggregate=agg, rank=rank)
+
+
+def test_plan_tables_match_oracle_exhaustively():
+    for tp in (1, 2, 4, 8):
+        cap = 96 * tp
+        h = _handle(cap, 64, tp)
+        try:
+            for T in sorted({tp, 8 * tp, 24 * tp, 40 * tp, cap}):
+                ub.ub_set_active_shape(h, (T, 64))
+                for method, ns, nms, agg, op in itertools.product(
+                        plan.METHODS, (1, 2, 3, 5, 8, 16), (1, 2, 3, 8, 12), (False, True), ("ag", "rs")):
+                    for rank in sorted({0, 1 % tp, tp - 1}):
+                        cfg = ub.make_cfg(method, ns, nms, agg, rank=rank)
+                        units, S = ub.ub_get_plan(h, cfg, ub.UB_OP_AG if op == "ag" else ub.UB_OP_RS)
+                        ref = plan.build(T, tp, _oracle_cfg(method, ns, nms, agg, rank), op,
+                                         stream_limit=ub.UB_MAX_STREAMS)
+                        assert units == [(u.pos, u.index, u.row0, u.row1, u.stream) for u in ref], \
+                            (T, tp, method, ns, nms, agg, rank, op)
+                        assert S == plan.num_streams(_oracle_cfg(method, ns, nms, agg, rank), tp,
+                                                     ub.UB_MAX_STREAMS)
+        finally:
+            ub.ub_destroy(h)
+
+
+def test_plan_of_the_workloads():
+    h = _handle(16384, 4096, 8)
+    try:
+        ub.ub_set_active_shape(h, (12280, 4096))
+        units, S = ub.ub_get_plan(h, ub.make_cfg("pipeline", 4), ub.UB_OP_RS)
+        assert [(u[2], u[3]) for u in units] == [(0, 3070), (3070, 6140), (6140, 9210), (9210, 12280)]
+        assert S == 3
+        ub.ub_set_active_shape(h, (16384, 4096))
+        units, S = ub.ub_get_plan(h, ub.make_cfg("ring_exchange", 8, aggregate=True), ub.UB_OP_AG)
+        assert [u[3] - u[2] for u in units] == [4096] * 4 and S == 3
+    finally:
+        ub.ub_destroy(h)
+
+
+def test_gemm_argument_errors_before_any_hip_call():
+    h = _handle(512, 256, 2)
+    h_nows = _handle(512, 256, 2, ws=False)
+    cfg = ub.make_cfg("ring_exchange", 2)
+    try:
+        def st(name, *args):
+            return ub.STATUS[ub.raw_call(name, *args)]
+        cp = ctypes.byref(cfg)
+        assert st("ub_gemm_ag_chunked", h, None, 384, 384, FAKE, 384, cp, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_gemm_ag_chunked", h, FAKE + 8, 384, 384, FAKE, 384, cp, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_gemm_ag_chunked", h, FAKE, 380, 384, FAKE, 384, cp, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_gemm_ag_chunked", h, FAKE, 384, 376, FAKE, 384, cp, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_gemm_ag_chunked", h, FAKE, 384, 384, FAKE, 100, cp, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_gemm_ag_chunked", h, FAKE, 384, 384, FAKE, 384, None, None) == "UB_ERR_INVALID_ARG"
+        bad = ub.make_cfg("ring_exchange", 2, rank=2)
+        assert st("ub_gemm_ag_chunked", h, FAKE, 384, 384, FAKE, 384, ctypes.byref(bad), None) == "UB_ERR_INVALID_ARG"
+        bad = ub.make_cfg("pipeline", 0)
+        assert st("ub_gemm_ag_chunked", h, FAKE, 384, 384, FAKE, 384, ctypes.byref(bad), None) == "UB_ERR_INVALID_ARG"
+        bad = ub.make_cfg("pipeline", 2, num_max_streams=0)
+        assert st("ub_gemm_ag_chunked", h, FAKE, 384, 384, FAKE, 384, ctypes.byref(bad), None) == "UB_ERR_INVALID_ARG"
+        bad = ub.make_cfg("pipeline", 2)
+        bad.method = 7
+        assert st("ub_gemm_ag_chunked", h, FAKE, 384, 384, FAKE, 384, ctypes.byref(bad), None) == "UB_ERR_INVALID_ARG"
+        # reduce-scatter
+        assert st("ub_gemm_rs_chunked", h_nows, FAKE, 256, 256, FAKE, 256, FAKE, 256, cp, None) == "UB_ERR_NOT_INITIALIZED"
+        assert st("ub_gemm_rs_chunked", h, FAKE, 255, 256, FAKE, 256, FAKE, 256, cp, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_gemm_rs_chunked", h, FAKE, 96, 96, FAKE, 256, FAKE, 256, cp, None) == "UB_ERR_UNSUPPORTED"
+        assert st("ub_gemm_rs_chunked", h, FAKE, 256, 248, FAKE, 256, FAKE, 256, cp, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_gemm_rs_chunked", h, FAKE, 256, 256, FAKE, 256, FAKE, 128, cp, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_reduce_partials", h_nows, FAKE, 256, None) == "UB_ERR_NOT_INITIALIZED"
+        # copy-size checks against the active T, not the capacity
+        ub.ub_set_active_shape(h, (256, 256))
+        assert st("ub_copy_in", h, FAKE, 129, 128, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_copy_in", h, FAKE, 1, -1, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_copy_in", h, FAKE, 0, 256, None) == "UB_OK"  # empty copy, nothing launched
+        # null handle
+        assert st("ub_set_active_shape", None, None, 2) == "UB_ERR_NOT_INITIALIZED"
+        assert ub.raw_call("ub_destroy", None) == 0
+    finally:
+        ub.ub_destroy(h)
+        ub.ub_destroy(h_nows)
+
+
+def test_hidden_not_multiple_of_kstep_is_unsupported():
+    h = _handle(64, 72, 1)
+    try:
+        cfg = ub.make_cfg("bulk", 1)
+        st = ub.raw_call("ub_gemm_ag_chunked", h, FAKE, 8, 8, FAKE, 8, ctypes.byref(cfg), None)
+        assert ub.STATUS[st] == "UB_ERR_UNSUPPORTED"
+    finally:
+        ub.ub_destroy(h)

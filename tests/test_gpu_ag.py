@@ -1,0 +1,303 @@
+"""GPU parity of the all-gather-side chunked GEMM (ub_gemm_ag_chunked) against the oracle.
+
+Element-by-element on the tiny workload and on ragged shapes; bit-exact on integer inputs
+and across every scheduling knob, capacity and buffer offset; sampled rows at the full
+sizes of the QKV, fc1 and GQA-bulk workloads in the launch configuration the bench uses.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from chunked_tp_overlap_amd import workloads as wl
+from oracle import gemm as og
+from oracle import manager as om
+from oracle import plan as op
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ub():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import chunked_tp_overlap_amd.ub as m  # fails loudly when the library is not built
+    return m
+
+
+def _ocfg(method="ring_exchange", num_splits=1, num_max_streams=3, aggregate=False, rank=0):
+    return op.OverlapCfg(method=method, num_splits=num_splits, num_max_streams=num_max_streams,
+                         aggregate=aggregate, rank=rank)
+
+
+def _run(ub, reg, w_t, n_cols, cfg, stream=None, extra_rows=8):
+    c = gu.canary((reg.capacity + extra_rows, n_cols))
+    ub.ub_gemm_ag_chunked(reg.h, w_t, n_cols, n_cols, c, n_cols, cfg, stream)
+    torch.cuda.synchronize()
+    return gu.host(c)
+
+
+def _oracle_ag(capacity, hidden, tp, a_bits, w_bits, cfg):
+    m = om.UserBufferModel(capacity, hidden, tp)
+    assert m.set_active_shape((a_bits.shape[0], hidden)) == om.OK
+    m.fill_active(a_bits)
+    n = w_bits.shape[1]
+    c = np.full((capacity, n), om.CANARY, np.uint16)
+    st, written = og.ag_chunked(m, w_bits, n, n, c, n, cfg)
+    assert st == om.OK and np.all(written == 1)
+    return c[: a_bits.shape[0]]
+
+
+def test_tiny_ag_matches_oracle(ub):
+    w = wl.tiny_ag()
+    ra, rw, _ = w.seeds()
+    T = 256
+    a = wl.activations(w, T, ra)
+    wt = wl.weights(w, rw)
+    print(f"[tiny_ag] T={T} H={w.hidden} N={w.n_cols}", flush=True)
+    reg = gu.Registration(ub, w.capacity, w.hidden, w.tp, workspace=False, pad_rows=16)
+    try:
+        reg.set_T(T)
+        reg.fill(a)
+        ub_before = gu.host(reg.ub_t)
+        c = _run(ub, reg, gu.dev(wt), w.n_cols, ub.make_cfg(w.method, w.num_splits))
+        ref = _oracle_ag(w.capacity, w.hidden, w.tp, a, wt, _ocfg(w.method, w.num_splits))
+        stats = gu.check_close(c[:T], ref, a, wt, "tiny_ag")
+        print(stats)
+        assert np.all(c[T:] == gu.CANARY)                      # rows >= T untouched
+        assert np.array_equal(gu.host(reg.ub_t), ub_before)   # the UB is only read
+    finally:
+        reg.close()
+
+
+@pytest.mark.parametrize("cap,H,N,T,tp,method,ns", [
+    (1024, 512, 136, 296, 8, "ring_exchange", 8),   # ragged rows and a partial column tile
+    (64, 64, 8, 8, 1, "bulk", 1),                    # smallest shapes
+    (2048, 1024, 264, 1000, 8, "pipeline", 3),       # uneven chunks
+    (512, 256, 384, 512, 2, "bulk", 7),              # T == capacity
+    (4096, 2048, 128, 40, 8, "bulk", 16),            # more chunks than some ranks' rows
+])
+def test_integer_inputs_bit_exact(ub, cap, H, N, T, tp, method, ns):
+    """Integer inputs in [-2, 2]: fp32 accumulation is exact, so GPU == oracle bit for bit,
+    including the bf16 ties the sums produce."""
+    rng = np.random.default_rng(cap + H + N + T)
+    a = wl.integer_bits(rng, (T, H))
+    wt = wl.integer_bits(rng, (H, N))
+    print(f"[int_ag] cap={cap} H={H} N={N} T={T} tp={tp} {method} ns={ns}", flush=True)
+    reg = gu.Registration(ub, cap, H, tp, workspace=False, pad_rows=8)
+    try:
+        reg.set_T(T)
+        reg.fill(a)
+        c = _run(ub, reg, gu.dev(wt), N, ub.make_cfg(method, ns))
+        ref = _oracle_ag(cap, H, tp, a, wt, _ocfg(method, ns))
+        assert np.array_equal(c[:T], ref)
+        assert np.all(c[T:] == gu.CANARY)
+        assert np.all(gu.host(reg.ub_t)[(cap) * H:] == gu.CANARY)
+    finally:
+        reg.close()
+
+
+def test_closed_forms(ub):
+    """All ones -> K exactly; identity weights -> A bit for bit; one-hot rows -> W rows."""
+    rng = np.random.default_rng(3)
+    H, T = 512, 200
+    reg = gu.Registration(ub, 256, H, 8, workspace=False)
+    try:
+        reg.set_T(T)
+        reg.fill(wl.const_bits((T, H), 1.0))
+        c = _run(ub, reg, gu.dev(wl.const_bits((H, 64), 1.0)), 64, ub.make_cfg("ring_exchange", 8))
+        assert np.all(c[:T] == 0x4400)  # 512.0
+        a = wl.normal_bits(rng, (T, H))
+        reg.fill(a)
+        eye = (np.eye(H, dtype=np.uint16) * 0x3F80).astype(np.uint16)
+        c = _run(ub, reg, gu.dev(eye), H, ub.make_cfg("bulk", 3))
+        assert np.array_equal(c[:T], a)
+        wt = wl.normal_bits(rng, (H, 72), 0.02)
+        idx = rng.integers(0, H, size=T)
+        onehot = np.zeros((T, H), np.uint16)
+        onehot[np.arange(T), idx] = 0x3F80
+        reg.fill(onehot)
+        c = _run(ub, reg, gu.dev(wt), 72, ub.make_cfg("pipeline", 5))
+        assert np.array_equal(c[:T], wt[idx])
+    finally:
+        reg.close()
+
+
+def test_bit_identical_across_schedules_capacity_and_offset(ub):
+    """GPU results are bit-identical for every chunk count, stream count, order, rank,
+    aggregate setting, capacity and UB base offset."""
+    rng = np.random.default_rng(4)
+    H, N, T, tp = 512, 200, 296, 8
+    a = wl.normal_bits(rng, (T, H))
+    wt = gu.dev(wl.normal_bits(rng, (H, N), 0.02))
+    reg = gu.Registration(ub, 512, H, tp, workspace=False)
+    try:
+        reg.set_T(T)
+        reg.fill(a)
+        ref = _run(ub, reg, wt, N, ub.make_cfg("bulk", 1))[:T]
+        for method in ("ring_exchange", "pipeline", "bulk"):
+            for ns in (1, 2, 3, 8, 13):
+                for nms in (1, 2, 3, 8):
+                    for agg in (False, True):
+                        for rank in (0, 5):
+                            cfg = ub.make_cfg(method, ns, nms, agg, rank=rank)
+                            got = _run(ub, reg, wt, N, cfg)[:T]
+                            assert np.array_equal(got, ref), (method, ns, nms, agg, rank)
+    finally:
+        reg.close()
+    # another capacity, and the UB registered at a 4 KiB + 16 B offset inside a larger tensor
+    for cap, off_elems in ((T, 0), (4096, 0), (1024, 2056)):
+        ub_bytes, _ = ub.ub_required_bytes(cap, H, tp)
+        big = gu.canary((off_elems + cap * H + 64,))
+        h = ub.ub_init(cap, H, tp, ub.UB_DTYPE_BF16, big.data_ptr() + 2 * off_elems, ub_bytes)
+        try:
+            ub.ub_set_active_shape(h, (T, H))
+            big[off_elems: off_elems + T * H].copy_(gu.dev(a).reshape(-1))
+            c = gu.canary((T + 4, N))
+            ub.ub_gemm_ag_chunked(h, wt, N, N, c, N, ub.make_cfg("ring_exchange", 8))
+            torch.cuda.synchronize()
+            assert np.array_equal(gu.host(c)[:T], ref), (cap, off_elems)
+        finally:
+            ub.ub_destroy(h)
+
+
+def test_strided_weights_and_output(ub):
+    """ldw > n_cols and ldc > n_cols: only the first n_cols columns are read / written."""
+    rng = np.random.default_rng(12)
+    H, N, T = 256, 96, 64
+    a = wl.normal_bits(rng, (T, H))
+    wfull = wl.normal_bits(rng, (H, N + 40), 0.02)
+    reg = gu.Registration(ub, 128, H, 2, workspace=False)
+    try:
+        reg.set_T(T)
+        reg.fill(a)
+        c = gu.canary((T, N + 24))
+        ub.ub_gemm_ag_chunked(reg.h, gu.dev(wfull), N, N + 40, c, N + 24, ub.make_cfg("bulk", 2))
+        torch.cuda.synchronize()
+        c = gu.host(c)
+        ref = og.ag_rows(a, wfull[:, :N])
+        gu.check_close(c[:, :N], ref, a, wfull[:, :N], "strided")
+        assert np.all(c[:, N:] == gu.CANARY)
+    finally:
+        reg.close()
+
+
+def test_caller_stream_ordering(ub):
+    """Work on a non-default caller stream: the call is ordered after a fill enqueued on
+    that stream and before a copy enqueued after it."""
+    rng = np.random.default_rng(13)
+    H, N, T = 1024, 512, 1024
+    a = wl.normal_bits(rng, (T, H))
+    wt = gu.dev(wl.normal_bits(rng, (H, N), 0.02))
+    reg = gu.Registration(ub, T, H, 8, workspace=False)
+    try:
+        reg.set_T(T)
+        reg.fill(a)
+        ref = _run(ub, reg, wt, N, ub.make_cfg("ring_exchange", 8))[:T]
+        s = torch.cuda.Stream()
+        a_dev = gu.dev(a).reshape(-1)
+        with torch.cuda.stream(s):
+            reg.ub_t[: T * H].fill_(0)
+            reg.ub_t[: T * H].copy_(a_dev)
+            c = gu.canary((T, N))
+            ub.ub_gemm_ag_chunked(reg.h, wt, N, N, c, N, ub.make_cfg("ring_exchange", 8), s)
+            out = c.clone()
+        torch.cuda.synchronize()
+        assert np.array_equal(gu.host(out), ref)
+    finally:
+        reg.close()
+
+
+def test_copy_in_places_a_shard(ub):
+    H, cap, tp = 256, 512, 4
+    reg = gu.Registration(ub, cap, H, tp, workspace=False)
+    try:
+        reg.set_T(256)
+        src = gu.dev(wl.normal_bits(np.random.default_rng(1), (64, H)))
+        ub.ub_copy_in(reg.h, src, 64, 128)
+        torch.cuda.synchronize()
+        u = gu.host(reg.ub_t).reshape(cap, H)
+        assert np.array_equal(u[128:192], gu.host(src))
+        assert np.all(u[:128] == gu.CANARY) and np.all(u[192:] == gu.CANARY)
+        with pytest.raises(ub.UBError):
+            ub.ub_copy_in(reg.h, src, 64, 224)  # past the active T
+    finally:
+        reg.close()
+
+
+def _sample_rows(rng, T, n_chunks, extra=40):
+    rows = set(rng.integers(0, T, size=extra).tolist()) | {0, T - 1}
+    for c in range(1, n_chunks):
+        b = (c * T) // n_chunks
+        rows |= {b - 1, b}
+    return np.array(sorted(rows))
+
+
+def _full_size_ag(ub, w, Ts, label):
+    ra, rw, _ = w.seeds()
+    a_all = wl.activations(w, w.capacity, ra)
+    wt = wl.weights(w, rw)
+    w_t = gu.dev(wt)
+    reg = gu.Registration(ub, w.capacity, w.hidden, w.tp, workspace=False, pad_rows=8)
+    rng = np.random.default_rng(99)
+    cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, w.aggregate)
+    n_chunks = w.tp if w.method == "ring_exchange" else w.num_splits
+    try:
+        reg.fill(a_all)  # one fill of the whole capacity; each T uses its prefix
+        c = gu.canary((w.capacity + 8, w.n_cols))
+        for T in Ts:
+            print(f"[{label}] T={T}", flush=True)
+            reg.set_T(T)
+            c.fill_(gu.CANARY)
+            ub.ub_gemm_ag_chunked(reg.h, w_t, w.n_cols, w.n_cols, c, w.n_cols, cfg)
+            torch.cuda.synchronize()
+            ch = gu.host(c)
+            rows = _sample_rows(rng, T, n_chunks)
+            ref = og.ag_rows(a_all[rows], wt)
+            gu.check_close(ch[rows], ref, a_all[rows], wt, f"{label} T={T}")
+            assert np.all(ch[T:] == gu.CANARY), f"{label}: rows >= T written at T={T}"
+    finally:
+        reg.close()
+
+
+def test_qkv_full_size_sampled(ub):
+    w = wl.qkv()
+    Ts = wl.tokens_for(w)
+    _full_size_ag(ub, w, Ts[:4] + [min(Ts), max(Ts)], "qkv")
+
+
+def test_fc1_full_size_sampled(ub):
+    w = wl.fc1()
+    Ts = wl.tokens_for(w)
+    _full_size_ag(ub, w, [Ts[0], min(Ts), max(Ts), w.capacity], "fc1")
+
+
+def test_gqa_bulk_sweep_sampled(ub):
+    """One capacity buffer, never reallocated, swept over a declared subset of the T grid
+    (first, every 4th, last on the 1016-step grid, and the capacity 32768)."""
+    w = wl.gqa_bulk()
+    Ts = wl.gqa_tokens(include_capacity=False)
+    subset = sorted(set(Ts[::4]) | {Ts[0], Ts[-1], 32768})
+    _full_size_ag(ub, w, subset, "gqa_bulk")
+
+
+def test_kernel_timing_counts_launches(ub):
+    H, N, T = 512, 256, 512
+    rng = np.random.default_rng(2)
+    reg = gu.Registration(ub, 1024, H, 8, workspace=False)
+    try:
+        reg.set_T(T)
+        reg.fill(wl.normal_bits(rng, (T, H)))
+        wt = gu.dev(wl.normal_bits(rng, (H, N), 0.02))
+        ub.ub_set_kernel_timing(reg.h, True)
+        for _ in range(3):
+            _run(ub, reg, wt, N, ub.make_cfg("ring_exchange", 8, aggregate=True))
+        g, r = ub.ub_get_kernel_timing(reg.h)
+        ub.ub_set_kernel_timing(reg.h, False)
+        assert g["launches"] == 3 * 4 and r["launches"] == 0
+        assert g["flops"] == pytest.approx(3 * 2.0 * T * H * N)
+        assert g["total_ms"] > 0
+        g2, _ = ub.ub_get_kernel_timing(reg.h)
+        assert g2["launches"] == 0  # counters cleared by the read
+    finally:
+        reg.close()

@@ -1,0 +1,191 @@
+"""GPU parity of the reduce-scatter-side chunked GEMM (ub_gemm_rs_chunked) and of the
+partial-sum reduction (ub_reduce_partials) against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+from chunked_tp_overlap_amd import workloads as wl
+from oracle import gemm as og
+from oracle import manager as om
+from oracle import plan as op
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ub():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import chunked_tp_overlap_amd.ub as m
+    return m
+
+
+def _run_rs(ub, reg, a_t, k, w_t, cfg, stream=None, extra_rows=8):
+    H = reg.hidden
+    out = gu.canary((reg.capacity + extra_rows, H))
+    ub.ub_gemm_rs_chunked(reg.h, a_t, k, k, w_t, H, out, H, cfg, stream)
+    torch.cuda.synchronize()
+    return gu.host(out)
+
+
+def _oracle_rs(capacity, H, tp, a_bits, w_bits, cfg):
+    T, k = a_bits.shape
+    m = om.UserBufferModel(capacity, H, tp)
+    assert m.set_active_shape((T, H)) == om.OK
+    out = np.full((capacity, H), om.CANARY, np.uint16)
+    st, written = og.rs_chunked(m, a_bits, k, k, w_bits, H, out, H, cfg)
+    assert st == om.OK and np.all(written == 1)
+    return out[:T], m.ws[: tp * T * H].reshape(tp, T, H)
+
+
+def test_tiny_rs_matches_oracle(ub):
+    w = wl.tiny_rs()
+    ra, rw, _ = w.seeds()
+    T = 256
+    a = wl.activations(w, T, ra)
+    wt = wl.weights(w, rw)
+    print(f"[tiny_rs] T={T} K={w.k} H={w.hidden} tp={w.tp}", flush=True)
+    reg = gu.Registration(ub, w.capacity, w.hidden, w.tp, pad_rows=16)
+    try:
+        reg.set_T(T)
+        out = _run_rs(ub, reg, gu.dev(a), w.k, gu.dev(wt), ub.make_cfg(w.method, w.num_splits))
+        ref, parts = _oracle_rs(w.capacity, w.hidden, w.tp, a, wt, op.OverlapCfg(method=w.method))
+        print(gu.check_rs_close(out[:T], ref, a, wt, w.tp, "tiny_rs"))
+        ws = gu.host(reg.ws_t)
+        ks = w.k // w.tp
+        for s in range(w.tp):
+            slot = ws[s * T * w.hidden:(s + 1) * T * w.hidden].reshape(T, w.hidden)
+            gu.check_close(slot, parts[s], a[:, s * ks:(s + 1) * ks], wt[s * ks:(s + 1) * ks],
+                           f"tiny_rs partial {s}")
+        assert np.all(ws[w.tp * T * w.hidden:] == gu.CANARY)  # workspace tail untouched
+        assert np.all(out[T:] == gu.CANARY)
+        shards = og.shards(out, T, w.hidden, w.tp)
+        assert np.array_equal(np.concatenate(shards), out[:T])
+    finally:
+        reg.close()
+
+
+@pytest.mark.parametrize("cap,H,K,T,tp,method,ns", [
+    (512, 256, 256, 256, 2, "ring_exchange", 2),
+    (1024, 512, 1024, 296, 8, "pipeline", 4),       # 8 slices of 128, ragged chunks
+    (256, 64, 1024, 96, 4, "bulk", 5),
+    (64, 128, 512, 64, 1, "pipeline", 2),            # tp = 1: a plain GEMM
+])
+def test_integer_inputs_bit_exact(ub, cap, H, K, T, tp, method, ns):
+    rng = np.random.default_rng(cap + H + K + T)
+    a = wl.integer_bits(rng, (T, K))
+    wt = wl.integer_bits(rng, (K, H))
+    print(f"[int_rs] cap={cap} H={H} K={K} T={T} tp={tp} {method} ns={ns}", flush=True)
+    reg = gu.Registration(ub, cap, H, tp, pad_rows=8)
+    try:
+        reg.set_T(T)
+        out = _run_rs(ub, reg, gu.dev(a), K, gu.dev(wt), ub.make_cfg(method, ns))
+        ref, parts = _oracle_rs(cap, H, tp, a, wt, op.OverlapCfg(method=method, num_splits=ns))
+        assert np.array_equal(out[:T], ref)
+        ws = gu.host(reg.ws_t)
+        assert np.array_equal(ws[: tp * T * H].reshape(tp, T, H), parts)
+        assert np.all(ws[tp * T * H:] == gu.CANARY)
+        assert np.all(out[T:] == gu.CANARY)
+    finally:
+        reg.close()
+
+
+def test_closed_form_fc2_ones(ub):
+    """K = 14336 in 8 slices: every partial is 1792 and every output 14336, exactly."""
+    T, H, K, tp = 64, 256, 14336, 8
+    reg = gu.Registration(ub, 128, H, tp)
+    try:
+        reg.set_T(T)
+        out = _run_rs(ub, reg, gu.dev(wl.const_bits((T, K), 1.0)), K,
+                      gu.dev(wl.const_bits((K, H), 1.0)), ub.make_cfg("pipeline", 4))
+        assert np.all(out[:T] == wl.const_bits((1,), 14336.0)[0])
+        ws = gu.host(reg.ws_t)[: tp * T * H]
+        assert np.all(ws == wl.const_bits((1,), 1792.0)[0])
+    finally:
+        reg.close()
+
+
+def test_bit_identical_across_schedules(ub):
+    rng = np.random.default_rng(5)
+    T, H, K, tp = 232, 128, 1024, 4
+    a = gu.dev(wl.normal_bits(rng, (T, K)))
+    wt = gu.dev(wl.normal_bits(rng, (K, H), 0.02))
+    reg = gu.Registration(ub, 512, H, tp)
+    try:
+        reg.set_T(T)
+        ref = _run_rs(ub, reg, a, K, wt, ub.make_cfg("pipeline", 1))[:T]
+        ref_ws = gu.host(reg.ws_t)[: tp * T * H].copy()
+        for method in ("ring_exchange", "pipeline", "bulk"):
+            for ns in (1, 2, 3, 4, 7):
+                for nms in (1, 2, 3):
+                    for rank in (0, 3):
+                        got = _run_rs(ub, reg, a, K, wt, ub.make_cfg(method, ns, nms, rank=rank))[:T]
+                        assert np.array_equal(got, ref), (method, ns, nms, rank)
+                        assert np.array_equal(gu.host(reg.ws_t)[: tp * T * H], ref_ws)
+    finally:
+        reg.close()
+
+
+def test_reduce_partials_alone_matches(ub):
+    rng = np.random.default_rng(6)
+    T, H, K, tp = 296, 256, 2048, 8
+    a = wl.normal_bits(rng, (T, K))
+    wt = wl.normal_bits(rng, (K, H), 0.02)
+    reg = gu.Registration(ub, 512, H, tp)
+    try:
+        reg.set_T(T)
+        out = _run_rs(ub, reg, gu.dev(a), K, gu.dev(wt), ub.make_cfg("pipeline", 4))
+        out2 = gu.canary((T + 4, H))
+        ub.ub_reduce_partials(reg.h, out2, H)
+        torch.cuda.synchronize()
+        out2 = gu.host(out2)
+        assert np.array_equal(out2[:T], out[:T])
+        assert np.all(out2[T:] == gu.CANARY)
+        # and the reduction itself against an exact sum of the GPU's own partials
+        ws = gu.host(reg.ws_t)[: tp * T * H].reshape(tp, T, H)
+        from oracle import bf16 as ob
+        exact = ob.encode_rne(og.exact_sum([ob.decode(ws[s]) for s in range(tp)]))
+        gap = np.abs(ob.decode(out2[:T]) - ob.decode(exact))
+        bound = ob.ulp(exact) + tp * 2.0 ** -24 * np.sum(np.abs(ob.decode(ws)), axis=0)
+        assert np.all(gap <= bound)
+    finally:
+        reg.close()
+
+
+def test_fc2_full_size_sampled(ub):
+    """The MLP fc2 workload (capacity 16384, hidden 4096, K 14336 in 8 slices, pipeline
+    with 4 chunks) at each T of its sweep, on one registration; sampled rows vs the
+    oracle, workspace and output tails untouched."""
+    w = wl.fc2()
+    ra, rw, _ = w.seeds()
+    a_all = wl.activations(w, w.capacity, ra)
+    wt = wl.weights(w, rw)
+    a_t, w_t = gu.dev(a_all), gu.dev(wt)
+    H, tp = w.hidden, w.tp
+    reg = gu.Registration(ub, w.capacity, H, tp, pad_rows=8)
+    rng = np.random.default_rng(7)
+    cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams)
+    try:
+        out = gu.canary((w.capacity + 8, H))
+        for T in wl.FC2_TOKENS:
+            print(f"[fc2] T={T}", flush=True)
+            reg.set_T(T)
+            out.fill_(gu.CANARY)
+            reg.ws_t.fill_(gu.CANARY)
+            ub.ub_gemm_rs_chunked(reg.h, a_t, w.k, w.k, w_t, H, out, H, cfg)
+            torch.cuda.synchronize()
+            oh = gu.host(out)
+            rows = set(rng.integers(0, T, size=24).tolist()) | {0, T - 1}
+            for c in range(1, w.num_splits):
+                rows |= {(c * T) // w.num_splits - 1, (c * T) // w.num_splits}
+            for r in range(1, tp):
+                rows |= {r * T // tp - 1, r * T // tp}  # shard boundaries
+            rows = np.array(sorted(rows))
+            ref, _ = og.rs_rows(a_all[rows], wt, tp)
+            gu.check_rs_close(oh[rows], ref, a_all[rows], wt, tp, f"fc2 T={T}")
+            assert np.all(oh[T:] == gu.CANARY)
+            tail = reg.ws_t[tp * T * H:]
+            assert bool((tail == gu.CANARY).all().item())
+    finally:
+        reg.close()
