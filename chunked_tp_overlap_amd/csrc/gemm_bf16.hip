@@ -1,21 +1,51 @@
 // bf16 GEMM on gfx950 matrix cores: C = bf16(A * B), fp32 accumulation.
 //
 // This is the per-chunk GEMM of the overlap schedule ("How to setup TP Overlap configs",
-// Transformer Engine issue 1344, "num_splits": the GEMM is cut into chunks, each a GEMM
-// of its own).  A chunk's A operand is read in place from the capacity-sized UserBuffer at
+// Transformer Engine issue 1344, "num_splits": the GEMM is cut into chunks, each a GEMM of
+// its own).  A chunk's A operand is read in place from the capacity-sized UserBuffer at
 // the chunk's row offset ("[Feature Request] Support dynamic token counts in TP
 // communication/GEMM overlap", Transformer Engine issue 3564, "Implementation approach in
 // the prototype": offsets from the active first dimension).
 //
-// All operands row-major.  A [m, k] (lda), B [k, n] (ldb), C [m, n] (ldc); blockIdx.z
+// All operands row-major: A [m, k] (lda), B [k, n] (ldb), C [m, n] (ldc).  blockIdx.z
 // selects a batch entry at the given element strides (the reduce-scatter side's K slices).
 //
-// Tiling: a 256-thread workgroup (4 waves of 64) computes a 128x128 tile of C; each wave
-// owns a 64x64 quadrant as 2x2 blocks of v_mfma_f32_32x32x16_bf16.  K advances 64 at a
-// time through LDS.  Every tile shape uses the same instruction and the same ascending-K
-// order, so an output element's bits depend only on its own A row and B column: the
-// chunking, the row offset and the tile position never change a result.
+// Design (CDNA4):
+//  - A workgroup computes a BM x BN tile of C with v_mfma_f32_32x32x16_bf16 (fp32
+//    accumulators).  K advances BK = 32 per step through S stages in LDS.
+//  - Global -> LDS moves use buffer_load_dwordx4 ... lds: 16 bytes per lane straight into
+//    LDS, no staging registers.  The buffer range check returns zeros for rows past m and
+//    for columns past n (those lanes get an offset beyond the resource's size), so ragged
+//    edges need no branches; every byte of the offset is in the per-lane VGPR offset, so
+//    the range check covers all of it.  The loads are issued from inline asm: the
+//    compiler cannot tell which stage an LDS read touches and would otherwise wait for
+//    every in-flight load before each read, which serialises loads and MFMAs.  Their
+//    completion is tracked by explicit vmcnt waits before the barriers instead.
+//  - A direct load writes 64 lanes x 16 bytes contiguously, so bank conflicts are avoided
+//    by XOR swizzles instead of padding (conflict-free whether the LDS serves 128 or 256
+//    bytes per clock): A row R keeps its 16-byte k-chunk c in slot c ^ a_swz(R); B k-row
+//    r keeps its 16-byte column chunk q in slot q ^ b_swz(r).
+//  - A operands: one ds_read_b128 per lane (8 consecutive k of one row).  B operands: two
+//    ds_read_b64_tr_b16 per lane: a 16-lane group reads 4 k-rows x 16 columns (lane j at
+//    k-row j/4, columns 4*(j%4)..+3) and lane i receives the 4 k values of column i, so the
+//    n-contiguous B tile feeds the MFMA without a transpose pass.
+//  - Large tiles use 8 waves in a ping-pong: two groups of four waves, one wave of each
+//    per SIMD, alternate memory clusters (fragment reads + their share of the direct
+//    loads) and compute clusters (MFMAs), one group a cluster behind the other, so every
+//    SIMD has one wave issuing MFMAs while its sibling waits on memory.  Small tiles use 4
+//    waves, two workgroups per CU.
+//  - Epilogue: accumulators are rounded to bf16 (RNE), staged through LDS as a row-major
+//    tile and written with 16-byte coalesced stores; rows >= m and columns >= n are masked.
+//  - Every tile shape uses the same instruction and the same ascending-K order, so an
+//    output element's bits depend only on its own A row and B column: chunking, row offset
+//    and tile choice never change a result.
+//  - Workgroups are numbered so that consecutive tiles of a launch land on the same XCD
+//    (the dispatcher deals workgroups round-robin over the 8 XCDs, each with its own L2),
+//    and within an XCD tiles are walked in groups of rows that share B columns.
 #include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
 
 #include "ub_internal.h"
 
@@ -23,15 +53,16 @@ namespace ubx {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+#define GLOBAL_PTR(T, p) ((__attribute__((address_space(1))) T*)(p))
 
-constexpr int BM = 128;
-constexpr int BN = 128;
-constexpr int BK = 64;
-constexpr int THREADS = 256;
-constexpr int LDA_S = BK + 8;  // A tile row in LDS (elements); +16 B keeps b128 reads conflict-free
-constexpr int LDB_S = BN + 8;  // B tile row in LDS (k-major)
+constexpr int NUM_XCD = 8;
+constexpr int RSRC_WORD3 = 0x00020000;   // gfx9-family raw buffer: 32-bit data format
+constexpr uint32_t OOB = 0x80000000u;    // an offset beyond every resource size used here
 
 struct Params {
   const uint16_t* a;
@@ -39,114 +70,422 @@ struct Params {
   uint16_t* c;
   int64_t lda, sa, ldb, sb, ldc, sc;
   int32_t m, n, k;
+  int32_t tiles_m, tiles_n;  // tile grid of one batch entry
 };
 
-__device__ inline uint16_t bf16_bits(float f) {
-  // fptrunc to bfloat lowers to gfx950's v_cvt_pk_bf16_f32: round to nearest even.
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+template <int BM_, int BN_, int BK_, int S_, int WGM_, int WGN_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_;
+  static constexpr int WGM = WGM_, WGN = WGN_;      // wave grid
+  static constexpr int NW = WGM * WGN;              // waves per workgroup
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int WM = BM / WGM;               // wave tile rows
+  static constexpr int WN = BN / WGN;               // wave tile cols
+  static constexpr int FM = WM / 32;                // 32x32 blocks per wave, along m
+  static constexpr int FN = WN / 32;                // along n
+  static constexpr int SUBS = BK / 16;              // 16-wide k sub-steps per step
+  static constexpr int A_ROW = BK * 2;              // bytes per A row in a stage
+  static constexpr int A_CPR = BK / 8;              // 16-byte chunks per A row
+  static constexpr int A_BYTES = BM * A_ROW;
+  static constexpr int B_ROW = BN * 2;              // bytes per B k-row
+  static constexpr int B_CPR = BN / 8;
+  static constexpr int B_BYTES = BK * B_ROW;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int NA = A_BYTES / 1024 / NW;    // 1 KB direct loads per wave per step, A
+  static constexpr int NB = B_BYTES / 1024 / NW;    // and B
+  static constexpr int L = NA + NB;                 // loads per wave per step
+  static constexpr int A_ROWS_PER_LOAD = 1024 / A_ROW;
+  static constexpr int B_ROWS_PER_LOAD = 1024 / B_ROW;
+  static constexpr int LDC = BN + 8;                // epilogue tile row (elements)
+  static constexpr int EPI = BM * LDC * 2;
+  static constexpr int LDS_BYTES = (S * STAGE > EPI) ? S * STAGE : EPI;
+  static_assert(NA >= 1 && NB >= 1, "tile too small for the load split");
+  static_assert(FM >= 1 && FN >= 1, "wave tile below one 32x32 block");
+  static_assert(S * L <= 63, "vmcnt is a 6-bit count");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS is 160 KiB per CU");
+};
+
+// Swizzles (see the header comment).
+template <int CPR>
+__device__ constexpr int a_swz(int R) {
+  return CPR == 8 ? ((R ^ (R >> 1)) & 7) : (((R >> 1) ^ (R >> 2)) & 3);
+}
+__device__ constexpr int b_swz(int r) { return (2 * (r & 3)) ^ (4 * (r & 3)); }
+
+// Raw buffer resource (base, num_records bytes) in scalar registers.
+__device__ inline i32x4 make_rsrc(const void* base, uint32_t num_records) {
+  const uint64_t b = (uint64_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((b >> 32) & 0xFFFF));
+  r[2] = __builtin_amdgcn_readfirstlane((int)num_records);
+  r[3] = RSRC_WORD3;
+  return r;
 }
 
-__global__ __launch_bounds__(THREADS) void gemm_bf16_tile128(Params p) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDA_S];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BK * LDB_S];
+// 16 bytes per lane from rsrc + voffset into LDS at lds_addr + 16 * lane (see the header
+// comment for why this is inline asm).
+__device__ inline void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voffset) {
+  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   ::"s"(lds_addr), "v"(voffset), "s"(rsrc)
+                   : "memory");
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
-  const uint16_t* A = p.a + blockIdx.z * p.sa;
-  const uint16_t* B = p.b + blockIdx.z * p.sb;
-  uint16_t* C = p.c + blockIdx.z * p.sc;
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(size_t)LDS_PTR(const void, p));
+}
 
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+template <int N>
+__device__ inline void wait_vmcnt_and_barrier() {
+  // this wave's direct loads older than the newest N have landed and its LDS reads are
+  // done; then the same for every wave of the workgroup
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
-  const uint4 zero = make_uint4(0, 0, 0, 0);
-  for (int k0 = 0; k0 < p.k; k0 += BK) {
-    uint4 ra[4], rb[4];
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  // fptrunc to bfloat lowers to gfx950's v_cvt_pk_bf16_f32: round to nearest even.
+  const uint32_t a = __builtin_bit_cast(uint16_t, static_cast<__bf16>(lo));
+  const uint32_t b = __builtin_bit_cast(uint16_t, static_cast<__bf16>(hi));
+  return a | (b << 16);
+}
+
+// Tile coordinates of workgroup `wg` of a batch entry: a contiguous block of tile indices
+// per XCD, walked in groups of G tile-rows so neighbours share B columns.
+__device__ inline void tile_of(int wg, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  int t = wg;
+  if (total >= NUM_XCD * 2) {
+    const int per = total / NUM_XCD;   // full share of each XCD
+    const int full = per * NUM_XCD;
+    if (wg < full) t = (wg % NUM_XCD) * per + wg / NUM_XCD;
+  }
+  constexpr int G = 4;
+  const int group = t / (G * tiles_n);
+  const int first_m = group * G;
+  const int gm = min(G, tiles_m - first_m);
+  const int r = t - group * G * tiles_n;
+  tm = first_m + r % gm;
+  tn = r / gm;
+}
+
+// Per-workgroup state shared by both kernels: tile position, buffer resources, and the
+// per-lane offsets of the direct loads and of the fragment reads.
+template <class C>
+struct Tile {
+  int lane, wave, wm, wn, m0, n0;
+  uint16_t* cg;
+  i32x4 ra, rb;
+  uint32_t a_off[C::NA], b_off[C::NB];
+  uint32_t a_kstep, b_kstep;
+  int a_rd_row, a_rd_c, a_rd_x, b_krow, b_col_chunk, b_x, b_in;
+
+  __device__ inline void init(const Params& p, int tid) {
+    lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    wm = wave / C::WGN;
+    wn = wave % C::WGN;
+    int tm, tn;
+    tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    m0 = tm * C::BM;
+    n0 = tn * C::BN;
+    const uint16_t* A = p.a + blockIdx.z * p.sa + (int64_t)m0 * p.lda;
+    const uint16_t* B = p.b + blockIdx.z * p.sb + n0;
+    cg = p.c + blockIdx.z * p.sc;
+    // A from this tile's first row, valid rows only; B from column n0 of the batch entry
+    const int rows_valid = min(C::BM, p.m - m0);
+    ra = make_rsrc(A, (uint32_t)(rows_valid * p.lda * 2));
+    rb = make_rsrc(B, (uint32_t)(((int64_t)p.k * p.ldb - n0) * 2));
+    // Direct load t of this wave: A rows A_ROWS_PER_LOAD*(wave*NA + t) + lane/A_CPR, slot
+    // lane%A_CPR holding k-chunk slot ^ a_swz(row); B k-rows B_ROWS_PER_LOAD*(wave*NB + t) +
+    // lane/B_CPR, slot lane%B_CPR holding column chunk slot ^ b_swz(krow).
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {  // A tile: 128 rows x 64 k, 8 k per lane
-      const int v = tid + i * THREADS;
-      const int r = v >> 3, cc = (v & 7) * 8;
-      const int gm = m0 + r;
-      ra[i] = gm < p.m ? *reinterpret_cast<const uint4*>(A + (int64_t)gm * p.lda + k0 + cc) : zero;
+    for (int t = 0; t < C::NA; ++t) {
+      const int row = C::A_ROWS_PER_LOAD * (wave * C::NA + t) + lane / C::A_CPR;
+      const int chunk = (lane % C::A_CPR) ^ a_swz<C::A_CPR>(row);
+      a_off[t] = (uint32_t)((row * p.lda + chunk * 8) * 2);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {  // B tile: 64 k x 128 cols, 8 cols per lane
-      const int v = tid + i * THREADS;
-      const int r = v >> 4, cc = (v & 15) * 8;
-      const int gn = n0 + cc;
-      rb[i] = gn < p.n ? *reinterpret_cast<const uint4*>(B + (int64_t)(k0 + r) * p.ldb + gn) : zero;
+    for (int t = 0; t < C::NB; ++t) {
+      const int krow = C::B_ROWS_PER_LOAD * (wave * C::NB + t) + lane / C::B_CPR;
+      const int chunk = (lane % C::B_CPR) ^ b_swz(krow);
+      const bool ok = n0 + chunk * 8 < p.n;
+      b_off[t] = ok ? (uint32_t)((krow * p.ldb + chunk * 8) * 2) : OOB;
     }
-    __syncthreads();  // the previous step's LDS reads are done
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int v = tid + i * THREADS;
-      *reinterpret_cast<uint4*>(&As[(v >> 3) * LDA_S + (v & 7) * 8]) = ra[i];
-      *reinterpret_cast<uint4*>(&Bs[(v >> 4) * LDB_S + (v & 15) * 8]) = rb[i];
-    }
-    __syncthreads();
+    a_kstep = C::BK * 2;
+    b_kstep = (uint32_t)(C::BK * p.ldb * 2);
+    // Fragment reads.  A: row R = wm*WM + i*32 + (lane&31), k-chunk (kk/8 + lane/32) in slot
+    // ^ a_swz(R) (a function of lane&31 only).  B: k-row kk + (lane/32)*8 + (lane>>2)&3
+    // (+4 for the second read), column wn*WN + j*32 + ((lane>>4)&1)*16 + (lane&3)*4.
+    a_rd_row = (wm * C::WM + (lane & 31)) * C::A_ROW;
+    a_rd_c = lane >> 5;
+    a_rd_x = a_swz<C::A_CPR>(lane & 31);
+    b_krow = (lane >> 5) * 8 + ((lane >> 2) & 3);
+    b_col_chunk = (wn * C::WN + ((lane >> 4) & 1) * 16 + (lane & 3) * 4) >> 3;
+    b_x = b_swz((lane >> 2) & 3);
+    b_in = (lane & 1) * 8;
+  }
 
+  // This wave's direct loads of step ks into stage ks % S.  Steps past the end are issued
+  // with out-of-range offsets (they write zeros and touch no memory) so that every wait
+  // can count a fixed number of newer loads.
+  __device__ inline void issue_loads(unsigned char* smem, int ks, int nk) const {
+    unsigned char* sa = smem + (ks % C::S) * C::STAGE;
+    unsigned char* sb = sa + C::A_BYTES;
+    const bool live = ks < nk;
+    const uint32_t ak = (uint32_t)ks * a_kstep, bk = (uint32_t)ks * b_kstep;
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 af[2], bfr[2];
-      const int kl = kk + (lane >> 5) * 8;  // this lane's 8 consecutive k
+    for (int t = 0; t < C::NA; ++t)
+      dma16(ra, lds_addr(sa + (wave * C::NA + t) * 1024), live ? a_off[t] + ak : OOB);
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        const int row = wm * 64 + mi * 32 + (lane & 31);
-        af[mi] = *reinterpret_cast<const bf16x8*>(&As[row * LDA_S + kl]);
-      }
+    for (int t = 0; t < C::NB; ++t)
+      dma16(rb, lds_addr(sb + (wave * C::NB + t) * 1024),
+            (live && b_off[t] != OOB) ? b_off[t] + bk : OOB);
+  }
+
+  __device__ inline void read_frags(const unsigned char* smem, int ks, int kk, bf16x8* af,
+                                    bf16x8* bf) const {
+    const unsigned char* sa = smem + (ks % C::S) * C::STAGE;
+    const unsigned char* sb = sa + C::A_BYTES;
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int col = wn * 64 + ni * 32 + (lane & 31);
-        u16x8 t;
+    for (int i = 0; i < C::FM; ++i)
+      af[i] = *LDS_PTR(const bf16x8,
+                       sa + a_rd_row + i * 32 * C::A_ROW + (((kk >> 3) + a_rd_c) ^ a_rd_x) * 16);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) t[e] = Bs[(kl + e) * LDB_S + col];
-        bfr[ni] = __builtin_bit_cast(bf16x8, t);
-      }
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+    for (int j = 0; j < C::FN; ++j) {
+      const unsigned char* q =
+          sb + (kk + b_krow) * C::B_ROW + (((b_col_chunk + j * 4) ^ b_x) * 16) + b_in;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, q));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, q + 4 * C::B_ROW));
+      bf[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   }
 
-  // 32x32 accumulator layout: lane holds column (lane & 31); element e holds row
-  // 8*(e/4) + 4*(lane/32) + (e%4).
+  // bf16 tile in LDS (the caller guarantees no wave still reads or loads into LDS), then
+  // 16-byte coalesced stores.  32x32 accumulator layout: lane holds column (lane & 31);
+  // element e holds row 8*(e/4) + 4*(lane/32) + (e%4).
+  __device__ inline void store(unsigned char* smem, const Params& p, int tid,
+                               const f32x16 (&acc)[C::FM][C::FN]) const {
+    uint16_t* ct = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+    for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int col = n0 + wn * 64 + ni * 32 + (lane & 31);
+      for (int j = 0; j < C::FN; ++j) {
+        const int col = wn * C::WN + j * 32 + (lane & 31);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * 64 + mi * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-        if (row < p.m && col < p.n) C[(int64_t)row * p.ldc + col] = bf16_bits(acc[mi][ni][e]);
+        for (int e = 0; e < 16; e += 2) {
+          const int row = wm * C::WM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+          const uint32_t v = pack_bf16x2(acc[i][j][e], acc[i][j][e + 1]);
+          *LDS_PTR(uint16_t, ct + row * C::LDC + col) = (uint16_t)(v & 0xFFFF);
+          *LDS_PTR(uint16_t, ct + (row + 1) * C::LDC + col) = (uint16_t)(v >> 16);
+        }
       }
+    __syncthreads();
+    constexpr int VPR = C::BN / 8;  // 16-byte vectors per tile row
+#pragma unroll
+    for (int i = 0; i < C::BM * VPR / C::THREADS; ++i) {
+      const int v = tid + i * C::THREADS;
+      const int r = v / VPR, cc = (v % VPR) * 8;
+      const int gr = m0 + r, gc = n0 + cc;
+      if (gr < p.m && gc < p.n)
+        *GLOBAL_PTR(u32x4, cg + (int64_t)gr * p.ldc + gc) =
+            *LDS_PTR(const u32x4, ct + r * C::LDC + cc);
     }
+  }
+};
+
+template <class C>
+__device__ inline void mfma_block(f32x16 (&acc)[C::FM][C::FN], const bf16x8* af, const bf16x8* bf) {
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+}
+
+// ---- 8-wave ping-pong ------------------------------------------------------------------
+// Waves 0-3 (group 0) and 4-7 (group 1) hold one SIMD each.  Each wave alternates a memory
+// cluster (all fragments of step ks from LDS; its share of the direct loads of step ks+D)
+// and a compute cluster (the MFMAs of step ks), with a barrier after each.  Group 1 starts
+// one barrier late, so the groups' clusters interleave.  With barriers b0, b1, ... group 0
+// runs memory clusters between b(2ks) and b(2ks+1), group 1 between b(2ks+1) and b(2ks+2).
+//  - stage reuse: step ks+D goes into the stage of step ks+D-S, whose last reader finished
+//    before b(2(ks+D-S)+2) <= b(2ks) because D <= S-1;
+//  - landing: before b(2ks+2) each wave waits for its own loads of step ks+1 (issued D-1
+//    memory clusters earlier, so (D-1)*L newer loads may stay in flight): group 1 at the
+//    end of its memory cluster, group 0 at the end of its compute cluster;
+//  - every wave executes the same number of barriers (2*nk + 4).
+template <class C, int D>
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_bf16_pingpong(Params p) {
+  static_assert(C::NW == 8, "ping-pong needs two waves per SIMD");
+  static_assert(D >= 2 && D <= C::S - 1, "load distance");
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int tid = threadIdx.x;
+  Tile<C> t;
+  t.init(p, tid);
+  const int group = t.wave >> 2;
+
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  bf16x8 af[C::SUBS][C::FM], bf[C::SUBS][C::FN];
+  const int nk = p.k / C::BK;
+
+#pragma unroll
+  for (int s = 0; s < D; ++s) t.issue_loads(smem, s, nk);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt_and_barrier<(D - 1) * C::L>();  // b0: step 0 landed everywhere
+  __builtin_amdgcn_sched_barrier(0);
+  if (group == 1) __asm__ volatile("s_barrier" ::: "memory");  // b1 for group 1
+  __builtin_amdgcn_sched_barrier(0);
+
+  for (int ks = 0; ks < nk; ++ks) {
+    // memory cluster
+#pragma unroll
+    for (int sub = 0; sub < C::SUBS; ++sub) t.read_frags(smem, ks, sub * 16, af[sub], bf[sub]);
+    t.issue_loads(smem, ks + D, nk);
+    __builtin_amdgcn_sched_barrier(0);
+    if (group == 1) {
+      __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((D - 1) * C::L) : "memory");
+    } else {
+      __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // compute cluster
+#pragma unroll
+    for (int sub = 0; sub < C::SUBS; ++sub) mfma_block<C>(acc, af[sub], bf[sub]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (group == 0) {
+      __asm__ volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((D - 1) * C::L) : "memory");
+    } else {
+      __asm__ volatile("s_barrier" ::: "memory");
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (group == 0) __asm__ volatile("s_barrier" ::: "memory");  // matches group 1's b1
+  wait_vmcnt_and_barrier<0>();  // trailing out-of-range loads landed before LDS is reused
+  t.store(smem, p, tid, acc);
+}
+
+// ---- 4-wave, S-stage pipeline -----------------------------------------------------------
+// One barrier per step, before its last sub-step: step ks+1 has landed (the S-2 newer
+// steps may still be in flight), every wave is done reading stage ks % S, which then takes
+// step ks + S; the first fragments of step ks+1 load while the last MFMAs of step ks run.
+template <class C>
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void gemm_bf16_pipelined(Params p) {
+  static_assert(C::S >= 2, "at least two stages");
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int tid = threadIdx.x;
+  Tile<C> t;
+  t.init(p, tid);
+
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  bf16x8 af[2][C::FM], bf[2][C::FN];
+  const int nk = p.k / C::BK;
+
+#pragma unroll
+  for (int s = 0; s < C::S; ++s) t.issue_loads(smem, s, nk);
+  wait_vmcnt_and_barrier<(C::S - 1) * C::L>();
+  t.read_frags(smem, 0, 0, af[0], bf[0]);
+
+  for (int ks = 0; ks < nk; ++ks) {
+#pragma unroll
+    for (int sub = 0; sub < C::SUBS; ++sub) {
+      const int b = sub & 1;
+      if (sub + 1 < C::SUBS) {
+        t.read_frags(smem, ks, (sub + 1) * 16, af[b ^ 1], bf[b ^ 1]);
+      } else {
+        wait_vmcnt_and_barrier<(C::S - 2) * C::L>();
+        t.issue_loads(smem, ks + C::S, nk);
+        // at the last step this reads a stage of zeros that is never used
+        t.read_frags(smem, ks + 1, 0, af[b ^ 1], bf[b ^ 1]);
+      }
+      mfma_block<C>(acc, af[b], bf[b]);
+    }
+  }
+  wait_vmcnt_and_barrier<0>();  // trailing out-of-range loads landed before LDS is reused
+  t.store(smem, p, tid, acc);
+}
+
+template <class C, class K>
+hipError_t launch(K kernel, const GemmArgs& g, hipStream_t stream) {
+  Params p{g.a, g.b, g.c, g.lda, g.a_batch_stride, g.ldb, g.b_batch_stride,
+           g.ldc, g.c_batch_stride, g.m, g.n, g.k, 0, 0};
+  p.tiles_m = (g.m + C::BM - 1) / C::BM;
+  p.tiles_n = (g.n + C::BN - 1) / C::BN;
+  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+  if (tiles > 0x7FFFFFFF || g.batch > 65535) return hipErrorInvalidValue;
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  hipLaunchKernelGGL(kernel, dim3((unsigned)tiles, 1, g.batch), dim3(C::THREADS),
+                     C::LDS_BYTES, stream, p);
+  return hipGetLastError();
+}
+
+using PP256x256 = Cfg<256, 256, 32, 4, 2, 4>;   // 8 waves of 128x64
+using PP256x128 = Cfg<256, 128, 32, 5, 4, 2>;   // 8 waves of 64x64
+using PL128x128 = Cfg<128, 128, 32, 4, 2, 2>;   // 4 waves of 64x64, 2 workgroups per CU
+constexpr int PP_D = 3;
+
+enum TileKind { kTile128x128 = 0, kTile256x128 = 1, kTile256x256 = 3 };
+
+// Tile choice.  Larger tiles halve the L2 -> LDS traffic per FLOP, which bounds this
+// kernel; smaller ones give more workgroups when a launch is small.
+int choose_tile(const GemmArgs& g) {
+  static int forced = [] {
+    const char* s = std::getenv("UBX_GEMM_TILE");  // tuning override
+    if (!s) return -1;
+    if (!std::strcmp(s, "128x128")) return (int)kTile128x128;
+    if (!std::strcmp(s, "256x128")) return (int)kTile256x128;
+    if (!std::strcmp(s, "256x256")) return (int)kTile256x256;
+    return -1;
+  }();
+  if (forced >= 0) return forced;
+  auto count = [&](int bm, int bn) {
+    return (int64_t)((g.m + bm - 1) / bm) * ((g.n + bn - 1) / bn) * g.batch;
+  };
+  if (count(256, 256) >= 256) return kTile256x256;
+  if (count(256, 128) >= 192) return kTile256x128;
+  return kTile128x128;
 }
 
 }  // namespace
 
+bool gemm_shape_supported(const GemmArgs& g) {
+  // Offsets into B are 32-bit byte offsets from column n0 of the batch entry, and one A
+  // tile spans at most 256 rows; both must stay below the out-of-range marker.
+  return (int64_t)g.k * g.ldb * 2 < (int64_t)OOB && (int64_t)256 * g.lda * 2 < (int64_t)OOB;
+}
+
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream) {
   if (g.m <= 0 || g.n <= 0 || g.batch <= 0) return hipSuccess;
-  if (g.k <= 0 || g.k % BK != 0 || g.n % 8 != 0) return hipErrorInvalidValue;
-  const int64_t gy = (g.m + BM - 1) / BM;
-  if (gy > 65535 || g.batch > 65535) return hipErrorInvalidValue;
-  Params p{g.a, g.b, g.c, g.lda, g.a_batch_stride, g.ldb, g.b_batch_stride,
-           g.ldc, g.c_batch_stride, g.m, g.n, g.k};
-  dim3 grid((g.n + BN - 1) / BN, static_cast<unsigned>(gy), g.batch);
-  hipLaunchKernelGGL(gemm_bf16_tile128, grid, dim3(THREADS), 0, stream, p);
-  return hipGetLastError();
+  if (g.k <= 0 || g.k % kGemmKStep != 0 || g.n % 8 != 0 || !gemm_shape_supported(g))
+    return hipErrorInvalidValue;
+  switch (choose_tile(g)) {
+    case kTile256x256:
+      return launch<PP256x256>(&gemm_bf16_pingpong<PP256x256, PP_D>, g, stream);
+    case kTile256x128:
+      return launch<PP256x128>(&gemm_bf16_pingpong<PP256x128, PP_D>, g, stream);
+    default:
+      return launch<PL128x128>(&gemm_bf16_pipelined<PL128x128>, g, stream);
+  }
 }
 
 }  // namespace ubx
