@@ -5,16 +5,20 @@ Metric: bf16 TFLOP/s of the chunked AG/RS GEMM at the active T, and its fraction
 dense bf16 MFMA peak.  One step = one pass of the hot path over one batch of the QKV
 workload: for each of its 32 THD microbatches, set the active shape [T, 4096] on the one
 capacity-8192 UserBuffer and run the chunked all-gather-side GEMM (W [4096, 1536], ring
-exchange over tp = 8 chunks, 3 compute streams).  FLOPs are algorithmic: 2 * T * 4096 *
-1536 per microbatch, active T only.  Inputs are seeded synthetic draws already resident
-in HBM when the timed region starts.
+exchange over tp = 8 chunks).  FLOPs are algorithmic: 2 * T * 4096 * 1536 per microbatch,
+active T only.  Inputs are seeded synthetic draws already resident in HBM when the timed
+region starts.
 
-The other workloads (fc1 with aggregate, fc2 reduce-scatter with its reduction, the GQA
-bulk sweep) are measured after the timed region and reported under "secondary".
-Prints one JSON line.
+The primary schedule is the device-side chunk loop (option atomic_gemm: one launch per
+call whose workgroups walk the 8 ring chunks in ring order); the host loop of per-chunk
+launches on min(8, 3) streams is measured as well and reported under "modes".
+
+Prints one JSON line.  --profile-pass runs only a short stretch of the primary workload
+(and a copy kernel of known size) for rocprofv3.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -22,6 +26,10 @@ import time
 
 MFMA_PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
 HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+GEMM_SRC = os.path.join(ROOT, "chunked_tp_overlap_amd", "csrc", "gemm_bf16.hip")
+REDUCE_SRC = os.path.join(ROOT, "chunked_tp_overlap_amd", "csrc", "reduce_partials.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def parse_args():
@@ -29,15 +37,81 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--cpu-seconds", type=float, default=12.0,
-                   help="bound on the CPU-oracle baseline sample (seconds of work)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="minimum CPU-oracle baseline work (seconds)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
+    p.add_argument("--profile-pass", action="store_true",
+                   help="run the primary workload briefly plus a 1 GiB copy, print nothing else")
     return p.parse_args()
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+class Qkv:
+    """The QKV workload on one registered UserBuffer."""
+
+    def __init__(self, ub, wl, torch, np, dev):
+        self.ub, self.torch = ub, torch
+        w = self.w = wl.qkv()
+        ra, rw, rt = w.seeds()
+        self.Ts, _ = wl.qkv_pack_tokens(rt)
+        log(f"generating inputs: capacity {w.capacity} x {w.hidden}, W {w.hidden} x {w.n_cols}")
+        self.a_host = wl.activations(w, w.capacity, ra)
+        self.w_host = wl.weights(w, rw)
+        ub_bytes, _ = ub.ub_required_bytes(w.capacity, w.hidden, w.tp)
+        self.ub_t = torch.from_numpy(self.a_host.view(np.int16).ravel()).to(dev)
+        self.w_t = torch.from_numpy(self.w_host.view(np.int16)).to(dev)
+        self.c_t = torch.empty((w.capacity, w.n_cols), dtype=torch.int16, device=dev)
+        self.h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, self.ub_t, ub_bytes)
+        self.flops = sum(2.0 * T * w.hidden * w.n_cols for T in self.Ts)
+        self.stream = torch.cuda.current_stream()
+
+    def cfg(self, atomic):
+        w = self.w
+        return self.ub.make_cfg(w.method, w.num_splits, w.num_max_streams, w.aggregate, atomic)
+
+    def step(self, cfg):
+        ub, w = self.ub, self.w
+        for T in self.Ts:
+            ub.ub_set_active_shape(self.h, (T, w.hidden))
+            ub.ub_gemm_ag_chunked(self.h, self.w_t, w.n_cols, w.n_cols, self.c_t, w.n_cols, cfg,
+                                  self.stream)
+
+    def timed(self, cfg, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step(cfg)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step(cfg)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    def per_microbatch(self, cfg, reps=5):
+        torch, ub, w = self.torch, self.ub, self.w
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        out = []
+        for T in self.Ts:
+            ub.ub_set_active_shape(self.h, (T, w.hidden))
+            ub.ub_gemm_ag_chunked(self.h, self.w_t, w.n_cols, w.n_cols, self.c_t, w.n_cols, cfg,
+                                  self.stream)
+            e0.record(self.stream)
+            for _ in range(reps):
+                ub.ub_gemm_ag_chunked(self.h, self.w_t, w.n_cols, w.n_cols, self.c_t, w.n_cols,
+                                      cfg, self.stream)
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            out.append((T, e0.elapsed_time(e1) / reps))
+        return out
 
 
 def main():
@@ -58,78 +132,67 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
+    q = Qkv(ub, wl, torch, np, dev)
+    primary = q.cfg(atomic=True)
 
-    # ---- the QKV workload -------------------------------------------------------------
-    w = wl.qkv()
-    ra, rw, rt = w.seeds()
-    Ts, packs = wl.qkv_pack_tokens(rt)
-    log(f"generating inputs: capacity {w.capacity} x {w.hidden}, W {w.hidden} x {w.n_cols}")
-    a_host = wl.activations(w, w.capacity, ra)
-    w_host = wl.weights(w, rw)
-    ub_bytes, _ = ub.ub_required_bytes(w.capacity, w.hidden, w.tp)
-    ub_t = torch.from_numpy(a_host.view(np.int16).ravel()).to(dev)
-    w_t = torch.from_numpy(w_host.view(np.int16)).to(dev)
-    c_t = torch.empty((w.capacity, w.n_cols), dtype=torch.int16, device=dev)
-    h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes)
-    cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, w.aggregate)
-    stream = torch.cuda.current_stream()
-    step_flops = sum(2.0 * T * w.hidden * w.n_cols for T in Ts)
-
-    def step():
-        for T in Ts:
-            ub.ub_set_active_shape(h, (T, w.hidden))
-            ub.ub_gemm_ag_chunked(h, w_t, w.n_cols, w.n_cols, c_t, w.n_cols, cfg, stream)
-
-    log(f"warmup {args.warmup} steps of {len(Ts)} microbatches")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    ub.ub_set_kernel_timing(h, True)
-    ub.ub_get_kernel_timing(h)  # clear
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    gemm_stats, _ = ub.ub_get_kernel_timing(h)
-    ub.ub_set_kernel_timing(h, False)
-    wall = t1 - t0
-    ev_ms = ev0.elapsed_time(ev1)
-    tflops = step_flops * args.steps / wall / 1e12
-    log(f"timed {args.steps} steps: {wall * 1e3:.2f} ms wall, {ev_ms:.2f} ms events, "
-        f"{tflops:.1f} TFLOP/s")
-
-    # per-microbatch times, one launch sequence each, for the T >= 4096 aggregate
-    per_mb = []
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for T in Ts:
-        ub.ub_set_active_shape(h, (T, w.hidden))
-        ub.ub_gemm_ag_chunked(h, w_t, w.n_cols, w.n_cols, c_t, w.n_cols, cfg, stream)
-        reps = 5
-        e0.record(stream)
-        for _ in range(reps):
-            ub.ub_gemm_ag_chunked(h, w_t, w.n_cols, w.n_cols, c_t, w.n_cols, cfg, stream)
-        e1.record(stream)
+    if args.profile_pass:
+        # primary workload, then a plain copy of 1 GiB (2^29 int16 -> 2^29 int16) used to
+        # calibrate FETCH_SIZE / WRITE_SIZE
+        q.timed(primary, steps=2, warmup=1)
+        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
         torch.cuda.synchronize()
-        per_mb.append((T, e0.elapsed_time(e1) / reps))
-    big = [(T, ms) for T, ms in per_mb if T >= 4096]
-    agg_ge4096 = sum(2.0 * T * w.hidden * w.n_cols for T, _ in big) / (sum(ms for _, ms in big) / 1e3) / 1e12
+        log("profile pass done")
+        ub.ub_destroy(q.h)
+        return
 
-    g_ach = gemm_stats["flops"] / (gemm_stats["total_ms"] / 1e3) / 1e12 if gemm_stats["launches"] else 0.0
+    log(f"warmup {args.warmup}, timed {args.steps} steps of {len(q.Ts)} microbatches (atomic_gemm)")
+    sec = q.timed(primary, args.steps, args.warmup)
+    tflops = q.flops / sec / 1e12
+    log(f"primary: {sec * 1e3:.3f} ms/step, {tflops:.1f} TFLOP/s")
+
+    # the same timed region again with per-launch HIP events on the launch stream
+    ub.ub_set_kernel_timing(q.h, True)
+    ub.ub_get_kernel_timing(q.h)
+    sec_i = q.timed(primary, args.steps, 0)
+    gemm_stats, _ = ub.ub_get_kernel_timing(q.h)
+    ub.ub_set_kernel_timing(q.h, False)
+    g_ach = gemm_stats["flops"] / (gemm_stats["total_ms"] / 1e3) / 1e12
+
+    per_mb = q.per_microbatch(primary)
+    big = [(T, ms) for T, ms in per_mb if T >= 4096]
+    agg_ge4096 = sum(2.0 * T * q.w.hidden * q.w.n_cols for T, _ in big) / (sum(ms for _, ms in big) / 1e3) / 1e12
+
+    host_cfg = q.cfg(atomic=False)
+    sec_h = q.timed(host_cfg, max(2, args.steps // 2), 1)
+    ub.ub_set_kernel_timing(q.h, True)
+    ub.ub_get_kernel_timing(q.h)
+    q.timed(host_cfg, 2, 0)
+    host_stats, _ = ub.ub_get_kernel_timing(q.h)
+    ub.ub_set_kernel_timing(q.h, False)
+
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("gemm_src_hash") == src_hash(GEMM_SRC):
+            traffic = tr.get("qkv_gemm_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+
     roofline = {
-        "bound": "mfma", "kernel": "gemm_bf16 (per-unit chunk GEMM)",
+        "bound": "mfma", "kernel": "gemm_bf16_pingpong (device-side chunk loop, one launch per call)",
         "achieved": round(g_ach, 2), "peak": MFMA_PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-        "frac": round(g_ach / MFMA_PEAK_BF16_TFLOPS, 4), "traffic": None,
+        "frac": round(g_ach / MFMA_PEAK_BF16_TFLOPS, 4), "traffic": traffic,
         "launches": gemm_stats["launches"],
         "avg_launch_us": round(gemm_stats["total_ms"] * 1e3 / max(1, gemm_stats["launches"]), 3),
         "avg_launch_gflop": round(gemm_stats["flops"] / max(1, gemm_stats["launches"]) / 1e9, 4),
+        "algorithmic_bytes_per_launch": round(gemm_stats["bytes"] / max(1, gemm_stats["launches"])),
+        "measured_pass_ms_per_step": round(sec_i * 1e3, 4),
     }
 
+    w = q.w
     result = {
         "metric": "bf16 TFLOP/s of chunked AG/RS GEMM at active T; % of MFMA peak",
         "value": round(tflops, 3),
@@ -137,7 +200,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "ms_per_step": round(sec * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -146,30 +209,37 @@ def main():
         "pct_of_mfma_peak": round(100 * tflops / MFMA_PEAK_BF16_TFLOPS, 2),
         "config": {
             "workload": "qkv_ag: column-parallel AG-GEMM over a [8192, 4096] bf16 UserBuffer, "
-                        "W [4096, 1536], tp 8, ring exchange (8 chunks), 3 streams, "
-                        "32 THD microbatches per step",
+                        "W [4096, 1536], tp 8, ring exchange (8 chunks), 32 THD microbatches "
+                        "per step, device-side chunk loop",
             "capacity": w.capacity, "hidden": w.hidden, "n_cols": w.n_cols, "tp": w.tp,
             "method": w.method, "num_splits": w.num_splits, "num_max_streams": w.num_max_streams,
-            "microbatches": len(Ts), "T_min": min(Ts), "T_max": max(Ts),
-            "T_mean": round(sum(Ts) / len(Ts), 1), "gflop_per_step": round(step_flops / 1e9, 2),
+            "atomic_gemm": True, "microbatches": len(q.Ts), "T_min": min(q.Ts), "T_max": max(q.Ts),
+            "T_mean": round(sum(q.Ts) / len(q.Ts), 1), "gflop_per_step": round(q.flops / 1e9, 2),
             "seed": w.seed,
         },
-        "event_ms_per_step": round(ev_ms / args.steps, 4),
         "tflops_T_ge_4096_per_microbatch_aggregate": round(agg_ge4096, 3),
+        "modes": {
+            "atomic_gemm": {"tflops": round(tflops, 2), "ms_per_step": round(sec * 1e3, 4)},
+            "host_loop_3_streams": {
+                "tflops": round(q.flops / sec_h / 1e12, 2), "ms_per_step": round(sec_h * 1e3, 4),
+                "avg_launch_us": round(host_stats["total_ms"] * 1e3 / max(1, host_stats["launches"]), 3),
+                "per_launch_tflops": round(host_stats["flops"] / max(1e-9, host_stats["total_ms"] / 1e3) / 1e12, 2)},
+        },
         "roofline": roofline,
     }
 
     props = torch.cuda.get_device_properties(0)
     result["device"] = {"name": props.name, "cus": props.multi_processor_count,
-                        "gcn_arch": getattr(props, "gcnArchName", "")}
+                        "gcn_arch": getattr(props, "gcnArchName", ""),
+                        "gemm_src_hash": src_hash(GEMM_SRC)}
 
     if not args.no_secondary:
-        result["secondary"] = secondary(ub, wl, torch, np, dev, log)
+        result["secondary"] = secondary(ub, wl, torch, np, dev)
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, Ts, a_host, w_host, args.cpu_seconds, log)
+        result["cpu_baseline"] = cpu_baseline(q, args.cpu_seconds)
 
-    ub.ub_destroy(h)
+    ub.ub_destroy(q.h)
     print(json.dumps(result), flush=True)
 
 
@@ -184,11 +254,11 @@ def _time_calls(fn, torch, stream, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def secondary(ub, wl, torch, np, dev, log):
+def secondary(ub, wl, torch, np, dev):
     out = {}
     stream = torch.cuda.current_stream()
 
-    # fc1: aggregate-2x, 16 microbatches
+    # fc1: SwiGLU gate+up, aggregate-2x, 16 microbatches
     w = wl.fc1()
     ra, rw, rt = w.seeds()
     Ts = wl.fc1_tokens(rt)
@@ -198,26 +268,30 @@ def secondary(ub, wl, torch, np, dev, log):
     w_t = torch.from_numpy(wl.weights(w, rw).view(np.int16)).to(dev)
     c_t = torch.empty((w.capacity, w.n_cols), dtype=torch.int16, device=dev)
     h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes)
-    cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, w.aggregate)
-    tot_f = tot_ms = big_f = big_ms = 0.0
-    for T in Ts:
-        ub.ub_set_active_shape(h, (T, w.hidden))
-        ms = _time_calls(lambda: ub.ub_gemm_ag_chunked(h, w_t, w.n_cols, w.n_cols, c_t, w.n_cols, cfg, stream),
-                         torch, stream, 5)
-        f = 2.0 * T * w.hidden * w.n_cols
-        tot_f += f
-        tot_ms += ms
-        if T >= 4096:
-            big_f += f
-            big_ms += ms
-    out["fc1_ag"] = {"tflops_all": round(tot_f / tot_ms / 1e9, 2),
-                     "tflops_T_ge_4096": round(big_f / big_ms / 1e9, 2) if big_ms else None,
-                     "pct_peak_T_ge_4096": round(100 * big_f / big_ms / 1e9 / MFMA_PEAK_BF16_TFLOPS, 2) if big_ms else None,
-                     "microbatches": len(Ts)}
+    res = {}
+    for atomic in (True, False):
+        cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, w.aggregate, atomic)
+        tot_f = tot_ms = big_f = big_ms = 0.0
+        for T in Ts:
+            ub.ub_set_active_shape(h, (T, w.hidden))
+            ms = _time_calls(lambda: ub.ub_gemm_ag_chunked(h, w_t, w.n_cols, w.n_cols, c_t, w.n_cols, cfg, stream),
+                             torch, stream, 5)
+            f = 2.0 * T * w.hidden * w.n_cols
+            tot_f += f
+            tot_ms += ms
+            if T >= 4096:
+                big_f += f
+                big_ms += ms
+        res["atomic_gemm" if atomic else "host_loop"] = {
+            "tflops_all": round(tot_f / tot_ms / 1e9, 2),
+            "tflops_T_ge_4096": round(big_f / big_ms / 1e9, 2) if big_ms else None,
+            "pct_peak_T_ge_4096": round(100 * big_f / big_ms / 1e9 / MFMA_PEAK_BF16_TFLOPS, 2) if big_ms else None}
+    res["microbatches"] = len(Ts)
+    out["fc1_ag"] = res
     ub.ub_destroy(h)
     del ub_t, w_t, c_t
 
-    # fc2: row-parallel RS GEMM + reduction over the T sweep
+    # fc2: row-parallel RS GEMM + reduction over the T sweep (pipeline, 4 chunks)
     w = wl.fc2()
     ra, rw, _ = w.seeds()
     log("secondary fc2_rs")
@@ -229,13 +303,18 @@ def secondary(ub, wl, torch, np, dev, log):
     o_t = torch.empty((w.capacity, w.hidden), dtype=torch.int16, device=dev)
     flush = torch.empty(768 * 1024 * 1024 // 2, dtype=torch.int16, device=dev)
     h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes, ws_t, ws_bytes)
-    cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams)
     rows = []
     for T in wl.FC2_TOKENS:
         ub.ub_set_active_shape(h, (T, w.hidden))
-        ms = _time_calls(lambda: ub.ub_gemm_rs_chunked(h, a_t, w.k, w.k, w_t, w.hidden, o_t, w.hidden, cfg, stream),
-                         torch, stream, 5)
         f = 2.0 * T * w.k * w.hidden
+        row = {"T": T}
+        for atomic in (False, True):
+            cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, False, atomic)
+            ms = _time_calls(lambda: ub.ub_gemm_rs_chunked(h, a_t, w.k, w.k, w_t, w.hidden, o_t, w.hidden, cfg, stream),
+                             torch, stream, 5)
+            key = "atomic_gemm" if atomic else "pipeline_3_streams"
+            row[key] = {"tflops": round(f / ms / 1e9, 2), "ms": round(ms, 4),
+                        "pct_peak": round(100 * f / ms / 1e9 / MFMA_PEAK_BF16_TFLOPS, 2)}
         rbytes = (w.tp + 1) * T * w.hidden * 2.0
         warm = _time_calls(lambda: ub.ub_reduce_partials(h, o_t, w.hidden, stream), torch, stream, 10)
         # honest: a 768 MB write between reductions evicts the 256 MB MALL
@@ -249,17 +328,15 @@ def secondary(ub, wl, torch, np, dev, log):
             torch.cuda.synchronize()
             cold.append(e0.elapsed_time(e1))
         cold_ms = sorted(cold)[len(cold) // 2]
-        rows.append({"T": T, "tflops": round(f / ms / 1e9, 2),
-                     "pct_peak": round(100 * f / ms / 1e9 / MFMA_PEAK_BF16_TFLOPS, 2),
-                     "ms": round(ms, 4),
-                     "reduce_gbs_warm": round(rbytes / warm / 1e6, 1),
-                     "reduce_gbs_flushed": round(rbytes / cold_ms / 1e6, 1),
-                     "reduce_pct_hbm_flushed": round(100 * rbytes / cold_ms / 1e6 / HBM_PEAK_GBS, 2)})
+        row.update({"reduce_gbs_warm": round(rbytes / warm / 1e6, 1),
+                    "reduce_gbs_flushed": round(rbytes / cold_ms / 1e6, 1),
+                    "reduce_pct_hbm_flushed": round(100 * rbytes / cold_ms / 1e6 / HBM_PEAK_GBS, 2)})
+        rows.append(row)
     out["fc2_rs"] = rows
     ub.ub_destroy(h)
     del ub_t, ws_t, a_t, w_t, o_t, flush
 
-    # GQA bulk sweep on one capacity-32768 buffer
+    # GQA bulk sweep on one capacity-32768 buffer, never reallocated
     w = wl.gqa_bulk()
     ra, rw, _ = w.seeds()
     log("secondary gqa_bulk_ag")
@@ -268,28 +345,32 @@ def secondary(ub, wl, torch, np, dev, log):
     w_t = torch.from_numpy(wl.weights(w, rw).view(np.int16)).to(dev)
     c_t = torch.empty((w.capacity, w.n_cols), dtype=torch.int16, device=dev)
     h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes)
-    cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams)
-    tot_f = tot_ms = 0.0
-    pts = []
-    for T in wl.gqa_tokens():
-        ub.ub_set_active_shape(h, (T, w.hidden))
-        ms = _time_calls(lambda: ub.ub_gemm_ag_chunked(h, w_t, w.n_cols, w.n_cols, c_t, w.n_cols, cfg, stream),
-                         torch, stream, 3)
-        f = 2.0 * T * w.hidden * w.n_cols
-        if T != 32768:
-            tot_f += f
-            tot_ms += ms
-        pts.append((T, round(f / ms / 1e9, 1)))
-    out["gqa_bulk_ag"] = {"tflops_sweep": round(tot_f / tot_ms / 1e9, 2),
-                          "pct_peak_sweep": round(100 * tot_f / tot_ms / 1e9 / MFMA_PEAK_BF16_TFLOPS, 2),
-                          "points_T_tflops": pts[::4] + [pts[-1]]}
+    res = {}
+    for atomic in (True, False):
+        cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, False, atomic)
+        tot_f = tot_ms = 0.0
+        pts = []
+        for T in wl.gqa_tokens():
+            ub.ub_set_active_shape(h, (T, w.hidden))
+            ms = _time_calls(lambda: ub.ub_gemm_ag_chunked(h, w_t, w.n_cols, w.n_cols, c_t, w.n_cols, cfg, stream),
+                             torch, stream, 3)
+            f = 2.0 * T * w.hidden * w.n_cols
+            if T != 32768:
+                tot_f += f
+                tot_ms += ms
+            pts.append((T, round(f / ms / 1e9, 1)))
+        res["atomic_gemm" if atomic else "host_loop"] = {
+            "tflops_sweep": round(tot_f / tot_ms / 1e9, 2),
+            "pct_peak_sweep": round(100 * tot_f / tot_ms / 1e9 / MFMA_PEAK_BF16_TFLOPS, 2),
+            "points_T_tflops": pts[::4] + [pts[-1]]}
+    out["gqa_bulk_ag"] = res
     ub.ub_destroy(h)
     return out
 
 
-def cpu_baseline(w, Ts, a_host, w_host, budget_s, log):
-    """The oracle as it stands, timed on the host cores over a bounded sample of the
-    same microbatches (whole microbatches, in order, until the time budget is used)."""
+def cpu_baseline(q, min_seconds):
+    """The oracle as it stands, timed on the host cores over the same microbatches (whole
+    microbatches, in order, repeating passes until at least `min_seconds` of work)."""
     import numpy as np
 
     from oracle import gemm as og
@@ -301,28 +382,29 @@ def cpu_baseline(w, Ts, a_host, w_host, budget_s, log):
         threads = sum(i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas")
     except Exception:  # threadpoolctl missing: report the core count
         threads = os.cpu_count()
+    w = q.w
     model = om.UserBufferModel(w.capacity, w.hidden, w.tp)
     cfg = op.OverlapCfg(method=w.method, num_splits=w.num_splits,
-                        num_max_streams=w.num_max_streams, aggregate=w.aggregate)
+                        num_max_streams=w.num_max_streams, aggregate=w.aggregate, atomic_gemm=True)
     c = np.empty((w.capacity, w.n_cols), np.uint16)
-    flops = 0.0
-    elapsed = 0.0
+    flops = elapsed = 0.0
     done = 0
-    for T in Ts:
-        model.set_active_shape((T, w.hidden))
-        model.fill_active(a_host[:T])
-        t0 = time.perf_counter()
-        og.ag_chunked(model, w_host, w.n_cols, w.n_cols, c, w.n_cols, cfg)
-        elapsed += time.perf_counter() - t0
-        flops += 2.0 * T * w.hidden * w.n_cols
-        done += 1
+    while elapsed < min_seconds:
+        for T in q.Ts:
+            model.set_active_shape((T, w.hidden))
+            model.fill_active(q.a_host[:T])
+            t0 = time.perf_counter()
+            og.ag_chunked(model, q.w_host, w.n_cols, w.n_cols, c, w.n_cols, cfg)
+            elapsed += time.perf_counter() - t0
+            flops += 2.0 * T * w.hidden * w.n_cols
+            done += 1
+            if elapsed >= min_seconds and done >= len(q.Ts):
+                break
         log(f"cpu oracle: {done} microbatches, {elapsed:.1f} s")
-        if elapsed >= budget_s:
-            break
     return {"value": round(flops / elapsed / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"first {done} of {len(Ts)} qkv microbatches (T={Ts[:done]}), numpy fp64 "
-                      f"chunked GEMM + bf16 RNE, {elapsed:.1f} s",
+            "sample": f"{done} qkv microbatches ({done / len(q.Ts):.2f} passes over the 32 of one "
+                      f"step), numpy fp64 chunked GEMM + bf16 RNE, {elapsed:.1f} s",
             "host_cpus": os.cpu_count()}
 
 

@@ -69,8 +69,12 @@ struct Params {
   const uint16_t* b;
   uint16_t* c;
   int64_t lda, sa, ldb, sb, ldc, sc;
-  int32_t m, n, k;
-  int32_t tiles_m, tiles_n;  // tile grid of one batch entry
+  int32_t n, k;
+  int32_t tiles_n;                       // tile columns
+  int32_t n_units;                       // row units, in processing order
+  int32_t unit_row0[kMaxGemmUnits];
+  int32_t unit_rows[kMaxGemmUnits];
+  int32_t unit_tile0[kMaxGemmUnits + 1];  // first workgroup of each unit (prefix sums)
 };
 
 template <int BM_, int BN_, int BK_, int S_, int WGM_, int WGN_>
@@ -150,22 +154,29 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   return a | (b << 16);
 }
 
-// Tile coordinates of workgroup `wg` of a batch entry: a contiguous block of tile indices
-// per XCD, walked in groups of G tile-rows so neighbours share B columns.
-__device__ inline void tile_of(int wg, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int total = tiles_m * tiles_n;
+// Tile of workgroup `wg` of a batch entry.  The workgroup index is first remapped so that a
+// contiguous block of tile indices lands on each XCD; the index then selects its row unit
+// (units are laid out in processing order) and, inside the unit, tiles are walked in
+// groups of G tile-rows so neighbours share B columns.  Returns the unit's row range.
+__device__ inline void tile_of(const Params& p, int wg, int bm, int& m0, int& m_end, int& tn) {
+  const int total = p.unit_tile0[p.n_units];
   int t = wg;
   if (total >= NUM_XCD * 2) {
     const int per = total / NUM_XCD;   // full share of each XCD
     const int full = per * NUM_XCD;
     if (wg < full) t = (wg % NUM_XCD) * per + wg / NUM_XCD;
   }
+  int u = 0;
+  while (u + 1 < p.n_units && p.unit_tile0[u + 1] <= t) ++u;
+  const int local = t - p.unit_tile0[u];
+  const int tiles_m = (p.unit_rows[u] + bm - 1) / bm;
   constexpr int G = 4;
-  const int group = t / (G * tiles_n);
+  const int group = local / (G * p.tiles_n);
   const int first_m = group * G;
   const int gm = min(G, tiles_m - first_m);
-  const int r = t - group * G * tiles_n;
-  tm = first_m + r % gm;
+  const int r = local - group * G * p.tiles_n;
+  m0 = p.unit_row0[u] + (first_m + r % gm) * bm;
+  m_end = p.unit_row0[u] + p.unit_rows[u];
   tn = r / gm;
 }
 
@@ -173,7 +184,7 @@ __device__ inline void tile_of(int wg, int tiles_m, int tiles_n, int& tm, int& t
 // per-lane offsets of the direct loads and of the fragment reads.
 template <class C>
 struct Tile {
-  int lane, wave, wm, wn, m0, n0;
+  int lane, wave, wm, wn, m0, m_end, n0;
   uint16_t* cg;
   i32x4 ra, rb;
   uint32_t a_off[C::NA], b_off[C::NB];
@@ -185,15 +196,14 @@ struct Tile {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     wm = wave / C::WGN;
     wn = wave % C::WGN;
-    int tm, tn;
-    tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
-    m0 = tm * C::BM;
+    int tn;
+    tile_of(p, blockIdx.x, C::BM, m0, m_end, tn);
     n0 = tn * C::BN;
     const uint16_t* A = p.a + blockIdx.z * p.sa + (int64_t)m0 * p.lda;
     const uint16_t* B = p.b + blockIdx.z * p.sb + n0;
     cg = p.c + blockIdx.z * p.sc;
     // A from this tile's first row, valid rows only; B from column n0 of the batch entry
-    const int rows_valid = min(C::BM, p.m - m0);
+    const int rows_valid = min(C::BM, m_end - m0);
     ra = make_rsrc(A, (uint32_t)(rows_valid * p.lda * 2));
     rb = make_rsrc(B, (uint32_t)(((int64_t)p.k * p.ldb - n0) * 2));
     // Direct load t of this wave: A rows A_ROWS_PER_LOAD*(wave*NA + t) + lane/A_CPR, slot
@@ -287,7 +297,7 @@ struct Tile {
       const int v = tid + i * C::THREADS;
       const int r = v / VPR, cc = (v % VPR) * 8;
       const int gr = m0 + r, gc = n0 + cc;
-      if (gr < p.m && gc < p.n)
+      if (gr < m_end && gc < p.n)
         *GLOBAL_PTR(u32x4, cg + (int64_t)gr * p.ldc + gc) =
             *LDS_PTR(const u32x4, ct + r * C::LDC + cc);
     }
@@ -420,12 +430,30 @@ void gemm_bf16_pipelined(Params p) {
 }
 
 template <class C, class K>
-hipError_t launch(K kernel, const GemmArgs& g, hipStream_t stream) {
-  Params p{g.a, g.b, g.c, g.lda, g.a_batch_stride, g.ldb, g.b_batch_stride,
-           g.ldc, g.c_batch_stride, g.m, g.n, g.k, 0, 0};
-  p.tiles_m = (g.m + C::BM - 1) / C::BM;
+hipError_t launch(K kernel, const GemmArgs& g, const GemmUnits& u, hipStream_t stream) {
+  Params p{};
+  p.a = g.a;
+  p.b = g.b;
+  p.c = g.c;
+  p.lda = g.lda;
+  p.sa = g.a_batch_stride;
+  p.ldb = g.ldb;
+  p.sb = g.b_batch_stride;
+  p.ldc = g.ldc;
+  p.sc = g.c_batch_stride;
+  p.n = g.n;
+  p.k = g.k;
   p.tiles_n = (g.n + C::BN - 1) / C::BN;
-  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+  p.n_units = u.n;
+  int64_t tiles = 0;
+  for (int i = 0; i < u.n; ++i) {
+    p.unit_row0[i] = u.row0[i];
+    p.unit_rows[i] = u.rows[i];
+    p.unit_tile0[i] = (int32_t)tiles;
+    tiles += (int64_t)((u.rows[i] + C::BM - 1) / C::BM) * p.tiles_n;
+  }
+  p.unit_tile0[u.n] = (int32_t)tiles;
+  if (tiles == 0) return hipSuccess;
   if (tiles > 0x7FFFFFFF || g.batch > 65535) return hipErrorInvalidValue;
   static bool configured = false;
   if (!configured) {
@@ -446,9 +474,13 @@ constexpr int PP_D = 3;
 
 enum TileKind { kTile128x128 = 0, kTile256x128 = 1, kTile256x256 = 3 };
 
-// Tile choice.  Larger tiles halve the L2 -> LDS traffic per FLOP, which bounds this
-// kernel; smaller ones give more workgroups when a launch is small.
-int choose_tile(const GemmArgs& g) {
+// Tile choice by a small cost model: a launch of `tiles` workgroups on the CUs left to it
+// (256 / concurrency, times the workgroups one CU holds) runs ceil(tiles / slots) rounds,
+// each as long as one tile takes at the tile's per-CU efficiency.  Efficiencies are the
+// measured per-CU throughputs relative to the 256x256 ping-pong on 8192^3 bf16 (the
+// 256x128 ping-pong reads more bytes per FLOP; the 128x128 kernel runs two workgroups per
+// CU that share its MFMA pipes).
+int choose_tile(const GemmArgs& g, const GemmUnits& u) {
   static int forced = [] {
     const char* s = std::getenv("UBX_GEMM_TILE");  // tuning override
     if (!s) return -1;
@@ -458,12 +490,26 @@ int choose_tile(const GemmArgs& g) {
     return -1;
   }();
   if (forced >= 0) return forced;
-  auto count = [&](int bm, int bn) {
-    return (int64_t)((g.m + bm - 1) / bm) * ((g.n + bn - 1) / bn) * g.batch;
-  };
-  if (count(256, 256) >= 256) return kTile256x256;
-  if (count(256, 128) >= 192) return kTile256x128;
-  return kTile128x128;
+  struct Opt { int kind, bm, bn, per_cu; double eff; };
+  static const Opt opts[] = {{kTile256x256, 256, 256, 1, 1.00},
+                             {kTile256x128, 256, 128, 1, 0.71},
+                             {kTile128x128, 128, 128, 2, 0.75}};
+  const int share = 256 / (g.concurrency > 1 ? g.concurrency : 1);
+  int best = kTile128x128;
+  double best_cost = 1e300;
+  for (const Opt& o : opts) {
+    int64_t rows = 0;
+    for (int i = 0; i < u.n; ++i) rows += (u.rows[i] + o.bm - 1) / o.bm;
+    const int64_t tiles = rows * ((g.n + o.bn - 1) / o.bn) * g.batch;
+    const int64_t slots = (int64_t)(share > 0 ? share : 1) * o.per_cu;
+    const double rounds = (double)((tiles + slots - 1) / slots);
+    const double cost = rounds * o.bm * o.bn / (o.eff / o.per_cu);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = o.kind;
+    }
+  }
+  return best;
 }
 
 }  // namespace
@@ -474,18 +520,30 @@ bool gemm_shape_supported(const GemmArgs& g) {
   return (int64_t)g.k * g.ldb * 2 < (int64_t)OOB && (int64_t)256 * g.lda * 2 < (int64_t)OOB;
 }
 
-hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream) {
-  if (g.m <= 0 || g.n <= 0 || g.batch <= 0) return hipSuccess;
-  if (g.k <= 0 || g.k % kGemmKStep != 0 || g.n % 8 != 0 || !gemm_shape_supported(g))
+hipError_t launch_gemm_bf16_units(const GemmArgs& g, const GemmUnits& u, hipStream_t stream) {
+  if (g.n <= 0 || g.batch <= 0 || u.n <= 0) return hipSuccess;
+  if (u.n > kMaxGemmUnits || g.k <= 0 || g.k % kGemmKStep != 0 || g.n % 8 != 0 ||
+      !gemm_shape_supported(g))
     return hipErrorInvalidValue;
-  switch (choose_tile(g)) {
+  for (int i = 0; i < u.n; ++i)
+    if (u.rows[i] < 0 || u.row0[i] < 0) return hipErrorInvalidValue;
+  switch (choose_tile(g, u)) {
     case kTile256x256:
-      return launch<PP256x256>(&gemm_bf16_pingpong<PP256x256, PP_D>, g, stream);
+      return launch<PP256x256>(&gemm_bf16_pingpong<PP256x256, PP_D>, g, u, stream);
     case kTile256x128:
-      return launch<PP256x128>(&gemm_bf16_pingpong<PP256x128, PP_D>, g, stream);
+      return launch<PP256x128>(&gemm_bf16_pingpong<PP256x128, PP_D>, g, u, stream);
     default:
-      return launch<PL128x128>(&gemm_bf16_pipelined<PL128x128>, g, stream);
+      return launch<PL128x128>(&gemm_bf16_pipelined<PL128x128>, g, u, stream);
   }
+}
+
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream) {
+  if (g.m <= 0) return hipSuccess;
+  GemmUnits u;
+  u.n = 1;
+  u.row0[0] = 0;
+  u.rows[0] = g.m;
+  return launch_gemm_bf16_units(g, u, stream);
 }
 
 }  // namespace ubx

@@ -210,8 +210,22 @@ ub_status_t join_streams(ub_ctx* h, hipStream_t caller, int S) {
 
 ub_status_t check_cfg_common(ub_ctx* h, const ub_overlap_cfg_t* cfg) {
   if (!cfg) return fail(h, UB_ERR_INVALID_ARG, "cfg is NULL");
-  if (cfg->atomic_gemm)
-    return fail(h, UB_ERR_UNSUPPORTED, "atomic_gemm (device-side chunk loop) is not built");
+  return UB_OK;
+}
+
+// Units of the plan, in execution order, for a device-side chunk loop.
+ub_status_t plan_units(ub_ctx* h, ubx::GemmUnits* u) {
+  u->n = 0;
+  for (const ub_plan_unit_t& pu : h->plan.units) {
+    const int64_t rows = pu.row1 - pu.row0;
+    if (rows <= 0) continue;
+    if (u->n == ubx::kMaxGemmUnits)
+      return fail(h, UB_ERR_UNSUPPORTED, "atomic_gemm supports at most %d non-empty units",
+                  ubx::kMaxGemmUnits);
+    u->row0[u->n] = static_cast<int32_t>(pu.row0);
+    u->rows[u->n] = static_cast<int32_t>(rows);
+    ++u->n;
+  }
   return UB_OK;
 }
 
@@ -393,12 +407,35 @@ UB_API ub_status_t ub_gemm_ag_chunked(ub_handle_t h, const void* w, int64_t n_co
                 (long long)h->hidden, ubx::kGemmKStep);
   st = ubx::build_plan(h->T, h->tp, *cfg, UB_OP_AG, &h->plan, &h->last_error);
   if (st != UB_OK) return st;
+  const int64_t H = h->hidden;
+  hipStream_t caller = static_cast<hipStream_t>(stream);
+
+  if (cfg->atomic_gemm) {
+    // One launch walks every unit in plan order on the caller's stream.
+    ubx::GemmUnits units;
+    if ((st = plan_units(h, &units)) != UB_OK) return st;
+    if ((st = ensure_device(h, 1)) != UB_OK) return st;
+    ubx::GemmArgs g{};
+    g.a = h->ub;
+    g.lda = H;
+    g.b = static_cast<const uint16_t*>(w);
+    g.ldb = ldw;
+    g.c = static_cast<uint16_t*>(c);
+    g.ldc = ldc;
+    g.n = static_cast<int32_t>(n_cols);
+    g.k = static_cast<int32_t>(H);
+    g.batch = 1;
+    g.concurrency = 1;
+    const double flops = 2.0 * h->T * H * n_cols;
+    const double bytes = 2.0 * (h->T * H + H * n_cols + h->T * n_cols);
+    return timed_launch(h, caller, 0, flops, bytes,
+                        [&] { return ubx::launch_gemm_bf16_units(g, units, caller); },
+                        "GEMM launch");
+  }
+
   const int S = h->plan.n_streams;
   if ((st = ensure_device(h, S)) != UB_OK) return st;
-
-  hipStream_t caller = static_cast<hipStream_t>(stream);
   if ((st = fork_streams(h, caller, S)) != UB_OK) return st;
-  const int64_t H = h->hidden;
   for (const ub_plan_unit_t& u : h->plan.units) {
     const int64_t rows = u.row1 - u.row0;
     if (rows <= 0) continue;
@@ -415,6 +452,7 @@ UB_API ub_status_t ub_gemm_ag_chunked(ub_handle_t h, const void* w, int64_t n_co
     g.n = static_cast<int32_t>(n_cols);
     g.k = static_cast<int32_t>(H);
     g.batch = 1;
+    g.concurrency = S;
     const double flops = 2.0 * rows * H * n_cols;
     const double bytes = 2.0 * (rows * H + H * n_cols + rows * n_cols);
     st = timed_launch(h, s, 0, flops, bytes, [&] { return ubx::launch_gemm_bf16(g, s); },
@@ -447,13 +485,50 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
   if ((st = check_ld(h, "ldo", ldo, H)) != UB_OK) return st;
   st = ubx::build_plan(h->T, h->tp, *cfg, UB_OP_RS, &h->plan, &h->last_error);
   if (st != UB_OK) return st;
-  const int S = h->plan.n_streams;
-  if ((st = ensure_device(h, S)) != UB_OK) return st;
-
-  hipStream_t caller = static_cast<hipStream_t>(stream);
-  if ((st = fork_streams(h, caller, S)) != UB_OK) return st;
   const int64_t T = h->T;
   const int32_t tp = h->tp;
+  hipStream_t caller = static_cast<hipStream_t>(stream);
+
+  if (cfg->atomic_gemm) {
+    // One launch computes every unit's tp slice partials in plan order, then one
+    // reduction sums the whole active prefix.
+    ubx::GemmUnits units;
+    if ((st = plan_units(h, &units)) != UB_OK) return st;
+    if ((st = ensure_device(h, 1)) != UB_OK) return st;
+    ubx::GemmArgs g{};
+    g.a = static_cast<const uint16_t*>(a);
+    g.lda = lda;
+    g.a_batch_stride = ks;
+    g.b = static_cast<const uint16_t*>(w);
+    g.ldb = ldw;
+    g.b_batch_stride = ks * ldw;
+    g.c = h->ws;
+    g.ldc = H;
+    g.c_batch_stride = T * H;
+    g.n = static_cast<int32_t>(H);
+    g.k = static_cast<int32_t>(ks);
+    g.batch = tp;
+    g.concurrency = 1;
+    st = timed_launch(h, caller, 0, 2.0 * T * k * H, 2.0 * (T * k + k * H + tp * T * H),
+                      [&] { return ubx::launch_gemm_bf16_units(g, units, caller); },
+                      "slice GEMM launch");
+    if (st != UB_OK) return st;
+    ubx::ReduceArgs r{};
+    r.parts = h->ws;
+    r.slot_stride = T * H;
+    r.ldp = H;
+    r.nslots = tp;
+    r.out = static_cast<uint16_t*>(out);
+    r.ldo = ldo;
+    r.rows = T;
+    r.cols = H;
+    return timed_launch(h, caller, 1, double(tp - 1) * T * H, 2.0 * (tp + 1) * T * H,
+                        [&] { return ubx::launch_reduce_partials(r, caller); }, "reduce launch");
+  }
+
+  const int S = h->plan.n_streams;
+  if ((st = ensure_device(h, S)) != UB_OK) return st;
+  if ((st = fork_streams(h, caller, S)) != UB_OK) return st;
   for (const ub_plan_unit_t& u : h->plan.units) {
     const int64_t rows = u.row1 - u.row0;
     if (rows <= 0) continue;
@@ -475,6 +550,7 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
     g.n = static_cast<int32_t>(H);
     g.k = static_cast<int32_t>(ks);
     g.batch = tp;
+    g.concurrency = S;
     const double flops = 2.0 * rows * k * H;
     const double gbytes = 2.0 * (rows * k + k * H + tp * rows * H);
     st = timed_launch(h, s, 0, flops, gbytes, [&] { return ubx::launch_gemm_bf16(g, s); },

@@ -38,9 +38,21 @@ struct GemmArgs {
   int64_t ldc;
   int64_t c_batch_stride;
   int32_t m, n, k, batch;
+  int32_t concurrency;  // launches expected to share the GPU with this one (>= 1)
 };
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream);
 constexpr int kGemmKStep = 64;  // k must be a multiple of this
+
+// Row units of a device-side chunk loop: one launch whose workgroups cover every unit's
+// tiles, units in the given order, no tile spanning two units.  Unit u covers rows
+// [row0[u], row0[u] + rows[u]) of A and C (g.m is ignored).
+constexpr int kMaxGemmUnits = 64;
+struct GemmUnits {
+  int32_t n;
+  int32_t row0[kMaxGemmUnits];
+  int32_t rows[kMaxGemmUnits];
+};
+hipError_t launch_gemm_bf16_units(const GemmArgs& g, const GemmUnits& u, hipStream_t stream);
 
 // out[r, c] = bf16( sum_{s < nslots} float(parts[s*slot_stride + r*ldp + c]) ), ascending s.
 // cols % 8 == 0, ldp/ldo % 8 == 0, pointers 16-byte aligned.

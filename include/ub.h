@@ -112,8 +112,11 @@ typedef enum { UB_OP_AG = 0, UB_OP_RS = 1 } ub_op_t;
  *   num_max_streams  compute streams = min(chunks, num_max_streams, UB_MAX_STREAMS), >= 1.
  *                    Default 3.
  *   aggregate        all-gather side only: chunks {2u, 2u+1} are merged into one launch.
- *   atomic_gemm      0: one kernel launch per chunk from a host loop; 1: one kernel that
- *                    walks the chunks on the device.  Results are identical.
+ *   atomic_gemm      0: one kernel launch per unit from a host loop on the compute
+ *                    streams; 1: one kernel on the caller's stream whose workgroups walk
+ *                    the units on the device in plan order (no tile spans two units; at
+ *                    most 64 non-empty units, else UB_ERR_UNSUPPORTED).  Results are
+ *                    bit-identical ([TE#1344] "atomic_gemm").
  *   rank             this rank in [0, tp_size): sets the ring order.
  *   use_ce, num_sm, set_sm_margin  accepted for compatibility and ignored: on one GPU
  *                    there is no send/recv to place on a copy engine and no

@@ -192,3 +192,14 @@ def test_hidden_not_multiple_of_kstep_is_unsupported():
         assert ub.STATUS[st] == "UB_ERR_UNSUPPORTED"
     finally:
         ub.ub_destroy(h)
+
+
+def test_atomic_gemm_unit_limit_checked_before_any_hip_call():
+    h = _handle(1024, 256, 1)
+    try:
+        cfg = ub.make_cfg("bulk", 65, atomic_gemm=True)
+        st = ub.raw_call("ub_gemm_ag_chunked", h, FAKE, 256, 256, FAKE, 256, ctypes.byref(cfg), None)
+        assert ub.STATUS[st] == "UB_ERR_UNSUPPORTED"
+        assert "64" in ub.ub_last_error(h)
+    finally:
+        ub.ub_destroy(h)

@@ -88,10 +88,11 @@ def test_integer_inputs_bit_exact(ub, cap, H, N, T, tp, method, ns):
     try:
         reg.set_T(T)
         reg.fill(a)
-        c = _run(ub, reg, gu.dev(wt), N, ub.make_cfg(method, ns))
         ref = _oracle_ag(cap, H, tp, a, wt, _ocfg(method, ns))
-        assert np.array_equal(c[:T], ref)
-        assert np.all(c[T:] == gu.CANARY)
+        for atomic in (False, True):
+            c = _run(ub, reg, gu.dev(wt), N, ub.make_cfg(method, ns, atomic_gemm=atomic))
+            assert np.array_equal(c[:T], ref), atomic
+            assert np.all(c[T:] == gu.CANARY)
         assert np.all(gu.host(reg.ub_t)[(cap) * H:] == gu.CANARY)
     finally:
         reg.close()
@@ -140,9 +141,10 @@ def test_bit_identical_across_schedules_capacity_and_offset(ub):
                 for nms in (1, 2, 3, 8):
                     for agg in (False, True):
                         for rank in (0, 5):
-                            cfg = ub.make_cfg(method, ns, nms, agg, rank=rank)
-                            got = _run(ub, reg, wt, N, cfg)[:T]
-                            assert np.array_equal(got, ref), (method, ns, nms, agg, rank)
+                            for atomic in (False, True):
+                                cfg = ub.make_cfg(method, ns, nms, agg, atomic, rank=rank)
+                                got = _run(ub, reg, wt, N, cfg)[:T]
+                                assert np.array_equal(got, ref), (method, ns, nms, agg, rank, atomic)
     finally:
         reg.close()
     # another capacity, and the UB registered at a 4 KiB + 16 B offset inside a larger tensor
@@ -233,20 +235,20 @@ def _sample_rows(rng, T, n_chunks, extra=40):
     return np.array(sorted(rows))
 
 
-def _full_size_ag(ub, w, Ts, label):
+def _full_size_ag(ub, w, Ts, label, atomic=False):
     ra, rw, _ = w.seeds()
     a_all = wl.activations(w, w.capacity, ra)
     wt = wl.weights(w, rw)
     w_t = gu.dev(wt)
     reg = gu.Registration(ub, w.capacity, w.hidden, w.tp, workspace=False, pad_rows=8)
     rng = np.random.default_rng(99)
-    cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, w.aggregate)
+    cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, w.aggregate, atomic)
     n_chunks = w.tp if w.method == "ring_exchange" else w.num_splits
     try:
         reg.fill(a_all)  # one fill of the whole capacity; each T uses its prefix
         c = gu.canary((w.capacity + 8, w.n_cols))
         for T in Ts:
-            print(f"[{label}] T={T}", flush=True)
+            print(f"[{label}] T={T} atomic={atomic}", flush=True)
             reg.set_T(T)
             c.fill_(gu.CANARY)
             ub.ub_gemm_ag_chunked(reg.h, w_t, w.n_cols, w.n_cols, c, w.n_cols, cfg)
@@ -260,16 +262,18 @@ def _full_size_ag(ub, w, Ts, label):
         reg.close()
 
 
-def test_qkv_full_size_sampled(ub):
+@pytest.mark.parametrize("atomic", [False, True])
+def test_qkv_full_size_sampled(ub, atomic):
     w = wl.qkv()
     Ts = wl.tokens_for(w)
-    _full_size_ag(ub, w, Ts[:4] + [min(Ts), max(Ts)], "qkv")
+    _full_size_ag(ub, w, Ts[:4] + [min(Ts), max(Ts)], "qkv", atomic)
 
 
-def test_fc1_full_size_sampled(ub):
+@pytest.mark.parametrize("atomic", [False, True])
+def test_fc1_full_size_sampled(ub, atomic):
     w = wl.fc1()
     Ts = wl.tokens_for(w)
-    _full_size_ag(ub, w, [Ts[0], min(Ts), max(Ts), w.capacity], "fc1")
+    _full_size_ag(ub, w, [Ts[0], min(Ts), max(Ts), w.capacity], "fc1", atomic)
 
 
 def test_gqa_bulk_sweep_sampled(ub):
@@ -279,6 +283,7 @@ def test_gqa_bulk_sweep_sampled(ub):
     Ts = wl.gqa_tokens(include_capacity=False)
     subset = sorted(set(Ts[::4]) | {Ts[0], Ts[-1], 32768})
     _full_size_ag(ub, w, subset, "gqa_bulk")
+    _full_size_ag(ub, w, [Ts[0], Ts[13], 32768], "gqa_bulk", atomic=True)
 
 
 def test_kernel_timing_counts_launches(ub):

@@ -80,13 +80,15 @@ def test_integer_inputs_bit_exact(ub, cap, H, K, T, tp, method, ns):
     reg = gu.Registration(ub, cap, H, tp, pad_rows=8)
     try:
         reg.set_T(T)
-        out = _run_rs(ub, reg, gu.dev(a), K, gu.dev(wt), ub.make_cfg(method, ns))
         ref, parts = _oracle_rs(cap, H, tp, a, wt, op.OverlapCfg(method=method, num_splits=ns))
-        assert np.array_equal(out[:T], ref)
-        ws = gu.host(reg.ws_t)
-        assert np.array_equal(ws[: tp * T * H].reshape(tp, T, H), parts)
-        assert np.all(ws[tp * T * H:] == gu.CANARY)
-        assert np.all(out[T:] == gu.CANARY)
+        for atomic in (False, True):
+            reg.ws_t.fill_(gu.CANARY)
+            out = _run_rs(ub, reg, gu.dev(a), K, gu.dev(wt), ub.make_cfg(method, ns, atomic_gemm=atomic))
+            assert np.array_equal(out[:T], ref), atomic
+            ws = gu.host(reg.ws_t)
+            assert np.array_equal(ws[: tp * T * H].reshape(tp, T, H), parts)
+            assert np.all(ws[tp * T * H:] == gu.CANARY)
+            assert np.all(out[T:] == gu.CANARY)
     finally:
         reg.close()
 
@@ -120,9 +122,11 @@ def test_bit_identical_across_schedules(ub):
             for ns in (1, 2, 3, 4, 7):
                 for nms in (1, 2, 3):
                     for rank in (0, 3):
-                        got = _run_rs(ub, reg, a, K, wt, ub.make_cfg(method, ns, nms, rank=rank))[:T]
-                        assert np.array_equal(got, ref), (method, ns, nms, rank)
-                        assert np.array_equal(gu.host(reg.ws_t)[: tp * T * H], ref_ws)
+                        for atomic in (False, True):
+                            cfg = ub.make_cfg(method, ns, nms, atomic_gemm=atomic, rank=rank)
+                            got = _run_rs(ub, reg, a, K, wt, cfg)[:T]
+                            assert np.array_equal(got, ref), (method, ns, nms, rank, atomic)
+                            assert np.array_equal(gu.host(reg.ws_t)[: tp * T * H], ref_ws)
     finally:
         reg.close()
 
