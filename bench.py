@@ -35,14 +35,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 def parse_args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU-oracle baseline work (seconds)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--profile-pass", action="store_true",
-                   help="run the primary workload briefly plus a 1 GiB copy, print nothing else")
+                   help="run only the primary timed region and its per-launch timing pass, then "
+                        "a 1 GiB copy (calibration of rocprofv3 byte counters)")
     return p.parse_args()
 
 
@@ -135,18 +136,6 @@ def main():
     q = Qkv(ub, wl, torch, np, dev)
     primary = q.cfg(atomic=True)
 
-    if args.profile_pass:
-        # primary workload, then a plain copy of 1 GiB (2^29 int16 -> 2^29 int16) used to
-        # calibrate FETCH_SIZE / WRITE_SIZE
-        q.timed(primary, steps=2, warmup=1)
-        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log("profile pass done")
-        ub.ub_destroy(q.h)
-        return
-
     log(f"warmup {args.warmup}, timed {args.steps} steps of {len(q.Ts)} microbatches (atomic_gemm)")
     sec = q.timed(primary, args.steps, args.warmup)
     tflops = q.flops / sec / 1e12
@@ -159,6 +148,24 @@ def main():
     gemm_stats, _ = ub.ub_get_kernel_timing(q.h)
     ub.ub_set_kernel_timing(q.h, False)
     g_ach = gemm_stats["flops"] / (gemm_stats["total_ms"] / 1e3) / 1e12
+    avg_launch_us = gemm_stats["total_ms"] * 1e3 / max(1, gemm_stats["launches"])
+
+    if args.profile_pass:
+        # a plain copy of 1 GiB (2^29 int16 -> 2^29 int16) that calibrates FETCH_SIZE / WRITE_SIZE
+        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        ub.ub_destroy(q.h)
+        print(json.dumps({"profile_pass": True, "ms_per_step": round(sec * 1e3, 4),
+                          "launches_per_step": len(q.Ts),
+                          "gemm_launches": (args.warmup + 2 * args.steps) * len(q.Ts),
+                          "warmup_launches": args.warmup * len(q.Ts),
+                          "avg_launch_us_hip_events": round(avg_launch_us, 3),
+                          "avg_launch_gflop": round(gemm_stats["flops"] / max(1, gemm_stats["launches"]) / 1e9, 4),
+                          "algorithmic_bytes_per_launch": round(gemm_stats["bytes"] / max(1, gemm_stats["launches"])),
+                          "gemm_src_hash": src_hash(GEMM_SRC)}), flush=True)
+        return
 
     per_mb = q.per_microbatch(primary)
     big = [(T, ms) for T, ms in per_mb if T >= 4096]
@@ -186,7 +193,7 @@ def main():
         "achieved": round(g_ach, 2), "peak": MFMA_PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
         "frac": round(g_ach / MFMA_PEAK_BF16_TFLOPS, 4), "traffic": traffic,
         "launches": gemm_stats["launches"],
-        "avg_launch_us": round(gemm_stats["total_ms"] * 1e3 / max(1, gemm_stats["launches"]), 3),
+        "avg_launch_us": round(avg_launch_us, 3),
         "avg_launch_gflop": round(gemm_stats["flops"] / max(1, gemm_stats["launches"]) / 1e9, 4),
         "algorithmic_bytes_per_launch": round(gemm_stats["bytes"] / max(1, gemm_stats["launches"])),
         "measured_pass_ms_per_step": round(sec_i * 1e3, 4),

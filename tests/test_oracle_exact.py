@@ -85,6 +85,17 @@ def test_integer_inputs_exact_at_larger_shape():
     assert np.any(vals > 256)  # rounding really happens in this set
 
 
+def test_square_integer_gemm_exact():
+    """A square weight (N = H): a transposed operand keeps every shape valid, so only the
+    values can show it.  Integer inputs, exact result."""
+    rng = np.random.default_rng(15)
+    T, H = 40, 96
+    a = wl.integer_bits(rng, (T, H))
+    wt = wl.integer_bits(rng, (H, H))
+    c, _, _ = _run_ag(64, H, 4, T, a, wt, plan.OverlapCfg(method="ring_exchange"))
+    assert np.array_equal(c[:T], exact.int_valued_gemm_rne(a, wt))
+
+
 def test_integer_inputs_rs_exact():
     rng = np.random.default_rng(6)
     T, H, K, tp = 32, 32, 4096, 4
