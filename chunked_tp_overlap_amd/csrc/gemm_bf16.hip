@@ -95,17 +95,31 @@ struct Cfg {
   static constexpr int B_CPR = BN / 8;
   static constexpr int B_BYTES = BK * B_ROW;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int NA = A_BYTES / 1024 / NW;    // 1 KB direct loads per wave per step, A
-  static constexpr int NB = B_BYTES / 1024 / NW;    // and B
-  static constexpr int L = NA + NB;                 // loads per wave per step
+  static constexpr int NA_ALL = A_BYTES / 1024;     // 1 KB direct loads per step, A
+  static constexpr int NB_ALL = B_BYTES / 1024;     // and B
+  // Loads per wave of group 0 (waves 0-3) and of group 1 (waves 4-7).  When both operands
+  // split evenly over all waves every wave takes its share of each; otherwise (a 192-row
+  // A tile: 12 loads) group 0 takes all of B and group 1 all of A.
+  static constexpr bool EVEN = NA_ALL % NW == 0 && NB_ALL % NW == 0;
+  static constexpr int NA0 = EVEN ? NA_ALL / NW : 0;
+  static constexpr int NB0 = EVEN ? NB_ALL / NW : NB_ALL / 4;
+  static constexpr int NA1 = EVEN ? NA_ALL / NW : NA_ALL / 4;
+  static constexpr int NB1 = EVEN ? NB_ALL / NW : 0;
+  static constexpr int L0 = NA0 + NB0;              // loads per wave per step, group 0
+  static constexpr int L1 = NA1 + NB1;              // and group 1
+  static constexpr int NA_MAX = NA0 > NA1 ? NA0 : NA1;
+  static constexpr int NB_MAX = NB0 > NB1 ? NB0 : NB1;
   static constexpr int A_ROWS_PER_LOAD = 1024 / A_ROW;
   static constexpr int B_ROWS_PER_LOAD = 1024 / B_ROW;
   static constexpr int LDC = BN + 8;                // epilogue tile row (elements)
   static constexpr int EPI = BM * LDC * 2;
   static constexpr int LDS_BYTES = (S * STAGE > EPI) ? S * STAGE : EPI;
-  static_assert(NA >= 1 && NB >= 1, "tile too small for the load split");
+  static_assert(EVEN ? (NA0 >= 1 && NB0 >= 1)
+                     : (NW == 8 && NA_ALL % 4 == 0 && NB_ALL % 4 == 0 && NA1 >= 1 && NB0 >= 1),
+                "direct loads do not split over the waves");
   static_assert(FM >= 1 && FN >= 1, "wave tile below one 32x32 block");
-  static_assert(S * L <= 63, "vmcnt is a 6-bit count");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile of whole 32x32 blocks");
+  static_assert(S * L0 <= 63 && S * L1 <= 63, "vmcnt is a 6-bit count");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS is 160 KiB per CU");
 };
 
@@ -184,16 +198,18 @@ __device__ inline void tile_of(const Params& p, int wg, int bm, int& m0, int& m_
 // per-lane offsets of the direct loads and of the fragment reads.
 template <class C>
 struct Tile {
-  int lane, wave, wm, wn, m0, m_end, n0;
+  int lane, wave, group, wm, wn, m0, m_end, n0;
   uint16_t* cg;
   i32x4 ra, rb;
-  uint32_t a_off[C::NA], b_off[C::NB];
+  uint32_t a_off[C::NA_MAX > 0 ? C::NA_MAX : 1], b_off[C::NB_MAX > 0 ? C::NB_MAX : 1];
+  uint32_t a_lds, b_lds;                 // LDS byte offset of this wave's first A / B load
   uint32_t a_kstep, b_kstep;
   int a_rd_row, a_rd_c, a_rd_x, b_krow, b_col_chunk, b_x, b_in;
 
   __device__ inline void init(const Params& p, int tid) {
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    group = wave >> 2;
     wm = wave / C::WGN;
     wn = wave % C::WGN;
     int tn;
@@ -206,20 +222,29 @@ struct Tile {
     const int rows_valid = min(C::BM, m_end - m0);
     ra = make_rsrc(A, (uint32_t)(rows_valid * p.lda * 2));
     rb = make_rsrc(B, (uint32_t)(((int64_t)p.k * p.ldb - n0) * 2));
-    // Direct load t of this wave: A rows A_ROWS_PER_LOAD*(wave*NA + t) + lane/A_CPR, slot
-    // lane%A_CPR holding k-chunk slot ^ a_swz(row); B k-rows B_ROWS_PER_LOAD*(wave*NB + t) +
-    // lane/B_CPR, slot lane%B_CPR holding column chunk slot ^ b_swz(krow).
+    // Direct loads of this wave: A loads ia0 .. ia0+na-1 and B loads ib0 .. ib0+nb-1 of the
+    // step.  A load i covers rows A_ROWS_PER_LOAD*i + lane/A_CPR, slot lane%A_CPR holding
+    // k-chunk slot ^ a_swz(row); B load i covers k-rows B_ROWS_PER_LOAD*i + lane/B_CPR, slot
+    // lane%B_CPR holding column chunk slot ^ b_swz(krow).  Load i of an operand lands at
+    // byte 1024*i of that operand's part of the stage.
+    const int w4 = wave - 4 * group;
+    const int na = group == 0 ? C::NA0 : C::NA1;
+    const int nb = group == 0 ? C::NB0 : C::NB1;
+    const int ia0 = group == 0 ? wave * C::NA0 : 4 * C::NA0 + w4 * C::NA1;
+    const int ib0 = group == 0 ? wave * C::NB0 : 4 * C::NB0 + w4 * C::NB1;
+    a_lds = (uint32_t)ia0 * 1024;
+    b_lds = (uint32_t)(C::A_BYTES + ib0 * 1024);
 #pragma unroll
-    for (int t = 0; t < C::NA; ++t) {
-      const int row = C::A_ROWS_PER_LOAD * (wave * C::NA + t) + lane / C::A_CPR;
+    for (int t = 0; t < C::NA_MAX; ++t) {
+      const int row = C::A_ROWS_PER_LOAD * (ia0 + t) + lane / C::A_CPR;
       const int chunk = (lane % C::A_CPR) ^ a_swz<C::A_CPR>(row);
-      a_off[t] = (uint32_t)((row * p.lda + chunk * 8) * 2);
+      a_off[t] = t < na ? (uint32_t)((row * p.lda + chunk * 8) * 2) : OOB;
     }
 #pragma unroll
-    for (int t = 0; t < C::NB; ++t) {
-      const int krow = C::B_ROWS_PER_LOAD * (wave * C::NB + t) + lane / C::B_CPR;
+    for (int t = 0; t < C::NB_MAX; ++t) {
+      const int krow = C::B_ROWS_PER_LOAD * (ib0 + t) + lane / C::B_CPR;
       const int chunk = (lane % C::B_CPR) ^ b_swz(krow);
-      const bool ok = n0 + chunk * 8 < p.n;
+      const bool ok = t < nb && n0 + chunk * 8 < p.n;
       b_off[t] = ok ? (uint32_t)((krow * p.ldb + chunk * 8) * 2) : OOB;
     }
     a_kstep = C::BK * 2;
@@ -236,21 +261,28 @@ struct Tile {
     b_in = (lane & 1) * 8;
   }
 
-  // This wave's direct loads of step ks into stage ks % S.  Steps past the end are issued
-  // with out-of-range offsets (they write zeros and touch no memory) so that every wait
-  // can count a fixed number of newer loads.
-  __device__ inline void issue_loads(unsigned char* smem, int ks, int nk) const {
-    unsigned char* sa = smem + (ks % C::S) * C::STAGE;
-    unsigned char* sb = sa + C::A_BYTES;
+  // This wave's direct loads of step ks into stage ks % S: NA_ A loads and NB_ B loads
+  // (its group's counts).  Steps past the end are issued with out-of-range offsets (they
+  // write zeros and touch no memory) so that every wait can count a fixed number of newer
+  // loads; so are B chunks past column n.
+  template <int NA_, int NB_>
+  __device__ inline void issue_group(unsigned char* smem, int ks, int nk) const {
+    unsigned char* st = smem + (ks % C::S) * C::STAGE;
     const bool live = ks < nk;
     const uint32_t ak = (uint32_t)ks * a_kstep, bk = (uint32_t)ks * b_kstep;
 #pragma unroll
-    for (int t = 0; t < C::NA; ++t)
-      dma16(ra, lds_addr(sa + (wave * C::NA + t) * 1024), live ? a_off[t] + ak : OOB);
+    for (int t = 0; t < NA_; ++t)
+      dma16(ra, lds_addr(st + a_lds + t * 1024), live ? a_off[t] + ak : OOB);
 #pragma unroll
-    for (int t = 0; t < C::NB; ++t)
-      dma16(rb, lds_addr(sb + (wave * C::NB + t) * 1024),
-            (live && b_off[t] != OOB) ? b_off[t] + bk : OOB);
+    for (int t = 0; t < NB_; ++t)
+      dma16(rb, lds_addr(st + b_lds + t * 1024), (live && b_off[t] != OOB) ? b_off[t] + bk : OOB);
+  }
+
+  __device__ inline void issue_loads(unsigned char* smem, int ks, int nk) const {
+    if (C::EVEN || group == 0)
+      issue_group<C::NA0, C::NB0>(smem, ks, nk);
+    else
+      issue_group<C::NA1, C::NB1>(smem, ks, nk);
   }
 
   __device__ inline void read_frags(const unsigned char* smem, int ks, int kk, bf16x8* af,
@@ -334,7 +366,7 @@ void gemm_bf16_pingpong(Params p) {
   const int tid = threadIdx.x;
   Tile<C> t;
   t.init(p, tid);
-  const int group = t.wave >> 2;
+  const int group = t.group;
 
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -349,7 +381,10 @@ void gemm_bf16_pingpong(Params p) {
 #pragma unroll
   for (int s = 0; s < D; ++s) t.issue_loads(smem, s, nk);
   __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt_and_barrier<(D - 1) * C::L>();  // b0: step 0 landed everywhere
+  if (group == 0)  // b0: step 0 landed everywhere
+    wait_vmcnt_and_barrier<(D - 1) * C::L0>();
+  else
+    wait_vmcnt_and_barrier<(D - 1) * C::L1>();
   __builtin_amdgcn_sched_barrier(0);
   if (group == 1) __asm__ volatile("s_barrier" ::: "memory");  // b1 for group 1
   __builtin_amdgcn_sched_barrier(0);
@@ -361,7 +396,7 @@ void gemm_bf16_pingpong(Params p) {
     t.issue_loads(smem, ks + D, nk);
     __builtin_amdgcn_sched_barrier(0);
     if (group == 1) {
-      __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((D - 1) * C::L) : "memory");
+      __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((D - 1) * C::L1) : "memory");
     } else {
       __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
@@ -371,7 +406,7 @@ void gemm_bf16_pingpong(Params p) {
     for (int sub = 0; sub < C::SUBS; ++sub) mfma_block<C>(acc, af[sub], bf[sub]);
     __builtin_amdgcn_sched_barrier(0);
     if (group == 0) {
-      __asm__ volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((D - 1) * C::L) : "memory");
+      __asm__ volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((D - 1) * C::L0) : "memory");
     } else {
       __asm__ volatile("s_barrier" ::: "memory");
     }
@@ -390,6 +425,7 @@ template <class C>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void gemm_bf16_pipelined(Params p) {
   static_assert(C::S >= 2, "at least two stages");
+  static_assert(C::NW == 4 && C::EVEN, "one group of four waves, even load split");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x;
   Tile<C> t;
@@ -407,7 +443,7 @@ void gemm_bf16_pipelined(Params p) {
 
 #pragma unroll
   for (int s = 0; s < C::S; ++s) t.issue_loads(smem, s, nk);
-  wait_vmcnt_and_barrier<(C::S - 1) * C::L>();
+  wait_vmcnt_and_barrier<(C::S - 1) * C::L0>();
   t.read_frags(smem, 0, 0, af[0], bf[0]);
 
   for (int ks = 0; ks < nk; ++ks) {
@@ -417,7 +453,7 @@ void gemm_bf16_pipelined(Params p) {
       if (sub + 1 < C::SUBS) {
         t.read_frags(smem, ks, (sub + 1) * 16, af[b ^ 1], bf[b ^ 1]);
       } else {
-        wait_vmcnt_and_barrier<(C::S - 2) * C::L>();
+        wait_vmcnt_and_barrier<(C::S - 2) * C::L0>();
         t.issue_loads(smem, ks + C::S, nk);
         // at the last step this reads a stage of zeros that is never used
         t.read_frags(smem, ks + 1, 0, af[b ^ 1], bf[b ^ 1]);
@@ -468,30 +504,39 @@ hipError_t launch(K kernel, const GemmArgs& g, const GemmUnits& u, hipStream_t s
 }
 
 using PP256x256 = Cfg<256, 256, 32, 4, 2, 4>;   // 8 waves of 128x64
+using PP192x256 = Cfg<192, 256, 32, 4, 2, 4>;   // 8 waves of 96x64
+using PP128x256 = Cfg<128, 256, 32, 4, 2, 4>;   // 8 waves of 64x64
 using PP256x128 = Cfg<256, 128, 32, 5, 4, 2>;   // 8 waves of 64x64
 using PL128x128 = Cfg<128, 128, 32, 4, 2, 2>;   // 4 waves of 64x64, 2 workgroups per CU
 constexpr int PP_D = 3;
 
-enum TileKind { kTile128x128 = 0, kTile256x128 = 1, kTile256x256 = 3 };
+enum TileKind {
+  kTile128x128 = 0, kTile256x128 = 1, kTile256x256 = 3, kTile192x256 = 4, kTile128x256 = 5
+};
 
 // Tile choice by a small cost model: a launch of `tiles` workgroups on the CUs left to it
 // (256 / concurrency, times the workgroups one CU holds) runs ceil(tiles / slots) rounds,
-// each as long as one tile takes at the tile's per-CU efficiency.  Efficiencies are the
-// measured per-CU throughputs relative to the 256x256 ping-pong on 8192^3 bf16 (the
-// 256x128 ping-pong reads more bytes per FLOP; the 128x128 kernel runs two workgroups per
-// CU that share its MFMA pipes).
+// each as long as one tile takes at the tile's efficiency.  Efficiencies are measured
+// relative to the 256x256 ping-pong.  The chip runs into its power limit under
+// sustained MFMA load, so a launch that leaves CUs idle runs the busy ones at a higher
+// clock: spreading the same work over more, smaller tiles gains much less than the tile
+// count suggests, and the efficiencies of the smaller tiles carry that (192x256 and
+// 128x256 were measured on AG GEMMs with K = 4096, N = 1536 over T = 4096 ... 8192; the
+// 128x128 kernel runs two workgroups per CU that share its MFMA pipes).
 int choose_tile(const GemmArgs& g, const GemmUnits& u) {
-  static int forced = [] {
-    const char* s = std::getenv("UBX_GEMM_TILE");  // tuning override
-    if (!s) return -1;
+  // Override for tuning and for tests that cover every tile shape; read on every call so
+  // that a process can switch it.
+  if (const char* s = std::getenv("UBX_GEMM_TILE")) {
     if (!std::strcmp(s, "128x128")) return (int)kTile128x128;
     if (!std::strcmp(s, "256x128")) return (int)kTile256x128;
     if (!std::strcmp(s, "256x256")) return (int)kTile256x256;
-    return -1;
-  }();
-  if (forced >= 0) return forced;
+    if (!std::strcmp(s, "192x256")) return (int)kTile192x256;
+    if (!std::strcmp(s, "128x256")) return (int)kTile128x256;
+  }
   struct Opt { int kind, bm, bn, per_cu; double eff; };
   static const Opt opts[] = {{kTile256x256, 256, 256, 1, 1.00},
+                             {kTile192x256, 192, 256, 1, 0.72},
+                             {kTile128x256, 128, 256, 1, 0.62},
                              {kTile256x128, 256, 128, 1, 0.71},
                              {kTile128x128, 128, 128, 2, 0.75}};
   const int share = 256 / (g.concurrency > 1 ? g.concurrency : 1);
@@ -530,6 +575,10 @@ hipError_t launch_gemm_bf16_units(const GemmArgs& g, const GemmUnits& u, hipStre
   switch (choose_tile(g, u)) {
     case kTile256x256:
       return launch<PP256x256>(&gemm_bf16_pingpong<PP256x256, PP_D>, g, u, stream);
+    case kTile192x256:
+      return launch<PP192x256>(&gemm_bf16_pingpong<PP192x256, PP_D>, g, u, stream);
+    case kTile128x256:
+      return launch<PP128x256>(&gemm_bf16_pingpong<PP128x256, PP_D>, g, u, stream);
     case kTile256x128:
       return launch<PP256x128>(&gemm_bf16_pingpong<PP256x128, PP_D>, g, u, stream);
     default:

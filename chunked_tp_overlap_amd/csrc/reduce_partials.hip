@@ -10,12 +10,15 @@
 //   out[r, c] = bf16( ((0 + P_0[r, c]) + P_1[r, c]) + ... + P_{tp-1}[r, c] )   in fp32
 //
 // HBM-bound: every element is read tp times and written once (2 (tp + 1) bytes per output
-// element).  Each lane handles 16-byte vectors (8 elements); consecutive lanes take
-// consecutive vectors; every lane keeps two vectors' worth of loads (2 tp x 16 bytes) in
-// flight.  The partials are read exactly once, so loads and stores are non-temporal.  When
-// the partial rows and the output rows are both packed (leading dimension == cols) the
-// region is one flat range of vectors; otherwise each vector's row is recovered by
-// division.
+// element).  Each lane handles V = 4 16-byte vectors (8 elements each) of one workgroup's
+// chunk of V * 256 consecutive vectors, and walks the slots in ascending order: V loads of
+// slot s, add them into the V fp32 accumulators, then slot s + 1.  Many short chunks with
+// this slot-major order stream faster on MI355X than long per-workgroup ranges or a
+// grid-stride walk with every slot's loads in flight (measured on 8 slots of
+// [16384, 4096]: about 6.1 TB/s against 5.1 - 5.7).  The partials are read exactly once,
+// so loads and stores are non-temporal.  When the partial rows and the output rows are
+// both packed (leading dimension == cols) the vectors are one flat run; otherwise each
+// vector's row is recovered by division.
 #include <hip/hip_runtime.h>
 
 #include "ub_internal.h"
@@ -52,67 +55,69 @@ __device__ inline u32x4 pack8(const float (&acc)[8]) {
   return o;
 }
 
-// Sum of the NS (or nslots, when NS == 0) partials of the vector at element offset `e`.
-template <int NS>
-__device__ inline u32x4 reduce_vec(const uint16_t* parts, int64_t slot_stride, int nslots,
-                                   int64_t e) {
-  float acc[8];
+constexpr int V = 4;  // vectors per lane
+
+// acc[j] += the V vectors of one slot (loads first, then the adds).
+__device__ inline void add_slot(float (&acc)[V][8], const bool (&ok)[V], const int64_t (&ein)[V],
+                                const uint16_t* slot) {
+  u32x4 x[V];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  for (int j = 0; j < V; ++j)
+    if (ok[j]) x[j] = __builtin_nontemporal_load(GLOBAL_PTR(const u32x4, slot + ein[j]));
+#pragma unroll
+  for (int j = 0; j < V; ++j)
+    if (ok[j]) add8(acc[j], x[j]);
+}
+
+// Workgroup b reduces vectors [b * V * THREADS, (b + 1) * V * THREADS) clipped to nvec; lane t
+// takes vectors t, t + THREADS, ...  PACKED: vector v is at element 8 v of every slot and
+// of out; otherwise at row v / vpr, column 8 (v % vpr).  NS = 0: nslots at run time.
+template <int NS, bool PACKED>
+__global__ __launch_bounds__(THREADS) void reduce_chunks(ReduceArgs r, int64_t nvec, int64_t vpr) {
+  const int64_t base = (int64_t)blockIdx.x * (V * THREADS) + threadIdx.x;
+  int64_t ein[V], eout[V];
+  bool ok[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int64_t v = base + j * THREADS;
+    ok[j] = v < nvec;
+    if (PACKED) {
+      ein[j] = eout[j] = v * 8;
+    } else {
+      const int64_t row = v / vpr;
+      const int64_t col = (v - row * vpr) * 8;
+      ein[j] = row * r.ldp + col;
+      eout[j] = row * r.ldo + col;
+    }
+  }
+  float acc[V][8];
+#pragma unroll
+  for (int j = 0; j < V; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[j][i] = 0.0f;
   if constexpr (NS > 0) {
-    u32x4 x[NS];
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      x[s] = __builtin_nontemporal_load(GLOBAL_PTR(const u32x4, parts + s * slot_stride + e));
-#pragma unroll
-    for (int s = 0; s < NS; ++s) add8(acc, x[s]);
+    for (int s = 0; s < NS; ++s) add_slot(acc, ok, ein, r.parts + s * r.slot_stride);
   } else {
-    for (int s = 0; s < nslots; ++s)
-      add8(acc, __builtin_nontemporal_load(GLOBAL_PTR(const u32x4, parts + s * slot_stride + e)));
+    for (int s = 0; s < r.nslots; ++s) add_slot(acc, ok, ein, r.parts + s * r.slot_stride);
   }
-  return pack8(acc);
-}
-
-// Packed rows: vectors v = 0 .. nvec-1 at element offset 8 v in every slot and in out.
-template <int NS>
-__global__ __launch_bounds__(THREADS) void reduce_packed(ReduceArgs r, int64_t nvec) {
-  const int64_t stride = (int64_t)gridDim.x * THREADS;
-  int64_t v = (int64_t)blockIdx.x * THREADS + threadIdx.x;
-  for (; v + stride < nvec; v += 2 * stride) {
-    const u32x4 a = reduce_vec<NS>(r.parts, r.slot_stride, r.nslots, v * 8);
-    const u32x4 b = reduce_vec<NS>(r.parts, r.slot_stride, r.nslots, (v + stride) * 8);
-    __builtin_nontemporal_store(a, GLOBAL_PTR(u32x4, r.out + v * 8));
-    __builtin_nontemporal_store(b, GLOBAL_PTR(u32x4, r.out + (v + stride) * 8));
-  }
-  if (v < nvec)
-    __builtin_nontemporal_store(reduce_vec<NS>(r.parts, r.slot_stride, r.nslots, v * 8),
-                                GLOBAL_PTR(u32x4, r.out + v * 8));
-}
-
-// Strided rows (ldp or ldo != cols).
-template <int NS>
-__global__ __launch_bounds__(THREADS) void reduce_strided(ReduceArgs r) {
-  const int64_t vpr = r.cols >> 3;  // 16-byte vectors per row
-  const int64_t total = r.rows * vpr;
-  for (int64_t v = (int64_t)blockIdx.x * THREADS + threadIdx.x; v < total;
-       v += (int64_t)gridDim.x * THREADS) {
-    const int64_t row = v / vpr;
-    const int64_t col = (v - row * vpr) * 8;
-    __builtin_nontemporal_store(reduce_vec<NS>(r.parts, r.slot_stride, r.nslots, row * r.ldp + col),
-                                GLOBAL_PTR(u32x4, r.out + row * r.ldo + col));
-  }
+#pragma unroll
+  for (int j = 0; j < V; ++j)
+    if (ok[j]) __builtin_nontemporal_store(pack8(acc[j]), GLOBAL_PTR(u32x4, r.out + eout[j]));
 }
 
 template <int NS>
 hipError_t launch_ns(const ReduceArgs& r, hipStream_t stream) {
-  const int64_t nvec = r.rows * (r.cols / 8);
-  // enough waves to cover HBM latency: up to 16 workgroups of 4 waves per CU
-  int64_t blocks = (nvec + THREADS - 1) / THREADS;
-  if (blocks > 256 * 16) blocks = 256 * 16;
+  const int64_t vpr = r.cols / 8;
+  const int64_t nvec = r.rows * vpr;
+  const int64_t blocks = (nvec + V * THREADS - 1) / (V * THREADS);
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (r.ldp == r.cols && r.ldo == r.cols)
-    hipLaunchKernelGGL(reduce_packed<NS>, dim3((unsigned)blocks), dim3(THREADS), 0, stream, r, nvec);
+    hipLaunchKernelGGL((reduce_chunks<NS, true>), dim3((unsigned)blocks), dim3(THREADS), 0, stream,
+                       r, nvec, vpr);
   else
-    hipLaunchKernelGGL(reduce_strided<NS>, dim3((unsigned)blocks), dim3(THREADS), 0, stream, r);
+    hipLaunchKernelGGL((reduce_chunks<NS, false>), dim3((unsigned)blocks), dim3(THREADS), 0,
+                       stream, r, nvec, vpr);
   return hipGetLastError();
 }
 

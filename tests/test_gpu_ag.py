@@ -124,6 +124,42 @@ def test_closed_forms(ub):
         reg.close()
 
 
+TILES = ("256x256", "192x256", "128x256", "256x128", "128x128")
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_every_tile_shape(ub, tile, monkeypatch):
+    """Each GEMM tile shape, forced: bit-exact on integer inputs with ragged rows, a partial
+    column tile and ragged chunks, and bit-identical to the automatic choice on random
+    inputs (an output element's bits depend only on its A row and W column)."""
+    rng = np.random.default_rng(21)
+    cap, H, N, T, tp = 2048, 1024, 520, 1000, 8
+    a_int = wl.integer_bits(rng, (T, H))
+    w_int = wl.integer_bits(rng, (H, N))
+    a = wl.normal_bits(rng, (T, H))
+    w = gu.dev(wl.normal_bits(rng, (H, N), 0.02))
+    print(f"[tile {tile}] cap={cap} H={H} N={N} T={T}", flush=True)
+    reg = gu.Registration(ub, cap, H, tp, workspace=False, pad_rows=8)
+    try:
+        reg.set_T(T)
+        reg.fill(a)
+        monkeypatch.delenv("UBX_GEMM_TILE", raising=False)
+        ref = _run(ub, reg, w, N, ub.make_cfg("bulk", 1))[:T]
+        monkeypatch.setenv("UBX_GEMM_TILE", tile)
+        for atomic in (False, True):
+            got = _run(ub, reg, w, N, ub.make_cfg("ring_exchange", 8, atomic_gemm=atomic))
+            assert np.array_equal(got[:T], ref), atomic
+            assert np.all(got[T:] == gu.CANARY)
+        reg.fill(a_int)
+        oref = _oracle_ag(cap, H, tp, a_int, w_int, _ocfg("pipeline", 3))
+        for atomic in (False, True):
+            got = _run(ub, reg, gu.dev(w_int), N, ub.make_cfg("pipeline", 3, atomic_gemm=atomic))
+            assert np.array_equal(got[:T], oref), atomic
+            assert np.all(got[T:] == gu.CANARY)
+    finally:
+        reg.close()
+
+
 def test_bit_identical_across_schedules_capacity_and_offset(ub):
     """GPU results are bit-identical for every chunk count, stream count, order, rank,
     aggregate setting, capacity and UB base offset."""

@@ -71,6 +71,7 @@ def test_tiny_rs_matches_oracle(ub):
     (1024, 512, 1024, 296, 8, "pipeline", 4),       # 8 slices of 128, ragged chunks
     (256, 64, 1024, 96, 4, "bulk", 5),
     (64, 128, 512, 64, 1, "pipeline", 2),            # tp = 1: a plain GEMM
+    (768, 136, 768, 294, 6, "ring_exchange", 6),     # tp = 6: the run-time slot count
 ])
 def test_integer_inputs_bit_exact(ub, cap, H, K, T, tp, method, ns):
     rng = np.random.default_rng(cap + H + K + T)
@@ -89,6 +90,59 @@ def test_integer_inputs_bit_exact(ub, cap, H, K, T, tp, method, ns):
             assert np.array_equal(ws[: tp * T * H].reshape(tp, T, H), parts)
             assert np.all(ws[tp * T * H:] == gu.CANARY)
             assert np.all(out[T:] == gu.CANARY)
+    finally:
+        reg.close()
+
+
+@pytest.mark.parametrize("tile", ("256x256", "192x256", "128x256", "256x128", "128x128"))
+def test_every_tile_shape_rs(ub, tile, monkeypatch):
+    """Each GEMM tile shape, forced, on the slice GEMMs: integer inputs bit-exact against
+    the oracle (partials and output), ragged rows and chunks."""
+    rng = np.random.default_rng(22)
+    cap, H, K, T, tp = 1024, 264, 2048, 600, 8
+    a = wl.integer_bits(rng, (T, K))
+    wt = wl.integer_bits(rng, (K, H))
+    print(f"[rs tile {tile}] cap={cap} H={H} K={K} T={T}", flush=True)
+    reg = gu.Registration(ub, cap, H, tp, pad_rows=8)
+    monkeypatch.setenv("UBX_GEMM_TILE", tile)
+    try:
+        reg.set_T(T)
+        ref, parts = _oracle_rs(cap, H, tp, a, wt, op.OverlapCfg(method="pipeline", num_splits=3))
+        for atomic in (False, True):
+            reg.ws_t.fill_(gu.CANARY)
+            out = _run_rs(ub, reg, gu.dev(a), K, gu.dev(wt), ub.make_cfg("pipeline", 3, atomic_gemm=atomic))
+            assert np.array_equal(out[:T], ref), atomic
+            ws = gu.host(reg.ws_t)
+            assert np.array_equal(ws[: tp * T * H].reshape(tp, T, H), parts)
+            assert np.all(ws[tp * T * H:] == gu.CANARY)
+            assert np.all(out[T:] == gu.CANARY)
+    finally:
+        reg.close()
+
+
+def test_strided_output_rows(ub):
+    """ldo > H: the reduction writes only the first H columns of each output row, and the
+    values equal those of the packed output."""
+    rng = np.random.default_rng(23)
+    T, H, K, tp, ldo = 200, 200, 1024, 8, 232
+    a = gu.dev(wl.normal_bits(rng, (T, K)))
+    wt = gu.dev(wl.normal_bits(rng, (K, H), 0.02))
+    reg = gu.Registration(ub, 256, H, tp)
+    try:
+        reg.set_T(T)
+        ref = _run_rs(ub, reg, a, K, wt, ub.make_cfg("pipeline", 3))[:T]
+        for atomic in (False, True):
+            out = gu.canary((T + 3, ldo))
+            ub.ub_gemm_rs_chunked(reg.h, a, K, K, wt, H, out, ldo, ub.make_cfg("pipeline", 3, atomic_gemm=atomic))
+            torch.cuda.synchronize()
+            oh = gu.host(out)
+            assert np.array_equal(oh[:T, :H], ref), atomic
+            assert np.all(oh[:T, H:] == gu.CANARY) and np.all(oh[T:] == gu.CANARY)
+            out2 = gu.canary((T, ldo))
+            ub.ub_reduce_partials(reg.h, out2, ldo)
+            torch.cuda.synchronize()
+            oh2 = gu.host(out2)
+            assert np.array_equal(oh2[:, :H], ref) and np.all(oh2[:, H:] == gu.CANARY)
     finally:
         reg.close()
 
