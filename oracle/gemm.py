@@ -18,6 +18,13 @@ Arithmetic (the pages fix none; the plain reading):
 * RS: with Ks = K / tp, partial P_s[t, j] = RNE_bf16( sum_{k in slice s} A[t, k] W[k, j] )
   for s = 0..tp-1, each stored as bf16 in the workspace, then
   out[t, j] = RNE_bf16( sum_s P_s[t, j] ), and shard r = out rows [r T/tp, (r+1) T/tp).
+* RS in ring order (option ``reduce_order="ring"``; [TE#1344] "ring_exchange": the
+  reduce-scatter moves chunks between neighbours): the partials of shard r's rows travel
+  around the ring starting at rank r+1; each rank on the way adds its own bf16 partial
+  to the arriving bf16 value in fp32 and rounds the sum to bf16 before passing it on,
+  and rank r adds last:  acc = P_{r+1};  acc = RNE_bf16(fp32(acc + P_{r+i})) for
+  i = 2 .. tp (indices mod tp).  Reading: the pages give neither the direction nor the
+  precision of a hop; this is the plain ring with bf16 on the wire and fp32 adds.
 
 Each product of two bf16 values is exact in fp64 (16 significant bits).  The K-term dot
 products use fp64 ``np.matmul`` per chunk: exact for integer-valued inputs whose partial
@@ -116,6 +123,8 @@ def rs_chunked(model, a_bits, k, lda, w_bits, ldw, out_bits, ldo, cfg, stream_li
     st = _check_cfg(cfg)
     if st != M.OK:
         return st, None
+    if cfg.reduce_order not in P.REDUCE_ORDERS:
+        return M.INVALID_ARG, None
     T, H = model.active_shape
     tp = model.tp
     if k <= 0 or k % tp != 0:
@@ -138,9 +147,41 @@ def rs_chunked(model, a_bits, k, lda, w_bits, ldw, out_bits, ldo, cfg, stream_li
             o = model.partial_offset_elems(s, r0)
             model.ws[o: o + rows * H] = ps.ravel()
             parts.append(bf16.decode(model.ws[o: o + rows * H]).reshape(rows, H))
-        out[r0:r1, :H] = bf16.encode_rne(exact_sum(parts) + 0.0)
+        if cfg.reduce_order == "ring":
+            out[r0:r1, :H] = ring_sum(parts, r0, T, tp)
+        else:
+            out[r0:r1, :H] = bf16.encode_rne(exact_sum(parts) + 0.0)
         written[r0:r1] += 1
     return M.OK, written
+
+
+def ring_hop(acc_bits, part_bits):
+    """One ring hop: two bf16 values added in fp32 (IEEE round to nearest even), the sum
+    rounded to bf16.  The fp32 sum converts to fp64 exactly, so ``encode_rne`` applies the
+    single bf16 rounding of the fp32 value."""
+    s32 = (bf16.decode(acc_bits).astype(np.float32) + bf16.decode(part_bits).astype(np.float32))
+    return bf16.encode_rne(s32.astype(np.float64))
+
+
+def ring_sum(parts, row0, T, tp):
+    """Ring-order reduce-scatter of the partials ``parts[s]`` (float64 arrays of bf16
+    values, rows [row0, row0 + rows) of slice s); returns bf16 bits.  Row t belongs to
+    shard r = t // (T / tp), whose sum starts at rank (r + 1) mod tp and ends at r."""
+    rows = parts[0].shape[0]
+    bits = [bf16.encode_rne(p) for p in parts]  # exact: the partials are bf16 values
+    out = np.empty(parts[0].shape, dtype=np.uint16)
+    shard_rows = T // tp
+    t = row0
+    while t < row0 + rows:
+        r = t // shard_rows
+        t1 = min(row0 + rows, (r + 1) * shard_rows)
+        sl = slice(t - row0, t1 - row0)
+        acc = bits[(r + 1) % tp][sl]
+        for i in range(2, tp + 1):
+            acc = ring_hop(acc, bits[(r + i) % tp][sl])
+        out[sl] = acc
+        t = t1
+    return out
 
 
 def shards(out_bits, T, H, tp, ldo=None):
@@ -158,6 +199,22 @@ def ag_rows(a_rows_bits, w_bits, n_cols=None):
     w = np.asarray(w_bits)
     n_cols = w.shape[1] if n_cols is None else n_cols
     return bf16.encode_rne(matmul_f64(a_rows_bits, w[:, :n_cols]))
+
+
+def rs_rows_ring(rows, a_rows_bits, w_bits, T, tp, H=None):
+    """Ring-order reduce-scatter of the given global rows (each row's own shard decides
+    its hop order): returns (out bits, partial bits)."""
+    a = np.asarray(a_rows_bits)
+    w = np.asarray(w_bits)
+    H = w.shape[1] if H is None else H
+    ks = a.shape[1] // tp
+    parts = [bf16.encode_rne(matmul_f64(a[:, s * ks:(s + 1) * ks], w[s * ks:(s + 1) * ks, :H]))
+             for s in range(tp)]
+    out = np.empty((len(rows), H), dtype=np.uint16)
+    for i, t in enumerate(rows):
+        dec = [bf16.decode(p[i:i + 1]) for p in parts]
+        out[i] = ring_sum(dec, int(t), T, tp)[0]
+    return out, parts
 
 
 def rs_rows(a_rows_bits, w_bits, tp, H=None):

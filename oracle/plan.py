@@ -39,6 +39,12 @@ METHODS = (RING, PIPELINE, BULK)
 DEFAULT_NUM_MAX_STREAMS = 3
 
 
+# Order of the reduce-scatter sum (reduce-scatter side only):
+#  "ascending" -- all tp partials summed at once, rounded to bf16 once;
+#  "ring"      -- the sum a ring reduce-scatter computes, rounded to bf16 at every hop.
+REDUCE_ORDERS = ("ascending", "ring")
+
+
 @dataclass(frozen=True)
 class OverlapCfg:
     method: str = RING
@@ -47,6 +53,7 @@ class OverlapCfg:
     aggregate: bool = False
     atomic_gemm: bool = False
     rank: int = 0
+    reduce_order: str = "ascending"
 
 
 @dataclass(frozen=True)

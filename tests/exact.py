@@ -122,3 +122,42 @@ def int_valued_gemm_rne(a_bits, w_bits):
     assert np.all(Ai.astype(object) * (1 << SCALE) == A) and np.all(Wi.astype(object) * (1 << SCALE) == W)
     S = Ai @ Wi
     return np.vectorize(lambda s: rne_int(int(s), 0), otypes=[np.uint16])(S)
+
+
+def round_scaled(a, frac_bits, sig_bits, emin):
+    """The value a / 2**frac_bits rounded to `sig_bits` significant bits (exponent clamped
+    below at `emin`), round to nearest even; returned at the same scale.  A value that
+    already fits is returned unchanged."""
+    a = int(a)
+    if a == 0:
+        return 0
+    neg = a < 0
+    m = -a if neg else a
+    e = max(m.bit_length() - 1 - frac_bits, emin)
+    shift = frac_bits + e - (sig_bits - 1)
+    if shift <= 0:
+        return a
+    q, r = divmod(m, 1 << shift)
+    half = 1 << (shift - 1)
+    if r > half or (r == half and (q & 1)):
+        q += 1
+    v = q << shift
+    return -v if neg else v
+
+
+def ring_rne(parts_bits, row0, T, tp):
+    """Ring reduce-scatter by brute force over integers: shard r = t // (T / tp) starts at
+    rank r+1; each hop rounds the exact sum first to fp32 (24 bits) and then to bf16
+    (8 bits).  The sign of an exact zero is not modelled (callers avoid zero sums)."""
+    P = [ints_of(p) for p in parts_bits]
+    rows, n = P[0].shape
+    out = np.zeros((rows, n), dtype=np.uint16)
+    for i in range(rows):
+        r = (row0 + i) // (T // tp)
+        for j in range(n):
+            acc = P[(r + 1) % tp][i, j]
+            for h in range(2, tp + 1):
+                acc = round_scaled(acc + P[(r + h) % tp][i, j], SCALE, 24, -126)
+                acc = round_scaled(acc, SCALE, 8, -126)
+            out[i, j] = rne_int(acc, SCALE)
+    return out
