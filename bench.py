@@ -322,22 +322,28 @@ def secondary(ub, wl, torch, np, dev):
             key = "atomic_gemm" if atomic else "pipeline_3_streams"
             row[key] = {"tflops": round(f / ms / 1e9, 2), "ms": round(ms, 4),
                         "pct_peak": round(100 * f / ms / 1e9 / MFMA_PEAK_BF16_TFLOPS, 2)}
+        cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, False, True, reduce_order="ring")
+        ms = _time_calls(lambda: ub.ub_gemm_rs_chunked(h, a_t, w.k, w.k, w_t, w.hidden, o_t, w.hidden, cfg, stream),
+                         torch, stream, 5)
+        row["atomic_gemm_ring_order"] = {"tflops": round(f / ms / 1e9, 2), "ms": round(ms, 4)}
         rbytes = (w.tp + 1) * T * w.hidden * 2.0
-        warm = _time_calls(lambda: ub.ub_reduce_partials(h, o_t, w.hidden, stream), torch, stream, 10)
-        # honest: a 768 MB write between reductions evicts the 256 MB MALL
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        cold = []
-        for _ in range(5):
-            flush.fill_(1)
-            e0.record(stream)
-            ub.ub_reduce_partials(h, o_t, w.hidden, stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            cold.append(e0.elapsed_time(e1))
-        cold_ms = sorted(cold)[len(cold) // 2]
-        row.update({"reduce_gbs_warm": round(rbytes / warm / 1e6, 1),
-                    "reduce_gbs_flushed": round(rbytes / cold_ms / 1e6, 1),
-                    "reduce_pct_hbm_flushed": round(100 * rbytes / cold_ms / 1e6 / HBM_PEAK_GBS, 2)})
+        for order in ("ascending", "ring"):
+            warm = _time_calls(lambda: ub.ub_reduce_partials(h, o_t, w.hidden, order, stream), torch, stream, 10)
+            # honest: a 768 MB write between reductions evicts the 256 MB MALL
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            cold = []
+            for _ in range(5):
+                flush.fill_(1)
+                e0.record(stream)
+                ub.ub_reduce_partials(h, o_t, w.hidden, order, stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                cold.append(e0.elapsed_time(e1))
+            cold_ms = sorted(cold)[len(cold) // 2]
+            sfx = "" if order == "ascending" else "_ring"
+            row.update({f"reduce{sfx}_gbs_warm": round(rbytes / warm / 1e6, 1),
+                        f"reduce{sfx}_gbs_flushed": round(rbytes / cold_ms / 1e6, 1),
+                        f"reduce{sfx}_pct_hbm_flushed": round(100 * rbytes / cold_ms / 1e6 / HBM_PEAK_GBS, 2)})
         rows.append(row)
     out["fc2_rs"] = rows
     ub.ub_destroy(h)

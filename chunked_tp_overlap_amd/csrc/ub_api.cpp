@@ -210,6 +210,9 @@ ub_status_t join_streams(ub_ctx* h, hipStream_t caller, int S) {
 
 ub_status_t check_cfg_common(ub_ctx* h, const ub_overlap_cfg_t* cfg) {
   if (!cfg) return fail(h, UB_ERR_INVALID_ARG, "cfg is NULL");
+  if (cfg->reduce_order != UB_REDUCE_ASCENDING && cfg->reduce_order != UB_REDUCE_RING)
+    return fail(h, UB_ERR_INVALID_ARG, "reduce_order=%d is not a ub_reduce_order_t",
+                cfg->reduce_order);
   return UB_OK;
 }
 
@@ -252,6 +255,7 @@ UB_API void ub_overlap_cfg_default(ub_overlap_cfg_t* cfg) {
   cfg->use_ce = 1;
   cfg->num_sm = 0;
   cfg->set_sm_margin = 0;
+  cfg->reduce_order = UB_REDUCE_ASCENDING;
 }
 
 UB_API const char* ub_status_string(ub_status_t s) {
@@ -522,6 +526,9 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
     r.ldo = ldo;
     r.rows = T;
     r.cols = H;
+    r.ring = cfg->reduce_order == UB_REDUCE_RING;
+    r.row0 = 0;
+    r.shard_rows = T / tp;
     return timed_launch(h, caller, 1, double(tp - 1) * T * H, 2.0 * (tp + 1) * T * H,
                         [&] { return ubx::launch_reduce_partials(r, caller); }, "reduce launch");
   }
@@ -566,6 +573,9 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
     r.ldo = ldo;
     r.rows = rows;
     r.cols = H;
+    r.ring = cfg->reduce_order == UB_REDUCE_RING;
+    r.row0 = u.row0;
+    r.shard_rows = T / tp;
     const double rbytes = 2.0 * (tp + 1) * rows * H;
     st = timed_launch(h, s, 1, double(tp - 1) * rows * H, rbytes,
                       [&] { return ubx::launch_reduce_partials(r, s); }, "reduce launch");
@@ -574,10 +584,13 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
   return join_streams(h, caller, S);
 }
 
-UB_API ub_status_t ub_reduce_partials(ub_handle_t h, void* out, int64_t ldo, ub_stream_t stream) {
+UB_API ub_status_t ub_reduce_partials(ub_handle_t h, void* out, int64_t ldo,
+                                      int32_t reduce_order, ub_stream_t stream) {
   if (!h) return UB_ERR_NOT_INITIALIZED;
   if (!h->ws) return fail(h, UB_ERR_NOT_INITIALIZED, "no reduce-scatter workspace registered");
   if (!out || !aligned16(out)) return fail(h, UB_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  if (reduce_order != UB_REDUCE_ASCENDING && reduce_order != UB_REDUCE_RING)
+    return fail(h, UB_ERR_INVALID_ARG, "reduce_order=%d is not a ub_reduce_order_t", reduce_order);
   ub_status_t st = check_ld(h, "ldo", ldo, h->hidden);
   if (st != UB_OK) return st;
   if ((st = ensure_device(h, 1)) != UB_OK) return st;
@@ -591,6 +604,9 @@ UB_API ub_status_t ub_reduce_partials(ub_handle_t h, void* out, int64_t ldo, ub_
   r.ldo = ldo;
   r.rows = h->T;
   r.cols = h->hidden;
+  r.ring = reduce_order == UB_REDUCE_RING;
+  r.row0 = 0;
+  r.shard_rows = h->T / h->tp;
   const double rbytes = 2.0 * (h->tp + 1) * h->T * h->hidden;
   return timed_launch(h, s, 1, double(h->tp - 1) * h->T * h->hidden, rbytes,
                       [&] { return ubx::launch_reduce_partials(r, s); }, "reduce launch");

@@ -56,6 +56,10 @@ hipError_t launch_gemm_bf16_units(const GemmArgs& g, const GemmUnits& u, hipStre
 
 // out[r, c] = bf16( sum_{s < nslots} float(parts[s*slot_stride + r*ldp + c]) ), ascending s.
 // cols % 8 == 0, ldp/ldo % 8 == 0, pointers 16-byte aligned.
+// Partial-sum reduction of `rows` x `cols` elements: slot s at parts + s * slot_stride
+// (row stride ldp), result at out (row stride ldo).  ring != 0: ring order with a bf16
+// rounding per hop, where local row i is global row row0 + i of shard
+// (row0 + i) / shard_rows.
 struct ReduceArgs {
   const uint16_t* parts;
   int64_t slot_stride;
@@ -65,6 +69,9 @@ struct ReduceArgs {
   int64_t ldo;
   int64_t rows;
   int64_t cols;
+  int32_t ring;
+  int64_t row0;
+  int64_t shard_rows;
 };
 hipError_t launch_reduce_partials(const ReduceArgs& r, hipStream_t stream);
 

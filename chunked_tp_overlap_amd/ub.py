@@ -35,6 +35,8 @@ UB_RING_EXCHANGE, UB_PIPELINE, UB_BULK = 0, 1, 2
 UB_OP_AG, UB_OP_RS = 0, 1
 UB_MAX_STREAMS = 8
 METHODS = {"ring_exchange": UB_RING_EXCHANGE, "pipeline": UB_PIPELINE, "bulk": UB_BULK}
+UB_REDUCE_ASCENDING, UB_REDUCE_RING = 0, 1
+REDUCE_ORDERS = {"ascending": UB_REDUCE_ASCENDING, "ring": UB_REDUCE_RING}
 
 # Every symbol include/ub.h declares.
 EXPORTS = (
@@ -57,7 +59,7 @@ class UBError(RuntimeError):
 class ub_overlap_cfg_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "method", "num_splits", "num_max_streams", "aggregate", "atomic_gemm", "rank",
-        "use_ce", "num_sm", "set_sm_margin")]
+        "use_ce", "num_sm", "set_sm_margin", "reduce_order")]
 
 
 class ub_plan_unit_t(ctypes.Structure):
@@ -87,7 +89,7 @@ _sig = {
     "ub_copy_in": (_I32, [_H, _P, _I64, _I64, _P]),
     "ub_gemm_ag_chunked": (_I32, [_H, _P, _I64, _I64, _P, _I64, _CFGP, _P]),
     "ub_gemm_rs_chunked": (_I32, [_H, _P, _I64, _I64, _P, _I64, _P, _I64, _CFGP, _P]),
-    "ub_reduce_partials": (_I32, [_H, _P, _I64, _P]),
+    "ub_reduce_partials": (_I32, [_H, _P, _I64, _I32, _P]),
     "ub_set_kernel_timing": (_I32, [_H, _I32]),
     "ub_get_kernel_timing": (_I32, [_H, ctypes.POINTER(ub_kernel_stats_t),
                                     ctypes.POINTER(ub_kernel_stats_t)]),
@@ -137,9 +139,15 @@ def ub_overlap_cfg_default():
     return cfg
 
 
+def _reduce_order(x):
+    return REDUCE_ORDERS[x] if isinstance(x, str) else int(x)
+
+
 def make_cfg(method="ring_exchange", num_splits=1, num_max_streams=3, aggregate=False,
-             atomic_gemm=False, rank=0, use_ce=True, num_sm=0, set_sm_margin=False):
-    """A ``ub_overlap_cfg_t`` from keyword options ([TE#1344] option names)."""
+             atomic_gemm=False, rank=0, use_ce=True, num_sm=0, set_sm_margin=False,
+             reduce_order="ascending"):
+    """A ``ub_overlap_cfg_t`` from keyword options ([TE#1344] option names, plus the
+    reduce-scatter summation order "ascending" or "ring")."""
     cfg = ub_overlap_cfg_default()
     cfg.method = METHODS[method] if isinstance(method, str) else int(method)
     cfg.num_splits = int(num_splits)
@@ -150,6 +158,7 @@ def make_cfg(method="ring_exchange", num_splits=1, num_max_streams=3, aggregate=
     cfg.use_ce = int(bool(use_ce))
     cfg.num_sm = int(num_sm)
     cfg.set_sm_margin = int(bool(set_sm_margin))
+    cfg.reduce_order = _reduce_order(reduce_order)
     return cfg
 
 
@@ -210,8 +219,9 @@ def ub_gemm_rs_chunked(h, a, k, lda, w, ldw, out, ldo, cfg, stream=None):
                                    ctypes.byref(cfg), _stream(stream)), h)
 
 
-def ub_reduce_partials(h, out, ldo, stream=None):
-    _check(_lib.ub_reduce_partials(h, _ptr(out), ldo, _stream(stream)), h)
+def ub_reduce_partials(h, out, ldo, reduce_order="ascending", stream=None):
+    _check(_lib.ub_reduce_partials(h, _ptr(out), ldo, _reduce_order(reduce_order),
+                                   _stream(stream)), h)
 
 
 def ub_set_kernel_timing(h, enable):

@@ -120,7 +120,16 @@ typedef enum { UB_OP_AG = 0, UB_OP_RS = 1 } ub_op_t;
  *   rank             this rank in [0, tp_size): sets the ring order.
  *   use_ce, num_sm, set_sm_margin  accepted for compatibility and ignored: on one GPU
  *                    there is no send/recv to place on a copy engine and no
- *                    communication kernel to reserve compute units for. */
+ *                    communication kernel to reserve compute units for.
+ *   reduce_order     reduce-scatter side only (ub_reduce_order_t).  UB_REDUCE_ASCENDING
+ *                    (default): out = bf16(sum of the tp bf16 partials in fp32, slice 0
+ *                    first), one rounding.  UB_REDUCE_RING: the sum a ring
+ *                    reduce-scatter computes ([TE#1344] "ring_exchange" moves chunks
+ *                    between neighbours): for shard r the partial of slice r+1 starts,
+ *                    slices r+2, ..., r (mod tp) are added one per hop in fp32 and the
+ *                    running value is rounded to bf16 after every hop. */
+typedef enum { UB_REDUCE_ASCENDING = 0, UB_REDUCE_RING = 1 } ub_reduce_order_t;
+
 typedef struct {
   int32_t method;
   int32_t num_splits;
@@ -131,6 +140,7 @@ typedef struct {
   int32_t use_ce;
   int32_t num_sm;
   int32_t set_sm_margin;
+  int32_t reduce_order;
 } ub_overlap_cfg_t;
 
 /* One unit of an execution plan: rows [row0, row1) of the active T, at position `pos`
@@ -154,7 +164,7 @@ typedef struct {
 
 /* Fill `cfg` with the defaults of [TE#1344]: ring exchange, num_splits 1,
  * num_max_streams 3, use_ce 1, aggregate 0, atomic_gemm 0, set_sm_margin 0, num_sm 0,
- * rank 0. */
+ * rank 0, reduce_order UB_REDUCE_ASCENDING. */
 UB_API void ub_overlap_cfg_default(ub_overlap_cfg_t* cfg);
 
 /* Bytes the caller must allocate for a registration of [capacity, hidden] over
@@ -241,13 +251,14 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
                                       const void* w, int64_t ldw, void* out, int64_t ldo,
                                       const ub_overlap_cfg_t* cfg, ub_stream_t stream);
 
-/* The reduce-scatter sum alone: out[t, :] = bf16(sum_s P_s[t, :]) for all active rows
- * t in [0, T), reading the tp_size partial slots currently in the workspace (as left by
- * ub_gemm_rs_chunked at the same T).  One launch on `stream`.  For measuring the
- * reduction by itself ([TE#1344] "pipeline": the reduce-scatter that the GEMM chunks
- * feed). */
+/* The reduce-scatter sum alone: out[t, :] for all active rows t in [0, T) from the
+ * tp_size partial slots currently in the workspace (as left by ub_gemm_rs_chunked at the
+ * same T), summed in the order `reduce_order` (ub_reduce_order_t, as in
+ * ub_overlap_cfg_t; anything else -> UB_ERR_INVALID_ARG).  One launch on `stream`.  For
+ * measuring the reduction by itself ([TE#1344] "pipeline": the reduce-scatter that the
+ * GEMM chunks feed). */
 UB_API ub_status_t ub_reduce_partials(ub_handle_t h, void* out, int64_t ldo,
-                                      ub_stream_t stream);
+                                      int32_t reduce_order, ub_stream_t stream);
 
 /* Per-launch kernel timing.  While enabled, every GEMM and reduction launch is bracketed
  * by HIP events recorded on the stream it is launched on; ub_get_kernel_timing waits for

@@ -170,7 +170,11 @@ def test_gemm_argument_errors_before_any_hip_call():
         assert st("ub_gemm_rs_chunked", h, FAKE, 96, 96, FAKE, 256, FAKE, 256, cp, None) == "UB_ERR_UNSUPPORTED"
         assert st("ub_gemm_rs_chunked", h, FAKE, 256, 248, FAKE, 256, FAKE, 256, cp, None) == "UB_ERR_INVALID_ARG"
         assert st("ub_gemm_rs_chunked", h, FAKE, 256, 256, FAKE, 256, FAKE, 128, cp, None) == "UB_ERR_INVALID_ARG"
-        assert st("ub_reduce_partials", h_nows, FAKE, 256, None) == "UB_ERR_NOT_INITIALIZED"
+        bad = ub.make_cfg("ring_exchange", 2, reduce_order=2)
+        assert st("ub_gemm_rs_chunked", h, FAKE, 256, 256, FAKE, 256, FAKE, 256, ctypes.byref(bad), None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_reduce_partials", h_nows, FAKE, 256, 0, None) == "UB_ERR_NOT_INITIALIZED"
+        assert st("ub_reduce_partials", h, FAKE, 256, 2, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_reduce_partials", h, FAKE, 256, -1, None) == "UB_ERR_INVALID_ARG"
         # copy-size checks against the active T, not the capacity
         ub.ub_set_active_shape(h, (256, 256))
         assert st("ub_copy_in", h, FAKE, 129, 128, None) == "UB_ERR_INVALID_ARG"
@@ -182,6 +186,24 @@ def test_gemm_argument_errors_before_any_hip_call():
     finally:
         ub.ub_destroy(h)
         ub.ub_destroy(h_nows)
+
+
+def test_cfg_default_fills_every_field():
+    """The defaults of the option list, read back through the ctypes layout (a field
+    missing or out of place in either struct shows up here)."""
+    cfg = ub.ub_overlap_cfg_default()
+    got = {n: getattr(cfg, n) for n, _ in cfg._fields_}
+    assert got == {"method": ub.UB_RING_EXCHANGE, "num_splits": 1, "num_max_streams": 3,
+                   "aggregate": 0, "atomic_gemm": 0, "rank": 0, "use_ce": 1, "num_sm": 0,
+                   "set_sm_margin": 0, "reduce_order": ub.UB_REDUCE_ASCENDING}
+    # the library writes exactly sizeof(ub_overlap_cfg_t) bytes: a guard word after the
+    # struct stays intact
+    class Guarded(ctypes.Structure):
+        _fields_ = [("cfg", ub.ub_overlap_cfg_t), ("guard", ctypes.c_uint32)]
+    g = Guarded()
+    g.guard = 0xDEADBEEF
+    ub.raw_call("ub_overlap_cfg_default", ctypes.byref(g.cfg))
+    assert g.guard == 0xDEADBEEF and g.cfg.reduce_order == 0 and g.cfg.use_ce == 1
 
 
 def test_hidden_not_multiple_of_kstep_is_unsupported():

@@ -247,3 +247,109 @@ def test_fc2_full_size_sampled(ub):
             assert bool((tail == gu.CANARY).all().item())
     finally:
         reg.close()
+
+
+# ---- ring-order reduce-scatter (reduce_order="ring") -------------------------------------
+
+def _gpu_parts(reg, tp, T, H):
+    return gu.host(reg.ws_t)[: tp * T * H].reshape(tp, T, H)
+
+
+def test_ring_reduce_bit_exact_on_gpu_partials(ub):
+    """The ring-order sum of the GPU's own partials equals the oracle's ring sum of the
+    same partials bit for bit, for every schedule; the partials are those of the default
+    order; and the ring result differs from the single-rounding one on random data."""
+    from oracle import bf16 as ob
+    rng = np.random.default_rng(41)
+    T, H, K, tp = 240, 136, 1024, 8
+    a = gu.dev(wl.normal_bits(rng, (T, K)))
+    wt = gu.dev(wl.normal_bits(rng, (K, H), 0.02))
+    reg = gu.Registration(ub, 512, H, tp)
+    try:
+        reg.set_T(T)
+        asc = _run_rs(ub, reg, a, K, wt, ub.make_cfg("pipeline", 1))[:T]
+        parts = _gpu_parts(reg, tp, T, H).copy()
+        ref = og.ring_sum([ob.decode(p) for p in parts], 0, T, tp)
+        assert not np.array_equal(ref, asc)
+        for method in ("ring_exchange", "pipeline", "bulk"):
+            for ns in (1, 3, 4):
+                for rank in (0, 5):
+                    for atomic in (False, True):
+                        cfg = ub.make_cfg(method, ns, 3, atomic_gemm=atomic, rank=rank,
+                                          reduce_order="ring")
+                        got = _run_rs(ub, reg, a, K, wt, cfg)
+                        assert np.array_equal(got[:T], ref), (method, ns, rank, atomic)
+                        assert np.all(got[T:] == gu.CANARY)
+                        assert np.array_equal(_gpu_parts(reg, tp, T, H), parts)
+        out2 = gu.canary((T + 2, H))
+        ub.ub_reduce_partials(reg.h, out2, H, "ring")
+        torch.cuda.synchronize()
+        o2 = gu.host(out2)
+        assert np.array_equal(o2[:T], ref) and np.all(o2[T:] == gu.CANARY)
+    finally:
+        reg.close()
+
+
+@pytest.mark.parametrize("tp,T,method,ns", [(8, 296, "ring_exchange", 8), (6, 294, "pipeline", 4),
+                                            (2, 64, "bulk", 3), (1, 40, "bulk", 2)])
+def test_ring_reduce_integer_inputs_end_to_end(ub, tp, T, method, ns):
+    """Integer inputs: GPU partials are exact, so the whole ring reduce-scatter equals the
+    oracle's bit for bit (hops round: partial values exceed 256)."""
+    rng = np.random.default_rng(42 + tp)
+    H, K = 128, 512 * tp
+    a = wl.integer_bits(rng, (T, K))
+    wt = wl.integer_bits(rng, (K, H))
+    cap = T + 8 * tp
+    reg = gu.Registration(ub, cap, H, tp, pad_rows=8)
+    try:
+        reg.set_T(T)
+        ref, parts = _oracle_rs(cap, H, tp, a, wt, op.OverlapCfg(method=method, num_splits=ns,
+                                                                 reduce_order="ring"))
+        for atomic in (False, True):
+            out = _run_rs(ub, reg, gu.dev(a), K, gu.dev(wt),
+                          ub.make_cfg(method, ns, atomic_gemm=atomic, reduce_order="ring"))
+            assert np.array_equal(out[:T], ref), atomic
+            assert np.array_equal(_gpu_parts(reg, tp, T, H), parts)
+    finally:
+        reg.close()
+
+
+def test_ring_reduce_fc2_full_size_sampled(ub):
+    """fc2 (capacity 16384, hidden 4096, K 14336 in 8 slices) at its largest T in ring
+    order: sampled rows (every shard and chunk boundary) against the oracle's ring sum of
+    the GPU partials, bit for bit, and the partials against the oracle's within the gate."""
+    from oracle import bf16 as ob
+    w = wl.fc2()
+    ra, rw, _ = w.seeds()
+    T = wl.FC2_TOKENS[-1]
+    a_all = wl.activations(w, T, ra)
+    wt = wl.weights(w, rw)
+    H, tp = w.hidden, w.tp
+    reg = gu.Registration(ub, w.capacity, H, tp, pad_rows=8)
+    rng = np.random.default_rng(43)
+    try:
+        reg.set_T(T)
+        out = gu.canary((w.capacity + 8, H))
+        cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, atomic_gemm=True,
+                          reduce_order="ring")
+        print(f"[fc2 ring] T={T}", flush=True)
+        ub.ub_gemm_rs_chunked(reg.h, gu.dev(a_all), w.k, w.k, gu.dev(wt), H, out, H, cfg)
+        torch.cuda.synchronize()
+        rows = set(rng.integers(0, T, size=16).tolist()) | {0, T - 1}
+        for r in range(1, tp):
+            rows |= {r * T // tp - 1, r * T // tp}
+        rows = np.array(sorted(rows))
+        ws = reg.ws_t[: tp * T * H].view(tp, T, H)
+        parts = [gu.host(ws[s][torch.as_tensor(rows, device=ws.device)]) for s in range(tp)]
+        oh = gu.host(out)
+        for i, t in enumerate(rows):
+            ref = og.ring_sum([ob.decode(p[i:i + 1]) for p in parts], int(t), T, tp)
+            assert np.array_equal(oh[t:t + 1], ref), t
+        _, oparts = og.rs_rows_ring(rows, a_all[rows], wt, T, tp)
+        ks = w.k // tp
+        for s in range(tp):
+            gu.check_close(parts[s], oparts[s], a_all[rows][:, s * ks:(s + 1) * ks],
+                           wt[s * ks:(s + 1) * ks], f"fc2 ring partial {s}")
+        assert np.all(oh[T:] == gu.CANARY)
+    finally:
+        reg.close()
