@@ -298,6 +298,8 @@ def secondary(ub, wl, torch, np, dev):
     ub.ub_destroy(h)
     del ub_t, w_t, c_t
 
+    out["qkv_arrival"] = arrival(ub, wl, torch, np, dev)
+
     # fc2: row-parallel RS GEMM + reduction over the T sweep (pipeline, 4 chunks)
     w = wl.fc2()
     ra, rw, _ = w.seeds()
@@ -379,6 +381,47 @@ def secondary(ub, wl, torch, np, dev):
     out["gqa_bulk_ag"] = res
     ub.ub_destroy(h)
     return out
+
+
+def arrival(ub, wl, torch, np, dev):
+    """Arrival stand-in on the QKV workload: the 7 non-local ring chunks are copied into the
+    UserBuffer on a copy stream while the 8 chunk GEMMs (host loop, 3 streams) wait on their
+    own chunk's event.  Sources: pinned host memory (SDMA over PCIe, about one xGMI link's
+    rate), device memory by SDMA, device memory by the runtime's copy kernel.  Reports the
+    GEMMs alone, the deliveries alone, both overlapped, the fraction of the delivery time
+    hidden behind the GEMMs, and the overlap as a fraction of the shorter of the two."""
+    w = wl.qkv()
+    ra, rw, _ = w.seeds()
+    log("secondary qkv_arrival")
+    ub_bytes, _ = ub.ub_required_bytes(w.capacity, w.hidden, w.tp)
+    ub_t = torch.from_numpy(wl.activations(w, w.capacity, ra).view(np.int16).ravel()).to(dev)
+    src = ub_t.clone()  # what the other ranks send: the same rows
+    src_host = ub_t.cpu().pin_memory()
+    w_t = torch.from_numpy(wl.weights(w, rw).view(np.int16)).to(dev)
+    c_t = torch.empty((w.capacity, w.n_cols), dtype=torch.int16, device=dev)
+    h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes)
+    stream = torch.cuda.current_stream()
+    res = []
+    for T in (4096, 6144, 8192):
+        ub.ub_set_active_shape(h, (T, w.hidden))
+        row = {"T": T}
+        for mode, use_ce, sb in (("host_pinned_sdma", True, src_host), ("device_sdma", True, src),
+                                 ("device_copy_kernel", False, src)):
+            cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, use_ce=use_ce, rank=0)
+            t_g = _time_calls(lambda: ub.ub_gemm_ag_chunked(h, w_t, w.n_cols, w.n_cols, c_t, w.n_cols, cfg, stream),
+                              torch, stream, 10)
+            t_c = _time_calls(lambda: ub.ub_deliver_chunks(h, sb, cfg, stream), torch, stream, 10)
+            t_o = _time_calls(lambda: ub.ub_gemm_ag_arrival(h, sb, w_t, w.n_cols, w.n_cols, c_t, w.n_cols, cfg, stream),
+                              torch, stream, 10)
+            copy_bytes = 2.0 * (T - T // w.tp) * w.hidden
+            row[mode] = {
+                "gemm_ms": round(t_g, 4), "deliver_ms": round(t_c, 4), "overlapped_ms": round(t_o, 4),
+                "deliver_gbs": round(copy_bytes / t_c / 1e6, 1),
+                "hidden_fraction_of_delivery": round(max(0.0, min(1.0, (t_g + t_c - t_o) / t_c)), 3),
+                "overlap_of_shorter": round(max(0.0, min(1.0, (t_g + t_c - t_o) / min(t_g, t_c))), 3)}
+        res.append(row)
+    ub.ub_destroy(h)
+    return res
 
 
 def cpu_baseline(q, min_seconds):

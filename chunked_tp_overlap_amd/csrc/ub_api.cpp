@@ -25,6 +25,8 @@
 
 #include "ub_internal.h"
 
+constexpr int kMaxArrivalChunks = 64;
+
 struct ub_ctx {
   // registration
   int64_t capacity = 0;
@@ -52,6 +54,10 @@ struct ub_ctx {
   std::vector<hipEvent_t> free_events;
   std::vector<TimedLaunch> pending;
   ub_kernel_stats_t stats[2] = {};
+  // arrival stand-in: copy stream, one arrival event per chunk, its join event
+  hipStream_t copy_stream = nullptr;
+  hipEvent_t ev_arrive[kMaxArrivalChunks] = {};
+  hipEvent_t ev_copy_join = nullptr;
   // scratch for plans
   ubx::Plan plan;
   std::string last_error;
@@ -128,6 +134,23 @@ ub_status_t ensure_device(ub_ctx* h, int need_streams) {
     e = hipEventCreateWithFlags(&h->ev_join[i], hipEventDisableTiming);
     if (e != hipSuccess) return hip_fail(h, e, "hipEventCreate");
     h->n_streams_created = i + 1;
+  }
+  return UB_OK;
+}
+
+// The copy stream and arrival events of the arrival stand-in.
+ub_status_t ensure_arrival(ub_ctx* h, int n_chunks) {
+  hipError_t e;
+  if (!h->copy_stream) {
+    e = hipStreamCreateWithFlags(&h->copy_stream, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(h, e, "hipStreamCreate(copy)");
+    e = hipEventCreateWithFlags(&h->ev_copy_join, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(h, e, "hipEventCreate");
+  }
+  for (int c = 0; c < n_chunks; ++c) {
+    if (h->ev_arrive[c]) continue;
+    e = hipEventCreateWithFlags(&h->ev_arrive[c], hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(h, e, "hipEventCreate");
   }
   return UB_OK;
 }
@@ -392,10 +415,11 @@ UB_API ub_status_t ub_copy_in(ub_handle_t h, const void* src, int64_t rows, int6
   return e == hipSuccess ? UB_OK : hip_fail(h, e, "hipMemcpyAsync");
 }
 
-UB_API ub_status_t ub_gemm_ag_chunked(ub_handle_t h, const void* w, int64_t n_cols, int64_t ldw,
-                                      void* c, int64_t ldc, const ub_overlap_cfg_t* cfg,
-                                      ub_stream_t stream) {
-  if (!h) return UB_ERR_NOT_INITIALIZED;
+namespace {
+
+// Arguments of an all-gather-side GEMM call, checked before any HIP call; builds the plan.
+ub_status_t check_ag_call(ub_ctx* h, const void* w, int64_t n_cols, int64_t ldw, const void* c,
+                          int64_t ldc, const ub_overlap_cfg_t* cfg) {
   ub_status_t st = check_cfg_common(h, cfg);
   if (st != UB_OK) return st;
   if (!w || !c) return fail(h, UB_ERR_INVALID_ARG, "w and c must be non-NULL");
@@ -409,8 +433,78 @@ UB_API ub_status_t ub_gemm_ag_chunked(ub_handle_t h, const void* w, int64_t n_co
   if (h->hidden % ubx::kGemmKStep != 0)
     return fail(h, UB_ERR_UNSUPPORTED, "hidden=%lld must be a multiple of %d",
                 (long long)h->hidden, ubx::kGemmKStep);
-  st = ubx::build_plan(h->T, h->tp, *cfg, UB_OP_AG, &h->plan, &h->last_error);
+  return ubx::build_plan(h->T, h->tp, *cfg, UB_OP_AG, &h->plan, &h->last_error);
+}
+
+// Chunk c of n covers rows [c*T/n, (c+1)*T/n); a unit of index u covers chunks
+// [u*agg, min((u+1)*agg, n)).
+struct ChunkMap {
+  int n = 0, agg = 1, local = -1;  // local: the chunk already in the UB (ring), or -1
+  int64_t row0(int64_t T, int c) const { return (int64_t)c * T / n; }
+  int first(int u) const { return u * agg; }
+  int last(int u) const { return std::min((u + 1) * agg, n); }
+};
+
+ChunkMap chunk_map(const ub_ctx* h, const ub_overlap_cfg_t* cfg) {
+  ChunkMap m;
+  m.n = cfg->method == UB_RING_EXCHANGE ? h->tp : cfg->num_splits;
+  m.agg = cfg->aggregate ? 2 : 1;
+  m.local = cfg->method == UB_RING_EXCHANGE ? cfg->rank : -1;
+  return m;
+}
+
+// The arrival copies on the copy stream, in plan order (each unit's chunks ascending),
+// after the caller's stream reaches this point; chunk c's event is recorded after its copy.
+ub_status_t deliver(ub_ctx* h, const uint16_t* src, int src_on_host, const ub_overlap_cfg_t* cfg,
+                    const ChunkMap& m, hipStream_t caller) {
+  ub_status_t st = ensure_arrival(h, m.n);
   if (st != UB_OK) return st;
+  hipError_t e = hipEventRecord(h->ev_fork, caller);
+  if (e == hipSuccess) e = hipStreamWaitEvent(h->copy_stream, h->ev_fork, 0);
+  if (e != hipSuccess) return hip_fail(h, e, "copy stream fork");
+  // Host source: pinned memory over PCIe, always on the SDMA engines.  Device source: the
+  // SDMA engines (use_ce) or the runtime's copy kernel.
+  const hipMemcpyKind kind = src_on_host  ? hipMemcpyHostToDevice
+                             : cfg->use_ce ? hipMemcpyDeviceToDeviceNoCU
+                                           : hipMemcpyDeviceToDevice;
+  const int64_t H = h->hidden, T = h->T;
+  for (const ub_plan_unit_t& u : h->plan.units) {
+    for (int c = m.first(u.unit); c < m.last(u.unit); ++c) {
+      if (c == m.local) continue;
+      const int64_t r0 = m.row0(T, c), rows = m.row0(T, c + 1) - r0;
+      if (rows > 0) {
+        e = hipMemcpyAsync(h->ub + r0 * H, src + r0 * H, static_cast<size_t>(rows * H) * 2, kind,
+                           h->copy_stream);
+        if (e != hipSuccess) return hip_fail(h, e, "hipMemcpyAsync(arrival)");
+      }
+      e = hipEventRecord(h->ev_arrive[c], h->copy_stream);
+      if (e != hipSuccess) return hip_fail(h, e, "hipEventRecord(arrival)");
+    }
+  }
+  return UB_OK;
+}
+
+ub_status_t check_arrival(ub_ctx* h, const void* src, const ub_overlap_cfg_t* cfg) {
+  if (!src || !aligned16(src)) return fail(h, UB_ERR_INVALID_ARG, "src must be 16-byte aligned");
+  if (cfg->atomic_gemm)
+    return fail(h, UB_ERR_UNSUPPORTED,
+                "arrival-gated units run on the host-loop schedule only (atomic_gemm=0)");
+  const ChunkMap m = chunk_map(h, cfg);
+  if (m.n > kMaxArrivalChunks)
+    return fail(h, UB_ERR_UNSUPPORTED, "at most %d chunks can be delivered", kMaxArrivalChunks);
+  return UB_OK;
+}
+
+// Body of both all-gather-side entry points.  src == nullptr: the UB prefix is already
+// complete.  Otherwise the non-local chunks are delivered from src while the units run,
+// each unit waiting for the arrival of its own chunks.
+ub_status_t ag_call(ub_ctx* h, const void* src, int src_on_host, const void* w, int64_t n_cols,
+                    int64_t ldw, void* c, int64_t ldc, const ub_overlap_cfg_t* cfg,
+                    ub_stream_t stream) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  ub_status_t st = check_ag_call(h, w, n_cols, ldw, c, ldc, cfg);
+  if (st != UB_OK) return st;
+  if (src && (st = check_arrival(h, src, cfg)) != UB_OK) return st;
   const int64_t H = h->hidden;
   hipStream_t caller = static_cast<hipStream_t>(stream);
 
@@ -439,12 +533,23 @@ UB_API ub_status_t ub_gemm_ag_chunked(ub_handle_t h, const void* w, int64_t n_co
 
   const int S = h->plan.n_streams;
   if ((st = ensure_device(h, S)) != UB_OK) return st;
+  const ChunkMap m = chunk_map(h, cfg);
+  if (src && (st = deliver(h, static_cast<const uint16_t*>(src), src_on_host, cfg, m, caller)) !=
+                 UB_OK)
+    return st;
   if ((st = fork_streams(h, caller, S)) != UB_OK) return st;
   for (const ub_plan_unit_t& u : h->plan.units) {
     const int64_t rows = u.row1 - u.row0;
     if (rows <= 0) continue;
     if (rows > kMaxRowsPerUnit) return fail(h, UB_ERR_UNSUPPORTED, "unit too large");
     hipStream_t s = u.stream == 0 ? caller : h->streams[u.stream];
+    if (src) {
+      for (int ch = m.first(u.unit); ch < m.last(u.unit); ++ch) {
+        if (ch == m.local) continue;
+        hipError_t e = hipStreamWaitEvent(s, h->ev_arrive[ch], 0);
+        if (e != hipSuccess) return hip_fail(h, e, "hipStreamWaitEvent(arrival)");
+      }
+    }
     ubx::GemmArgs g{};
     g.a = h->ub + u.row0 * H;  // byte offset row0 * hidden * 2 into the capacity buffer
     g.lda = H;
@@ -463,7 +568,47 @@ UB_API ub_status_t ub_gemm_ag_chunked(ub_handle_t h, const void* w, int64_t n_co
                       "GEMM launch");
     if (st != UB_OK) return st;
   }
+  if (src) {  // every chunk was consumed by a unit; join the copy stream all the same
+    hipError_t e = hipEventRecord(h->ev_copy_join, h->copy_stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(caller, h->ev_copy_join, 0);
+    if (e != hipSuccess) return hip_fail(h, e, "copy stream join");
+  }
   return join_streams(h, caller, S);
+}
+
+}  // namespace
+
+UB_API ub_status_t ub_gemm_ag_chunked(ub_handle_t h, const void* w, int64_t n_cols, int64_t ldw,
+                                      void* c, int64_t ldc, const ub_overlap_cfg_t* cfg,
+                                      ub_stream_t stream) {
+  return ag_call(h, nullptr, 0, w, n_cols, ldw, c, ldc, cfg, stream);
+}
+
+UB_API ub_status_t ub_gemm_ag_arrival(ub_handle_t h, const void* src, int32_t src_on_host,
+                                      const void* w, int64_t n_cols, int64_t ldw, void* c,
+                                      int64_t ldc, const ub_overlap_cfg_t* cfg,
+                                      ub_stream_t stream) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  if (!src) return fail(h, UB_ERR_INVALID_ARG, "src is NULL");
+  return ag_call(h, src, src_on_host != 0, w, n_cols, ldw, c, ldc, cfg, stream);
+}
+
+UB_API ub_status_t ub_deliver_chunks(ub_handle_t h, const void* src, int32_t src_on_host,
+                                     const ub_overlap_cfg_t* cfg, ub_stream_t stream) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  ub_status_t st = check_cfg_common(h, cfg);
+  if (st != UB_OK) return st;
+  if ((st = check_arrival(h, src, cfg)) != UB_OK) return st;
+  if ((st = ubx::build_plan(h->T, h->tp, *cfg, UB_OP_AG, &h->plan, &h->last_error)) != UB_OK)
+    return st;
+  if ((st = ensure_device(h, 1)) != UB_OK) return st;
+  hipStream_t caller = static_cast<hipStream_t>(stream);
+  if ((st = deliver(h, static_cast<const uint16_t*>(src), src_on_host != 0, cfg, chunk_map(h, cfg),
+                    caller)) != UB_OK)
+    return st;
+  hipError_t e = hipEventRecord(h->ev_copy_join, h->copy_stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(caller, h->ev_copy_join, 0);
+  return e == hipSuccess ? UB_OK : hip_fail(h, e, "copy stream join");
 }
 
 UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, int64_t lda,
@@ -643,6 +788,13 @@ UB_API ub_status_t ub_destroy(ub_handle_t h) {
       (void)hipEventDestroy(h->ev_join[i]);
     }
     if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+    if (h->copy_stream) {
+      (void)hipStreamSynchronize(h->copy_stream);
+      (void)hipStreamDestroy(h->copy_stream);
+      (void)hipEventDestroy(h->ev_copy_join);
+    }
+    for (hipEvent_t ev : h->ev_arrive)
+      if (ev) (void)hipEventDestroy(ev);
     for (hipEvent_t ev : h->free_events) (void)hipEventDestroy(ev);
     if (cur >= 0 && cur != h->device) (void)hipSetDevice(cur);
   }

@@ -234,6 +234,40 @@ UB_API ub_status_t ub_gemm_ag_chunked(ub_handle_t h, const void* w, int64_t n_co
                                       int64_t ldw, void* c, int64_t ldc,
                                       const ub_overlap_cfg_t* cfg, ub_stream_t stream);
 
+/* Arrival stand-in for the all-gather side ([TE#1344] "ring_exchange": the other ranks'
+ * chunks arrive by point-to-point copies, "use_ce": on the Copy Engine, without compute
+ * units; each GEMM chunk runs once its data is there).
+ *
+ * Same result as ub_gemm_ag_chunked, but the UB prefix is completed while the call runs:
+ * `src` ([T, hidden] bf16 packed, 16-byte aligned; device memory, or pinned host memory
+ * when src_on_host is nonzero) holds the active rows as the other ranks would send them,
+ * and the non-local chunks are copied from src into
+ * the UB rows they belong to on the handle's copy stream, in plan order (each unit's
+ * chunks ascending), one event per chunk.  Each unit's GEMM waits on the events of its own
+ * chunks only, so GEMMs on arrived chunks overlap the remaining copies.
+ *   Local chunk: with method ring exchange, chunk `rank` (rows [rank*T/tp,
+ *     (rank+1)*T/tp)) is this rank's own shard, already in the UB (ub_copy_in); its rows
+ *     of src are never read.  With pipeline or bulk every chunk is delivered.
+ *   Copy kind: host source: hipMemcpyHostToDevice over PCIe (SDMA engines; src must be
+ *     pinned, e.g. hipHostMalloc).  Device source: use_ce = 1 -> hipMemcpyDeviceToDeviceNoCU
+ *     (SDMA engines, no compute units), use_ce = 0 -> hipMemcpyDeviceToDevice (the
+ *     runtime's copy kernel, which shares the compute units with the GEMMs).  Measured on
+ *     MI355X with ROCm 7.2: host-to-device SDMA copies and copy-kernel copies run
+ *     alongside kernels of other streams, device-to-device SDMA copies wait for them.
+ *   atomic_gemm = 1 -> UB_ERR_UNSUPPORTED (units are gated by events, which needs the
+ *     host-loop schedule); more than 64 chunks -> UB_ERR_UNSUPPORTED.
+ * The copies start when the caller's stream reaches the call; the call as a whole is
+ * ordered on `stream`.  The caller must not touch the UB prefix or src until then. */
+UB_API ub_status_t ub_gemm_ag_arrival(ub_handle_t h, const void* src, int32_t src_on_host,
+                                      const void* w, int64_t n_cols, int64_t ldw, void* c,
+                                      int64_t ldc, const ub_overlap_cfg_t* cfg,
+                                      ub_stream_t stream);
+
+/* The deliveries of ub_gemm_ag_arrival alone (same copies, order, stream and kind, no
+ * GEMM), ordered on `stream`: for measuring how long the arrivals take by themselves. */
+UB_API ub_status_t ub_deliver_chunks(ub_handle_t h, const void* src, int32_t src_on_host,
+                                     const ub_overlap_cfg_t* cfg, ub_stream_t stream);
+
 /* Reduce-scatter-side row-parallel GEMM ([MLM#1240] MLP diagram, RowParallelLinear;
  * [TE#3564]: partial chunks inside the workspace's allocation, offsets from active T):
  * with Ks = k / tp_size, for every plan unit (rows [r0, r1)) and slice s:

@@ -206,6 +206,28 @@ def test_cfg_default_fills_every_field():
     assert g.guard == 0xDEADBEEF and g.cfg.reduce_order == 0 and g.cfg.use_ce == 1
 
 
+def test_arrival_argument_errors_before_any_hip_call():
+    h = _handle(512, 256, 2)
+    try:
+        def st(name, *args):
+            return ub.STATUS[ub.raw_call(name, *args)]
+        cfg = ub.make_cfg("ring_exchange", 2)
+        cp = ctypes.byref(cfg)
+        assert st("ub_gemm_ag_arrival", h, None, 0, FAKE, 384, 384, FAKE, 384, cp, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_gemm_ag_arrival", h, FAKE + 8, 0, FAKE, 384, 384, FAKE, 384, cp, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_gemm_ag_arrival", h, FAKE, 0, FAKE, 380, 384, FAKE, 384, cp, None) == "UB_ERR_INVALID_ARG"
+        atomic = ub.make_cfg("ring_exchange", 2, atomic_gemm=True)
+        assert st("ub_gemm_ag_arrival", h, FAKE, 0, FAKE, 384, 384, FAKE, 384, ctypes.byref(atomic), None) == "UB_ERR_UNSUPPORTED"
+        many = ub.make_cfg("pipeline", 65)
+        assert st("ub_gemm_ag_arrival", h, FAKE, 0, FAKE, 384, 384, FAKE, 384, ctypes.byref(many), None) == "UB_ERR_UNSUPPORTED"
+        assert st("ub_deliver_chunks", h, None, 0, cp, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_deliver_chunks", h, FAKE, 0, ctypes.byref(many), None) == "UB_ERR_UNSUPPORTED"
+        assert st("ub_deliver_chunks", h, FAKE, 0, None, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_deliver_chunks", None, FAKE, 0, cp, None) == "UB_ERR_NOT_INITIALIZED"
+    finally:
+        ub.ub_destroy(h)
+
+
 def test_hidden_not_multiple_of_kstep_is_unsupported():
     h = _handle(64, 72, 1)
     try:

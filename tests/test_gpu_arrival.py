@@ -1,0 +1,156 @@
+"""GPU tests of the arrival stand-in (ub_gemm_ag_arrival, ub_deliver_chunks): the non-local
+chunks are copied into the UserBuffer on a copy stream while the GEMM units that need them
+wait on per-chunk events.  Results must be bit-identical to the all-gather GEMM over a
+complete buffer, the local chunk's rows of the source are never read, and nothing beyond
+the active prefix is touched."""
+
+import numpy as np
+import pytest
+import torch
+
+from chunked_tp_overlap_amd import workloads as wl
+from oracle import gemm as og
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ub():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import chunked_tp_overlap_amd.ub as m
+    return m
+
+
+def _local_rows(method, rank, T, tp):
+    if method != "ring_exchange":
+        return None
+    return (rank * T // tp, (rank + 1) * T // tp)
+
+
+def _pinned(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).pin_memory()
+
+
+def _case(ub, reg, a, w_t, N, cfg_kw, ref, T, tp, host_src=False):
+    """UB: canary except the local chunk; src: every row, local rows replaced by canary
+    (device memory, or pinned host memory when host_src)."""
+    H = reg.hidden
+    loc = _local_rows(cfg_kw["method"], cfg_kw.get("rank", 0), T, tp)
+    reg.ub_t.fill_(gu.CANARY)
+    src_h = a.copy()
+    if loc:
+        reg.ub_t[loc[0] * H: loc[1] * H].copy_(gu.dev(a[loc[0]:loc[1]]).reshape(-1))
+        src_h[loc[0]:loc[1]] = gu.CANARY
+    src = _pinned(src_h) if host_src else gu.dev(src_h)
+    c = gu.canary((reg.capacity + 4, N))
+    ub.ub_gemm_ag_arrival(reg.h, src, w_t, N, N, c, N, ub.make_cfg(**cfg_kw))
+    torch.cuda.synchronize()
+    ch = gu.host(c)
+    assert np.array_equal(ch[:T], ref), cfg_kw
+    assert np.all(ch[T:] == gu.CANARY)
+    ubh = gu.host(reg.ub_t)
+    assert np.array_equal(ubh[: T * H].reshape(T, H), a), cfg_kw  # prefix complete
+    assert np.all(ubh[T * H:] == gu.CANARY)
+
+
+def test_arrival_bit_identical_to_complete_buffer(ub):
+    rng = np.random.default_rng(51)
+    cap, H, N, T, tp = 1024, 512, 264, 600, 8
+    a = wl.normal_bits(rng, (T, H))
+    w_t = gu.dev(wl.normal_bits(rng, (H, N), 0.02))
+    reg = gu.Registration(ub, cap, H, tp, workspace=False, pad_rows=8)
+    try:
+        reg.set_T(T)
+        reg.fill(a)
+        c = gu.canary((T, N))
+        ub.ub_gemm_ag_chunked(reg.h, w_t, N, N, c, N, ub.make_cfg("bulk", 1))
+        torch.cuda.synchronize()
+        ref = gu.host(c)
+        for kw in (dict(method="ring_exchange", rank=0), dict(method="ring_exchange", rank=5),
+                   dict(method="ring_exchange", rank=3, aggregate=True),
+                   dict(method="ring_exchange", rank=7, num_max_streams=1),
+                   dict(method="pipeline", num_splits=5), dict(method="bulk", num_splits=3, aggregate=True)):
+            for use_ce in (True, False):
+                print(f"[arrival] {kw} use_ce={use_ce}", flush=True)
+                _case(ub, reg, a, w_t, N, dict(kw, use_ce=use_ce), ref, T, tp)
+            print(f"[arrival] {kw} host source", flush=True)
+            _case(ub, reg, a, w_t, N, kw, ref, T, tp, host_src=True)
+    finally:
+        reg.close()
+
+
+def test_deliver_chunks_alone(ub):
+    rng = np.random.default_rng(52)
+    cap, H, T, tp, rank = 512, 256, 296, 8, 2
+    a = wl.normal_bits(rng, (T, H))
+    reg = gu.Registration(ub, cap, H, tp, workspace=False, pad_rows=8)
+    try:
+        reg.set_T(T)
+        for use_ce, src in ((True, gu.dev(a)), (False, gu.dev(a)), (True, _pinned(a))):
+            reg.ub_t.fill_(gu.CANARY)
+            ub.ub_deliver_chunks(reg.h, src, ub.make_cfg("ring_exchange", rank=rank, use_ce=use_ce))
+            torch.cuda.synchronize()
+            got = gu.host(reg.ub_t)[: T * H].reshape(T, H)
+            lo, hi = rank * T // tp, (rank + 1) * T // tp
+            assert np.array_equal(got[:lo], a[:lo]) and np.array_equal(got[hi:], a[hi:])
+            assert np.all(got[lo:hi] == gu.CANARY)  # the local chunk is not delivered
+            assert np.all(gu.host(reg.ub_t)[T * H:] == gu.CANARY)
+    finally:
+        reg.close()
+
+
+def test_arrival_ordered_after_caller_stream_work(ub):
+    """The local shard is written on the caller's stream right before the call (no host
+    synchronisation): the copies and GEMMs must see it."""
+    rng = np.random.default_rng(53)
+    cap, H, N, T, tp, rank = 512, 256, 128, 256, 4, 1
+    a = wl.normal_bits(rng, (T, H))
+    w = wl.normal_bits(rng, (H, N), 0.02)
+    reg = gu.Registration(ub, cap, H, tp, workspace=False)
+    s = torch.cuda.Stream()
+    try:
+        reg.set_T(T)
+        lo, hi = rank * T // tp, (rank + 1) * T // tp
+        src_h = a.copy()
+        src_h[lo:hi] = gu.CANARY
+        src, loc, w_t = gu.dev(src_h), gu.dev(a[lo:hi]), gu.dev(w)
+        c = gu.canary((T, N))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            reg.ub_t.fill_(gu.CANARY)
+            torch.cuda._sleep(2_000_000)  # keep the stream busy before the writes land
+            ub.ub_copy_in(reg.h, loc, hi - lo, lo, s)
+            ub.ub_gemm_ag_arrival(reg.h, src, w_t, N, N, c, N, ub.make_cfg("ring_exchange", rank=rank), s)
+        torch.cuda.synchronize()
+        gu.check_close(gu.host(c), og.ag_rows(a, w, N), a, w, "arrival stream order")
+    finally:
+        reg.close()
+
+
+def test_arrival_qkv_full_size(ub):
+    """The QKV workload at T = 8192 (capacity 8192, hidden 4096, W [4096, 1536], ring of
+    8): bit-identical to the GEMM over the complete buffer, sampled rows vs the oracle."""
+    w = wl.qkv()
+    ra, rw, _ = w.seeds()
+    T = w.capacity
+    a = wl.activations(w, T, ra)
+    wt = wl.weights(w, rw)
+    N, H, tp = w.n_cols, w.hidden, w.tp
+    w_t = gu.dev(wt)
+    reg = gu.Registration(ub, w.capacity, H, tp, workspace=False, pad_rows=8)
+    try:
+        reg.set_T(T)
+        reg.fill(a)
+        c = gu.canary((T, N))
+        ub.ub_gemm_ag_chunked(reg.h, w_t, N, N, c, N, ub.make_cfg("ring_exchange", atomic_gemm=True))
+        torch.cuda.synchronize()
+        ref = gu.host(c)
+        for use_ce, host_src in ((True, False), (False, False), (True, True)):
+            print(f"[arrival qkv] use_ce={use_ce} host_src={host_src}", flush=True)
+            _case(ub, reg, a, w_t, N, dict(method="ring_exchange", rank=3, use_ce=use_ce), ref, T, tp,
+                  host_src=host_src)
+        rows = np.array(sorted({0, 1, T // 2, T - 1} | {r * T // tp for r in range(tp)}))
+        gu.check_close(ref[rows], og.ag_rows(a[rows], wt, N), a[rows], wt, "arrival qkv rows")
+    finally:
+        reg.close()
