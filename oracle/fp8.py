@@ -1,0 +1,99 @@
+"""FP8 (E4M3) UserBuffers for the oracle (test infrastructure only; see ``oracle/__init__``).
+
+The pages name quantized (FP8) UserBuffers and leave them outside the prototype's initial
+scope ([TE#3564], "Implementation approach in the prototype", last paragraph: the
+prototype targets unquantized 2-byte buffers).  They give no format or scaling rule, so
+the plain reading is taken here:
+
+* element format: OCP 8-bit E4M3 ("FN"): 1 sign bit, 4 exponent bits with bias 7, 3
+  stored significand bits; subnormals with spacing 2**-9; largest finite value 448; no
+  infinities; S.1111.111 is NaN;
+* quantization with a per-tensor scale: q = sat(RNE_e4m3(fp32(x * scale))) -- the product
+  is formed in fp32 (IEEE round to nearest even), then rounded to the nearest E4M3 value
+  (ties to even), and magnitudes beyond 448 saturate to 448; NaN stays NaN;
+* the all-gather GEMM on quantized operands, with the weights stored [N, K] (K
+  contiguous) as FP8 GEMMs conventionally take them:
+      C[t, j] = RNE_bf16( (sum_k qa[t, k] * qw[j, k]) * sa * sw ),
+  sa and sw being the per-tensor dequantization factors (1 / scale of each operand).
+
+FP8 codes are carried as uint8 arrays.
+"""
+
+import numpy as np
+
+from . import bf16
+
+_MAX = 448.0
+_EMIN = -6          # smallest normal exponent
+_MAN = 3            # stored significand bits
+NAN_CODE = 0x7F
+
+
+def decode(codes):
+    """uint8 E4M3 codes -> float64 values (exact); NaN codes give NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    normal = np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int32))
+    sub = np.ldexp(m / 8.0, _EMIN)
+    v = np.where(e == 0, sub, normal)
+    v = np.where((c & 0x7F) == 0x7F, np.nan, v)
+    return sign * v
+
+
+def encode(x):
+    """float64 values -> uint8 E4M3 codes: round to nearest, ties to even, saturating at
+    +-448.  For finite nonzero x with e = max(floor(log2|x|), -6) the neighbouring E4M3
+    values are spaced q = 2**(e - 3); x / q is exact and ``np.rint`` rounds halves to
+    even.  Zeros keep their sign."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint8)
+    ax = np.abs(x)
+    nz = np.isfinite(x) & (ax != 0.0)
+    _, E = np.frexp(np.where(nz, ax, 1.0))
+    e = np.maximum(E.astype(np.int64) - 1, _EMIN)
+    q = np.ldexp(1.0, (e - _MAN).astype(np.int32))
+    y = np.where(nz, np.rint(np.where(nz, ax, 0.0) / q) * q, 0.0)
+    y = np.minimum(y, _MAX)
+    y = np.where(np.isinf(x), _MAX, y)  # saturating conversion
+    # y is now an exact E4M3 magnitude: find its code
+    _, E2 = np.frexp(np.where(y > 0, y, 1.0))
+    e2 = E2.astype(np.int64) - 1
+    normal = y >= 2.0 ** _EMIN
+    man_n = np.where(normal, np.rint(np.ldexp(y, (-e2).astype(np.int32)) * 8.0 - 8.0), 0)
+    code_n = ((e2 + 7) << 3) + man_n.astype(np.int64)
+    code_s = np.rint(np.ldexp(y, 9)).astype(np.int64)  # multiples of 2**-9
+    code = np.where(normal, code_n, code_s)
+    code = np.where(np.signbit(x), code | 0x80, code)
+    out[...] = code.astype(np.uint8)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = NAN_CODE | np.where(np.signbit(x[nan]), 0x80, 0).astype(np.uint8)
+    return out
+
+
+def quantize(x_bf16_bits, scale):
+    """bf16 patterns -> E4M3 codes of fp32(x * scale) (see the module docstring)."""
+    x = bf16.decode(x_bf16_bits).astype(np.float32)
+    y = (x * np.float32(scale)).astype(np.float64)  # IEEE fp32 product, then exact widening
+    return encode(y)
+
+
+def ag_chunked_fp8(model_T, ub_codes, hidden, w_codes, n_cols, sa, sw, units):
+    """All-gather GEMM over E4M3 operands, unit by unit: rows [r0, r1) of the UserBuffer's
+    active prefix (``ub_codes`` flat, row stride ``hidden``) against ``w_codes`` [n_cols,
+    >= hidden] (row j = output column j, K contiguous).  Returns the bf16 bits of the T
+    rows and a per-row write count.  ``units`` is the plan (``oracle.plan.build``)."""
+    T = model_T
+    W = decode(np.asarray(w_codes)[:n_cols, :hidden])
+    C = np.zeros((T, n_cols), dtype=np.uint16)
+    written = np.zeros(T, dtype=np.int64)
+    for u in units:
+        if u.row1 == u.row0:
+            continue
+        A = decode(np.asarray(ub_codes)[u.row0 * hidden: u.row1 * hidden]).reshape(-1, hidden)
+        dot = (A @ W.T) + 0.0  # exact: products have 8 significant bits, sums stay short
+        C[u.row0:u.row1] = bf16.encode_rne(dot * float(sa) * float(sw))
+        written[u.row0:u.row1] += 1
+    return C, written

@@ -161,3 +161,29 @@ def ring_rne(parts_bits, row0, T, tp):
                 acc = round_scaled(acc, SCALE, 8, -126)
             out[i, j] = rne_int(acc, SCALE)
     return out
+
+
+def e4m3_to_int(code):
+    """One finite E4M3 code -> integer value * 2**9 (written from the bit fields)."""
+    c = int(code)
+    sign = -1 if c & 0x80 else 1
+    e = (c >> 3) & 0xF
+    m = c & 7
+    if (c & 0x7F) == 0x7F:
+        raise ValueError("NaN has no integer form")
+    mag = m if e == 0 else (8 + m) << (e - 1)  # (8+m)/8 * 2**(e-7) * 2**9
+    return sign * mag
+
+
+def fp8_gemm_rne(a_codes, w_codes_nk, sa_log2, sw_log2):
+    """bf16( sum_k a[t,k] * w[j,k] * 2**sa_log2 * 2**sw_log2 ) by integer brute force
+    (w given [N, K]); power-of-two scales keep everything exact."""
+    A = [[e4m3_to_int(x) for x in row] for row in np.asarray(a_codes)]
+    W = [[e4m3_to_int(x) for x in row] for row in np.asarray(w_codes_nk)]
+    out = np.zeros((len(A), len(W)), dtype=np.uint16)
+    frac = 18 - sa_log2 - sw_log2  # value = S / 2**frac
+    for i, ar in enumerate(A):
+        for j, wr in enumerate(W):
+            S = sum(x * y for x, y in zip(ar, wr))
+            out[i, j] = rne_int(S << max(0, -frac), max(frac, 0))
+    return out
