@@ -25,6 +25,7 @@ import sys
 import time
 
 MFMA_PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
+MFMA_PEAK_FP8_TFLOPS = 5033.2   # dense fp8: twice the bf16 rate
 HBM_PEAK_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 GEMM_SRC = os.path.join(ROOT, "chunked_tp_overlap_amd", "csrc", "gemm_bf16.hip")
@@ -299,6 +300,7 @@ def secondary(ub, wl, torch, np, dev):
     del ub_t, w_t, c_t
 
     out["qkv_arrival"] = arrival(ub, wl, torch, np, dev)
+    out["qkv_fp8"] = qkv_fp8(ub, wl, torch, np, dev)
 
     # fc2: row-parallel RS GEMM + reduction over the T sweep (pipeline, 4 chunks)
     w = wl.fc2()
@@ -422,6 +424,52 @@ def arrival(ub, wl, torch, np, dev):
         res.append(row)
     ub.ub_destroy(h)
     return res
+
+
+def qkv_fp8(ub, wl, torch, np, dev):
+    """The QKV step on an FP8 (E4M3) UserBuffer: activations quantized into the buffer with
+    a per-tensor scale, the weight quantized [N, K] through a scratch fp8 registration,
+    then the 32 microbatches of one step through the device-side chunk loop."""
+    w = wl.qkv()
+    ra, rw, rt = w.seeds()
+    Ts, _ = wl.qkv_pack_tokens(rt)
+    log("secondary qkv_fp8")
+    H, N = w.hidden, w.n_cols
+    x = torch.from_numpy(wl.activations(w, w.capacity, ra).view(np.int16)).to(dev)
+    wt = torch.from_numpy(wl.weights(w, rw).view(np.int16)).to(dev)
+    sx = 448.0 / float(x.view(torch.bfloat16).float().abs().max())
+    sw = 448.0 / float(wt.view(torch.bfloat16).float().abs().max())
+    ub_t = torch.empty(w.capacity * H, dtype=torch.uint8, device=dev)
+    h = ub.ub_init(w.capacity, H, w.tp, ub.UB_DTYPE_FP8_E4M3, ub_t, w.capacity * H)
+    w8 = torch.empty(N * H, dtype=torch.uint8, device=dev)
+    hw = ub.ub_init(N, H, 1, ub.UB_DTYPE_FP8_E4M3, w8, N * H)
+    ub.ub_quantize_in(hw, wt.t().contiguous(), N, 0, sw)
+    stream = torch.cuda.current_stream()
+    q_ms = _time_calls(lambda: ub.ub_quantize_in(h, x, w.capacity, 0, sx), torch, stream, 10)
+    cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, w.aggregate, True)
+    c_t = torch.empty((w.capacity, N), dtype=torch.int16, device=dev)
+
+    def step():
+        for T in Ts:
+            ub.ub_set_active_shape(h, (T, H))
+            ub.ub_gemm_ag_chunked_fp8(h, w8, N, H, 1.0 / sx, 1.0 / sw, c_t, N, cfg, stream)
+
+    for _ in range(10):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(20):
+        step()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / 20
+    flops = sum(2.0 * T * H * N for T in Ts)
+    tf = flops / sec / 1e12
+    ub.ub_destroy(h)
+    ub.ub_destroy(hw)
+    return {"tflops": round(tf, 2), "ms_per_step": round(sec * 1e3, 4),
+            "pct_of_fp8_peak": round(100 * tf / MFMA_PEAK_FP8_TFLOPS, 2),
+            "quantize_gbs": round(3.0 * w.capacity * H / q_ms / 1e6, 1),
+            "note": "E4M3 operands, per-tensor scales, bf16 output; device-side chunk loop"}
 
 
 def cpu_baseline(q, min_seconds):

@@ -19,7 +19,8 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libub.so")
 
-SOURCES = ["ub_api.cpp", "ub_plan.cpp", "gemm_bf16.hip", "reduce_partials.hip"]
+SOURCES = ["ub_api.cpp", "ub_plan.cpp", "gemm_bf16.hip", "gemm_fp8.hip", "quantize_fp8.hip",
+           "reduce_partials.hip"]
 
 ARCH = "gfx950"
 COMMON = [

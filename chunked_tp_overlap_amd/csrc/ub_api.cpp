@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -32,7 +33,10 @@ struct ub_ctx {
   int64_t capacity = 0;
   int64_t hidden = 0;
   int32_t tp = 1;
-  uint16_t* ub = nullptr;
+  ub_dtype_t dtype = UB_DTYPE_BF16;
+  int64_t elem_bytes = 2;        // 2 (bf16) or 1 (fp8)
+  uint16_t* ub = nullptr;        // the buffer as bf16 elements
+  uint8_t* ub8 = nullptr;        // the same buffer as bytes (fp8 codes)
   size_t ub_bytes = 0;
   uint16_t* ws = nullptr;
   size_t ws_bytes = 0;
@@ -81,11 +85,17 @@ ub_status_t fail(ub_ctx* h, ub_status_t st, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+int64_t elem_bytes_of(ub_dtype_t dtype) { return dtype == UB_DTYPE_FP8_E4M3 ? 1 : 2; }
+
 ub_status_t check_registration(int64_t capacity, int64_t hidden, int32_t tp, ub_dtype_t dtype,
                                std::string* err) {
-  if (dtype != UB_DTYPE_BF16) {
-    *err = "only unquantized bf16 UserBuffers are supported";
+  if (dtype != UB_DTYPE_BF16 && dtype != UB_DTYPE_FP8_E4M3) {
+    *err = "UserBuffers are bf16 or fp8 E4M3";
     return UB_ERR_DTYPE;
+  }
+  if (dtype == UB_DTYPE_FP8_E4M3 && hidden % 16 != 0) {
+    *err = "an fp8 UserBuffer needs hidden to be a multiple of 16 (16-byte rows)";
+    return UB_ERR_INVALID_ARG;
   }
   if (capacity <= 0 || hidden <= 0) {
     *err = "capacity and hidden must be > 0";
@@ -231,6 +241,12 @@ ub_status_t join_streams(ub_ctx* h, hipStream_t caller, int S) {
   return UB_OK;
 }
 
+ub_status_t need_dtype(ub_ctx* h, ub_dtype_t want, const char* what) {
+  if (h->dtype == want) return UB_OK;
+  return fail(h, UB_ERR_DTYPE, "%s needs a %s UserBuffer", what,
+              want == UB_DTYPE_BF16 ? "bf16" : "fp8 E4M3");
+}
+
 ub_status_t check_cfg_common(ub_ctx* h, const ub_overlap_cfg_t* cfg) {
   if (!cfg) return fail(h, UB_ERR_INVALID_ARG, "cfg is NULL");
   if (cfg->reduce_order != UB_REDUCE_ASCENDING && cfg->reduce_order != UB_REDUCE_RING)
@@ -308,8 +324,10 @@ UB_API ub_status_t ub_required_bytes(int64_t capacity, int64_t hidden, int32_t t
   ub_status_t st = check_registration(capacity, hidden, tp_size, dtype, &err);
   if (st != UB_OK) return st;
   const size_t elems = static_cast<size_t>(capacity) * static_cast<size_t>(hidden);
-  if (ub_bytes) *ub_bytes = elems * 2;
-  if (rs_workspace_bytes) *rs_workspace_bytes = elems * 2 * static_cast<size_t>(tp_size);
+  if (ub_bytes) *ub_bytes = elems * static_cast<size_t>(elem_bytes_of(dtype));
+  // the reduce-scatter side (bf16 partials) exists for bf16 buffers only
+  if (rs_workspace_bytes)
+    *rs_workspace_bytes = dtype == UB_DTYPE_BF16 ? elems * 2 * static_cast<size_t>(tp_size) : 0;
   return UB_OK;
 }
 
@@ -321,12 +339,14 @@ UB_API ub_status_t ub_init(ub_handle_t* out, int64_t capacity, int64_t hidden, i
   std::string err;
   ub_status_t st = check_registration(capacity, hidden, tp_size, dtype, &err);
   if (st != UB_OK) return st;
-  const size_t need = static_cast<size_t>(capacity) * static_cast<size_t>(hidden) * 2;
+  const size_t elems = static_cast<size_t>(capacity) * static_cast<size_t>(hidden);
+  const size_t need = elems * static_cast<size_t>(elem_bytes_of(dtype));
   if (!ub_buf || !aligned16(ub_buf)) return UB_ERR_INVALID_ARG;
   if (ub_bytes < need) return UB_ERR_BUFFER_TOO_SMALL;
+  if (dtype != UB_DTYPE_BF16 && (rs_ws || rs_ws_bytes)) return UB_ERR_INVALID_ARG;
   if (rs_ws) {
     if (!aligned16(rs_ws)) return UB_ERR_INVALID_ARG;
-    if (rs_ws_bytes < need * static_cast<size_t>(tp_size)) return UB_ERR_BUFFER_TOO_SMALL;
+    if (rs_ws_bytes < elems * 2 * static_cast<size_t>(tp_size)) return UB_ERR_BUFFER_TOO_SMALL;
   } else if (rs_ws_bytes != 0) {
     return UB_ERR_INVALID_ARG;
   }
@@ -335,7 +355,10 @@ UB_API ub_status_t ub_init(ub_handle_t* out, int64_t capacity, int64_t hidden, i
   h->capacity = capacity;
   h->hidden = hidden;
   h->tp = tp_size;
+  h->dtype = dtype;
+  h->elem_bytes = elem_bytes_of(dtype);
   h->ub = static_cast<uint16_t*>(ub_buf);
+  h->ub8 = static_cast<uint8_t*>(ub_buf);
   h->ub_bytes = ub_bytes;
   h->ws = static_cast<uint16_t*>(rs_ws);
   h->ws_bytes = rs_ws_bytes;
@@ -409,9 +432,10 @@ UB_API ub_status_t ub_copy_in(ub_handle_t h, const void* src, int64_t rows, int6
   if (rows == 0) return UB_OK;
   ub_status_t st = ensure_device(h, 1);
   if (st != UB_OK) return st;
-  hipError_t e = hipMemcpyAsync(h->ub + row_offset * h->hidden, src,
-                                static_cast<size_t>(rows * h->hidden) * 2,
-                                hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream));
+  const int64_t row_bytes = h->hidden * h->elem_bytes;
+  hipError_t e = hipMemcpyAsync(h->ub8 + row_offset * row_bytes, src,
+                                static_cast<size_t>(rows * row_bytes), hipMemcpyDeviceToDevice,
+                                static_cast<hipStream_t>(stream));
   return e == hipSuccess ? UB_OK : hip_fail(h, e, "hipMemcpyAsync");
 }
 
@@ -502,7 +526,9 @@ ub_status_t ag_call(ub_ctx* h, const void* src, int src_on_host, const void* w, 
                     int64_t ldw, void* c, int64_t ldc, const ub_overlap_cfg_t* cfg,
                     ub_stream_t stream) {
   if (!h) return UB_ERR_NOT_INITIALIZED;
-  ub_status_t st = check_ag_call(h, w, n_cols, ldw, c, ldc, cfg);
+  ub_status_t st = need_dtype(h, UB_DTYPE_BF16, "this all-gather GEMM");
+  if (st != UB_OK) return st;
+  st = check_ag_call(h, w, n_cols, ldw, c, ldc, cfg);
   if (st != UB_OK) return st;
   if (src && (st = check_arrival(h, src, cfg)) != UB_OK) return st;
   const int64_t H = h->hidden;
@@ -596,8 +622,9 @@ UB_API ub_status_t ub_gemm_ag_arrival(ub_handle_t h, const void* src, int32_t sr
 UB_API ub_status_t ub_deliver_chunks(ub_handle_t h, const void* src, int32_t src_on_host,
                                      const ub_overlap_cfg_t* cfg, ub_stream_t stream) {
   if (!h) return UB_ERR_NOT_INITIALIZED;
-  ub_status_t st = check_cfg_common(h, cfg);
+  ub_status_t st = need_dtype(h, UB_DTYPE_BF16, "ub_deliver_chunks");
   if (st != UB_OK) return st;
+  if ((st = check_cfg_common(h, cfg)) != UB_OK) return st;
   if ((st = check_arrival(h, src, cfg)) != UB_OK) return st;
   if ((st = ubx::build_plan(h->T, h->tp, *cfg, UB_OP_AG, &h->plan, &h->last_error)) != UB_OK)
     return st;
@@ -611,12 +638,101 @@ UB_API ub_status_t ub_deliver_chunks(ub_handle_t h, const void* src, int32_t src
   return e == hipSuccess ? UB_OK : hip_fail(h, e, "copy stream join");
 }
 
+UB_API ub_status_t ub_quantize_in(ub_handle_t h, const void* src, int64_t rows,
+                                  int64_t row_offset, float scale, ub_stream_t stream) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  ub_status_t st = need_dtype(h, UB_DTYPE_FP8_E4M3, "ub_quantize_in");
+  if (st != UB_OK) return st;
+  if (!src || !aligned16(src)) return fail(h, UB_ERR_INVALID_ARG, "src must be 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(h, UB_ERR_INVALID_ARG, "scale must be finite");
+  if (rows < 0 || row_offset < 0 || row_offset + rows > h->T)
+    return fail(h, UB_ERR_INVALID_ARG,
+                "quantizing %lld rows at row %lld does not fit the active T=%lld",
+                (long long)rows, (long long)row_offset, (long long)h->T);
+  if (rows == 0) return UB_OK;
+  if ((st = ensure_device(h, 1)) != UB_OK) return st;
+  const int64_t H = h->hidden;
+  hipError_t e = ubx::launch_quantize_e4m3(static_cast<const uint16_t*>(src), H,
+                                           h->ub8 + row_offset * H, H, rows, H, scale,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? UB_OK : hip_fail(h, e, "quantize launch");
+}
+
+UB_API ub_status_t ub_gemm_ag_chunked_fp8(ub_handle_t h, const void* w, int64_t n_cols,
+                                          int64_t ldw, float scale_inv_a, float scale_inv_w,
+                                          void* c, int64_t ldc, const ub_overlap_cfg_t* cfg,
+                                          ub_stream_t stream) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  ub_status_t st = need_dtype(h, UB_DTYPE_FP8_E4M3, "ub_gemm_ag_chunked_fp8");
+  if (st != UB_OK) return st;
+  if ((st = check_cfg_common(h, cfg)) != UB_OK) return st;
+  const int64_t H = h->hidden;
+  if (!w || !c || !aligned16(w) || !aligned16(c))
+    return fail(h, UB_ERR_INVALID_ARG, "w and c must be non-NULL and 16-byte aligned");
+  if (n_cols <= 0 || n_cols % 8 != 0 || n_cols > INT32_MAX)
+    return fail(h, UB_ERR_INVALID_ARG, "n_cols=%lld must be > 0 and a multiple of 8",
+                (long long)n_cols);
+  if (ldw < H || ldw % 16 != 0)
+    return fail(h, UB_ERR_INVALID_ARG, "ldw=%lld must be >= hidden=%lld and a multiple of 16",
+                (long long)ldw, (long long)H);
+  if ((st = check_ld(h, "ldc", ldc, n_cols)) != UB_OK) return st;
+  if (!std::isfinite(scale_inv_a) || !std::isfinite(scale_inv_w))
+    return fail(h, UB_ERR_INVALID_ARG, "scales must be finite");
+  if (H % ubx::kGemmF8KStep != 0)
+    return fail(h, UB_ERR_UNSUPPORTED, "hidden=%lld must be a multiple of %d", (long long)H,
+                ubx::kGemmF8KStep);
+  ubx::GemmF8Args g{};
+  g.a = h->ub8;
+  g.lda = H;
+  g.b = static_cast<const uint8_t*>(w);
+  g.ldb = ldw;
+  g.c = static_cast<uint16_t*>(c);
+  g.ldc = ldc;
+  g.n = static_cast<int32_t>(n_cols);
+  g.k = static_cast<int32_t>(H);
+  g.scale = scale_inv_a * scale_inv_w;  // one fp32 product
+  if (!ubx::gemm_fp8_shape_supported(g)) return fail(h, UB_ERR_UNSUPPORTED, "ldw too large");
+  if ((st = ubx::build_plan(h->T, h->tp, *cfg, UB_OP_AG, &h->plan, &h->last_error)) != UB_OK)
+    return st;
+  hipStream_t caller = static_cast<hipStream_t>(stream);
+  if (cfg->atomic_gemm) {
+    ubx::GemmUnits units;
+    if ((st = plan_units(h, &units)) != UB_OK) return st;
+    if ((st = ensure_device(h, 1)) != UB_OK) return st;
+    g.concurrency = 1;
+    return timed_launch(h, caller, 0, 2.0 * h->T * H * n_cols,
+                        double(h->T * H + H * n_cols + 2 * h->T * n_cols),
+                        [&] { return ubx::launch_gemm_fp8_units(g, units, caller); },
+                        "fp8 GEMM launch");
+  }
+  const int S = h->plan.n_streams;
+  if ((st = ensure_device(h, S)) != UB_OK) return st;
+  if ((st = fork_streams(h, caller, S)) != UB_OK) return st;
+  g.concurrency = S;
+  for (const ub_plan_unit_t& u : h->plan.units) {
+    const int64_t rows = u.row1 - u.row0;
+    if (rows <= 0) continue;
+    if (rows > kMaxRowsPerUnit) return fail(h, UB_ERR_UNSUPPORTED, "unit too large");
+    hipStream_t s = u.stream == 0 ? caller : h->streams[u.stream];
+    ubx::GemmUnits one;
+    one.n = 1;
+    one.row0[0] = static_cast<int32_t>(u.row0);
+    one.rows[0] = static_cast<int32_t>(rows);
+    st = timed_launch(h, s, 0, 2.0 * rows * H * n_cols,
+                      double(rows * H + H * n_cols + 2 * rows * n_cols),
+                      [&] { return ubx::launch_gemm_fp8_units(g, one, s); }, "fp8 GEMM launch");
+    if (st != UB_OK) return st;
+  }
+  return join_streams(h, caller, S);
+}
+
 UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, int64_t lda,
                                       const void* w, int64_t ldw, void* out, int64_t ldo,
                                       const ub_overlap_cfg_t* cfg, ub_stream_t stream) {
   if (!h) return UB_ERR_NOT_INITIALIZED;
-  ub_status_t st = check_cfg_common(h, cfg);
+  ub_status_t st = need_dtype(h, UB_DTYPE_BF16, "the reduce-scatter GEMM");
   if (st != UB_OK) return st;
+  if ((st = check_cfg_common(h, cfg)) != UB_OK) return st;
   if (!h->ws) return fail(h, UB_ERR_NOT_INITIALIZED, "no reduce-scatter workspace registered");
   if (!a || !w || !out) return fail(h, UB_ERR_INVALID_ARG, "a, w and out must be non-NULL");
   if (!aligned16(a) || !aligned16(w) || !aligned16(out))
@@ -732,6 +848,7 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
 UB_API ub_status_t ub_reduce_partials(ub_handle_t h, void* out, int64_t ldo,
                                       int32_t reduce_order, ub_stream_t stream) {
   if (!h) return UB_ERR_NOT_INITIALIZED;
+  if (need_dtype(h, UB_DTYPE_BF16, "ub_reduce_partials") != UB_OK) return UB_ERR_DTYPE;
   if (!h->ws) return fail(h, UB_ERR_NOT_INITIALIZED, "no reduce-scatter workspace registered");
   if (!out || !aligned16(out)) return fail(h, UB_ERR_INVALID_ARG, "out must be 16-byte aligned");
   if (reduce_order != UB_REDUCE_ASCENDING && reduce_order != UB_REDUCE_RING)

@@ -56,6 +56,27 @@ hipError_t launch_gemm_bf16_units(const GemmArgs& g, const GemmUnits& u, hipStre
 
 // out[r, c] = bf16( sum_{s < nslots} float(parts[s*slot_stride + r*ldp + c]) ), ascending s.
 // cols % 8 == 0, ldp/ldo % 8 == 0, pointers 16-byte aligned.
+// FP8 (E4M3) all-gather GEMM: C [*, n] bf16 = bf16(scale * A B^T) with A [*, k] and
+// B [n, k] E4M3 codes (row strides in bytes), units of rows as for launch_gemm_bf16_units.
+constexpr int kGemmF8KStep = 64;
+struct GemmF8Args {
+  const uint8_t* a;
+  int64_t lda;
+  const uint8_t* b;
+  int64_t ldb;
+  uint16_t* c;
+  int64_t ldc;
+  int32_t n, k;
+  float scale;
+  int concurrency;
+};
+bool gemm_fp8_shape_supported(const GemmF8Args& g);
+hipError_t launch_gemm_fp8_units(const GemmF8Args& g, const GemmUnits& u, hipStream_t stream);
+
+// bf16 rows -> E4M3 rows: dst[r, c] = sat(RNE_e4m3(fp32(src[r, c] * scale))).
+hipError_t launch_quantize_e4m3(const uint16_t* src, int64_t lds, uint8_t* dst, int64_t ldd,
+                                int64_t rows, int64_t cols, float scale, hipStream_t stream);
+
 // Partial-sum reduction of `rows` x `cols` elements: slot s at parts + s * slot_stride
 // (row stride ldp), result at out (row stride ldo).  ring != 0: ring order with a bf16
 // rounding per hop, where local row i is global row row0 + i of shard

@@ -42,8 +42,8 @@ REDUCE_ORDERS = {"ascending": UB_REDUCE_ASCENDING, "ring": UB_REDUCE_RING}
 EXPORTS = (
     "ub_overlap_cfg_default", "ub_required_bytes", "ub_init", "ub_set_active_shape",
     "ub_get_active_shape", "ub_get_capacity_shape", "ub_get_plan", "ub_copy_in",
-    "ub_gemm_ag_chunked", "ub_gemm_ag_arrival", "ub_deliver_chunks", "ub_gemm_rs_chunked",
-    "ub_reduce_partials",
+    "ub_gemm_ag_chunked", "ub_gemm_ag_arrival", "ub_deliver_chunks", "ub_quantize_in",
+    "ub_gemm_ag_chunked_fp8", "ub_gemm_rs_chunked", "ub_reduce_partials",
     "ub_set_kernel_timing", "ub_get_kernel_timing", "ub_destroy", "ub_status_string",
     "ub_last_error",
 )
@@ -91,6 +91,9 @@ _sig = {
     "ub_gemm_ag_chunked": (_I32, [_H, _P, _I64, _I64, _P, _I64, _CFGP, _P]),
     "ub_gemm_ag_arrival": (_I32, [_H, _P, _I32, _P, _I64, _I64, _P, _I64, _CFGP, _P]),
     "ub_deliver_chunks": (_I32, [_H, _P, _I32, _CFGP, _P]),
+    "ub_quantize_in": (_I32, [_H, _P, _I64, _I64, ctypes.c_float, _P]),
+    "ub_gemm_ag_chunked_fp8": (_I32, [_H, _P, _I64, _I64, ctypes.c_float, ctypes.c_float, _P,
+                                      _I64, _CFGP, _P]),
     "ub_gemm_rs_chunked": (_I32, [_H, _P, _I64, _I64, _P, _I64, _P, _I64, _CFGP, _P]),
     "ub_reduce_partials": (_I32, [_H, _P, _I64, _I32, _P]),
     "ub_set_kernel_timing": (_I32, [_H, _I32]),
@@ -230,6 +233,16 @@ def ub_gemm_ag_arrival(h, src, w, n_cols, ldw, c, ldc, cfg, stream=None):
 def ub_deliver_chunks(h, src, cfg, stream=None):
     _check(_lib.ub_deliver_chunks(h, _ptr(src), _on_host(src), ctypes.byref(cfg),
                                   _stream(stream)), h)
+
+
+def ub_quantize_in(h, src, rows, row_offset, scale, stream=None):
+    _check(_lib.ub_quantize_in(h, _ptr(src), rows, row_offset, float(scale), _stream(stream)), h)
+
+
+def ub_gemm_ag_chunked_fp8(h, w, n_cols, ldw, scale_inv_a, scale_inv_w, c, ldc, cfg, stream=None):
+    _check(_lib.ub_gemm_ag_chunked_fp8(h, _ptr(w), n_cols, ldw, float(scale_inv_a),
+                                       float(scale_inv_w), _ptr(c), ldc, ctypes.byref(cfg),
+                                       _stream(stream)), h)
 
 
 def ub_gemm_rs_chunked(h, a, k, lda, w, ldw, out, ldo, cfg, stream=None):

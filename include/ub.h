@@ -86,9 +86,12 @@ typedef enum {
   UB_ERR_HIP = 11               /* a HIP runtime call failed; see ub_last_error */
 } ub_status_t;
 
-/* Element type of a UserBuffer.  Only UB_DTYPE_BF16 is accepted: the pages scope the
- * prototype to unquantized 2-byte bf16 buffers ([TE#3564] "Implementation approach",
- * last paragraph); the others are rejected with UB_ERR_DTYPE. */
+/* Element type of a UserBuffer.  The pages scope the prototype to unquantized 2-byte
+ * bf16 buffers and name quantized (FP8) ones as outside that first scope ([TE#3564]
+ * "Implementation approach", last paragraph).  UB_DTYPE_BF16 is the main path;
+ * UB_DTYPE_FP8_E4M3 is the extension to quantized buffers (OCP E4M3 codes, one byte per
+ * element, all-gather side only: ub_quantize_in, ub_gemm_ag_chunked_fp8).  FP16 and E5M2
+ * are rejected with UB_ERR_DTYPE. */
 typedef enum {
   UB_DTYPE_BF16 = 0,
   UB_DTYPE_FP16 = 1,
@@ -168,23 +171,26 @@ typedef struct {
 UB_API void ub_overlap_cfg_default(ub_overlap_cfg_t* cfg);
 
 /* Bytes the caller must allocate for a registration of [capacity, hidden] over
- * tp_size ranks: the UB itself (capacity * hidden * 2) and the reduce-scatter workspace
- * of tp_size partial slots (tp_size * capacity * hidden * 2).  Same validation as
- * ub_init.  Either output pointer may be NULL. */
+ * tp_size ranks: the UB itself (capacity * hidden * element size: 2 for bf16, 1 for
+ * fp8) and the reduce-scatter workspace of tp_size bf16 partial slots
+ * (tp_size * capacity * hidden * 2; 0 for fp8, which has no reduce-scatter side).  Same
+ * validation as ub_init.  Either output pointer may be NULL. */
 UB_API ub_status_t ub_required_bytes(int64_t capacity, int64_t hidden, int32_t tp_size,
                                      ub_dtype_t dtype, size_t* ub_bytes,
                                      size_t* rs_workspace_bytes);
 
 /* Register a UserBuffer at its maximum token capacity ([TE#3564] "Proposed API":
  * initialize at [max_tokens, hidden_size] with tp_size, unquantized, bf16).
- *   capacity, hidden  > 0; hidden % 8 == 0; capacity % tp_size == 0 (so that the initial
- *                     active shape, which equals the capacity shape, is valid).
+ *   capacity, hidden  > 0; hidden % 8 == 0 (bf16) or % 16 == 0 (fp8); capacity %
+ *                     tp_size == 0 (so that the initial active shape, which equals the
+ *                     capacity shape, is valid).
  *   tp_size           1 .. UB_MAX_TP.
- *   dtype             UB_DTYPE_BF16, else UB_ERR_DTYPE.
- *   ub_buf, ub_bytes  device memory of at least capacity*hidden*2 bytes (16-byte
- *                     aligned), else UB_ERR_BUFFER_TOO_SMALL / UB_ERR_INVALID_ARG.
+ *   dtype             UB_DTYPE_BF16 or UB_DTYPE_FP8_E4M3, else UB_ERR_DTYPE.
+ *   ub_buf, ub_bytes  device memory of at least capacity*hidden*element-size bytes
+ *                     (16-byte aligned), else UB_ERR_BUFFER_TOO_SMALL / UB_ERR_INVALID_ARG.
  *   rs_ws, rs_ws_bytes reduce-scatter workspace of at least tp_size*capacity*hidden*2
- *                     bytes, or NULL/0 when the reduce-scatter side is not used.
+ *                     bytes, or NULL/0 when the reduce-scatter side is not used (always
+ *                     NULL/0 for fp8, else UB_ERR_INVALID_ARG).
  * Records the pointers and sizes; allocates no device memory and makes no HIP call
  * (streams and events are created on the first GEMM call, on the device current then).
  * On success *out is a new handle whose active shape is [capacity, hidden]. */
@@ -213,7 +219,8 @@ UB_API ub_status_t ub_get_plan(ub_handle_t h, const ub_overlap_cfg_t* cfg, ub_op
                                ub_plan_unit_t* out, int32_t max_units, int32_t* n_units,
                                int32_t* n_streams);
 
-/* Copy `rows` rows of [*, hidden] bf16 from device memory `src` (row stride hidden) into
+/* Copy `rows` rows of [*, hidden] elements (bf16, or fp8 codes for an fp8 buffer) from
+ * device memory `src` (row stride hidden) into
  * active rows [row_offset, row_offset + rows) of the UB, asynchronously on `stream`
  * (this is where a rank's own shard enters the buffer).  The copy-size check is against
  * the active T, not the capacity ([TE#3564]: copy-size checks use the active element
@@ -229,10 +236,39 @@ UB_API ub_status_t ub_copy_in(ub_handle_t h, const void* src, int64_t rows,
  * into the plan's units; unit u is one GEMM reading the UB at byte offset
  * row0_u * hidden * 2.  Reads no UB byte beyond T*hidden elements; writes only C rows
  * [0, T).  n_cols, ldw, ldc multiples of 8; hidden a multiple of 64 (else
- * UB_ERR_UNSUPPORTED).  aggregate is honoured; W and C are caller memory. */
+ * UB_ERR_UNSUPPORTED).  aggregate is honoured; W and C are caller memory.  Needs a bf16
+ * handle, as do ub_gemm_ag_arrival, ub_deliver_chunks, ub_gemm_rs_chunked and
+ * ub_reduce_partials (else UB_ERR_DTYPE). */
 UB_API ub_status_t ub_gemm_ag_chunked(ub_handle_t h, const void* w, int64_t n_cols,
                                       int64_t ldw, void* c, int64_t ldc,
                                       const ub_overlap_cfg_t* cfg, ub_stream_t stream);
+
+/* FP8 (E4M3) UserBuffers: the extension to quantized buffers that [TE#3564]
+ * ("Implementation approach", last paragraph) leaves outside the first scope.  The pages
+ * give no format or scaling rule; the reading taken: OCP E4M3 codes (bias 7, 3 significand
+ * bits, largest finite 448, no infinities) with one scale per tensor.
+ *
+ * ub_quantize_in: rows [row_offset, row_offset + rows) of the fp8 UB receive
+ *   q = sat(RNE_e4m3(fp32(x * scale))) of the bf16 rows `src` ([rows, hidden] packed,
+ *   16-byte aligned device memory): one fp32 multiply, round to the nearest E4M3 value
+ *   with ties to even, magnitudes beyond 448 saturate to 448, NaN stays NaN.  The size
+ *   check is against the active T, as for ub_copy_in.  scale must be finite.  Needs an
+ *   fp8 handle (else UB_ERR_DTYPE).  Asynchronous on `stream`. */
+UB_API ub_status_t ub_quantize_in(ub_handle_t h, const void* src, int64_t rows,
+                                  int64_t row_offset, float scale, ub_stream_t stream);
+
+/* ub_gemm_ag_chunked_fp8: the all-gather-side chunked GEMM over an fp8 UB, with the same
+ * plan, options, streams and device-side chunk loop as ub_gemm_ag_chunked:
+ *   C[t, j] = bf16_rne( (scale_inv_a * scale_inv_w) * sum_k UB[t, k] * W[j, k] )
+ * for t < T, with fp32 accumulation and the two dequantization factors multiplied once in
+ * fp32.  W is [n_cols, hidden] E4M3 codes, row stride ldw bytes (>= hidden, multiple of
+ * 16; the weight stored N x K, as FP8 GEMMs take it); C is [T, n_cols] bf16 (ldc >= n_cols,
+ * multiple of 8).  hidden must be a multiple of 64 (else UB_ERR_UNSUPPORTED).  Needs an
+ * fp8 handle (else UB_ERR_DTYPE). */
+UB_API ub_status_t ub_gemm_ag_chunked_fp8(ub_handle_t h, const void* w, int64_t n_cols,
+                                          int64_t ldw, float scale_inv_a, float scale_inv_w,
+                                          void* c, int64_t ldc, const ub_overlap_cfg_t* cfg,
+                                          ub_stream_t stream);
 
 /* Arrival stand-in for the all-gather side ([TE#1344] "ring_exchange": the other ranks'
  * chunks arrive by point-to-point copies, "use_ce": on the Copy Engine, without compute

@@ -97,3 +97,11 @@ def ag_chunked_fp8(model_T, ub_codes, hidden, w_codes, n_cols, sa, sw, units):
         C[u.row0:u.row1] = bf16.encode_rne(dot * float(sa) * float(sw))
         written[u.row0:u.row1] += 1
     return C, written
+
+
+def ag_rows_fp8(a_codes_rows, w_codes, n_cols, sa, sw):
+    """All-gather GEMM output for the given rows of the quantized UserBuffer (rows are
+    independent): bf16 bits of RNE_bf16(sum_k a[t, k] * w[j, k] * sa * sw)."""
+    A = decode(a_codes_rows)
+    W = decode(np.asarray(w_codes)[:n_cols, :A.shape[1]])
+    return bf16.encode_rne(((A @ W.T) + 0.0) * float(sa) * float(sw))

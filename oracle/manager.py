@@ -52,7 +52,7 @@ class ModelError(Exception):
 
 def check_registration(capacity, hidden, tp_size, dtype="bf16"):
     """Status of registering a ``[capacity, hidden]`` buffer for tp_size ranks."""
-    if dtype != "bf16":
+    if dtype not in ("bf16", "fp8_e4m3"):
         return DTYPE
     if capacity <= 0 or hidden <= 0 or tp_size < 1:
         return INVALID_ARG

@@ -54,9 +54,20 @@ def _handle(capacity, hidden, tp, ws=True):
 
 def test_required_bytes_and_registration_errors():
     assert ub.ub_required_bytes(8192, 4096, 8) == (8192 * 4096 * 2, 8 * 8192 * 4096 * 2)
+    assert ub.ub_required_bytes(512, 256, 2, ub.UB_DTYPE_FP8_E4M3) == (512 * 256, 0)
+    for dt in (ub.UB_DTYPE_FP8_E5M2, ub.UB_DTYPE_FP16, 9):
+        with pytest.raises(ub.UBError) as e:
+            ub.ub_required_bytes(512, 256, 2, dt)
+        assert e.value.name == "UB_ERR_DTYPE"
+    with pytest.raises(ub.UBError) as e:  # fp8 rows of 16 bytes
+        ub.ub_required_bytes(512, 264, 2, ub.UB_DTYPE_FP8_E4M3)
+    assert e.value.name == "UB_ERR_INVALID_ARG"
     with pytest.raises(ub.UBError) as e:
-        ub.ub_required_bytes(512, 256, 2, ub.UB_DTYPE_FP8_E4M3)
-    assert e.value.name == "UB_ERR_DTYPE"
+        ub.ub_init(512, 256, 2, ub.UB_DTYPE_FP8_E4M3, FAKE, 512 * 256 - 1)
+    assert e.value.name == "UB_ERR_BUFFER_TOO_SMALL"
+    with pytest.raises(ub.UBError) as e:  # no reduce-scatter workspace for fp8
+        ub.ub_init(512, 256, 2, ub.UB_DTYPE_FP8_E4M3, FAKE, 512 * 256, FAKE, 8 << 20)
+    assert e.value.name == "UB_ERR_INVALID_ARG"
     with pytest.raises(ub.UBError) as e:
         ub.ub_required_bytes(510, 256, 4)
     assert e.value.name == "UB_ERR_TP_DIVISIBILITY"
@@ -224,6 +235,49 @@ def test_arrival_argument_errors_before_any_hip_call():
         assert st("ub_deliver_chunks", h, FAKE, 0, ctypes.byref(many), None) == "UB_ERR_UNSUPPORTED"
         assert st("ub_deliver_chunks", h, FAKE, 0, None, None) == "UB_ERR_INVALID_ARG"
         assert st("ub_deliver_chunks", None, FAKE, 0, cp, None) == "UB_ERR_NOT_INITIALIZED"
+    finally:
+        ub.ub_destroy(h)
+
+
+def test_fp8_handle_argument_errors_before_any_hip_call():
+    h = ub.ub_init(512, 256, 2, ub.UB_DTYPE_FP8_E4M3, FAKE, 512 * 256)
+    hb = _handle(512, 256, 2)
+    try:
+        def st(name, *args):
+            return ub.STATUS[ub.raw_call(name, *args)]
+        cfg = ub.make_cfg("ring_exchange", 2)
+        cp = ctypes.byref(cfg)
+        f = ctypes.c_float
+        # bf16-only entry points refuse an fp8 buffer, and the reverse
+        assert st("ub_gemm_ag_chunked", h, FAKE, 384, 384, FAKE, 384, cp, None) == "UB_ERR_DTYPE"
+        assert st("ub_gemm_ag_arrival", h, FAKE, 0, FAKE, 384, 384, FAKE, 384, cp, None) == "UB_ERR_DTYPE"
+        assert st("ub_deliver_chunks", h, FAKE, 0, cp, None) == "UB_ERR_DTYPE"
+        assert st("ub_gemm_rs_chunked", h, FAKE, 256, 256, FAKE, 256, FAKE, 256, cp, None) == "UB_ERR_DTYPE"
+        assert st("ub_reduce_partials", h, FAKE, 256, 0, None) == "UB_ERR_DTYPE"
+        assert st("ub_quantize_in", hb, FAKE, 1, 0, f(1.0), None) == "UB_ERR_DTYPE"
+        assert st("ub_gemm_ag_chunked_fp8", hb, FAKE, 384, 256, f(1), f(1), FAKE, 384, cp, None) == "UB_ERR_DTYPE"
+        # quantize: alignment, finite scale, size check against the active T
+        ub.ub_set_active_shape(h, (256, 256))
+        assert st("ub_quantize_in", h, FAKE + 8, 1, 0, f(1.0), None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_quantize_in", h, FAKE, 1, 0, f(float("inf")), None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_quantize_in", h, FAKE, 129, 128, f(1.0), None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_quantize_in", h, FAKE, 0, 256, f(1.0), None) == "UB_OK"
+        # fp8 GEMM: weight row stride >= hidden and a multiple of 16, columns multiple of 8
+        assert st("ub_gemm_ag_chunked_fp8", h, FAKE, 384, 240, f(1), f(1), FAKE, 384, cp, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_gemm_ag_chunked_fp8", h, FAKE, 384, 264, f(1), f(1), FAKE, 384, cp, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_gemm_ag_chunked_fp8", h, FAKE, 380, 256, f(1), f(1), FAKE, 384, cp, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_gemm_ag_chunked_fp8", h, FAKE, 384, 256, f(1), f(1), FAKE, 376, cp, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_gemm_ag_chunked_fp8", h, FAKE, 384, 256, f(float("nan")), f(1), FAKE, 384, cp, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_gemm_ag_chunked_fp8", h, FAKE, 384, 256, f(1), f(1), FAKE, 384, None, None) == "UB_ERR_INVALID_ARG"
+    finally:
+        ub.ub_destroy(h)
+        ub.ub_destroy(hb)
+    h = ub.ub_init(64, 80, 1, ub.UB_DTYPE_FP8_E4M3, FAKE, 64 * 80)
+    try:  # hidden not a multiple of the 64-code k step
+        cfg = ub.make_cfg("bulk", 1)
+        st = ub.raw_call("ub_gemm_ag_chunked_fp8", h, FAKE, 8, 80, ctypes.c_float(1), ctypes.c_float(1),
+                         FAKE, 8, ctypes.byref(cfg), None)
+        assert ub.STATUS[st] == "UB_ERR_UNSUPPORTED"
     finally:
         ub.ub_destroy(h)
 

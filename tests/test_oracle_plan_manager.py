@@ -54,6 +54,8 @@ def test_active_shape_constraints(cap, hid, tp, shape, expected):
 def test_registration_rules():
     assert manager.check_registration(512, 256, 2) == manager.OK
     assert manager.check_registration(512, 256, 2, "fp8") == manager.DTYPE
+    assert manager.check_registration(512, 256, 2, "fp8_e5m2") == manager.DTYPE
+    assert manager.check_registration(512, 256, 2, "fp8_e4m3") == manager.OK
     assert manager.check_registration(0, 256, 2) == manager.INVALID_ARG
     assert manager.check_registration(512, 0, 2) == manager.INVALID_ARG
     assert manager.check_registration(512, 256, 0) == manager.INVALID_ARG
