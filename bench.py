@@ -13,7 +13,7 @@ The primary schedule is the device-side chunk loop (option atomic_gemm: one laun
 call whose workgroups walk the 8 ring chunks in ring order); the host loop of per-chunk
 launches on min(8, 3) streams is measured as well and reported under "modes".
 
-Prints one JSON line.  --profile-pass runs only a short stretch of the primary workload
+Prints one JSON line.  --profile-pass [qkv|reduce|fp8] runs only one kernel's timed region
 (and a copy kernel of known size) for rocprofv3.
 """
 
@@ -42,9 +42,12 @@ def parse_args():
                    help="minimum CPU-oracle baseline work (seconds)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
-    p.add_argument("--profile-pass", action="store_true",
-                   help="run only the primary timed region and its per-launch timing pass, then "
-                        "a 1 GiB copy (calibration of rocprofv3 byte counters)")
+    p.add_argument("--profile-pass", nargs="?", const="qkv", default=None,
+                   choices=["qkv", "reduce", "fp8"],
+                   help="for rocprofv3: run only one kernel's timed region and its per-launch "
+                        "timing pass (qkv: the primary bf16 GEMM; reduce: the fc2 reduction at "
+                        "T = 16384; fp8: the qkv step on an fp8 buffer), then a 1 GiB copy that "
+                        "calibrates the byte counters; print one JSON line")
     return p.parse_args()
 
 
@@ -134,6 +137,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
+    if args.profile_pass in ("reduce", "fp8"):
+        fn = profile_reduce if args.profile_pass == "reduce" else profile_fp8
+        res = fn(ub, wl, torch, np, dev, args.steps, args.warmup)
+        calibration_copy(torch, dev)
+        print(json.dumps(res), flush=True)
+        return
     q = Qkv(ub, wl, torch, np, dev)
     primary = q.cfg(atomic=True)
 
@@ -152,20 +161,17 @@ def main():
     avg_launch_us = gemm_stats["total_ms"] * 1e3 / max(1, gemm_stats["launches"])
 
     if args.profile_pass:
-        # a plain copy of 1 GiB (2^29 int16 -> 2^29 int16) that calibrates FETCH_SIZE / WRITE_SIZE
-        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
+        calibration_copy(torch, dev)
         ub.ub_destroy(q.h)
-        print(json.dumps({"profile_pass": True, "ms_per_step": round(sec * 1e3, 4),
+        print(json.dumps({"profile_pass": "qkv", "ms_per_step": round(sec * 1e3, 4),
                           "launches_per_step": len(q.Ts),
-                          "gemm_launches": (args.warmup + 2 * args.steps) * len(q.Ts),
-                          "warmup_launches": args.warmup * len(q.Ts),
+                          "launches": (args.warmup + 2 * args.steps) * len(q.Ts),
+                          "timed_launches": 2 * args.steps * len(q.Ts),
                           "avg_launch_us_hip_events": round(avg_launch_us, 3),
                           "avg_launch_gflop": round(gemm_stats["flops"] / max(1, gemm_stats["launches"]) / 1e9, 4),
                           "algorithmic_bytes_per_launch": round(gemm_stats["bytes"] / max(1, gemm_stats["launches"])),
-                          "gemm_src_hash": src_hash(GEMM_SRC)}), flush=True)
+                          "src_file": os.path.relpath(GEMM_SRC, ROOT),
+                          "src_hash": src_hash(GEMM_SRC)}), flush=True)
         return
 
     per_mb = q.per_microbatch(primary)
@@ -184,7 +190,7 @@ def main():
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if tr.get("gemm_src_hash") == src_hash(GEMM_SRC):
+        if tr.get("src_hash") == src_hash(GEMM_SRC):
             traffic = tr.get("qkv_gemm_bytes_per_launch")
     except (OSError, ValueError):
         pass
@@ -249,6 +255,98 @@ def main():
 
     ub.ub_destroy(q.h)
     print(json.dumps(result), flush=True)
+
+
+def calibration_copy(torch, dev):
+    """A plain device copy of exactly 1 GiB (2^29 int16 -> 2^29 int16): rocprofv3's
+    FETCH_SIZE / WRITE_SIZE of it calibrate the counters of the profiled kernels."""
+    src = torch.ones(1 << 29, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def _instrumented(ub, h, torch, fn, reps, kind):
+    """Run fn() reps times with the library's per-launch HIP events; (launches, mean us,
+    mean GFLOP, mean algorithmic bytes) of launches of `kind` (0 GEMM, 1 reduction)."""
+    ub.ub_set_kernel_timing(h, True)
+    ub.ub_get_kernel_timing(h)
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    stats = ub.ub_get_kernel_timing(h)[kind]
+    ub.ub_set_kernel_timing(h, False)
+    n = max(1, stats["launches"])
+    return stats["launches"], stats["total_ms"] * 1e3 / n, stats["flops"] / n / 1e9, stats["bytes"] / n
+
+
+def profile_reduce(ub, wl, torch, np, dev, steps, warmup):
+    """The fc2 reduction at T = 16384 (8 bf16 partial slots of [16384, 4096]): warm-up
+    launches, timed launches, then the same with per-launch events; ascending order first,
+    then ring order."""
+    w = wl.fc2()
+    ra, rw, _ = w.seeds()
+    T = wl.FC2_TOKENS[-1]
+    ub_bytes, ws_bytes = ub.ub_required_bytes(w.capacity, w.hidden, w.tp)
+    ub_t = torch.empty(w.capacity * w.hidden, dtype=torch.int16, device=dev)
+    ws_t = torch.empty(w.tp * w.capacity * w.hidden, dtype=torch.int16, device=dev)
+    a_t = torch.from_numpy(wl.activations(w, T, ra).view(np.int16)).to(dev)
+    w_t = torch.from_numpy(wl.weights(w, rw).view(np.int16)).to(dev)
+    o_t = torch.empty((w.capacity, w.hidden), dtype=torch.int16, device=dev)
+    h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes, ws_t, ws_bytes)
+    ub.ub_set_active_shape(h, (T, w.hidden))
+    ub.ub_gemm_rs_chunked(h, a_t, w.k, w.k, w_t, w.hidden, o_t, w.hidden,
+                          ub.make_cfg(w.method, w.num_splits, atomic_gemm=True))
+    stream = torch.cuda.current_stream()
+    out = {"profile_pass": "reduce", "T": T, "launches_per_order": warmup + 2 * steps}
+    for order in ("ascending", "ring"):
+        fn = lambda: ub.ub_reduce_partials(h, o_t, w.hidden, order, stream)
+        for _ in range(warmup + steps):
+            fn()
+        n, us, _, nbytes = _instrumented(ub, h, torch, fn, steps, 1)
+        out[order] = {"avg_launch_us_hip_events": round(us, 3), "algorithmic_bytes_per_launch": round(nbytes),
+                      "gbs_hip_events": round(nbytes / us / 1e3, 1), "timed_launches": 2 * steps}
+    out["src_file"] = os.path.relpath(REDUCE_SRC, ROOT)
+    out["src_hash"] = src_hash(REDUCE_SRC)
+    ub.ub_destroy(h)
+    return out
+
+
+def profile_fp8(ub, wl, torch, np, dev, steps, warmup):
+    """The qkv step on an fp8 buffer (see qkv_fp8): warm-up steps, timed steps, then the
+    same with per-launch events."""
+    w = wl.qkv()
+    ra, rw, rt = w.seeds()
+    Ts, _ = wl.qkv_pack_tokens(rt)
+    H, N = w.hidden, w.n_cols
+    x = torch.from_numpy(wl.activations(w, w.capacity, ra).view(np.int16)).to(dev)
+    wt = torch.from_numpy(wl.weights(w, rw).view(np.int16)).to(dev)
+    sx = 448.0 / float(x.view(torch.bfloat16).float().abs().max())
+    sw = 448.0 / float(wt.view(torch.bfloat16).float().abs().max())
+    ub_t = torch.empty(w.capacity * H, dtype=torch.uint8, device=dev)
+    h = ub.ub_init(w.capacity, H, w.tp, ub.UB_DTYPE_FP8_E4M3, ub_t, w.capacity * H)
+    w8 = torch.empty(N * H, dtype=torch.uint8, device=dev)
+    hw = ub.ub_init(N, H, 1, ub.UB_DTYPE_FP8_E4M3, w8, N * H)
+    ub.ub_quantize_in(hw, wt.t().contiguous(), N, 0, sw)
+    ub.ub_quantize_in(h, x, w.capacity, 0, sx)
+    cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, w.aggregate, True)
+    c_t = torch.empty((w.capacity, N), dtype=torch.int16, device=dev)
+
+    def step():
+        for T in Ts:
+            ub.ub_set_active_shape(h, (T, H))
+            ub.ub_gemm_ag_chunked_fp8(h, w8, N, H, 1.0 / sx, 1.0 / sw, c_t, N, cfg)
+
+    for _ in range(warmup + steps):
+        step()
+    n, us, gflop, nbytes = _instrumented(ub, h, torch, step, steps, 0)
+    ub.ub_destroy(h)
+    ub.ub_destroy(hw)
+    src = os.path.join(ROOT, "chunked_tp_overlap_amd", "csrc", "gemm_fp8.hip")
+    return {"profile_pass": "fp8", "launches": (warmup + 2 * steps) * len(Ts),
+            "timed_launches": 2 * steps * len(Ts), "avg_launch_us_hip_events": round(us, 3),
+            "avg_launch_gflop": round(gflop, 4), "algorithmic_bytes_per_launch": round(nbytes),
+            "src_file": os.path.relpath(src, ROOT), "src_hash": src_hash(src)}
 
 
 def _time_calls(fn, torch, stream, reps):

@@ -1,14 +1,19 @@
-"""Summarise rocprofv3 CSV output of ``bench.py --profile-pass`` into a short text report and
-the per-launch HBM traffic figure that bench.py reports beside its roofline.
+"""Summarise rocprofv3 CSV output of ``bench.py --profile-pass [qkv|reduce|fp8]`` into a short
+text report, and (for the primary GEMM) the per-launch HBM traffic figure that bench.py
+reports beside its roofline.
 
-Three rocprofv3 runs of the same command feed it (a kernel trace with statistics, then one
-counter pass for FETCH_SIZE and one for WRITE_SIZE); the profile pass ends with a plain
-1 GiB device copy whose true traffic is known (2^30 bytes read, 2^30 written), and each
-counter is scaled by (known bytes / counted bytes) of that copy before it is applied to the
-GEMM's dispatches.
+Three rocprofv3 runs of the same command feed it: a kernel trace with statistics, then one
+counter pass for FETCH_SIZE and one for WRITE_SIZE.  Each profile pass ends with a plain
+1 GiB device copy whose true traffic is known (2^30 bytes read, 2^30 written); each counter
+is scaled by (known bytes / counted bytes) of that copy before it is applied to the
+kernel's dispatches.
 
     python -m chunked_tp_overlap_amd.rocprof_summary --kt DIR --fetch DIR --write DIR \\
-        --bench-json FILE --kernel gemm_bf16_pingpong --out profiles/x.md --traffic profiles/t.json
+        --bench-json FILE [--key K] --kernel SUBSTRING --out profiles/x.md [--traffic FILE]
+
+--key selects a sub-object of the profile pass's JSON line (the reduce pass reports the
+ascending and the ring order separately).  The timed launches are the last
+`timed_launches` dispatches of the kernel in the trace.
 """
 
 import argparse
@@ -34,13 +39,17 @@ def _rows(path):
 
 
 def counter_means(dirname, counter, kernel):
-    """Mean of `counter` (KiB) over the dispatches of `kernel` and of the runtime's copy."""
+    """Mean of `counter` (KiB) over the dispatches of `kernel`, and its value for the copy."""
     rows = [r for r in _rows(_one(dirname, "_counter_collection.csv")) if r["Counter_Name"] == counter]
     mine = [float(r["Counter_Value"]) for r in rows if kernel in r["Kernel_Name"]]
+    # the calibration copy is the last and largest runtime copy of the pass (host-to-device
+    # input uploads may show up as smaller copies before it)
     copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
-    if not mine or len(copy) != 1:
+    if not mine or not copy:
         raise SystemExit(f"{counter}: {len(mine)} dispatches of {kernel}, {len(copy)} copies")
-    return statistics.fmean(mine), len(mine), copy[0]
+    if copy[-1] != max(copy):
+        raise SystemExit(f"{counter}: the last copy is not the largest: {copy}")
+    return statistics.fmean(mine), len(mine), copy[-1]
 
 
 def main():
@@ -49,31 +58,37 @@ def main():
     p.add_argument("--fetch", required=True, help="rocprofv3 --pmc FETCH_SIZE output directory")
     p.add_argument("--write", required=True, help="rocprofv3 --pmc WRITE_SIZE output directory")
     p.add_argument("--bench-json", required=True, help="the JSON line the profiled command printed")
+    p.add_argument("--key", default=None, help="sub-object of the JSON line for this kernel")
     p.add_argument("--kernel", required=True, help="substring of the kernel name")
-    p.add_argument("--command", default="", help="the rocprofv3 command lines, for the report")
+    p.add_argument("--title", default=None)
+    p.add_argument("--command", default="", help="the commands, for the report")
     p.add_argument("--out", required=True)
-    p.add_argument("--traffic", required=True)
+    p.add_argument("--traffic", default=None, help="write the traffic figure here (JSON)")
     a = p.parse_args()
 
     with open(a.bench_json) as f:
-        bench = json.loads([ln for ln in f if ln.startswith("{")][-1])
+        top = json.loads([ln for ln in f if ln.startswith("{")][-1])
+    bench = top[a.key] if a.key else top
 
-    stats = [r for r in _rows(_one(a.kt, "_kernel_stats.csv"))]
+    stats = _rows(_one(a.kt, "_kernel_stats.csv"))
     trace = _rows(_one(a.kt, "_kernel_trace.csv"))
     mine = [r for r in trace if a.kernel in r["Kernel_Name"]]
+    if not mine:
+        raise SystemExit(f"no dispatch of {a.kernel} in the trace")
     dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in mine]
     names = sorted({r["Kernel_Name"] for r in mine})
-    # launch order in the pass: warm-up steps, timed steps, the same steps with HIP events
-    after_warmup = dur[bench["warmup_launches"]:]
+    timed = dur[-bench["timed_launches"]:]
+    t_mean = statistics.fmean(timed)
+    ev = bench["avg_launch_us_hip_events"]
+    alg = bench["algorithmic_bytes_per_launch"]
 
     f_mean, f_n, f_copy = counter_means(a.fetch, "FETCH_SIZE", a.kernel)
     w_mean, w_n, w_copy = counter_means(a.write, "WRITE_SIZE", a.kernel)
     f_scale = (COPY_BYTES / 1024) / f_copy
     w_scale = (COPY_BYTES / 1024) / w_copy
     traffic = round(f_mean * 1024 * f_scale + w_mean * 1024 * w_scale)
-    alg = bench["algorithmic_bytes_per_launch"]
 
-    lines = [f"# rocprofv3 summary: {a.kernel}", ""]
+    lines = [f"# rocprofv3 summary: {a.title or a.kernel}", ""]
     if a.command:
         lines += ["Commands (from the repository root):", "", "```", a.command.strip(), "```", ""]
     lines += ["## Kernel trace (--kernel-trace --stats)", "",
@@ -81,40 +96,37 @@ def main():
     for r in stats:
         lines.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
-    k_all = statistics.fmean(dur)
     lines += ["", f"Kernel `{names[0] if len(names) == 1 else names}`:", "",
-              f"- launches traced: {len(dur)}; mean {k_all:.2f} us, median "
-              f"{statistics.median(dur):.2f} us",
-              f"- the {len(after_warmup)} launches after warm-up: mean "
-              f"{statistics.fmean(after_warmup):.2f} us",
-              f"- the profiled command's own per-launch HIP-event mean: "
-              f"{bench['avg_launch_us_hip_events']:.2f} us "
-              f"(trace mean after warm-up / events = "
-              f"{statistics.fmean(after_warmup) / bench['avg_launch_us_hip_events']:.3f})",
-              f"- algorithmic work per launch: {bench['avg_launch_gflop']:.3f} GFLOP, "
-              f"{alg / 1e6:.2f} MB; at the traced mean: "
-              f"{bench['avg_launch_gflop'] / k_all * 1e3:.1f} TFLOP/s", "",
-              "## HBM-side traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
+              f"- dispatches traced: {len(dur)}; mean {statistics.fmean(dur):.2f} us",
+              f"- the {len(timed)} timed dispatches (the last ones): mean {t_mean:.2f} us, "
+              f"median {statistics.median(timed):.2f} us",
+              f"- the profiled command's own per-launch HIP-event mean: {ev:.2f} us "
+              f"(trace / events = {t_mean / ev:.3f})",
+              f"- algorithmic bytes per launch: {alg / 1e6:.2f} MB, i.e. "
+              f"{alg / t_mean / 1e3:.1f} GB/s at the traced mean"]
+    if bench.get("avg_launch_gflop"):
+        lines.append(f"- algorithmic work per launch: {bench['avg_launch_gflop']:.3f} GFLOP, i.e. "
+                     f"{bench['avg_launch_gflop'] / t_mean * 1e3:.1f} TFLOP/s at the traced mean")
+    lines += ["", "## HBM-side traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
               "| counter | kernel KiB / dispatch (raw) | dispatches | 1 GiB copy (raw KiB) | scale | "
               "kernel MB / dispatch (scaled) |", "|---|---|---|---|---|---|",
               f"| FETCH_SIZE | {f_mean:.1f} | {f_n} | {f_copy:.1f} | {f_scale:.4f} | "
               f"{f_mean * 1024 * f_scale / 1e6:.2f} |",
               f"| WRITE_SIZE | {w_mean:.1f} | {w_n} | {w_copy:.1f} | {w_scale:.4f} | "
               f"{w_mean * 1024 * w_scale / 1e6:.2f} |", "",
-              f"Scaled traffic per launch: {traffic / 1e6:.2f} MB, against {alg / 1e6:.2f} MB "
+              f"Scaled traffic per dispatch: {traffic / 1e6:.2f} MB, against {alg / 1e6:.2f} MB "
               f"algorithmic ({traffic / alg:.2f}x).", "",
-              f"Kernel source hash (sha256[:16] of gemm_bf16.hip): {bench['gemm_src_hash']}"]
+              f"Kernel source: {top['src_file']}, sha256[:16] {top['src_hash']}"]
     with open(a.out, "w") as f:
         f.write("\n".join(lines) + "\n")
-    with open(a.traffic, "w") as f:
-        json.dump({"gemm_src_hash": bench["gemm_src_hash"], "kernel": a.kernel,
-                   "qkv_gemm_bytes_per_launch": traffic,
-                   "algorithmic_bytes_per_launch": alg,
-                   "fetch_kib_per_dispatch_raw": round(f_mean, 2), "fetch_scale": round(f_scale, 5),
-                   "write_kib_per_dispatch_raw": round(w_mean, 2), "write_scale": round(w_scale, 5),
-                   "trace_mean_us": round(k_all, 3),
-                   "hip_event_mean_us": bench["avg_launch_us_hip_events"]}, f, indent=1)
-        f.write("\n")
+    if a.traffic:
+        with open(a.traffic, "w") as f:
+            json.dump({"src_file": top["src_file"], "src_hash": top["src_hash"], "kernel": a.kernel,
+                       "qkv_gemm_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": alg,
+                       "fetch_kib_per_dispatch_raw": round(f_mean, 2), "fetch_scale": round(f_scale, 5),
+                       "write_kib_per_dispatch_raw": round(w_mean, 2), "write_scale": round(w_scale, 5),
+                       "trace_mean_us": round(t_mean, 3), "hip_event_mean_us": ev}, f, indent=1)
+            f.write("\n")
     print("\n".join(lines))
 
 
