@@ -39,6 +39,9 @@
 //  - Every tile shape uses the same instruction and the same ascending-K order, so an
 //    output element's bits depend only on its own A row and B column: chunking, row offset
 //    and tile choice never change a result.
+//  - In the device-side chunk loop the plan's units are re-cut at tile boundaries (each
+//    tile goes to the unit holding its last row), so a chunk that is not a multiple of the
+//    tile height does not leave a partly empty tile behind.
 //  - Workgroups are numbered so that consecutive tiles of a launch land on the same XCD
 //    (the dispatcher deals workgroups round-robin over the 8 XCDs, each with its own L2),
 //    and within an XCD tiles are walked in groups of rows that share B columns.
@@ -384,7 +387,8 @@ void gemm_bf16_pipelined(Params p) {
 }
 
 template <class C, class K>
-hipError_t launch(K kernel, const GemmArgs& g, const GemmUnits& u, hipStream_t stream) {
+hipError_t launch(K kernel, const GemmArgs& g, const GemmUnits& units, hipStream_t stream) {
+  const GemmUnits u = tile_aligned_units(units, C::BM);
   Params p{};
   p.a = g.a;
   p.b = g.b;
@@ -461,8 +465,7 @@ int choose_tile(const GemmArgs& g, const GemmUnits& u) {
   int best = kTile128x128;
   double best_cost = 1e300;
   for (const Opt& o : opts) {
-    int64_t rows = 0;
-    for (int i = 0; i < u.n; ++i) rows += (u.rows[i] + o.bm - 1) / o.bm;
+    const int64_t rows = row_tiles(u, o.bm);
     const int64_t tiles = rows * ((g.n + o.bn - 1) / o.bn) * g.batch;
     const int64_t slots = (int64_t)(share > 0 ? share : 1) * o.per_cu;
     const double rounds = (double)((tiles + slots - 1) / slots);

@@ -247,7 +247,8 @@ using F8_128x256 = F8Cfg<128, 256, 4, 2, 4>;  // 8 waves of 64x64
 constexpr int F8_D = 3;
 
 template <class C>
-hipError_t launch(const GemmF8Args& g, const GemmUnits& u, hipStream_t stream) {
+hipError_t launch(const GemmF8Args& g, const GemmUnits& units, hipStream_t stream) {
+  const GemmUnits u = tile_aligned_units(units, C::BM);
   F8Params p{};
   p.a = g.a;
   p.b = g.b;
@@ -291,9 +292,7 @@ bool use_128(const GemmF8Args& g, const GemmUnits& u) {
   }
   const int share = 256 / (g.concurrency > 1 ? g.concurrency : 1);
   auto cost = [&](int bm, double eff) {
-    int64_t rows = 0;
-    for (int i = 0; i < u.n; ++i) rows += (u.rows[i] + bm - 1) / bm;
-    const int64_t tiles = rows * ((g.n + 255) / 256);
+    const int64_t tiles = row_tiles(u, bm) * ((g.n + 255) / 256);
     const int64_t slots = share > 0 ? share : 1;
     return (double)((tiles + slots - 1) / slots) * bm * 256 / eff;
   };

@@ -54,6 +54,19 @@ struct GemmUnits {
 };
 hipError_t launch_gemm_bf16_units(const GemmArgs& g, const GemmUnits& u, hipStream_t stream);
 
+// Units of a device-side chunk loop re-cut for tiles of `bm` rows.  When the units tile a
+// contiguous row range (they do for every plan), the range is cut into bm-row tiles from
+// its first row, and each tile goes to the unit that holds its last row; the result lists,
+// in the units' order, each unit's run of tiles as one unit (units left without a tile are
+// dropped).  A tile then spans a unit boundary only where a unit is not a multiple of bm,
+// and no row is computed twice.  Such a tile also reads rows of the unit before its own in
+// row order, which a device-side wait for arriving chunks would have to cover; the
+// arrival stand-in therefore runs on the host-loop schedule only.  Units that do not
+// tile a contiguous range are returned unchanged.
+GemmUnits tile_aligned_units(const GemmUnits& u, int bm);
+// Row tiles of bm rows that a launch over `u` runs (after tile_aligned_units).
+int64_t row_tiles(const GemmUnits& u, int bm);
+
 // out[r, c] = bf16( sum_{s < nslots} float(parts[s*slot_stride + r*ldp + c]) ), ascending s.
 // cols % 8 == 0, ldp/ldo % 8 == 0, pointers 16-byte aligned.
 // FP8 (E4M3) all-gather GEMM: C [*, n] bf16 = bf16(scale * A B^T) with A [*, k] and

@@ -78,3 +78,56 @@ ub_status_t build_plan(int64_t T, int32_t tp, const ub_overlap_cfg_t& cfg, ub_op
 }
 
 }  // namespace ubx
+
+namespace ubx {
+
+namespace {
+
+// Whether the units tile one contiguous row range [*lo, *hi) without gaps or overlaps.
+bool contiguous(const GemmUnits& u, int64_t* lo, int64_t* hi) {
+  if (u.n <= 0) return false;
+  int32_t order[kMaxGemmUnits];
+  for (int i = 0; i < u.n; ++i) order[i] = i;
+  std::sort(order, order + u.n, [&](int32_t a, int32_t b) { return u.row0[a] < u.row0[b]; });
+  int64_t end = u.row0[order[0]];
+  *lo = end;
+  for (int i = 0; i < u.n; ++i) {
+    const int k = order[i];
+    if (u.rows[k] <= 0 || u.row0[k] != end) return false;
+    end += u.rows[k];
+  }
+  *hi = end;
+  return true;
+}
+
+}  // namespace
+
+GemmUnits tile_aligned_units(const GemmUnits& u, int bm) {
+  int64_t lo = 0, hi = 0;
+  if (u.n <= 1 || bm <= 0 || !contiguous(u, &lo, &hi)) return u;
+  const int64_t nt = (hi - lo + bm - 1) / bm;
+  GemmUnits out;
+  out.n = 0;
+  for (int i = 0; i < u.n; ++i) {
+    // tiles t whose last row min(hi, lo + (t+1) bm) - 1 lies in [row0, row0 + rows)
+    const int64_t r0 = u.row0[i], r1 = u.row0[i] + u.rows[i];
+    int64_t t0 = (r0 - lo + 1 + bm - 1) / bm - 1;  // smallest t with lo + (t+1) bm - 1 >= r0
+    if (t0 < 0) t0 = 0;
+    int64_t t1 = (r1 - lo) / bm - 1;                // largest t with lo + (t+1) bm - 1 < r1
+    if (r1 == hi) t1 = nt - 1;                      // the last tile ends at hi
+    if (t1 < t0) continue;
+    out.row0[out.n] = static_cast<int32_t>(lo + t0 * bm);
+    out.rows[out.n] = static_cast<int32_t>(std::min(hi, lo + (t1 + 1) * bm) - (lo + t0 * bm));
+    ++out.n;
+  }
+  return out;
+}
+
+int64_t row_tiles(const GemmUnits& u, int bm) {
+  const GemmUnits a = tile_aligned_units(u, bm);
+  int64_t n = 0;
+  for (int i = 0; i < a.n; ++i) n += (a.rows[i] + bm - 1) / bm;
+  return n;
+}
+
+}  // namespace ubx
