@@ -63,6 +63,7 @@ struct Params {
   int64_t lda, sa, ldb, sb, ldc, sc;
   int32_t n, k;
   int32_t tiles_n;                       // tile columns
+  int32_t group;                         // row tiles per group (tile_of)
   int32_t n_units;                       // row units, in processing order
   int32_t unit_row0[kMaxGemmUnits];
   int32_t unit_rows[kMaxGemmUnits];
@@ -127,14 +128,15 @@ struct Tile {
   uint32_t a_kstep, b_kstep;
   int a_rd_row, a_rd_c, a_rd_x, b_krow, b_col_chunk, b_x, b_in;
 
-  __device__ inline void init(const Params& p, int tid) {
+  // false: this workgroup has no tile (the whole workgroup returns before any barrier)
+  __device__ inline bool init(const Params& p, int tid) {
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     group = wave >> 2;
     wm = wave / C::WGN;
     wn = wave % C::WGN;
     int tn;
-    tile_of(p, blockIdx.x, C::BM, m0, m_end, tn);
+    if (!tile_of(p, blockIdx.x, C::BM, m0, m_end, tn)) return false;
     n0 = tn * C::BN;
     const uint16_t* A = p.a + blockIdx.z * p.sa + (int64_t)m0 * p.lda;
     const uint16_t* B = p.b + blockIdx.z * p.sb + n0;
@@ -180,6 +182,8 @@ struct Tile {
     b_col_chunk = (wn * C::WN + ((lane >> 4) & 1) * 16 + (lane & 3) * 4) >> 3;
     b_x = b_swz((lane >> 2) & 3);
     b_in = (lane & 1) * 8;
+
+    return true;
   }
 
   // This wave's direct loads of step ks into stage ks % S: NA_ A loads and NB_ B loads
@@ -286,7 +290,7 @@ void gemm_bf16_pingpong(Params p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x;
   Tile<C> t;
-  t.init(p, tid);
+  if (!t.init(p, tid)) return;
   const int group = t.group;
 
   f32x16 acc[C::FM][C::FN];
@@ -350,7 +354,7 @@ void gemm_bf16_pipelined(Params p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x;
   Tile<C> t;
-  t.init(p, tid);
+  if (!t.init(p, tid)) return;
 
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -412,7 +416,9 @@ hipError_t launch(K kernel, const GemmArgs& g, const GemmUnits& units, hipStream
   }
   p.unit_tile0[u.n] = (int32_t)tiles;
   if (tiles == 0) return hipSuccess;
-  if (tiles > 0x7FFFFFFF || g.batch > 65535) return hipErrorInvalidValue;
+  p.group = tile_group(tiles, C::NW == 8 ? 1 : 2);
+  const int64_t grid = tiles;
+  if (grid > 0x7FFFFFFF || g.batch > 65535) return hipErrorInvalidValue;
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -420,7 +426,7 @@ hipError_t launch(K kernel, const GemmArgs& g, const GemmUnits& units, hipStream
     if (e != hipSuccess) return e;
     configured = true;
   }
-  hipLaunchKernelGGL(kernel, dim3((unsigned)tiles, 1, g.batch), dim3(C::THREADS),
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid, 1, g.batch), dim3(C::THREADS),
                      C::LDS_BYTES, stream, p);
   return hipGetLastError();
 }

@@ -45,6 +45,7 @@ struct F8Params {
   int32_t n, k;
   float scale;
   int32_t tiles_n;
+  int32_t group;                         // row tiles per group (tile_of)
   int32_t n_units;
   int32_t unit_row0[kMaxGemmUnits];
   int32_t unit_rows[kMaxGemmUnits];
@@ -87,14 +88,15 @@ struct F8Tile {
   uint32_t rd_a, rd_b;  // byte offset of this lane's first A / B fragment row in a stage
   int rd_c0, rd_c1;     // the two 16-byte chunk slots (swizzled) this lane reads
 
-  __device__ inline void init(const F8Params& p, int tid) {
+  // false: this workgroup has no tile (the whole workgroup returns before any barrier)
+  __device__ inline bool init(const F8Params& p, int tid) {
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     group = wave >> 2;
     wm = wave / C::WGN;
     wn = wave % C::WGN;
     int tn;
-    tile_of(p, blockIdx.x, C::BM, m0, m_end, tn);
+    if (!tile_of(p, blockIdx.x, C::BM, m0, m_end, tn)) return false;
     n0 = tn * C::BN;
     const int rows_a = min(C::BM, m_end - m0);
     const int rows_b = min(C::BN, p.n - n0);
@@ -120,6 +122,8 @@ struct F8Tile {
     const int x = a_swz<C::CPR>(lane & 31);
     rd_c0 = ((2 * (lane >> 5)) ^ x) * 16;
     rd_c1 = ((2 * (lane >> 5) + 1) ^ x) * 16;
+
+    return true;
   }
 
   // Steps past the end are issued with out-of-range offsets (zeros, no memory touched) so
@@ -192,7 +196,7 @@ void gemm_fp8_pingpong(F8Params p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x;
   F8Tile<C> t;
-  t.init(p, tid);
+  if (!t.init(p, tid)) return;
   const int group = t.group;
 
   f32x16 acc[C::FM][C::FN];
@@ -270,7 +274,9 @@ hipError_t launch(const GemmF8Args& g, const GemmUnits& units, hipStream_t strea
   }
   p.unit_tile0[u.n] = (int32_t)tiles;
   if (tiles == 0) return hipSuccess;
-  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  p.group = tile_group(tiles, 1);
+  const int64_t grid = tiles;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   auto kernel = &gemm_fp8_pingpong<C, F8_D>;
   static bool configured = false;
   if (!configured) {
@@ -279,7 +285,7 @@ hipError_t launch(const GemmF8Args& g, const GemmUnits& units, hipStream_t strea
     if (e != hipSuccess) return e;
     configured = true;
   }
-  hipLaunchKernelGGL(kernel, dim3((unsigned)tiles), dim3(C::THREADS), C::LDS_BYTES, stream, p);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(C::THREADS), C::LDS_BYTES, stream, p);
   return hipGetLastError();
 }
 

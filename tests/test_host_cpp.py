@@ -28,3 +28,15 @@ def test_tile_aligned_units(tmp_path):
     res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0, res.stdout + res.stderr
     assert res.stdout.startswith("ok"), res.stdout
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
+def test_tile_of(tmp_path):
+    """The workgroup -> tile map of the device-side chunk loop covers every tile once."""
+    exe = tmp_path / "tile_of_check"
+    cmd = [_hipcc(), "-O1", "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+           "-I", CSRC, os.path.join(ROOT, "tests", "cpp", "tile_of_check.cpp"), "-o", str(exe)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert res.stdout.startswith("ok"), res.stdout
