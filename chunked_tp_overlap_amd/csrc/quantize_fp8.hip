@@ -14,7 +14,7 @@
 // exactly that definition for every input.
 //
 // HBM-bound: 2 bytes read and 1 written per element; a lane converts 8 elements (16 bytes
-// in, 8 out) per vector.
+// in, 8 out) per vector, four vectors per lane, one short chunk of rows per workgroup.
 #include <hip/hip_runtime.h>
 
 #include "ub_internal.h"
@@ -43,28 +43,45 @@ __device__ inline uint32_t e4m3(float y) {
   return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
 }
 
+constexpr int V = 4;  // vectors per lane
+
+__device__ inline u32x2 quantize8(u32x4 x, float scale) {
+  uint32_t q[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    q[2 * i] = e4m3(__uint_as_float(x[i] << 16) * scale);
+    q[2 * i + 1] = e4m3(__uint_as_float(x[i] & 0xFFFF0000u) * scale);
+  }
+  u32x2 o;
+  o[0] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+  o[1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+  return o;
+}
+
 // dst row r (stride ldd bytes) = quantized src row r (stride lds elements), cols elements.
+// Workgroup b converts vectors [b V THREADS, (b + 1) V THREADS) of 8 elements each; lane t
+// takes vectors t, t + THREADS, ... (all V loads in flight before the conversions).
 __global__ __launch_bounds__(THREADS) void quantize_rows(const uint16_t* src, int64_t lds,
                                                          uint8_t* dst, int64_t ldd, int64_t rows,
                                                          int64_t cols, float scale) {
   const int64_t vpr = cols / 8;
   const int64_t total = rows * vpr;
-  for (int64_t v = (int64_t)blockIdx.x * THREADS + threadIdx.x; v < total;
-       v += (int64_t)gridDim.x * THREADS) {
-    const int64_t row = v / vpr;
-    const int64_t col = (v - row * vpr) * 8;
-    const u32x4 x = __builtin_nontemporal_load(GLOBAL_PTR(const u32x4, src + row * lds + col));
-    uint32_t q[8];
+  const int64_t base = (int64_t)blockIdx.x * (V * THREADS) + threadIdx.x;
+  u32x4 x[V];
+  int64_t row[V], col[V];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      q[2 * i] = e4m3(__uint_as_float(x[i] << 16) * scale);
-      q[2 * i + 1] = e4m3(__uint_as_float(x[i] & 0xFFFF0000u) * scale);
-    }
-    u32x2 o;
-    o[0] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-    o[1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
-    *GLOBAL_PTR(u32x2, dst + row * ldd + col) = o;
+  for (int j = 0; j < V; ++j) {
+    const int64_t v = base + j * THREADS;
+    row[j] = v / vpr;
+    col[j] = (v - row[j] * vpr) * 8;
+    if (v < total)
+      x[j] = __builtin_nontemporal_load(GLOBAL_PTR(const u32x4, src + row[j] * lds + col[j]));
   }
+#pragma unroll
+  for (int j = 0; j < V; ++j)
+    if (base + j * THREADS < total)
+      __builtin_nontemporal_store(quantize8(x[j], scale),
+                                  GLOBAL_PTR(u32x2, dst + row[j] * ldd + col[j]));
 }
 
 }  // namespace
@@ -73,8 +90,8 @@ hipError_t launch_quantize_e4m3(const uint16_t* src, int64_t lds, uint8_t* dst, 
                                 int64_t rows, int64_t cols, float scale, hipStream_t stream) {
   if (rows <= 0 || cols <= 0) return hipSuccess;
   if (cols % 8 != 0 || lds % 8 != 0 || ldd % 8 != 0) return hipErrorInvalidValue;
-  int64_t blocks = (rows * (cols / 8) + THREADS - 1) / THREADS;
-  if (blocks > 256 * 32) blocks = 256 * 32;
+  const int64_t blocks = (rows * (cols / 8) + V * THREADS - 1) / (V * THREADS);
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(quantize_rows, dim3((unsigned)blocks), dim3(THREADS), 0, stream, src, lds,
                      dst, ldd, rows, cols, scale);
   return hipGetLastError();
