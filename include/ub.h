@@ -27,15 +27,21 @@
  *     [T/tp, hidden] ([MLM#1240] MLP diagram; [TE#3564]: reduce-scatter keeps its extra
  *     per-rank chunks inside its own allocation).
  * One process drives one GPU; the library moves no data between GPUs.  The UB holds what
- * a rank would have after the all-gather; the caller fills its active prefix.
+ * a rank would have after the all-gather; the caller fills its active prefix, or lets
+ * ub_gemm_ag_arrival deliver the other ranks' chunks while the chunk GEMMs run.
+ * Extensions beyond the pages' first scope: a device-side chunk loop (option
+ * atomic_gemm, [TE#1344]), the reduce-scatter sum in ring order with a bf16 rounding per
+ * hop (reduce_order), and FP8 (E4M3) UserBuffers on the all-gather side.
  *
  * Conventions for every entry point.
- *   - Tensors are row-major bf16 (2 bytes, IEEE binary32 upper half).  Device pointers
- *     must be 16-byte aligned; leading dimensions and the hidden size are counted in
- *     elements and must be multiples of 8 (16-byte rows).
+ *   - Tensors are row-major bf16 (2 bytes, IEEE binary32 upper half), or E4M3 codes (1
+ *     byte) where an entry point says so.  Device pointers must be 16-byte aligned;
+ *     leading dimensions and the hidden size are counted in elements and must be
+ *     multiples of 8 (16-byte rows; 16 for fp8).
  *   - Every device buffer is owned by the caller (allocated by PyTorch or hipMalloc) and
  *     must outlive the handle.  The library never allocates, frees or registers device
- *     memory.  A handle owns only host state and its HIP streams and events.
+ *     memory.  A handle owns only host state and its HIP streams and events (created on
+ *     first use; ub_gemm_ag_arrival adds a copy stream and one event per chunk).
  *   - Functions return a ub_status_t; no C++ exception crosses the ABI.  Arguments are
  *     checked before anything is launched; a rejected call changes no state and enqueues
  *     nothing.  ub_last_error() returns a message for the last failure on a handle.
@@ -46,9 +52,11 @@
  *   - A handle is not thread-safe.  The caller must not modify the UB prefix, the
  *     weights or the outputs while a call that uses them is in flight.
  *   - Rounding: products are accumulated in fp32 (MFMA) and each stored result is
- *     rounded once to bf16, round-to-nearest-even.  An output element depends only on
- *     its own input row and weight column: results are bit-identical for every chunk
- *     count, stream count, order, aggregate setting, capacity and buffer offset.
+ *     rounded once to bf16, round-to-nearest-even (the reduce-scatter partials once
+ *     each, then their sum once, or once per hop in ring order).  An output element
+ *     depends only on its own input row and weight column: results are bit-identical
+ *     for every chunk count, stream count, order, aggregate setting, atomic_gemm,
+ *     capacity and buffer offset.
  */
 #ifndef CHUNKED_TP_OVERLAP_AMD_UB_H
 #define CHUNKED_TP_OVERLAP_AMD_UB_H
@@ -117,12 +125,17 @@ typedef enum { UB_OP_AG = 0, UB_OP_RS = 1 } ub_op_t;
  *   aggregate        all-gather side only: chunks {2u, 2u+1} are merged into one launch.
  *   atomic_gemm      0: one kernel launch per unit from a host loop on the compute
  *                    streams; 1: one kernel on the caller's stream whose workgroups walk
- *                    the units on the device in plan order (no tile spans two units; at
- *                    most 64 non-empty units, else UB_ERR_UNSUPPORTED).  Results are
- *                    bit-identical ([TE#1344] "atomic_gemm").
+ *                    the units on the device in plan order (at most 64 non-empty units,
+ *                    else UB_ERR_UNSUPPORTED).  The units' rows are cut into tiles from
+ *                    the first active row, each tile going to the unit that holds its
+ *                    last row, so a tile may read rows of two neighbouring units.
+ *                    Results are bit-identical to the host loop ([TE#1344]
+ *                    "atomic_gemm").
  *   rank             this rank in [0, tp_size): sets the ring order.
- *   use_ce, num_sm, set_sm_margin  accepted for compatibility and ignored: on one GPU
- *                    there is no send/recv to place on a copy engine and no
+ *   use_ce           ub_gemm_ag_arrival / ub_deliver_chunks only: deliveries from device
+ *                    memory go on the SDMA engines (1, the default) or through the
+ *                    runtime's copy kernel (0).  Ignored elsewhere.
+ *   num_sm, set_sm_margin  accepted for compatibility and ignored: on one GPU there is no
  *                    communication kernel to reserve compute units for.
  *   reduce_order     reduce-scatter side only (ub_reduce_order_t).  UB_REDUCE_ASCENDING
  *                    (default): out = bf16(sum of the tp bf16 partials in fp32, slice 0
@@ -277,9 +290,9 @@ UB_API ub_status_t ub_gemm_ag_chunked_fp8(ub_handle_t h, const void* w, int64_t 
  * Same result as ub_gemm_ag_chunked, but the UB prefix is completed while the call runs:
  * `src` ([T, hidden] bf16 packed, 16-byte aligned; device memory, or pinned host memory
  * when src_on_host is nonzero) holds the active rows as the other ranks would send them,
- * and the non-local chunks are copied from src into
- * the UB rows they belong to on the handle's copy stream, in plan order (each unit's
- * chunks ascending), one event per chunk.  Each unit's GEMM waits on the events of its own
+ * and the non-local chunks are copied from src into the UB rows they belong to on the
+ * handle's copy stream, in plan order (each unit's chunks ascending), one event per
+ * chunk.  Each unit's GEMM waits on the events of its own
  * chunks only, so GEMMs on arrived chunks overlap the remaining copies.
  *   Local chunk: with method ring exchange, chunk `rank` (rows [rank*T/tp,
  *     (rank+1)*T/tp)) is this rank's own shard, already in the UB (ub_copy_in); its rows
@@ -311,7 +324,9 @@ UB_API ub_status_t ub_deliver_chunks(ub_handle_t h, const void* src, int32_t src
  * written to the workspace at element (s*T + t) * hidden + j (the packed active prefix
  * of tp_size slots), then
  *   out[t, j] = bf16( sum_{s = 0..tp_size-1} P_s[t, j] )   (fp32 sum, ascending s)
- * so that rank r's shard is out rows [r T/tp, (r+1) T/tp), contiguous.
+ * or, with cfg->reduce_order = UB_REDUCE_RING, the ring-order sum with a bf16 rounding
+ * per hop (see ub_overlap_cfg_t), so that rank r's shard is out rows
+ * [r T/tp, (r+1) T/tp), contiguous.
  * A is [T, k] (row stride lda >= k), W is [k, hidden] (row stride ldw >= hidden), out is
  * [T, hidden] (row stride ldo >= hidden).  k % tp_size == 0 (else INVALID_ARG) and
  * Ks % 64 == 0 (else UNSUPPORTED).  Requires a registered workspace (else
