@@ -1,0 +1,80 @@
+"""HIP-graph capture of the chunked GEMM calls: none of them synchronises the host,
+allocates, or records a memset, so a whole step (several microbatches, each with its own
+active shape) can be captured once and replayed.  Every replay is checked bit for bit
+against the eager results, with eager work and host synchronisation between replays."""
+
+import numpy as np
+import pytest
+import torch
+
+from chunked_tp_overlap_amd import workloads as wl
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ub():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import chunked_tp_overlap_amd.ub as m
+    return m
+
+
+def test_graph_replays_match_eager(ub):
+    rng = np.random.default_rng(91)
+    cap, H, N, tp, K = 1024, 512, 264, 8, 1024
+    Ts = (1024, 600, 296)
+    a = gu.dev(wl.normal_bits(rng, (cap, H)))
+    w = gu.dev(wl.normal_bits(rng, (H, N), 0.02))
+    a_rs = gu.dev(wl.normal_bits(rng, (cap, K)))
+    w_rs = gu.dev(wl.normal_bits(rng, (K, H), 0.02))
+    reg = gu.Registration(ub, cap, H, tp)
+    cfgs = [ub.make_cfg("ring_exchange", atomic_gemm=True, rank=3),
+            ub.make_cfg("pipeline", 5, 3, rank=0),                      # host loop, 3 streams
+            ub.make_cfg("ring_exchange", 1, 2, True, False, rank=6)]    # aggregate, 2 streams
+    rs_cfgs = [ub.make_cfg("pipeline", 4, 3, atomic_gemm=True),
+               ub.make_cfg("ring_exchange", 1, 3, reduce_order="ring", rank=1)]
+    outs = [gu.canary((cap, N)) for _ in range(len(Ts) * len(cfgs))]
+    rs_outs = [gu.canary((cap, H)) for _ in range(len(Ts) * len(rs_cfgs))]
+
+    def step(stream):
+        i = j = 0
+        for T in Ts:
+            ub.ub_set_active_shape(reg.h, (T, H))
+            for cfg in cfgs:
+                ub.ub_gemm_ag_chunked(reg.h, w, N, N, outs[i], N, cfg, stream)
+                i += 1
+            for cfg in rs_cfgs:
+                ub.ub_gemm_rs_chunked(reg.h, a_rs, K, K, w_rs, H, rs_outs[j], H, cfg, stream)
+                j += 1
+
+    try:
+        reg.ub_t[: cap * H].copy_(a.reshape(-1))
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            step(s)
+        torch.cuda.synchronize()
+        eager = [gu.host(o) for o in outs]
+        eager_rs = [gu.host(o) for o in rs_outs]
+        for o in outs + rs_outs:
+            o.fill_(gu.CANARY)
+        torch.cuda.synchronize()
+
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step(s)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            for o in outs + rs_outs:  # eager work between replays
+                o.fill_(gu.CANARY)
+            scratch = torch.randn(1 << 20, device="cuda").sum()  # more eager work
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for k, o in enumerate(outs):
+                assert np.array_equal(gu.host(o), eager[k]), (rep, "ag", k)
+            for k, o in enumerate(rs_outs):
+                assert np.array_equal(gu.host(o), eager_rs[k]), (rep, "rs", k)
+            del scratch
+    finally:
+        reg.close()
