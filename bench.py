@@ -101,6 +101,31 @@ class Qkv:
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / steps
 
+    def graph_replay(self, cfg, reps):
+        """Seconds per step when one step (32 microbatches, each with its own active
+        shape) is captured once in a HIP graph and replayed."""
+        torch = self.torch
+        s = torch.cuda.Stream()
+        old = self.stream
+        self.stream = s
+        try:
+            with torch.cuda.stream(s):
+                self.step(cfg)  # warm: streams and events exist before capture
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                self.step(cfg)
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                g.replay()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t0) / reps
+        finally:
+            self.stream = old
+
     def per_microbatch(self, cfg, reps=5):
         torch, ub, w = self.torch, self.ub, self.w
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -179,6 +204,9 @@ def main():
     agg_ge4096 = sum(2.0 * T * q.w.hidden * q.w.n_cols for T, _ in big) / (sum(ms for _, ms in big) / 1e3) / 1e12
 
     host_cfg = q.cfg(atomic=False)
+    graph = {}
+    for name, cfg in (("atomic_gemm", primary), ("host_loop_3_streams", host_cfg)):
+        graph[name] = round(q.flops / q.graph_replay(cfg, args.steps) / 1e12, 2)
     sec_h = q.timed(host_cfg, max(2, args.steps // 2), 1)
     ub.ub_set_kernel_timing(q.h, True)
     ub.ub_get_kernel_timing(q.h)
@@ -232,6 +260,7 @@ def main():
             "seed": w.seed,
         },
         "tflops_T_ge_4096_per_microbatch_aggregate": round(agg_ge4096, 3),
+        "graph_replay_tflops": graph,
         "modes": {
             "atomic_gemm": {"tflops": round(tflops, 2), "ms_per_step": round(sec * 1e3, 4)},
             "host_loop_3_streams": {
