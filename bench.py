@@ -518,7 +518,10 @@ def arrival(ub, wl, torch, np, dev):
     own chunk's event.  Sources: pinned host memory (SDMA over PCIe, about one xGMI link's
     rate), device memory by SDMA, device memory by the runtime's copy kernel.  Reports the
     GEMMs alone, the deliveries alone, both overlapped, the fraction of the delivery time
-    hidden behind the GEMMs, and the overlap as a fraction of the shorter of the two."""
+    hidden behind the GEMMs, the overlap as a fraction of the shorter of the two, the time
+    the call runs past the deliveries alone, and max(GEMMs, deliveries) / overlapped (1.0
+    when the shorter side is wholly hidden; the last chunk's GEMM can only follow its copy,
+    so the bound is a little below 1)."""
     w = wl.qkv()
     ra, rw, _ = w.seeds()
     log("secondary qkv_arrival")
@@ -547,7 +550,9 @@ def arrival(ub, wl, torch, np, dev):
                 "gemm_ms": round(t_g, 4), "deliver_ms": round(t_c, 4), "overlapped_ms": round(t_o, 4),
                 "deliver_gbs": round(copy_bytes / t_c / 1e6, 1),
                 "hidden_fraction_of_delivery": round(max(0.0, min(1.0, (t_g + t_c - t_o) / t_c)), 3),
-                "overlap_of_shorter": round(max(0.0, min(1.0, (t_g + t_c - t_o) / min(t_g, t_c))), 3)}
+                "overlap_of_shorter": round(max(0.0, min(1.0, (t_g + t_c - t_o) / min(t_g, t_c))), 3),
+                "exposed_after_delivery_ms": round(t_o - t_c, 4),
+                "overlap_efficiency": round(max(t_g, t_c) / t_o, 3)}
         res.append(row)
     ub.ub_destroy(h)
     return res

@@ -477,35 +477,43 @@ ChunkMap chunk_map(const ub_ctx* h, const ub_overlap_cfg_t* cfg) {
   return m;
 }
 
-// The arrival copies on the copy stream, in plan order (each unit's chunks ascending),
-// after the caller's stream reaches this point; chunk c's event is recorded after its copy.
-ub_status_t deliver(ub_ctx* h, const uint16_t* src, int src_on_host, const ub_overlap_cfg_t* cfg,
-                    const ChunkMap& m, hipStream_t caller) {
-  ub_status_t st = ensure_arrival(h, m.n);
+// The arrival stand-in's copy stream starts when the caller's stream reaches the call.
+ub_status_t start_deliveries(ub_ctx* h, int n_chunks, hipStream_t caller) {
+  ub_status_t st = ensure_arrival(h, n_chunks);
   if (st != UB_OK) return st;
   hipError_t e = hipEventRecord(h->ev_fork, caller);
   if (e == hipSuccess) e = hipStreamWaitEvent(h->copy_stream, h->ev_fork, 0);
-  if (e != hipSuccess) return hip_fail(h, e, "copy stream fork");
+  return e == hipSuccess ? UB_OK : hip_fail(h, e, "copy stream fork");
+}
+
+// The copies of one unit's non-local chunks (ascending) on the copy stream; chunk c's
+// event is recorded after its copy.
+ub_status_t deliver_unit(ub_ctx* h, const uint16_t* src, int src_on_host,
+                         const ub_overlap_cfg_t* cfg, const ChunkMap& m,
+                         const ub_plan_unit_t& u) {
   // Host source: pinned memory over PCIe, always on the SDMA engines.  Device source: the
   // SDMA engines (use_ce) or the runtime's copy kernel.
   const hipMemcpyKind kind = src_on_host  ? hipMemcpyHostToDevice
                              : cfg->use_ce ? hipMemcpyDeviceToDeviceNoCU
                                            : hipMemcpyDeviceToDevice;
   const int64_t H = h->hidden, T = h->T;
-  for (const ub_plan_unit_t& u : h->plan.units) {
-    for (int c = m.first(u.unit); c < m.last(u.unit); ++c) {
-      if (c == m.local) continue;
-      const int64_t r0 = m.row0(T, c), rows = m.row0(T, c + 1) - r0;
-      if (rows > 0) {
-        e = hipMemcpyAsync(h->ub + r0 * H, src + r0 * H, static_cast<size_t>(rows * H) * 2, kind,
-                           h->copy_stream);
-        if (e != hipSuccess) return hip_fail(h, e, "hipMemcpyAsync(arrival)");
-      }
-      e = hipEventRecord(h->ev_arrive[c], h->copy_stream);
-      if (e != hipSuccess) return hip_fail(h, e, "hipEventRecord(arrival)");
-    }
+  for (int c = m.first(u.unit); c < m.last(u.unit); ++c) {
+    if (c == m.local) continue;
+    const int64_t r0 = m.row0(T, c), rows = m.row0(T, c + 1) - r0;
+    hipError_t e = hipSuccess;
+    if (rows > 0)
+      e = hipMemcpyAsync(h->ub + r0 * H, src + r0 * H, static_cast<size_t>(rows * H) * 2, kind,
+                         h->copy_stream);
+    if (e == hipSuccess) e = hipEventRecord(h->ev_arrive[c], h->copy_stream);
+    if (e != hipSuccess) return hip_fail(h, e, "arrival copy");
   }
   return UB_OK;
+}
+
+ub_status_t join_deliveries(ub_ctx* h, hipStream_t caller) {
+  hipError_t e = hipEventRecord(h->ev_copy_join, h->copy_stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(caller, h->ev_copy_join, 0);
+  return e == hipSuccess ? UB_OK : hip_fail(h, e, "copy stream join");
 }
 
 ub_status_t check_arrival(ub_ctx* h, const void* src, const ub_overlap_cfg_t* cfg) {
@@ -560,11 +568,15 @@ ub_status_t ag_call(ub_ctx* h, const void* src, int src_on_host, const void* w, 
   const int S = h->plan.n_streams;
   if ((st = ensure_device(h, S)) != UB_OK) return st;
   const ChunkMap m = chunk_map(h, cfg);
-  if (src && (st = deliver(h, static_cast<const uint16_t*>(src), src_on_host, cfg, m, caller)) !=
-                 UB_OK)
-    return st;
+  if (src && (st = start_deliveries(h, m.n, caller)) != UB_OK) return st;
   if ((st = fork_streams(h, caller, S)) != UB_OK) return st;
+  // With deliveries, each unit's copies are issued just before its GEMM, in plan order, so
+  // that no GEMM is enqueued behind copies it does not need (streams may share hardware
+  // queues).
   for (const ub_plan_unit_t& u : h->plan.units) {
+    if (src && (st = deliver_unit(h, static_cast<const uint16_t*>(src), src_on_host, cfg, m, u)) !=
+                   UB_OK)
+      return st;
     const int64_t rows = u.row1 - u.row0;
     if (rows <= 0) continue;
     if (rows > kMaxRowsPerUnit) return fail(h, UB_ERR_UNSUPPORTED, "unit too large");
@@ -594,11 +606,8 @@ ub_status_t ag_call(ub_ctx* h, const void* src, int src_on_host, const void* w, 
                       "GEMM launch");
     if (st != UB_OK) return st;
   }
-  if (src) {  // every chunk was consumed by a unit; join the copy stream all the same
-    hipError_t e = hipEventRecord(h->ev_copy_join, h->copy_stream);
-    if (e == hipSuccess) e = hipStreamWaitEvent(caller, h->ev_copy_join, 0);
-    if (e != hipSuccess) return hip_fail(h, e, "copy stream join");
-  }
+  // every chunk was consumed by a unit; join the copy stream all the same
+  if (src && (st = join_deliveries(h, caller)) != UB_OK) return st;
   return join_streams(h, caller, S);
 }
 
@@ -630,12 +639,13 @@ UB_API ub_status_t ub_deliver_chunks(ub_handle_t h, const void* src, int32_t src
     return st;
   if ((st = ensure_device(h, 1)) != UB_OK) return st;
   hipStream_t caller = static_cast<hipStream_t>(stream);
-  if ((st = deliver(h, static_cast<const uint16_t*>(src), src_on_host != 0, cfg, chunk_map(h, cfg),
-                    caller)) != UB_OK)
-    return st;
-  hipError_t e = hipEventRecord(h->ev_copy_join, h->copy_stream);
-  if (e == hipSuccess) e = hipStreamWaitEvent(caller, h->ev_copy_join, 0);
-  return e == hipSuccess ? UB_OK : hip_fail(h, e, "copy stream join");
+  const ChunkMap m = chunk_map(h, cfg);
+  if ((st = start_deliveries(h, m.n, caller)) != UB_OK) return st;
+  for (const ub_plan_unit_t& u : h->plan.units)
+    if ((st = deliver_unit(h, static_cast<const uint16_t*>(src), src_on_host != 0, cfg, m, u)) !=
+        UB_OK)
+      return st;
+  return join_deliveries(h, caller);
 }
 
 UB_API ub_status_t ub_quantize_in(ub_handle_t h, const void* src, int64_t rows,
