@@ -172,7 +172,9 @@ def main():
     primary = q.cfg(atomic=True)
 
     log(f"warmup {args.warmup}, timed {args.steps} steps of {len(q.Ts)} microbatches (atomic_gemm)")
-    sec = q.timed(primary, args.steps, args.warmup)
+    state = DeviceState(torch)
+    with state:
+        sec = q.timed(primary, args.steps, args.warmup)
     tflops = q.flops / sec / 1e12
     log(f"primary: {sec * 1e3:.3f} ms/step, {tflops:.1f} TFLOP/s")
 
@@ -214,12 +216,13 @@ def main():
     host_stats, _ = ub.ub_get_kernel_timing(q.h)
     ub.ub_set_kernel_timing(q.h, False)
 
-    traffic = None
+    traffic, util = None, None
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if tr.get("src_hash") == src_hash(GEMM_SRC):
             traffic = tr.get("qkv_gemm_bytes_per_launch")
+            util = tr.get("util")
     except (OSError, ValueError):
         pass
 
@@ -233,6 +236,11 @@ def main():
         "algorithmic_bytes_per_launch": round(gemm_stats["bytes"] / max(1, gemm_stats["launches"])),
         "measured_pass_ms_per_step": round(sec_i * 1e3, 4),
     }
+    if util:
+        # from the committed counter pass of the same kernel source (rocprofv3 --pmc
+        # GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES): the effective clock,
+        # the mean number of CUs holding a tile, and how busy their matrix cores are
+        roofline["counters"] = util
 
     w = q.w
     result = {
@@ -275,6 +283,7 @@ def main():
     result["device"] = {"name": props.name, "cus": props.multi_processor_count,
                         "gcn_arch": getattr(props, "gcnArchName", ""),
                         "gemm_src_hash": src_hash(GEMM_SRC)}
+    result["device_state"] = state.summary(tflops)
 
     if not args.no_secondary:
         result["secondary"] = secondary(ub, wl, torch, np, dev)
@@ -284,6 +293,93 @@ def main():
 
     ub.ub_destroy(q.h)
     print(json.dumps(result), flush=True)
+
+
+class DeviceState:
+    """Samples the GPU's shader clock and socket power (amdsmi) on a thread while a timed
+    region runs, and reports the mean clock, the power against the cap, and the dense bf16
+    peak recomputed at the mean clock.  Reports why when amdsmi is not usable."""
+
+    def __init__(self, torch, period_s=0.005):
+        self.period, self.samples, self.error = period_s, [], None
+        self.cap_w, self.bdf, self._h, self._stop, self._thr = None, None, None, None, None
+        try:
+            import amdsmi
+            self._smi = amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            p = torch.cuda.get_device_properties(0)
+            bus = getattr(p, "pci_bus_id", None)
+            if bus is not None:
+                want = f"{getattr(p, 'pci_domain_id', 0):04x}:{bus:02x}:{getattr(p, 'pci_device_id', 0):02x}"
+                for h in handles:
+                    if amdsmi.amdsmi_get_gpu_device_bdf(h).lower().startswith(want):
+                        self._h = h
+            if self._h is None and len(handles) == 1:
+                self._h = handles[0]
+            if self._h is None:
+                raise RuntimeError(f"no amdsmi device matches cuda:0 among {len(handles)}")
+            self.bdf = amdsmi.amdsmi_get_gpu_device_bdf(self._h)
+            try:
+                cap = amdsmi.amdsmi_get_power_cap_info(self._h).get("power_cap")
+                self.cap_w = round(cap / 1e6 if cap and cap > 1e4 else cap, 1) if cap else None
+            except Exception:  # noqa: BLE001 - the cap is optional
+                pass
+        except Exception as e:  # noqa: BLE001 - any failure just disables the sampling
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _sample(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+        if not clks and isinstance(m.get("current_gfxclk"), (int, float)):
+            clks = [m["current_gfxclk"]]
+        pw = m.get("current_socket_power")
+        if not isinstance(pw, (int, float)) or not 0 < pw < 10000:
+            pw = m.get("average_socket_power")
+        return (sum(clks) / len(clks) if clks else None,
+                pw if isinstance(pw, (int, float)) and 0 < pw < 10000 else None)
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._sample())
+            except Exception as e:  # noqa: BLE001
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+        if self._h is not None:
+            self._stop = threading.Event()
+            self._thr = threading.Thread(target=self._run, daemon=True)
+            self._thr.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thr is not None:
+            self._stop.set()
+            self._thr.join()
+        return False
+
+    def summary(self, tflops):
+        clk = [c for c, _ in self.samples if c]
+        pw = [w for _, w in self.samples if w]
+        out = {"source": "amdsmi gpu metrics, sampled every %.0f ms over the timed region" % (self.period * 1e3),
+               "bdf": self.bdf, "samples": len(self.samples)}
+        if self.error:
+            out["error"] = self.error
+        if clk:
+            mean = sum(clk) / len(clk)
+            peak = 256 * 4096 * mean * 1e6 / 1e12
+            out.update({"gfx_clock_mhz_mean": round(mean, 1), "gfx_clock_mhz_min": round(min(clk), 1),
+                        "gfx_clock_mhz_max": round(max(clk), 1),
+                        "bf16_peak_at_mean_clock_tflops": round(peak, 1),
+                        "frac_of_peak_at_mean_clock": round(tflops / peak, 4)})
+        if pw:
+            out.update({"socket_power_w_mean": round(sum(pw) / len(pw), 1), "socket_power_w_max": round(max(pw), 1)})
+        out["power_cap_w"] = self.cap_w
+        return out
 
 
 def calibration_copy(torch, dev):

@@ -14,6 +14,18 @@ kernel's dispatches.
 --key selects a sub-object of the profile pass's JSON line (the reduce pass reports the
 ascending and the ring order separately).  The timed launches are the last
 `timed_launches` dispatches of the kernel in the trace.
+
+--util DIR adds a fourth run, --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES
+SQ_BUSY_CU_CYCLES, read per dispatch with that run's own timestamps:
+  - GRBM_GUI_ACTIVE sums the busy cycles of the 8 XCDs' GRBMs, so /8 is the dispatch's
+    length in shader cycles, and over its duration the effective clock (an upper bound for
+    short dispatches: the count includes the dispatch's set-up and drain);
+  - SQ_VALU_MFMA_BUSY_CYCLES counts SIMD-cycles of issued MFMA work (1024 bf16 FLOP per
+    SIMD-cycle), so against the algorithmic FLOPs it shows the MFMA work spent on the
+    padded rows of partial tiles;
+  - SQ_BUSY_CU_CYCLES sums the cycles each CU holds waves: over the dispatch's cycles, the
+    mean number of busy CUs; against the MFMA cycles (4 SIMDs per CU), how busy the matrix
+    cores of the busy CUs are.
 """
 
 import argparse
@@ -52,6 +64,25 @@ def counter_means(dirname, counter, kernel):
     return statistics.fmean(mine), len(mine), copy[-1]
 
 
+def counter_timed_dispatches(dirname, counters, kernel, n_timed):
+    """Per-dispatch counter values (and duration in us, from the same run's timestamps) of
+    the last n_timed dispatches of `kernel`."""
+    by = {}
+    for r in _rows(_one(dirname, "_counter_collection.csv")):
+        if kernel not in r["Kernel_Name"] or r["Counter_Name"] not in counters:
+            continue
+        d = by.setdefault(int(r["Dispatch_Id"]), {})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    ds = [by[k] for k in sorted(by) if all(c in by[k] for c in counters)]
+    if not ds:
+        raise SystemExit(f"no dispatch of {kernel} with all of {counters}")
+    return ds[-n_timed:]
+
+
+UTIL_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES")
+
+
 def main():
     p = argparse.ArgumentParser()
     p.add_argument("--kt", required=True, help="rocprofv3 --kernel-trace --stats output directory")
@@ -64,6 +95,10 @@ def main():
     p.add_argument("--command", default="", help="the commands, for the report")
     p.add_argument("--out", required=True)
     p.add_argument("--traffic", default=None, help="write the traffic figure here (JSON)")
+    p.add_argument("--util", default=None,
+                   help="rocprofv3 --pmc " + " ".join(UTIL_COUNTERS) + " output directory")
+    p.add_argument("--peak-flop-per-cu-cycle", type=float, default=4096.0,
+                   help="dense MFMA FLOP per CU per cycle of the kernel's dtype (bf16 4096, fp8 8192)")
     a = p.parse_args()
 
     with open(a.bench_json) as f:
@@ -117,6 +152,37 @@ def main():
               f"Scaled traffic per dispatch: {traffic / 1e6:.2f} MB, against {alg / 1e6:.2f} MB "
               f"algorithmic ({traffic / alg:.2f}x).", "",
               f"Kernel source: {top['src_file']}, sha256[:16] {top['src_hash']}"]
+    util = None
+    if a.util:
+        ds = counter_timed_dispatches(a.util, UTIL_COUNTERS, a.kernel, bench["timed_launches"])
+        mean = {c: statistics.fmean(d[c] for d in ds) for c in UTIL_COUNTERS + ("us",)}
+        cyc = mean["GRBM_GUI_ACTIVE"] / 8               # shader cycles of one dispatch
+        mfma, cu_busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"], mean["SQ_BUSY_CU_CYCLES"]
+        mhz = cyc / mean["us"]
+        need = bench["avg_launch_gflop"] * 1e9 / (a.peak_flop_per_cu_cycle / 4)  # SIMD-cycles
+        util = {"effective_clock_mhz": round(mhz, 1),
+                "peak_at_clock_tflops": round(256 * a.peak_flop_per_cu_cycle * mhz / 1e6, 1),
+                "busy_cus_mean": round(cu_busy / cyc, 1),
+                "mfma_active_of_busy_cu_cycles": round(mfma / (4 * cu_busy), 4),
+                "mfma_active_of_all_cu_cycles": round(mfma / (4 * 256 * cyc), 4),
+                "mfma_issued_per_algorithmic": round(mfma / need, 4)}
+        lines += ["", "## Clock and MFMA activity (--pmc " + " ".join(UTIL_COUNTERS) + ")", "",
+                  f"Means over the last {len(ds)} dispatches of the counter run (its own "
+                  f"timestamps: {mean['us']:.2f} us per dispatch):", "",
+                  "| counter | per dispatch |", "|---|---|"]
+        lines += [f"| {c} | {mean[c]:.5g} |" for c in UTIL_COUNTERS]
+        lines += ["",
+                  f"- dispatch length: GRBM_GUI_ACTIVE / 8 XCDs = {cyc:.4g} cycles; over "
+                  f"{mean['us']:.2f} us, an effective clock of {mhz:.0f} MHz (nominal 2400; an "
+                  f"upper bound, the count includes the dispatch's set-up and drain)",
+                  f"- MFMA work issued: {mfma:.4g} SIMD-cycles, {mfma / need:.3f}x the "
+                  f"algorithmic FLOPs at {a.peak_flop_per_cu_cycle / 4:.0f} FLOP per SIMD-cycle "
+                  f"(the excess is padded rows of partial tiles)",
+                  f"- busy CUs: SQ_BUSY_CU_CYCLES / dispatch cycles = {cu_busy / cyc:.1f} of 256 "
+                  f"on average",
+                  f"- matrix cores of the busy CUs: MFMA SIMD-cycles / (4 x busy CU-cycles) = "
+                  f"{mfma / (4 * cu_busy):.3f}",
+                  f"- matrix cores of the whole chip over the dispatch: {mfma / (4 * 256 * cyc):.3f}"]
     with open(a.out, "w") as f:
         f.write("\n".join(lines) + "\n")
     if a.traffic:
@@ -125,7 +191,8 @@ def main():
                        "qkv_gemm_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": alg,
                        "fetch_kib_per_dispatch_raw": round(f_mean, 2), "fetch_scale": round(f_scale, 5),
                        "write_kib_per_dispatch_raw": round(w_mean, 2), "write_scale": round(w_scale, 5),
-                       "trace_mean_us": round(t_mean, 3), "hip_event_mean_us": ev}, f, indent=1)
+                       "trace_mean_us": round(t_mean, 3), "hip_event_mean_us": ev,
+                       "util": util}, f, indent=1)
             f.write("\n")
     print("\n".join(lines))
 

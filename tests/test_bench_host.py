@@ -1,0 +1,128 @@
+"""Host-side checks of the benchmark harness: the one-GPU guard, the rocprofv3 summariser's
+arithmetic on synthetic CSVs, and the device-state sampler's failure path (no GPU here)."""
+
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL = "void ubx::gemm_bf16_pingpong<Cfg<256, 256>>(Params)"
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr or "single MI355X" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+def _write(path, header, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def _counter_dir(base, name, values, copy_kib=None):
+    """A rocprofv3-like counter CSV: `values` = list of {counter: value} per kernel
+    dispatch (100 us each), then optionally one calibration copy."""
+    d = base / name
+    d.mkdir()
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    rows, t = [], 1_000_000
+    for i, v in enumerate(values):
+        for c, x in v.items():
+            rows.append([i, KERNEL, c, x, t, t + 100_000])
+        t += 200_000
+    if copy_kib is not None:
+        for c, x in copy_kib.items():
+            rows.append([len(values), "__amd_rocclr_copyBuffer", c, x, t, t + 1000])
+    _write(d / f"{name}_counter_collection.csv", hdr, rows)
+    return d
+
+
+@pytest.fixture()
+def profile_dirs(tmp_path):
+    kt = tmp_path / "kt"
+    kt.mkdir()
+    _write(kt / "kt_kernel_stats.csv", ["Name", "Calls", "AverageNs", "MinNs", "MaxNs"],
+           [[KERNEL, 4, 100000, 90000, 110000]])
+    # 4 dispatches: the first 2 untimed (300 us), the last 2 timed (100 us)
+    _write(kt / "kt_kernel_trace.csv", ["Kernel_Name", "Start_Timestamp", "End_Timestamp"],
+           [[KERNEL, 0, 300_000], [KERNEL, 0, 300_000], [KERNEL, 0, 100_000], [KERNEL, 0, 100_000]])
+    # raw FETCH counts half the copy's true 1 GiB read, WRITE counts it exactly
+    fetch = _counter_dir(tmp_path, "fetch", [{"FETCH_SIZE": 1000.0}] * 4,
+                         {"FETCH_SIZE": (1 << 30) / 1024 / 2})
+    write = _counter_dir(tmp_path, "write", [{"WRITE_SIZE": 500.0}] * 4,
+                         {"WRITE_SIZE": (1 << 30) / 1024})
+    # 2.4e5 GUI cycles summed over 8 XCDs in 100 us -> 300 MHz; MFMA and CU-busy counts
+    util = _counter_dir(tmp_path, "util", [{"GRBM_GUI_ACTIVE": 240000.0, "SQ_VALU_MFMA_BUSY_CYCLES": 2.0e6,
+                                            "SQ_BUSY_CU_CYCLES": 3.0e6}] * 4)
+    bench = tmp_path / "b.json"
+    bench.write_text("[bench] log line\n" + json.dumps({
+        "timed_launches": 2, "avg_launch_us_hip_events": 105.0, "avg_launch_gflop": 2.048,
+        "algorithmic_bytes_per_launch": 1_000_000, "src_file": "x.hip", "src_hash": "abc"}) + "\n")
+    return kt, fetch, write, util, bench
+
+
+def test_rocprof_summary_arithmetic(profile_dirs, tmp_path):
+    kt, fetch, write, util, bench = profile_dirs
+    out, traffic = tmp_path / "s.md", tmp_path / "t.json"
+    r = subprocess.run([sys.executable, "-m", "chunked_tp_overlap_amd.rocprof_summary", "--kt", str(kt),
+                        "--fetch", str(fetch), "--write", str(write), "--util", str(util),
+                        "--bench-json", str(bench), "--kernel", "gemm_bf16_pingpong",
+                        "--out", str(out), "--traffic", str(traffic)],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 0, r.stderr
+    t = json.loads(traffic.read_text())
+    # fetch scaled x2 (the copy read half of 1 GiB), write x1: (1000*2 + 500) KiB
+    assert t["fetch_scale"] == pytest.approx(2.0)
+    assert t["write_scale"] == pytest.approx(1.0)
+    assert t["qkv_gemm_bytes_per_launch"] == (1000 * 2 + 500) * 1024
+    assert t["trace_mean_us"] == pytest.approx(100.0)   # the timed (last 2) dispatches only
+    u = t["util"]
+    cyc = 240000.0 / 8                                   # 3e4 cycles per dispatch
+    assert u["effective_clock_mhz"] == pytest.approx(cyc / 100.0)
+    assert u["busy_cus_mean"] == pytest.approx(3.0e6 / cyc, abs=0.05)
+    assert u["mfma_active_of_busy_cu_cycles"] == pytest.approx(2.0e6 / (4 * 3.0e6), abs=1e-4)
+    assert u["mfma_active_of_all_cu_cycles"] == pytest.approx(2.0e6 / (4 * 256 * cyc), abs=1e-4)
+    # 2.048 GFLOP at 1024 FLOP per SIMD-cycle = 2e6 SIMD-cycles: issued == algorithmic
+    assert u["mfma_issued_per_algorithmic"] == pytest.approx(1.0, abs=1e-4)
+    md = out.read_text()
+    assert "2.50x" not in md and "(2.56x)" in md      # 2.56 MB scaled against 1.00 MB
+
+
+def test_rocprof_summary_rejects_out_of_order_copies(profile_dirs, tmp_path):
+    kt, _, write, _, bench = profile_dirs
+    bad = _counter_dir(tmp_path, "badfetch", [{"FETCH_SIZE": 1000.0}] * 4)
+    with open(bad / "badfetch_counter_collection.csv", "a", newline="") as f:
+        w = csv.writer(f)
+        w.writerow([9, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 999999.0, 0, 1])
+        w.writerow([10, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 10.0, 0, 1])
+    r = subprocess.run([sys.executable, "-m", "chunked_tp_overlap_amd.rocprof_summary", "--kt", str(kt),
+                        "--fetch", str(bad), "--write", str(write), "--bench-json", str(bench),
+                        "--kernel", "gemm_bf16_pingpong", "--out", str(tmp_path / "s.md")],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode != 0
+    assert "not the largest" in (r.stderr + r.stdout)
+
+
+def test_device_state_fails_softly_without_gpu():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("host-only check")
+    sys.path.insert(0, ROOT)
+    import bench
+
+    st = bench.DeviceState(torch)
+    with st:
+        pass
+    s = st.summary(100.0)
+    assert s["samples"] == 0
+    assert "error" in s and s["error"]
+    assert "gfx_clock_mhz_mean" not in s
