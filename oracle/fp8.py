@@ -16,12 +16,24 @@ the plain reading is taken here:
       C[t, j] = RNE_bf16( (sum_k qa[t, k] * qw[j, k]) * sa * sw ),
   sa and sw being the per-tensor dequantization factors (1 / scale of each operand).
 
-FP8 codes are carried as uint8 arrays.
+* the reduce-scatter GEMM on quantized operands: the slice partials are bf16 as on the
+  unquantized path, so only the slice GEMMs change:
+      P_s[t, j] = RNE_bf16( (sum_{k in slice s} qa[t, k] * qw[j, k]) * fp32(sa * sw) ),
+  then the same sum of the partials (ascending, or ring order with a bf16 rounding per hop).
+  The product of the two factors is formed once in fp32 (the reading the library's C
+  interface states for both FP8 GEMMs).
+
+FP8 codes are carried as uint8 arrays.  Dots of decoded codes are exact in fp64: every
+product is a multiple of 2**-18 below 448**2 < 2**17.61, so a dot over K < 2**17 terms is an
+integer number of 2**-18 quanta below 2**53 and no partial sum of any order rounds.
 """
 
 import numpy as np
 
 from . import bf16
+from . import manager as M
+from . import plan as P
+from .gemm import exact_sum, ring_sum
 
 _MAX = 448.0
 _EMIN = -6          # smallest normal exponent
@@ -105,3 +117,77 @@ def ag_rows_fp8(a_codes_rows, w_codes, n_cols, sa, sw):
     A = decode(a_codes_rows)
     W = decode(np.asarray(w_codes)[:n_cols, :A.shape[1]])
     return bf16.encode_rne(((A @ W.T) + 0.0) * float(sa) * float(sw))
+
+
+def _dot8(a_codes, w_codes):
+    """Exact dot of decoded E4M3 rows: A [t, K] against W [j, K] (see the module notes)."""
+    A, W = decode(a_codes), decode(w_codes)
+    assert A.shape[1] < 2 ** 17
+    return (A @ W.T) + 0.0
+
+
+def _scale(sa, sw):
+    return float(np.float32(sa) * np.float32(sw))
+
+
+def rs_chunked_fp8(model, a_codes, k, lda, w_codes, ldw, out_bits, ldo, cfg, sa, sw,
+                   stream_limit=None):
+    """Row-parallel GEMM over E4M3 operands, unit by unit of the reduce-scatter plan:
+    ``a_codes`` [rows >= T, lda] (first k columns used), ``w_codes`` [H, ldw] (row j =
+    output column j, first k columns used), ``out_bits`` [rows >= T, ldo] bf16.  Slice s
+    (columns [s k/tp, (s+1) k/tp)) of chunk rows [r0, r1) gives the bf16 partial P_s,
+    written to workspace elements from (s T + r0) H; then the sum as for the bf16
+    reduce-scatter.  Returns ``(status, written)``."""
+    if cfg.num_splits < 1 or cfg.num_max_streams < 1 or cfg.method not in P.METHODS:
+        return M.INVALID_ARG, None
+    if cfg.reduce_order not in P.REDUCE_ORDERS:
+        return M.INVALID_ARG, None
+    T, H = model.active_shape
+    tp = model.tp
+    if k <= 0 or k % tp != 0:
+        return M.INVALID_ARG, None
+    ks = k // tp
+    s_ = _scale(sa, sw)
+    A_all = np.asarray(a_codes).reshape(-1, lda)
+    W_all = np.asarray(w_codes).reshape(-1, ldw)[:H]
+    out = np.asarray(out_bits).reshape(-1, ldo)
+    written = np.zeros(T, dtype=np.int64)
+    for unit in P.build(T, tp, cfg, "rs", stream_limit):
+        r0, r1 = unit.row0, unit.row1
+        rows = r1 - r0
+        if rows == 0:
+            continue
+        parts = []
+        for s in range(tp):
+            sl = slice(s * ks, (s + 1) * ks)
+            ps = bf16.encode_rne(_dot8(A_all[r0:r1, sl], W_all[:, sl]) * s_)
+            o = model.partial_offset_elems(s, r0)
+            model.ws[o: o + rows * H] = ps.ravel()
+            parts.append(bf16.decode(model.ws[o: o + rows * H]).reshape(rows, H))
+        if cfg.reduce_order == "ring":
+            out[r0:r1, :H] = ring_sum(parts, r0, T, tp)
+        else:
+            out[r0:r1, :H] = bf16.encode_rne(exact_sum(parts) + 0.0)
+        written[r0:r1] += 1
+    return M.OK, written
+
+
+def rs_rows_fp8(rows, a_codes_rows, w_codes, T, tp, sa, sw, ring=False):
+    """Reduce-scatter output for the given global rows (``a_codes_rows`` [len(rows), K]
+    E4M3 codes, ``w_codes`` [H, >= K]): returns (out bits, list of the tp partials' bits).
+    Rows are independent; with ring order each row's own shard (row // (T / tp)) decides
+    its hop order."""
+    a = np.asarray(a_codes_rows)
+    K = a.shape[1]
+    ks = K // tp
+    w = np.asarray(w_codes)[:, :K]
+    s_ = _scale(sa, sw)
+    parts = [bf16.encode_rne(_dot8(a[:, s * ks:(s + 1) * ks], w[:, s * ks:(s + 1) * ks]) * s_)
+             for s in range(tp)]
+    dec = [bf16.decode(p) for p in parts]
+    if not ring:
+        return bf16.encode_rne(exact_sum(dec) + 0.0), parts
+    out = np.empty(parts[0].shape, dtype=np.uint16)
+    for i, t in enumerate(rows):
+        out[i] = ring_sum([d[i:i + 1] for d in dec], int(t), T, tp)[0]
+    return out, parts
