@@ -1,6 +1,7 @@
 // FP8 (E4M3) GEMM on gfx950 matrix cores: C = bf16(scale * (A * B^T)), fp32 accumulation.
 //
-// The all-gather-side chunk GEMM over a quantized UserBuffer.  "[Feature Request] Support
+// The all-gather-side chunk GEMM over a quantized UserBuffer, and the reduce-scatter
+// side's K-slice GEMMs on quantized operands (batch entries, bf16 partials).  "[Feature Request] Support
 // dynamic token counts in TP communication/GEMM overlap" (Transformer Engine issue 3564),
 // "Implementation approach in the prototype", names quantized (FP8) buffers and leaves
 // them outside the prototype's first scope; this is that extension, with the plain
@@ -42,6 +43,7 @@ struct F8Params {
   const uint8_t* b;
   uint16_t* c;
   int64_t lda, ldb, ldc;
+  int64_t sa, sb, sc;                    // batch strides (bytes, bytes, elements)
   int32_t n, k;
   float scale;
   int32_t tiles_n;
@@ -83,6 +85,7 @@ struct F8Cfg {
 template <class C>
 struct F8Tile {
   int lane, wave, group, wm, wn, m0, m_end, n0;
+  uint16_t* cg;
   i32x4 ra, rb;
   uint32_t a_off[C::NA], b_off[C::NB];
   uint32_t rd_a, rd_b;  // byte offset of this lane's first A / B fragment row in a stage
@@ -100,8 +103,10 @@ struct F8Tile {
     n0 = tn * C::BN;
     const int rows_a = min(C::BM, m_end - m0);
     const int rows_b = min(C::BN, p.n - n0);
-    ra = make_rsrc(p.a + (int64_t)m0 * p.lda, (uint32_t)(rows_a * p.lda));
-    rb = make_rsrc(p.b + (int64_t)n0 * p.ldb, (uint32_t)(rows_b * p.ldb));
+    // batch entry blockIdx.z: A and B start sa / sb bytes further (a K slice), C sc elements
+    ra = make_rsrc(p.a + blockIdx.z * p.sa + (int64_t)m0 * p.lda, (uint32_t)(rows_a * p.lda));
+    rb = make_rsrc(p.b + blockIdx.z * p.sb + (int64_t)n0 * p.ldb, (uint32_t)(rows_b * p.ldb));
+    cg = p.c + blockIdx.z * p.sc;
     // Direct load t of this wave covers operand rows 16 (wave * N + t) + lane / 4; lane
     // slot lane % 4 holds k-chunk slot ^ a_swz(row).  Rows past the operand's valid rows
     // are beyond the resource's size and read as zeros.
@@ -182,7 +187,7 @@ struct F8Tile {
       const int r = v / VPR, cc = (v % VPR) * 8;
       const int gr = m0 + r, gc = n0 + cc;
       if (gr < m_end && gc < p.n)
-        *GLOBAL_PTR(u32x4, p.c + (int64_t)gr * p.ldc + gc) = *LDS_PTR(const u32x4, ct + r * C::LDC + cc);
+        *GLOBAL_PTR(u32x4, cg + (int64_t)gr * p.ldc + gc) = *LDS_PTR(const u32x4, ct + r * C::LDC + cc);
     }
   }
 };
@@ -260,6 +265,9 @@ hipError_t launch(const GemmF8Args& g, const GemmUnits& units, hipStream_t strea
   p.lda = g.lda;
   p.ldb = g.ldb;
   p.ldc = g.ldc;
+  p.sa = g.a_batch_stride;
+  p.sb = g.b_batch_stride;
+  p.sc = g.c_batch_stride;
   p.n = g.n;
   p.k = g.k;
   p.scale = g.scale;
@@ -276,7 +284,7 @@ hipError_t launch(const GemmF8Args& g, const GemmUnits& units, hipStream_t strea
   if (tiles == 0) return hipSuccess;
   p.group = tile_group(tiles, 1);
   const int64_t grid = tiles;
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (grid > 0x7FFFFFFF || g.batch < 1 || g.batch > 65535) return hipErrorInvalidValue;
   auto kernel = &gemm_fp8_pingpong<C, F8_D>;
   static bool configured = false;
   if (!configured) {
@@ -285,7 +293,8 @@ hipError_t launch(const GemmF8Args& g, const GemmUnits& units, hipStream_t strea
     if (e != hipSuccess) return e;
     configured = true;
   }
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(C::THREADS), C::LDS_BYTES, stream, p);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid, 1, g.batch), dim3(C::THREADS), C::LDS_BYTES,
+                     stream, p);
   return hipGetLastError();
 }
 
@@ -298,7 +307,7 @@ bool use_128(const GemmF8Args& g, const GemmUnits& u) {
   }
   const int share = 256 / (g.concurrency > 1 ? g.concurrency : 1);
   auto cost = [&](int bm, double eff) {
-    const int64_t tiles = row_tiles(u, bm) * ((g.n + 255) / 256);
+    const int64_t tiles = row_tiles(u, bm) * ((g.n + 255) / 256) * g.batch;
     const int64_t slots = share > 0 ? share : 1;
     return (double)((tiles + slots - 1) / slots) * bm * 256 / eff;
   };
@@ -313,7 +322,7 @@ bool gemm_fp8_shape_supported(const GemmF8Args& g) {
 }
 
 hipError_t launch_gemm_fp8_units(const GemmF8Args& g, const GemmUnits& u, hipStream_t stream) {
-  if (g.n <= 0 || u.n <= 0) return hipSuccess;
+  if (g.n <= 0 || u.n <= 0 || g.batch <= 0) return hipSuccess;
   if (u.n > kMaxGemmUnits || g.k <= 0 || g.k % kGemmF8KStep != 0 || g.n % 8 != 0 ||
       g.lda % 16 != 0 || g.ldb % 16 != 0 || g.ldc % 8 != 0 || !gemm_fp8_shape_supported(g))
     return hipErrorInvalidValue;

@@ -278,6 +278,27 @@ ub_status_t check_ld(ub_ctx* h, const char* name, int64_t ld, int64_t cols) {
   return UB_OK;
 }
 
+// The reduction of active rows [row0, row0 + rows): the tp partial slots of the packed
+// workspace prefix (slot s at element s*T*H) into out (row stride ldo), ascending or in ring
+// order (each row's shard T/tp decides its hop order).
+ubx::ReduceArgs reduce_args(const ub_ctx* h, int64_t row0, int64_t rows, void* out, int64_t ldo,
+                            bool ring) {
+  const int64_t H = h->hidden;
+  ubx::ReduceArgs r{};
+  r.parts = h->ws + row0 * H;
+  r.slot_stride = h->T * H;
+  r.ldp = H;
+  r.nslots = h->tp;
+  r.out = static_cast<uint16_t*>(out) + row0 * ldo;
+  r.ldo = ldo;
+  r.rows = rows;
+  r.cols = H;
+  r.ring = ring;
+  r.row0 = row0;
+  r.shard_rows = h->T / h->tp;
+  return r;
+}
+
 }  // namespace
 
 extern "C" {
@@ -668,6 +689,19 @@ UB_API ub_status_t ub_quantize_in(ub_handle_t h, const void* src, int64_t rows,
   return e == hipSuccess ? UB_OK : hip_fail(h, e, "quantize launch");
 }
 
+UB_API ub_status_t ub_quantize_e4m3(const void* src, int64_t lds, void* dst, int64_t ldd,
+                                    int64_t rows, int64_t cols, float scale, ub_stream_t stream) {
+  if (!src || !dst || !aligned16(src) || !aligned16(dst)) return UB_ERR_INVALID_ARG;
+  if (rows < 0 || cols < 0 || cols % 8 != 0 || lds % 8 != 0 || ldd % 8 != 0 || lds < cols ||
+      ldd < cols || !std::isfinite(scale))
+    return UB_ERR_INVALID_ARG;
+  if (rows == 0 || cols == 0) return UB_OK;
+  hipError_t e = ubx::launch_quantize_e4m3(static_cast<const uint16_t*>(src), lds,
+                                           static_cast<uint8_t*>(dst), ldd, rows, cols, scale,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? UB_OK : UB_ERR_HIP;
+}
+
 UB_API ub_status_t ub_gemm_ag_chunked_fp8(ub_handle_t h, const void* w, int64_t n_cols,
                                           int64_t ldw, float scale_inv_a, float scale_inv_w,
                                           void* c, int64_t ldc, const ub_overlap_cfg_t* cfg,
@@ -788,18 +822,7 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
                       [&] { return ubx::launch_gemm_bf16_units(g, units, caller); },
                       "slice GEMM launch");
     if (st != UB_OK) return st;
-    ubx::ReduceArgs r{};
-    r.parts = h->ws;
-    r.slot_stride = T * H;
-    r.ldp = H;
-    r.nslots = tp;
-    r.out = static_cast<uint16_t*>(out);
-    r.ldo = ldo;
-    r.rows = T;
-    r.cols = H;
-    r.ring = cfg->reduce_order == UB_REDUCE_RING;
-    r.row0 = 0;
-    r.shard_rows = T / tp;
+    const ubx::ReduceArgs r = reduce_args(h, 0, T, out, ldo, cfg->reduce_order == UB_REDUCE_RING);
     return timed_launch(h, caller, 1, double(tp - 1) * T * H, 2.0 * (tp + 1) * T * H,
                         [&] { return ubx::launch_reduce_partials(r, caller); }, "reduce launch");
   }
@@ -835,20 +858,103 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
                       "slice GEMM launch");
     if (st != UB_OK) return st;
     // the reduction of this chunk follows its GEMMs on the same stream
-    ubx::ReduceArgs r{};
-    r.parts = h->ws + u.row0 * H;
-    r.slot_stride = T * H;
-    r.ldp = H;
-    r.nslots = tp;
-    r.out = static_cast<uint16_t*>(out) + u.row0 * ldo;
-    r.ldo = ldo;
-    r.rows = rows;
-    r.cols = H;
-    r.ring = cfg->reduce_order == UB_REDUCE_RING;
-    r.row0 = u.row0;
-    r.shard_rows = T / tp;
+    const ubx::ReduceArgs r =
+        reduce_args(h, u.row0, rows, out, ldo, cfg->reduce_order == UB_REDUCE_RING);
     const double rbytes = 2.0 * (tp + 1) * rows * H;
     st = timed_launch(h, s, 1, double(tp - 1) * rows * H, rbytes,
+                      [&] { return ubx::launch_reduce_partials(r, s); }, "reduce launch");
+    if (st != UB_OK) return st;
+  }
+  return join_streams(h, caller, S);
+}
+
+UB_API ub_status_t ub_gemm_rs_chunked_fp8(ub_handle_t h, const void* a, int64_t k, int64_t lda,
+                                          const void* w, int64_t ldw, float scale_inv_a,
+                                          float scale_inv_w, void* out, int64_t ldo,
+                                          const ub_overlap_cfg_t* cfg, ub_stream_t stream) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  ub_status_t st = need_dtype(h, UB_DTYPE_BF16, "the reduce-scatter GEMM (bf16 partials)");
+  if (st != UB_OK) return st;
+  if ((st = check_cfg_common(h, cfg)) != UB_OK) return st;
+  if (!h->ws) return fail(h, UB_ERR_NOT_INITIALIZED, "no reduce-scatter workspace registered");
+  if (!a || !w || !out) return fail(h, UB_ERR_INVALID_ARG, "a, w and out must be non-NULL");
+  if (!aligned16(a) || !aligned16(w) || !aligned16(out))
+    return fail(h, UB_ERR_INVALID_ARG, "a, w and out must be 16-byte aligned");
+  if (k <= 0 || k % h->tp != 0 || k > INT32_MAX)
+    return fail(h, UB_ERR_INVALID_ARG, "k=%lld must be > 0 and divisible by tp_size %d",
+                (long long)k, h->tp);
+  const int64_t ks = k / h->tp;
+  if (ks % ubx::kGemmF8KStep != 0)
+    return fail(h, UB_ERR_UNSUPPORTED, "k / tp_size = %lld must be a multiple of %d",
+                (long long)ks, ubx::kGemmF8KStep);
+  const int64_t H = h->hidden;
+  if (lda < k || lda % 16 != 0)
+    return fail(h, UB_ERR_INVALID_ARG, "lda=%lld must be >= k=%lld and a multiple of 16",
+                (long long)lda, (long long)k);
+  if (ldw < k || ldw % 16 != 0)
+    return fail(h, UB_ERR_INVALID_ARG, "ldw=%lld must be >= k=%lld and a multiple of 16",
+                (long long)ldw, (long long)k);
+  if ((st = check_ld(h, "ldo", ldo, H)) != UB_OK) return st;
+  if (!std::isfinite(scale_inv_a) || !std::isfinite(scale_inv_w))
+    return fail(h, UB_ERR_INVALID_ARG, "scales must be finite");
+  const int64_t T = h->T;
+  const int32_t tp = h->tp;
+  // slice s: columns [s*ks, (s+1)*ks) of A's rows and of W's rows; partial s at workspace
+  // element s*T*H (offsets from the active T)
+  ubx::GemmF8Args g{};
+  g.a = static_cast<const uint8_t*>(a);
+  g.lda = lda;
+  g.a_batch_stride = ks;
+  g.b = static_cast<const uint8_t*>(w);
+  g.ldb = ldw;
+  g.b_batch_stride = ks;
+  g.c = h->ws;
+  g.ldc = H;
+  g.c_batch_stride = T * H;
+  g.n = static_cast<int32_t>(H);
+  g.k = static_cast<int32_t>(ks);
+  g.batch = tp;
+  g.scale = scale_inv_a * scale_inv_w;  // one fp32 product
+  if (!ubx::gemm_fp8_shape_supported(g))
+    return fail(h, UB_ERR_UNSUPPORTED, "lda or ldw too large");
+  st = ubx::build_plan(T, tp, *cfg, UB_OP_RS, &h->plan, &h->last_error);
+  if (st != UB_OK) return st;
+  hipStream_t caller = static_cast<hipStream_t>(stream);
+  const bool ring = cfg->reduce_order == UB_REDUCE_RING;
+
+  if (cfg->atomic_gemm) {
+    ubx::GemmUnits units;
+    if ((st = plan_units(h, &units)) != UB_OK) return st;
+    if ((st = ensure_device(h, 1)) != UB_OK) return st;
+    g.concurrency = 1;
+    st = timed_launch(h, caller, 0, 2.0 * T * k * H, double(T * k + k * H + 2 * tp * T * H),
+                      [&] { return ubx::launch_gemm_fp8_units(g, units, caller); },
+                      "fp8 slice GEMM launch");
+    if (st != UB_OK) return st;
+    const ubx::ReduceArgs r = reduce_args(h, 0, T, out, ldo, ring);
+    return timed_launch(h, caller, 1, double(tp - 1) * T * H, 2.0 * (tp + 1) * T * H,
+                        [&] { return ubx::launch_reduce_partials(r, caller); }, "reduce launch");
+  }
+
+  const int S = h->plan.n_streams;
+  if ((st = ensure_device(h, S)) != UB_OK) return st;
+  if ((st = fork_streams(h, caller, S)) != UB_OK) return st;
+  g.concurrency = S;
+  for (const ub_plan_unit_t& u : h->plan.units) {
+    const int64_t rows = u.row1 - u.row0;
+    if (rows <= 0) continue;
+    if (rows > kMaxRowsPerUnit) return fail(h, UB_ERR_UNSUPPORTED, "unit too large");
+    hipStream_t s = u.stream == 0 ? caller : h->streams[u.stream];
+    ubx::GemmUnits one;
+    one.n = 1;
+    one.row0[0] = static_cast<int32_t>(u.row0);
+    one.rows[0] = static_cast<int32_t>(rows);
+    st = timed_launch(h, s, 0, 2.0 * rows * k * H, double(rows * k + k * H + 2 * tp * rows * H),
+                      [&] { return ubx::launch_gemm_fp8_units(g, one, s); },
+                      "fp8 slice GEMM launch");
+    if (st != UB_OK) return st;
+    const ubx::ReduceArgs r = reduce_args(h, u.row0, rows, out, ldo, ring);
+    st = timed_launch(h, s, 1, double(tp - 1) * rows * H, 2.0 * (tp + 1) * rows * H,
                       [&] { return ubx::launch_reduce_partials(r, s); }, "reduce launch");
     if (st != UB_OK) return st;
   }
@@ -867,18 +973,7 @@ UB_API ub_status_t ub_reduce_partials(ub_handle_t h, void* out, int64_t ldo,
   if (st != UB_OK) return st;
   if ((st = ensure_device(h, 1)) != UB_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  ubx::ReduceArgs r{};
-  r.parts = h->ws;
-  r.slot_stride = h->T * h->hidden;
-  r.ldp = h->hidden;
-  r.nslots = h->tp;
-  r.out = static_cast<uint16_t*>(out);
-  r.ldo = ldo;
-  r.rows = h->T;
-  r.cols = h->hidden;
-  r.ring = reduce_order == UB_REDUCE_RING;
-  r.row0 = 0;
-  r.shard_rows = h->T / h->tp;
+  const ubx::ReduceArgs r = reduce_args(h, 0, h->T, out, ldo, reduce_order == UB_REDUCE_RING);
   const double rbytes = 2.0 * (h->tp + 1) * h->T * h->hidden;
   return timed_launch(h, s, 1, double(h->tp - 1) * h->T * h->hidden, rbytes,
                       [&] { return ubx::launch_reduce_partials(r, s); }, "reduce launch");

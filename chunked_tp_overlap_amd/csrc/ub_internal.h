@@ -69,8 +69,10 @@ int64_t row_tiles(const GemmUnits& u, int bm);
 
 // out[r, c] = bf16( sum_{s < nslots} float(parts[s*slot_stride + r*ldp + c]) ), ascending s.
 // cols % 8 == 0, ldp/ldo % 8 == 0, pointers 16-byte aligned.
-// FP8 (E4M3) all-gather GEMM: C [*, n] bf16 = bf16(scale * A B^T) with A [*, k] and
-// B [n, k] E4M3 codes (row strides in bytes), units of rows as for launch_gemm_bf16_units.
+// FP8 (E4M3) GEMM: C [*, n] bf16 = bf16(scale * A B^T) with A [*, k] and B [n, k] E4M3
+// codes (row strides in bytes), units of rows as for launch_gemm_bf16_units.  batch > 1
+// runs batch entries (blockIdx.z) whose A and B start a/b_batch_stride bytes further and
+// whose C starts c_batch_stride elements further (the reduce-scatter side's K slices).
 constexpr int kGemmF8KStep = 64;
 struct GemmF8Args {
   const uint8_t* a;
@@ -82,6 +84,8 @@ struct GemmF8Args {
   int32_t n, k;
   float scale;
   int concurrency;
+  int64_t a_batch_stride = 0, b_batch_stride = 0, c_batch_stride = 0;
+  int32_t batch = 1;
 };
 bool gemm_fp8_shape_supported(const GemmF8Args& g);
 hipError_t launch_gemm_fp8_units(const GemmF8Args& g, const GemmUnits& u, hipStream_t stream);

@@ -43,7 +43,8 @@ EXPORTS = (
     "ub_overlap_cfg_default", "ub_required_bytes", "ub_init", "ub_set_active_shape",
     "ub_get_active_shape", "ub_get_capacity_shape", "ub_get_plan", "ub_copy_in",
     "ub_gemm_ag_chunked", "ub_gemm_ag_arrival", "ub_deliver_chunks", "ub_quantize_in",
-    "ub_gemm_ag_chunked_fp8", "ub_gemm_rs_chunked", "ub_reduce_partials",
+    "ub_gemm_ag_chunked_fp8", "ub_gemm_rs_chunked", "ub_gemm_rs_chunked_fp8",
+    "ub_quantize_e4m3", "ub_reduce_partials",
     "ub_set_kernel_timing", "ub_get_kernel_timing", "ub_destroy", "ub_status_string",
     "ub_last_error",
 )
@@ -95,6 +96,9 @@ _sig = {
     "ub_gemm_ag_chunked_fp8": (_I32, [_H, _P, _I64, _I64, ctypes.c_float, ctypes.c_float, _P,
                                       _I64, _CFGP, _P]),
     "ub_gemm_rs_chunked": (_I32, [_H, _P, _I64, _I64, _P, _I64, _P, _I64, _CFGP, _P]),
+    "ub_gemm_rs_chunked_fp8": (_I32, [_H, _P, _I64, _I64, _P, _I64, ctypes.c_float, ctypes.c_float,
+                                      _P, _I64, _CFGP, _P]),
+    "ub_quantize_e4m3": (_I32, [_P, _I64, _P, _I64, _I64, _I64, ctypes.c_float, _P]),
     "ub_reduce_partials": (_I32, [_H, _P, _I64, _I32, _P]),
     "ub_set_kernel_timing": (_I32, [_H, _I32]),
     "ub_get_kernel_timing": (_I32, [_H, ctypes.POINTER(ub_kernel_stats_t),
@@ -248,6 +252,21 @@ def ub_gemm_ag_chunked_fp8(h, w, n_cols, ldw, scale_inv_a, scale_inv_w, c, ldc, 
 def ub_gemm_rs_chunked(h, a, k, lda, w, ldw, out, ldo, cfg, stream=None):
     _check(_lib.ub_gemm_rs_chunked(h, _ptr(a), k, lda, _ptr(w), ldw, _ptr(out), ldo,
                                    ctypes.byref(cfg), _stream(stream)), h)
+
+
+def ub_gemm_rs_chunked_fp8(h, a, k, lda, w, ldw, scale_inv_a, scale_inv_w, out, ldo, cfg,
+                           stream=None):
+    """a: [T, k] E4M3 codes (row stride lda bytes); w: [hidden, k] E4M3 codes (row stride
+    ldw bytes); out: [T, hidden] bf16 (row stride ldo elements)."""
+    _check(_lib.ub_gemm_rs_chunked_fp8(h, _ptr(a), k, lda, _ptr(w), ldw, float(scale_inv_a),
+                                       float(scale_inv_w), _ptr(out), ldo, ctypes.byref(cfg),
+                                       _stream(stream)), h)
+
+
+def ub_quantize_e4m3(src, lds, dst, ldd, rows, cols, scale, stream=None):
+    """dst [rows, cols] E4M3 (row stride ldd bytes) = quantized src (bf16, row stride lds)."""
+    _check(_lib.ub_quantize_e4m3(_ptr(src), lds, _ptr(dst), ldd, rows, cols, float(scale),
+                                 _stream(stream)))
 
 
 def ub_reduce_partials(h, out, ldo, reduce_order="ascending", stream=None):

@@ -98,8 +98,9 @@ typedef enum {
  * bf16 buffers and name quantized (FP8) ones as outside that first scope ([TE#3564]
  * "Implementation approach", last paragraph).  UB_DTYPE_BF16 is the main path;
  * UB_DTYPE_FP8_E4M3 is the extension to quantized buffers (OCP E4M3 codes, one byte per
- * element, all-gather side only: ub_quantize_in, ub_gemm_ag_chunked_fp8).  FP16 and E5M2
- * are rejected with UB_ERR_DTYPE. */
+ * element) on the all-gather side: ub_quantize_in, ub_gemm_ag_chunked_fp8.  On the
+ * reduce-scatter side the communicated partials stay bf16, so ub_gemm_rs_chunked_fp8
+ * takes E4M3 operands on a bf16 handle.  FP16 and E5M2 are rejected with UB_ERR_DTYPE. */
 typedef enum {
   UB_DTYPE_BF16 = 0,
   UB_DTYPE_FP16 = 1,
@@ -306,6 +307,12 @@ UB_API ub_status_t ub_gemm_ag_chunked_fp8(ub_handle_t h, const void* w, int64_t 
  *     SDMA copy costs about 80 us whatever its size.
  *   atomic_gemm = 1 -> UB_ERR_UNSUPPORTED (units are gated by events, which needs the
  *     host-loop schedule); more than 64 chunks -> UB_ERR_UNSUPPORTED.
+ *   Hardware queues: the call keeps up to four streams busy (the caller's, two workers,
+ *     the copy stream).  HIP maps a process's streams onto GPU_MAX_HW_QUEUES hardware
+ *     queues (4 by default), and streams that share a queue run in issue order: with
+ *     other streams in the process, copies and GEMMs then serialise (measured on qkv:
+ *     0.30 instead of 0.22 ms per call with three other streams and 4 queues, 0.22 ms with
+ *     8 queues).  A process that overlaps arrivals should raise GPU_MAX_HW_QUEUES.
  * The copies start when the caller's stream reaches the call; the call as a whole is
  * ordered on `stream`.  The caller must not touch the UB prefix or src until then. */
 UB_API ub_status_t ub_gemm_ag_arrival(ub_handle_t h, const void* src, int32_t src_on_host,
@@ -336,6 +343,39 @@ UB_API ub_status_t ub_deliver_chunks(ub_handle_t h, const void* src, int32_t src
 UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, int64_t lda,
                                       const void* w, int64_t ldw, void* out, int64_t ldo,
                                       const ub_overlap_cfg_t* cfg, ub_stream_t stream);
+
+/* FP8 (E4M3) reduce-scatter GEMM: ub_gemm_rs_chunked with E4M3 operands and one
+ * dequantization factor per tensor (the reading of [TE#3564]'s quantized buffers taken
+ * for ub_gemm_ag_chunked_fp8).  The partials and the sum are bf16, as in
+ * ub_gemm_rs_chunked, so the handle is a bf16 one with a registered workspace.  With
+ * Ks = k / tp_size, for every plan unit and slice s:
+ *   P_s[t, j] = bf16_rne( (scale_inv_a * scale_inv_w) * sum_{k in [s Ks, (s+1) Ks)} A[t, k] * W[j, k] )
+ * (fp32 accumulation; the two factors multiplied once in fp32), written to the workspace
+ * at element (s*T + t) * hidden + j, then summed into out exactly as ub_gemm_rs_chunked
+ * sums (cfg->reduce_order).
+ *   A   [T, k] E4M3 codes, row stride lda bytes (>= k, multiple of 16), device memory;
+ *   W   [hidden, k] E4M3 codes, row j = output column j, row stride ldw bytes (>= k,
+ *       multiple of 16): the weight stored N x K, as FP8 GEMMs take it;
+ *   out [T, hidden] bf16, row stride ldo elements (>= hidden, multiple of 8).
+ * k % tp_size == 0 (else INVALID_ARG), Ks % 64 == 0 (else UNSUPPORTED); scales finite
+ * (else INVALID_ARG); a bf16 handle (else UB_ERR_DTYPE) with a workspace (else
+ * NOT_INITIALIZED).  Plan, streams, atomic_gemm and the write bounds as for
+ * ub_gemm_rs_chunked. */
+UB_API ub_status_t ub_gemm_rs_chunked_fp8(ub_handle_t h, const void* a, int64_t k, int64_t lda,
+                                          const void* w, int64_t ldw, float scale_inv_a,
+                                          float scale_inv_w, void* out, int64_t ldo,
+                                          const ub_overlap_cfg_t* cfg, ub_stream_t stream);
+
+/* E4M3 quantization of a bf16 matrix into caller memory, with no handle: the operands of
+ * ub_gemm_rs_chunked_fp8 (and weights for ub_gemm_ag_chunked_fp8).
+ *   dst[r, c] = sat(RNE_e4m3(fp32(src[r, c] * scale)))   for r < rows, c < cols,
+ * the rule of ub_quantize_in.  src is bf16 with row stride lds elements, dst is E4M3 with
+ * row stride ldd bytes; both device memory and 16-byte aligned; cols, lds and ldd
+ * multiples of 8 with lds, ldd >= cols; rows, cols >= 0; scale finite (else
+ * UB_ERR_INVALID_ARG; there is no handle, so no message).  rows == 0 or cols == 0 does
+ * nothing.  Asynchronous on `stream`. */
+UB_API ub_status_t ub_quantize_e4m3(const void* src, int64_t lds, void* dst, int64_t ldd,
+                                    int64_t rows, int64_t cols, float scale, ub_stream_t stream);
 
 /* The reduce-scatter sum alone: out[t, :] for all active rows t in [0, T) from the
  * tp_size partial slots currently in the workspace (as left by ub_gemm_rs_chunked at the

@@ -78,12 +78,20 @@ def check_close(g_bits, o_bits, a_bits, w_bits, what, k_terms=None, gate=4e-3, m
     return stats
 
 
-def check_rs_close(g_out, o_out, a_bits, w_bits, tp, what, gate=4e-3, min_equal=0.97):
+def check_rs_close(g_out, o_out, a_bits, w_bits, tp, what, gate=4e-3, min_equal=0.97, ring=False,
+                   scale=1.0, slice_err=None):
     """Row-parallel result: gate with full-K norms; tight bound adds each bf16 partial's
-    rounding and the fp32 sum of the tp partials."""
+    rounding and the fp32 sum of the tp partials.  ring=True (the ring-order sum, one bf16
+    rounding per hop on each side): the two sides' running sums start from different
+    partials and each hop rounds both to bf16, so each of the tp - 1 hops adds up to one
+    bf16 ulp of the hop's magnitude (at most sum_s |partial_s|).  scale: a factor applied to
+    every product before the partials' rounding (the FP8 path's dequantization; its one
+    fp32 multiply is far inside the bf16 terms).  slice_err: per slice, the bound on its
+    accumulation error before the bf16 rounding, in the scaled units (default: Ks fp32
+    roundings of sum|ab|)."""
     g = obf16.decode(g_out)
     o = obf16.decode(o_out)
-    A = obf16.decode(a_bits)
+    A = obf16.decode(a_bits) * float(scale)
     W = obf16.decode(w_bits)
     k = A.shape[1]
     ks = k // tp
@@ -97,9 +105,15 @@ def check_rs_close(g_out, o_out, a_bits, w_bits, tp, what, gate=4e-3, min_equal=
         part = np.abs(A[:, sl] @ W[sl])
         # |p_gpu - p_oracle| <= 2 u16 |E_s| + (1 + u16) Ks u32 sum|ab|, plus the fp32 sum of
         # the tp partials: tp u32 |p_gpu| with |p_gpu| <= (1 + u16)(|E_s| + Ks u32 sum|ab|)
-        slice_err = ks * 2.0 ** -24 * absprod
-        tight_b = tight_b + 2 * 2.0 ** -8 * part + (1 + 2.0 ** -8) * slice_err \
-            + tp * 2.0 ** -24 * (1 + 2.0 ** -8) * (part + slice_err)
+        s_err = ks * 2.0 ** -24 * absprod if slice_err is None else slice_err[s]
+        tight_b = tight_b + 2 * 2.0 ** -8 * part + (1 + 2.0 ** -8) * s_err \
+            + tp * 2.0 ** -24 * (1 + 2.0 ** -8) * (part + s_err)
+    if ring:
+        mag = sum(np.abs(A[:, s * ks:(s + 1) * ks] @ W[s * ks:(s + 1) * ks])
+                  + (ks * 2.0 ** -24 * (np.abs(A[:, s * ks:(s + 1) * ks]) @ np.abs(W[s * ks:(s + 1) * ks]))
+                     if slice_err is None else slice_err[s])
+                  for s in range(tp)) * (1 + 2.0 ** -6)
+        tight_b = tight_b + (tp - 1) * obf16.ulp(obf16.encode_rne(mag))
     eq = float(np.mean(np.asarray(g_out) == np.asarray(o_out)))
     stats = {"max_gate_ratio": float(np.max(err / np.maximum(gate_b, 1e-300))),
              "max_tight_ratio": float(np.max(err / tight_b)), "bit_equal": eq}

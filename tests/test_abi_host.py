@@ -301,3 +301,53 @@ def test_atomic_gemm_unit_limit_checked_before_any_hip_call():
         assert "64" in ub.ub_last_error(h)
     finally:
         ub.ub_destroy(h)
+
+
+def test_rs_fp8_and_quantize_argument_errors_before_any_hip_call():
+    """ub_gemm_rs_chunked_fp8 runs on a bf16 handle with a workspace (the partials are
+    bf16); its operand checks, and ub_quantize_e4m3's, all come before any HIP call."""
+    h8 = ub.ub_init(512, 256, 2, ub.UB_DTYPE_FP8_E4M3, FAKE, 512 * 256)
+    hb = _handle(512, 256, 2)
+    hn = ub.ub_init(512, 256, 2, ub.UB_DTYPE_BF16, FAKE, 512 * 256 * 2)  # no workspace
+    try:
+        def st(name, *args):
+            return ub.STATUS[ub.raw_call(name, *args)]
+        cfg = ub.make_cfg("pipeline", 2)
+        cp = ctypes.byref(cfg)
+        f = ctypes.c_float
+        ok = (FAKE, 512, 512, FAKE, 512, f(1), f(1), FAKE, 256, cp, None)
+        assert st("ub_gemm_rs_chunked_fp8", h8, *ok) == "UB_ERR_DTYPE"
+        assert st("ub_gemm_rs_chunked_fp8", hn, *ok) == "UB_ERR_NOT_INITIALIZED"
+        assert st("ub_gemm_rs_chunked_fp8", None, *ok) == "UB_ERR_NOT_INITIALIZED"
+        bad = [
+            (FAKE, 511, 512, FAKE, 512, f(1), f(1), FAKE, 256, cp, None),        # k % tp
+            (FAKE, 512, 496, FAKE, 512, f(1), f(1), FAKE, 256, cp, None),        # lda < k
+            (FAKE, 512, 520, FAKE, 512, f(1), f(1), FAKE, 256, cp, None),        # lda % 16
+            (FAKE, 512, 512, FAKE, 504, f(1), f(1), FAKE, 256, cp, None),        # ldw < k
+            (FAKE, 512, 512, FAKE, 512, f(float("inf")), f(1), FAKE, 256, cp, None),
+            (FAKE, 512, 512, FAKE, 512, f(1), f(1), FAKE, 252, cp, None),        # ldo
+            (FAKE + 8, 512, 512, FAKE, 512, f(1), f(1), FAKE, 256, cp, None),    # alignment
+            (None, 512, 512, FAKE, 512, f(1), f(1), FAKE, 256, cp, None),
+            (FAKE, 512, 512, FAKE, 512, f(1), f(1), FAKE, 256, None, None),      # cfg
+        ]
+        for args in bad:
+            assert st("ub_gemm_rs_chunked_fp8", hb, *args) == "UB_ERR_INVALID_ARG", args
+        # k / tp not a multiple of the 64-code step
+        assert st("ub_gemm_rs_chunked_fp8", hb, FAKE, 192, 192, FAKE, 192, f(1), f(1), FAKE, 256,
+                  cp, None) == "UB_ERR_UNSUPPORTED"
+        # quantize: alignment, strides, sizes, scale; empty is a no-op
+        q = "ub_quantize_e4m3"
+        assert st(q, FAKE + 8, 64, FAKE, 64, 4, 64, f(1), None) == "UB_ERR_INVALID_ARG"
+        assert st(q, FAKE, 64, FAKE + 4, 64, 4, 64, f(1), None) == "UB_ERR_INVALID_ARG"
+        assert st(q, FAKE, 60, FAKE, 64, 4, 60, f(1), None) == "UB_ERR_INVALID_ARG"   # cols % 8
+        assert st(q, FAKE, 56, FAKE, 64, 4, 64, f(1), None) == "UB_ERR_INVALID_ARG"   # lds < cols
+        assert st(q, FAKE, 64, FAKE, 56, 4, 64, f(1), None) == "UB_ERR_INVALID_ARG"   # ldd < cols
+        assert st(q, FAKE, 64, FAKE, 64, -1, 64, f(1), None) == "UB_ERR_INVALID_ARG"
+        assert st(q, FAKE, 64, FAKE, 64, 4, 64, f(float("nan")), None) == "UB_ERR_INVALID_ARG"
+        assert st(q, None, 64, FAKE, 64, 4, 64, f(1), None) == "UB_ERR_INVALID_ARG"
+        assert st(q, FAKE, 64, FAKE, 64, 0, 64, f(1), None) == "UB_OK"
+        assert st(q, FAKE, 64, FAKE, 64, 4, 0, f(1), None) == "UB_OK"
+    finally:
+        ub.ub_destroy(h8)
+        ub.ub_destroy(hb)
+        ub.ub_destroy(hn)
