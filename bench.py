@@ -157,9 +157,13 @@ def main():
     # workers, the copy stream).  HIP maps a process's streams onto GPU_MAX_HW_QUEUES
     # hardware queues (default 4); streams that share a queue run in issue order, which
     # serialises the arrival copies with the GEMMs once the benchmark's earlier sections
-    # have created streams of their own.  Eight queues keep them apart.  Set before HIP
-    # initialises; an explicit setting in the environment wins.
-    os.environ.setdefault("GPU_MAX_HW_QUEUES", "8")
+    # have created streams of their own.  At least eight queues keep them apart.  Set
+    # before HIP initialises; a larger setting in the environment is kept.
+    try:
+        queues = int(os.environ.get("GPU_MAX_HW_QUEUES", "4"))
+    except ValueError:
+        queues = 4
+    os.environ["GPU_MAX_HW_QUEUES"] = str(max(queues, 8))
     import numpy as np
     import torch
 
@@ -179,9 +183,7 @@ def main():
     primary = q.cfg(atomic=True)
 
     log(f"warmup {args.warmup}, timed {args.steps} steps of {len(q.Ts)} microbatches (atomic_gemm)")
-    state = DeviceState(torch)
-    with state:
-        sec = q.timed(primary, args.steps, args.warmup)
+    sec = q.timed(primary, args.steps, args.warmup)
     tflops = q.flops / sec / 1e12
     log(f"primary: {sec * 1e3:.3f} ms/step, {tflops:.1f} TFLOP/s")
 
@@ -291,7 +293,7 @@ def main():
                         "gcn_arch": getattr(props, "gcnArchName", ""),
                         "gemm_src_hash": src_hash(GEMM_SRC),
                         "gpu_max_hw_queues": os.environ.get("GPU_MAX_HW_QUEUES")}
-    result["device_state"] = state.summary()
+    result["device_state"] = device_state(torch)
 
     if not args.no_secondary:
         result["secondary"] = secondary(ub, wl, torch, np, dev)
@@ -303,90 +305,31 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-class DeviceState:
-    """Samples the GPU's shader clock and socket power (amdsmi) on a thread while a timed
-    region runs, and reports the mean clock, the power against the cap, and the dense bf16
-    peak recomputed at the mean clock.  Reports why when amdsmi is not usable."""
-
-    def __init__(self, torch, period_s=0.005):
-        self.period, self.samples, self.error = period_s, [], None
-        self.cap_w, self.bdf, self._h, self._stop, self._thr = None, None, None, None, None
-        try:
-            import amdsmi
-            self._smi = amdsmi
-            amdsmi.amdsmi_init()
-            handles = amdsmi.amdsmi_get_processor_handles()
-            p = torch.cuda.get_device_properties(0)
-            bus = getattr(p, "pci_bus_id", None)
-            if bus is not None:
-                want = f"{getattr(p, 'pci_domain_id', 0):04x}:{bus:02x}:{getattr(p, 'pci_device_id', 0):02x}"
-                for h in handles:
-                    if amdsmi.amdsmi_get_gpu_device_bdf(h).lower().startswith(want):
-                        self._h = h
-            if self._h is None and len(handles) == 1:
-                self._h = handles[0]
-            if self._h is None:
-                raise RuntimeError(f"no amdsmi device matches cuda:0 among {len(handles)}")
-            self.bdf = amdsmi.amdsmi_get_gpu_device_bdf(self._h)
-            try:
-                cap = amdsmi.amdsmi_get_power_cap_info(self._h).get("power_cap")
-                self.cap_w = round(cap / 1e6 if cap and cap > 1e4 else cap, 1) if cap else None
-            except Exception:  # noqa: BLE001 - the cap is optional
-                pass
-        except Exception as e:  # noqa: BLE001 - any failure just disables the sampling
-            self.error = f"{type(e).__name__}: {e}"
-
-    def _sample(self):
-        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
-        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
-        if not clks and isinstance(m.get("current_gfxclk"), (int, float)):
-            clks = [m["current_gfxclk"]]
-        pw = m.get("current_socket_power")
-        if not isinstance(pw, (int, float)) or not 0 < pw < 10000:
-            pw = m.get("average_socket_power")
-        return (sum(clks) / len(clks) if clks else None,
-                pw if isinstance(pw, (int, float)) and 0 < pw < 10000 else None)
-
-    def _run(self):
-        while not self._stop.is_set():
-            try:
-                self.samples.append(self._sample())
-            except Exception as e:  # noqa: BLE001
-                self.error = f"{type(e).__name__}: {e}"
-                return
-            self._stop.wait(self.period)
-
-    def __enter__(self):
-        import threading
-        if self._h is not None:
-            self._stop = threading.Event()
-            self._thr = threading.Thread(target=self._run, daemon=True)
-            self._thr.start()
-        return self
-
-    def __exit__(self, *exc):
-        if self._thr is not None:
-            self._stop.set()
-            self._thr.join()
-        return False
-
-    def summary(self):
-        """The amdsmi metrics table refreshes only every ~50-100 ms and lags the load, so
-        its clock readings are snapshots, not the timed region's clock: they are listed
-        as seen.  The effective clock of the primary kernel comes from the counter pass
-        (roofline.counters)."""
-        clk = sorted({round(c) for c, _ in self.samples if c})
-        pw = [w for _, w in self.samples if w]
-        out = {"source": "amdsmi gpu metrics, sampled every %.0f ms over the timed region; "
-                         "coarse snapshots" % (self.period * 1e3),
-               "bdf": self.bdf, "samples": len(self.samples), "power_cap_w": self.cap_w}
-        if self.error:
-            out["error"] = self.error
-        if clk:
-            out["gfx_clock_mhz_seen"] = clk
-        if pw:
-            out["socket_power_w_max_seen"] = round(max(pw), 1)
-        return out
+def device_state(torch):
+    """The GPU's PCI address and socket power cap (amdsmi).  amdsmi's metrics table refreshes
+    too slowly to sample the ~0.1 s timed region, so no clock is read here: the effective
+    clock of the timed kernel comes from the counter pass (roofline.counters)."""
+    out = {"source": "amdsmi", "power_cap_w": None, "bdf": None}
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handles = amdsmi.amdsmi_get_processor_handles()
+        p = torch.cuda.get_device_properties(0)
+        bus = getattr(p, "pci_bus_id", None)
+        h = None
+        if bus is not None:
+            want = f"{getattr(p, 'pci_domain_id', 0):04x}:{bus:02x}:{getattr(p, 'pci_device_id', 0):02x}"
+            h = next((x for x in handles if amdsmi.amdsmi_get_gpu_device_bdf(x).lower().startswith(want)), None)
+        if h is None and len(handles) == 1:
+            h = handles[0]
+        if h is None:
+            raise RuntimeError(f"no amdsmi device matches cuda:0 among {len(handles)}")
+        out["bdf"] = amdsmi.amdsmi_get_gpu_device_bdf(h)
+        cap = amdsmi.amdsmi_get_power_cap_info(h).get("power_cap")
+        out["power_cap_w"] = round(cap / 1e6 if cap and cap > 1e4 else cap, 1) if cap else None
+    except Exception as e:  # noqa: BLE001 - the record is informational
+        out["error"] = f"{type(e).__name__}: {e}"
+    return out
 
 
 def calibration_copy(torch, dev):
