@@ -442,3 +442,48 @@ def test_mfma_block_sum_model(ub):
             assert got[3 * i + 2] == 2.0 ** j, ("alone", j)
     finally:
         reg.close()
+
+
+@pytest.mark.parametrize("tp,T,cap,K,H,pad_a,pad_w,pad_o,order,method,ns,atomic", [
+    (1, 40, 64, 128, 64, 0, 0, 0, "ascending", "bulk", 3, False),        # one slice
+    (8, 8, 8, 512, 64, 0, 0, 0, "ring", "ring_exchange", 1, True),       # one row per shard
+    (6, 294, 300, 384, 136, 64, 32, 8, "ascending", "pipeline", 4, False),  # strided a, w, out
+    (6, 294, 300, 384, 136, 64, 32, 8, "ring", "pipeline", 4, True),
+    (4, 512, 512, 256, 256, 16, 0, 0, "ascending", "ring_exchange", 1, True),  # T == capacity
+])
+def test_rs_fp8_edges(ub, tp, T, cap, K, H, pad_a, pad_w, pad_o, order, method, ns, atomic):
+    """Integer codes, power-of-two scales (exact partials and sums): one slice, one row per
+    shard, row strides beyond k / hidden on every operand, and T equal to the capacity,
+    bit for bit against the oracle; nothing written past T rows or between output rows."""
+    rng = np.random.default_rng(79 + tp + T)
+    lda, ldw, ldo = K + pad_a, K + pad_w, H + pad_o
+    a = np.zeros((T, lda), np.uint8)
+    w = np.zeros((H, ldw), np.uint8)
+    a[:, :K] = _int_codes(rng, (T, K))
+    w[:, :K] = _int_codes(rng, (H, K))
+    a[:, K:] = 0x7F  # NaN codes past k: a read of them would poison the result
+    w[:, K:] = 0x7F
+    sa, sw = 2.0 ** -2, 2.0 ** -4
+    print(f"[rs fp8 edge] tp={tp} T={T} {order} {method} atomic={atomic}", flush=True)
+    reg = gu.Registration(ub, cap, H, tp, pad_rows=8)
+    try:
+        reg.set_T(T)
+        from oracle import manager as om
+        m = om.UserBufferModel(cap, H, tp)
+        assert m.set_active_shape((T, H)) == om.OK
+        want = np.full((cap, ldo), om.CANARY, np.uint16)
+        st, written = of.rs_chunked_fp8(m, a, K, lda, w, ldw, want, ldo,
+                                        op.OverlapCfg(method=method, num_splits=ns, reduce_order=order), sa, sw)
+        assert st == om.OK and np.all(written == 1)
+        out = gu.canary((cap + 4, ldo))
+        ub.ub_gemm_rs_chunked_fp8(reg.h, _dev8(a), K, lda, _dev8(w), ldw, sa, sw, out, ldo,
+                                  ub.make_cfg(method, ns, 3, atomic_gemm=atomic, reduce_order=order))
+        torch.cuda.synchronize()
+        got = gu.host(out)
+        assert np.array_equal(got[:T, :H], want[:T, :H])
+        assert np.all(got[:T, H:] == gu.CANARY) and np.all(got[T:] == gu.CANARY)
+        ws = gu.host(reg.ws_t)
+        assert np.array_equal(ws[: tp * T * H], m.ws[: tp * T * H])
+        assert np.all(ws[tp * T * H:] == gu.CANARY)
+    finally:
+        reg.close()

@@ -1,4 +1,5 @@
-"""HIP-graph capture of the chunked GEMM calls: none of them synchronises the host,
+"""HIP-graph capture of the chunked GEMM calls (bf16 all-gather and reduce-scatter, FP8
+reduce-scatter): none of them synchronises the host,
 allocates, or records a memset, so a whole step (several microbatches, each with its own
 active shape) can be captured once and replayed.  Every replay is checked bit for bit
 against the eager results, with eager work and host synchronisation between replays."""
@@ -35,7 +36,12 @@ def test_graph_replays_match_eager(ub):
     rs_cfgs = [ub.make_cfg("pipeline", 4, 3, atomic_gemm=True),
                ub.make_cfg("ring_exchange", 1, 3, reduce_order="ring", rank=1)]
     outs = [gu.canary((cap, N)) for _ in range(len(Ts) * len(cfgs))]
-    rs_outs = [gu.canary((cap, H)) for _ in range(len(Ts) * len(rs_cfgs))]
+    rs_outs = [gu.canary((cap, H)) for _ in range(len(Ts) * len(rs_cfgs) * 2)]
+    # E4M3 operands of the reduce-scatter GEMM, quantized once (eagerly) on the GPU
+    a8 = torch.empty((cap, K), dtype=torch.uint8, device="cuda")
+    w8 = torch.empty((H, K), dtype=torch.uint8, device="cuda")
+    ub.ub_quantize_e4m3(a_rs, K, a8, K, cap, K, 64.0)
+    ub.ub_quantize_e4m3(w_rs.t().contiguous(), K, w8, K, H, K, 4096.0)
 
     def step(stream):
         i = j = 0
@@ -46,7 +52,9 @@ def test_graph_replays_match_eager(ub):
                 i += 1
             for cfg in rs_cfgs:
                 ub.ub_gemm_rs_chunked(reg.h, a_rs, K, K, w_rs, H, rs_outs[j], H, cfg, stream)
-                j += 1
+                ub.ub_gemm_rs_chunked_fp8(reg.h, a8, K, K, w8, K, 1.0 / 64, 1.0 / 4096, rs_outs[j + 1],
+                                          H, cfg, stream)
+                j += 2
 
     try:
         reg.ub_t[: cap * H].copy_(a.reshape(-1))
