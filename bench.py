@@ -586,8 +586,10 @@ def secondary(ub, wl, torch, np, dev):
 def arrival(ub, wl, torch, np, dev):
     """Arrival stand-in on the QKV workload: the 7 non-local ring chunks are copied into the
     UserBuffer on a copy stream while the 8 chunk GEMMs (host loop, 3 streams) wait on their
-    own chunk's event.  Sources: pinned host memory (SDMA over PCIe, about one xGMI link's
-    rate), device memory by SDMA, device memory by the runtime's copy kernel.  Reports the
+    own chunk's event, or (modes *_device_loop) while the one device-side chunk loop's tiles
+    wait on per-chunk flags written after each copy.  Sources: pinned host memory (SDMA
+    over PCIe, about one xGMI link's rate), device memory by SDMA, device memory by the
+    runtime's copy kernel (host loop only).  Reports the
     GEMMs alone, the deliveries alone, both overlapped, the fraction of the delivery time
     hidden behind the GEMMs, the overlap as a fraction of the shorter of the two, the time
     the call runs past the deliveries alone, and max(GEMMs, deliveries) / overlapped (1.0
@@ -608,9 +610,13 @@ def arrival(ub, wl, torch, np, dev):
     for T in (4096, 6144, 8192):
         ub.ub_set_active_shape(h, (T, w.hidden))
         row = {"T": T}
-        for mode, use_ce, sb in (("host_pinned_sdma", True, src_host), ("device_sdma", True, src),
-                                 ("device_copy_kernel", False, src)):
-            cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, use_ce=use_ce, rank=0)
+        for mode, use_ce, sb, atomic in (("host_pinned_sdma", True, src_host, False),
+                                         ("device_sdma", True, src, False),
+                                         ("device_copy_kernel", False, src, False),
+                                         ("host_pinned_sdma_device_loop", True, src_host, True),
+                                         ("device_sdma_device_loop", True, src, True)):
+            cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, use_ce=use_ce, rank=0,
+                              atomic_gemm=atomic)
             t_g = _time_calls(lambda: ub.ub_gemm_ag_chunked(h, w_t, w.n_cols, w.n_cols, c_t, w.n_cols, cfg, stream),
                               torch, stream, 10)
             t_c = _time_calls(lambda: ub.ub_deliver_chunks(h, sb, cfg, stream), torch, stream, 10)
@@ -625,7 +631,10 @@ def arrival(ub, wl, torch, np, dev):
                 "exposed_after_delivery_ms": round(t_o - t_c, 4),
                 "overlap_efficiency": round(max(t_g, t_c) / t_o, 3)}
         res.append(row)
+    timeouts = ub.ub_arrival_timeouts(h)
     ub.ub_destroy(h)
+    if timeouts:
+        raise RuntimeError(f"arrival-gated device loop: {timeouts} tile waits timed out")
     return res
 
 

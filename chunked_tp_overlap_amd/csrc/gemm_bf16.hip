@@ -49,6 +49,8 @@
 
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
 
 #include "gemm_common.h"
 #include "ub_internal.h"
@@ -68,7 +70,43 @@ struct Params {
   int32_t unit_row0[kMaxGemmUnits];
   int32_t unit_rows[kMaxGemmUnits];
   int32_t unit_tile0[kMaxGemmUnits + 1];  // first workgroup of each unit (prefix sums)
+  // arrival gating (GemmArgs): nullptr ready = none
+  const uint32_t* ready;
+  uint32_t* timeouts;
+  uint32_t epoch;
+  int32_t n_chunks;
+  int32_t chunk_row0[kMaxGemmUnits + 1];
 };
+
+// Arrival flags (see ub_internal.h).  Host code takes the array's device address from
+// hipGetSymbolAddress (ready_flags_base), never its name.
+static __device__ __align__(256) uint32_t g_ready[kReadySlots * kReadyWords];
+
+constexpr uint64_t kReadyTimeoutTicks = 50000000ull;  // 0.5 s of the 100 MHz s_memrealtime clock
+
+// Arrival gating: wait until every chunk holding a row of [r0, r1) has been delivered
+// (its flag equals the call's epoch; the copy stream writes it after the chunk's copy),
+// then acquire at system scope so that the A loads see the delivered rows rather than
+// lines cached before they arrived.  The wait is bounded in time: past the bound the wave
+// counts a timeout and goes on, so every wave ends.
+__device__ inline void wait_ready(const Params& p, int r0, int r1) {
+  int c = 0;
+  while (c + 1 < p.n_chunks && p.chunk_row0[c + 1] <= r0) ++c;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  bool late = false;
+  for (; !late && c < p.n_chunks && p.chunk_row0[c] < r1; ++c) {
+    while (__hip_atomic_load(p.ready + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != p.epoch) {
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kReadyTimeoutTicks) {
+        late = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+  }
+  if (late && (threadIdx.x & 63) == 0)
+    __hip_atomic_fetch_add(p.timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+}
 
 template <int BM_, int BN_, int BK_, int S_, int WGM_, int WGN_>
 struct Cfg {
@@ -291,6 +329,7 @@ void gemm_bf16_pingpong(Params p) {
   const int tid = threadIdx.x;
   Tile<C> t;
   if (!t.init(p, tid)) return;
+  if (p.ready) wait_ready(p, t.m0, min(t.m0 + C::BM, t.m_end));
   const int group = t.group;
 
   f32x16 acc[C::FM][C::FN];
@@ -355,6 +394,7 @@ void gemm_bf16_pipelined(Params p) {
   const int tid = threadIdx.x;
   Tile<C> t;
   if (!t.init(p, tid)) return;
+  if (p.ready) wait_ready(p, t.m0, min(t.m0 + C::BM, t.m_end));
 
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -417,6 +457,11 @@ hipError_t launch(K kernel, const GemmArgs& g, const GemmUnits& units, hipStream
   p.unit_tile0[u.n] = (int32_t)tiles;
   if (tiles == 0) return hipSuccess;
   p.group = tile_group(tiles, C::NW == 8 ? 1 : 2);
+  p.ready = g.ready;
+  p.timeouts = g.timeouts;
+  p.epoch = g.epoch;
+  p.n_chunks = g.ready ? g.n_chunks : 0;
+  for (int c = 0; c <= p.n_chunks && c <= kMaxGemmUnits; ++c) p.chunk_row0[c] = g.chunk_row0[c];
   const int64_t grid = tiles;
   if (grid > 0x7FFFFFFF || g.batch > 65535) return hipErrorInvalidValue;
   static bool configured = false;
@@ -485,6 +530,28 @@ int choose_tile(const GemmArgs& g, const GemmUnits& u) {
 }
 
 }  // namespace
+
+uint32_t* ready_flags_base(hipError_t* err) {
+  static std::mutex mu;
+  static std::map<int, uint32_t*> by_device;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = by_device.find(dev);
+  if (it != by_device.end()) return it->second;
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_ready));
+  if (e != hipSuccess || !ptr) {
+    *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+    return nullptr;
+  }
+  by_device[dev] = static_cast<uint32_t*>(ptr);
+  return by_device[dev];
+}
 
 bool gemm_shape_supported(const GemmArgs& g) {
   // Offsets into B are 32-bit byte offsets from column n0 of the batch entry, and one A

@@ -16,7 +16,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -62,6 +64,9 @@ struct ub_ctx {
   hipStream_t copy_stream = nullptr;
   hipEvent_t ev_arrive[kMaxArrivalChunks] = {};
   hipEvent_t ev_copy_join = nullptr;
+  // device-side arrival gating: this handle's slot of arrival flags (-1: none yet)
+  int ready_slot = -1;
+  uint32_t* ready = nullptr;  // device address of the slot's words
   // scratch for plans
   ubx::Plan plan;
   std::string last_error;
@@ -163,6 +168,47 @@ ub_status_t ensure_arrival(ub_ctx* h, int n_chunks) {
     if (e != hipSuccess) return hip_fail(h, e, "hipEventCreate");
   }
   return UB_OK;
+}
+
+// ---- arrival flags of the device-side chunk loop -----------------------------------------
+// Slots of the flag array are handed to handles on their first gated call and returned by
+// ub_destroy.  Epochs come from one process-wide counter, so a flag left by an earlier call
+// (of any handle that held the slot) never equals the epoch of a later call; 0 is skipped,
+// the value the flags start from.
+std::mutex g_slot_mu;
+uint64_t g_slot_used = 0;
+std::atomic<uint32_t> g_epoch{0};
+
+uint32_t next_epoch() {
+  uint32_t e = ++g_epoch;
+  if (e == 0) e = ++g_epoch;
+  return e;
+}
+
+ub_status_t ensure_ready_slot(ub_ctx* h) {
+  if (h->ready) return UB_OK;
+  hipError_t e = hipSuccess;
+  uint32_t* base = ubx::ready_flags_base(&e);
+  if (!base) return hip_fail(h, e, "hipGetSymbolAddress(arrival flags)");
+  std::lock_guard<std::mutex> lock(g_slot_mu);
+  for (int s = 0; s < ubx::kReadySlots; ++s) {
+    if (g_slot_used >> s & 1) continue;
+    g_slot_used |= uint64_t(1) << s;
+    h->ready_slot = s;
+    h->ready = base + (size_t)s * ubx::kReadyWords;
+    return UB_OK;
+  }
+  return fail(h, UB_ERR_UNSUPPORTED,
+              "more than %d handles gate the device-side chunk loop on arrivals at once",
+              ubx::kReadySlots);
+}
+
+void release_ready_slot(ub_ctx* h) {
+  if (h->ready_slot < 0) return;
+  std::lock_guard<std::mutex> lock(g_slot_mu);
+  g_slot_used &= ~(uint64_t(1) << h->ready_slot);
+  h->ready_slot = -1;
+  h->ready = nullptr;
 }
 
 // ---- per-launch timing ----------------------------------------------------------------
@@ -537,11 +583,44 @@ ub_status_t join_deliveries(ub_ctx* h, hipStream_t caller) {
   return e == hipSuccess ? UB_OK : hip_fail(h, e, "copy stream join");
 }
 
-ub_status_t check_arrival(ub_ctx* h, const void* src, const ub_overlap_cfg_t* cfg) {
+// Device-side chunk loop with arrivals: every chunk's copy is followed, on the copy stream,
+// by a write of the call's epoch to the chunk's flag (the local chunk's flag first: it is
+// already in the UB); the tiles of the one GEMM launch wait for the flags of the chunks
+// they read.  Everything on the copy stream is issued before the GEMM, so where the two
+// streams share a hardware queue the copies run first and nothing waits on work queued
+// behind it.
+ub_status_t deliver_flagged(ub_ctx* h, const uint16_t* src, int src_on_host,
+                            const ub_overlap_cfg_t* cfg, const ChunkMap& m, uint32_t epoch) {
+  const hipMemcpyKind kind = src_on_host ? hipMemcpyHostToDevice : hipMemcpyDeviceToDeviceNoCU;
+  const int64_t H = h->hidden, T = h->T;
+  auto flag = [&](int c) {
+    hipError_t e = hipStreamWriteValue32(h->copy_stream, h->ready + c, epoch, 0);
+    return e == hipSuccess ? UB_OK : hip_fail(h, e, "hipStreamWriteValue32(arrival flag)");
+  };
+  ub_status_t st;
+  if (m.local >= 0 && (st = flag(m.local)) != UB_OK) return st;
+  for (const ub_plan_unit_t& u : h->plan.units) {
+    for (int c = m.first(u.unit); c < m.last(u.unit); ++c) {
+      if (c == m.local) continue;
+      const int64_t r0 = m.row0(T, c), rows = m.row0(T, c + 1) - r0;
+      if (rows > 0) {
+        hipError_t e = hipMemcpyAsync(h->ub + r0 * H, src + r0 * H,
+                                      static_cast<size_t>(rows * H) * 2, kind, h->copy_stream);
+        if (e != hipSuccess) return hip_fail(h, e, "arrival copy");
+      }
+      if ((st = flag(c)) != UB_OK) return st;
+    }
+  }
+  return UB_OK;
+}
+
+ub_status_t check_arrival(ub_ctx* h, const void* src, int src_on_host,
+                          const ub_overlap_cfg_t* cfg) {
   if (!src || !aligned16(src)) return fail(h, UB_ERR_INVALID_ARG, "src must be 16-byte aligned");
-  if (cfg->atomic_gemm)
+  if (cfg->atomic_gemm && !src_on_host && !cfg->use_ce)
     return fail(h, UB_ERR_UNSUPPORTED,
-                "arrival-gated units run on the host-loop schedule only (atomic_gemm=0)");
+                "the device-side chunk loop gates on SDMA deliveries only (use_ce=1 or a host "
+                "source): the runtime's copy kernel would need CUs that waiting tiles hold");
   const ChunkMap m = chunk_map(h, cfg);
   if (m.n > kMaxArrivalChunks)
     return fail(h, UB_ERR_UNSUPPORTED, "at most %d chunks can be delivered", kMaxArrivalChunks);
@@ -559,7 +638,7 @@ ub_status_t ag_call(ub_ctx* h, const void* src, int src_on_host, const void* w, 
   if (st != UB_OK) return st;
   st = check_ag_call(h, w, n_cols, ldw, c, ldc, cfg);
   if (st != UB_OK) return st;
-  if (src && (st = check_arrival(h, src, cfg)) != UB_OK) return st;
+  if (src && (st = check_arrival(h, src, src_on_host, cfg)) != UB_OK) return st;
   const int64_t H = h->hidden;
   hipStream_t caller = static_cast<hipStream_t>(stream);
 
@@ -579,11 +658,27 @@ ub_status_t ag_call(ub_ctx* h, const void* src, int src_on_host, const void* w, 
     g.k = static_cast<int32_t>(H);
     g.batch = 1;
     g.concurrency = 1;
+    if (src) {
+      const ChunkMap m = chunk_map(h, cfg);
+      if ((st = ensure_ready_slot(h)) != UB_OK) return st;
+      const uint32_t epoch = next_epoch();
+      if ((st = start_deliveries(h, m.n, caller)) != UB_OK) return st;
+      if ((st = deliver_flagged(h, static_cast<const uint16_t*>(src), src_on_host, cfg, m,
+                                epoch)) != UB_OK)
+        return st;
+      g.ready = h->ready;
+      g.epoch = epoch;
+      g.timeouts = h->ready + ubx::kReadyTimeoutWord;
+      g.n_chunks = m.n;
+      for (int c = 0; c <= m.n; ++c) g.chunk_row0[c] = static_cast<int32_t>(m.row0(h->T, c));
+    }
     const double flops = 2.0 * h->T * H * n_cols;
     const double bytes = 2.0 * (h->T * H + H * n_cols + h->T * n_cols);
-    return timed_launch(h, caller, 0, flops, bytes,
-                        [&] { return ubx::launch_gemm_bf16_units(g, units, caller); },
-                        "GEMM launch");
+    st = timed_launch(h, caller, 0, flops, bytes,
+                      [&] { return ubx::launch_gemm_bf16_units(g, units, caller); },
+                      "GEMM launch");
+    if (st != UB_OK) return st;
+    return src ? join_deliveries(h, caller) : UB_OK;
   }
 
   const int S = h->plan.n_streams;
@@ -655,7 +750,7 @@ UB_API ub_status_t ub_deliver_chunks(ub_handle_t h, const void* src, int32_t src
   ub_status_t st = need_dtype(h, UB_DTYPE_BF16, "ub_deliver_chunks");
   if (st != UB_OK) return st;
   if ((st = check_cfg_common(h, cfg)) != UB_OK) return st;
-  if ((st = check_arrival(h, src, cfg)) != UB_OK) return st;
+  if ((st = check_arrival(h, src, src_on_host != 0, cfg)) != UB_OK) return st;
   if ((st = ubx::build_plan(h->T, h->tp, *cfg, UB_OP_AG, &h->plan, &h->last_error)) != UB_OK)
     return st;
   if ((st = ensure_device(h, 1)) != UB_OK) return st;
@@ -997,6 +1092,16 @@ UB_API ub_status_t ub_get_kernel_timing(ub_handle_t h, ub_kernel_stats_t* gemm,
   return UB_OK;
 }
 
+UB_API ub_status_t ub_arrival_timeouts(ub_handle_t h, uint32_t* count) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  if (!count) return fail(h, UB_ERR_INVALID_ARG, "count must be non-NULL");
+  *count = 0;
+  if (!h->ready) return UB_OK;
+  hipError_t e = hipMemcpy(count, h->ready + ubx::kReadyTimeoutWord, sizeof(uint32_t),
+                           hipMemcpyDeviceToHost);
+  return e == hipSuccess ? UB_OK : hip_fail(h, e, "hipMemcpy(arrival timeouts)");
+}
+
 UB_API ub_status_t ub_destroy(ub_handle_t h) {
   if (!h) return UB_OK;
   if (h->device >= 0) {
@@ -1020,6 +1125,7 @@ UB_API ub_status_t ub_destroy(ub_handle_t h) {
     for (hipEvent_t ev : h->free_events) (void)hipEventDestroy(ev);
     if (cur >= 0 && cur != h->device) (void)hipSetDevice(cur);
   }
+  release_ready_slot(h);
   delete h;
   return UB_OK;
 }

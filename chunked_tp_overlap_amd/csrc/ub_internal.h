@@ -27,6 +27,17 @@ ub_status_t build_plan(int64_t T, int32_t tp, const ub_overlap_cfg_t& cfg, ub_op
 // Batched row-major bf16 GEMM, C[b] = bf16(A[b] * B[b]) with fp32 accumulation.
 // All strides in elements.  Requirements checked by the caller: k % 64 == 0,
 // n % 8 == 0, lda/ldb/ldc % 8 == 0, pointers 16-byte aligned.
+constexpr int kMaxGemmUnits = 64;
+
+// Arrival flags of the device-side chunk loop: kReadySlots slots of kReadyWords words, one
+// slot per handle that gates on arrivals (words 0..63: the chunks' flags; word 64: a count
+// of waits that timed out).  ready_flags_base() is the device address of slot 0 on the
+// current device (nullptr and *err set on failure).
+constexpr int kReadySlots = 64;
+constexpr int kReadyWords = 72;
+constexpr int kReadyTimeoutWord = 64;
+uint32_t* ready_flags_base(hipError_t* err);
+
 struct GemmArgs {
   const uint16_t* a;
   int64_t lda;
@@ -39,6 +50,15 @@ struct GemmArgs {
   int64_t c_batch_stride;
   int32_t m, n, k, batch;
   int32_t concurrency;  // launches expected to share the GPU with this one (>= 1)
+  // Arrival gating (device-side chunk loop): before loading A, a tile waits until
+  // ready[c] == epoch for every chunk c its rows touch (chunk c = rows [chunk_row0[c],
+  // chunk_row0[c + 1])), then acquires; a wait over ~0.5 s gives up and counts one in
+  // *timeouts.  ready == nullptr: no gating.
+  const uint32_t* ready = nullptr;
+  uint32_t epoch = 0;
+  uint32_t* timeouts = nullptr;
+  int32_t n_chunks = 0;
+  int32_t chunk_row0[kMaxGemmUnits + 1] = {};
 };
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream);
 constexpr int kGemmKStep = 64;  // k must be a multiple of this
@@ -46,7 +66,6 @@ constexpr int kGemmKStep = 64;  // k must be a multiple of this
 // Row units of a device-side chunk loop: one launch whose workgroups cover every unit's
 // tiles, units in the given order, no tile spanning two units.  Unit u covers rows
 // [row0[u], row0[u] + rows[u]) of A and C (g.m is ignored).
-constexpr int kMaxGemmUnits = 64;
 struct GemmUnits {
   int32_t n;
   int32_t row0[kMaxGemmUnits];
@@ -60,8 +79,8 @@ hipError_t launch_gemm_bf16_units(const GemmArgs& g, const GemmUnits& u, hipStre
 // in the units' order, each unit's run of tiles as one unit (units left without a tile are
 // dropped).  A tile then spans a unit boundary only where a unit is not a multiple of bm,
 // and no row is computed twice.  Such a tile also reads rows of the unit before its own in
-// row order, which a device-side wait for arriving chunks would have to cover; the
-// arrival stand-in therefore runs on the host-loop schedule only.  Units that do not
+// row order; the device-side wait for arriving chunks therefore covers every chunk that
+// the tile's rows touch, not the unit's alone.  Units that do not
 // tile a contiguous range are returned unchanged.
 GemmUnits tile_aligned_units(const GemmUnits& u, int bm);
 // Row tiles of bm rows that a launch over `u` runs (after tile_aligned_units).

@@ -42,7 +42,8 @@ REDUCE_ORDERS = {"ascending": UB_REDUCE_ASCENDING, "ring": UB_REDUCE_RING}
 EXPORTS = (
     "ub_overlap_cfg_default", "ub_required_bytes", "ub_init", "ub_set_active_shape",
     "ub_get_active_shape", "ub_get_capacity_shape", "ub_get_plan", "ub_copy_in",
-    "ub_gemm_ag_chunked", "ub_gemm_ag_arrival", "ub_deliver_chunks", "ub_quantize_in",
+    "ub_gemm_ag_chunked", "ub_gemm_ag_arrival", "ub_arrival_timeouts", "ub_deliver_chunks",
+    "ub_quantize_in",
     "ub_gemm_ag_chunked_fp8", "ub_gemm_rs_chunked", "ub_gemm_rs_chunked_fp8",
     "ub_quantize_e4m3", "ub_reduce_partials",
     "ub_set_kernel_timing", "ub_get_kernel_timing", "ub_destroy", "ub_status_string",
@@ -92,6 +93,7 @@ _sig = {
     "ub_gemm_ag_chunked": (_I32, [_H, _P, _I64, _I64, _P, _I64, _CFGP, _P]),
     "ub_gemm_ag_arrival": (_I32, [_H, _P, _I32, _P, _I64, _I64, _P, _I64, _CFGP, _P]),
     "ub_deliver_chunks": (_I32, [_H, _P, _I32, _CFGP, _P]),
+    "ub_arrival_timeouts": (_I32, [_H, ctypes.POINTER(ctypes.c_uint32)]),
     "ub_quantize_in": (_I32, [_H, _P, _I64, _I64, ctypes.c_float, _P]),
     "ub_gemm_ag_chunked_fp8": (_I32, [_H, _P, _I64, _I64, ctypes.c_float, ctypes.c_float, _P,
                                       _I64, _CFGP, _P]),
@@ -237,6 +239,13 @@ def ub_gemm_ag_arrival(h, src, w, n_cols, ldw, c, ldc, cfg, stream=None):
 def ub_deliver_chunks(h, src, cfg, stream=None):
     _check(_lib.ub_deliver_chunks(h, _ptr(src), _on_host(src), ctypes.byref(cfg),
                                   _stream(stream)), h)
+
+
+def ub_arrival_timeouts(h):
+    """Tile waits of the arrival-gated device-side chunk loop that hit the time bound."""
+    n = ctypes.c_uint32(0)
+    _check(_lib.ub_arrival_timeouts(h, ctypes.byref(n)), h)
+    return n.value
 
 
 def ub_quantize_in(h, src, rows, row_offset, scale, stream=None):

@@ -305,8 +305,22 @@ UB_API ub_status_t ub_gemm_ag_chunked_fp8(ub_handle_t h, const void* w, int64_t 
  *     runtime's copy kernel, which shares the compute units with the GEMMs).  Measured on
  *     MI355X with ROCm 7.2: all three kinds run alongside the GEMMs of other streams; an
  *     SDMA copy costs about 80 us whatever its size.
- *   atomic_gemm = 1 -> UB_ERR_UNSUPPORTED (units are gated by events, which needs the
- *     host-loop schedule); more than 64 chunks -> UB_ERR_UNSUPPORTED.
+ *   atomic_gemm = 1: the device-side chunk loop ([TE#1344] "atomic_gemm") gated by a
+ *     ready flag per chunk.  After each chunk's copy, the copy stream writes the call's
+ *     epoch to the chunk's flag (hipStreamWriteValue32; the local chunk's flag first).
+ *     The one GEMM launch's tiles wait for the flags of the chunks whose rows they read,
+ *     acquire at system scope, then load.  The copy stream's work is all issued before
+ *     the GEMM, so streams that share a hardware queue serialise rather than wait on each
+ *     other.
+ *     - Deliveries must be SDMA copies: use_ce = 1 or a host source.  Otherwise
+ *       UB_ERR_UNSUPPORTED, because the runtime's copy kernel would need CUs that waiting
+ *       tiles hold.
+ *     - A tile's wait is bounded (~0.5 s); past it the tile goes on, and the wait is
+ *       counted (ub_arrival_timeouts).
+ *     - The flags live in a fixed device array of 64 slots, one per handle, taken on its
+ *       first such call and returned by ub_destroy; a 65th handle gets
+ *       UB_ERR_UNSUPPORTED.
+ *   More than 64 chunks -> UB_ERR_UNSUPPORTED.
  *   Hardware queues: the call keeps up to four streams busy (the caller's, two workers,
  *     the copy stream).  HIP maps a process's streams onto GPU_MAX_HW_QUEUES hardware
  *     queues (4 by default), and streams that share a queue run in issue order: with
@@ -319,6 +333,13 @@ UB_API ub_status_t ub_gemm_ag_arrival(ub_handle_t h, const void* src, int32_t sr
                                       const void* w, int64_t n_cols, int64_t ldw, void* c,
                                       int64_t ldc, const ub_overlap_cfg_t* cfg,
                                       ub_stream_t stream);
+
+/* Number of tile waits in the device-side chunk loop of ub_gemm_ag_arrival that hit the
+ * time bound on this handle's flag slot since the slot was first used in this process (0
+ * if the handle never gated on arrivals).  A nonzero count means a chunk's flag never
+ * came, and the results of that call are not to be trusted.  Synchronous (copies one word
+ * from the device). */
+UB_API ub_status_t ub_arrival_timeouts(ub_handle_t h, uint32_t* count);
 
 /* The deliveries of ub_gemm_ag_arrival alone (same copies, order, stream and kind, no
  * GEMM), ordered on `stream`: for measuring how long the arrivals take by themselves. */

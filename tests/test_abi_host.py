@@ -227,8 +227,17 @@ def test_arrival_argument_errors_before_any_hip_call():
         assert st("ub_gemm_ag_arrival", h, None, 0, FAKE, 384, 384, FAKE, 384, cp, None) == "UB_ERR_INVALID_ARG"
         assert st("ub_gemm_ag_arrival", h, FAKE + 8, 0, FAKE, 384, 384, FAKE, 384, cp, None) == "UB_ERR_INVALID_ARG"
         assert st("ub_gemm_ag_arrival", h, FAKE, 0, FAKE, 380, 384, FAKE, 384, cp, None) == "UB_ERR_INVALID_ARG"
-        atomic = ub.make_cfg("ring_exchange", 2, atomic_gemm=True)
-        assert st("ub_gemm_ag_arrival", h, FAKE, 0, FAKE, 384, 384, FAKE, 384, ctypes.byref(atomic), None) == "UB_ERR_UNSUPPORTED"
+        # the device-side chunk loop gates on SDMA deliveries only: a device source through
+        # the copy kernel (use_ce=0) is refused before any HIP call
+        atomic_ck = ub.make_cfg("ring_exchange", 2, atomic_gemm=True, use_ce=False)
+        assert st("ub_gemm_ag_arrival", h, FAKE, 0, FAKE, 384, 384, FAKE, 384, ctypes.byref(atomic_ck), None) == "UB_ERR_UNSUPPORTED"
+        assert "SDMA" in ub.ub_last_error(h)
+        many_atomic = ub.make_cfg("pipeline", 65, atomic_gemm=True)
+        assert st("ub_gemm_ag_arrival", h, FAKE, 0, FAKE, 384, 384, FAKE, 384, ctypes.byref(many_atomic), None) == "UB_ERR_UNSUPPORTED"
+        n = ctypes.c_uint32(7)
+        assert st("ub_arrival_timeouts", h, ctypes.byref(n)) == "UB_OK" and n.value == 0  # never gated
+        assert st("ub_arrival_timeouts", h, None) == "UB_ERR_INVALID_ARG"
+        assert st("ub_arrival_timeouts", None, ctypes.byref(n)) == "UB_ERR_NOT_INITIALIZED"
         many = ub.make_cfg("pipeline", 65)
         assert st("ub_gemm_ag_arrival", h, FAKE, 0, FAKE, 384, 384, FAKE, 384, ctypes.byref(many), None) == "UB_ERR_UNSUPPORTED"
         assert st("ub_deliver_chunks", h, None, 0, cp, None) == "UB_ERR_INVALID_ARG"

@@ -1,6 +1,7 @@
 """GPU tests of the arrival stand-in (ub_gemm_ag_arrival, ub_deliver_chunks): the non-local
 chunks are copied into the UserBuffer on a copy stream while the GEMM units that need them
-wait on per-chunk events.  Results must be bit-identical to the all-gather GEMM over a
+wait on per-chunk events (host loop) or, in the device-side chunk loop, the tiles wait on
+per-chunk flags that the copy stream writes after each copy.  Results must be bit-identical to the all-gather GEMM over a
 complete buffer, the local chunk's rows of the source are never read, and nothing beyond
 the active prefix is touched."""
 
@@ -76,8 +77,70 @@ def test_arrival_bit_identical_to_complete_buffer(ub):
                 _case(ub, reg, a, w_t, N, dict(kw, use_ce=use_ce), ref, T, tp)
             print(f"[arrival] {kw} host source", flush=True)
             _case(ub, reg, a, w_t, N, kw, ref, T, tp, host_src=True)
+            # the device-side chunk loop gated by per-chunk flags: SDMA and host sources
+            print(f"[arrival] {kw} atomic_gemm, SDMA", flush=True)
+            _case(ub, reg, a, w_t, N, dict(kw, atomic_gemm=True, use_ce=True), ref, T, tp)
+            print(f"[arrival] {kw} atomic_gemm, host source", flush=True)
+            _case(ub, reg, a, w_t, N, dict(kw, atomic_gemm=True), ref, T, tp, host_src=True)
+        assert ub.ub_arrival_timeouts(reg.h) == 0
+        with pytest.raises(ub.UBError) as e:  # copy-kernel deliveries cannot gate the loop
+            ub.ub_gemm_ag_arrival(reg.h, gu.dev(a), w_t, N, N, gu.canary((T, N)), N,
+                                  ub.make_cfg("pipeline", 4, atomic_gemm=True, use_ce=False))
+        assert e.value.name == "UB_ERR_UNSUPPORTED"
     finally:
         reg.close()
+
+
+def test_arrival_device_loop_flag_slots(ub):
+    """Flag slots: two handles gate at once, and 70 handles in a row (more than the 64
+    slots) each take and return one."""
+    rng = np.random.default_rng(54)
+    cap, H, N, T, tp = 256, 128, 64, 256, 4
+    a = wl.normal_bits(rng, (T, H))
+    w_t = gu.dev(wl.normal_bits(rng, (H, N), 0.02))
+    src = gu.dev(a)
+    ref_reg = gu.Registration(ub, cap, H, tp, workspace=False)
+    try:
+        ref_reg.set_T(T)
+        ref_reg.fill(a)
+        ref = gu.canary((T, N))
+        ub.ub_gemm_ag_chunked(ref_reg.h, w_t, N, N, ref, N, ub.make_cfg("bulk", 1))
+        torch.cuda.synchronize()
+        ref = gu.host(ref)
+    finally:
+        ref_reg.close()
+    regs = [gu.Registration(ub, cap, H, tp, workspace=False) for _ in range(2)]
+    try:
+        outs = []
+        for i, r in enumerate(regs):  # both calls in flight on the null stream's order
+            r.set_T(T)
+            r.ub_t.fill_(gu.CANARY)
+            c = gu.canary((T, N))
+            ub.ub_gemm_ag_arrival(r.h, src, w_t, N, N, c, N,
+                                  ub.make_cfg("pipeline", 4, atomic_gemm=True))
+            outs.append(c)
+        torch.cuda.synchronize()
+        for c in outs:
+            assert np.array_equal(gu.host(c), ref)
+        assert all(ub.ub_arrival_timeouts(r.h) == 0 for r in regs)
+    finally:
+        for r in regs:
+            r.close()
+    for i in range(70):
+        r = gu.Registration(ub, cap, H, tp, workspace=False)
+        try:
+            r.set_T(T)
+            c = gu.canary((T, N))
+            ub.ub_gemm_ag_arrival(r.h, src, w_t, N, N, c, N, ub.make_cfg("ring_exchange", rank=i % tp,
+                                                                           atomic_gemm=True))
+            torch.cuda.synchronize()
+            lo, hi = (i % tp) * T // tp, (i % tp + 1) * T // tp
+            got = gu.host(c)
+            # the local chunk was never written (canary), so only the delivered rows compare
+            assert np.array_equal(np.delete(got, np.s_[lo:hi], axis=0), np.delete(ref, np.s_[lo:hi], axis=0)), i
+            assert ub.ub_arrival_timeouts(r.h) == 0
+        finally:
+            r.close()
 
 
 def test_deliver_chunks_alone(ub):
@@ -146,10 +209,12 @@ def test_arrival_qkv_full_size(ub):
         ub.ub_gemm_ag_chunked(reg.h, w_t, N, N, c, N, ub.make_cfg("ring_exchange", atomic_gemm=True))
         torch.cuda.synchronize()
         ref = gu.host(c)
-        for use_ce, host_src in ((True, False), (False, False), (True, True)):
-            print(f"[arrival qkv] use_ce={use_ce} host_src={host_src}", flush=True)
-            _case(ub, reg, a, w_t, N, dict(method="ring_exchange", rank=3, use_ce=use_ce), ref, T, tp,
-                  host_src=host_src)
+        for use_ce, host_src, atomic in ((True, False, False), (False, False, False), (True, True, False),
+                                         (True, False, True), (True, True, True)):
+            print(f"[arrival qkv] use_ce={use_ce} host_src={host_src} atomic={atomic}", flush=True)
+            _case(ub, reg, a, w_t, N, dict(method="ring_exchange", rank=3, use_ce=use_ce,
+                                           atomic_gemm=atomic), ref, T, tp, host_src=host_src)
+        assert ub.ub_arrival_timeouts(reg.h) == 0
         rows = np.array(sorted({0, 1, T // 2, T - 1} | {r * T // tp for r in range(tp)}))
         gu.check_close(ref[rows], og.ag_rows(a[rows], wt, N), a[rows], wt, "arrival qkv rows")
     finally:
