@@ -416,8 +416,12 @@ UB_API ub_status_t ub_set_kernel_timing(ub_handle_t h, int32_t enable);
 UB_API ub_status_t ub_get_kernel_timing(ub_handle_t h, ub_kernel_stats_t* gemm,
                                         ub_kernel_stats_t* reduce);
 
-/* Destroy a handle: waits for the handle's streams, then releases its streams and
- * events.  Caller buffers are untouched.  NULL is accepted. */
+/* Destroy a handle: waits for the handle's own streams, then releases its streams,
+ * events and arrival-flag slot.  The caller's streams are not waited for: work of this
+ * handle still queued there must have finished (the caller synchronises first), or a
+ * device-side loop of a gated arrival could wait on a slot that another handle has taken
+ * (it would end at its time bound, with wrong results).  Caller buffers are untouched.
+ * NULL is accepted. */
 UB_API ub_status_t ub_destroy(ub_handle_t h);
 
 /* Static name of a status code ("UB_OK", "UB_ERR_CAPACITY", ...). */
