@@ -126,21 +126,17 @@ class Qkv:
         finally:
             self.stream = old
 
-    def per_microbatch(self, cfg, reps=5):
-        torch, ub, w = self.torch, self.ub, self.w
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    def per_microbatch(self, cfg, reps=20):
+        """(T, median ms, min ms) per microbatch: 5 warm-up calls, then `reps` calls timed
+        one by one with HIP events on the launch stream."""
+        ub, w = self.ub, self.w
         out = []
         for T in self.Ts:
             ub.ub_set_active_shape(self.h, (T, w.hidden))
-            ub.ub_gemm_ag_chunked(self.h, self.w_t, w.n_cols, w.n_cols, self.c_t, w.n_cols, cfg,
-                                  self.stream)
-            e0.record(self.stream)
-            for _ in range(reps):
-                ub.ub_gemm_ag_chunked(self.h, self.w_t, w.n_cols, w.n_cols, self.c_t, w.n_cols,
-                                      cfg, self.stream)
-            e1.record(self.stream)
-            torch.cuda.synchronize()
-            out.append((T, e0.elapsed_time(e1) / reps))
+            med, best, _ = _call_stats(
+                lambda: ub.ub_gemm_ag_chunked(self.h, self.w_t, w.n_cols, w.n_cols, self.c_t, w.n_cols,
+                                              cfg, self.stream), self.torch, self.stream, reps)
+            out.append((T, med, best))
         return out
 
 
@@ -211,8 +207,10 @@ def main():
         return
 
     per_mb = q.per_microbatch(primary)
-    big = [(T, ms) for T, ms in per_mb if T >= 4096]
-    agg_ge4096 = sum(2.0 * T * q.w.hidden * q.w.n_cols for T, _ in big) / (sum(ms for _, ms in big) / 1e3) / 1e12
+    fl = lambda T: 2.0 * T * q.w.hidden * q.w.n_cols
+    big = [(T, med) for T, med, _ in per_mb if T >= 4096]
+    agg_ge4096 = sum(fl(T) for T, _ in big) / (sum(ms for _, ms in big) / 1e3) / 1e12
+    agg_all = sum(fl(T) for T, _, _ in per_mb) / (sum(ms for _, ms, _ in per_mb) / 1e3) / 1e12
 
     host_cfg = q.cfg(atomic=False)
     graph = {}
@@ -277,6 +275,11 @@ def main():
             "seed": w.seed,
         },
         "tflops_T_ge_4096_per_microbatch_aggregate": round(agg_ge4096, 3),
+        "tflops_all_per_microbatch_aggregate": round(agg_all, 3),
+        "per_microbatch": {"columns": ["T", "tflops_median", "tflops_best"],
+                           "note": "each microbatch: 5 warm-up calls, 20 calls timed one by one (HIP events)",
+                           "rows": [[T, round(fl(T) / med / 1e9, 1), round(fl(T) / best / 1e9, 1)]
+                                    for T, med, best in per_mb]},
         "graph_replay_tflops": graph,
         "modes": {
             "atomic_gemm": {"tflops": round(tflops, 2), "ms_per_step": round(sec * 1e3, 4)},
@@ -424,6 +427,28 @@ def profile_fp8(ub, wl, torch, np, dev, steps, warmup):
             "src_file": os.path.relpath(src, ROOT), "src_hash": src_hash(src)}
 
 
+def _call_stats(fn, torch, stream, reps=20, warmup=5):
+    """Per-call times (ms) of fn() with HIP events around each call on `stream`: `warmup`
+    untimed calls, then `reps` timed ones.  Returns (median, minimum, mean)."""
+    for _ in range(warmup):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    return t[len(t) // 2], t[0], sum(t) / len(t)
+
+
+def _stats_row(flops, stats, peak):
+    med, best, mean = stats
+    return {"tflops": round(flops / med / 1e9, 2), "tflops_best": round(flops / best / 1e9, 2),
+            "ms_median": round(med, 4), "ms_min": round(best, 4), "ms_mean": round(mean, 4),
+            "pct_peak": round(100 * flops / med / 1e9 / peak, 2)}
+
+
 def _time_calls(fn, torch, stream, reps):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     fn()
@@ -455,8 +480,8 @@ def secondary(ub, wl, torch, np, dev):
         tot_f = tot_ms = big_f = big_ms = 0.0
         for T in Ts:
             ub.ub_set_active_shape(h, (T, w.hidden))
-            ms = _time_calls(lambda: ub.ub_gemm_ag_chunked(h, w_t, w.n_cols, w.n_cols, c_t, w.n_cols, cfg, stream),
-                             torch, stream, 5)
+            ms, _, _ = _call_stats(lambda: ub.ub_gemm_ag_chunked(h, w_t, w.n_cols, w.n_cols, c_t, w.n_cols, cfg, stream),
+                                   torch, stream)
             f = 2.0 * T * w.hidden * w.n_cols
             tot_f += f
             tot_ms += ms
@@ -468,6 +493,7 @@ def secondary(ub, wl, torch, np, dev):
             "tflops_T_ge_4096": round(big_f / big_ms / 1e9, 2) if big_ms else None,
             "pct_peak_T_ge_4096": round(100 * big_f / big_ms / 1e9 / MFMA_PEAK_BF16_TFLOPS, 2) if big_ms else None}
     res["microbatches"] = len(Ts)
+    res["note"] = "per microbatch the median of 20 calls timed one by one; aggregates are sum FLOPs / sum medians"
     out["fc1_ag"] = res
     ub.ub_destroy(h)
     del ub_t, w_t, c_t
@@ -494,15 +520,13 @@ def secondary(ub, wl, torch, np, dev):
         row = {"T": T}
         for atomic in (False, True):
             cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, False, atomic)
-            ms = _time_calls(lambda: ub.ub_gemm_rs_chunked(h, a_t, w.k, w.k, w_t, w.hidden, o_t, w.hidden, cfg, stream),
-                             torch, stream, 5)
-            key = "atomic_gemm" if atomic else "pipeline_3_streams"
-            row[key] = {"tflops": round(f / ms / 1e9, 2), "ms": round(ms, 4),
-                        "pct_peak": round(100 * f / ms / 1e9 / MFMA_PEAK_BF16_TFLOPS, 2)}
+            st = _call_stats(lambda: ub.ub_gemm_rs_chunked(h, a_t, w.k, w.k, w_t, w.hidden, o_t, w.hidden, cfg, stream),
+                             torch, stream)
+            row["atomic_gemm" if atomic else "pipeline_3_streams"] = _stats_row(f, st, MFMA_PEAK_BF16_TFLOPS)
         cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, False, True, reduce_order="ring")
-        ms = _time_calls(lambda: ub.ub_gemm_rs_chunked(h, a_t, w.k, w.k, w_t, w.hidden, o_t, w.hidden, cfg, stream),
-                         torch, stream, 5)
-        row["atomic_gemm_ring_order"] = {"tflops": round(f / ms / 1e9, 2), "ms": round(ms, 4)}
+        st = _call_stats(lambda: ub.ub_gemm_rs_chunked(h, a_t, w.k, w.k, w_t, w.hidden, o_t, w.hidden, cfg, stream),
+                         torch, stream)
+        row["atomic_gemm_ring_order"] = _stats_row(f, st, MFMA_PEAK_BF16_TFLOPS)
         rbytes = (w.tp + 1) * T * w.hidden * 2.0
         for order in ("ascending", "ring"):
             warm = _time_calls(lambda: ub.ub_reduce_partials(h, o_t, w.hidden, order, stream), torch, stream, 10)
@@ -540,14 +564,12 @@ def secondary(ub, wl, torch, np, dev):
         row = {"T": T}
         for atomic in (False, True):
             cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, False, atomic)
-            ms = _time_calls(lambda: ub.ub_gemm_rs_chunked_fp8(h, a8, w.k, w.k, w8, w.k, 1.0 / sa_q, 1.0 / sw_q,
-                                                               o_t, w.hidden, cfg, stream), torch, stream, 5)
-            key = "atomic_gemm" if atomic else "pipeline_3_streams"
-            row[key] = {"tflops": round(f / ms / 1e9, 2), "ms": round(ms, 4),
-                        "pct_fp8_peak": round(100 * f / ms / 1e9 / MFMA_PEAK_FP8_TFLOPS, 2)}
+            st = _call_stats(lambda: ub.ub_gemm_rs_chunked_fp8(h, a8, w.k, w.k, w8, w.k, 1.0 / sa_q, 1.0 / sw_q,
+                                                               o_t, w.hidden, cfg, stream), torch, stream)
+            row["atomic_gemm" if atomic else "pipeline_3_streams"] = _stats_row(f, st, MFMA_PEAK_FP8_TFLOPS)
         rows8.append(row)
     out["fc2_rs_fp8"] = {"rows": rows8, "note": "E4M3 A [T, 14336] and W [4096, 14336], per-tensor "
-                         "scales, bf16 partials and sum; FLOPs 2 T K H per call"}
+                         "scales, bf16 partials and sum; FLOPs 2 T K H per call; pct_peak of the fp8 peak"}
     ub.ub_destroy(h)
     del ub_t, ws_t, a_t, w_t, o_t, flush, a8, w8
 
@@ -567,17 +589,18 @@ def secondary(ub, wl, torch, np, dev):
         pts = []
         for T in wl.gqa_tokens():
             ub.ub_set_active_shape(h, (T, w.hidden))
-            ms = _time_calls(lambda: ub.ub_gemm_ag_chunked(h, w_t, w.n_cols, w.n_cols, c_t, w.n_cols, cfg, stream),
-                             torch, stream, 3)
+            ms, best, _ = _call_stats(lambda: ub.ub_gemm_ag_chunked(h, w_t, w.n_cols, w.n_cols, c_t, w.n_cols, cfg, stream),
+                                      torch, stream)
             f = 2.0 * T * w.hidden * w.n_cols
             if T != 32768:
                 tot_f += f
                 tot_ms += ms
-            pts.append((T, round(f / ms / 1e9, 1)))
+            pts.append((T, round(f / ms / 1e9, 1), round(f / best / 1e9, 1)))
         res["atomic_gemm" if atomic else "host_loop"] = {
             "tflops_sweep": round(tot_f / tot_ms / 1e9, 2),
             "pct_peak_sweep": round(100 * tot_f / tot_ms / 1e9 / MFMA_PEAK_BF16_TFLOPS, 2),
-            "points_T_tflops": pts[::4] + [pts[-1]]}
+            "points_T_tflops_median_best": pts}
+    res["note"] = "per point the median (and best) of 20 calls timed one by one; the sweep is sum FLOPs / sum medians"
     out["gqa_bulk_ag"] = res
     ub.ub_destroy(h)
     return out
