@@ -43,11 +43,12 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--profile-pass", nargs="?", const="qkv", default=None,
-                   choices=["qkv", "reduce", "fp8"],
+                   choices=["qkv", "reduce", "fp8", "arrival"],
                    help="for rocprofv3: run only one kernel's timed region and its per-launch "
                         "timing pass (qkv: the primary bf16 GEMM; reduce: the fc2 reduction at "
                         "T = 16384; fp8: the qkv step on an fp8 buffer), then a 1 GiB copy that "
-                        "calibrates the byte counters; print one JSON line")
+                        "calibrates the byte counters; arrival: separated arrival-stand-in calls "
+                        "of every mode, for a timeline; print one JSON line")
     return p.parse_args()
 
 
@@ -169,8 +170,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    if args.profile_pass in ("reduce", "fp8"):
-        fn = profile_reduce if args.profile_pass == "reduce" else profile_fp8
+    if args.profile_pass in ("reduce", "fp8", "arrival"):
+        fn = {"reduce": profile_reduce, "fp8": profile_fp8, "arrival": profile_arrival}[args.profile_pass]
         res = fn(ub, wl, torch, np, dev, args.steps, args.warmup)
         calibration_copy(torch, dev)
         print(json.dumps(res), flush=True)
@@ -388,6 +389,48 @@ def profile_reduce(ub, wl, torch, np, dev, steps, warmup):
     out["src_hash"] = src_hash(REDUCE_SRC)
     ub.ub_destroy(h)
     return out
+
+
+ARRIVAL_MODES = (("host_loop_pinned_host", True, True, False),
+                 ("host_loop_device_sdma", True, False, False),
+                 ("host_loop_device_copy_kernel", False, False, False),
+                 ("device_loop_pinned_host", True, True, True),
+                 ("device_loop_device_sdma", True, False, True))
+
+
+def profile_arrival(ub, wl, torch, np, dev, steps, warmup):
+    """Arrival stand-in on qkv at T = 8192 (ring, rank 0, 3 streams), for a rocprofv3
+    kernel and memory-copy trace: per mode (host loop or device-side loop; pinned-host,
+    device SDMA or copy-kernel source) `steps` calls, each followed by a device
+    synchronisation and a 20 ms pause, so that every call stands alone on the timeline.
+    Prints the modes in trace order."""
+    w = wl.qkv()
+    ra, rw, _ = w.seeds()
+    T = w.capacity
+    ub_bytes, _ = ub.ub_required_bytes(w.capacity, w.hidden, w.tp)
+    ub_t = torch.from_numpy(wl.activations(w, w.capacity, ra).view(np.int16).ravel()).to(dev)
+    src = ub_t.clone()
+    src_host = ub_t.cpu().pin_memory()
+    w_t = torch.from_numpy(wl.weights(w, rw).view(np.int16)).to(dev)
+    c_t = torch.empty((w.capacity, w.n_cols), dtype=torch.int16, device=dev)
+    h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes)
+    ub.ub_set_active_shape(h, (T, w.hidden))
+    torch.cuda.synchronize()
+    time.sleep(0.05)  # the uploads above stand apart from the first call on the timeline
+    modes = []
+    for name, use_ce, host, atomic in ARRIVAL_MODES:
+        cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, use_ce=use_ce, rank=0,
+                          atomic_gemm=atomic)
+        sb = src_host if host else src
+        for _ in range(steps):
+            ub.ub_gemm_ag_arrival(h, sb, w_t, w.n_cols, w.n_cols, c_t, w.n_cols, cfg)
+            torch.cuda.synchronize()
+            time.sleep(0.02)
+        modes.append({"mode": name, "calls": steps})
+    timeouts = ub.ub_arrival_timeouts(h)
+    ub.ub_destroy(h)
+    return {"profile_pass": "arrival", "T": T, "chunks": w.tp, "modes": modes,
+            "timeouts": timeouts, "gpu_max_hw_queues": os.environ.get("GPU_MAX_HW_QUEUES")}
 
 
 def profile_fp8(ub, wl, torch, np, dev, steps, warmup):

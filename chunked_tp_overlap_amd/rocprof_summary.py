@@ -15,6 +15,10 @@ kernel's dispatches.
 ascending and the ring order separately).  The timed launches are the last
 `timed_launches` dispatches of the kernel in the trace.
 
+--timeline DIR --bench-json FILE --out FILE instead summarises `bench.py --profile-pass
+arrival` under `rocprofv3 --kernel-trace --memory-copy-trace`: per delivery mode, the
+median call span, the time copies and GEMMs are active, and their overlap.
+
 --util DIR adds a fourth run, --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES
 SQ_BUSY_CU_CYCLES, read per dispatch with that run's own timestamps:
   - GRBM_GUI_ACTIVE sums the busy cycles of the 8 XCDs' GRBMs, so /8 is the dispatch's
@@ -30,6 +34,7 @@ SQ_BUSY_CU_CYCLES, read per dispatch with that run's own timestamps:
 
 import argparse
 import csv
+import sys
 import glob
 import json
 import os
@@ -83,7 +88,98 @@ def counter_timed_dispatches(dirname, counters, kernel, n_timed):
 UTIL_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES")
 
 
+def _union(iv):
+    """Total length of the union of [start, end) intervals."""
+    tot, cur_s, cur_e = 0, None, None
+    for a, b in sorted(iv):
+        if cur_e is None or a > cur_e:
+            if cur_e is not None:
+                tot += cur_e - cur_s
+            cur_s, cur_e = a, b
+        else:
+            cur_e = max(cur_e, b)
+    return tot + (cur_e - cur_s if cur_e is not None else 0)
+
+
+def _intersect(xs, ys):
+    """Length of (union of xs) intersected with (union of ys)."""
+    return _union(xs) + _union(ys) - _union(list(xs) + list(ys))
+
+
+def timeline(kt_dir, bench_json, out, title, command):
+    """Per-call timelines of `bench.py --profile-pass arrival` from a kernel trace plus a
+    memory-copy trace: the calls are the groups of events separated by the pass's 20 ms
+    pauses that hold a GEMM; they are assigned to the pass's modes in order."""
+    with open(bench_json) as f:
+        top = json.loads([ln for ln in f if ln.startswith("{")][-1])
+    ev = []
+    for r in _rows(_one(kt_dir, "_kernel_trace.csv")):
+        name = r["Kernel_Name"]
+        kind = "gemm" if "gemm_bf16" in name else ("copy" if "copyBuffer" in name else "other")
+        ev.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), kind, name[:48], r.get("Stream_Id", "")))
+    for r in _rows(_one(kt_dir, "_memory_copy_trace.csv")):
+        ev.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), "copy", r["Direction"], r.get("Stream_Id", "")))
+    ev.sort()
+    groups, cur, last_end = [], [], 0
+    for e in ev:  # a gap of more than 5 ms after every event so far starts a new group
+        if cur and e[0] - last_end > 5_000_000:
+            groups.append(cur)
+            cur = []
+        if not cur:
+            last_end = e[1]
+        cur.append(e)
+        last_end = max(last_end, e[1])
+    if cur:
+        groups.append(cur)
+    calls = [g for g in groups if any(k == "gemm" for _, _, k, _, _ in g)]
+    want = sum(m["calls"] for m in top["modes"])
+    if len(calls) < want:
+        raise SystemExit(f"found {len(calls)} calls with a GEMM, expected {want}")
+    calls = calls[-want:]  # the pass's calls are the last ones
+    lines = [f"# rocprofv3 summary: {title}", ""]
+    if command:
+        lines += ["Commands (from the repository root):", "", "```", command.strip(), "```", ""]
+    lines += [f"T = {top['T']}, {top['chunks']} ring chunks, hardware queues {top.get('gpu_max_hw_queues')}, "
+              f"wait timeouts {top.get('timeouts')}.  Per mode, medians over its calls (us):", "",
+              "| mode | calls | call span | copies active | GEMMs active | both active | copies alone + GEMMs alone |",
+              "|---|---|---|---|---|---|---|"]
+    i = 0
+    details = []
+    for m in top["modes"]:
+        rows = []
+        for g in calls[i:i + m["calls"]]:
+            t0 = g[0][0]
+            cp = [(a, b) for a, b, k, _, _ in g if k == "copy"]
+            gm = [(a, b) for a, b, k, _, _ in g if k == "gemm"]
+            rows.append(((max(b for _, b, _, _, _ in g) - t0) / 1e3, _union(cp) / 1e3, _union(gm) / 1e3,
+                         _intersect(cp, gm) / 1e3))
+        i += m["calls"]
+        med = [statistics.median(c[j] for c in rows) for j in range(4)]
+        lines.append(f"| {m['mode']} | {m['calls']} | {med[0]:.1f} | {med[1]:.1f} | {med[2]:.1f} | {med[3]:.1f} | "
+                     f"{med[1] + med[2]:.1f} |")
+        g = calls[i - 1]
+        t0 = g[0][0]
+        details += ["", f"### {m['mode']}: its last call", "", "| kind | stream | start us | end us | name |",
+                    "|---|---|---|---|---|"]
+        details += [f"| {k} | {st} | {(a - t0) / 1e3:.1f} | {(b - t0) / 1e3:.1f} | `{n}` |" for a, b, k, n, st in g]
+    lines += ["", "`both active` is the time during which a copy and a GEMM run at once (the overlap)."]
+    lines += details
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines[:14 + len(top["modes"])]))
+
+
 def main():
+    if "--timeline" in sys.argv:
+        p = argparse.ArgumentParser()
+        p.add_argument("--timeline", required=True, help="rocprofv3 --kernel-trace --memory-copy-trace directory")
+        p.add_argument("--bench-json", required=True)
+        p.add_argument("--title", default="arrival stand-in timelines")
+        p.add_argument("--command", default="")
+        p.add_argument("--out", required=True)
+        a = p.parse_args()
+        timeline(a.timeline, a.bench_json, a.out, a.title, a.command)
+        return
     p = argparse.ArgumentParser()
     p.add_argument("--kt", required=True, help="rocprofv3 --kernel-trace --stats output directory")
     p.add_argument("--fetch", required=True, help="rocprofv3 --pmc FETCH_SIZE output directory")

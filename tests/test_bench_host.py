@@ -121,3 +121,35 @@ def test_device_state_fails_softly_without_gpu():
 
     s = bench.device_state(torch)
     assert s["power_cap_w"] is None and s["error"]
+
+
+def test_timeline_summary_on_synthetic_trace(tmp_path):
+    """Two modes, two calls each, 20 ms apart: copies [0, 100) and [100, 200) us with GEMMs
+    [50, 150) and [150, 250) us in every call of mode a; mode b has no overlap."""
+    d = tmp_path / "tr"
+    d.mkdir()
+    kt, mc = [], []
+    t = 50_000_000
+    for mode in ("a", "b"):
+        for _ in range(2):
+            if mode == "a":
+                mc += [["MEMORY_COPY_HOST_TO_DEVICE", t, t + 100_000, 3], ["MEMORY_COPY_HOST_TO_DEVICE", t + 100_000, t + 200_000, 3]]
+                kt += [[KERNEL, t + 50_000, t + 150_000, 0], [KERNEL, t + 150_000, t + 250_000, 1]]
+            else:
+                mc += [["MEMORY_COPY_DEVICE_TO_DEVICE", t, t + 100_000, 3]]
+                kt += [[KERNEL, t + 100_000, t + 180_000, 0]]
+            t += 20_000_000
+    kt.insert(0, ["void at::native::fill(int)", 1_000_000, 1_010_000, 0])  # setup, no GEMM
+    _write(d / "tr_kernel_trace.csv", ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Stream_Id"], kt)
+    _write(d / "tr_memory_copy_trace.csv", ["Direction", "Start_Timestamp", "End_Timestamp", "Stream_Id"], mc)
+    bench = tmp_path / "b.json"
+    bench.write_text(json.dumps({"profile_pass": "arrival", "T": 8192, "chunks": 8, "timeouts": 0,
+                                 "modes": [{"mode": "a", "calls": 2}, {"mode": "b", "calls": 2}]}) + "\n")
+    out = tmp_path / "tl.md"
+    r = subprocess.run([sys.executable, "-m", "chunked_tp_overlap_amd.rocprof_summary", "--timeline", str(d),
+                        "--bench-json", str(bench), "--out", str(out)],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 0, r.stderr
+    md = out.read_text()
+    assert "| a | 2 | 250.0 | 200.0 | 200.0 | 150.0 | 400.0 |" in md
+    assert "| b | 2 | 180.0 | 100.0 | 80.0 | 0.0 | 180.0 |" in md
