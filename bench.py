@@ -752,12 +752,21 @@ def qkv_fp8(ub, wl, torch, np, dev):
 
 def cpu_baseline(q, min_seconds):
     """The oracle as it stands, timed on the host cores over the same microbatches (whole
-    microbatches, in order, repeating passes until at least `min_seconds` of work)."""
+    microbatches, in order, repeating passes until at least `min_seconds` of work).  Every
+    fourth microbatch of the first pass is also run on the GPU (outside the oracle's timing)
+    and compared with the oracle's output: the bit-equal fraction and the largest error as
+    a fraction of the gate 4e-3 * |a_row| * |w_col|."""
     import numpy as np
 
+    from oracle import bf16 as ob
     from oracle import gemm as og
     from oracle import manager as om
     from oracle import plan as op
+
+    ub, torch = q.ub, q.torch
+    gpu_cfg = q.cfg(atomic=True)
+    w_cols = np.linalg.norm(ob.decode(q.w_host), axis=0)
+    parity = {"microbatches": 0, "elements": 0, "bit_equal": 0, "max_err_over_gate": 0.0}
 
     try:
         from threadpoolctl import threadpool_info
@@ -779,6 +788,17 @@ def cpu_baseline(q, min_seconds):
             og.ag_chunked(model, q.w_host, w.n_cols, w.n_cols, c, w.n_cols, cfg)
             elapsed += time.perf_counter() - t0
             flops += 2.0 * T * w.hidden * w.n_cols
+            if done < len(q.Ts) and done % 4 == 0:  # parity of this microbatch, untimed
+                ub.ub_set_active_shape(q.h, (T, w.hidden))
+                ub.ub_gemm_ag_chunked(q.h, q.w_t, w.n_cols, w.n_cols, q.c_t, w.n_cols, gpu_cfg, q.stream)
+                torch.cuda.synchronize()
+                g = q.c_t[:T].cpu().numpy().view(np.uint16)
+                err = np.abs(ob.decode(g) - ob.decode(c[:T]))
+                gate = 4e-3 * np.outer(np.linalg.norm(ob.decode(q.a_host[:T]), axis=1), w_cols)
+                parity["microbatches"] += 1
+                parity["elements"] += int(g.size)
+                parity["bit_equal"] += int(np.sum(g == c[:T]))
+                parity["max_err_over_gate"] = max(parity["max_err_over_gate"], float(np.max(err / gate)))
             done += 1
             if elapsed >= min_seconds and done >= len(q.Ts):
                 break
@@ -787,7 +807,11 @@ def cpu_baseline(q, min_seconds):
             "kind": "oracle",
             "sample": f"{done} qkv microbatches ({done / len(q.Ts):.2f} passes over the 32 of one "
                       f"step), numpy fp64 chunked GEMM + bf16 RNE, {elapsed:.1f} s",
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(),
+            "parity": {"microbatches": parity["microbatches"], "elements": parity["elements"],
+                       "bit_equal_fraction": round(parity["bit_equal"] / max(1, parity["elements"]), 5),
+                       "max_err_over_gate": round(parity["max_err_over_gate"], 5),
+                       "note": "device-side chunk loop vs the oracle on every 4th microbatch of one step"}}
 
 
 if __name__ == "__main__":
