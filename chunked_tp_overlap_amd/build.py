@@ -23,6 +23,7 @@ SOURCES = ["ub_api.cpp", "ub_plan.cpp", "gemm_bf16.hip", "gemm_fp8.hip", "quanti
            "reduce_partials.hip"]
 
 ARCH = "gfx950"
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
     "-I", INCLUDE, "-I", CSRC,
@@ -66,7 +67,8 @@ def build(verbose=False):
     with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, *objs, "-o", tmp]
+    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, *objs,
+           "-L" + os.path.join(ROCM, "lib"), "-lrocprofiler-sdk-roctx", "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -26,6 +26,8 @@
 #include <string>
 #include <vector>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "ub_internal.h"
 
 constexpr int kMaxArrivalChunks = 64;
@@ -73,6 +75,16 @@ struct ub_ctx {
 };
 
 namespace {
+
+// A roctx range around each work-issuing entry point, so that a marker trace
+// (rocprofv3 --marker-trace) shows which library call issued which launches and copies.
+// Without a profiler attached the push and pop do nothing.
+struct TraceRange {
+  explicit TraceRange(const char* name) { roctxRangePushA(name); }
+  ~TraceRange() { roctxRangePop(); }
+  TraceRange(const TraceRange&) = delete;
+  TraceRange& operator=(const TraceRange&) = delete;
+};
 
 constexpr int64_t kMaxRowsPerUnit = int64_t(1) << 30;
 
@@ -490,6 +502,7 @@ UB_API ub_status_t ub_get_plan(ub_handle_t h, const ub_overlap_cfg_t* cfg, ub_op
 
 UB_API ub_status_t ub_copy_in(ub_handle_t h, const void* src, int64_t rows, int64_t row_offset,
                               ub_stream_t stream) {
+  const TraceRange range("ub_copy_in");
   if (!h) return UB_ERR_NOT_INITIALIZED;
   if (!src) return fail(h, UB_ERR_INVALID_ARG, "src is NULL");
   if (rows < 0 || row_offset < 0 || row_offset + rows > h->T)
@@ -732,6 +745,7 @@ ub_status_t ag_call(ub_ctx* h, const void* src, int src_on_host, const void* w, 
 UB_API ub_status_t ub_gemm_ag_chunked(ub_handle_t h, const void* w, int64_t n_cols, int64_t ldw,
                                       void* c, int64_t ldc, const ub_overlap_cfg_t* cfg,
                                       ub_stream_t stream) {
+  const TraceRange range("ub_gemm_ag_chunked");
   return ag_call(h, nullptr, 0, w, n_cols, ldw, c, ldc, cfg, stream);
 }
 
@@ -739,6 +753,7 @@ UB_API ub_status_t ub_gemm_ag_arrival(ub_handle_t h, const void* src, int32_t sr
                                       const void* w, int64_t n_cols, int64_t ldw, void* c,
                                       int64_t ldc, const ub_overlap_cfg_t* cfg,
                                       ub_stream_t stream) {
+  const TraceRange range("ub_gemm_ag_arrival");
   if (!h) return UB_ERR_NOT_INITIALIZED;
   if (!src) return fail(h, UB_ERR_INVALID_ARG, "src is NULL");
   return ag_call(h, src, src_on_host != 0, w, n_cols, ldw, c, ldc, cfg, stream);
@@ -746,6 +761,7 @@ UB_API ub_status_t ub_gemm_ag_arrival(ub_handle_t h, const void* src, int32_t sr
 
 UB_API ub_status_t ub_deliver_chunks(ub_handle_t h, const void* src, int32_t src_on_host,
                                      const ub_overlap_cfg_t* cfg, ub_stream_t stream) {
+  const TraceRange range("ub_deliver_chunks");
   if (!h) return UB_ERR_NOT_INITIALIZED;
   ub_status_t st = need_dtype(h, UB_DTYPE_BF16, "ub_deliver_chunks");
   if (st != UB_OK) return st;
@@ -766,6 +782,7 @@ UB_API ub_status_t ub_deliver_chunks(ub_handle_t h, const void* src, int32_t src
 
 UB_API ub_status_t ub_quantize_in(ub_handle_t h, const void* src, int64_t rows,
                                   int64_t row_offset, float scale, ub_stream_t stream) {
+  const TraceRange range("ub_quantize_in");
   if (!h) return UB_ERR_NOT_INITIALIZED;
   ub_status_t st = need_dtype(h, UB_DTYPE_FP8_E4M3, "ub_quantize_in");
   if (st != UB_OK) return st;
@@ -801,6 +818,7 @@ UB_API ub_status_t ub_gemm_ag_chunked_fp8(ub_handle_t h, const void* w, int64_t 
                                           int64_t ldw, float scale_inv_a, float scale_inv_w,
                                           void* c, int64_t ldc, const ub_overlap_cfg_t* cfg,
                                           ub_stream_t stream) {
+  const TraceRange range("ub_gemm_ag_chunked_fp8");
   if (!h) return UB_ERR_NOT_INITIALIZED;
   ub_status_t st = need_dtype(h, UB_DTYPE_FP8_E4M3, "ub_gemm_ag_chunked_fp8");
   if (st != UB_OK) return st;
@@ -868,6 +886,7 @@ UB_API ub_status_t ub_gemm_ag_chunked_fp8(ub_handle_t h, const void* w, int64_t 
 UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, int64_t lda,
                                       const void* w, int64_t ldw, void* out, int64_t ldo,
                                       const ub_overlap_cfg_t* cfg, ub_stream_t stream) {
+  const TraceRange range("ub_gemm_rs_chunked");
   if (!h) return UB_ERR_NOT_INITIALIZED;
   ub_status_t st = need_dtype(h, UB_DTYPE_BF16, "the reduce-scatter GEMM");
   if (st != UB_OK) return st;
@@ -967,6 +986,7 @@ UB_API ub_status_t ub_gemm_rs_chunked_fp8(ub_handle_t h, const void* a, int64_t 
                                           const void* w, int64_t ldw, float scale_inv_a,
                                           float scale_inv_w, void* out, int64_t ldo,
                                           const ub_overlap_cfg_t* cfg, ub_stream_t stream) {
+  const TraceRange range("ub_gemm_rs_chunked_fp8");
   if (!h) return UB_ERR_NOT_INITIALIZED;
   ub_status_t st = need_dtype(h, UB_DTYPE_BF16, "the reduce-scatter GEMM (bf16 partials)");
   if (st != UB_OK) return st;
@@ -1058,6 +1078,7 @@ UB_API ub_status_t ub_gemm_rs_chunked_fp8(ub_handle_t h, const void* a, int64_t 
 
 UB_API ub_status_t ub_reduce_partials(ub_handle_t h, void* out, int64_t ldo,
                                       int32_t reduce_order, ub_stream_t stream) {
+  const TraceRange range("ub_reduce_partials");
   if (!h) return UB_ERR_NOT_INITIALIZED;
   if (need_dtype(h, UB_DTYPE_BF16, "ub_reduce_partials") != UB_OK) return UB_ERR_DTYPE;
   if (!h->ws) return fail(h, UB_ERR_NOT_INITIALIZED, "no reduce-scatter workspace registered");
