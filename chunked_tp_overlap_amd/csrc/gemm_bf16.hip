@@ -73,6 +73,7 @@ struct Params {
   // arrival gating (GemmArgs): nullptr ready = none
   const uint32_t* ready;
   uint32_t* timeouts;
+  uint64_t wait_ticks;
   uint32_t epoch;
   int32_t n_chunks;
   int32_t chunk_row0[kMaxGemmUnits + 1];
@@ -96,7 +97,7 @@ __device__ inline void wait_ready(const Params& p, int r0, int r1) {
   bool late = false;
   for (; !late && c < p.n_chunks && p.chunk_row0[c] < r1; ++c) {
     while (__hip_atomic_load(p.ready + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != p.epoch) {
-      if (__builtin_amdgcn_s_memrealtime() - t0 > kReadyTimeoutTicks) {
+      if (__builtin_amdgcn_s_memrealtime() - t0 > p.wait_ticks) {
         late = true;
         break;
       }
@@ -459,6 +460,7 @@ hipError_t launch(K kernel, const GemmArgs& g, const GemmUnits& units, hipStream
   p.group = tile_group(tiles, C::NW == 8 ? 1 : 2);
   p.ready = g.ready;
   p.timeouts = g.timeouts;
+  p.wait_ticks = g.wait_ticks ? g.wait_ticks : kReadyTimeoutTicks;
   p.epoch = g.epoch;
   p.n_chunks = g.ready ? g.n_chunks : 0;
   for (int c = 0; c <= p.n_chunks && c <= kMaxGemmUnits; ++c) p.chunk_row0[c] = g.chunk_row0[c];

@@ -21,6 +21,7 @@
 #include <mutex>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -602,9 +603,24 @@ ub_status_t join_deliveries(ub_ctx* h, hipStream_t caller) {
 // they read.  Everything on the copy stream is issued before the GEMM, so where the two
 // streams share a hardware queue the copies run first and nothing waits on work queued
 // behind it.
+// Test hooks of the wait's failure path, read on every call: UBX_ARRIVAL_WAIT_US sets the
+// bound of a tile's wait (microseconds; default 0.5 s), and UBX_ARRIVAL_DROP_FLAGS=1 writes
+// no flag for the delivered chunks, so that their tiles run into the bound and end.
+uint64_t arrival_wait_ticks() {
+  const char* s = std::getenv("UBX_ARRIVAL_WAIT_US");
+  const long long us = s ? std::atoll(s) : 0;
+  return us > 0 ? static_cast<uint64_t>(us) * 100 : 0;  // 100 MHz ticks
+}
+
+bool arrival_drop_flags() {
+  const char* s = std::getenv("UBX_ARRIVAL_DROP_FLAGS");
+  return s && std::strcmp(s, "1") == 0;
+}
+
 ub_status_t deliver_flagged(ub_ctx* h, const uint16_t* src, int src_on_host,
                             const ub_overlap_cfg_t* cfg, const ChunkMap& m, uint32_t epoch) {
   const hipMemcpyKind kind = src_on_host ? hipMemcpyHostToDevice : hipMemcpyDeviceToDeviceNoCU;
+  const bool drop = arrival_drop_flags();
   const int64_t H = h->hidden, T = h->T;
   auto flag = [&](int c) {
     hipError_t e = hipStreamWriteValue32(h->copy_stream, h->ready + c, epoch, 0);
@@ -621,7 +637,7 @@ ub_status_t deliver_flagged(ub_ctx* h, const uint16_t* src, int src_on_host,
                                       static_cast<size_t>(rows * H) * 2, kind, h->copy_stream);
         if (e != hipSuccess) return hip_fail(h, e, "arrival copy");
       }
-      if ((st = flag(c)) != UB_OK) return st;
+      if (!drop && (st = flag(c)) != UB_OK) return st;
     }
   }
   return UB_OK;
@@ -682,6 +698,7 @@ ub_status_t ag_call(ub_ctx* h, const void* src, int src_on_host, const void* w, 
       g.ready = h->ready;
       g.epoch = epoch;
       g.timeouts = h->ready + ubx::kReadyTimeoutWord;
+      g.wait_ticks = arrival_wait_ticks();
       g.n_chunks = m.n;
       for (int c = 0; c <= m.n; ++c) g.chunk_row0[c] = static_cast<int32_t>(m.row0(h->T, c));
     }

@@ -57,6 +57,7 @@ struct GemmArgs {
   const uint32_t* ready = nullptr;
   uint32_t epoch = 0;
   uint32_t* timeouts = nullptr;
+  uint64_t wait_ticks = 0;  // bound of a tile's wait in 100 MHz ticks (0: ~0.5 s)
   int32_t n_chunks = 0;
   int32_t chunk_row0[kMaxGemmUnits + 1] = {};
 };

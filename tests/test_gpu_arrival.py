@@ -219,3 +219,44 @@ def test_arrival_qkv_full_size(ub):
         gu.check_close(ref[rows], og.ag_rows(a[rows], wt, N), a[rows], wt, "arrival qkv rows")
     finally:
         reg.close()
+
+
+def test_arrival_device_loop_wait_bound(ub, monkeypatch):
+    """The failure path of the device-side loop's wait, forced from the host: no flag is
+    written for the delivered chunks (UBX_ARRIVAL_DROP_FLAGS=1) and the bound is 2 ms
+    (UBX_ARRIVAL_WAIT_US), so the tiles that need those chunks give up, count timeouts and
+    end: the call returns and nothing hangs.  The tiles of the local chunk, whose flag is
+    written, are still right.  A normal call afterwards is bit-identical to the
+    complete-buffer GEMM and adds no timeout."""
+    monkeypatch.setenv("UBX_GEMM_TILE", "256x256")  # the local chunk is exactly one tile row
+    rng = np.random.default_rng(55)
+    cap, H, N, T, tp, rank = 1024, 512, 264, 1024, 4, 1
+    a = wl.normal_bits(rng, (T, H))
+    w_t = gu.dev(wl.normal_bits(rng, (H, N), 0.02))
+    reg = gu.Registration(ub, cap, H, tp, workspace=False, pad_rows=8)
+    try:
+        reg.set_T(T)
+        reg.fill(a)
+        ref = gu.canary((T, N))
+        ub.ub_gemm_ag_chunked(reg.h, w_t, N, N, ref, N, ub.make_cfg("bulk", 1))
+        torch.cuda.synchronize()
+        ref = gu.host(ref)
+        lo, hi = rank * T // tp, (rank + 1) * T // tp
+        cfg = ub.make_cfg("ring_exchange", rank=rank, atomic_gemm=True)
+        before = ub.ub_arrival_timeouts(reg.h)
+        monkeypatch.setenv("UBX_ARRIVAL_WAIT_US", "2000")
+        monkeypatch.setenv("UBX_ARRIVAL_DROP_FLAGS", "1")
+        print("[arrival wait bound] flags dropped, 2 ms bound", flush=True)
+        c = gu.canary((T, N))
+        ub.ub_gemm_ag_arrival(reg.h, gu.dev(a), w_t, N, N, c, N, cfg)
+        torch.cuda.synchronize()
+        after = ub.ub_arrival_timeouts(reg.h)
+        assert after > before
+        assert np.array_equal(gu.host(c)[lo:hi], ref[lo:hi])
+        monkeypatch.delenv("UBX_ARRIVAL_WAIT_US")
+        monkeypatch.delenv("UBX_ARRIVAL_DROP_FLAGS")
+        print("[arrival wait bound] normal call", flush=True)
+        _case(ub, reg, a, w_t, N, dict(method="ring_exchange", rank=rank, atomic_gemm=True), ref, T, tp)
+        assert ub.ub_arrival_timeouts(reg.h) == after
+    finally:
+        reg.close()
