@@ -87,8 +87,6 @@ GemmUnits tile_aligned_units(const GemmUnits& u, int bm);
 // Row tiles of bm rows that a launch over `u` runs (after tile_aligned_units).
 int64_t row_tiles(const GemmUnits& u, int bm);
 
-// out[r, c] = bf16( sum_{s < nslots} float(parts[s*slot_stride + r*ldp + c]) ), ascending s.
-// cols % 8 == 0, ldp/ldo % 8 == 0, pointers 16-byte aligned.
 // FP8 (E4M3) GEMM: C [*, n] bf16 = bf16(scale * A B^T) with A [*, k] and B [n, k] E4M3
 // codes (row strides in bytes), units of rows as for launch_gemm_bf16_units.  batch > 1
 // runs batch entries (blockIdx.z) whose A and B start a/b_batch_stride bytes further and
@@ -115,9 +113,11 @@ hipError_t launch_quantize_e4m3(const uint16_t* src, int64_t lds, uint8_t* dst, 
                                 int64_t rows, int64_t cols, float scale, hipStream_t stream);
 
 // Partial-sum reduction of `rows` x `cols` elements: slot s at parts + s * slot_stride
-// (row stride ldp), result at out (row stride ldo).  ring != 0: ring order with a bf16
-// rounding per hop, where local row i is global row row0 + i of shard
-// (row0 + i) / shard_rows.
+// (row stride ldp), result at out (row stride ldo).  ring == 0:
+// out[r, c] = bf16(sum_{s < nslots} float(parts[s*slot_stride + r*ldp + c])), ascending s.
+// ring != 0: ring order with a bf16 rounding per hop, where local row i is global row
+// row0 + i of shard (row0 + i) / shard_rows.  cols % 8 == 0, ldp/ldo % 8 == 0, pointers
+// 16-byte aligned.
 struct ReduceArgs {
   const uint16_t* parts;
   int64_t slot_stride;
