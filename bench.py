@@ -570,6 +570,13 @@ def secondary(ub, wl, torch, np, dev):
         st = _call_stats(lambda: ub.ub_gemm_rs_chunked(h, a_t, w.k, w.k, w_t, w.hidden, o_t, w.hidden, cfg, stream),
                          torch, stream)
         row["atomic_gemm_ring_order"] = _stats_row(f, st, MFMA_PEAK_BF16_TFLOPS)
+        # the sum fused into the slice-GEMM launch (same bits as the separate reduction)
+        for atomic in (False, True):
+            cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, False, atomic, fuse_reduce=True)
+            st = _call_stats(lambda: ub.ub_gemm_rs_chunked(h, a_t, w.k, w.k, w_t, w.hidden, o_t, w.hidden, cfg, stream),
+                             torch, stream)
+            row["fused_atomic_gemm" if atomic else "fused_pipeline_3_streams"] = _stats_row(
+                f, st, MFMA_PEAK_BF16_TFLOPS)
         rbytes = (w.tp + 1) * T * w.hidden * 2.0
         for order in ("ascending", "ring"):
             warm = _time_calls(lambda: ub.ub_reduce_partials(h, o_t, w.hidden, order, stream), torch, stream, 10)

@@ -47,6 +47,7 @@
 //    and within an XCD tiles are walked in groups of rows that share B columns.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <map>
@@ -77,6 +78,13 @@ struct Params {
   uint32_t epoch;
   int32_t n_chunks;
   int32_t chunk_row0[kMaxGemmUnits + 1];
+  // fused reduction (GemmArgs): nslots == 0 = none
+  uint16_t* out;
+  int64_t ldo;
+  uint32_t* counters;
+  int64_t row0, shard_rows;
+  int32_t nslots;
+  int32_t ring;
 };
 
 // Arrival flags (see ub_internal.h).  Host code takes the array's device address from
@@ -107,6 +115,39 @@ __device__ inline void wait_ready(const Params& p, int r0, int r1) {
   if (late && (threadIdx.x & 63) == 0)
     __hip_atomic_fetch_add(p.timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+}
+
+// ---- fused reduction arithmetic (the same operations as the separate reduction kernel) --
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ inline float round_to_bf16(float x) {  // RNE, as an fp32 value
+  return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x)) << 16);
+}
+
+// Hop h of the sum of 8 elements.  Ascending order: fp32 adds from a zero start, one
+// rounding at the end.  Ring order: start from the first partial, round to bf16 after
+// every later hop.
+__device__ inline void add_hop(float (&acc)[8], u32x4 x, int h, bool ring) {
+  const float v[8] = {bf16_lo(x[0]), bf16_hi(x[0]), bf16_lo(x[1]), bf16_hi(x[1]),
+                      bf16_lo(x[2]), bf16_hi(x[2]), bf16_lo(x[3]), bf16_hi(x[3])};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (h == 0)
+      acc[i] = ring ? v[i] : 0.0f + v[i];
+    else
+      acc[i] = ring ? round_to_bf16(acc[i] + v[i]) : acc[i] + v[i];
+  }
+}
+
+template <int NL>
+__device__ inline void sum_slots(float (&acc)[8], const u32x4 (&x)[NL], bool ring) {
+#pragma unroll
+  for (int h = 0; h < NL; ++h) add_hop(acc, x[h], h, ring);
+}
+
+__device__ inline u32x4 pack8(const float (&acc)[8]) {
+  return u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+               pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
 }
 
 template <int BM_, int BN_, int BK_, int S_, int WGM_, int WGN_>
@@ -160,6 +201,7 @@ struct Cfg {
 template <class C>
 struct Tile {
   int lane, wave, group, wm, wn, m0, m_end, n0;
+  int tile, z;                           // tile of the launch and batch entry
   uint16_t* cg;
   i32x4 ra, rb;
   uint32_t a_off[C::NA_MAX > 0 ? C::NA_MAX : 1], b_off[C::NB_MAX > 0 ? C::NB_MAX : 1];
@@ -174,12 +216,14 @@ struct Tile {
     group = wave >> 2;
     wm = wave / C::WGN;
     wn = wave % C::WGN;
+    z = blockIdx.z;
+    tile = blockIdx.x;
     int tn;
-    if (!tile_of(p, blockIdx.x, C::BM, m0, m_end, tn)) return false;
+    if (!tile_of(p, tile, C::BM, m0, m_end, tn)) return false;
     n0 = tn * C::BN;
-    const uint16_t* A = p.a + blockIdx.z * p.sa + (int64_t)m0 * p.lda;
-    const uint16_t* B = p.b + blockIdx.z * p.sb + n0;
-    cg = p.c + blockIdx.z * p.sc;
+    const uint16_t* A = p.a + z * p.sa + (int64_t)m0 * p.lda;
+    const uint16_t* B = p.b + z * p.sb + n0;
+    cg = p.c + z * p.sc;
     // A from this tile's first row, valid rows only; B from column n0 of the batch entry
     const int rows_valid = min(C::BM, m_end - m0);
     ra = make_rsrc(A, (uint32_t)(rows_valid * p.lda * 2));
@@ -298,6 +342,103 @@ struct Tile {
             *LDS_PTR(const u32x4, ct + r * C::LDC + cc);
     }
   }
+
+  // Fused reduction, after store().  The batch entries' tiles of one output tile (the
+  // slices) may run on different XCDs, each with its own L2: every wave makes its partial
+  // stores visible at agent scope, then one lane counts the tile's arrival.  The slice
+  // that arrives last resets the counter, acquires, and sums every slice's partial in the
+  // order launch_reduce_partials uses, so the result is bit-identical to the separate
+  // reduction.  The arrival count goes through row 0's padding of the LDS tile, which the
+  // store loop never reads.
+  __device__ inline void fused_reduce(unsigned char* smem, const Params& p, int tid) const {
+    switch (p.nslots) {
+      case 2: reduce_tile<2>(smem, p, tid); break;
+      case 4: reduce_tile<4>(smem, p, tid); break;
+      case 8: reduce_tile<8>(smem, p, tid); break;
+      default: reduce_tile<0>(smem, p, tid); break;
+    }
+  }
+
+  template <int NS>
+  __device__ inline void reduce_tile(unsigned char* smem, const Params& p, int tid) const {
+    uint32_t* arrived = reinterpret_cast<uint32_t*>(smem + C::BN * 2);
+    const int ns = NS > 0 ? NS : p.nslots;
+    uint32_t* counter = p.counters + tile;
+    // Each wave's partial stores complete (reach the L2) before the barrier; after it one
+    // release RMW (an L2 write-back, then the count) publishes the whole tile.
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t before =
+          __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      // the last slice acquires every other slice's release before anyone reads
+      if (before == (uint32_t)(ns - 1)) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      *LDS_PTR(uint32_t, arrived) = before;
+    }
+    __syncthreads();
+    if (*LDS_PTR(const uint32_t, arrived) != (uint32_t)(ns - 1)) return;
+    if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    constexpr int VPR = C::BN / 8;
+    constexpr int NV = C::BM * VPR / C::THREADS;  // 16-byte vectors per lane
+    // G vectors per round with all their slices' loads in flight (16 loads per lane)
+    constexpr int G0 = NS > 0 && NS <= 16 ? 16 / NS : 1;
+    constexpr int G = NV % G0 == 0 ? G0 : (NV % 4 == 0 ? 4 : (NV % 2 == 0 ? 2 : 1));
+    static_assert(NV % G == 0, "vectors per lane split into rounds");
+    constexpr int NL = NS > 0 ? NS : 1;
+    for (int i0 = 0; i0 < NV; i0 += G) {
+      int64_t off[G], oo[G];
+      int first[G];
+      bool ok[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const int v = tid + (i0 + j) * C::THREADS;
+        const int r = v / VPR, cc = (v % VPR) * 8;
+        const int gr = m0 + r, gc = n0 + cc;
+        ok[j] = gr < m_end && gc < p.n;
+        off[j] = ok[j] ? (int64_t)gr * p.ldc + gc : 0;
+        oo[j] = ok[j] ? (int64_t)gr * p.ldo + gc : 0;
+        first[j] = p.ring ? (int)(((p.row0 + gr) / p.shard_rows + 1) % ns) : 0;
+      }
+      if constexpr (NS > 0) {
+        // hop h of vector j reads slot (first + h) mod NS: every partial of the vector, in
+        // the order it is summed
+        u32x4 x[G][NL];
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+          for (int h = 0; h < NL; ++h) {
+            int s = first[j] + h;
+            if (s >= NL) s -= NL;
+            x[j][h] = ok[j] ? __builtin_nontemporal_load(
+                                  GLOBAL_PTR(const u32x4, p.c + s * p.sc + off[j]))
+                            : u32x4{0, 0, 0, 0};
+          }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          float acc[8];
+          sum_slots<NL>(acc, x[j], p.ring != 0);
+          if (ok[j])
+            __builtin_nontemporal_store(pack8(acc), GLOBAL_PTR(u32x4, p.out + oo[j]));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          float acc[8];
+          for (int h = 0; h < ns; ++h) {
+            int s = first[j] + h;
+            if (s >= ns) s -= ns;
+            const u32x4 x = ok[j] ? __builtin_nontemporal_load(
+                                        GLOBAL_PTR(const u32x4, p.c + s * p.sc + off[j]))
+                                  : u32x4{0, 0, 0, 0};
+            add_hop(acc, x, h, p.ring != 0);
+          }
+          if (ok[j])
+            __builtin_nontemporal_store(pack8(acc), GLOBAL_PTR(u32x4, p.out + oo[j]));
+        }
+      }
+    }
+  }
 };
 
 template <class C>
@@ -380,6 +521,7 @@ void gemm_bf16_pingpong(Params p) {
   if (group == 0) __asm__ volatile("s_barrier" ::: "memory");  // matches group 1's b1
   wait_vmcnt_and_barrier<0>();  // trailing out-of-range loads landed before LDS is reused
   t.store(smem, p, tid, acc);
+  if (p.nslots) t.fused_reduce(smem, p, tid);
 }
 
 // ---- 4-wave, S-stage pipeline -----------------------------------------------------------
@@ -429,6 +571,7 @@ void gemm_bf16_pipelined(Params p) {
   }
   wait_vmcnt_and_barrier<0>();  // trailing out-of-range loads landed before LDS is reused
   t.store(smem, p, tid, acc);
+  if (p.nslots) t.fused_reduce(smem, p, tid);
 }
 
 template <class C, class K>
@@ -464,6 +607,16 @@ hipError_t launch(K kernel, const GemmArgs& g, const GemmUnits& units, hipStream
   p.epoch = g.epoch;
   p.n_chunks = g.ready ? g.n_chunks : 0;
   for (int c = 0; c <= p.n_chunks && c <= kMaxGemmUnits; ++c) p.chunk_row0[c] = g.chunk_row0[c];
+  p.nslots = g.fuse_nslots;
+  if (p.nslots > 0) {
+    if (tiles > g.counters_n) return hipErrorInvalidValue;
+    p.out = g.fuse_out;
+    p.ldo = g.fuse_ldo;
+    p.counters = g.counters;
+    p.ring = g.fuse_ring;
+    p.row0 = g.fuse_row0;
+    p.shard_rows = g.fuse_shard_rows;
+  }
   const int64_t grid = tiles;
   if (grid > 0x7FFFFFFF || g.batch > 65535) return hipErrorInvalidValue;
   static bool configured = false;
@@ -473,8 +626,8 @@ hipError_t launch(K kernel, const GemmArgs& g, const GemmUnits& units, hipStream
     if (e != hipSuccess) return e;
     configured = true;
   }
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid, 1, g.batch), dim3(C::THREADS),
-                     C::LDS_BYTES, stream, p);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid, 1, g.batch), dim3(C::THREADS), C::LDS_BYTES,
+                     stream, p);
   return hipGetLastError();
 }
 
@@ -568,6 +721,19 @@ hipError_t launch_gemm_bf16_units(const GemmArgs& g, const GemmUnits& u, hipStre
     return hipErrorInvalidValue;
   for (int i = 0; i < u.n; ++i)
     if (u.rows[i] < 0 || u.row0[i] < 0) return hipErrorInvalidValue;
+  if (g.fuse_nslots != 0) {
+    if (g.fuse_nslots != g.batch || !g.fuse_out || !g.counters || g.fuse_ldo < g.n ||
+        g.fuse_ldo % 8 != 0)
+      return hipErrorInvalidValue;
+    if (g.fuse_ring) {  // every row's shard index must lie in [0, nslots)
+      int64_t last = 0;
+      for (int i = 0; i < u.n; ++i)
+        if (u.rows[i] > 0) last = std::max<int64_t>(last, (int64_t)u.row0[i] + u.rows[i] - 1);
+      if (g.fuse_shard_rows <= 0 || g.fuse_row0 < 0 ||
+          (g.fuse_row0 + last) / g.fuse_shard_rows >= g.fuse_nslots)
+        return hipErrorInvalidValue;
+    }
+  }
   switch (choose_tile(g, u)) {
     case kTile256x256:
       return launch<PP256x256>(&gemm_bf16_pingpong<PP256x256, PP_D>, g, u, stream);
@@ -580,6 +746,15 @@ hipError_t launch_gemm_bf16_units(const GemmArgs& g, const GemmUnits& u, hipStre
     default:
       return launch<PL128x128>(&gemm_bf16_pipelined<PL128x128>, g, u, stream);
   }
+}
+
+int64_t fuse_counter_bound(const int64_t* rows, int n_units, int64_t n) {
+  // The smallest tile is 128 x 128; re-cutting units at tile boundaries adds at most one
+  // row tile per unit.
+  int64_t row_tiles_max = 0;
+  for (int i = 0; i < n_units; ++i)
+    if (rows[i] > 0) row_tiles_max += (rows[i] + 127) / 128 + 1;
+  return row_tiles_max * ((n + 127) / 128);
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream) {

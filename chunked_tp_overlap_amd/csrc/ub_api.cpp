@@ -70,6 +70,9 @@ struct ub_ctx {
   // device-side arrival gating: this handle's slot of arrival flags (-1: none yet)
   int ready_slot = -1;
   uint32_t* ready = nullptr;  // device address of the slot's words
+  // fused reduction: per-tile arrival counters (zero between launches)
+  uint32_t* fuse_counters = nullptr;
+  int64_t fuse_counters_n = 0;
   // scratch for plans
   ubx::Plan plan;
   std::string last_error;
@@ -311,6 +314,34 @@ ub_status_t check_cfg_common(ub_ctx* h, const ub_overlap_cfg_t* cfg) {
   if (cfg->reduce_order != UB_REDUCE_ASCENDING && cfg->reduce_order != UB_REDUCE_RING)
     return fail(h, UB_ERR_INVALID_ARG, "reduce_order=%d is not a ub_reduce_order_t",
                 cfg->reduce_order);
+  if (cfg->fuse_reduce != 0 && cfg->fuse_reduce != 1)
+    return fail(h, UB_ERR_INVALID_ARG, "fuse_reduce=%d must be 0 or 1", cfg->fuse_reduce);
+  return UB_OK;
+}
+
+// Counters of the fused reduction for `need` tiles: allocated on first use or when a plan
+// needs more than any before, and zeroed on the caller's stream, ahead of the launches that
+// use them (the compute streams fork from the caller's stream after it).  The kernels leave
+// them zero.
+ub_status_t ensure_fuse_counters(ub_ctx* h, int64_t need, hipStream_t caller) {
+  if (need <= h->fuse_counters_n) return UB_OK;
+  hipError_t e;
+  if (h->fuse_counters) {
+    e = hipFree(h->fuse_counters);  // waits for the device
+    h->fuse_counters = nullptr;
+    h->fuse_counters_n = 0;
+    if (e != hipSuccess) return hip_fail(h, e, "hipFree(fused-reduction counters)");
+  }
+  void* p = nullptr;
+  e = hipMalloc(&p, static_cast<size_t>(need) * sizeof(uint32_t));
+  if (e != hipSuccess) return hip_fail(h, e, "hipMalloc(fused-reduction counters)");
+  e = hipMemsetAsync(p, 0, static_cast<size_t>(need) * sizeof(uint32_t), caller);
+  if (e != hipSuccess) {
+    (void)hipFree(p);
+    return hip_fail(h, e, "hipMemset(fused-reduction counters)");
+  }
+  h->fuse_counters = static_cast<uint32_t*>(p);
+  h->fuse_counters_n = need;
   return UB_OK;
 }
 
@@ -375,6 +406,7 @@ UB_API void ub_overlap_cfg_default(ub_overlap_cfg_t* cfg) {
   cfg->num_sm = 0;
   cfg->set_sm_margin = 0;
   cfg->reduce_order = UB_REDUCE_ASCENDING;
+  cfg->fuse_reduce = 0;
 }
 
 UB_API const char* ub_status_string(ub_status_t s) {
@@ -928,10 +960,39 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
   const int64_t T = h->T;
   const int32_t tp = h->tp;
   hipStream_t caller = static_cast<hipStream_t>(stream);
+  const bool ring = cfg->reduce_order == UB_REDUCE_RING;
+  const bool fuse = cfg->fuse_reduce != 0;
+  // Fused reduction: unit u's launch counts its tiles in its own range of counters
+  // (units on different streams run at once); the device-side loop uses one range.
+  std::vector<int64_t> counter0;
+  if (fuse) {
+    std::vector<int64_t> rows;
+    for (const ub_plan_unit_t& u : h->plan.units) rows.push_back(u.row1 - u.row0);
+    int64_t need = 0;
+    for (size_t i = 0; i < rows.size(); ++i) {
+      counter0.push_back(need);
+      need += ubx::fuse_counter_bound(&rows[i], 1, H);
+    }
+    if ((st = ensure_device(h, 1)) != UB_OK) return st;
+    if ((st = ensure_fuse_counters(h, need, caller)) != UB_OK) return st;
+  }
+  auto set_fuse = [&](ubx::GemmArgs& g, int64_t row0, int64_t c0) {
+    if (!fuse) return;
+    g.fuse_out = static_cast<uint16_t*>(out) + row0 * ldo;
+    g.fuse_ldo = ldo;
+    g.fuse_nslots = tp;
+    g.fuse_ring = ring;
+    g.fuse_row0 = row0;
+    g.fuse_shard_rows = T / tp;
+    g.counters = h->fuse_counters + c0;
+    g.counters_n = h->fuse_counters_n - c0;
+  };
+  const double fused_flops = double(tp - 1) * H;  // per row: the reduction's adds
+  const double fused_bytes = 2.0 * (tp + 1) * H;  // per row: the reduction's reads and write
 
   if (cfg->atomic_gemm) {
     // One launch computes every unit's tp slice partials in plan order, then one
-    // reduction sums the whole active prefix.
+    // reduction sums the whole active prefix (or the launch's tiles sum them).
     ubx::GemmUnits units;
     if ((st = plan_units(h, &units)) != UB_OK) return st;
     if ((st = ensure_device(h, 1)) != UB_OK) return st;
@@ -949,11 +1010,13 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
     g.k = static_cast<int32_t>(ks);
     g.batch = tp;
     g.concurrency = 1;
-    st = timed_launch(h, caller, 0, 2.0 * T * k * H, 2.0 * (T * k + k * H + tp * T * H),
+    set_fuse(g, 0, 0);
+    st = timed_launch(h, caller, 0, 2.0 * T * k * H + (fuse ? fused_flops * T : 0.0),
+                      2.0 * (T * k + k * H + tp * T * H) + (fuse ? fused_bytes * T : 0.0),
                       [&] { return ubx::launch_gemm_bf16_units(g, units, caller); },
                       "slice GEMM launch");
-    if (st != UB_OK) return st;
-    const ubx::ReduceArgs r = reduce_args(h, 0, T, out, ldo, cfg->reduce_order == UB_REDUCE_RING);
+    if (st != UB_OK || fuse) return st;
+    const ubx::ReduceArgs r = reduce_args(h, 0, T, out, ldo, ring);
     return timed_launch(h, caller, 1, double(tp - 1) * T * H, 2.0 * (tp + 1) * T * H,
                         [&] { return ubx::launch_reduce_partials(r, caller); }, "reduce launch");
   }
@@ -961,7 +1024,8 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
   const int S = h->plan.n_streams;
   if ((st = ensure_device(h, S)) != UB_OK) return st;
   if ((st = fork_streams(h, caller, S)) != UB_OK) return st;
-  for (const ub_plan_unit_t& u : h->plan.units) {
+  for (size_t ui = 0; ui < h->plan.units.size(); ++ui) {
+    const ub_plan_unit_t& u = h->plan.units[ui];
     const int64_t rows = u.row1 - u.row0;
     if (rows <= 0) continue;
     if (rows > kMaxRowsPerUnit) return fail(h, UB_ERR_UNSUPPORTED, "unit too large");
@@ -983,14 +1047,15 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
     g.k = static_cast<int32_t>(ks);
     g.batch = tp;
     g.concurrency = S;
-    const double flops = 2.0 * rows * k * H;
-    const double gbytes = 2.0 * (rows * k + k * H + tp * rows * H);
+    if (fuse) set_fuse(g, u.row0, counter0[ui]);
+    const double flops = 2.0 * rows * k * H + (fuse ? fused_flops * rows : 0.0);
+    const double gbytes = 2.0 * (rows * k + k * H + tp * rows * H) + (fuse ? fused_bytes * rows : 0.0);
     st = timed_launch(h, s, 0, flops, gbytes, [&] { return ubx::launch_gemm_bf16(g, s); },
                       "slice GEMM launch");
     if (st != UB_OK) return st;
+    if (fuse) continue;
     // the reduction of this chunk follows its GEMMs on the same stream
-    const ubx::ReduceArgs r =
-        reduce_args(h, u.row0, rows, out, ldo, cfg->reduce_order == UB_REDUCE_RING);
+    const ubx::ReduceArgs r = reduce_args(h, u.row0, rows, out, ldo, ring);
     const double rbytes = 2.0 * (tp + 1) * rows * H;
     st = timed_launch(h, s, 1, double(tp - 1) * rows * H, rbytes,
                       [&] { return ubx::launch_reduce_partials(r, s); }, "reduce launch");
@@ -1008,6 +1073,8 @@ UB_API ub_status_t ub_gemm_rs_chunked_fp8(ub_handle_t h, const void* a, int64_t 
   ub_status_t st = need_dtype(h, UB_DTYPE_BF16, "the reduce-scatter GEMM (bf16 partials)");
   if (st != UB_OK) return st;
   if ((st = check_cfg_common(h, cfg)) != UB_OK) return st;
+  if (cfg->fuse_reduce)
+    return fail(h, UB_ERR_UNSUPPORTED, "fuse_reduce is implemented for bf16 operands only");
   if (!h->ws) return fail(h, UB_ERR_NOT_INITIALIZED, "no reduce-scatter workspace registered");
   if (!a || !w || !out) return fail(h, UB_ERR_INVALID_ARG, "a, w and out must be non-NULL");
   if (!aligned16(a) || !aligned16(w) || !aligned16(out))
@@ -1161,6 +1228,7 @@ UB_API ub_status_t ub_destroy(ub_handle_t h) {
     for (hipEvent_t ev : h->ev_arrive)
       if (ev) (void)hipEventDestroy(ev);
     for (hipEvent_t ev : h->free_events) (void)hipEventDestroy(ev);
+    if (h->fuse_counters) (void)hipFree(h->fuse_counters);
     if (cur >= 0 && cur != h->device) (void)hipSetDevice(cur);
   }
   release_ready_slot(h);

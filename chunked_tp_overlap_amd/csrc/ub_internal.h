@@ -60,7 +60,24 @@ struct GemmArgs {
   uint64_t wait_ticks = 0;  // bound of a tile's wait in 100 MHz ticks (0: ~0.5 s)
   int32_t n_chunks = 0;
   int32_t chunk_row0[kMaxGemmUnits + 1] = {};
+  // Fused reduction (reduce-scatter side): fuse_nslots > 0 (== batch) makes the last of the
+  // batch entries' tiles of each output tile to finish sum the entries' bf16 C tiles (the
+  // slice partials) into fuse_out (row stride fuse_ldo), exactly as launch_reduce_partials
+  // sums them: ascending slot order, or ring order (fuse_ring) with local row i in shard
+  // (fuse_row0 + i) / fuse_shard_rows.  counters holds one word per tile of the launch,
+  // zero at launch and left zero; a launch of more than counters_n tiles fails with
+  // hipErrorInvalidValue.
+  uint16_t* fuse_out = nullptr;
+  int64_t fuse_ldo = 0;
+  int32_t fuse_nslots = 0;
+  int32_t fuse_ring = 0;
+  int64_t fuse_row0 = 0;
+  int64_t fuse_shard_rows = 1;
+  uint32_t* counters = nullptr;
+  int64_t counters_n = 0;
 };
+// Counter words a fused launch over units of the given rows can need (for any tile shape).
+int64_t fuse_counter_bound(const int64_t* rows, int n_units, int64_t n);
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream);
 constexpr int kGemmKStep = 64;  // k must be a multiple of this
 

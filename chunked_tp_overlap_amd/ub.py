@@ -62,7 +62,7 @@ class UBError(RuntimeError):
 class ub_overlap_cfg_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "method", "num_splits", "num_max_streams", "aggregate", "atomic_gemm", "rank",
-        "use_ce", "num_sm", "set_sm_margin", "reduce_order")]
+        "use_ce", "num_sm", "set_sm_margin", "reduce_order", "fuse_reduce")]
 
 
 class ub_plan_unit_t(ctypes.Structure):
@@ -157,9 +157,10 @@ def _reduce_order(x):
 
 def make_cfg(method="ring_exchange", num_splits=1, num_max_streams=3, aggregate=False,
              atomic_gemm=False, rank=0, use_ce=True, num_sm=0, set_sm_margin=False,
-             reduce_order="ascending"):
+             reduce_order="ascending", fuse_reduce=False):
     """A ``ub_overlap_cfg_t`` from keyword options ([TE#1344] option names, plus the
-    reduce-scatter summation order "ascending" or "ring")."""
+    reduce-scatter summation order "ascending" or "ring" and whether the reduce-scatter
+    sum runs inside the slice-GEMM launch)."""
     cfg = ub_overlap_cfg_default()
     cfg.method = METHODS[method] if isinstance(method, str) else int(method)
     cfg.num_splits = int(num_splits)
@@ -171,6 +172,7 @@ def make_cfg(method="ring_exchange", num_splits=1, num_max_streams=3, aggregate=
     cfg.num_sm = int(num_sm)
     cfg.set_sm_margin = int(bool(set_sm_margin))
     cfg.reduce_order = _reduce_order(reduce_order)
+    cfg.fuse_reduce = int(bool(fuse_reduce))
     return cfg
 
 

@@ -144,7 +144,21 @@ typedef enum { UB_OP_AG = 0, UB_OP_RS = 1 } ub_op_t;
  *                    reduce-scatter computes ([TE#1344] "ring_exchange" moves chunks
  *                    between neighbours): for shard r the partial of slice r+1 starts,
  *                    slices r+2, ..., r (mod tp) are added one per hop in fp32 and the
- *                    running value is rounded to bf16 after every hop. */
+ *                    running value is rounded to bf16 after every hop.
+ *   fuse_reduce      reduce-scatter side, bf16 operands only (ignored on the all-gather
+ *                    side; 1 with ub_gemm_rs_chunked_fp8 -> UB_ERR_UNSUPPORTED).  0: the
+ *                    sum runs as its own launch after each unit's slice GEMMs.  1: inside
+ *                    the slice-GEMM launch, the last of the tp slice tiles of each output
+ *                    tile to finish sums the tp partials ([TE#1344] "pipeline": the
+ *                    GEMM chunks feed the reduce-scatter; here with no separate pass).  The
+ *                    partials still go through the workspace, and out is bit-identical to
+ *                    fuse_reduce 0 for either reduce_order.  The first fused call on a
+ *                    handle (and one whose plan needs more tiles than any before) allocates
+ *                    a small counter array, one 4-byte word per possible output tile
+ *                    (tiles of 128 x 128), and zeroes it on `stream`; a larger array
+ *                    replaces a smaller one after a device-wide wait.  It is freed by
+ *                    ub_destroy.  Such a call must not be captured into a graph; later
+ *                    calls may be. */
 typedef enum { UB_REDUCE_ASCENDING = 0, UB_REDUCE_RING = 1 } ub_reduce_order_t;
 
 typedef struct {
@@ -158,6 +172,7 @@ typedef struct {
   int32_t num_sm;
   int32_t set_sm_margin;
   int32_t reduce_order;
+  int32_t fuse_reduce;
 } ub_overlap_cfg_t;
 
 /* One unit of an execution plan: rows [row0, row1) of the active T, at position `pos`
@@ -181,7 +196,7 @@ typedef struct {
 
 /* Fill `cfg` with the defaults of [TE#1344]: ring exchange, num_splits 1,
  * num_max_streams 3, use_ce 1, aggregate 0, atomic_gemm 0, set_sm_margin 0, num_sm 0,
- * rank 0, reduce_order UB_REDUCE_ASCENDING. */
+ * rank 0, reduce_order UB_REDUCE_ASCENDING, fuse_reduce 0. */
 UB_API void ub_overlap_cfg_default(ub_overlap_cfg_t* cfg);
 
 /* Bytes the caller must allocate for a registration of [capacity, hidden] over
@@ -417,7 +432,7 @@ UB_API ub_status_t ub_get_kernel_timing(ub_handle_t h, ub_kernel_stats_t* gemm,
                                         ub_kernel_stats_t* reduce);
 
 /* Destroy a handle: waits for the handle's own streams, then releases its streams,
- * events and arrival-flag slot.  The caller's streams are not waited for: work of this
+ * events, arrival-flag slot and fused-reduction counters.  The caller's streams are not waited for: work of this
  * handle still queued there must have finished (the caller synchronises first), or a
  * device-side loop of a gated arrival could wait on a slot that another handle has taken
  * (it would end at its time bound, with wrong results).  Caller buffers are untouched.

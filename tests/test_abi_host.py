@@ -183,6 +183,10 @@ def test_gemm_argument_errors_before_any_hip_call():
         assert st("ub_gemm_rs_chunked", h, FAKE, 256, 256, FAKE, 256, FAKE, 128, cp, None) == "UB_ERR_INVALID_ARG"
         bad = ub.make_cfg("ring_exchange", 2, reduce_order=2)
         assert st("ub_gemm_rs_chunked", h, FAKE, 256, 256, FAKE, 256, FAKE, 256, ctypes.byref(bad), None) == "UB_ERR_INVALID_ARG"
+        bad = ub.make_cfg("ring_exchange", 2)
+        bad.fuse_reduce = 2
+        assert st("ub_gemm_rs_chunked", h, FAKE, 256, 256, FAKE, 256, FAKE, 256, ctypes.byref(bad), None) == "UB_ERR_INVALID_ARG"
+        assert "fuse_reduce" in ub.ub_last_error(h)
         assert st("ub_reduce_partials", h_nows, FAKE, 256, 0, None) == "UB_ERR_NOT_INITIALIZED"
         assert st("ub_reduce_partials", h, FAKE, 256, 2, None) == "UB_ERR_INVALID_ARG"
         assert st("ub_reduce_partials", h, FAKE, 256, -1, None) == "UB_ERR_INVALID_ARG"
@@ -206,7 +210,7 @@ def test_cfg_default_fills_every_field():
     got = {n: getattr(cfg, n) for n, _ in cfg._fields_}
     assert got == {"method": ub.UB_RING_EXCHANGE, "num_splits": 1, "num_max_streams": 3,
                    "aggregate": 0, "atomic_gemm": 0, "rank": 0, "use_ce": 1, "num_sm": 0,
-                   "set_sm_margin": 0, "reduce_order": ub.UB_REDUCE_ASCENDING}
+                   "set_sm_margin": 0, "reduce_order": ub.UB_REDUCE_ASCENDING, "fuse_reduce": 0}
     # the library writes exactly sizeof(ub_overlap_cfg_t) bytes: a guard word after the
     # struct stays intact
     class Guarded(ctypes.Structure):
@@ -344,6 +348,10 @@ def test_rs_fp8_and_quantize_argument_errors_before_any_hip_call():
         # k / tp not a multiple of the 64-code step
         assert st("ub_gemm_rs_chunked_fp8", hb, FAKE, 192, 192, FAKE, 192, f(1), f(1), FAKE, 256,
                   cp, None) == "UB_ERR_UNSUPPORTED"
+        # the fused reduction exists for bf16 operands only
+        fused = ub.make_cfg("pipeline", 2, fuse_reduce=True)
+        assert st("ub_gemm_rs_chunked_fp8", hb, *ok[:9], ctypes.byref(fused), None) == "UB_ERR_UNSUPPORTED"
+        assert "bf16" in ub.ub_last_error(hb)
         # quantize: alignment, strides, sizes, scale; empty is a no-op
         q = "ub_quantize_e4m3"
         assert st(q, FAKE + 8, 64, FAKE, 64, 4, 64, f(1), None) == "UB_ERR_INVALID_ARG"

@@ -35,8 +35,14 @@ def test_graph_replays_match_eager(ub):
             ub.make_cfg("ring_exchange", 1, 2, True, False, rank=6)]    # aggregate, 2 streams
     rs_cfgs = [ub.make_cfg("pipeline", 4, 3, atomic_gemm=True),
                ub.make_cfg("ring_exchange", 1, 3, reduce_order="ring", rank=1)]
+    # the same sums with the reduction fused into the slice-GEMM launch (bf16 only); the
+    # eager pass allocates their counters (largest T first), so capture allocates nothing
+    fused_cfgs = [ub.make_cfg("pipeline", 4, 3, fuse_reduce=True),
+                  ub.make_cfg("ring_exchange", 1, 3, atomic_gemm=True, reduce_order="ring", rank=1,
+                              fuse_reduce=True)]
     outs = [gu.canary((cap, N)) for _ in range(len(Ts) * len(cfgs))]
     rs_outs = [gu.canary((cap, H)) for _ in range(len(Ts) * len(rs_cfgs) * 2)]
+    fused_outs = [gu.canary((cap, H)) for _ in range(len(Ts) * len(fused_cfgs))]
     # E4M3 operands of the reduce-scatter GEMM, quantized once (eagerly) on the GPU
     a8 = torch.empty((cap, K), dtype=torch.uint8, device="cuda")
     w8 = torch.empty((H, K), dtype=torch.uint8, device="cuda")
@@ -44,7 +50,7 @@ def test_graph_replays_match_eager(ub):
     ub.ub_quantize_e4m3(w_rs.t().contiguous(), K, w8, K, H, K, 4096.0)
 
     def step(stream):
-        i = j = 0
+        i = j = f = 0
         for T in Ts:
             ub.ub_set_active_shape(reg.h, (T, H))
             for cfg in cfgs:
@@ -55,6 +61,9 @@ def test_graph_replays_match_eager(ub):
                 ub.ub_gemm_rs_chunked_fp8(reg.h, a8, K, K, w8, K, 1.0 / 64, 1.0 / 4096, rs_outs[j + 1],
                                           H, cfg, stream)
                 j += 2
+            for cfg in fused_cfgs:
+                ub.ub_gemm_rs_chunked(reg.h, a_rs, K, K, w_rs, H, fused_outs[f], H, cfg, stream)
+                f += 1
 
     try:
         reg.ub_t[: cap * H].copy_(a.reshape(-1))
@@ -64,6 +73,13 @@ def test_graph_replays_match_eager(ub):
         torch.cuda.synchronize()
         eager = [gu.host(o) for o in outs]
         eager_rs = [gu.host(o) for o in rs_outs]
+        eager_fused = [gu.host(o) for o in fused_outs]
+        for t in range(len(Ts)):  # fused == separate reduction, same order
+            for c in range(len(fused_cfgs)):
+                assert np.array_equal(eager_fused[t * len(fused_cfgs) + c],
+                                      eager_rs[(t * len(rs_cfgs) + c) * 2]), (t, c)
+        rs_outs = rs_outs + fused_outs
+        eager_rs = eager_rs + eager_fused
         for o in outs + rs_outs:
             o.fill_(gu.CANARY)
         torch.cuda.synchronize()
