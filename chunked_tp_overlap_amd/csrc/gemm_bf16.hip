@@ -48,6 +48,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <map>
@@ -651,37 +652,121 @@ enum TileKind {
 // count suggests, and the efficiencies of the smaller tiles carry that (192x256 and
 // 128x256 were measured on AG GEMMs with K = 4096, N = 1536 over T = 4096 ... 8192; the
 // 128x128 kernel runs two workgroups per CU that share its MFMA pipes).
-int choose_tile(const GemmArgs& g, const GemmUnits& u) {
-  // Override for tuning and for tests that cover every tile shape; read on every call so
-  // that a process can switch it.
-  if (const char* s = std::getenv("UBX_GEMM_TILE")) {
-    if (!std::strcmp(s, "128x128")) return (int)kTile128x128;
-    if (!std::strcmp(s, "256x128")) return (int)kTile256x128;
-    if (!std::strcmp(s, "256x256")) return (int)kTile256x256;
-    if (!std::strcmp(s, "192x256")) return (int)kTile192x256;
-    if (!std::strcmp(s, "128x256")) return (int)kTile128x256;
-  }
-  struct Opt { int kind, bm, bn, per_cu; double eff; };
-  static const Opt opts[] = {{kTile256x256, 256, 256, 1, 1.00},
+//
+// A launch whose last round would hold only a few tiles (say 260 tiles of 256 x 256 on
+// 256 CUs: the last 4 run alone, as long as all the others) is cut in two launches on the
+// same stream: the leading row bands that fill whole rounds with the large tile, then the
+// remaining rows with the tile that finishes them soonest.  Rows are cut at a band
+// boundary, so every row is still computed once, by one instruction sequence: the results
+// do not change.  Measured on the GQA shape (hidden 8192, 1280 columns, device-side loop)
+// over T = 13216 ... 32520, the cut gains 7-22% while the second launch fills at most
+// about 60% of its slots and nothing or a little beyond; so it is taken only then, and
+// only for a launch that has the chip to itself (with several streams the other streams'
+// launches fill the idle CUs, and a cut costs 10% on fc1's host loop).
+struct TileOpt { int kind, bm, bn, per_cu; double eff; };
+const TileOpt kTileOpts[] = {{kTile256x256, 256, 256, 1, 1.00},
                              {kTile192x256, 192, 256, 1, 0.72},
                              {kTile128x256, 128, 256, 1, 0.62},
                              {kTile256x128, 256, 128, 1, 0.71},
                              {kTile128x128, 128, 128, 2, 0.75}};
-  const int share = 256 / (g.concurrency > 1 ? g.concurrency : 1);
-  int best = kTile128x128;
+
+struct TilePlan {
+  int kind;           // tile of the (first) launch
+  int64_t cut = -1;   // >= 0: rows from `cut` on go to a second launch
+  int tail_kind = 0;  // tile of the second launch
+};
+
+// Rows [lo, hi) of the units, in the same order (empty pieces dropped).
+GemmUnits clip_units(const GemmUnits& u, int64_t lo, int64_t hi) {
+  GemmUnits out;
+  out.n = 0;
+  for (int i = 0; i < u.n; ++i) {
+    const int64_t r0 = std::max<int64_t>(u.row0[i], lo);
+    const int64_t r1 = std::min<int64_t>((int64_t)u.row0[i] + u.rows[i], hi);
+    if (r1 <= r0) continue;
+    out.row0[out.n] = (int32_t)r0;
+    out.rows[out.n] = (int32_t)(r1 - r0);
+    ++out.n;
+  }
+  return out;
+}
+
+double tile_cost(const TileOpt& o, int64_t row_tiles_, const GemmArgs& g, int share) {
+  const int64_t tiles = row_tiles_ * ((g.n + o.bn - 1) / o.bn) * g.batch;
+  const int64_t slots = (int64_t)(share > 0 ? share : 1) * o.per_cu;
+  const double rounds = (double)((tiles + slots - 1) / slots);
+  return rounds * o.bm * o.bn / (o.eff / o.per_cu);
+}
+
+// The cheapest single tile over the units; its cost in *cost.
+const TileOpt& best_single(const GemmArgs& g, const GemmUnits& u, int share, double* cost) {
+  const TileOpt* best = &kTileOpts[4];
   double best_cost = 1e300;
-  for (const Opt& o : opts) {
-    const int64_t rows = row_tiles(u, o.bm);
-    const int64_t tiles = rows * ((g.n + o.bn - 1) / o.bn) * g.batch;
-    const int64_t slots = (int64_t)(share > 0 ? share : 1) * o.per_cu;
-    const double rounds = (double)((tiles + slots - 1) / slots);
-    const double cost = rounds * o.bm * o.bn / (o.eff / o.per_cu);
-    if (cost < best_cost) {
-      best_cost = cost;
-      best = o.kind;
+  for (const TileOpt& o : kTileOpts) {
+    const double c = tile_cost(o, row_tiles(u, o.bm), g, share);
+    if (c < best_cost) {
+      best_cost = c;
+      best = &o;
     }
   }
-  return best;
+  *cost = best_cost;
+  return *best;
+}
+
+TilePlan choose_plan(const GemmArgs& g, const GemmUnits& u) {
+  // Override for tuning and for tests that cover every tile shape (one launch, no cut);
+  // read on every call so that a process can switch it.
+  if (const char* s = std::getenv("UBX_GEMM_TILE")) {
+    if (!std::strcmp(s, "128x128")) return {kTile128x128};
+    if (!std::strcmp(s, "256x128")) return {kTile256x128};
+    if (!std::strcmp(s, "256x256")) return {kTile256x256};
+    if (!std::strcmp(s, "192x256")) return {kTile192x256};
+    if (!std::strcmp(s, "128x256")) return {kTile128x256};
+  }
+  const int share = 256 / (g.concurrency > 1 ? g.concurrency : 1);
+  double best_cost;
+  const TileOpt& one = best_single(g, u, share, &best_cost);
+  TilePlan plan{one.kind};
+  int64_t lo = 0, hi = 0;
+  if (g.concurrency > 1 || !contiguous_rows(u, &lo, &hi)) return plan;
+  // cuts: for each large tile, the row bands that fill its whole rounds
+  for (const TileOpt& o : kTileOpts) {
+    if (o.per_cu != 1) continue;
+    const int64_t bands = (hi - lo + o.bm - 1) / o.bm;
+    const int64_t band_tiles = (int64_t)((g.n + o.bn - 1) / o.bn) * g.batch;
+    const int64_t slots = share > 0 ? share : 1;
+    const int64_t full = bands * band_tiles / slots;          // whole rounds
+    const int64_t b1 = full * slots / band_tiles;             // bands inside them
+    if (b1 <= 0 || b1 >= bands) continue;
+    const int64_t cut = lo + b1 * o.bm;
+    const GemmUnits tail = clip_units(u, cut, hi);
+    double tail_cost;
+    const TileOpt& t = best_single(g, tail, share, &tail_cost);
+    const int64_t tail_tiles = row_tiles(tail, t.bm) * ((g.n + t.bn - 1) / t.bn) * g.batch;
+    if (tail_tiles * 10 > (int64_t)share * t.per_cu * 6) continue;  // at most ~60% of the slots
+    const double c = tile_cost(o, b1, g, share) + tail_cost;
+    if (c < best_cost * 0.97) {  // a second launch costs a little: cut only for a clear gain
+      best_cost = c;
+      plan = {o.kind, cut, t.kind};
+    }
+  }
+  return plan;
+}
+
+hipError_t launch_kind(int kind, const GemmArgs& g, const GemmUnits& u, hipStream_t stream) {
+  if (u.n <= 0) return hipSuccess;
+  switch (kind) {
+    case kTile256x256:
+      return launch<PP256x256>(&gemm_bf16_pingpong<PP256x256, PP_D>, g, u, stream);
+    case kTile192x256:
+      return launch<PP192x256>(&gemm_bf16_pingpong<PP192x256, PP_D>, g, u, stream);
+    case kTile128x256:
+      return launch<PP128x256>(&gemm_bf16_pingpong<PP128x256, PP_D>, g, u, stream);
+    case kTile256x128:
+      return launch<PP256x128>(&gemm_bf16_pingpong<PP256x128, PP_D>, g, u, stream);
+    default:
+      return launch<PL128x128>(&gemm_bf16_pipelined<PL128x128>, g, u, stream);
+  }
 }
 
 }  // namespace
@@ -734,18 +819,22 @@ hipError_t launch_gemm_bf16_units(const GemmArgs& g, const GemmUnits& u, hipStre
         return hipErrorInvalidValue;
     }
   }
-  switch (choose_tile(g, u)) {
-    case kTile256x256:
-      return launch<PP256x256>(&gemm_bf16_pingpong<PP256x256, PP_D>, g, u, stream);
-    case kTile192x256:
-      return launch<PP192x256>(&gemm_bf16_pingpong<PP192x256, PP_D>, g, u, stream);
-    case kTile128x256:
-      return launch<PP128x256>(&gemm_bf16_pingpong<PP128x256, PP_D>, g, u, stream);
-    case kTile256x128:
-      return launch<PP256x128>(&gemm_bf16_pingpong<PP256x128, PP_D>, g, u, stream);
-    default:
-      return launch<PL128x128>(&gemm_bf16_pipelined<PL128x128>, g, u, stream);
+  const TilePlan plan = choose_plan(g, u);
+  if (const char* path = std::getenv("UBX_GEMM_LOG")) {  // tile plans, for tests and tuning
+    if (FILE* f = std::fopen(path, "a")) {
+      std::fprintf(f, "kind=%d cut=%lld tail_kind=%d n=%d k=%d batch=%d units=%d\n", plan.kind,
+                   (long long)plan.cut, plan.tail_kind, g.n, g.k, g.batch, u.n);
+      std::fclose(f);
+    }
   }
+  if (plan.cut < 0) return launch_kind(plan.kind, g, u, stream);
+  // two launches on one stream: the leading whole-round bands, then the rest (the fused
+  // reduction's counters are back at zero when the second starts)
+  int64_t lo = 0, hi = 0;
+  contiguous_rows(u, &lo, &hi);
+  hipError_t e = launch_kind(plan.kind, g, clip_units(u, lo, plan.cut), stream);
+  if (e != hipSuccess) return e;
+  return launch_kind(plan.tail_kind, g, clip_units(u, plan.cut, hi), stream);
 }
 
 int64_t fuse_counter_bound(const int64_t* rows, int n_units, int64_t n) {

@@ -103,6 +103,8 @@ hipError_t launch_gemm_bf16_units(const GemmArgs& g, const GemmUnits& u, hipStre
 GemmUnits tile_aligned_units(const GemmUnits& u, int bm);
 // Row tiles of bm rows that a launch over `u` runs (after tile_aligned_units).
 int64_t row_tiles(const GemmUnits& u, int bm);
+// Whether the units tile one contiguous row range [*lo, *hi) without gaps or overlaps.
+bool contiguous_rows(const GemmUnits& u, int64_t* lo, int64_t* hi);
 
 // FP8 (E4M3) GEMM: C [*, n] bf16 = bf16(scale * A B^T) with A [*, k] and B [n, k] E4M3
 // codes (row strides in bytes), units of rows as for launch_gemm_bf16_units.  batch > 1

@@ -102,6 +102,8 @@ bool contiguous(const GemmUnits& u, int64_t* lo, int64_t* hi) {
 
 }  // namespace
 
+bool contiguous_rows(const GemmUnits& u, int64_t* lo, int64_t* hi) { return contiguous(u, lo, hi); }
+
 GemmUnits tile_aligned_units(const GemmUnits& u, int bm) {
   int64_t lo = 0, hi = 0;
   if (u.n <= 1 || bm <= 0 || !contiguous(u, &lo, &hi)) return u;
