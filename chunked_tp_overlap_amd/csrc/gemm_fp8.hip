@@ -239,11 +239,12 @@ void gemm_fp8_pingpong(F8Params p) {
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j],
                                                                     0, 0, 0, 127, 0, 127);
     __builtin_amdgcn_sched_barrier(0);
-    if (group == 0) {
-      __asm__ volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((D - 1) * C::L) : "memory");
-    } else {
-      __asm__ volatile("s_barrier" ::: "memory");
-    }
+    // Both groups take the same wait and barrier here: group 1 has issued no loads since
+    // its own wait at the end of its memory cluster, so the wait costs it nothing.  With
+    // this one unconditional statement the MFMAs stay in front of the barrier: behind a
+    // branch on the group, the compiler sank them past it, so that both groups computed
+    // at the same time and the clusters no longer alternated.
+    __asm__ volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((D - 1) * C::L) : "memory");
     __builtin_amdgcn_sched_barrier(0);
   }
   if (group == 0) __asm__ volatile("s_barrier" ::: "memory");  // matches group 1's b1
