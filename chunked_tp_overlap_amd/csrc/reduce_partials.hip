@@ -18,12 +18,15 @@
 // with q = (row0 + r) / shard_rows the shard of row r.
 //
 // HBM-bound: every element is read tp times and written once (2 (tp + 1) bytes per output
-// element).  Each lane handles V = 4 16-byte vectors (8 elements each) of one workgroup's
+// element).  Each lane handles V 16-byte vectors (8 elements each) of one workgroup's
 // chunk of V * 256 consecutive vectors, and walks the slots in ascending order: V loads of
 // slot s, add them into the V fp32 accumulators, then slot s + 1.  Many short chunks with
 // this slot-major order stream faster on MI355X than long per-workgroup ranges or a
 // grid-stride walk with every slot's loads in flight (measured on 8 slots of
-// [16384, 4096]: about 6.1 TB/s against 5.1 - 5.7).  The partials are read exactly once,
+// [16384, 4096]: about 6.1 TB/s against 5.1 - 5.7).  V = 4, except for small sums (at most
+// 2^21 vectors), where V = 2 gives twice the workgroups: measured with the MALL flushed,
+// 8 slots of [2048, 4096] at 5.6 TB/s against 5.1 - 5.2 with V = 4, while V = 2 loses
+// 6% at [16384, 4096] and V = 8 loses everywhere.  The partials are read exactly once,
 // so loads and stores are non-temporal.  When the partial rows and the output rows are
 // both packed (leading dimension == cols) the vectors are one flat run; otherwise each
 // vector's row is recovered by division.
@@ -63,7 +66,6 @@ __device__ inline u32x4 pack8(const float (&acc)[8]) {
   return o;
 }
 
-constexpr int V = 4;  // vectors per lane
 
 // fp32 -> nearest bf16 (ties to even), returned as the fp32 of the same value.
 __device__ inline float round_bf16(float x) {
@@ -79,6 +81,7 @@ __device__ inline void hop8(float (&acc)[8], u32x4 x, bool first) {
 }
 
 // acc[j] += the V vectors of one slot (loads first, then the adds).
+template <int V>
 __device__ inline void add_slot(float (&acc)[V][8], const bool (&ok)[V], const int64_t (&ein)[V],
                                 const uint16_t* slot) {
   u32x4 x[V];
@@ -91,7 +94,7 @@ __device__ inline void add_slot(float (&acc)[V][8], const bool (&ok)[V], const i
 }
 
 // Ring hop i for the V vectors: slot (first[j] + i) mod nslots of each vector j.
-template <int NS>
+template <int NS, int V>
 __device__ inline void hop_slot(float (&acc)[V][8], const bool (&ok)[V], const int64_t (&ein)[V],
                                 const int (&first)[V], int i, const ReduceArgs& r) {
   u32x4 x[V];
@@ -109,7 +112,7 @@ __device__ inline void hop_slot(float (&acc)[V][8], const bool (&ok)[V], const i
 // Workgroup b reduces vectors [b * V * THREADS, (b + 1) * V * THREADS) clipped to nvec; lane t
 // takes vectors t, t + THREADS, ...  PACKED: vector v is at element 8 v of every slot and
 // of out; otherwise at row v / vpr, column 8 (v % vpr).  NS = 0: nslots at run time.
-template <int NS, bool PACKED, bool RING>
+template <int NS, bool PACKED, bool RING, int V>
 __global__ __launch_bounds__(THREADS) void reduce_chunks(ReduceArgs r, int64_t nvec, int64_t vpr) {
   const int64_t base = (int64_t)blockIdx.x * (V * THREADS) + threadIdx.x;
   int64_t ein[V], eout[V];
@@ -141,41 +144,49 @@ __global__ __launch_bounds__(THREADS) void reduce_chunks(ReduceArgs r, int64_t n
   if constexpr (RING) {
     if constexpr (NS > 0) {
 #pragma unroll
-      for (int i = 0; i < NS; ++i) hop_slot<NS>(acc, ok, ein, first, i, r);
+      for (int i = 0; i < NS; ++i) hop_slot<NS, V>(acc, ok, ein, first, i, r);
     } else {
-      for (int i = 0; i < r.nslots; ++i) hop_slot<NS>(acc, ok, ein, first, i, r);
+      for (int i = 0; i < r.nslots; ++i) hop_slot<NS, V>(acc, ok, ein, first, i, r);
     }
   } else if constexpr (NS > 0) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) add_slot(acc, ok, ein, r.parts + s * r.slot_stride);
+    for (int s = 0; s < NS; ++s) add_slot<V>(acc, ok, ein, r.parts + s * r.slot_stride);
   } else {
-    for (int s = 0; s < r.nslots; ++s) add_slot(acc, ok, ein, r.parts + s * r.slot_stride);
+    for (int s = 0; s < r.nslots; ++s) add_slot<V>(acc, ok, ein, r.parts + s * r.slot_stride);
   }
 #pragma unroll
   for (int j = 0; j < V; ++j)
     if (ok[j]) __builtin_nontemporal_store(pack8(acc[j]), GLOBAL_PTR(u32x4, r.out + eout[j]));
 }
 
-template <int NS>
-hipError_t launch_ns(const ReduceArgs& r, hipStream_t stream) {
-  const int64_t vpr = r.cols / 8;
-  const int64_t nvec = r.rows * vpr;
+template <int NS, int V>
+hipError_t launch_nsv(const ReduceArgs& r, int64_t nvec, int64_t vpr, hipStream_t stream) {
   const int64_t blocks = (nvec + V * THREADS - 1) / (V * THREADS);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const bool packed = r.ldp == r.cols && r.ldo == r.cols;
   const dim3 grid((unsigned)blocks), block(THREADS);
   if (r.ring) {
     if (packed)
-      hipLaunchKernelGGL((reduce_chunks<NS, true, true>), grid, block, 0, stream, r, nvec, vpr);
+      hipLaunchKernelGGL((reduce_chunks<NS, true, true, V>), grid, block, 0, stream, r, nvec, vpr);
     else
-      hipLaunchKernelGGL((reduce_chunks<NS, false, true>), grid, block, 0, stream, r, nvec, vpr);
+      hipLaunchKernelGGL((reduce_chunks<NS, false, true, V>), grid, block, 0, stream, r, nvec, vpr);
   } else {
     if (packed)
-      hipLaunchKernelGGL((reduce_chunks<NS, true, false>), grid, block, 0, stream, r, nvec, vpr);
+      hipLaunchKernelGGL((reduce_chunks<NS, true, false, V>), grid, block, 0, stream, r, nvec, vpr);
     else
-      hipLaunchKernelGGL((reduce_chunks<NS, false, false>), grid, block, 0, stream, r, nvec, vpr);
+      hipLaunchKernelGGL((reduce_chunks<NS, false, false, V>), grid, block, 0, stream, r, nvec, vpr);
   }
   return hipGetLastError();
+}
+
+constexpr int64_t kSmallSumVectors = int64_t(1) << 21;
+
+template <int NS>
+hipError_t launch_ns(const ReduceArgs& r, hipStream_t stream) {
+  const int64_t vpr = r.cols / 8;
+  const int64_t nvec = r.rows * vpr;
+  return nvec <= kSmallSumVectors ? launch_nsv<NS, 2>(r, nvec, vpr, stream)
+                                  : launch_nsv<NS, 4>(r, nvec, vpr, stream);
 }
 
 }  // namespace
