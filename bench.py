@@ -146,7 +146,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU's share of the work on a single MI355X; "
-              f"--gpus {args.gpus} (WORLD_SIZE={world}) is not supported: this build has no "
+              f"--gpus {args.gpus} (WORLD_SIZE={world}) is not supported: the library has no "
               "multi-GPU path.", file=sys.stderr, flush=True)
         sys.exit(2)
 

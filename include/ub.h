@@ -87,8 +87,8 @@ typedef enum {
   UB_ERR_CAPACITY = 4,          /* active T exceeds the registered capacity   [TE#3564] */
   UB_ERR_HIDDEN_MISMATCH = 5,   /* active hidden differs from the registered  [TE#3564] */
   UB_ERR_TP_DIVISIBILITY = 6,   /* T (or capacity) not divisible by tp_size   [TE#3564] */
-  UB_ERR_DTYPE = 7,             /* not bf16: quantized buffers are out of scope [TE#3564] */
-  UB_ERR_UNSUPPORTED = 8,       /* a valid request this build does not implement */
+  UB_ERR_DTYPE = 7,             /* not bf16 or fp8 E4M3, or the wrong one for the call */
+  UB_ERR_UNSUPPORTED = 8,       /* a valid request the library does not implement */
   UB_ERR_BUFFER_TOO_SMALL = 9,  /* a registered byte size is below what the shape needs */
   UB_ERR_NOT_INITIALIZED = 10,  /* null handle, or a reduce-scatter call without workspace */
   UB_ERR_HIP = 11               /* a HIP runtime call failed; see ub_last_error */
