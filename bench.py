@@ -775,9 +775,13 @@ def cpu_baseline(q, min_seconds):
     w_cols = np.linalg.norm(ob.decode(q.w_host), axis=0)
     parity = {"microbatches": 0, "elements": 0, "bit_equal": 0, "max_err_over_gate": 0.0}
 
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = sum(i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas")
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = sum(i.get("num_threads", 0) for i in libs)
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
+                         for i in libs) or "none found"
     except Exception:  # threadpoolctl missing: report the core count
         threads = os.cpu_count()
     w = q.w
@@ -814,7 +818,7 @@ def cpu_baseline(q, min_seconds):
             "kind": "oracle",
             "sample": f"{done} qkv microbatches ({done / len(q.Ts):.2f} passes over the 32 of one "
                       f"step), numpy fp64 chunked GEMM + bf16 RNE, {elapsed:.1f} s",
-            "host_cpus": os.cpu_count(),
+            "host_cpus": os.cpu_count(), "blas": blas,
             "parity": {"microbatches": parity["microbatches"], "elements": parity["elements"],
                        "bit_equal_fraction": round(parity["bit_equal"] / max(1, parity["elements"]), 5),
                        "max_err_over_gate": round(parity["max_err_over_gate"], 5),
