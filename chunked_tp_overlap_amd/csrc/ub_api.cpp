@@ -1229,6 +1229,10 @@ UB_API ub_status_t ub_destroy(ub_handle_t h) {
       if (ev) (void)hipEventDestroy(ev);
     for (hipEvent_t ev : h->free_events) (void)hipEventDestroy(ev);
     if (h->fuse_counters) (void)hipFree(h->fuse_counters);
+    if (h->ready) {  // the next handle to take this slot starts with no counted timeouts
+      const uint32_t zero = 0;
+      (void)hipMemcpy(h->ready + ubx::kReadyTimeoutWord, &zero, sizeof(zero), hipMemcpyHostToDevice);
+    }
     if (cur >= 0 && cur != h->device) (void)hipSetDevice(cur);
   }
   release_ready_slot(h);

@@ -323,7 +323,8 @@ UB_API ub_status_t ub_gemm_ag_chunked_fp8(ub_handle_t h, const void* w, int64_t 
  *   atomic_gemm = 1: the device-side chunk loop ([TE#1344] "atomic_gemm") gated by a
  *     ready flag per chunk.  After each chunk's copy, the copy stream writes the call's
  *     epoch to the chunk's flag (hipStreamWriteValue32; the local chunk's flag first).
- *     The one GEMM launch's tiles wait for the flags of the chunks whose rows they read,
+ *     The GEMM's tiles (one launch, or two when a ragged last round is cut off) wait for
+ *     the flags of the chunks whose rows they read,
  *     acquire at system scope, then load.  The copy stream's work is all issued before
  *     the GEMM, so streams that share a hardware queue serialise rather than wait on each
  *     other.
@@ -350,8 +351,9 @@ UB_API ub_status_t ub_gemm_ag_arrival(ub_handle_t h, const void* src, int32_t sr
                                       ub_stream_t stream);
 
 /* Number of tile waits in the device-side chunk loop of ub_gemm_ag_arrival that hit the
- * time bound on this handle's flag slot since the slot was first used in this process (0
- * if the handle never gated on arrivals).  A nonzero count means a chunk's flag never
+ * time bound on this handle's flag slot since the handle took the slot (0 if the handle
+ * never gated on arrivals; ub_destroy clears the count, so a slot handed to a later handle
+ * starts from zero).  A nonzero count means a chunk's flag never
  * came, and the results of that call are not to be trusted.  Synchronous (copies one word
  * from the device). */
 UB_API ub_status_t ub_arrival_timeouts(ub_handle_t h, uint32_t* count);

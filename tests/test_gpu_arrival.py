@@ -258,5 +258,46 @@ def test_arrival_device_loop_wait_bound(ub, monkeypatch):
         print("[arrival wait bound] normal call", flush=True)
         _case(ub, reg, a, w_t, N, dict(method="ring_exchange", rank=rank, atomic_gemm=True), ref, T, tp)
         assert ub.ub_arrival_timeouts(reg.h) == after
+        # destroying the handle clears its slot's count: a new handle (which takes the
+        # lowest free slot, the one just released) starts from zero
+        reg.close()
+        reg = gu.Registration(ub, cap, H, tp, workspace=False, pad_rows=8)
+        reg.set_T(T)
+        print("[arrival wait bound] next handle", flush=True)
+        _case(ub, reg, a, w_t, N, dict(method="ring_exchange", rank=rank, atomic_gemm=True), ref, T, tp)
+        assert ub.ub_arrival_timeouts(reg.h) == 0
+    finally:
+        reg.close()
+
+
+def test_arrival_device_loop_with_cut(ub, tmp_path, monkeypatch):
+    """The device-side loop gated on arrivals when its tile plan is cut in two launches
+    (13216 rows x 1280 columns: 260 tiles of 256 x 256, the last 160 rows as 128 x 128
+    tiles): both launches wait on the flags of the chunks they read, no wait runs into its
+    bound, and the output equals the ungated GEMM over the complete buffer bit for bit.
+    The handle's timeout count starts at zero even when its flag slot was used (and timed
+    out on purpose) by a handle destroyed before it."""
+    rng = np.random.default_rng(57)
+    cap, H, N, T, tp = 13312, 256, 1280, 13216, 8
+    a = wl.normal_bits(rng, (T, H))
+    w_t = gu.dev(wl.normal_bits(rng, (H, N), 0.02))
+    reg = gu.Registration(ub, cap, H, tp, workspace=False, pad_rows=8)
+    log = str(tmp_path / "plans.txt")
+    try:
+        reg.set_T(T)
+        reg.fill(a)
+        c = gu.canary((T, N))
+        ub.ub_gemm_ag_chunked(reg.h, w_t, N, N, c, N, ub.make_cfg("bulk", 1, 1))
+        torch.cuda.synchronize()
+        ref = gu.host(c)
+        monkeypatch.setenv("UBX_GEMM_LOG", log)
+        for rank, host_src in ((0, False), (5, False), (3, True)):
+            print(f"[arrival cut] rank={rank} host_src={host_src}", flush=True)
+            _case(ub, reg, a, w_t, N, dict(method="ring_exchange", rank=rank, atomic_gemm=True,
+                                          use_ce=True), ref, T, tp, host_src=host_src)
+        with open(log) as f:
+            cuts = [int(dict(kv.split("=") for kv in line.split())["cut"]) for line in f if line.strip()]
+        assert cuts == [51 * 256] * 3, cuts
+        assert ub.ub_arrival_timeouts(reg.h) == 0
     finally:
         reg.close()
