@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -306,7 +307,42 @@ def main():
         result["cpu_baseline"] = cpu_baseline(q, args.cpu_seconds)
 
     ub.ub_destroy(q.h)
+    busy = int(round(util["busy_cus_mean"])) if util and util.get("busy_cus_mean") else 142
+    ceiling = mfma_ceiling(busy, props.multi_processor_count)
+    if ceiling:
+        burst = ceiling.get("bursts_tflops_at_busy_cus")
+        if burst:
+            ceiling["achieved_over_bursts_ceiling"] = round(g_ach / burst, 4)
+        roofline["mfma_ceiling"] = ceiling
     print(json.dumps(result), flush=True)
+
+
+def mfma_ceiling(busy_cus, all_cus):
+    """The matrix cores' own ceiling under the power limit, from the calibration program
+    ``lib/mfma_ceiling`` (the GEMM's MFMA sequence on register operands, no memory work),
+    run as a child process: 32 launches of ~80 us back to back (the qkv step's launch
+    pattern) and one sustained launch, on `busy_cus` CUs and on all of them, with the clock
+    each ran at.  None if the program is missing or fails."""
+    exe = os.path.join(ROOT, "chunked_tp_overlap_amd", "lib", "mfma_ceiling")
+    if not os.path.exists(exe):
+        log("mfma_ceiling program not built; skipping the ceiling")
+        return None
+    cus = sorted({max(1, min(busy_cus, all_cus)), all_cus})
+    cmd = [exe, "0.5", *[str(c) for c in cus]]
+    try:
+        res = subprocess.run(cmd, capture_output=True, text=True, timeout=120)
+    except subprocess.TimeoutExpired:
+        log("mfma_ceiling timed out")
+        return None
+    if res.returncode != 0:
+        log(f"mfma_ceiling failed ({res.returncode}): {res.stderr.strip()[-300:]}")
+        return None
+    rows = [json.loads(ln) for ln in res.stdout.splitlines() if ln.startswith("{")]
+    burst = [r["bursts_32x80us"]["tflops"] for r in rows
+             if r["cus"] == cus[0] and r["waves_per_simd"] == 2]
+    return {"program": "chunked_tp_overlap_amd/lib/mfma_ceiling " + " ".join(cmd[1:]),
+            "busy_cus": cus[0], "bursts_tflops_at_busy_cus": burst[0] if burst else None,
+            "rows": rows}
 
 
 def device_state(torch):

@@ -153,3 +153,30 @@ def test_timeline_summary_on_synthetic_trace(tmp_path):
     md = out.read_text()
     assert "| a | 2 | 250.0 | 200.0 | 200.0 | 150.0 | 400.0 |" in md
     assert "| b | 2 | 180.0 | 100.0 | 80.0 | 0.0 | 180.0 |" in md
+
+
+CEILING = os.path.join(ROOT, "chunked_tp_overlap_amd", "lib", "mfma_ceiling")
+
+
+@pytest.mark.skipif(not os.path.exists(CEILING), reason="calibration program not built")
+@pytest.mark.parametrize("args", [["0"], ["11"], ["abc"], ["0.5", "0"], ["0.5", "100000"]])
+def test_mfma_ceiling_rejects_bad_arguments(args):
+    """The calibration program checks its arguments before it touches a GPU: a run length
+    outside (0, 10] s or a busy-CU count outside [1, CUs] exits with status 2."""
+    r = subprocess.run([CEILING, *args], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2 or (args[0] == "0.5" and r.returncode != 0), (args, r.returncode)
+    assert r.stdout.strip() == ""
+
+
+def test_bench_ceiling_fails_softly(monkeypatch, tmp_path):
+    """bench.mfma_ceiling returns None (and the bench line carries no ceiling) when the
+    program is missing or exits with an error; here it has no GPU to run on."""
+    sys.path.insert(0, ROOT)
+    try:
+        import bench
+    finally:
+        sys.path.remove(ROOT)
+    if os.path.exists(CEILING):
+        assert bench.mfma_ceiling(142, 256) is None  # no GPU in this container
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.mfma_ceiling(142, 256) is None  # not built under this root
