@@ -180,3 +180,15 @@ def test_bench_ceiling_fails_softly(monkeypatch, tmp_path):
         assert bench.mfma_ceiling(142, 256) is None  # no GPU in this container
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.mfma_ceiling(142, 256) is None  # not built under this root
+
+
+HBM = os.path.join(ROOT, "chunked_tp_overlap_amd", "lib", "hbm_ceiling")
+
+
+@pytest.mark.skipif(not os.path.exists(HBM), reason="calibration program not built")
+@pytest.mark.parametrize("args", [["0"], ["7"], ["32769"], ["2048", "abc"]])
+def test_hbm_ceiling_rejects_bad_arguments(args):
+    """Row counts outside [8, 32768] exit with status 2 before any GPU call."""
+    r = subprocess.run([HBM, *args], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2, (args, r.returncode, r.stderr)
+    assert r.stdout.strip() == ""
