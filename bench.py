@@ -313,13 +313,19 @@ def main():
         burst = ceiling.get("bursts_tflops_at_busy_cus")
         if burst:
             ceiling["achieved_over_bursts_ceiling"] = round(g_ach / burst, 4)
+        fp8 = (result.get("secondary") or {}).get("qkv_fp8")
+        burst8 = ceiling.get("fp8_bursts_tflops_at_busy_cus")
+        if fp8 and burst8:
+            # the FP8 qkv step's rate (launch gaps included) over the FP8 MFMAs' own ceiling
+            ceiling["fp8_step_over_fp8_bursts_ceiling"] = round(fp8["tflops"] / burst8, 4)
         roofline["mfma_ceiling"] = ceiling
     print(json.dumps(result), flush=True)
 
 
 def mfma_ceiling(busy_cus, all_cus):
     """The matrix cores' own ceiling under the power limit, from the calibration program
-    ``lib/mfma_ceiling`` (the GEMM's MFMA sequence on register operands, no memory work),
+    ``lib/mfma_ceiling`` (the bf16 and FP8 GEMMs' MFMA sequences on register operands, no
+    memory work),
     run as a child process: 32 launches of ~80 us back to back (the qkv step's launch
     pattern) and one sustained launch, on `busy_cus` CUs and on all of them, with the clock
     each ran at.  None if the program is missing or fails."""
@@ -338,11 +344,15 @@ def mfma_ceiling(busy_cus, all_cus):
         log(f"mfma_ceiling failed ({res.returncode}): {res.stderr.strip()[-300:]}")
         return None
     rows = [json.loads(ln) for ln in res.stdout.splitlines() if ln.startswith("{")]
-    burst = [r["bursts_32x80us"]["tflops"] for r in rows
-             if r["cus"] == cus[0] and r["waves_per_simd"] == 2]
+
+    def burst(kind):
+        b = [r["bursts_32x80us"]["tflops"] for r in rows
+             if r.get("kind") == kind and r["cus"] == cus[0] and r["waves_per_simd"] == 2]
+        return b[0] if b else None
+
     return {"program": "chunked_tp_overlap_amd/lib/mfma_ceiling " + " ".join(cmd[1:]),
-            "busy_cus": cus[0], "bursts_tflops_at_busy_cus": burst[0] if burst else None,
-            "rows": rows}
+            "busy_cus": cus[0], "bursts_tflops_at_busy_cus": burst("bf16"),
+            "fp8_bursts_tflops_at_busy_cus": burst("fp8"), "rows": rows}
 
 
 def device_state(torch):
