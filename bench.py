@@ -179,6 +179,13 @@ def main():
         return
     q = Qkv(ub, wl, torch, np, dev)
     primary = q.cfg(atomic=True)
+    # One host-loop call first, so that the handle's worker streams exist before the
+    # benchmark's graph captures start using torch's stream pool.  HIP places each stream
+    # on one of GPU_MAX_HW_QUEUES hardware queues, and streams that share a queue run in
+    # issue order.  When the worker streams were first created inside the capture code, the
+    # eager host loop measured ~320 TFLOP/s instead of ~440, with the same kernels.
+    q.step(q.cfg(atomic=False))
+    torch.cuda.synchronize()
 
     log(f"warmup {args.warmup}, timed {args.steps} steps of {len(q.Ts)} microbatches (atomic_gemm)")
     sec = q.timed(primary, args.steps, args.warmup)

@@ -122,7 +122,14 @@ typedef enum { UB_OP_AG = 0, UB_OP_RS = 1 } ub_op_t;
  *   num_splits       chunks the GEMM is cut into (>= 1); ignored for ring exchange,
  *                    which uses tp_size chunks.
  *   num_max_streams  compute streams = min(chunks, num_max_streams, UB_MAX_STREAMS), >= 1.
- *                    Default 3.
+ *                    Default 3.  The handle creates its worker streams on first use.
+ *                    They overlap with the caller's stream only on hardware queues of
+ *                    their own: HIP places streams on GPU_MAX_HW_QUEUES queues, and
+ *                    streams that share one run in issue order.  Measured on qkv with 3
+ *                    streams: 440 TFLOP/s when the handle's first call came before the
+ *                    process's other streams were in use, ~320 when it came after.
+ *                    Make a first call early, and raise GPU_MAX_HW_QUEUES in processes
+ *                    with many streams.
  *   aggregate        all-gather side only: chunks {2u, 2u+1} are merged into one launch.
  *   atomic_gemm      0: one kernel launch per unit from a host loop on the compute
  *                    streams; 1: one kernel on the caller's stream whose workgroups walk
