@@ -6,7 +6,11 @@
 //   bf16: the 16 v_mfma_f32_32x32x16_bf16 of one 32-deep k-step of a 128 x 64 wave tile
 //         (4 x 2 blocks of 32 x 32, two 16-deep sub-steps), as the bf16 GEMM;
 //   fp8:  the 8 v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, unit scales) of one 64-deep
-//         k-step of the same wave tile, as the FP8 GEMM.  One workgroup per CU (its LDS request leaves room for no
+//         k-step of the same wave tile, as the FP8 GEMM;
+//   bf16_16x16x32: the 32 v_mfma_f32_16x16x32_bf16 (8 x 4 blocks of 16 x 16) that cover the
+//         same bf16 step with the smaller instruction, for comparison.
+// Every variant is compiled for at most 256 registers per lane (two waves per SIMD), so one
+// and two waves per SIMD run the same code.  One workgroup per CU (its LDS request leaves room for no
 // second), 4 or 8 waves (one or two per SIMD, as the GEMM's four-wave and ping-pong
 // kernels), on a chosen number of CUs.  What this sustains is the most any GEMM built on
 // this instruction can reach with that many CUs busy, whatever its memory side does.
@@ -31,12 +35,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int FM = 4, FN = 2, SUBS = 2;          // the GEMM's 128 x 64 wave tile, BK = 32
-enum Kind { kBf16 = 0, kFp8 = 1 };
+enum Kind { kBf16 = 0, kFp8 = 1, kBf16Small = 2 };
 // flops per wave per iteration: bf16 a 32-deep step, fp8 a 64-deep step of the wave tile
 constexpr double flop_per_iter_wave(int kind) { return 2.0 * 128 * 64 * (kind == kFp8 ? 64 : 32); }
-constexpr double PEAK[2] = {2516.6, 5033.2};     // dense TFLOP/s: bf16, fp8
+constexpr double PEAK[3] = {2516.6, 5033.2, 2516.6};  // dense TFLOP/s
+const char* const KIND_NAME[3] = {"bf16", "fp8", "bf16_16x16x32"};
 constexpr size_t LDS_FORCE_ONE_PER_CU = 96 * 1024;  // two would need 192 KiB of 160
 
 #define CHECK(x)                                                                       \
@@ -49,7 +55,7 @@ constexpr size_t LDS_FORCE_ONE_PER_CU = 96 * 1024;  // two would need 192 KiB of
   } while (0)
 
 template <int WAVES, int KIND>
-__global__ __launch_bounds__(64 * WAVES) void mfma_loop(const bf16x8* src, float* sink,
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma_loop(const bf16x8* src, float* sink,
                                                          unsigned long long* clk, int iters) {
   extern __shared__ unsigned char lds[];
   const int lane = threadIdx.x & 63;
@@ -81,12 +87,26 @@ __global__ __launch_bounds__(64 * WAVES) void mfma_loop(const bf16x8* src, float
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  f32x4 acc4[2 * FM][2 * FN];  // bf16_16x16x32: 16 x 16 blocks over the same wave tile
+#pragma unroll
+  for (int i = 0; i < 2 * FM; ++i)
+#pragma unroll
+    for (int j = 0; j < 2 * FN; ++j) acc4[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   lds[threadIdx.x] = 0;  // the LDS request only limits occupancy
   __syncthreads();
   const unsigned long long t0 = __builtin_amdgcn_s_memtime();
   const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
   for (int it = 0; it < iters; ++it) {
-    if constexpr (KIND == kFp8) {
+    if constexpr (KIND == kBf16Small) {
+      // a 16-row block takes row block i/2 and k half i%2 of the 32 x 32 operands' vectors:
+      // any 8 bf16 per lane serve, the operand values only set the data the units switch
+#pragma unroll
+      for (int i = 0; i < 2 * FM; ++i)
+#pragma unroll
+        for (int j = 0; j < 2 * FN; ++j)
+          acc4[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i & 1][i >> 1], b[j & 1][j >> 1],
+                                                               acc4[i][j], 0, 0, 0);
+    } else if constexpr (KIND == kFp8) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -106,6 +126,10 @@ __global__ __launch_bounds__(64 * WAVES) void mfma_loop(const bf16x8* src, float
   const unsigned long long t1 = __builtin_amdgcn_s_memtime();
   const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
   float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 2 * FM; ++i)
+#pragma unroll
+    for (int j = 0; j < 2 * FN; ++j) sum += acc4[i][j][0] + acc4[i][j][1] + acc4[i][j][2] + acc4[i][j][3];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -186,7 +210,9 @@ int main(int argc, char** argv) {
   for (const void* k : {reinterpret_cast<const void*>(&mfma_loop<4, kBf16>),
                         reinterpret_cast<const void*>(&mfma_loop<8, kBf16>),
                         reinterpret_cast<const void*>(&mfma_loop<4, kFp8>),
-                        reinterpret_cast<const void*>(&mfma_loop<8, kFp8>)})
+                        reinterpret_cast<const void*>(&mfma_loop<8, kFp8>),
+                        reinterpret_cast<const void*>(&mfma_loop<4, kBf16Small>),
+                        reinterpret_cast<const void*>(&mfma_loop<8, kBf16Small>)})
     CHECK(hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)LDS_FORCE_ONE_PER_CU));
 
@@ -216,7 +242,7 @@ int main(int argc, char** argv) {
   // wave per iteration, two waves -> 1024 cycles per iteration
   const double iters_per_us = 2400.0 / 1024.0;
   run<8, kBf16>(src, sink, clk, ncu, 100, 10);  // warm-up
-  for (int kind : {kBf16, kFp8}) {
+  for (int kind : {kBf16, kFp8, kBf16Small}) {
     for (int waves : {8, 4}) {
       for (int cus : busy) {
         const double per_wave = waves == 8 ? 1.0 : 2.0;  // one wave per SIMD issues half as often
@@ -227,6 +253,9 @@ int main(int argc, char** argv) {
         // the sustained run first, so that the bursts start with the clock already settled
         // (after an idle gap the clock takes milliseconds to ramp up)
         auto go = [&](int iters, int launches) {
+          if (kind == kBf16Small)
+            return waves == 8 ? run<8, kBf16Small>(src, sink, clk, cus, iters, launches)
+                              : run<4, kBf16Small>(src, sink, clk, cus, iters, launches);
           if (kind == kFp8)
             return waves == 8 ? run<8, kFp8>(src, sink, clk, cus, iters, launches)
                               : run<4, kFp8>(src, sink, clk, cus, iters, launches);
@@ -239,7 +268,7 @@ int main(int argc, char** argv) {
         std::printf("{\"kind\": \"%s\", \"peak_tflops\": %.1f, \"waves_per_simd\": %d, \"cus\": %d, "
                     "\"bursts_32x80us\": {\"tflops\": %.1f, \"pct_of_peak\": %.1f, \"clock_mhz\": %.0f, \"ms\": %.3f}, "
                     "\"sustained\": {\"tflops\": %.1f, \"pct_of_peak\": %.1f, \"clock_mhz\": %.0f, \"ms\": %.1f}}\n",
-                    kind == kFp8 ? "fp8" : "bf16", peak, waves / 4, cus, b.tflops,
+                    KIND_NAME[kind], peak, waves / 4, cus, b.tflops,
                     100.0 * b.tflops / peak, b.clock_mhz, b.seconds * 1e3, s.tflops,
                     100.0 * s.tflops / peak, s.clock_mhz, s.seconds * 1e3);
         std::fflush(stdout);
