@@ -11,8 +11,15 @@
 // selects a batch entry at the given element strides (the reduce-scatter side's K slices).
 //
 // Design (CDNA4):
-//  - A workgroup computes a BM x BN tile of C with v_mfma_f32_32x32x16_bf16 (fp32
-//    accumulators).  K advances BK = 32 per step through S stages in LDS.
+//  - A workgroup computes a BM x BN tile of C with v_mfma_f32_16x16x32_bf16 (fp32
+//    accumulators): one 32-deep instruction per 16x16 block of a wave's tile per step.
+//    K advances BK = 32 per step through S stages in LDS.  The 16x16x32 form moves fewer
+//    register bytes per flop than the 32x32x16 form, and under the part's power limit
+//    it holds a higher clock: measured +1-2% on the qkv launches, +3-5% on longer
+//    full-chip launches (fc1, the GQA sweep, 8192^3), same LDS traffic.
+//  - A fragment (16 rows x 32 k): lane l holds row l % 16, k 8 (l / 16) .. + 7.  B
+//    fragment (32 k x 16 columns): lane l holds column l % 16, the same k.  Accumulator:
+//    lane l holds column l % 16 of rows 4 (l / 16) .. + 3.
 //  - Global -> LDS moves use buffer_load_dwordx4 ... lds: 16 bytes per lane straight into
 //    LDS, no staging registers.  The buffer range check returns zeros for rows past m and
 //    for columns past n (those lanes get an offset beyond the resource's size), so ragged
@@ -159,9 +166,9 @@ struct Cfg {
   static constexpr int THREADS = 64 * NW;
   static constexpr int WM = BM / WGM;               // wave tile rows
   static constexpr int WN = BN / WGN;               // wave tile cols
-  static constexpr int FM = WM / 32;                // 32x32 blocks per wave, along m
-  static constexpr int FN = WN / 32;                // along n
-  static constexpr int SUBS = BK / 16;              // 16-wide k sub-steps per step
+  static constexpr int FM = WM / 16;                // 16x16 blocks per wave, along m
+  static constexpr int FN = WN / 16;                // along n
+  static constexpr int SUBS = BK / 32;              // 32-deep k sub-steps per step
   static constexpr int A_ROW = BK * 2;              // bytes per A row in a stage
   static constexpr int A_CPR = BK / 8;              // 16-byte chunks per A row
   static constexpr int A_BYTES = BM * A_ROW;
@@ -191,8 +198,8 @@ struct Cfg {
   static_assert(EVEN ? (NA0 >= 1 && NB0 >= 1)
                      : (NW == 8 && NA_ALL % 4 == 0 && NB_ALL % 4 == 0 && NA1 >= 1 && NB0 >= 1),
                 "direct loads do not split over the waves");
-  static_assert(FM >= 1 && FN >= 1, "wave tile below one 32x32 block");
-  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile of whole 32x32 blocks");
+  static_assert(FM >= 1 && FN >= 1 && SUBS >= 1, "wave tile below one 16x16 block");
+  static_assert(WM % 16 == 0 && WN % 16 == 0 && BK % 32 == 0, "whole 16x16x32 blocks");
   static_assert(S * L0 <= 63 && S * L1 <= 63, "vmcnt is a 6-bit count");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS is 160 KiB per CU");
 };
@@ -259,11 +266,11 @@ struct Tile {
     // Fragment reads.  A: row R = wm*WM + i*32 + (lane&31), k-chunk (kk/8 + lane/32) in slot
     // ^ a_swz(R) (a function of lane&31 only).  B: k-row kk + (lane/32)*8 + (lane>>2)&3
     // (+4 for the second read), column wn*WN + j*32 + ((lane>>4)&1)*16 + (lane&3)*4.
-    a_rd_row = (wm * C::WM + (lane & 31)) * C::A_ROW;
-    a_rd_c = lane >> 5;
-    a_rd_x = a_swz<C::A_CPR>(lane & 31);
-    b_krow = (lane >> 5) * 8 + ((lane >> 2) & 3);
-    b_col_chunk = (wn * C::WN + ((lane >> 4) & 1) * 16 + (lane & 3) * 4) >> 3;
+    a_rd_row = (wm * C::WM + (lane & 15)) * C::A_ROW;
+    a_rd_c = lane >> 4;
+    a_rd_x = a_swz<C::A_CPR>(lane & 15);
+    b_krow = (lane >> 4) * 8 + ((lane >> 2) & 3);
+    b_col_chunk = (wn * C::WN + (lane & 3) * 4) >> 3;
     b_x = b_swz((lane >> 2) & 3);
     b_in = (lane & 1) * 8;
 
@@ -301,11 +308,11 @@ struct Tile {
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
       af[i] = *LDS_PTR(const bf16x8,
-                       sa + a_rd_row + i * 32 * C::A_ROW + (((kk >> 3) + a_rd_c) ^ a_rd_x) * 16);
+                       sa + a_rd_row + i * 16 * C::A_ROW + (((kk >> 3) + a_rd_c) ^ a_rd_x) * 16);
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
       const unsigned char* q =
-          sb + (kk + b_krow) * C::B_ROW + (((b_col_chunk + j * 4) ^ b_x) * 16) + b_in;
+          sb + (kk + b_krow) * C::B_ROW + (((b_col_chunk + j * 2) ^ b_x) * 16) + b_in;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, q));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, q + 4 * C::B_ROW));
       bf[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -313,22 +320,22 @@ struct Tile {
   }
 
   // bf16 tile in LDS (the caller guarantees no wave still reads or loads into LDS), then
-  // 16-byte coalesced stores.  32x32 accumulator layout: lane holds column (lane & 31);
-  // element e holds row 8*(e/4) + 4*(lane/32) + (e%4).
+  // 16-byte coalesced stores.  16x16 accumulator layout: lane holds column (lane & 15);
+  // element e holds row 4*(lane/16) + e.
   __device__ inline void store(unsigned char* smem, const Params& p, int tid,
-                               const f32x16 (&acc)[C::FM][C::FN]) const {
+                               const f32x4 (&acc)[C::FM][C::FN]) const {
     uint16_t* ct = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
-        const int col = wn * C::WN + j * 32 + (lane & 31);
+        const int col = wn * C::WN + j * 16 + (lane & 15);
+        const int row = wm * C::WM + i * 16 + (lane >> 4) * 4;
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          const int row = wm * C::WM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+        for (int e = 0; e < 4; e += 2) {
           const uint32_t v = pack_bf16x2(acc[i][j][e], acc[i][j][e + 1]);
-          *LDS_PTR(uint16_t, ct + row * C::LDC + col) = (uint16_t)(v & 0xFFFF);
-          *LDS_PTR(uint16_t, ct + (row + 1) * C::LDC + col) = (uint16_t)(v >> 16);
+          *LDS_PTR(uint16_t, ct + (row + e) * C::LDC + col) = (uint16_t)(v & 0xFFFF);
+          *LDS_PTR(uint16_t, ct + (row + e + 1) * C::LDC + col) = (uint16_t)(v >> 16);
         }
       }
     __syncthreads();
@@ -443,12 +450,12 @@ struct Tile {
 };
 
 template <class C>
-__device__ inline void mfma_block(f32x16 (&acc)[C::FM][C::FN], const bf16x8* af, const bf16x8* bf) {
+__device__ inline void mfma_block(f32x4 (&acc)[C::FM][C::FN], const bf16x8* af, const bf16x8* bf) {
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
 }
 
 // ---- 8-wave ping-pong ------------------------------------------------------------------
@@ -475,13 +482,11 @@ void gemm_bf16_pingpong(Params p) {
   if (p.ready) wait_ready(p, t.m0, min(t.m0 + C::BM, t.m_end));
   const int group = t.group;
 
-  f32x16 acc[C::FM][C::FN];
+  f32x4 acc[C::FM][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   bf16x8 af[C::SUBS][C::FM], bf[C::SUBS][C::FN];
   const int nk = p.k / C::BK;
 
@@ -499,7 +504,7 @@ void gemm_bf16_pingpong(Params p) {
   for (int ks = 0; ks < nk; ++ks) {
     // memory cluster
 #pragma unroll
-    for (int sub = 0; sub < C::SUBS; ++sub) t.read_frags(smem, ks, sub * 16, af[sub], bf[sub]);
+    for (int sub = 0; sub < C::SUBS; ++sub) t.read_frags(smem, ks, sub * 32, af[sub], bf[sub]);
     t.issue_loads(smem, ks + D, nk);
     __builtin_amdgcn_sched_barrier(0);
     if (group == 1) {
@@ -526,7 +531,7 @@ void gemm_bf16_pingpong(Params p) {
 }
 
 // ---- 4-wave, S-stage pipeline -----------------------------------------------------------
-// One barrier per step, before its last sub-step: step ks+1 has landed (the S-2 newer
+// One barrier per step, before its last 32-deep sub-step: step ks+1 has landed (the S-2 newer
 // steps may still be in flight), every wave is done reading stage ks % S, which then takes
 // step ks + S; the first fragments of step ks+1 load while the last MFMAs of step ks run.
 template <class C>
@@ -540,13 +545,11 @@ void gemm_bf16_pipelined(Params p) {
   if (!t.init(p, tid)) return;
   if (p.ready) wait_ready(p, t.m0, min(t.m0 + C::BM, t.m_end));
 
-  f32x16 acc[C::FM][C::FN];
+  f32x4 acc[C::FM][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   bf16x8 af[2][C::FM], bf[2][C::FN];
   const int nk = p.k / C::BK;
 
@@ -555,12 +558,17 @@ void gemm_bf16_pipelined(Params p) {
   wait_vmcnt_and_barrier<(C::S - 1) * C::L0>();
   t.read_frags(smem, 0, 0, af[0], bf[0]);
 
-  for (int ks = 0; ks < nk; ++ks) {
+  // The two fragment buffers alternate per sub-step; with one sub-step per k-step an
+  // iteration takes two k-steps (nk is even: k is a multiple of 64), so that each
+  // iteration starts on buffer 0.
+  constexpr int PAIR = C::SUBS == 1 ? 2 : 1;
+  static_assert((PAIR * C::SUBS) % 2 == 0, "an even number of sub-steps per iteration");
+  for (int ks0 = 0; ks0 < nk; ks0 += PAIR) {
 #pragma unroll
-    for (int sub = 0; sub < C::SUBS; ++sub) {
-      const int b = sub & 1;
+    for (int u = 0; u < PAIR * C::SUBS; ++u) {
+      const int ks = ks0 + u / C::SUBS, sub = u % C::SUBS, b = u & 1;
       if (sub + 1 < C::SUBS) {
-        t.read_frags(smem, ks, (sub + 1) * 16, af[b ^ 1], bf[b ^ 1]);
+        t.read_frags(smem, ks, (sub + 1) * 32, af[b ^ 1], bf[b ^ 1]);
       } else {
         wait_vmcnt_and_barrier<(C::S - 2) * C::L0>();
         t.issue_loads(smem, ks + C::S, nk);
