@@ -331,8 +331,8 @@ def main():
 
 def mfma_ceiling(busy_cus, all_cus):
     """The matrix cores' own ceiling under the power limit, from the calibration program
-    ``lib/mfma_ceiling`` (the bf16 and FP8 GEMMs' MFMA sequences on register operands, no
-    memory work),
+    ``lib/mfma_ceiling`` (the bf16 GEMM's MFMA sequence in its 16x16x32 and 32x32x16 forms
+    and the FP8 GEMM's, on register operands, no memory work),
     run as a child process: 32 launches of ~80 us back to back (the qkv step's launch
     pattern) and one sustained launch, on `busy_cus` CUs and on all of them, with the clock
     each ran at.  None if the program is missing or fails."""
@@ -357,8 +357,11 @@ def mfma_ceiling(busy_cus, all_cus):
              if r.get("kind") == kind and r["cus"] == cus[0] and r["waves_per_simd"] == 2]
         return b[0] if b else None
 
+    # the bf16 GEMM issues v_mfma_f32_16x16x32_bf16 (kind "bf16_16x16x32"); the 32x32x16
+    # form ("bf16") is kept for reference
     return {"program": "chunked_tp_overlap_amd/lib/mfma_ceiling " + " ".join(cmd[1:]),
-            "busy_cus": cus[0], "bursts_tflops_at_busy_cus": burst("bf16"),
+            "busy_cus": cus[0], "bursts_tflops_at_busy_cus": burst("bf16_16x16x32"),
+            "bursts_32x32x16_tflops_at_busy_cus": burst("bf16"),
             "fp8_bursts_tflops_at_busy_cus": burst("fp8"), "rows": rows}
 
 

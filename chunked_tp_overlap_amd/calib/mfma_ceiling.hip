@@ -4,15 +4,15 @@
 // Every wave runs a GEMM's inner work without its memory side, repeated `iters` times over
 // register operands drawn from random data:
 //   bf16: the 16 v_mfma_f32_32x32x16_bf16 of one 32-deep k-step of a 128 x 64 wave tile
-//         (4 x 2 blocks of 32 x 32, two 16-deep sub-steps), as the bf16 GEMM;
+//         (4 x 2 blocks of 32 x 32, two 16-deep sub-steps);
 //   fp8:  the 8 v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, unit scales) of one 64-deep
 //         k-step of the same wave tile, as the FP8 GEMM;
 //   bf16_16x16x32: the 32 v_mfma_f32_16x16x32_bf16 (8 x 4 blocks of 16 x 16) that cover the
-//         same bf16 step with the smaller instruction, for comparison.
+//         same bf16 step with the smaller instruction, as the bf16 GEMM.
 // Every variant is compiled for at most 256 registers per lane (two waves per SIMD), so one
-// and two waves per SIMD run the same code.  One workgroup per CU (its LDS request leaves room for no
-// second), 4 or 8 waves (one or two per SIMD, as the GEMM's four-wave and ping-pong
-// kernels), on a chosen number of CUs.  What this sustains is the most any GEMM built on
+// and two waves per SIMD run the same code.  One workgroup per CU (its LDS request leaves
+// room for no second), 4 or 8 waves (one or two per SIMD, as the GEMMs' four-wave and
+// ping-pong kernels), on a chosen number of CUs.  What this sustains is the most any GEMM built on
 // this instruction can reach with that many CUs busy, whatever its memory side does.
 //
 // Lane 0 of each workgroup records the shader clock counter (s_memtime) and the constant
@@ -55,8 +55,8 @@ constexpr size_t LDS_FORCE_ONE_PER_CU = 96 * 1024;  // two would need 192 KiB of
   } while (0)
 
 template <int WAVES, int KIND>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma_loop(const bf16x8* src, float* sink,
-                                                         unsigned long long* clk, int iters) {
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mfma_loop(const bf16x8* src, float* sink, unsigned long long* clk, int iters) {
   extern __shared__ unsigned char lds[];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
