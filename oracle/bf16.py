@@ -70,7 +70,11 @@ def encode_rne(x):
 
 
 def ulp(bits):
-    """Spacing of bf16 values at each given bf16 value (float64): 2**(max(e,-126) - 7)."""
+    """Spacing of bf16 values at each given finite bf16 value (float64): the gap from its
+    magnitude to the next larger bf16 magnitude, 2**(max(e, -126) - 7) with
+    e = floor(log2|v|) (8 significant bits; the subnormals and zero share the smallest
+    normal binade's spacing 2**-133).  At a power of two this is the binade above, the
+    larger of the two gaps around the value.  Used for error bounds in the tests."""
     v = np.abs(decode(bits))
     _, E = np.frexp(np.where(v > 0, v, 1.0))
     e = np.where(v > 0, np.maximum(E.astype(np.int64) - 1, _EMIN), _EMIN)

@@ -229,7 +229,3 @@ def rs_rows(a_rows_bits, w_bits, tp, H=None):
     out = bf16.encode_rne(exact_sum([bf16.decode(p) for p in parts]) + 0.0)
     return out, parts
 
-
-def unrounded(a_bits, w_bits):
-    """A @ W in fp64 with no bf16 rounding anywhere (for error-bound checks)."""
-    return matmul_f64(a_bits, w_bits)

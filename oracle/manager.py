@@ -20,10 +20,10 @@ Readings (the pages leave these open):
   T <= capacity rows;
 * the initial active shape is the capacity shape (quantized buffers are "left at their
   capacity shape"), so capacity itself must be divisible by tp;
-* the reduce-scatter side keeps its extra per-rank partial chunks inside its own
-  allocation ("Reduce-scatter retains its extra P2P chunks within the original
-  allocation"): a workspace of tp partial slots sized by capacity, whose active part is
-  the packed prefix of tp * T rows.
+* the reduce-scatter side holds its extra per-rank partial chunks inside the same
+  capacity-sized allocation rather than a new one (same page and section): a workspace
+  of tp partial slots sized by capacity, whose active part is the packed prefix of
+  tp * T rows.
 """
 
 import numpy as np

@@ -29,6 +29,20 @@ def bf16_bits_to_int(b):
     return sign * mag
 
 
+def spacing_int(b):
+    """Gap between the magnitude of finite bf16 pattern b and the next larger bf16
+    magnitude, as an integer multiple of 2**-133, from the bit fields: patterns that share
+    an exponent field are evenly spaced by one unit of the last stored bit, which is
+    2**-133 for the subnormals and for exponent field 1, and doubles with each exponent
+    field above that.  Past the largest finite magnitude (exponent field 254) the same
+    binade's spacing is returned."""
+    b = int(b) & 0x7FFF
+    expf = b >> 7
+    if expf == 0xFF:
+        raise ValueError("inf/nan has no spacing")
+    return 1 << max(expf - 1, 0)
+
+
 def ints_of(bits):
     flat = np.asarray(bits, dtype=np.uint16).ravel()
     return np.array([bf16_bits_to_int(x) for x in flat], dtype=object).reshape(np.shape(bits))

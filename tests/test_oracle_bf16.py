@@ -94,3 +94,47 @@ def test_fp32_double_rounding_would_differ():
     assert int(bf16.encode_rne(np.array([x]))[0]) == 0x3F81
     via32 = torch.tensor([x], dtype=torch.float64).float().to(torch.bfloat16).view(torch.int16)
     assert int(via32.item()) & 0xFFFF == 0x3F80
+
+
+# ---- spacing (ulp) ----------------------------------------------------------------------
+# The spacing of bf16 values at a value sets the tight error bound of every random-input
+# parity test, so it is pinned three ways: hand-worked values, the gap to the next
+# pattern over every finite pattern (exact integer arithmetic), and the bit-field rule of
+# tests/exact.py.
+
+@pytest.mark.parametrize("bits, spacing", [
+    (0x3F80, 2.0 ** -7),    # 1.0: 8 significant bits, so the next value is 1 + 2**-7
+    (0xBF80, 2.0 ** -7),    # -1.0: the spacing of the magnitude
+    (0x437F, 1.0),          # 255 = 1.9921875 * 2**7: spacing 2**0
+    (0x4380, 2.0),          # 256 = 2**8: spacing 2**1 (the binade above, not 1 below)
+    (0x3F00, 2.0 ** -8),    # 0.5
+    (0x0080, 2.0 ** -133),  # smallest normal 2**-126: spacing 2**-133
+    (0x0001, 2.0 ** -133),  # smallest subnormal: the fixed subnormal spacing
+    (0x007F, 2.0 ** -133),  # largest subnormal
+    (0x7F7F, 2.0 ** 120),   # largest finite, (2 - 2**-7) * 2**127
+    (0x0000, 2.0 ** -133),  # +0
+    (0x8000, 2.0 ** -133),  # -0
+])
+def test_ulp_hand_cases(bits, spacing):
+    assert bf16.ulp(np.array([bits], np.uint16))[0] == spacing
+
+
+def test_ulp_is_gap_to_next_pattern_everywhere():
+    """For every finite non-negative pattern below the largest, the spacing equals the
+    exact difference to the next pattern up (integers scaled by 2**133); negative patterns
+    take their magnitude's.  The largest finite pattern follows the bit-field rule."""
+    b = np.arange(0x7F7F, dtype=np.uint16)           # 0x0000 .. 0x7F7E
+    got = bf16.ulp(b)
+    gaps = np.array([exact.bf16_bits_to_int(x + 1) - exact.bf16_bits_to_int(x) for x in range(0x7F7F)],
+                    dtype=object)
+    assert np.array_equal(np.array([int(np.ldexp(v, 133)) for v in got], dtype=object), gaps)
+    neg = bf16.ulp(b | np.uint16(0x8000))
+    assert np.array_equal(neg, got)
+
+
+def test_ulp_matches_bit_field_rule():
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = b[((b >> 7) & 0xFF) != 0xFF]
+    got = bf16.ulp(finite)
+    want = np.array([2.0 ** -133 * exact.spacing_int(x) for x in finite])
+    assert np.array_equal(got, want)

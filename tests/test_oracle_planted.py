@@ -65,3 +65,34 @@ def test_shifted_row_offset_is_caught(monkeypatch):
     monkeypatch.setattr(gemm.M.UserBufferModel, "row_offset_elems",
                         lambda self, r: real(self, r) + (self.hidden if r > 0 else 0))
     _fails(pins.test_integer_inputs_exact_at_larger_shape)
+
+
+def _ulp_pins():
+    from tests import test_oracle_bf16 as b
+    b.test_ulp_is_gap_to_next_pattern_everywhere()
+    b.test_ulp_matches_bit_field_rule()
+
+
+def test_ulp_pins_pass_unmodified():
+    _ulp_pins()
+
+
+def test_ulp_off_by_one_exponent_is_caught(monkeypatch):
+    from oracle import bf16
+    real = bf16.ulp
+    monkeypatch.setattr(bf16, "ulp", lambda bits: real(bits) * 2.0)
+    _fails(_ulp_pins)
+
+
+def test_ulp_binade_below_at_powers_of_two_is_caught(monkeypatch):
+    from oracle import bf16
+
+    def below(bits):  # the spacing below |v|: half as large where |v| is a power of two
+        v = np.abs(bf16.decode(bits))
+        _, E = np.frexp(np.where(v > 0, v, 1.0))
+        m = np.where(v > 0, np.frexp(np.where(v > 0, v, 1.0))[0], 0.75)
+        e = np.maximum(E.astype(np.int64) - 1 - (m == 0.5), -126)
+        return np.ldexp(1.0, (e - 7).astype(np.int32))
+
+    monkeypatch.setattr(bf16, "ulp", below)
+    _fails(_ulp_pins)
