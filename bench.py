@@ -2,26 +2,30 @@
 """Benchmark of the chunked tensor-parallel overlap GEMMs on one MI355X.
 
 Metric: bf16 TFLOP/s of the chunked AG/RS GEMM at the active T, and its fraction of the
-dense bf16 MFMA peak.  One step = one pass of the hot path over one batch of the QKV
-workload: for each of its 32 THD microbatches, set the active shape [T, 4096] on the one
-capacity-8192 UserBuffer and run the chunked all-gather-side GEMM (W [4096, 1536], ring
-exchange over tp = 8 chunks).  FLOPs are algorithmic: 2 * T * 4096 * 1536 per microbatch,
-active T only.  Inputs are seeded synthetic draws already resident in HBM when the timed
-region starts.
+dense bf16 MFMA peak.  The headline workload is the largest single-GPU configuration, the
+GQA QKV all-gather-side GEMM in bulk mode: one UserBuffer registered once at capacity
+[32768, 8192], W [8192, 1280], tp 8, num_splits 8, and a T sweep from 1024 to 32520 in steps
+of 1016 (32 points) on that one registration, with no reallocation between points.  One
+step = the whole sweep: for each T, ub_set_active_shape([T, 8192]) then one
+ub_gemm_ag_chunked call.  FLOPs are algorithmic: 2 * T * 8192 * 1280 per point, active T
+only.  Inputs are seeded synthetic draws already resident in HBM when the timed region
+starts.
 
-The primary schedule is the device-side chunk loop (option atomic_gemm: one launch per
-call whose workgroups walk the 8 ring chunks in ring order); the host loop of per-chunk
-launches on min(8, 3) streams is measured as well and reported under "modes".
+The schedule is the device-side chunk loop (option atomic_gemm: one launch per call, or two
+when the plan cuts a nearly empty last round, whose workgroups walk the 8 chunks in plan
+order); the host loop of per-chunk launches on min(8, 3) streams is measured as a secondary
+row, as are the QKV, fc1 and fc2 workloads, the reduction, FP8 and the arrival stand-in.
 
-Prints one JSON line.  --profile-pass [qkv|reduce|fp8] runs only one kernel's timed region
-(and a copy kernel of known size) for rocprofv3.
+Per-launch HIP events (the library's kernel timing, recorded on the stream each launch runs
+on) are taken inside the headline's timed region itself, so the roofline's kernel time is
+part of the timed step.  Prints one JSON line.  --profile-pass runs only one workload's
+timed region (and a copy of known size that calibrates rocprofv3's byte counters).
 """
 
 import argparse
 import hashlib
 import json
 import os
-import subprocess
 import sys
 import time
 
@@ -32,24 +36,25 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 GEMM_SRC = os.path.join(ROOT, "chunked_tp_overlap_amd", "csrc", "gemm_bf16.hip")
 REDUCE_SRC = os.path.join(ROOT, "chunked_tp_overlap_amd", "csrc", "reduce_partials.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+PROFILE_PASSES = ("gqa", "qkv", "fc1", "fc2", "reduce", "fp8", "arrival")
 
 
 def parse_args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--cpu-seconds", type=float, default=10.0,
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="minimum CPU-oracle baseline work (seconds)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
-    p.add_argument("--profile-pass", nargs="?", const="qkv", default=None,
-                   choices=["qkv", "reduce", "fp8", "arrival"],
-                   help="for rocprofv3: run only one kernel's timed region and its per-launch "
-                        "timing pass (qkv: the primary bf16 GEMM; reduce: the fc2 reduction at "
-                        "T = 16384; fp8: the qkv step on an fp8 buffer), then a 1 GiB copy that "
-                        "calibrates the byte counters; arrival: separated arrival-stand-in calls "
-                        "of every mode, for a timeline; print one JSON line")
+    p.add_argument("--profile-pass", default=None, choices=PROFILE_PASSES,
+                   help="for rocprofv3: run only this workload's timed region (with the "
+                        "library's per-launch events), then a 1 GiB copy that calibrates the "
+                        "byte counters, and print one JSON line (gqa: the headline sweep; qkv, "
+                        "fc1: their microbatches; fc2: the slice GEMMs and reductions over its T "
+                        "sweep; reduce: the fc2 reduction at T = 16384; fp8: the qkv step on an "
+                        "fp8 buffer; arrival: separated arrival-stand-in calls of every mode)")
     return p.parse_args()
 
 
@@ -62,15 +67,16 @@ def src_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-class Qkv:
-    """The QKV workload on one registered UserBuffer."""
+# ---- workloads ---------------------------------------------------------------------------
 
-    def __init__(self, ub, wl, torch, np, dev):
-        self.ub, self.torch = ub, torch
-        w = self.w = wl.qkv()
-        ra, rw, rt = w.seeds()
-        self.Ts, _ = wl.qkv_pack_tokens(rt)
-        log(f"generating inputs: capacity {w.capacity} x {w.hidden}, W {w.hidden} x {w.n_cols}")
+class AgSweep:
+    """An all-gather-side workload on one registered UserBuffer: a list of active T values,
+    one ub_gemm_ag_chunked call per T."""
+
+    def __init__(self, ub, wl, torch, np, dev, w, Ts):
+        self.ub, self.torch, self.w, self.Ts = ub, torch, w, list(Ts)
+        ra, rw, _ = w.seeds()
+        log(f"generating {w.name}: capacity {w.capacity} x {w.hidden}, W {w.hidden} x {w.n_cols}")
         self.a_host = wl.activations(w, w.capacity, ra)
         self.w_host = wl.weights(w, rw)
         ub_bytes, _ = ub.ub_required_bytes(w.capacity, w.hidden, w.tp)
@@ -78,41 +84,82 @@ class Qkv:
         self.w_t = torch.from_numpy(self.w_host.view(np.int16)).to(dev)
         self.c_t = torch.empty((w.capacity, w.n_cols), dtype=torch.int16, device=dev)
         self.h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, self.ub_t, ub_bytes)
-        self.flops = sum(2.0 * T * w.hidden * w.n_cols for T in self.Ts)
+        # worker streams right after registration: they take hardware queues of their own
+        ub.ub_prepare_streams(self.h, w.num_max_streams)
         self.stream = torch.cuda.current_stream()
+        self.flops = sum(self.flop(T) for T in self.Ts)
+
+    def flop(self, T):
+        return 2.0 * T * self.w.hidden * self.w.n_cols
+
+    def alg_bytes(self, T):
+        w = self.w
+        return 2.0 * (T * w.hidden + w.hidden * w.n_cols + T * w.n_cols)
 
     def cfg(self, atomic):
         w = self.w
         return self.ub.make_cfg(w.method, w.num_splits, w.num_max_streams, w.aggregate, atomic)
 
-    def step(self, cfg):
+    def call(self, T, cfg):
         ub, w = self.ub, self.w
-        for T in self.Ts:
-            ub.ub_set_active_shape(self.h, (T, w.hidden))
-            ub.ub_gemm_ag_chunked(self.h, self.w_t, w.n_cols, w.n_cols, self.c_t, w.n_cols, cfg,
-                                  self.stream)
+        ub.ub_set_active_shape(self.h, (T, w.hidden))
+        ub.ub_gemm_ag_chunked(self.h, self.w_t, w.n_cols, w.n_cols, self.c_t, w.n_cols, cfg,
+                              self.stream)
 
-    def timed(self, cfg, steps, warmup):
-        torch = self.torch
+    def step(self, cfg):
+        for T in self.Ts:
+            self.call(T, cfg)
+
+    def timed(self, cfg, steps, warmup, events=False):
+        """Seconds per step over `steps` steps after `warmup` untimed ones.  events: the
+        library's per-launch HIP events are on during the timed steps; returns (seconds,
+        GEMM launch stats of those steps)."""
+        ub, torch = self.ub, self.torch
         for _ in range(warmup):
             self.step(cfg)
         torch.cuda.synchronize()
+        if events:
+            ub.ub_set_kernel_timing(self.h, True)
+            ub.ub_get_kernel_timing(self.h)
         t0 = time.perf_counter()
         for _ in range(steps):
             self.step(cfg)
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / steps
+        sec = (time.perf_counter() - t0) / steps
+        stats = None
+        if events:
+            stats, _ = ub.ub_get_kernel_timing(self.h)
+            ub.ub_set_kernel_timing(self.h, False)
+        return sec, stats
+
+    def per_point(self, cfg, reps=20):
+        """(T, median ms, min ms) per point: 5 warm-up calls, then `reps` calls timed one by
+        one with HIP events on the launch stream."""
+        out = []
+        for T in self.Ts:
+            med, best, _ = _call_stats(lambda: self.call(T, cfg), self.torch, self.stream, reps)
+            out.append((T, med, best))
+        return out
+
+    def plans(self, cfg):
+        """The tile plan of each point's call: (T, tile_m, tile_n, cut_row, tail_m, tail_n)."""
+        rows = []
+        for T in self.Ts:
+            self.call(T, cfg)
+            rows.append((T,) + tuple(self.ub.ub_debug_last_plan(self.h)))
+        self.torch.cuda.synchronize()
+        return rows
 
     def graph_replay(self, cfg, reps):
-        """Seconds per step when one step (32 microbatches, each with its own active
-        shape) is captured once in a HIP graph and replayed."""
+        """Seconds per step when one step (every T, each with its own active shape) is
+        captured once in a HIP graph and replayed."""
         torch = self.torch
         s = torch.cuda.Stream()
         old = self.stream
         self.stream = s
         try:
             with torch.cuda.stream(s):
-                self.step(cfg)  # warm: streams and events exist before capture
+                self.step(cfg)
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=s):
@@ -128,19 +175,31 @@ class Qkv:
         finally:
             self.stream = old
 
-    def per_microbatch(self, cfg, reps=20):
-        """(T, median ms, min ms) per microbatch: 5 warm-up calls, then `reps` calls timed
-        one by one with HIP events on the launch stream."""
-        ub, w = self.ub, self.w
-        out = []
-        for T in self.Ts:
-            ub.ub_set_active_shape(self.h, (T, w.hidden))
-            med, best, _ = _call_stats(
-                lambda: ub.ub_gemm_ag_chunked(self.h, self.w_t, w.n_cols, w.n_cols, self.c_t, w.n_cols,
-                                              cfg, self.stream), self.torch, self.stream, reps)
-            out.append((T, med, best))
-        return out
+    def close(self):
+        self.torch.cuda.synchronize()
+        self.ub.ub_destroy(self.h)
 
+
+def gqa_sweep(ub, wl, torch, np, dev):
+    """The headline: the GQA bulk sweep's 32 grid points (1024 ... 32520; the extra point
+    T = 32768 is reported with the secondary rows)."""
+    return AgSweep(ub, wl, torch, np, dev, wl.gqa_bulk(), [T for T in wl.gqa_tokens() if T != 32768])
+
+
+def qkv_step(ub, wl, torch, np, dev):
+    w = wl.qkv()
+    _, _, rt = w.seeds()
+    Ts, _ = wl.qkv_pack_tokens(rt)
+    return AgSweep(ub, wl, torch, np, dev, w, Ts)
+
+
+def fc1_step(ub, wl, torch, np, dev):
+    w = wl.fc1()
+    _, _, rt = w.seeds()
+    return AgSweep(ub, wl, torch, np, dev, w, wl.fc1_tokens(rt))
+
+
+# ---- main --------------------------------------------------------------------------------
 
 def main():
     args = parse_args()
@@ -151,17 +210,6 @@ def main():
               "multi-GPU path.", file=sys.stderr, flush=True)
         sys.exit(2)
 
-    # A handle's host-loop and arrival schedules use up to four streams (the caller's, two
-    # workers, the copy stream).  HIP maps a process's streams onto GPU_MAX_HW_QUEUES
-    # hardware queues (default 4); streams that share a queue run in issue order, which
-    # serialises the arrival copies with the GEMMs once the benchmark's earlier sections
-    # have created streams of their own.  At least eight queues keep them apart.  Set
-    # before HIP initialises; a larger setting in the environment is kept.
-    try:
-        queues = int(os.environ.get("GPU_MAX_HW_QUEUES", "4"))
-    except ValueError:
-        queues = 4
-    os.environ["GPU_MAX_HW_QUEUES"] = str(max(queues, 8))
     import numpy as np
     import torch
 
@@ -171,94 +219,55 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    if args.profile_pass in ("reduce", "fp8", "arrival"):
-        fn = {"reduce": profile_reduce, "fp8": profile_fp8, "arrival": profile_arrival}[args.profile_pass]
-        res = fn(ub, wl, torch, np, dev, args.steps, args.warmup)
+    if args.profile_pass:
+        fn = {"gqa": profile_ag, "qkv": profile_ag, "fc1": profile_ag, "fc2": profile_fc2,
+              "reduce": profile_reduce, "fp8": profile_fp8, "arrival": profile_arrival}[args.profile_pass]
+        res = fn(ub, wl, torch, np, dev, args)
         calibration_copy(torch, dev)
         print(json.dumps(res), flush=True)
         return
-    q = Qkv(ub, wl, torch, np, dev)
-    primary = q.cfg(atomic=True)
-    # One host-loop call first, so that the handle's worker streams exist before the
-    # benchmark's graph captures start using torch's stream pool.  HIP places each stream
-    # on one of GPU_MAX_HW_QUEUES hardware queues, and streams that share a queue run in
-    # issue order.  When the worker streams were first created inside the capture code, the
-    # eager host loop measured ~320 TFLOP/s instead of ~440, with the same kernels.
-    q.step(q.cfg(atomic=False))
-    torch.cuda.synchronize()
 
-    log(f"warmup {args.warmup}, timed {args.steps} steps of {len(q.Ts)} microbatches (atomic_gemm)")
-    sec = q.timed(primary, args.steps, args.warmup)
-    tflops = q.flops / sec / 1e12
-    log(f"primary: {sec * 1e3:.3f} ms/step, {tflops:.1f} TFLOP/s")
+    g = gqa_sweep(ub, wl, torch, np, dev)
+    primary = g.cfg(atomic=True)
+    log(f"warmup {args.warmup}, timed {args.steps} steps of {len(g.Ts)} GQA points (atomic_gemm)")
+    sec, stats = g.timed(primary, args.steps, args.warmup, events=True)
+    tflops = g.flops / sec / 1e12
+    log(f"primary: {sec * 1e3:.3f} ms/step, {tflops:.1f} TFLOP/s (per-launch events on)")
+    sec_clean, _ = g.timed(primary, args.steps, 1)
+    log(f"same steps without events: {sec_clean * 1e3:.3f} ms/step")
 
-    # the same timed region again with per-launch HIP events on the launch stream
-    ub.ub_set_kernel_timing(q.h, True)
-    ub.ub_get_kernel_timing(q.h)
-    sec_i = q.timed(primary, args.steps, 0)
-    gemm_stats, _ = ub.ub_get_kernel_timing(q.h)
-    ub.ub_set_kernel_timing(q.h, False)
-    g_ach = gemm_stats["flops"] / (gemm_stats["total_ms"] / 1e3) / 1e12
-    avg_launch_us = gemm_stats["total_ms"] * 1e3 / max(1, gemm_stats["launches"])
-
-    if args.profile_pass:
-        calibration_copy(torch, dev)
-        ub.ub_destroy(q.h)
-        print(json.dumps({"profile_pass": "qkv", "ms_per_step": round(sec * 1e3, 4),
-                          "launches_per_step": len(q.Ts),
-                          "launches": (args.warmup + 2 * args.steps) * len(q.Ts),
-                          "timed_launches": 2 * args.steps * len(q.Ts),
-                          "avg_launch_us_hip_events": round(avg_launch_us, 3),
-                          "avg_launch_gflop": round(gemm_stats["flops"] / max(1, gemm_stats["launches"]) / 1e9, 4),
-                          "algorithmic_bytes_per_launch": round(gemm_stats["bytes"] / max(1, gemm_stats["launches"])),
-                          "src_file": os.path.relpath(GEMM_SRC, ROOT),
-                          "src_hash": src_hash(GEMM_SRC)}), flush=True)
-        return
-
-    per_mb = q.per_microbatch(primary)
-    fl = lambda T: 2.0 * T * q.w.hidden * q.w.n_cols
-    big = [(T, med) for T, med, _ in per_mb if T >= 4096]
-    agg_ge4096 = sum(fl(T) for T, _ in big) / (sum(ms for _, ms in big) / 1e3) / 1e12
-    agg_all = sum(fl(T) for T, _, _ in per_mb) / (sum(ms for _, ms, _ in per_mb) / 1e3) / 1e12
-
-    host_cfg = q.cfg(atomic=False)
-    graph = {}
-    for name, cfg in (("atomic_gemm", primary), ("host_loop_3_streams", host_cfg)):
-        graph[name] = round(q.flops / q.graph_replay(cfg, args.steps) / 1e12, 2)
-    sec_h = q.timed(host_cfg, max(2, args.steps // 2), 1)
-    ub.ub_set_kernel_timing(q.h, True)
-    ub.ub_get_kernel_timing(q.h)
-    q.timed(host_cfg, 2, 0)
-    host_stats, _ = ub.ub_get_kernel_timing(q.h)
-    ub.ub_set_kernel_timing(q.h, False)
-
-    traffic, util = None, None
+    kernel_ms_per_step = stats["total_ms"] / args.steps
+    achieved = stats["flops"] / (stats["total_ms"] / 1e3) / 1e12
+    calls = stats["launches"]
+    traffic, traffic_src = None, None
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if tr.get("src_hash") == src_hash(GEMM_SRC):
-            traffic = tr.get("qkv_gemm_bytes_per_launch")
-            util = tr.get("util")
+        if tr.get("src_hash") == src_hash(GEMM_SRC) and tr.get("workload") == "gqa":
+            traffic = tr.get("bytes_per_call")
+            traffic_src = tr.get("source")
     except (OSError, ValueError):
         pass
-
     roofline = {
-        "bound": "mfma", "kernel": "gemm_bf16_pingpong (device-side chunk loop, one launch per call)",
-        "achieved": round(g_ach, 2), "peak": MFMA_PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-        "frac": round(g_ach / MFMA_PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-        "launches": gemm_stats["launches"],
-        "avg_launch_us": round(avg_launch_us, 3),
-        "avg_launch_gflop": round(gemm_stats["flops"] / max(1, gemm_stats["launches"]) / 1e9, 4),
-        "algorithmic_bytes_per_launch": round(gemm_stats["bytes"] / max(1, gemm_stats["launches"])),
-        "measured_pass_ms_per_step": round(sec_i * 1e3, 4),
+        "bound": "mfma",
+        "kernel": "gemm_bf16_pingpong / gemm_bf16_pipelined (device-side chunk loop; one call = "
+                  "one launch, or two when the plan cuts a nearly empty last round)",
+        "achieved": round(achieved, 2), "peak": MFMA_PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(achieved / MFMA_PEAK_BF16_TFLOPS, 4),
+        "traffic": traffic,
+        "traffic_note": (f"HBM bytes per call, mean over the sweep, from rocprofv3 FETCH_SIZE + "
+                         f"WRITE_SIZE passes of this kernel source ({traffic_src})" if traffic
+                         else "no counter pass of this kernel source"),
+        "calls": calls,
+        "avg_call_us": round(stats["total_ms"] * 1e3 / max(1, calls), 3),
+        "avg_call_gflop": round(stats["flops"] / max(1, calls) / 1e9, 4),
+        "algorithmic_bytes_per_call": round(stats["bytes"] / max(1, calls)),
+        "kernel_ms_per_step": round(kernel_ms_per_step, 4),
+        "timing": "HIP events around every GEMM call on its launch stream, inside the timed "
+                  "region; kernel_ms_per_step <= ms_per_step",
     }
-    if util:
-        # from the committed counter pass of the same kernel source (rocprofv3 --pmc
-        # GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES): the effective clock,
-        # the mean number of CUs holding a tile, and how busy their matrix cores are
-        roofline["counters"] = util
 
-    w = q.w
+    w = g.w
     result = {
         "metric": "bf16 TFLOP/s of chunked AG/RS GEMM at active T; % of MFMA peak",
         "value": round(tflops, 3),
@@ -274,101 +283,66 @@ def main():
         "data": "synthetic",
         "pct_of_mfma_peak": round(100 * tflops / MFMA_PEAK_BF16_TFLOPS, 2),
         "config": {
-            "workload": "qkv_ag: column-parallel AG-GEMM over a [8192, 4096] bf16 UserBuffer, "
-                        "W [4096, 1536], tp 8, ring exchange (8 chunks), 32 THD microbatches "
-                        "per step, device-side chunk loop",
+            "workload": "gqa_bulk_ag: GQA QKV column-parallel AG-GEMM, bulk mode, one [32768, 8192] "
+                        "bf16 UserBuffer registered once, W [8192, 1280], tp 8, num_splits 8; one "
+                        "step = the T sweep 1024, 2040, ..., 32520 (32 points, step 1016) with "
+                        "ub_set_active_shape per point; device-side chunk loop",
             "capacity": w.capacity, "hidden": w.hidden, "n_cols": w.n_cols, "tp": w.tp,
             "method": w.method, "num_splits": w.num_splits, "num_max_streams": w.num_max_streams,
-            "atomic_gemm": True, "microbatches": len(q.Ts), "T_min": min(q.Ts), "T_max": max(q.Ts),
-            "T_mean": round(sum(q.Ts) / len(q.Ts), 1), "gflop_per_step": round(q.flops / 1e9, 2),
-            "seed": w.seed,
+            "atomic_gemm": True, "points": len(g.Ts), "T_min": min(g.Ts), "T_max": max(g.Ts),
+            "gflop_per_step": round(g.flops / 1e9, 2), "seed": w.seed,
         },
-        "tflops_T_ge_4096_per_microbatch_aggregate": round(agg_ge4096, 3),
-        "tflops_all_per_microbatch_aggregate": round(agg_all, 3),
-        "per_microbatch": {"columns": ["T", "tflops_median", "tflops_best"],
-                           "note": "each microbatch: 5 warm-up calls, 20 calls timed one by one (HIP events)",
-                           "rows": [[T, round(fl(T) / med / 1e9, 1), round(fl(T) / best / 1e9, 1)]
-                                    for T, med, best in per_mb]},
-        "graph_replay_tflops": graph,
-        "modes": {
-            "atomic_gemm": {"tflops": round(tflops, 2), "ms_per_step": round(sec * 1e3, 4)},
-            "host_loop_3_streams": {
-                "tflops": round(q.flops / sec_h / 1e12, 2), "ms_per_step": round(sec_h * 1e3, 4),
-                "avg_launch_us": round(host_stats["total_ms"] * 1e3 / max(1, host_stats["launches"]), 3),
-                "per_launch_tflops": round(host_stats["flops"] / max(1e-9, host_stats["total_ms"] / 1e3) / 1e12, 2)},
-        },
+        "ms_per_step_without_events": round(sec_clean * 1e3, 4),
         "roofline": roofline,
     }
+    per_pt = g.per_point(primary)
+    result["per_point"] = {"columns": ["T", "tflops_median", "tflops_best", "plan"],
+                           "note": "each point: 5 warm-up calls, 20 calls timed one by one (HIP events); "
+                                   "plan = tile_m x tile_n [cut row: tail tile]",
+                           "rows": []}
+    plans = {p[0]: p[1:] for p in g.plans(primary)}
+    for T, med, best in per_pt:
+        tm, tn, cut, sm, sn = plans[T]
+        plan = f"{tm}x{tn}" + (f" cut {cut}: {sm}x{sn}" if cut >= 0 else "")
+        result["per_point"]["rows"].append([T, round(g.flop(T) / med / 1e9, 1),
+                                            round(g.flop(T) / best / 1e9, 1), plan])
+    result["per_point"]["tflops_sum_flops_over_sum_medians"] = round(
+        g.flops / (sum(m for _, m, _ in per_pt) / 1e3) / 1e12, 2)
+    host_cfg = g.cfg(atomic=False)
+    sec_h, _ = g.timed(host_cfg, max(2, args.steps // 4), 1)
+    result["modes"] = {
+        "atomic_gemm": {"tflops": round(tflops, 2), "ms_per_step": round(sec * 1e3, 4)},
+        "host_loop_3_streams": {"tflops": round(g.flops / sec_h / 1e12, 2),
+                                "ms_per_step": round(sec_h * 1e3, 4)},
+    }
+    result["graph_replay_tflops"] = {"atomic_gemm": round(g.flops / g.graph_replay(primary, 5) / 1e12, 2)}
 
     props = torch.cuda.get_device_properties(0)
     result["device"] = {"name": props.name, "cus": props.multi_processor_count,
                         "gcn_arch": getattr(props, "gcnArchName", ""),
                         "gemm_src_hash": src_hash(GEMM_SRC),
-                        "gpu_max_hw_queues": os.environ.get("GPU_MAX_HW_QUEUES")}
+                        "gpu_max_hw_queues": os.environ.get("GPU_MAX_HW_QUEUES", "(runtime default)")}
     result["device_state"] = device_state(torch)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(g, args.cpu_seconds)
+    g.close()
+    del g
 
     if not args.no_secondary:
         result["secondary"] = secondary(ub, wl, torch, np, dev)
-
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(q, args.cpu_seconds)
-
-    ub.ub_destroy(q.h)
-    busy = int(round(util["busy_cus_mean"])) if util and util.get("busy_cus_mean") else 142
-    ceiling = mfma_ceiling(busy, props.multi_processor_count)
-    if ceiling:
-        burst = ceiling.get("bursts_tflops_at_busy_cus")
-        if burst:
-            ceiling["achieved_over_bursts_ceiling"] = round(g_ach / burst, 4)
-        fp8 = (result.get("secondary") or {}).get("qkv_fp8")
-        burst8 = ceiling.get("fp8_bursts_tflops_at_busy_cus")
-        if fp8 and burst8:
-            # the FP8 qkv step's rate (launch gaps included) over the FP8 MFMAs' own ceiling
-            ceiling["fp8_step_over_fp8_bursts_ceiling"] = round(fp8["tflops"] / burst8, 4)
-        roofline["mfma_ceiling"] = ceiling
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 
-def mfma_ceiling(busy_cus, all_cus):
-    """The matrix cores' own ceiling under the power limit, from the calibration program
-    ``lib/mfma_ceiling`` (the bf16 GEMM's MFMA sequence in its 16x16x32 and 32x32x16 forms
-    and the FP8 GEMM's, on register operands, no memory work),
-    run as a child process: 32 launches of ~80 us back to back (the qkv step's launch
-    pattern) and one sustained launch, on `busy_cus` CUs and on all of them, with the clock
-    each ran at.  None if the program is missing or fails."""
-    exe = os.path.join(ROOT, "chunked_tp_overlap_amd", "lib", "mfma_ceiling")
-    if not os.path.exists(exe):
-        log("mfma_ceiling program not built; skipping the ceiling")
-        return None
-    cus = sorted({max(1, min(busy_cus, all_cus)), all_cus})
-    cmd = [exe, "0.5", *[str(c) for c in cus]]
-    try:
-        res = subprocess.run(cmd, capture_output=True, text=True, timeout=120)
-    except subprocess.TimeoutExpired:
-        log("mfma_ceiling timed out")
-        return None
-    if res.returncode != 0:
-        log(f"mfma_ceiling failed ({res.returncode}): {res.stderr.strip()[-300:]}")
-        return None
-    rows = [json.loads(ln) for ln in res.stdout.splitlines() if ln.startswith("{")]
-
-    def burst(kind):
-        b = [r["bursts_32x80us"]["tflops"] for r in rows
-             if r.get("kind") == kind and r["cus"] == cus[0] and r["waves_per_simd"] == 2]
-        return b[0] if b else None
-
-    # the bf16 GEMM issues v_mfma_f32_16x16x32_bf16 (kind "bf16_16x16x32"); the 32x32x16
-    # form ("bf16") is kept for reference
-    return {"program": "chunked_tp_overlap_amd/lib/mfma_ceiling " + " ".join(cmd[1:]),
-            "busy_cus": cus[0], "bursts_tflops_at_busy_cus": burst("bf16_16x16x32"),
-            "bursts_32x32x16_tflops_at_busy_cus": burst("bf16"),
-            "fp8_bursts_tflops_at_busy_cus": burst("fp8"), "rows": rows}
-
+# ---- helpers -----------------------------------------------------------------------------
 
 def device_state(torch):
     """The GPU's PCI address and socket power cap (amdsmi).  amdsmi's metrics table refreshes
-    too slowly to sample the ~0.1 s timed region, so no clock is read here: the effective
-    clock of the timed kernel comes from the counter pass (roofline.counters)."""
+    too slowly to sample the timed region, so no clock is read here: the effective clock of
+    the profiled kernels is in their counter summaries under profiles/."""
     out = {"source": "amdsmi", "power_cap_w": None, "bdf": None}
     try:
         import amdsmi
@@ -399,131 +373,6 @@ def calibration_copy(torch, dev):
     dst = torch.empty_like(src)
     dst.copy_(src)
     torch.cuda.synchronize()
-
-
-def _instrumented(ub, h, torch, fn, reps, kind):
-    """Run fn() reps times with the library's per-launch HIP events; (launches, mean us,
-    mean GFLOP, mean algorithmic bytes) of launches of `kind` (0 GEMM, 1 reduction)."""
-    ub.ub_set_kernel_timing(h, True)
-    ub.ub_get_kernel_timing(h)
-    for _ in range(reps):
-        fn()
-    torch.cuda.synchronize()
-    stats = ub.ub_get_kernel_timing(h)[kind]
-    ub.ub_set_kernel_timing(h, False)
-    n = max(1, stats["launches"])
-    return stats["launches"], stats["total_ms"] * 1e3 / n, stats["flops"] / n / 1e9, stats["bytes"] / n
-
-
-def profile_reduce(ub, wl, torch, np, dev, steps, warmup):
-    """The fc2 reduction at T = 16384 (8 bf16 partial slots of [16384, 4096]): warm-up
-    launches, timed launches, then the same with per-launch events; ascending order first,
-    then ring order."""
-    w = wl.fc2()
-    ra, rw, _ = w.seeds()
-    T = wl.FC2_TOKENS[-1]
-    ub_bytes, ws_bytes = ub.ub_required_bytes(w.capacity, w.hidden, w.tp)
-    ub_t = torch.empty(w.capacity * w.hidden, dtype=torch.int16, device=dev)
-    ws_t = torch.empty(w.tp * w.capacity * w.hidden, dtype=torch.int16, device=dev)
-    a_t = torch.from_numpy(wl.activations(w, T, ra).view(np.int16)).to(dev)
-    w_t = torch.from_numpy(wl.weights(w, rw).view(np.int16)).to(dev)
-    o_t = torch.empty((w.capacity, w.hidden), dtype=torch.int16, device=dev)
-    h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes, ws_t, ws_bytes)
-    ub.ub_set_active_shape(h, (T, w.hidden))
-    ub.ub_gemm_rs_chunked(h, a_t, w.k, w.k, w_t, w.hidden, o_t, w.hidden,
-                          ub.make_cfg(w.method, w.num_splits, atomic_gemm=True))
-    stream = torch.cuda.current_stream()
-    out = {"profile_pass": "reduce", "T": T, "launches_per_order": warmup + 2 * steps}
-    for order in ("ascending", "ring"):
-        fn = lambda: ub.ub_reduce_partials(h, o_t, w.hidden, order, stream)
-        for _ in range(warmup + steps):
-            fn()
-        n, us, _, nbytes = _instrumented(ub, h, torch, fn, steps, 1)
-        out[order] = {"avg_launch_us_hip_events": round(us, 3), "algorithmic_bytes_per_launch": round(nbytes),
-                      "gbs_hip_events": round(nbytes / us / 1e3, 1), "timed_launches": 2 * steps}
-    out["src_file"] = os.path.relpath(REDUCE_SRC, ROOT)
-    out["src_hash"] = src_hash(REDUCE_SRC)
-    ub.ub_destroy(h)
-    return out
-
-
-ARRIVAL_MODES = (("host_loop_pinned_host", True, True, False),
-                 ("host_loop_device_sdma", True, False, False),
-                 ("host_loop_device_copy_kernel", False, False, False),
-                 ("device_loop_pinned_host", True, True, True),
-                 ("device_loop_device_sdma", True, False, True))
-
-
-def profile_arrival(ub, wl, torch, np, dev, steps, warmup):
-    """Arrival stand-in on qkv at T = 8192 (ring, rank 0, 3 streams), for a rocprofv3
-    kernel and memory-copy trace: per mode (host loop or device-side loop; pinned-host,
-    device SDMA or copy-kernel source) `steps` calls, each followed by a device
-    synchronisation and a 20 ms pause, so that every call stands alone on the timeline.
-    Prints the modes in trace order."""
-    w = wl.qkv()
-    ra, rw, _ = w.seeds()
-    T = w.capacity
-    ub_bytes, _ = ub.ub_required_bytes(w.capacity, w.hidden, w.tp)
-    ub_t = torch.from_numpy(wl.activations(w, w.capacity, ra).view(np.int16).ravel()).to(dev)
-    src = ub_t.clone()
-    src_host = ub_t.cpu().pin_memory()
-    w_t = torch.from_numpy(wl.weights(w, rw).view(np.int16)).to(dev)
-    c_t = torch.empty((w.capacity, w.n_cols), dtype=torch.int16, device=dev)
-    h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes)
-    ub.ub_set_active_shape(h, (T, w.hidden))
-    torch.cuda.synchronize()
-    time.sleep(0.05)  # the uploads above stand apart from the first call on the timeline
-    modes = []
-    for name, use_ce, host, atomic in ARRIVAL_MODES:
-        cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, use_ce=use_ce, rank=0,
-                          atomic_gemm=atomic)
-        sb = src_host if host else src
-        for _ in range(steps):
-            ub.ub_gemm_ag_arrival(h, sb, w_t, w.n_cols, w.n_cols, c_t, w.n_cols, cfg)
-            torch.cuda.synchronize()
-            time.sleep(0.02)
-        modes.append({"mode": name, "calls": steps})
-    timeouts = ub.ub_arrival_timeouts(h)
-    ub.ub_destroy(h)
-    return {"profile_pass": "arrival", "T": T, "chunks": w.tp, "modes": modes,
-            "timeouts": timeouts, "gpu_max_hw_queues": os.environ.get("GPU_MAX_HW_QUEUES")}
-
-
-def profile_fp8(ub, wl, torch, np, dev, steps, warmup):
-    """The qkv step on an fp8 buffer (see qkv_fp8): warm-up steps, timed steps, then the
-    same with per-launch events."""
-    w = wl.qkv()
-    ra, rw, rt = w.seeds()
-    Ts, _ = wl.qkv_pack_tokens(rt)
-    H, N = w.hidden, w.n_cols
-    x = torch.from_numpy(wl.activations(w, w.capacity, ra).view(np.int16)).to(dev)
-    wt = torch.from_numpy(wl.weights(w, rw).view(np.int16)).to(dev)
-    sx = 448.0 / float(x.view(torch.bfloat16).float().abs().max())
-    sw = 448.0 / float(wt.view(torch.bfloat16).float().abs().max())
-    ub_t = torch.empty(w.capacity * H, dtype=torch.uint8, device=dev)
-    h = ub.ub_init(w.capacity, H, w.tp, ub.UB_DTYPE_FP8_E4M3, ub_t, w.capacity * H)
-    w8 = torch.empty(N * H, dtype=torch.uint8, device=dev)
-    hw = ub.ub_init(N, H, 1, ub.UB_DTYPE_FP8_E4M3, w8, N * H)
-    ub.ub_quantize_in(hw, wt.t().contiguous(), N, 0, sw)
-    ub.ub_quantize_in(h, x, w.capacity, 0, sx)
-    cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, w.aggregate, True)
-    c_t = torch.empty((w.capacity, N), dtype=torch.int16, device=dev)
-
-    def step():
-        for T in Ts:
-            ub.ub_set_active_shape(h, (T, H))
-            ub.ub_gemm_ag_chunked_fp8(h, w8, N, H, 1.0 / sx, 1.0 / sw, c_t, N, cfg)
-
-    for _ in range(warmup + steps):
-        step()
-    n, us, gflop, nbytes = _instrumented(ub, h, torch, step, steps, 0)
-    ub.ub_destroy(h)
-    ub.ub_destroy(hw)
-    src = os.path.join(ROOT, "chunked_tp_overlap_amd", "csrc", "gemm_fp8.hip")
-    return {"profile_pass": "fp8", "launches": (warmup + 2 * steps) * len(Ts),
-            "timed_launches": 2 * steps * len(Ts), "avg_launch_us_hip_events": round(us, 3),
-            "avg_launch_gflop": round(gflop, 4), "algorithmic_bytes_per_launch": round(nbytes),
-            "src_file": os.path.relpath(src, ROOT), "src_hash": src_hash(src)}
 
 
 def _call_stats(fn, torch, stream, reps=20, warmup=5):
@@ -559,43 +408,66 @@ def _time_calls(fn, torch, stream, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def _ag_rows(sw, cfg, label):
+    """Per-microbatch medians of an AG workload and its aggregates (all, and T >= 4096)."""
+    pts = sw.per_point(cfg)
+    big = [(T, ms) for T, ms, _ in pts if T >= 4096]
+    agg = lambda rows: (sum(sw.flop(T) for T, _ in rows) / (sum(ms for _, ms in rows) / 1e3) / 1e12
+                        if rows else None)
+    tf_all = agg([(T, ms) for T, ms, _ in pts])
+    tf_big = agg(big)
+    log(f"{label}: {tf_all:.1f} TFLOP/s over all points")
+    return {"tflops_all": round(tf_all, 2),
+            "tflops_T_ge_4096": round(tf_big, 2) if tf_big else None,
+            "pct_peak_T_ge_4096": round(100 * tf_big / MFMA_PEAK_BF16_TFLOPS, 2) if tf_big else None}
+
+
+# ---- secondary rows ----------------------------------------------------------------------
+
 def secondary(ub, wl, torch, np, dev):
     out = {}
     stream = torch.cuda.current_stream()
 
+    # GQA: the host loop per point, and the flagged extra point T = 32768
+    g = AgSweep(ub, wl, torch, np, dev, wl.gqa_bulk(), wl.gqa_tokens())
+    log("secondary gqa_bulk_ag host loop")
+    res = {"host_loop_3_streams": _ag_rows(g, g.cfg(False), "gqa host loop")}
+    med, best, _ = _call_stats(lambda: g.call(32768, g.cfg(True)), torch, g.stream)
+    res["T_32768_atomic_gemm"] = {"tflops": round(g.flop(32768) / med / 1e9, 1),
+                                  "plan": list(ub.ub_debug_last_plan(g.h))}
+    out["gqa_bulk_ag"] = res
+    g.close()
+    del g
+
+    # QKV: 32 THD microbatches of one step
+    q = qkv_step(ub, wl, torch, np, dev)
+    log("secondary qkv_ag")
+    sec, qst = q.timed(q.cfg(True), 20, 5, events=True)
+    sec_h, _ = q.timed(q.cfg(False), 10, 2)
+    hl_ev = q.timed(q.cfg(False), 2, 0, events=True)[1]
+    res = {"atomic_gemm": {"tflops_step": round(q.flops / sec / 1e12, 2), "ms_per_step": round(sec * 1e3, 4),
+                           "kernel_tflops": round(qst["flops"] / (qst["total_ms"] / 1e3) / 1e12, 2),
+                           **_ag_rows(q, q.cfg(True), "qkv device loop")},
+           "host_loop_3_streams": {"tflops_step": round(q.flops / sec_h / 1e12, 2),
+                                   "ms_per_step": round(sec_h * 1e3, 4),
+                                   "avg_launch_us": round(hl_ev["total_ms"] * 1e3 / max(1, hl_ev["launches"]), 3)},
+           "graph_replay_tflops": {"atomic_gemm": round(q.flops / q.graph_replay(q.cfg(True), 10) / 1e12, 2),
+                                   "host_loop_3_streams": round(q.flops / q.graph_replay(q.cfg(False), 10) / 1e12, 2)},
+           "microbatches": len(q.Ts), "T_mean": round(sum(q.Ts) / len(q.Ts), 1)}
+    out["qkv_ag"] = res
+    q.close()
+    del q
+
     # fc1: SwiGLU gate+up, aggregate-2x, 16 microbatches
-    w = wl.fc1()
-    ra, rw, rt = w.seeds()
-    Ts = wl.fc1_tokens(rt)
+    f1 = fc1_step(ub, wl, torch, np, dev)
     log("secondary fc1_ag")
-    ub_bytes, _ = ub.ub_required_bytes(w.capacity, w.hidden, w.tp)
-    ub_t = torch.from_numpy(wl.activations(w, w.capacity, ra).view(np.int16).ravel()).to(dev)
-    w_t = torch.from_numpy(wl.weights(w, rw).view(np.int16)).to(dev)
-    c_t = torch.empty((w.capacity, w.n_cols), dtype=torch.int16, device=dev)
-    h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes)
-    res = {}
-    for atomic in (True, False):
-        cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, w.aggregate, atomic)
-        tot_f = tot_ms = big_f = big_ms = 0.0
-        for T in Ts:
-            ub.ub_set_active_shape(h, (T, w.hidden))
-            ms, _, _ = _call_stats(lambda: ub.ub_gemm_ag_chunked(h, w_t, w.n_cols, w.n_cols, c_t, w.n_cols, cfg, stream),
-                                   torch, stream)
-            f = 2.0 * T * w.hidden * w.n_cols
-            tot_f += f
-            tot_ms += ms
-            if T >= 4096:
-                big_f += f
-                big_ms += ms
-        res["atomic_gemm" if atomic else "host_loop"] = {
-            "tflops_all": round(tot_f / tot_ms / 1e9, 2),
-            "tflops_T_ge_4096": round(big_f / big_ms / 1e9, 2) if big_ms else None,
-            "pct_peak_T_ge_4096": round(100 * big_f / big_ms / 1e9 / MFMA_PEAK_BF16_TFLOPS, 2) if big_ms else None}
-    res["microbatches"] = len(Ts)
-    res["note"] = "per microbatch the median of 20 calls timed one by one; aggregates are sum FLOPs / sum medians"
-    out["fc1_ag"] = res
-    ub.ub_destroy(h)
-    del ub_t, w_t, c_t
+    out["fc1_ag"] = {"atomic_gemm": _ag_rows(f1, f1.cfg(True), "fc1 device loop"),
+                     "host_loop_3_streams": _ag_rows(f1, f1.cfg(False), "fc1 host loop"),
+                     "microbatches": len(f1.Ts),
+                     "note": "per microbatch the median of 20 calls timed one by one; aggregates are "
+                             "sum FLOPs / sum medians"}
+    f1.close()
+    del f1
 
     out["qkv_arrival"] = arrival(ub, wl, torch, np, dev)
     out["qkv_fp8"] = qkv_fp8(ub, wl, torch, np, dev)
@@ -606,33 +478,28 @@ def secondary(ub, wl, torch, np, dev):
     log("secondary fc2_rs")
     ub_bytes, ws_bytes = ub.ub_required_bytes(w.capacity, w.hidden, w.tp)
     ub_t = torch.empty(w.capacity * w.hidden, dtype=torch.int16, device=dev)
-    ws_t = torch.empty(w.tp * w.capacity * w.hidden, dtype=torch.int16, device=dev)
+    ws_t = torch.zeros(ws_bytes // 2, dtype=torch.int16, device=dev)  # counter region zero
     a_t = torch.from_numpy(wl.activations(w, w.capacity, ra).view(np.int16)).to(dev)
     w_t = torch.from_numpy(wl.weights(w, rw).view(np.int16)).to(dev)
     o_t = torch.empty((w.capacity, w.hidden), dtype=torch.int16, device=dev)
     flush = torch.empty(768 * 1024 * 1024 // 2, dtype=torch.int16, device=dev)
     h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes, ws_t, ws_bytes)
+    ub.ub_prepare_streams(h, w.num_max_streams)
     rows = []
     for T in wl.FC2_TOKENS:
         ub.ub_set_active_shape(h, (T, w.hidden))
         f = 2.0 * T * w.k * w.hidden
         row = {"T": T}
-        for atomic in (False, True):
-            cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, False, atomic)
+        variants = (("pipeline_3_streams", dict(atomic_gemm=False)),
+                    ("atomic_gemm", dict(atomic_gemm=True)),
+                    ("atomic_gemm_ring_order", dict(atomic_gemm=True, reduce_order="ring")),
+                    ("fused_pipeline_3_streams", dict(atomic_gemm=False, fuse_reduce=True)),
+                    ("fused_atomic_gemm", dict(atomic_gemm=True, fuse_reduce=True)))
+        for name, kw in variants:
+            cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, False, **kw)
             st = _call_stats(lambda: ub.ub_gemm_rs_chunked(h, a_t, w.k, w.k, w_t, w.hidden, o_t, w.hidden, cfg, stream),
                              torch, stream)
-            row["atomic_gemm" if atomic else "pipeline_3_streams"] = _stats_row(f, st, MFMA_PEAK_BF16_TFLOPS)
-        cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, False, True, reduce_order="ring")
-        st = _call_stats(lambda: ub.ub_gemm_rs_chunked(h, a_t, w.k, w.k, w_t, w.hidden, o_t, w.hidden, cfg, stream),
-                         torch, stream)
-        row["atomic_gemm_ring_order"] = _stats_row(f, st, MFMA_PEAK_BF16_TFLOPS)
-        # the sum fused into the slice-GEMM launch (same bits as the separate reduction)
-        for atomic in (False, True):
-            cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, False, atomic, fuse_reduce=True)
-            st = _call_stats(lambda: ub.ub_gemm_rs_chunked(h, a_t, w.k, w.k, w_t, w.hidden, o_t, w.hidden, cfg, stream),
-                             torch, stream)
-            row["fused_atomic_gemm" if atomic else "fused_pipeline_3_streams"] = _stats_row(
-                f, st, MFMA_PEAK_BF16_TFLOPS)
+            row[name] = _stats_row(f, st, MFMA_PEAK_BF16_TFLOPS)
         rbytes = (w.tp + 1) * T * w.hidden * 2.0
         for order in ("ascending", "ring"):
             warm = _time_calls(lambda: ub.ub_reduce_partials(h, o_t, w.hidden, order, stream), torch, stream, 10)
@@ -678,37 +545,6 @@ def secondary(ub, wl, torch, np, dev):
                          "scales, bf16 partials and sum; FLOPs 2 T K H per call; pct_peak of the fp8 peak"}
     ub.ub_destroy(h)
     del ub_t, ws_t, a_t, w_t, o_t, flush, a8, w8
-
-    # GQA bulk sweep on one capacity-32768 buffer, never reallocated
-    w = wl.gqa_bulk()
-    ra, rw, _ = w.seeds()
-    log("secondary gqa_bulk_ag")
-    ub_bytes, _ = ub.ub_required_bytes(w.capacity, w.hidden, w.tp)
-    ub_t = torch.from_numpy(wl.activations(w, w.capacity, ra).view(np.int16).ravel()).to(dev)
-    w_t = torch.from_numpy(wl.weights(w, rw).view(np.int16)).to(dev)
-    c_t = torch.empty((w.capacity, w.n_cols), dtype=torch.int16, device=dev)
-    h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes)
-    res = {}
-    for atomic in (True, False):
-        cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, False, atomic)
-        tot_f = tot_ms = 0.0
-        pts = []
-        for T in wl.gqa_tokens():
-            ub.ub_set_active_shape(h, (T, w.hidden))
-            ms, best, _ = _call_stats(lambda: ub.ub_gemm_ag_chunked(h, w_t, w.n_cols, w.n_cols, c_t, w.n_cols, cfg, stream),
-                                      torch, stream)
-            f = 2.0 * T * w.hidden * w.n_cols
-            if T != 32768:
-                tot_f += f
-                tot_ms += ms
-            pts.append((T, round(f / ms / 1e9, 1), round(f / best / 1e9, 1)))
-        res["atomic_gemm" if atomic else "host_loop"] = {
-            "tflops_sweep": round(tot_f / tot_ms / 1e9, 2),
-            "pct_peak_sweep": round(100 * tot_f / tot_ms / 1e9 / MFMA_PEAK_BF16_TFLOPS, 2),
-            "points_T_tflops_median_best": pts}
-    res["note"] = "per point the median (and best) of 20 calls timed one by one; the sweep is sum FLOPs / sum medians"
-    out["gqa_bulk_ag"] = res
-    ub.ub_destroy(h)
     return out
 
 
@@ -718,12 +554,13 @@ def arrival(ub, wl, torch, np, dev):
     own chunk's event, or (modes *_device_loop) while the one device-side chunk loop's tiles
     wait on per-chunk flags written after each copy.  Sources: pinned host memory (SDMA
     over PCIe, about one xGMI link's rate), device memory by SDMA, device memory by the
-    runtime's copy kernel (host loop only).  Reports the
-    GEMMs alone, the deliveries alone, both overlapped, the fraction of the delivery time
-    hidden behind the GEMMs, the overlap as a fraction of the shorter of the two, the time
-    the call runs past the deliveries alone, and max(GEMMs, deliveries) / overlapped (1.0
-    when the shorter side is wholly hidden; the last chunk's GEMM can only follow its copy,
-    so the bound is a little below 1)."""
+    runtime's copy kernel (host loop only).  Reports the GEMMs alone, the deliveries alone,
+    both overlapped, the fraction of the delivery time hidden behind the GEMMs, the overlap
+    as a fraction of the shorter of the two, the time the call runs past the deliveries
+    alone, and max(GEMMs, deliveries) / overlapped (1.0 when the shorter side is wholly
+    hidden; the last chunk's GEMM can only follow its copy, so the bound is a little
+    below 1).  The handle's streams (two workers and the copy stream) are created right
+    after registration."""
     w = wl.qkv()
     ra, rw, _ = w.seeds()
     log("secondary qkv_arrival")
@@ -734,6 +571,7 @@ def arrival(ub, wl, torch, np, dev):
     w_t = torch.from_numpy(wl.weights(w, rw).view(np.int16)).to(dev)
     c_t = torch.empty((w.capacity, w.n_cols), dtype=torch.int16, device=dev)
     h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes)
+    ub.ub_prepare_streams(h, w.num_max_streams, copy_stream=True)
     stream = torch.cuda.current_stream()
     res = []
     for T in (4096, 6144, 8192):
@@ -813,12 +651,222 @@ def qkv_fp8(ub, wl, torch, np, dev):
             "note": "E4M3 operands, per-tensor scales, bf16 output; device-side chunk loop"}
 
 
-def cpu_baseline(q, min_seconds):
-    """The oracle as it stands, timed on the host cores over the same microbatches (whole
-    microbatches, in order, repeating passes until at least `min_seconds` of work).  Every
-    fourth microbatch of the first pass is also run on the GPU (outside the oracle's timing)
-    and compared with the oracle's output: the bit-equal fraction and the largest error as
-    a fraction of the gate 4e-3 * |a_row| * |w_col|."""
+# ---- profile passes (for rocprofv3) ------------------------------------------------------
+
+def _dispatches(ub, sw, cfg):
+    """Kernel dispatches of one step (a call whose plan is cut launches twice)."""
+    return sum(2 if p[3] >= 0 else 1 for p in sw.plans(cfg))
+
+
+def profile_ag(ub, wl, torch, np, dev, args):
+    """One AG workload's timed region in the device-side loop: warm-up steps, then timed
+    steps with the library's per-launch events."""
+    make = {"gqa": gqa_sweep, "qkv": qkv_step, "fc1": fc1_step}[args.profile_pass]
+    sw = make(ub, wl, torch, np, dev)
+    cfg = sw.cfg(True)
+    per_step = _dispatches(ub, sw, cfg)  # one untimed step that records the plans
+    sec, stats = sw.timed(cfg, args.steps, args.warmup, events=True)
+    alg = sum(sw.alg_bytes(T) for T in sw.Ts)
+    out = {"profile_pass": args.profile_pass, "ms_per_step": round(sec * 1e3, 4),
+           "calls_per_step": len(sw.Ts), "dispatches_per_step": per_step,
+           "timed_calls": args.steps * len(sw.Ts), "timed_dispatches": args.steps * per_step,
+           "timed_gflop": round(args.steps * sw.flops / 1e9, 3),
+           "timed_algorithmic_bytes": round(args.steps * alg),
+           "hip_event_total_ms": round(stats["total_ms"], 4),
+           "src_file": os.path.relpath(GEMM_SRC, ROOT), "src_hash": src_hash(GEMM_SRC)}
+    sw.close()
+    return out
+
+
+def profile_fc2(ub, wl, torch, np, dev, args):
+    """The fc2 RS GEMM (device-side loop, then the pipeline on 3 streams) over its T sweep:
+    per call the slice-GEMM launch and the reduction launch."""
+    w = wl.fc2()
+    ra, rw, _ = w.seeds()
+    ub_bytes, ws_bytes = ub.ub_required_bytes(w.capacity, w.hidden, w.tp)
+    ub_t = torch.empty(w.capacity * w.hidden, dtype=torch.int16, device=dev)
+    ws_t = torch.zeros(ws_bytes // 2, dtype=torch.int16, device=dev)
+    a_t = torch.from_numpy(wl.activations(w, w.capacity, ra).view(np.int16)).to(dev)
+    w_t = torch.from_numpy(wl.weights(w, rw).view(np.int16)).to(dev)
+    o_t = torch.empty((w.capacity, w.hidden), dtype=torch.int16, device=dev)
+    h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes, ws_t, ws_bytes)
+    ub.ub_prepare_streams(h, w.num_max_streams)
+    stream = torch.cuda.current_stream()
+    out = {"profile_pass": "fc2", "T": list(wl.FC2_TOKENS), "modes": []}
+    for atomic in (True, False):
+        cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, False, atomic)
+
+        def step():
+            for T in wl.FC2_TOKENS:
+                ub.ub_set_active_shape(h, (T, w.hidden))
+                ub.ub_gemm_rs_chunked(h, a_t, w.k, w.k, w_t, w.hidden, o_t, w.hidden, cfg, stream)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ub.ub_set_kernel_timing(h, True)
+        ub.ub_get_kernel_timing(h)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / args.steps
+        gs, rs = ub.ub_get_kernel_timing(h)
+        ub.ub_set_kernel_timing(h, False)
+        flops = sum(2.0 * T * w.k * w.hidden for T in wl.FC2_TOKENS)
+        out["modes"].append({"mode": "atomic_gemm" if atomic else "pipeline_3_streams",
+                             "ms_per_step": round(sec * 1e3, 4), "tflops_step": round(flops / sec / 1e12, 2),
+                             "gemm_launches": gs["launches"], "gemm_event_ms": round(gs["total_ms"], 4),
+                             "reduce_launches": rs["launches"], "reduce_event_ms": round(rs["total_ms"], 4),
+                             "timed_gflop": round(args.steps * flops / 1e9, 3)})
+        torch.cuda.synchronize()
+        time.sleep(0.05)  # the two modes stand apart on the timeline
+    out["src_file"] = os.path.relpath(GEMM_SRC, ROOT)
+    out["src_hash"] = src_hash(GEMM_SRC)
+    ub.ub_destroy(h)
+    return out
+
+
+def profile_reduce(ub, wl, torch, np, dev, args):
+    """The fc2 reduction at T = 16384 (8 bf16 partial slots of [16384, 4096]): warm-up
+    launches, then timed launches with per-launch events; ascending order first, then ring
+    order."""
+    w = wl.fc2()
+    ra, rw, _ = w.seeds()
+    T = wl.FC2_TOKENS[-1]
+    ub_bytes, ws_bytes = ub.ub_required_bytes(w.capacity, w.hidden, w.tp)
+    ub_t = torch.empty(w.capacity * w.hidden, dtype=torch.int16, device=dev)
+    ws_t = torch.zeros(ws_bytes // 2, dtype=torch.int16, device=dev)
+    a_t = torch.from_numpy(wl.activations(w, T, ra).view(np.int16)).to(dev)
+    w_t = torch.from_numpy(wl.weights(w, rw).view(np.int16)).to(dev)
+    o_t = torch.empty((w.capacity, w.hidden), dtype=torch.int16, device=dev)
+    h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes, ws_t, ws_bytes)
+    ub.ub_set_active_shape(h, (T, w.hidden))
+    ub.ub_gemm_rs_chunked(h, a_t, w.k, w.k, w_t, w.hidden, o_t, w.hidden,
+                          ub.make_cfg(w.method, w.num_splits, atomic_gemm=True))
+    stream = torch.cuda.current_stream()
+    out = {"profile_pass": "reduce", "T": T, "launches_per_order": args.warmup + args.steps}
+    for order in ("ascending", "ring"):
+        fn = lambda: ub.ub_reduce_partials(h, o_t, w.hidden, order, stream)
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ub.ub_set_kernel_timing(h, True)
+        ub.ub_get_kernel_timing(h)
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        rs = ub.ub_get_kernel_timing(h)[1]
+        ub.ub_set_kernel_timing(h, False)
+        n = max(1, rs["launches"])
+        out[order] = {"avg_launch_us_hip_events": round(rs["total_ms"] * 1e3 / n, 3),
+                      "algorithmic_bytes_per_launch": round(rs["bytes"] / n),
+                      "gbs_hip_events": round(rs["bytes"] / (rs["total_ms"] / 1e3) / 1e9, 1),
+                      "timed_dispatches": args.steps,
+                      "timed_algorithmic_bytes": round(rs["bytes"]),
+                      "hip_event_total_ms": round(rs["total_ms"], 4)}
+    out["src_file"] = os.path.relpath(REDUCE_SRC, ROOT)
+    out["src_hash"] = src_hash(REDUCE_SRC)
+    ub.ub_destroy(h)
+    return out
+
+
+ARRIVAL_MODES = (("host_loop_pinned_host", True, True, False),
+                 ("host_loop_device_sdma", True, False, False),
+                 ("host_loop_device_copy_kernel", False, False, False),
+                 ("device_loop_pinned_host", True, True, True),
+                 ("device_loop_device_sdma", True, False, True))
+
+
+def profile_arrival(ub, wl, torch, np, dev, args):
+    """Arrival stand-in on qkv at T = 8192 (ring, rank 0, 3 streams), for a rocprofv3
+    kernel and memory-copy trace: per mode (host loop or device-side loop; pinned-host,
+    device SDMA or copy-kernel source) `steps` calls, each followed by a device
+    synchronisation and a 20 ms pause, so that every call stands alone on the timeline.
+    Prints the modes in trace order."""
+    w = wl.qkv()
+    ra, rw, _ = w.seeds()
+    T = w.capacity
+    ub_bytes, _ = ub.ub_required_bytes(w.capacity, w.hidden, w.tp)
+    ub_t = torch.from_numpy(wl.activations(w, w.capacity, ra).view(np.int16).ravel()).to(dev)
+    src = ub_t.clone()
+    src_host = ub_t.cpu().pin_memory()
+    w_t = torch.from_numpy(wl.weights(w, rw).view(np.int16)).to(dev)
+    c_t = torch.empty((w.capacity, w.n_cols), dtype=torch.int16, device=dev)
+    h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes)
+    ub.ub_prepare_streams(h, w.num_max_streams, copy_stream=True)
+    ub.ub_set_active_shape(h, (T, w.hidden))
+    torch.cuda.synchronize()
+    time.sleep(0.05)  # the uploads above stand apart from the first call on the timeline
+    modes = []
+    for name, use_ce, host, atomic in ARRIVAL_MODES:
+        cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, use_ce=use_ce, rank=0,
+                          atomic_gemm=atomic)
+        sb = src_host if host else src
+        for _ in range(args.steps):
+            ub.ub_gemm_ag_arrival(h, sb, w_t, w.n_cols, w.n_cols, c_t, w.n_cols, cfg)
+            torch.cuda.synchronize()
+            time.sleep(0.02)
+        modes.append({"mode": name, "calls": args.steps})
+    timeouts = ub.ub_arrival_timeouts(h)
+    ub.ub_destroy(h)
+    return {"profile_pass": "arrival", "T": T, "chunks": w.tp, "modes": modes,
+            "timeouts": timeouts, "gpu_max_hw_queues": os.environ.get("GPU_MAX_HW_QUEUES", "(runtime default)")}
+
+
+def profile_fp8(ub, wl, torch, np, dev, args):
+    """The qkv step on an fp8 buffer (see qkv_fp8): warm-up steps, then timed steps with
+    per-launch events."""
+    w = wl.qkv()
+    ra, rw, rt = w.seeds()
+    Ts, _ = wl.qkv_pack_tokens(rt)
+    H, N = w.hidden, w.n_cols
+    x = torch.from_numpy(wl.activations(w, w.capacity, ra).view(np.int16)).to(dev)
+    wt = torch.from_numpy(wl.weights(w, rw).view(np.int16)).to(dev)
+    sx = 448.0 / float(x.view(torch.bfloat16).float().abs().max())
+    sw = 448.0 / float(wt.view(torch.bfloat16).float().abs().max())
+    ub_t = torch.empty(w.capacity * H, dtype=torch.uint8, device=dev)
+    h = ub.ub_init(w.capacity, H, w.tp, ub.UB_DTYPE_FP8_E4M3, ub_t, w.capacity * H)
+    w8 = torch.empty(N * H, dtype=torch.uint8, device=dev)
+    hw = ub.ub_init(N, H, 1, ub.UB_DTYPE_FP8_E4M3, w8, N * H)
+    ub.ub_quantize_in(hw, wt.t().contiguous(), N, 0, sw)
+    ub.ub_quantize_in(h, x, w.capacity, 0, sx)
+    cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, w.aggregate, True)
+    c_t = torch.empty((w.capacity, N), dtype=torch.int16, device=dev)
+
+    def step():
+        for T in Ts:
+            ub.ub_set_active_shape(h, (T, H))
+            ub.ub_gemm_ag_chunked_fp8(h, w8, N, H, 1.0 / sx, 1.0 / sw, c_t, N, cfg)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ub.ub_set_kernel_timing(h, True)
+    ub.ub_get_kernel_timing(h)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    gs = ub.ub_get_kernel_timing(h)[0]
+    ub.ub_destroy(h)
+    ub.ub_destroy(hw)
+    src = os.path.join(ROOT, "chunked_tp_overlap_amd", "csrc", "gemm_fp8.hip")
+    flops = sum(2.0 * T * H * N for T in Ts)
+    return {"profile_pass": "fp8", "timed_dispatches": args.steps * len(Ts),
+            "timed_gflop": round(args.steps * flops / 1e9, 3),
+            "timed_algorithmic_bytes": round(gs["bytes"]), "hip_event_total_ms": round(gs["total_ms"], 4),
+            "src_file": os.path.relpath(src, ROOT), "src_hash": src_hash(src)}
+
+
+# ---- CPU baseline ------------------------------------------------------------------------
+
+def cpu_baseline(sw, min_seconds):
+    """The oracle as it stands, timed on the host cores over a bounded sample of the
+    headline sweep: whole points of it (every 4th T, then the rest in order), until at
+    least `min_seconds` of oracle work.  Each sampled point is also run on the GPU (outside
+    the oracle's timing) and compared with the oracle's output element by element: the
+    bit-equal fraction and the largest error as a fraction of the gate
+    4e-3 * |a_row| * |w_col|."""
     import numpy as np
 
     from oracle import bf16 as ob
@@ -826,11 +874,10 @@ def cpu_baseline(q, min_seconds):
     from oracle import manager as om
     from oracle import plan as op
 
-    ub, torch = q.ub, q.torch
-    gpu_cfg = q.cfg(atomic=True)
-    w_cols = np.linalg.norm(ob.decode(q.w_host), axis=0)
-    parity = {"microbatches": 0, "elements": 0, "bit_equal": 0, "max_err_over_gate": 0.0}
-
+    ub, torch = sw.ub, sw.torch
+    gpu_cfg = sw.cfg(True)
+    w_cols = np.linalg.norm(ob.decode(sw.w_host), axis=0)
+    parity = {"points": 0, "elements": 0, "bit_equal": 0, "max_err_over_gate": 0.0}
     blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
@@ -840,45 +887,43 @@ def cpu_baseline(q, min_seconds):
                          for i in libs) or "none found"
     except Exception:  # threadpoolctl missing: report the core count
         threads = os.cpu_count()
-    w = q.w
+    w = sw.w
     model = om.UserBufferModel(w.capacity, w.hidden, w.tp)
     cfg = op.OverlapCfg(method=w.method, num_splits=w.num_splits,
                         num_max_streams=w.num_max_streams, aggregate=w.aggregate, atomic_gemm=True)
     c = np.empty((w.capacity, w.n_cols), np.uint16)
+    order = sw.Ts[::4] + [T for i, T in enumerate(sw.Ts) if i % 4]
     flops = elapsed = 0.0
-    done = 0
-    while elapsed < min_seconds:
-        for T in q.Ts:
-            model.set_active_shape((T, w.hidden))
-            model.fill_active(q.a_host[:T])
-            t0 = time.perf_counter()
-            og.ag_chunked(model, q.w_host, w.n_cols, w.n_cols, c, w.n_cols, cfg)
-            elapsed += time.perf_counter() - t0
-            flops += 2.0 * T * w.hidden * w.n_cols
-            if done < len(q.Ts) and done % 4 == 0:  # parity of this microbatch, untimed
-                ub.ub_set_active_shape(q.h, (T, w.hidden))
-                ub.ub_gemm_ag_chunked(q.h, q.w_t, w.n_cols, w.n_cols, q.c_t, w.n_cols, gpu_cfg, q.stream)
-                torch.cuda.synchronize()
-                g = q.c_t[:T].cpu().numpy().view(np.uint16)
-                err = np.abs(ob.decode(g) - ob.decode(c[:T]))
-                gate = 4e-3 * np.outer(np.linalg.norm(ob.decode(q.a_host[:T]), axis=1), w_cols)
-                parity["microbatches"] += 1
-                parity["elements"] += int(g.size)
-                parity["bit_equal"] += int(np.sum(g == c[:T]))
-                parity["max_err_over_gate"] = max(parity["max_err_over_gate"], float(np.max(err / gate)))
-            done += 1
-            if elapsed >= min_seconds and done >= len(q.Ts):
-                break
-        log(f"cpu oracle: {done} microbatches, {elapsed:.1f} s")
+    done = []
+    for T in order:
+        if elapsed >= min_seconds:
+            break
+        model.set_active_shape((T, w.hidden))
+        model.fill_active(sw.a_host[:T])
+        t0 = time.perf_counter()
+        og.ag_chunked(model, sw.w_host, w.n_cols, w.n_cols, c, w.n_cols, cfg)
+        elapsed += time.perf_counter() - t0
+        flops += sw.flop(T)
+        done.append(T)
+        sw.call(T, gpu_cfg)  # parity of this point, untimed
+        torch.cuda.synchronize()
+        g = sw.c_t[:T].cpu().numpy().view(np.uint16)
+        err = np.abs(ob.decode(g) - ob.decode(c[:T]))
+        gate = 4e-3 * np.outer(np.linalg.norm(ob.decode(sw.a_host[:T]), axis=1), w_cols)
+        parity["points"] += 1
+        parity["elements"] += int(g.size)
+        parity["bit_equal"] += int(np.sum(g == c[:T]))
+        parity["max_err_over_gate"] = max(parity["max_err_over_gate"], float(np.max(err / gate)))
+        log(f"cpu oracle: T={T}, {elapsed:.1f} s so far")
     return {"value": round(flops / elapsed / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{done} qkv microbatches ({done / len(q.Ts):.2f} passes over the 32 of one "
-                      f"step), numpy fp64 chunked GEMM + bf16 RNE, {elapsed:.1f} s",
+            "sample": f"{len(done)} points of the GQA sweep (T = {done}), whole points, numpy fp64 "
+                      f"chunked GEMM + bf16 RNE over the capacity-buffer model, {elapsed:.1f} s",
             "host_cpus": os.cpu_count(), "blas": blas,
-            "parity": {"microbatches": parity["microbatches"], "elements": parity["elements"],
+            "parity": {"points": parity["points"], "elements": parity["elements"],
                        "bit_equal_fraction": round(parity["bit_equal"] / max(1, parity["elements"]), 5),
                        "max_err_over_gate": round(parity["max_err_over_gate"], 5),
-                       "note": "device-side chunk loop vs the oracle on every 4th microbatch of one step"}}
+                       "note": "device-side chunk loop vs the oracle on every sampled point"}}
 
 
 if __name__ == "__main__":

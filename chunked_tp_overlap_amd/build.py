@@ -18,10 +18,6 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libub.so")
-# Calibration programs (not part of the library): the matrix cores' throughput under the
-# power limit with no memory work, at a chosen number of busy CUs; and the HBM bandwidth of
-# the reduce-scatter sum's access pattern with no arithmetic.
-CALIB_PROGRAMS = ("mfma_ceiling", "hbm_ceiling")
 
 SOURCES = ["ub_api.cpp", "ub_plan.cpp", "gemm_bf16.hip", "gemm_fp8.hip", "quantize_fp8.hip",
            "reduce_partials.hip"]
@@ -79,23 +75,7 @@ def build(verbose=False):
     if res.returncode != 0:
         raise RuntimeError(f"linking libub.so failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
-    build_calibration(verbose)
     return LIB_PATH
-
-
-def build_calibration(verbose=False):
-    """Compile the calibration programs ``lib/mfma_ceiling`` and ``lib/hbm_ceiling``."""
-    for name in CALIB_PROGRAMS:
-        src = os.path.join(PKG, "calib", name + ".hip")
-        exe = os.path.join(LIB_DIR, name)
-        tmp = exe + ".tmp"
-        cmd = [hipcc(), *COMMON, "-x", "hip", *DEVICE, src, "-o", tmp]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        if res.returncode != 0:
-            raise RuntimeError(f"compiling {src} failed:\n{res.stdout}\n{res.stderr}")
-        os.replace(tmp, exe)
 
 
 if __name__ == "__main__":

@@ -104,25 +104,28 @@ constexpr uint64_t kReadyTimeoutTicks = 50000000ull;  // 0.5 s of the 100 MHz s_
 // Arrival gating: wait until every chunk holding a row of [r0, r1) has been delivered
 // (its flag equals the call's epoch; the copy stream writes it after the chunk's copy),
 // then acquire at system scope so that the A loads see the delivered rows rather than
-// lines cached before they arrived.  The wait is bounded in time: past the bound the wave
-// counts a timeout and goes on, so every wave ends.
-__device__ inline void wait_ready(const Params& p, int r0, int r1) {
+// lines cached before they arrived.  The wait is bounded in time, so every wave ends.
+// Returns, to every wave of the workgroup alike, whether some wave ran past the bound; the
+// workgroup then counts one timeout and stores NaN instead of computing its tile.
+__device__ inline bool wait_ready(const Params& p, int r0, int r1) {
   int c = 0;
   while (c + 1 < p.n_chunks && p.chunk_row0[c + 1] <= r0) ++c;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  bool late = false;
+  int late = 0;
   for (; !late && c < p.n_chunks && p.chunk_row0[c] < r1; ++c) {
     while (__hip_atomic_load(p.ready + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != p.epoch) {
       if (__builtin_amdgcn_s_memrealtime() - t0 > p.wait_ticks) {
-        late = true;
+        late = 1;
         break;
       }
       __builtin_amdgcn_s_sleep(8);
     }
   }
-  if (late && (threadIdx.x & 63) == 0)
+  late = __syncthreads_or(late);
+  if (late && threadIdx.x == 0)
     __hip_atomic_fetch_add(p.timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+  return late != 0;
 }
 
 // ---- fused reduction arithmetic (the same operations as the separate reduction kernel) --
@@ -178,29 +181,28 @@ struct Cfg {
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int NA_ALL = A_BYTES / 1024;     // 1 KB direct loads per step, A
   static constexpr int NB_ALL = B_BYTES / 1024;     // and B
-  // Loads per wave of group 0 (waves 0-3) and of group 1 (waves 4-7).  When both operands
-  // split evenly over all waves every wave takes its share of each; otherwise (a 192-row
-  // A tile: 12 loads) group 0 takes all of B and group 1 all of A.
-  static constexpr bool EVEN = NA_ALL % NW == 0 && NB_ALL % NW == 0;
-  static constexpr int NA0 = EVEN ? NA_ALL / NW : 0;
-  static constexpr int NB0 = EVEN ? NB_ALL / NW : NB_ALL / 4;
-  static constexpr int NA1 = EVEN ? NA_ALL / NW : NA_ALL / 4;
-  static constexpr int NB1 = EVEN ? NB_ALL / NW : 0;
-  static constexpr int L0 = NA0 + NB0;              // loads per wave per step, group 0
-  static constexpr int L1 = NA1 + NB1;              // and group 1
-  static constexpr int NA_MAX = NA0 > NA1 ? NA0 : NA1;
-  static constexpr int NB_MAX = NB0 > NB1 ? NB0 : NB1;
+  // The step's NL loads, B's first, are dealt round-robin over the waves: wave w issues
+  // loads w, w + NW, w + 2 NW, ...  B's loads fill whole rounds of NW, so every wave's
+  // load slot j is of the same operand.  The first NFULL waves issue LMAX loads per step,
+  // the others LMAX - 1 (the last slot, an A load); each wave waits on its own count.
+  static constexpr int NL = NA_ALL + NB_ALL;
+  static constexpr int LMAX = (NL + NW - 1) / NW;
+  static constexpr int NFULL = NL % NW == 0 ? NW : NL % NW;
   static constexpr int A_ROWS_PER_LOAD = 1024 / A_ROW;
   static constexpr int B_ROWS_PER_LOAD = 1024 / B_ROW;
   static constexpr int LDC = BN + 8;                // epilogue tile row (elements)
-  static constexpr int EPI = BM * LDC * 2;
+  // The epilogue stages the bf16 tile in LDS: in one pass, or, when the whole tile does not
+  // fit in 160 KiB, one pass per wave row.
+  static constexpr int EPI_PASSES = BM * LDC * 2 <= 160 * 1024 ? 1 : WGM;
+  static constexpr int EPI = (BM / EPI_PASSES) * LDC * 2;
   static constexpr int LDS_BYTES = (S * STAGE > EPI) ? S * STAGE : EPI;
-  static_assert(EVEN ? (NA0 >= 1 && NB0 >= 1)
-                     : (NW == 8 && NA_ALL % 4 == 0 && NB_ALL % 4 == 0 && NA1 >= 1 && NB0 >= 1),
-                "direct loads do not split over the waves");
+  static_assert(NW == 8 || NL % NW == 0, "four-wave tiles split the loads evenly");
+  static_assert(NB_ALL % NW == 0, "B loads fill whole rounds of the waves");
   static_assert(FM >= 1 && FN >= 1 && SUBS >= 1, "wave tile below one 16x16 block");
   static_assert(WM % 16 == 0 && WN % 16 == 0 && BK % 32 == 0, "whole 16x16x32 blocks");
-  static_assert(S * L0 <= 63 && S * L1 <= 63, "vmcnt is a 6-bit count");
+  static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "whole 1 KB loads");
+  static_assert(1024 % A_ROW == 0 && 1024 % B_ROW == 0, "a load covers whole rows");
+  static_assert(S * LMAX <= 63, "vmcnt is a 6-bit count");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS is 160 KiB per CU");
 };
 
@@ -210,11 +212,18 @@ template <class C>
 struct Tile {
   int lane, wave, group, wm, wn, m0, m_end, n0;
   int tile, z;                           // tile of the launch and batch entry
+  int nl;                                // direct loads this wave issues per step
   uint16_t* cg;
   i32x4 ra, rb;
-  uint32_t a_off[C::NA_MAX > 0 ? C::NA_MAX : 1], b_off[C::NB_MAX > 0 ? C::NB_MAX : 1];
-  uint32_t a_lds, b_lds;                 // LDS byte offset of this wave's first A / B load
+  // Load slot j of this wave is load w + NW j of the step: B load w + NW j for the first
+  // NB_ALL / NW slots, then A load w + NW j - NB_ALL (a compile-time kind per slot keeps
+  // the issue code free of branches and selects).
+  static constexpr bool slot_is_a(int j) { return j * C::NW >= C::NB_ALL; }
+  uint32_t lds_off[C::LMAX];             // byte offset in a stage
+  uint32_t off[C::LMAX];                 // per-lane byte offset of step 0 (OOB: none)
+  uint32_t tail_mask[C::LMAX];           // OOB for A chunks past k in the last step, else 0
   uint32_t a_kstep, b_kstep;
+  int k_tail_step;                       // the step whose A chunks past k are masked, or -1
   int a_rd_row, a_rd_c, a_rd_x, b_krow, b_col_chunk, b_x, b_in;
 
   // false: this workgroup has no tile (the whole workgroup returns before any barrier)
@@ -232,40 +241,42 @@ struct Tile {
     const uint16_t* A = p.a + z * p.sa + (int64_t)m0 * p.lda;
     const uint16_t* B = p.b + z * p.sb + n0;
     cg = p.c + z * p.sc;
-    // A from this tile's first row, valid rows only; B from column n0 of the batch entry
+    // A from this tile's first row, valid rows only; B from column n0 of the batch entry,
+    // k rows only (rows past k read zeros)
     const int rows_valid = min(C::BM, m_end - m0);
     ra = make_rsrc(A, (uint32_t)(rows_valid * p.lda * 2));
     rb = make_rsrc(B, (uint32_t)(((int64_t)p.k * p.ldb - n0) * 2));
-    // Direct loads of this wave: A loads ia0 .. ia0+na-1 and B loads ib0 .. ib0+nb-1 of the
-    // step.  A load i covers rows A_ROWS_PER_LOAD*i + lane/A_CPR, slot lane%A_CPR holding
-    // k-chunk slot ^ a_swz(row); B load i covers k-rows B_ROWS_PER_LOAD*i + lane/B_CPR, slot
-    // lane%B_CPR holding column chunk slot ^ b_swz(krow).  Load i of an operand lands at
-    // byte 1024*i of that operand's part of the stage.
-    const int w4 = wave - 4 * group;
-    const int na = group == 0 ? C::NA0 : C::NA1;
-    const int nb = group == 0 ? C::NB0 : C::NB1;
-    const int ia0 = group == 0 ? wave * C::NA0 : 4 * C::NA0 + w4 * C::NA1;
-    const int ib0 = group == 0 ? wave * C::NB0 : 4 * C::NB0 + w4 * C::NB1;
-    a_lds = (uint32_t)ia0 * 1024;
-    b_lds = (uint32_t)(C::A_BYTES + ib0 * 1024);
+    // Direct loads: A load i covers rows A_ROWS_PER_LOAD*i + lane/A_CPR, slot lane%A_CPR
+    // holding k-chunk slot ^ a_swz(row); B load i covers k-rows B_ROWS_PER_LOAD*i +
+    // lane/B_CPR, slot lane%B_CPR holding column chunk slot ^ b_swz(krow).  Load i of an
+    // operand lands at byte 1024*i of that operand's part of the stage.
+    nl = wave < C::NFULL ? C::LMAX : C::LMAX - 1;
+    k_tail_step = p.k % C::BK ? p.k / C::BK : -1;
+    const int k_tail = p.k - (p.k / C::BK) * C::BK;  // valid k of the last step (if partial)
 #pragma unroll
-    for (int t = 0; t < C::NA_MAX; ++t) {
-      const int row = C::A_ROWS_PER_LOAD * (ia0 + t) + lane / C::A_CPR;
-      const int chunk = (lane % C::A_CPR) ^ a_swz<C::A_CPR>(row);
-      a_off[t] = t < na ? (uint32_t)((row * p.lda + chunk * 8) * 2) : OOB;
-    }
-#pragma unroll
-    for (int t = 0; t < C::NB_MAX; ++t) {
-      const int krow = C::B_ROWS_PER_LOAD * (ib0 + t) + lane / C::B_CPR;
-      const int chunk = (lane % C::B_CPR) ^ b_swz(krow);
-      const bool ok = t < nb && n0 + chunk * 8 < p.n;
-      b_off[t] = ok ? (uint32_t)((krow * p.ldb + chunk * 8) * 2) : OOB;
+    for (int j = 0; j < C::LMAX; ++j) {
+      const int li = wave + C::NW * j;
+      const int idx = slot_is_a(j) ? li - C::NB_ALL : li;
+      tail_mask[j] = 0;
+      if (slot_is_a(j)) {
+        const int row = C::A_ROWS_PER_LOAD * idx + lane / C::A_CPR;
+        const int chunk = (lane % C::A_CPR) ^ a_swz<C::A_CPR>(row);
+        lds_off[j] = (uint32_t)idx * 1024;
+        off[j] = (uint32_t)((row * p.lda + chunk * 8) * 2);
+        if (k_tail_step >= 0 && chunk * 8 >= k_tail) tail_mask[j] = OOB;
+      } else {
+        const int krow = C::B_ROWS_PER_LOAD * idx + lane / C::B_CPR;
+        const int chunk = (lane % C::B_CPR) ^ b_swz(krow);
+        lds_off[j] = (uint32_t)(C::A_BYTES + idx * 1024);
+        off[j] = n0 + chunk * 8 < p.n ? (uint32_t)((krow * p.ldb + chunk * 8) * 2) : OOB;
+      }
+      if (j >= nl) off[j] = OOB;
     }
     a_kstep = C::BK * 2;
     b_kstep = (uint32_t)(C::BK * p.ldb * 2);
-    // Fragment reads.  A: row R = wm*WM + i*32 + (lane&31), k-chunk (kk/8 + lane/32) in slot
-    // ^ a_swz(R) (a function of lane&31 only).  B: k-row kk + (lane/32)*8 + (lane>>2)&3
-    // (+4 for the second read), column wn*WN + j*32 + ((lane>>4)&1)*16 + (lane&3)*4.
+    // Fragment reads.  A: row R = wm*WM + i*16 + (lane&15), k-chunk (kk/8 + lane/16) in
+    // slot ^ a_swz(R) (a function of lane&15 only).  B: k-row kk + (lane/16)*8 + (lane>>2)&3
+    // (+4 for the second read), column wn*WN + j*16 + (lane&3)*4.
     a_rd_row = (wm * C::WM + (lane & 15)) * C::A_ROW;
     a_rd_c = lane >> 4;
     a_rd_x = a_swz<C::A_CPR>(lane & 15);
@@ -277,28 +288,27 @@ struct Tile {
     return true;
   }
 
-  // This wave's direct loads of step ks into stage ks % S: NA_ A loads and NB_ B loads
-  // (its group's counts).  Steps past the end are issued with out-of-range offsets (they
-  // write zeros and touch no memory) so that every wait can count a fixed number of newer
-  // loads; so are B chunks past column n.
-  template <int NA_, int NB_>
-  __device__ inline void issue_group(unsigned char* smem, int ks, int nk) const {
-    unsigned char* st = smem + (ks % C::S) * C::STAGE;
-    const bool live = ks < nk;
+  // This wave's direct loads of step ks into stage ks % S.  Steps past the end are issued
+  // with out-of-range offsets (they write zeros and touch no memory) so that every wait
+  // can count a fixed number of newer loads; so are B chunks past column n, and, in the
+  // last step of a k that is not a multiple of BK, A chunks past k (B rows past k are past
+  // the B resource).  An offset is made out of range by setting its top bit: every
+  // in-range offset is below 2^31 - 64 (gemm_shape_supported), so the result stays out of
+  // range without wrapping.  No branches and no selects on the wave: the memory cluster
+  // is the kernel's critical path.
+  __device__ inline void issue_loads(unsigned char* smem, int ks, int nk) const {
+    const uint32_t st = lds_addr(smem) + (uint32_t)((ks % C::S) * C::STAGE);
+    const uint32_t dead = ks < nk ? 0u : OOB;
+    const uint32_t tail = ks == k_tail_step ? ~0u : 0u;
     const uint32_t ak = (uint32_t)ks * a_kstep, bk = (uint32_t)ks * b_kstep;
 #pragma unroll
-    for (int t = 0; t < NA_; ++t)
-      dma16(ra, lds_addr(st + a_lds + t * 1024), live ? a_off[t] + ak : OOB);
-#pragma unroll
-    for (int t = 0; t < NB_; ++t)
-      dma16(rb, lds_addr(st + b_lds + t * 1024), (live && b_off[t] != OOB) ? b_off[t] + bk : OOB);
-  }
-
-  __device__ inline void issue_loads(unsigned char* smem, int ks, int nk) const {
-    if (C::EVEN || group == 0)
-      issue_group<C::NA0, C::NB0>(smem, ks, nk);
-    else
-      issue_group<C::NA1, C::NB1>(smem, ks, nk);
+    for (int j = 0; j < C::LMAX; ++j) {
+      if (j + 1 == C::LMAX && C::LMAX * C::NW != C::NL && j >= nl) break;
+      if (slot_is_a(j))
+        dma16(ra, st + lds_off[j], ((off[j] + ak) | dead) | (tail_mask[j] & tail));
+      else
+        dma16(rb, st + lds_off[j], (off[j] + bk) | dead);
+    }
   }
 
   __device__ inline void read_frags(const unsigned char* smem, int ks, int kk, bf16x8* af,
@@ -320,34 +330,56 @@ struct Tile {
   }
 
   // bf16 tile in LDS (the caller guarantees no wave still reads or loads into LDS), then
-  // 16-byte coalesced stores.  16x16 accumulator layout: lane holds column (lane & 15);
-  // element e holds row 4*(lane/16) + e.
+  // 16-byte coalesced stores; in EPI_PASSES passes of BM / EPI_PASSES rows (one per wave
+  // row when the whole tile does not fit in LDS).  16x16 accumulator layout: lane holds
+  // column (lane & 15); element e holds row 4*(lane/16) + e.
   __device__ inline void store(unsigned char* smem, const Params& p, int tid,
                                const f32x4 (&acc)[C::FM][C::FN]) const {
     uint16_t* ct = reinterpret_cast<uint16_t*>(smem);
+    constexpr int PR = C::BM / C::EPI_PASSES;  // rows per pass
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+    for (int pass = 0; pass < C::EPI_PASSES; ++pass) {
+      if (pass > 0) __syncthreads();  // the previous pass's reads of the LDS tile are done
+      if (C::EPI_PASSES == 1 || wm == pass) {
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        const int col = wn * C::WN + j * 16 + (lane & 15);
-        const int row = wm * C::WM + i * 16 + (lane >> 4) * 4;
+        for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          const uint32_t v = pack_bf16x2(acc[i][j][e], acc[i][j][e + 1]);
-          *LDS_PTR(uint16_t, ct + (row + e) * C::LDC + col) = (uint16_t)(v & 0xFFFF);
-          *LDS_PTR(uint16_t, ct + (row + e + 1) * C::LDC + col) = (uint16_t)(v >> 16);
-        }
+          for (int j = 0; j < C::FN; ++j) {
+            const int col = wn * C::WN + j * 16 + (lane & 15);
+            const int row = (C::EPI_PASSES == 1 ? wm * C::WM : 0) + i * 16 + (lane >> 4) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; e += 2) {
+              const uint32_t v = pack_bf16x2(acc[i][j][e], acc[i][j][e + 1]);
+              *LDS_PTR(uint16_t, ct + (row + e) * C::LDC + col) = (uint16_t)(v & 0xFFFF);
+              *LDS_PTR(uint16_t, ct + (row + e + 1) * C::LDC + col) = (uint16_t)(v >> 16);
+            }
+          }
       }
-    __syncthreads();
-    constexpr int VPR = C::BN / 8;  // 16-byte vectors per tile row
+      __syncthreads();
+      constexpr int VPR = C::BN / 8;  // 16-byte vectors per tile row
+      static_assert(PR * VPR % C::THREADS == 0, "whole vectors per lane");
 #pragma unroll
-    for (int i = 0; i < C::BM * VPR / C::THREADS; ++i) {
-      const int v = tid + i * C::THREADS;
+      for (int i = 0; i < PR * VPR / C::THREADS; ++i) {
+        const int v = tid + i * C::THREADS;
+        const int r = v / VPR, cc = (v % VPR) * 8;
+        const int gr = m0 + pass * PR + r, gc = n0 + cc;
+        if (gr < m_end && gc < p.n)
+          *GLOBAL_PTR(u32x4, cg + (int64_t)gr * p.ldc + gc) =
+              *LDS_PTR(const u32x4, ct + r * C::LDC + cc);
+      }
+    }
+  }
+
+  // The tile's output as bf16 quiet NaNs (0x7FC0): what a tile stores when its arrival wait
+  // ran out, so that rows computed from data that may not have arrived cannot pass for
+  // results.
+  __device__ inline void store_nan(const Params& p, int tid) const {
+    constexpr int VPR = C::BN / 8;
+    const u32x4 nan4 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+    for (int v = tid; v < C::BM * VPR; v += C::THREADS) {
       const int r = v / VPR, cc = (v % VPR) * 8;
       const int gr = m0 + r, gc = n0 + cc;
-      if (gr < m_end && gc < p.n)
-        *GLOBAL_PTR(u32x4, cg + (int64_t)gr * p.ldc + gc) =
-            *LDS_PTR(const u32x4, ct + r * C::LDC + cc);
+      if (gr < m_end && gc < p.n) *GLOBAL_PTR(u32x4, cg + (int64_t)gr * p.ldc + gc) = nan4;
     }
   }
 
@@ -467,9 +499,29 @@ __device__ inline void mfma_block(f32x4 (&acc)[C::FM][C::FN], const bf16x8* af, 
 //  - stage reuse: step ks+D goes into the stage of step ks+D-S, whose last reader finished
 //    before b(2(ks+D-S)+2) <= b(2ks) because D <= S-1;
 //  - landing: before b(2ks+2) each wave waits for its own loads of step ks+1 (issued D-1
-//    memory clusters earlier, so (D-1)*L newer loads may stay in flight): group 1 at the
-//    end of its memory cluster, group 0 at the end of its compute cluster;
+//    memory clusters earlier, so (D-1)*L newer loads may stay in flight, L = this wave's
+//    loads per step): group 1 at the end of its memory cluster, group 0 at the end of its
+//    compute cluster;
 //  - every wave executes the same number of barriers (2*nk + 4).
+
+// s_waitcnt for this wave's loads: at most (D-1) steps' worth (LMAX or LMAX-1 per step) in
+// flight, optionally with the LDS reads drained, then the workgroup barrier.
+template <class C, int D, bool LGKM>
+__device__ inline void wait_loads_barrier(bool full) {
+  if (full) {
+    if (LGKM)
+      __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((D - 1) * C::LMAX) : "memory");
+    else
+      __asm__ volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((D - 1) * C::LMAX) : "memory");
+  } else {
+    constexpr int L = C::LMAX > 1 ? C::LMAX - 1 : 1;
+    if (LGKM)
+      __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((D - 1) * L) : "memory");
+    else
+      __asm__ volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((D - 1) * L) : "memory");
+  }
+}
+
 template <class C, int D>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_pingpong(Params p) {
@@ -479,8 +531,12 @@ void gemm_bf16_pingpong(Params p) {
   const int tid = threadIdx.x;
   Tile<C> t;
   if (!t.init(p, tid)) return;
-  if (p.ready) wait_ready(p, t.m0, min(t.m0 + C::BM, t.m_end));
+  if (p.ready && wait_ready(p, t.m0, min(t.m0 + C::BM, t.m_end))) {
+    t.store_nan(p, tid);
+    return;
+  }
   const int group = t.group;
+  const bool full = C::NFULL == C::NW || t.nl == C::LMAX;
 
   f32x4 acc[C::FM][C::FN];
 #pragma unroll
@@ -488,15 +544,12 @@ void gemm_bf16_pingpong(Params p) {
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   bf16x8 af[C::SUBS][C::FM], bf[C::SUBS][C::FN];
-  const int nk = p.k / C::BK;
+  const int nk = (p.k + C::BK - 1) / C::BK;
 
 #pragma unroll
   for (int s = 0; s < D; ++s) t.issue_loads(smem, s, nk);
   __builtin_amdgcn_sched_barrier(0);
-  if (group == 0)  // b0: step 0 landed everywhere
-    wait_vmcnt_and_barrier<(D - 1) * C::L0>();
-  else
-    wait_vmcnt_and_barrier<(D - 1) * C::L1>();
+  wait_loads_barrier<C, D, true>(full);  // b0: step 0 landed everywhere
   __builtin_amdgcn_sched_barrier(0);
   if (group == 1) __asm__ volatile("s_barrier" ::: "memory");  // b1 for group 1
   __builtin_amdgcn_sched_barrier(0);
@@ -508,7 +561,7 @@ void gemm_bf16_pingpong(Params p) {
     t.issue_loads(smem, ks + D, nk);
     __builtin_amdgcn_sched_barrier(0);
     if (group == 1) {
-      __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((D - 1) * C::L1) : "memory");
+      wait_loads_barrier<C, D, true>(full);
     } else {
       __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
@@ -518,7 +571,7 @@ void gemm_bf16_pingpong(Params p) {
     for (int sub = 0; sub < C::SUBS; ++sub) mfma_block<C>(acc, af[sub], bf[sub]);
     __builtin_amdgcn_sched_barrier(0);
     if (group == 0) {
-      __asm__ volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((D - 1) * C::L0) : "memory");
+      wait_loads_barrier<C, D, false>(full);
     } else {
       __asm__ volatile("s_barrier" ::: "memory");
     }
@@ -538,12 +591,15 @@ template <class C>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void gemm_bf16_pipelined(Params p) {
   static_assert(C::S >= 2, "at least two stages");
-  static_assert(C::NW == 4 && C::EVEN, "one group of four waves, even load split");
+  static_assert(C::NW == 4 && C::NL % C::NW == 0, "one group of four waves, even load split");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x;
   Tile<C> t;
   if (!t.init(p, tid)) return;
-  if (p.ready) wait_ready(p, t.m0, min(t.m0 + C::BM, t.m_end));
+  if (p.ready && wait_ready(p, t.m0, min(t.m0 + C::BM, t.m_end))) {
+    t.store_nan(p, tid);
+    return;
+  }
 
   f32x4 acc[C::FM][C::FN];
 #pragma unroll
@@ -551,16 +607,17 @@ void gemm_bf16_pipelined(Params p) {
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   bf16x8 af[2][C::FM], bf[2][C::FN];
-  const int nk = p.k / C::BK;
+  const int nk = (p.k + C::BK - 1) / C::BK;
 
 #pragma unroll
   for (int s = 0; s < C::S; ++s) t.issue_loads(smem, s, nk);
-  wait_vmcnt_and_barrier<(C::S - 1) * C::L0>();
+  wait_vmcnt_and_barrier<(C::S - 1) * C::LMAX>();
   t.read_frags(smem, 0, 0, af[0], bf[0]);
 
   // The two fragment buffers alternate per sub-step; with one sub-step per k-step an
-  // iteration takes two k-steps (nk is even: k is a multiple of 64), so that each
-  // iteration starts on buffer 0.
+  // iteration takes two k-steps, so that each iteration starts on buffer 0.  With an odd
+  // step count the last iteration's second step is past the end: its loads were issued out
+  // of range, and its MFMAs are skipped, so every tile shape runs exactly nk steps.
   constexpr int PAIR = C::SUBS == 1 ? 2 : 1;
   static_assert((PAIR * C::SUBS) % 2 == 0, "an even number of sub-steps per iteration");
   for (int ks0 = 0; ks0 < nk; ks0 += PAIR) {
@@ -570,12 +627,12 @@ void gemm_bf16_pipelined(Params p) {
       if (sub + 1 < C::SUBS) {
         t.read_frags(smem, ks, (sub + 1) * 32, af[b ^ 1], bf[b ^ 1]);
       } else {
-        wait_vmcnt_and_barrier<(C::S - 2) * C::L0>();
+        wait_vmcnt_and_barrier<(C::S - 2) * C::LMAX>();
         t.issue_loads(smem, ks + C::S, nk);
         // at the last step this reads a stage of zeros that is never used
         t.read_frags(smem, ks + 1, 0, af[b ^ 1], bf[b ^ 1]);
       }
-      mfma_block<C>(acc, af[b], bf[b]);
+      if (PAIR == 1 || ks < nk) mfma_block<C>(acc, af[b], bf[b]);
     }
   }
   wait_vmcnt_and_barrier<0>();  // trailing out-of-range loads landed before LDS is reused
@@ -609,7 +666,7 @@ hipError_t launch(K kernel, const GemmArgs& g, const GemmUnits& units, hipStream
   }
   p.unit_tile0[u.n] = (int32_t)tiles;
   if (tiles == 0) return hipSuccess;
-  p.group = tile_group(tiles, C::NW == 8 ? 1 : 2);
+  p.group = tile_group(tiles, C::NW == 8 ? 1 : 2, g.dbg ? g.dbg->tile_group : 0);
   p.ready = g.ready;
   p.timeouts = g.timeouts;
   p.wait_ticks = g.wait_ticks ? g.wait_ticks : kReadyTimeoutTicks;
@@ -628,55 +685,52 @@ hipError_t launch(K kernel, const GemmArgs& g, const GemmUnits& units, hipStream
   }
   const int64_t grid = tiles;
   if (grid > 0x7FFFFFFF || g.batch > 65535) return hipErrorInvalidValue;
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kernel), C::LDS_BYTES);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid, 1, g.batch), dim3(C::THREADS), C::LDS_BYTES,
                      stream, p);
   return hipGetLastError();
 }
 
+using PP320x256 = Cfg<320, 256, 32, 4, 2, 4>;   // 8 waves of 160x64
 using PP256x256 = Cfg<256, 256, 32, 4, 2, 4>;   // 8 waves of 128x64
-using PP192x256 = Cfg<192, 256, 32, 4, 2, 4>;   // 8 waves of 96x64
 using PP128x256 = Cfg<128, 256, 32, 4, 2, 4>;   // 8 waves of 64x64
-using PP256x128 = Cfg<256, 128, 32, 5, 4, 2>;   // 8 waves of 64x64
 using PL128x128 = Cfg<128, 128, 32, 4, 2, 2>;   // 4 waves of 64x64, 2 workgroups per CU
 constexpr int PP_D = 3;
 
-enum TileKind {
-  kTile128x128 = 0, kTile256x128 = 1, kTile256x256 = 3, kTile192x256 = 4, kTile128x256 = 5
-};
-
 // Tile choice by a small cost model: a launch of `tiles` workgroups on the CUs left to it
 // (256 / concurrency, times the workgroups one CU holds) runs ceil(tiles / slots) rounds,
-// each as long as one tile takes at the tile's efficiency.  Efficiencies are measured
-// relative to the 256x256 ping-pong.  The chip runs into its power limit under
-// sustained MFMA load, so a launch that leaves CUs idle runs the busy ones at a higher
-// clock: spreading the same work over more, smaller tiles gains much less than the tile
-// count suggests, and the efficiencies of the smaller tiles carry that (192x256 and
-// 128x256 were measured on AG GEMMs with K = 4096, N = 1536 over T = 4096 ... 8192; the
-// 128x128 kernel runs two workgroups per CU that share its MFMA pipes).
+// each as long as one tile takes at the tile's efficiency.  Efficiencies are relative to
+// the 256x256 ping-pong.  Measured on MI355X with rocprofv3 counters of the GEMM (GQA
+// shape, hidden 8192, 1280 columns): the 256x256 ping-pong keeps the matrix cores of its
+// busy CUs ~75% busy, the 128x256 one ~48% (a 64x64 wave tile reads more LDS bytes per
+// MFMA); the 128x128 kernel runs two workgroups per CU that share its MFMA pipes.  The
+// chip runs into its power limit under sustained MFMA load, so a launch that leaves CUs
+// idle runs the busy ones at a higher clock (2.25 GHz with ~145 busy CUs, 2.0 with ~217):
+// spreading the same work over more, smaller tiles gains much less than the tile count
+// suggests, and the efficiencies carry that.
 //
 // A launch whose last round would hold only a few tiles (say 260 tiles of 256 x 256 on
 // 256 CUs: the last 4 run alone, as long as all the others) is cut in two launches on the
 // same stream: the leading row bands that fill whole rounds with the large tile, then the
 // remaining rows with the tile that finishes them soonest.  Rows are cut at a band
 // boundary, so every row is still computed once, by one instruction sequence: the results
-// do not change.  Measured on the GQA shape (hidden 8192, 1280 columns, device-side loop)
-// over T = 13216 ... 32520, the cut gains 7-22% while the second launch fills at most
-// about 60% of its slots and nothing or a little beyond; so it is taken only then, and
-// only for a launch that has the chip to itself (with several streams the other streams'
-// launches fill the idle CUs, and a cut costs 10% on fc1's host loop).
+// do not change.  The cut is taken only when the second launch fills at most about 60%
+// of its slots, and only for a launch that has the chip to itself (with several streams
+// the other streams' launches fill the idle CUs, and a cut measured 10% slower on fc1's
+// host loop).
 struct TileOpt { int kind, bm, bn, per_cu; double eff; };
-const TileOpt kTileOpts[] = {{kTile256x256, 256, 256, 1, 1.00},
-                             {kTile192x256, 192, 256, 1, 0.72},
+enum TileKind { kTile128x128 = 0, kTile128x256 = 1, kTile256x256 = 2, kTile320x256 = 3 };
+const TileOpt kTileOpts[] = {{kTile320x256, 320, 256, 1, 1.00},
+                             {kTile256x256, 256, 256, 1, 1.00},
                              {kTile128x256, 128, 256, 1, 0.62},
-                             {kTile256x128, 256, 128, 1, 0.71},
                              {kTile128x128, 128, 128, 2, 0.75}};
+
+const TileOpt* find_tile(int bm, int bn) {
+  for (const TileOpt& o : kTileOpts)
+    if (o.bm == bm && o.bn == bn) return &o;
+  return nullptr;
+}
 
 struct TilePlan {
   int kind;           // tile of the (first) launch
@@ -708,7 +762,7 @@ double tile_cost(const TileOpt& o, int64_t row_tiles_, const GemmArgs& g, int sh
 
 // The cheapest single tile over the units; its cost in *cost.
 const TileOpt& best_single(const GemmArgs& g, const GemmUnits& u, int share, double* cost) {
-  const TileOpt* best = &kTileOpts[4];
+  const TileOpt* best = &kTileOpts[1];
   double best_cost = 1e300;
   for (const TileOpt& o : kTileOpts) {
     const double c = tile_cost(o, row_tiles(u, o.bm), g, share);
@@ -722,14 +776,20 @@ const TileOpt& best_single(const GemmArgs& g, const GemmUnits& u, int share, dou
 }
 
 TilePlan choose_plan(const GemmArgs& g, const GemmUnits& u) {
-  // Override for tuning and for tests that cover every tile shape (one launch, no cut);
-  // read on every call so that a process can switch it.
-  if (const char* s = std::getenv("UBX_GEMM_TILE")) {
-    if (!std::strcmp(s, "128x128")) return {kTile128x128};
-    if (!std::strcmp(s, "256x128")) return {kTile256x128};
-    if (!std::strcmp(s, "256x256")) return {kTile256x256};
-    if (!std::strcmp(s, "192x256")) return {kTile192x256};
-    if (!std::strcmp(s, "128x256")) return {kTile128x256};
+  if (g.dbg && (g.dbg->tile_m > 0 || g.dbg->cut_row > 0)) {
+    // forced by the handle's debug settings (validated by the caller): the tile, and a cut
+    // at cut_row when that row lies inside this launch group and on a band boundary
+    const TileOpt* o = find_tile(g.dbg->tile_m, g.dbg->tile_n);
+    if (!o) o = find_tile(256, 256);
+    TilePlan plan{o->kind};
+    int64_t lo = 0, hi = 0;
+    const int64_t cut = g.dbg->cut_row;
+    if (cut > 0 && contiguous_rows(u, &lo, &hi) && lo < cut && cut < hi && (cut - lo) % o->bm == 0) {
+      const TileOpt* t = find_tile(g.dbg->tail_m, g.dbg->tail_n);
+      plan.cut = cut;
+      plan.tail_kind = t ? t->kind : kTile128x128;
+    }
+    return plan;
   }
   const int share = 256 / (g.concurrency > 1 ? g.concurrency : 1);
   double best_cost;
@@ -764,20 +824,26 @@ TilePlan choose_plan(const GemmArgs& g, const GemmUnits& u) {
 hipError_t launch_kind(int kind, const GemmArgs& g, const GemmUnits& u, hipStream_t stream) {
   if (u.n <= 0) return hipSuccess;
   switch (kind) {
+    case kTile320x256:
+      return launch<PP320x256>(&gemm_bf16_pingpong<PP320x256, PP_D>, g, u, stream);
     case kTile256x256:
       return launch<PP256x256>(&gemm_bf16_pingpong<PP256x256, PP_D>, g, u, stream);
-    case kTile192x256:
-      return launch<PP192x256>(&gemm_bf16_pingpong<PP192x256, PP_D>, g, u, stream);
     case kTile128x256:
       return launch<PP128x256>(&gemm_bf16_pingpong<PP128x256, PP_D>, g, u, stream);
-    case kTile256x128:
-      return launch<PP256x128>(&gemm_bf16_pingpong<PP256x128, PP_D>, g, u, stream);
     default:
       return launch<PL128x128>(&gemm_bf16_pipelined<PL128x128>, g, u, stream);
   }
 }
 
+const TileOpt& opt_of(int kind) {
+  for (const TileOpt& o : kTileOpts)
+    if (o.kind == kind) return o;
+  return kTileOpts[1];
+}
+
 }  // namespace
+
+bool gemm_bf16_tile_supported(int tile_m, int tile_n) { return find_tile(tile_m, tile_n) != nullptr; }
 
 uint32_t* ready_flags_base(hipError_t* err) {
   static std::mutex mu;
@@ -802,9 +868,11 @@ uint32_t* ready_flags_base(hipError_t* err) {
 }
 
 bool gemm_shape_supported(const GemmArgs& g) {
-  // Offsets into B are 32-bit byte offsets from column n0 of the batch entry, and one A
-  // tile spans at most 256 rows; both must stay below the out-of-range marker.
-  return (int64_t)g.k * g.ldb * 2 < (int64_t)OOB && (int64_t)256 * g.lda * 2 < (int64_t)OOB;
+  // Offsets into B are 32-bit byte offsets from column n0 of the batch entry (up to a
+  // step past k), and one A tile spans at most 320 rows; both must stay below the
+  // out-of-range marker with room for a 16-byte access.
+  const int64_t lim = (int64_t)OOB - 64;
+  return ((int64_t)g.k + 64) * g.ldb * 2 < lim && (int64_t)320 * g.lda * 2 < lim;
 }
 
 hipError_t launch_gemm_bf16_units(const GemmArgs& g, const GemmUnits& u, hipStream_t stream) {
@@ -828,12 +896,14 @@ hipError_t launch_gemm_bf16_units(const GemmArgs& g, const GemmUnits& u, hipStre
     }
   }
   const TilePlan plan = choose_plan(g, u);
-  if (const char* path = std::getenv("UBX_GEMM_LOG")) {  // tile plans, for tests and tuning
-    if (FILE* f = std::fopen(path, "a")) {
-      std::fprintf(f, "kind=%d cut=%lld tail_kind=%d n=%d k=%d batch=%d units=%d\n", plan.kind,
-                   (long long)plan.cut, plan.tail_kind, g.n, g.k, g.batch, u.n);
-      std::fclose(f);
-    }
+  if (g.plan_out) {
+    const TileOpt& a = opt_of(plan.kind);
+    g.plan_out->tile_m = a.bm;
+    g.plan_out->tile_n = a.bn;
+    g.plan_out->cut = plan.cut;
+    const TileOpt& b = opt_of(plan.tail_kind);
+    g.plan_out->tail_m = plan.cut >= 0 ? b.bm : 0;
+    g.plan_out->tail_n = plan.cut >= 0 ? b.bn : 0;
   }
   if (plan.cut < 0) return launch_kind(plan.kind, g, u, stream);
   // two launches on one stream: the leading whole-round bands, then the rest (the fused
@@ -843,15 +913,6 @@ hipError_t launch_gemm_bf16_units(const GemmArgs& g, const GemmUnits& u, hipStre
   hipError_t e = launch_kind(plan.kind, g, clip_units(u, lo, plan.cut), stream);
   if (e != hipSuccess) return e;
   return launch_kind(plan.tail_kind, g, clip_units(u, plan.cut, hi), stream);
-}
-
-int64_t fuse_counter_bound(const int64_t* rows, int n_units, int64_t n) {
-  // The smallest tile is 128 x 128; re-cutting units at tile boundaries adds at most one
-  // row tile per unit.
-  int64_t row_tiles_max = 0;
-  for (int i = 0; i < n_units; ++i)
-    if (rows[i] > 0) row_tiles_max += (rows[i] + 127) / 128 + 1;
-  return row_tiles_max * ((n + 127) / 128);
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream) {

@@ -6,7 +6,9 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <cstdlib>
+#include <mutex>
+#include <set>
+#include <utility>
 
 namespace ubx {
 namespace {
@@ -82,12 +84,26 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
 // gains nothing from column groups and lists its tiles row by row (group 1), which keeps
 // each XCD's block on the fewest A rows; larger launches use groups of 4 (measured on
 // MI355X: qkv shapes ~1-2% faster with 1, 8192^3 and 16384 x 3584 x 4096 3-5% faster with 4).
-inline int tile_group(int64_t tiles, int per_cu) {
-  if (const char* g = std::getenv("UBX_TILE_GROUP")) {  // tuning override
-    const int v = std::atoi(g);
-    if (v >= 1) return v;
-  }
+// forced > 0 (a handle's debug setting) overrides the choice.
+inline int tile_group(int64_t tiles, int per_cu, int forced) {
+  if (forced >= 1) return forced;
   return tiles <= 256 * (int64_t)per_cu ? 1 : 4;
+}
+
+// Sets a kernel's dynamic-LDS limit on the current device, once per (device, kernel):
+// HIP keeps the attribute per device, and launches from several host threads may come
+// first at the same time, hence the lock.
+inline hipError_t ensure_lds_attr(const void* kernel, int bytes) {
+  static std::mutex mu;
+  static std::set<std::pair<int, const void*>> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({dev, kernel})) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.insert({dev, kernel});
+  return e;
 }
 
 template <class P>

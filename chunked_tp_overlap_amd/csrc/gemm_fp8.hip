@@ -283,29 +283,21 @@ hipError_t launch(const GemmF8Args& g, const GemmUnits& units, hipStream_t strea
   }
   p.unit_tile0[u.n] = (int32_t)tiles;
   if (tiles == 0) return hipSuccess;
-  p.group = tile_group(tiles, 1);
+  p.group = tile_group(tiles, 1, g.dbg ? g.dbg->tile_group : 0);
   const int64_t grid = tiles;
   if (grid > 0x7FFFFFFF || g.batch < 1 || g.batch > 65535) return hipErrorInvalidValue;
   auto kernel = &gemm_fp8_pingpong<C, F8_D>;
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kernel), C::LDS_BYTES);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid, 1, g.batch), dim3(C::THREADS), C::LDS_BYTES,
                      stream, p);
   return hipGetLastError();
 }
 
-// Tile choice as for bf16 (rounds of a launch x tile area / efficiency); UBX_GEMM_TILE
-// ("128x256" or "256x256") forces one.
+// Tile choice as for bf16 (rounds of a launch x tile area / efficiency); a handle's debug
+// setting can force one of the two shapes.
 bool use_128(const GemmF8Args& g, const GemmUnits& u) {
-  if (const char* s = std::getenv("UBX_GEMM_TILE")) {
-    if (!std::strcmp(s, "128x256")) return true;
-    if (!std::strcmp(s, "256x256")) return false;
-  }
+  if (g.dbg && g.dbg->tile_m > 0) return g.dbg->tile_m == 128;
   const int share = 256 / (g.concurrency > 1 ? g.concurrency : 1);
   auto cost = [&](int bm, double eff) {
     const int64_t tiles = row_tiles(u, bm) * ((g.n + 255) / 256) * g.batch;
@@ -329,7 +321,17 @@ hipError_t launch_gemm_fp8_units(const GemmF8Args& g, const GemmUnits& u, hipStr
     return hipErrorInvalidValue;
   for (int i = 0; i < u.n; ++i)
     if (u.rows[i] < 0 || u.row0[i] < 0) return hipErrorInvalidValue;
-  return use_128(g, u) ? launch<F8_128x256>(g, u, stream) : launch<F8_256x256>(g, u, stream);
+  const bool small = use_128(g, u);
+  if (g.plan_out) {
+    *g.plan_out = TilePlanRecord{};
+    g.plan_out->tile_m = small ? 128 : 256;
+    g.plan_out->tile_n = 256;
+  }
+  return small ? launch<F8_128x256>(g, u, stream) : launch<F8_256x256>(g, u, stream);
+}
+
+bool gemm_fp8_tile_supported(int tile_m, int tile_n) {
+  return tile_n == 256 && (tile_m == 128 || tile_m == 256);
 }
 
 }  // namespace ubx

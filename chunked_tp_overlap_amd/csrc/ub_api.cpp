@@ -70,9 +70,13 @@ struct ub_ctx {
   // device-side arrival gating: this handle's slot of arrival flags (-1: none yet)
   int ready_slot = -1;
   uint32_t* ready = nullptr;  // device address of the slot's words
-  // fused reduction: per-tile arrival counters (zero between launches)
+  // fused reduction: per-tile arrival counters in the workspace, after the partial slots
+  // (zero at registration, left zero by every launch)
   uint32_t* fuse_counters = nullptr;
   int64_t fuse_counters_n = 0;
+  // debug settings (ub_debug_set) and the tile plan of the last GEMM launch group
+  ubx::DebugOpts dbg;
+  ubx::TilePlanRecord last_plan;
   // scratch for plans
   ubx::Plan plan;
   std::string last_error;
@@ -139,6 +143,22 @@ ub_status_t check_registration(int64_t capacity, int64_t hidden, int32_t tp, ub_
     return UB_ERR_INVALID_ARG;
   }
   return UB_OK;
+}
+
+// Reduce-scatter workspace: tp_size partial slots of [capacity, hidden] bf16, then, from
+// the next 256-byte boundary, the fused reduction's counter words (ubx::fuse_counter_words).
+struct WsLayout {
+  size_t partial_bytes, counter_offset, counter_words, total;
+};
+
+WsLayout ws_layout(int64_t capacity, int64_t hidden, int32_t tp) {
+  WsLayout l;
+  l.partial_bytes = static_cast<size_t>(capacity) * static_cast<size_t>(hidden) * 2 *
+                    static_cast<size_t>(tp);
+  l.counter_offset = (l.partial_bytes + 255) / 256 * 256;
+  l.counter_words = static_cast<size_t>(ubx::fuse_counter_words(capacity, hidden));
+  l.total = l.counter_offset + l.counter_words * sizeof(uint32_t);
+  return l;
 }
 
 ub_status_t hip_fail(ub_ctx* h, hipError_t e, const char* what) {
@@ -319,32 +339,6 @@ ub_status_t check_cfg_common(ub_ctx* h, const ub_overlap_cfg_t* cfg) {
   return UB_OK;
 }
 
-// Counters of the fused reduction for `need` tiles: allocated on first use or when a plan
-// needs more than any before, and zeroed on the caller's stream, ahead of the launches that
-// use them (the compute streams fork from the caller's stream after it).  The kernels leave
-// them zero.
-ub_status_t ensure_fuse_counters(ub_ctx* h, int64_t need, hipStream_t caller) {
-  if (need <= h->fuse_counters_n) return UB_OK;
-  hipError_t e;
-  if (h->fuse_counters) {
-    e = hipFree(h->fuse_counters);  // waits for the device
-    h->fuse_counters = nullptr;
-    h->fuse_counters_n = 0;
-    if (e != hipSuccess) return hip_fail(h, e, "hipFree(fused-reduction counters)");
-  }
-  void* p = nullptr;
-  e = hipMalloc(&p, static_cast<size_t>(need) * sizeof(uint32_t));
-  if (e != hipSuccess) return hip_fail(h, e, "hipMalloc(fused-reduction counters)");
-  e = hipMemsetAsync(p, 0, static_cast<size_t>(need) * sizeof(uint32_t), caller);
-  if (e != hipSuccess) {
-    (void)hipFree(p);
-    return hip_fail(h, e, "hipMemset(fused-reduction counters)");
-  }
-  h->fuse_counters = static_cast<uint32_t*>(p);
-  h->fuse_counters_n = need;
-  return UB_OK;
-}
-
 // Units of the plan, in execution order, for a device-side chunk loop.
 ub_status_t plan_units(ub_ctx* h, ubx::GemmUnits* u) {
   u->n = 0;
@@ -358,6 +352,23 @@ ub_status_t plan_units(ub_ctx* h, ubx::GemmUnits* u) {
     u->rows[u->n] = static_cast<int32_t>(rows);
     ++u->n;
   }
+  return UB_OK;
+}
+
+// A tile shape forced by ub_debug_set must be one the call's kernel builds.
+ub_status_t check_forced_tile(ub_ctx* h, bool fp8) {
+  const ubx::DebugOpts& d = h->dbg;
+  auto ok = [&](int m, int n) {
+    return fp8 ? ubx::gemm_fp8_tile_supported(m, n) : ubx::gemm_bf16_tile_supported(m, n);
+  };
+  if ((d.tile_m || d.tile_n) && !ok(d.tile_m, d.tile_n))
+    return fail(h, UB_ERR_INVALID_ARG, "the %s GEMM has no %dx%d tile (debug tile_m/tile_n)",
+                fp8 ? "fp8" : "bf16", d.tile_m, d.tile_n);
+  if (d.cut_row > 0 && fp8)
+    return fail(h, UB_ERR_INVALID_ARG, "the fp8 GEMM takes no forced cut (debug cut_row)");
+  if (d.cut_row > 0 && (d.tail_m || d.tail_n) && !ok(d.tail_m, d.tail_n))
+    return fail(h, UB_ERR_INVALID_ARG, "the bf16 GEMM has no %dx%d tile (debug tail_tile_m/n)",
+                d.tail_m, d.tail_n);
   return UB_OK;
 }
 
@@ -439,7 +450,7 @@ UB_API ub_status_t ub_required_bytes(int64_t capacity, int64_t hidden, int32_t t
   if (ub_bytes) *ub_bytes = elems * static_cast<size_t>(elem_bytes_of(dtype));
   // the reduce-scatter side (bf16 partials) exists for bf16 buffers only
   if (rs_workspace_bytes)
-    *rs_workspace_bytes = dtype == UB_DTYPE_BF16 ? elems * 2 * static_cast<size_t>(tp_size) : 0;
+    *rs_workspace_bytes = dtype == UB_DTYPE_BF16 ? ws_layout(capacity, hidden, tp_size).total : 0;
   return UB_OK;
 }
 
@@ -456,9 +467,10 @@ UB_API ub_status_t ub_init(ub_handle_t* out, int64_t capacity, int64_t hidden, i
   if (!ub_buf || !aligned16(ub_buf)) return UB_ERR_INVALID_ARG;
   if (ub_bytes < need) return UB_ERR_BUFFER_TOO_SMALL;
   if (dtype != UB_DTYPE_BF16 && (rs_ws || rs_ws_bytes)) return UB_ERR_INVALID_ARG;
+  const WsLayout wl = ws_layout(capacity, hidden, tp_size);
   if (rs_ws) {
     if (!aligned16(rs_ws)) return UB_ERR_INVALID_ARG;
-    if (rs_ws_bytes < elems * 2 * static_cast<size_t>(tp_size)) return UB_ERR_BUFFER_TOO_SMALL;
+    if (rs_ws_bytes < wl.total) return UB_ERR_BUFFER_TOO_SMALL;
   } else if (rs_ws_bytes != 0) {
     return UB_ERR_INVALID_ARG;
   }
@@ -474,6 +486,11 @@ UB_API ub_status_t ub_init(ub_handle_t* out, int64_t capacity, int64_t hidden, i
   h->ub_bytes = ub_bytes;
   h->ws = static_cast<uint16_t*>(rs_ws);
   h->ws_bytes = rs_ws_bytes;
+  if (rs_ws) {
+    h->fuse_counters =
+        reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(rs_ws) + wl.counter_offset);
+    h->fuse_counters_n = static_cast<int64_t>(wl.counter_words);
+  }
   h->T = capacity;  // the initial active shape is the capacity shape
   *out = h;
   return UB_OK;
@@ -570,6 +587,7 @@ ub_status_t check_ag_call(ub_ctx* h, const void* w, int64_t n_cols, int64_t ldw,
   if (h->hidden % ubx::kGemmKStep != 0)
     return fail(h, UB_ERR_UNSUPPORTED, "hidden=%lld must be a multiple of %d",
                 (long long)h->hidden, ubx::kGemmKStep);
+  if ((st = check_forced_tile(h, false)) != UB_OK) return st;
   return ubx::build_plan(h->T, h->tp, *cfg, UB_OP_AG, &h->plan, &h->last_error);
 }
 
@@ -635,24 +653,15 @@ ub_status_t join_deliveries(ub_ctx* h, hipStream_t caller) {
 // they read.  Everything on the copy stream is issued before the GEMM, so where the two
 // streams share a hardware queue the copies run first and nothing waits on work queued
 // behind it.
-// Test hooks of the wait's failure path, read on every call: UBX_ARRIVAL_WAIT_US sets the
-// bound of a tile's wait (microseconds; default 0.5 s), and UBX_ARRIVAL_DROP_FLAGS=1 writes
-// no flag for the delivered chunks, so that their tiles run into the bound and end.
-uint64_t arrival_wait_ticks() {
-  const char* s = std::getenv("UBX_ARRIVAL_WAIT_US");
-  const long long us = s ? std::atoll(s) : 0;
-  return us > 0 ? static_cast<uint64_t>(us) * 100 : 0;  // 100 MHz ticks
-}
-
-bool arrival_drop_flags() {
-  const char* s = std::getenv("UBX_ARRIVAL_DROP_FLAGS");
-  return s && std::strcmp(s, "1") == 0;
+// Bound of a gated tile's wait in 100 MHz ticks (0: the kernel's default of ~0.5 s).
+uint64_t arrival_wait_ticks(const ub_ctx* h) {
+  return h->dbg.arrival_wait_us > 0 ? static_cast<uint64_t>(h->dbg.arrival_wait_us) * 100 : 0;
 }
 
 ub_status_t deliver_flagged(ub_ctx* h, const uint16_t* src, int src_on_host,
                             const ub_overlap_cfg_t* cfg, const ChunkMap& m, uint32_t epoch) {
   const hipMemcpyKind kind = src_on_host ? hipMemcpyHostToDevice : hipMemcpyDeviceToDeviceNoCU;
-  const bool drop = arrival_drop_flags();
+  const bool drop = h->dbg.arrival_drop_flags != 0;
   const int64_t H = h->hidden, T = h->T;
   auto flag = [&](int c) {
     hipError_t e = hipStreamWriteValue32(h->copy_stream, h->ready + c, epoch, 0);
@@ -709,6 +718,8 @@ ub_status_t ag_call(ub_ctx* h, const void* src, int src_on_host, const void* w, 
     if ((st = plan_units(h, &units)) != UB_OK) return st;
     if ((st = ensure_device(h, 1)) != UB_OK) return st;
     ubx::GemmArgs g{};
+    g.dbg = &h->dbg;
+    g.plan_out = &h->last_plan;
     g.a = h->ub;
     g.lda = H;
     g.b = static_cast<const uint16_t*>(w);
@@ -730,7 +741,7 @@ ub_status_t ag_call(ub_ctx* h, const void* src, int src_on_host, const void* w, 
       g.ready = h->ready;
       g.epoch = epoch;
       g.timeouts = h->ready + ubx::kReadyTimeoutWord;
-      g.wait_ticks = arrival_wait_ticks();
+      g.wait_ticks = arrival_wait_ticks(h);
       g.n_chunks = m.n;
       for (int c = 0; c <= m.n; ++c) g.chunk_row0[c] = static_cast<int32_t>(m.row0(h->T, c));
     }
@@ -767,6 +778,8 @@ ub_status_t ag_call(ub_ctx* h, const void* src, int src_on_host, const void* w, 
       }
     }
     ubx::GemmArgs g{};
+    g.dbg = &h->dbg;
+    g.plan_out = &h->last_plan;
     g.a = h->ub + u.row0 * H;  // byte offset row0 * hidden * 2 into the capacity buffer
     g.lda = H;
     g.b = static_cast<const uint16_t*>(w);
@@ -887,7 +900,10 @@ UB_API ub_status_t ub_gemm_ag_chunked_fp8(ub_handle_t h, const void* w, int64_t 
   if (H % ubx::kGemmF8KStep != 0)
     return fail(h, UB_ERR_UNSUPPORTED, "hidden=%lld must be a multiple of %d", (long long)H,
                 ubx::kGemmF8KStep);
+  if ((st = check_forced_tile(h, true)) != UB_OK) return st;
   ubx::GemmF8Args g{};
+  g.dbg = &h->dbg;
+  g.plan_out = &h->last_plan;
   g.a = h->ub8;
   g.lda = H;
   g.b = static_cast<const uint8_t*>(w);
@@ -951,6 +967,7 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
   if (ks % ubx::kGemmKStep != 0)
     return fail(h, UB_ERR_UNSUPPORTED, "k / tp_size = %lld must be a multiple of %d",
                 (long long)ks, ubx::kGemmKStep);
+  if ((st = check_forced_tile(h, false)) != UB_OK) return st;
   const int64_t H = h->hidden;
   if ((st = check_ld(h, "lda", lda, k)) != UB_OK) return st;
   if ((st = check_ld(h, "ldw", ldw, H)) != UB_OK) return st;
@@ -962,21 +979,11 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
   hipStream_t caller = static_cast<hipStream_t>(stream);
   const bool ring = cfg->reduce_order == UB_REDUCE_RING;
   const bool fuse = cfg->fuse_reduce != 0;
-  // Fused reduction: unit u's launch counts its tiles in its own range of counters
-  // (units on different streams run at once); the device-side loop uses one range.
-  std::vector<int64_t> counter0;
-  if (fuse) {
-    std::vector<int64_t> rows;
-    for (const ub_plan_unit_t& u : h->plan.units) rows.push_back(u.row1 - u.row0);
-    int64_t need = 0;
-    for (size_t i = 0; i < rows.size(); ++i) {
-      counter0.push_back(need);
-      need += ubx::fuse_counter_bound(&rows[i], 1, H);
-    }
-    if ((st = ensure_device(h, 1)) != UB_OK) return st;
-    if ((st = ensure_fuse_counters(h, need, caller)) != UB_OK) return st;
-  }
-  auto set_fuse = [&](ubx::GemmArgs& g, int64_t row0, int64_t c0) {
+  // Fused reduction: the counters were sized at registration from the capacity.  The
+  // launches of one compute stream run one after another and leave their counters at zero,
+  // so each stream counts in its own range; the device-side loop uses the whole array.
+  const int64_t stream_words = ubx::fuse_counter_stream_words(h->capacity, H);
+  auto set_fuse = [&](ubx::GemmArgs& g, int64_t row0, int stream_index) {
     if (!fuse) return;
     g.fuse_out = static_cast<uint16_t*>(out) + row0 * ldo;
     g.fuse_ldo = ldo;
@@ -984,8 +991,13 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
     g.fuse_ring = ring;
     g.fuse_row0 = row0;
     g.fuse_shard_rows = T / tp;
-    g.counters = h->fuse_counters + c0;
-    g.counters_n = h->fuse_counters_n - c0;
+    if (stream_index < 0) {
+      g.counters = h->fuse_counters;
+      g.counters_n = h->fuse_counters_n;
+    } else {
+      g.counters = h->fuse_counters + stream_index * stream_words;
+      g.counters_n = stream_words;
+    }
   };
   const double fused_flops = double(tp - 1) * H;  // per row: the reduction's adds
   const double fused_bytes = 2.0 * (tp + 1) * H;  // per row: the reduction's reads and write
@@ -997,6 +1009,8 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
     if ((st = plan_units(h, &units)) != UB_OK) return st;
     if ((st = ensure_device(h, 1)) != UB_OK) return st;
     ubx::GemmArgs g{};
+    g.dbg = &h->dbg;
+    g.plan_out = &h->last_plan;
     g.a = static_cast<const uint16_t*>(a);
     g.lda = lda;
     g.a_batch_stride = ks;
@@ -1010,7 +1024,7 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
     g.k = static_cast<int32_t>(ks);
     g.batch = tp;
     g.concurrency = 1;
-    set_fuse(g, 0, 0);
+    set_fuse(g, 0, -1);
     st = timed_launch(h, caller, 0, 2.0 * T * k * H + (fuse ? fused_flops * T : 0.0),
                       2.0 * (T * k + k * H + tp * T * H) + (fuse ? fused_bytes * T : 0.0),
                       [&] { return ubx::launch_gemm_bf16_units(g, units, caller); },
@@ -1033,6 +1047,8 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
     // tp slice GEMMs of this chunk in one batched launch; slot s of the packed active
     // prefix starts at workspace element s*T*H (offsets from the active T).
     ubx::GemmArgs g{};
+    g.dbg = &h->dbg;
+    g.plan_out = &h->last_plan;
     g.a = static_cast<const uint16_t*>(a) + u.row0 * lda;
     g.lda = lda;
     g.a_batch_stride = ks;
@@ -1047,7 +1063,7 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
     g.k = static_cast<int32_t>(ks);
     g.batch = tp;
     g.concurrency = S;
-    if (fuse) set_fuse(g, u.row0, counter0[ui]);
+    if (fuse) set_fuse(g, u.row0, u.stream);
     const double flops = 2.0 * rows * k * H + (fuse ? fused_flops * rows : 0.0);
     const double gbytes = 2.0 * (rows * k + k * H + tp * rows * H) + (fuse ? fused_bytes * rows : 0.0);
     st = timed_launch(h, s, 0, flops, gbytes, [&] { return ubx::launch_gemm_bf16(g, s); },
@@ -1086,6 +1102,7 @@ UB_API ub_status_t ub_gemm_rs_chunked_fp8(ub_handle_t h, const void* a, int64_t 
   if (ks % ubx::kGemmF8KStep != 0)
     return fail(h, UB_ERR_UNSUPPORTED, "k / tp_size = %lld must be a multiple of %d",
                 (long long)ks, ubx::kGemmF8KStep);
+  if ((st = check_forced_tile(h, true)) != UB_OK) return st;
   const int64_t H = h->hidden;
   if (lda < k || lda % 16 != 0)
     return fail(h, UB_ERR_INVALID_ARG, "lda=%lld must be >= k=%lld and a multiple of 16",
@@ -1101,6 +1118,8 @@ UB_API ub_status_t ub_gemm_rs_chunked_fp8(ub_handle_t h, const void* a, int64_t 
   // slice s: columns [s*ks, (s+1)*ks) of A's rows and of W's rows; partial s at workspace
   // element s*T*H (offsets from the active T)
   ubx::GemmF8Args g{};
+  g.dbg = &h->dbg;
+  g.plan_out = &h->last_plan;
   g.a = static_cast<const uint8_t*>(a);
   g.lda = lda;
   g.a_batch_stride = ks;
@@ -1207,6 +1226,65 @@ UB_API ub_status_t ub_arrival_timeouts(ub_handle_t h, uint32_t* count) {
   return e == hipSuccess ? UB_OK : hip_fail(h, e, "hipMemcpy(arrival timeouts)");
 }
 
+UB_API ub_status_t ub_prepare_streams(ub_handle_t h, int32_t num_max_streams,
+                                      int32_t copy_stream) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  if (num_max_streams < 1)
+    return fail(h, UB_ERR_INVALID_ARG, "num_max_streams=%d must be >= 1", num_max_streams);
+  ub_status_t st = ensure_device(h, std::min<int32_t>(num_max_streams, UB_MAX_STREAMS));
+  if (st != UB_OK || !copy_stream) return st;
+  return ensure_arrival(h, 0);
+}
+
+UB_API ub_status_t ub_debug_set(ub_handle_t h, const char* key, int64_t value) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  if (!key) return fail(h, UB_ERR_INVALID_ARG, "key is NULL");
+  ubx::DebugOpts& d = h->dbg;
+  const std::string k(key);
+  if (k == "tile_m" || k == "tile_n") {
+    if (value < 0 || value > 4096) return fail(h, UB_ERR_INVALID_ARG, "%s=%lld", key, (long long)value);
+    (k == "tile_m" ? d.tile_m : d.tile_n) = static_cast<int32_t>(value);
+    return UB_OK;
+  }
+  if (k == "cut_row") {
+    if (value < 0 || value > (int64_t(1) << 31)) return fail(h, UB_ERR_INVALID_ARG, "cut_row=%lld", (long long)value);
+    d.cut_row = value;
+    return UB_OK;
+  }
+  if (k == "tail_tile_m" || k == "tail_tile_n") {
+    if (value < 0 || value > 4096) return fail(h, UB_ERR_INVALID_ARG, "%s=%lld", key, (long long)value);
+    (k == "tail_tile_m" ? d.tail_m : d.tail_n) = static_cast<int32_t>(value);
+    return UB_OK;
+  }
+  if (k == "tile_group") {
+    if (value < 0 || value > 4096) return fail(h, UB_ERR_INVALID_ARG, "tile_group=%lld", (long long)value);
+    d.tile_group = static_cast<int32_t>(value);
+    return UB_OK;
+  }
+  if (k == "arrival_wait_us") {
+    if (value < 0 || value > 60000000) return fail(h, UB_ERR_INVALID_ARG, "arrival_wait_us=%lld", (long long)value);
+    d.arrival_wait_us = value;
+    return UB_OK;
+  }
+  if (k == "arrival_drop_flags") {
+    if (value != 0 && value != 1) return fail(h, UB_ERR_INVALID_ARG, "arrival_drop_flags=%lld", (long long)value);
+    d.arrival_drop_flags = static_cast<int32_t>(value);
+    return UB_OK;
+  }
+  return fail(h, UB_ERR_INVALID_ARG, "unknown debug key '%s'", key);
+}
+
+UB_API ub_status_t ub_debug_last_plan(ub_handle_t h, ub_tile_plan_t* out) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  if (!out) return fail(h, UB_ERR_INVALID_ARG, "out is NULL");
+  out->tile_m = h->last_plan.tile_m;
+  out->tile_n = h->last_plan.tile_n;
+  out->cut_row = h->last_plan.cut;
+  out->tail_tile_m = h->last_plan.tail_m;
+  out->tail_tile_n = h->last_plan.tail_n;
+  return UB_OK;
+}
+
 UB_API ub_status_t ub_destroy(ub_handle_t h) {
   if (!h) return UB_OK;
   if (h->device >= 0) {
@@ -1228,7 +1306,6 @@ UB_API ub_status_t ub_destroy(ub_handle_t h) {
     for (hipEvent_t ev : h->ev_arrive)
       if (ev) (void)hipEventDestroy(ev);
     for (hipEvent_t ev : h->free_events) (void)hipEventDestroy(ev);
-    if (h->fuse_counters) (void)hipFree(h->fuse_counters);
     if (h->ready) {  // the next handle to take this slot starts with no counted timeouts
       const uint32_t zero = 0;
       (void)hipMemcpy(h->ready + ubx::kReadyTimeoutWord, &zero, sizeof(zero), hipMemcpyHostToDevice);

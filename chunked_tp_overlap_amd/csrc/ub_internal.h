@@ -25,7 +25,7 @@ ub_status_t build_plan(int64_t T, int32_t tp, const ub_overlap_cfg_t& cfg, ub_op
 
 // ---- kernels (gemm_bf16.hip, reduce_partials.hip) ----------------------------------------
 // Batched row-major bf16 GEMM, C[b] = bf16(A[b] * B[b]) with fp32 accumulation.
-// All strides in elements.  Requirements checked by the caller: k % 64 == 0,
+// All strides in elements.  Requirements checked by the caller: k % 8 == 0,
 // n % 8 == 0, lda/ldb/ldc % 8 == 0, pointers 16-byte aligned.
 constexpr int kMaxGemmUnits = 64;
 
@@ -37,6 +37,24 @@ constexpr int kReadySlots = 64;
 constexpr int kReadyWords = 72;
 constexpr int kReadyTimeoutWord = 64;
 uint32_t* ready_flags_base(hipError_t* err);
+
+// Per-handle debug and tuning settings (ub_debug_set).  All zero: the library's own
+// choices.  Nothing else (no environment variable) changes what a launch does.
+struct DebugOpts {
+  int32_t tile_m = 0, tile_n = 0;  // force one tile shape (one launch, unless cut_row)
+  int64_t cut_row = 0;             // > 0: cut a launch group's rows there (see ub_debug_set)
+  int32_t tail_m = 0, tail_n = 0;  // tile of the second launch of a forced cut
+  int32_t tile_group = 0;          // force the row-tile group size of the workgroup map
+  int64_t arrival_wait_us = 0;     // bound of a gated tile's wait (0: ~0.5 s)
+  int32_t arrival_drop_flags = 0;  // write no flag after delivered chunks
+};
+
+// The tile plan the last GEMM launch group took (ub_debug_last_plan).
+struct TilePlanRecord {
+  int32_t tile_m = 0, tile_n = 0;
+  int64_t cut = -1;
+  int32_t tail_m = 0, tail_n = 0;
+};
 
 struct GemmArgs {
   const uint16_t* a;
@@ -75,11 +93,21 @@ struct GemmArgs {
   int64_t fuse_shard_rows = 1;
   uint32_t* counters = nullptr;
   int64_t counters_n = 0;
+  // debug settings of the handle (nullptr: none) and where to record the plan taken
+  const DebugOpts* dbg = nullptr;
+  TilePlanRecord* plan_out = nullptr;
 };
-// Counter words a fused launch over units of the given rows can need (for any tile shape).
-int64_t fuse_counter_bound(const int64_t* rows, int n_units, int64_t n);
+// Counter words the fused reduction of a handle can need: one range per compute stream,
+// each large enough for one launch over up to `capacity` rows, and one for a device-side
+// chunk loop over up to kMaxGemmUnits units (tiles of every shape counted at the smallest
+// tile).  The words live in the registered workspace, after the partial slots.
+int64_t fuse_counter_words(int64_t capacity, int64_t n);
+// The range of one compute stream within those words.
+int64_t fuse_counter_stream_words(int64_t capacity, int64_t n);
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream);
-constexpr int kGemmKStep = 64;  // k must be a multiple of this
+// Whether the bf16 GEMM builds a tile of tile_m x tile_n.
+bool gemm_bf16_tile_supported(int tile_m, int tile_n);
+constexpr int kGemmKStep = 8;  // k must be a multiple of this (16-byte rows)
 
 // Row units of a device-side chunk loop: one launch whose workgroups cover every unit's
 // tiles, units in the given order, no tile spanning two units.  Unit u covers rows
@@ -123,7 +151,11 @@ struct GemmF8Args {
   int concurrency;
   int64_t a_batch_stride = 0, b_batch_stride = 0, c_batch_stride = 0;
   int32_t batch = 1;
+  const DebugOpts* dbg = nullptr;
+  TilePlanRecord* plan_out = nullptr;
 };
+// Whether the FP8 GEMM builds a tile of tile_m x tile_n.
+bool gemm_fp8_tile_supported(int tile_m, int tile_n);
 bool gemm_fp8_shape_supported(const GemmF8Args& g);
 hipError_t launch_gemm_fp8_units(const GemmF8Args& g, const GemmUnits& u, hipStream_t stream);
 

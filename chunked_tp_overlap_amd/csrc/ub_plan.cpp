@@ -132,4 +132,16 @@ int64_t row_tiles(const GemmUnits& u, int bm) {
   return n;
 }
 
+int64_t fuse_counter_stream_words(int64_t capacity, int64_t n) {
+  // One launch over up to `capacity` rows: re-cutting a unit at tile boundaries adds at
+  // most one row tile, and no tile is smaller than 128 x 128.
+  return ((capacity + 127) / 128 + 1) * ((n + 127) / 128);
+}
+
+int64_t fuse_counter_words(int64_t capacity, int64_t n) {
+  const int64_t streams = UB_MAX_STREAMS * fuse_counter_stream_words(capacity, n);
+  const int64_t device_loop = ((capacity + 127) / 128 + kMaxGemmUnits) * ((n + 127) / 128);
+  return std::max(streams, device_loop);
+}
+
 }  // namespace ubx

@@ -1,6 +1,5 @@
-"""Summarise rocprofv3 CSV output of ``bench.py --profile-pass [qkv|reduce|fp8]`` into a short
-text report, and (for the primary GEMM) the per-launch HBM traffic figure that bench.py
-reports beside its roofline.
+"""Summarise rocprofv3 CSV output of ``bench.py --profile-pass ...`` into a short text report,
+and (for the GEMMs) the HBM traffic figure that bench.py reports beside its roofline.
 
 Three rocprofv3 runs of the same command feed it: a kernel trace with statistics, then one
 counter pass for FETCH_SIZE and one for WRITE_SIZE.  Each profile pass ends with a plain
@@ -11,9 +10,12 @@ kernel's dispatches.
     python -m chunked_tp_overlap_amd.rocprof_summary --kt DIR --fetch DIR --write DIR \\
         --bench-json FILE [--key K] --kernel SUBSTRING --out profiles/x.md [--traffic FILE]
 
---key selects a sub-object of the profile pass's JSON line (the reduce pass reports the
-ascending and the ring order separately).  The timed launches are the last
-`timed_launches` dispatches of the kernel in the trace.
+The profile pass's JSON line (or its sub-object --key) names the timed region:
+timed_dispatches (the last that many dispatches whose name contains SUBSTRING, in every
+run), timed_algorithmic_bytes, optionally timed_gflop, timed_calls and
+hip_event_total_ms.  Everything is summed over those dispatches, so a sweep of shapes, or
+calls that launch two kernels, is summarised as a whole: work over traced time, traffic
+over algorithmic bytes.
 
 --timeline DIR --bench-json FILE --out FILE instead summarises `bench.py --profile-pass
 arrival` under `rocprofv3 --kernel-trace --memory-copy-trace`: per delivery mode, the
@@ -55,10 +57,15 @@ def _rows(path):
         return list(csv.DictReader(f))
 
 
-def counter_means(dirname, counter, kernel):
-    """Mean of `counter` (KiB) over the dispatches of `kernel`, and its value for the copy."""
+def counter_sum(dirname, counter, kernel, n_timed):
+    """Sum of `counter` (KiB) over the last n_timed dispatches of `kernel`, the number of
+    them found, and the counter's value for the calibration copy."""
     rows = [r for r in _rows(_one(dirname, "_counter_collection.csv")) if r["Counter_Name"] == counter]
-    mine = [float(r["Counter_Value"]) for r in rows if kernel in r["Kernel_Name"]]
+    by = {}
+    for r in rows:
+        if kernel in r["Kernel_Name"]:
+            by[int(r["Dispatch_Id"])] = float(r["Counter_Value"])
+    mine = [by[k] for k in sorted(by)][-n_timed:]
     # the calibration copy is the last and largest runtime copy of the pass (host-to-device
     # input uploads may show up as smaller copies before it)
     copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
@@ -66,7 +73,7 @@ def counter_means(dirname, counter, kernel):
         raise SystemExit(f"{counter}: {len(mine)} dispatches of {kernel}, {len(copy)} copies")
     if copy[-1] != max(copy):
         raise SystemExit(f"{counter}: the last copy is not the largest: {copy}")
-    return statistics.fmean(mine), len(mine), copy[-1]
+    return sum(mine), len(mine), copy[-1]
 
 
 def counter_timed_dispatches(dirname, counters, kernel, n_timed):
@@ -200,24 +207,25 @@ def main():
     with open(a.bench_json) as f:
         top = json.loads([ln for ln in f if ln.startswith("{")][-1])
     bench = top[a.key] if a.key else top
+    n_timed = bench["timed_dispatches"]
+    alg = bench["timed_algorithmic_bytes"]
+    gflop = bench.get("timed_gflop")
+    calls = bench.get("timed_calls", n_timed)
 
     stats = _rows(_one(a.kt, "_kernel_stats.csv"))
     trace = _rows(_one(a.kt, "_kernel_trace.csv"))
     mine = [r for r in trace if a.kernel in r["Kernel_Name"]]
-    if not mine:
-        raise SystemExit(f"no dispatch of {a.kernel} in the trace")
-    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in mine]
-    names = sorted({r["Kernel_Name"] for r in mine})
-    timed = dur[-bench["timed_launches"]:]
-    t_mean = statistics.fmean(timed)
-    ev = bench["avg_launch_us_hip_events"]
-    alg = bench["algorithmic_bytes_per_launch"]
+    if len(mine) < n_timed:
+        raise SystemExit(f"{len(mine)} dispatches of {a.kernel} in the trace, {n_timed} timed")
+    timed = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in mine][-n_timed:]
+    names = sorted({r["Kernel_Name"] for r in mine[-n_timed:]})
+    t_total = sum(timed)  # us
 
-    f_mean, f_n, f_copy = counter_means(a.fetch, "FETCH_SIZE", a.kernel)
-    w_mean, w_n, w_copy = counter_means(a.write, "WRITE_SIZE", a.kernel)
+    f_sum, f_n, f_copy = counter_sum(a.fetch, "FETCH_SIZE", a.kernel, n_timed)
+    w_sum, w_n, w_copy = counter_sum(a.write, "WRITE_SIZE", a.kernel, n_timed)
     f_scale = (COPY_BYTES / 1024) / f_copy
     w_scale = (COPY_BYTES / 1024) / w_copy
-    traffic = round(f_mean * 1024 * f_scale + w_mean * 1024 * w_scale)
+    traffic_total = f_sum * 1024 * f_scale + w_sum * 1024 * w_scale
 
     lines = [f"# rocprofv3 summary: {a.title or a.kernel}", ""]
     if a.command:
@@ -227,68 +235,78 @@ def main():
     for r in stats:
         lines.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
-    lines += ["", f"Kernel `{names[0] if len(names) == 1 else names}`:", "",
-              f"- dispatches traced: {len(dur)}; mean {statistics.fmean(dur):.2f} us",
-              f"- the {len(timed)} timed dispatches (the last ones): mean {t_mean:.2f} us, "
-              f"median {statistics.median(timed):.2f} us",
-              f"- the profiled command's own per-launch HIP-event mean: {ev:.2f} us "
-              f"(trace / events = {t_mean / ev:.3f})",
-              f"- algorithmic bytes per launch: {alg / 1e6:.2f} MB, i.e. "
-              f"{alg / t_mean / 1e3:.1f} GB/s at the traced mean"]
-    if bench.get("avg_launch_gflop"):
-        lines.append(f"- algorithmic work per launch: {bench['avg_launch_gflop']:.3f} GFLOP, i.e. "
-                     f"{bench['avg_launch_gflop'] / t_mean * 1e3:.1f} TFLOP/s at the traced mean")
+    lines += ["", "Timed region: the last "
+              f"{n_timed} dispatches whose name contains `{a.kernel}` ({calls} library calls); "
+              f"kernels among them:", ""]
+    lines += [f"- `{n[:150]}`" for n in names]
+    lines += ["",
+              f"- traced kernel time: {t_total / 1e3:.3f} ms in total, {t_total / n_timed:.2f} us per "
+              f"dispatch, {t_total / calls:.2f} us per call"]
+    if bench.get("hip_event_total_ms"):
+        ev = bench["hip_event_total_ms"] * 1e3
+        lines.append(f"- the profiled command's own per-call HIP events: {ev / 1e3:.3f} ms in total "
+                     f"(trace / events = {t_total / ev:.3f})")
+    lines.append(f"- algorithmic bytes: {alg / 1e6:.2f} MB, i.e. {alg / t_total / 1e3:.1f} GB/s over "
+                 f"the traced time")
+    if gflop:
+        lines.append(f"- algorithmic work: {gflop:.3f} GFLOP, i.e. {gflop / t_total * 1e3:.1f} TFLOP/s "
+                     f"over the traced time")
     lines += ["", "## HBM-side traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
-              "| counter | kernel KiB / dispatch (raw) | dispatches | 1 GiB copy (raw KiB) | scale | "
-              "kernel MB / dispatch (scaled) |", "|---|---|---|---|---|---|",
-              f"| FETCH_SIZE | {f_mean:.1f} | {f_n} | {f_copy:.1f} | {f_scale:.4f} | "
-              f"{f_mean * 1024 * f_scale / 1e6:.2f} |",
-              f"| WRITE_SIZE | {w_mean:.1f} | {w_n} | {w_copy:.1f} | {w_scale:.4f} | "
-              f"{w_mean * 1024 * w_scale / 1e6:.2f} |", "",
-              f"Scaled traffic per dispatch: {traffic / 1e6:.2f} MB, against {alg / 1e6:.2f} MB "
-              f"algorithmic ({traffic / alg:.2f}x).", "",
+              "| counter | timed dispatches | kernel KiB (raw, summed) | 1 GiB copy (raw KiB) | scale | "
+              "kernel MB (scaled) |", "|---|---|---|---|---|---|",
+              f"| FETCH_SIZE | {f_n} | {f_sum:.1f} | {f_copy:.1f} | {f_scale:.4f} | "
+              f"{f_sum * 1024 * f_scale / 1e6:.2f} |",
+              f"| WRITE_SIZE | {w_n} | {w_sum:.1f} | {w_copy:.1f} | {w_scale:.4f} | "
+              f"{w_sum * 1024 * w_scale / 1e6:.2f} |", "",
+              f"Scaled traffic: {traffic_total / 1e6:.2f} MB over the timed region "
+              f"({traffic_total / calls / 1e6:.2f} MB per call), against {alg / 1e6:.2f} MB "
+              f"algorithmic ({traffic_total / alg:.2f}x).", "",
               f"Kernel source: {top['src_file']}, sha256[:16] {top['src_hash']}"]
     util = None
     if a.util:
-        ds = counter_timed_dispatches(a.util, UTIL_COUNTERS, a.kernel, bench["timed_launches"])
-        mean = {c: statistics.fmean(d[c] for d in ds) for c in UTIL_COUNTERS + ("us",)}
-        cyc = mean["GRBM_GUI_ACTIVE"] / 8               # shader cycles of one dispatch
-        mfma, cu_busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"], mean["SQ_BUSY_CU_CYCLES"]
-        mhz = cyc / mean["us"]
-        need = bench["avg_launch_gflop"] * 1e9 / (a.peak_flop_per_cu_cycle / 4)  # SIMD-cycles
+        ds = counter_timed_dispatches(a.util, UTIL_COUNTERS, a.kernel, n_timed)
+        tot = {c: sum(d[c] for d in ds) for c in UTIL_COUNTERS + ("us",)}
+        cyc = tot["GRBM_GUI_ACTIVE"] / 8               # shader cycles of the dispatches
+        mfma, cu_busy = tot["SQ_VALU_MFMA_BUSY_CYCLES"], tot["SQ_BUSY_CU_CYCLES"]
+        mhz = cyc / tot["us"]
         util = {"effective_clock_mhz": round(mhz, 1),
                 "peak_at_clock_tflops": round(256 * a.peak_flop_per_cu_cycle * mhz / 1e6, 1),
                 "busy_cus_mean": round(cu_busy / cyc, 1),
                 "mfma_active_of_busy_cu_cycles": round(mfma / (4 * cu_busy), 4),
-                "mfma_active_of_all_cu_cycles": round(mfma / (4 * 256 * cyc), 4),
-                "mfma_issued_per_algorithmic": round(mfma / need, 4)}
+                "mfma_active_of_all_cu_cycles": round(mfma / (4 * 256 * cyc), 4)}
+        if gflop:
+            need = gflop * 1e9 / (a.peak_flop_per_cu_cycle / 4)  # SIMD-cycles
+            util["mfma_issued_per_algorithmic"] = round(mfma / need, 4)
         lines += ["", "## Clock and MFMA activity (--pmc " + " ".join(UTIL_COUNTERS) + ")", "",
-                  f"Means over the last {len(ds)} dispatches of the counter run (its own "
-                  f"timestamps: {mean['us']:.2f} us per dispatch):", "",
-                  "| counter | per dispatch |", "|---|---|"]
-        lines += [f"| {c} | {mean[c]:.5g} |" for c in UTIL_COUNTERS]
+                  f"Sums over the last {len(ds)} dispatches of the counter run (its own timestamps: "
+                  f"{tot['us'] / 1e3:.3f} ms of kernel time):", "",
+                  "| counter | total |", "|---|---|"]
+        lines += [f"| {c} | {tot[c]:.5g} |" for c in UTIL_COUNTERS]
         lines += ["",
-                  f"- dispatch length: GRBM_GUI_ACTIVE / 8 XCDs = {cyc:.4g} cycles; over "
-                  f"{mean['us']:.2f} us, an effective clock of {mhz:.0f} MHz (nominal 2400; an "
-                  f"upper bound, the count includes the dispatch's set-up and drain)",
-                  f"- MFMA work issued: {mfma:.4g} SIMD-cycles, {mfma / need:.3f}x the "
-                  f"algorithmic FLOPs at {a.peak_flop_per_cu_cycle / 4:.0f} FLOP per SIMD-cycle "
-                  f"(the excess is padded rows of partial tiles)",
-                  f"- busy CUs: SQ_BUSY_CU_CYCLES / dispatch cycles = {cu_busy / cyc:.1f} of 256 "
-                  f"on average",
+                  f"- length: GRBM_GUI_ACTIVE / 8 XCDs = {cyc:.4g} cycles; over "
+                  f"{tot['us'] / 1e3:.3f} ms, an effective clock of {mhz:.0f} MHz (nominal 2400; an "
+                  f"upper bound, the count includes each dispatch's set-up and drain)",
+                  f"- busy CUs: SQ_BUSY_CU_CYCLES / cycles = {cu_busy / cyc:.1f} of 256 on average",
                   f"- matrix cores of the busy CUs: MFMA SIMD-cycles / (4 x busy CU-cycles) = "
                   f"{mfma / (4 * cu_busy):.3f}",
-                  f"- matrix cores of the whole chip over the dispatch: {mfma / (4 * 256 * cyc):.3f}"]
+                  f"- matrix cores of the whole chip: {mfma / (4 * 256 * cyc):.3f}"]
+        if gflop:
+            lines.append(f"- MFMA work issued: {mfma:.4g} SIMD-cycles, {util['mfma_issued_per_algorithmic']:.3f}x "
+                         f"the algorithmic FLOPs at {a.peak_flop_per_cu_cycle / 4:.0f} FLOP per "
+                         f"SIMD-cycle (the excess is padded rows of partial tiles)")
     with open(a.out, "w") as f:
         f.write("\n".join(lines) + "\n")
     if a.traffic:
         with open(a.traffic, "w") as f:
-            json.dump({"src_file": top["src_file"], "src_hash": top["src_hash"], "kernel": a.kernel,
-                       "qkv_gemm_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": alg,
-                       "fetch_kib_per_dispatch_raw": round(f_mean, 2), "fetch_scale": round(f_scale, 5),
-                       "write_kib_per_dispatch_raw": round(w_mean, 2), "write_scale": round(w_scale, 5),
-                       "trace_mean_us": round(t_mean, 3), "hip_event_mean_us": ev,
-                       "util": util}, f, indent=1)
+            json.dump({"workload": top.get("profile_pass"), "src_file": top["src_file"],
+                       "src_hash": top["src_hash"], "kernel": a.kernel,
+                       "source": os.path.relpath(a.out),
+                       "bytes_per_call": round(traffic_total / calls),
+                       "algorithmic_bytes_per_call": round(alg / calls),
+                       "traffic_over_algorithmic": round(traffic_total / alg, 4),
+                       "fetch_kib_raw_total": round(f_sum, 2), "fetch_scale": round(f_scale, 5),
+                       "write_kib_raw_total": round(w_sum, 2), "write_scale": round(w_scale, 5),
+                       "trace_us_per_call": round(t_total / calls, 3), "util": util}, f, indent=1)
             f.write("\n")
     print("\n".join(lines))
 

@@ -46,8 +46,8 @@ EXPORTS = (
     "ub_quantize_in",
     "ub_gemm_ag_chunked_fp8", "ub_gemm_rs_chunked", "ub_gemm_rs_chunked_fp8",
     "ub_quantize_e4m3", "ub_reduce_partials",
-    "ub_set_kernel_timing", "ub_get_kernel_timing", "ub_destroy", "ub_status_string",
-    "ub_last_error",
+    "ub_set_kernel_timing", "ub_get_kernel_timing", "ub_prepare_streams", "ub_debug_set",
+    "ub_debug_last_plan", "ub_destroy", "ub_status_string", "ub_last_error",
 )
 
 
@@ -68,6 +68,11 @@ class ub_overlap_cfg_t(ctypes.Structure):
 class ub_plan_unit_t(ctypes.Structure):
     _fields_ = [("pos", ctypes.c_int32), ("unit", ctypes.c_int32), ("row0", ctypes.c_int64),
                 ("row1", ctypes.c_int64), ("stream", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class ub_tile_plan_t(ctypes.Structure):
+    _fields_ = [("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("cut_row", ctypes.c_int64),
+                ("tail_tile_m", ctypes.c_int32), ("tail_tile_n", ctypes.c_int32)]
 
 
 class ub_kernel_stats_t(ctypes.Structure):
@@ -105,6 +110,9 @@ _sig = {
     "ub_set_kernel_timing": (_I32, [_H, _I32]),
     "ub_get_kernel_timing": (_I32, [_H, ctypes.POINTER(ub_kernel_stats_t),
                                     ctypes.POINTER(ub_kernel_stats_t)]),
+    "ub_prepare_streams": (_I32, [_H, _I32, _I32]),
+    "ub_debug_set": (_I32, [_H, ctypes.c_char_p, _I64]),
+    "ub_debug_last_plan": (_I32, [_H, ctypes.POINTER(ub_tile_plan_t)]),
     "ub_destroy": (_I32, [_H]),
     "ub_status_string": (ctypes.c_char_p, [_I32]),
     "ub_last_error": (ctypes.c_char_p, [_H]),
@@ -182,7 +190,19 @@ def ub_required_bytes(capacity, hidden, tp_size, dtype=UB_DTYPE_BF16):
     return a.value, b.value
 
 
+def _fits(buf, nbytes, what):
+    """A tensor passed with a byte count must hold that many bytes (the library trusts the
+    count and addresses up to it)."""
+    if hasattr(buf, "numel") and hasattr(buf, "element_size"):
+        have = buf.numel() * buf.element_size()
+        if int(nbytes) > have:
+            raise ValueError(f"{what}: {int(nbytes)} bytes declared, the tensor holds {have}")
+
+
 def ub_init(capacity, hidden, tp_size, dtype, ub_buf, ub_bytes, rs_ws=None, rs_ws_bytes=0):
+    _fits(ub_buf, ub_bytes, "ub_buf")
+    if rs_ws is not None:
+        _fits(rs_ws, rs_ws_bytes, "rs_ws")
     h = _H()
     _check(_lib.ub_init(ctypes.byref(h), capacity, hidden, tp_size, dtype, _ptr(ub_buf),
                         int(ub_bytes), _ptr(rs_ws), int(rs_ws_bytes)))
@@ -295,6 +315,21 @@ def ub_get_kernel_timing(h):
     _check(_lib.ub_get_kernel_timing(h, ctypes.byref(g), ctypes.byref(r)), h)
     conv = lambda s: {"launches": s.launches, "total_ms": s.total_ms, "flops": s.flops, "bytes": s.bytes}
     return conv(g), conv(r)
+
+
+def ub_prepare_streams(h, num_max_streams=3, copy_stream=False):
+    _check(_lib.ub_prepare_streams(h, int(num_max_streams), int(bool(copy_stream))), h)
+
+
+def ub_debug_set(h, key, value):
+    _check(_lib.ub_debug_set(h, key.encode(), int(value)), h)
+
+
+def ub_debug_last_plan(h):
+    """Returns (tile_m, tile_n, cut_row, tail_tile_m, tail_tile_n) of the last GEMM launch group."""
+    p = ub_tile_plan_t()
+    _check(_lib.ub_debug_last_plan(h, ctypes.byref(p)), h)
+    return p.tile_m, p.tile_n, p.cut_row, p.tail_tile_m, p.tail_tile_n
 
 
 def ub_destroy(h):

@@ -40,8 +40,10 @@
  *     multiples of 8 (16-byte rows; 16 for fp8).
  *   - Every device buffer is owned by the caller (allocated by PyTorch or hipMalloc) and
  *     must outlive the handle.  The library never allocates, frees or registers device
- *     memory.  A handle owns only host state and its HIP streams and events (created on
- *     first use; ub_gemm_ag_arrival adds a copy stream and one event per chunk).
+ *     memory, and no call makes a device-wide wait.  A handle owns only host state and its
+ *     HIP streams and events (created by ub_prepare_streams, or on first use;
+ *     ub_gemm_ag_arrival adds a copy stream and one event per chunk).  The library's only
+ *     device memory of its own is a fixed array of arrival flags in its code object.
  *   - Functions return a ub_status_t; no C++ exception crosses the ABI.  Arguments are
  *     checked before anything is launched; a rejected call changes no state and enqueues
  *     nothing.  ub_last_error() returns a message for the last failure on a handle.
@@ -105,7 +107,8 @@ typedef enum {
   UB_DTYPE_BF16 = 0,
   UB_DTYPE_FP16 = 1,
   UB_DTYPE_FP8_E4M3 = 2,
-  UB_DTYPE_FP8_E5M2 = 3
+  UB_DTYPE_FP8_E5M2 = 3,
+  UB_DTYPE_INT32_RANGE_ = 0x7FFFFFFF /* not a type: any int32 value may be passed and is checked */
 } ub_dtype_t;
 
 /* Overlap method ([TE#1344] "method"). */
@@ -116,20 +119,19 @@ typedef enum {
 } ub_method_t;
 
 /* Which side of the overlap a plan describes. */
-typedef enum { UB_OP_AG = 0, UB_OP_RS = 1 } ub_op_t;
+typedef enum { UB_OP_AG = 0, UB_OP_RS = 1, UB_OP_INT32_RANGE_ = 0x7FFFFFFF } ub_op_t;
 
 /* Per-call overlap options: the keys of [TE#1344]'s option list.
  *   num_splits       chunks the GEMM is cut into (>= 1); ignored for ring exchange,
  *                    which uses tp_size chunks.
  *   num_max_streams  compute streams = min(chunks, num_max_streams, UB_MAX_STREAMS), >= 1.
- *                    Default 3.  The handle creates its worker streams on first use.
- *                    They overlap with the caller's stream only on hardware queues of
- *                    their own: HIP places streams on GPU_MAX_HW_QUEUES queues, and
- *                    streams that share one run in issue order.  Measured on qkv with 3
- *                    streams: 440 TFLOP/s when the handle's first call came before the
- *                    process's other streams were in use, ~320 when it came after.
- *                    Make a first call early, and raise GPU_MAX_HW_QUEUES in processes
- *                    with many streams.
+ *                    Default 3.  The handle's worker streams overlap with the caller's
+ *                    stream only on hardware queues of their own: HIP places streams on
+ *                    GPU_MAX_HW_QUEUES queues (4 by default) in creation order, and streams
+ *                    that share one run in issue order.  ub_prepare_streams creates them
+ *                    right after registration, before the process's other streams, so that
+ *                    they take queues of their own; otherwise the first call that needs
+ *                    them creates them.
  *   aggregate        all-gather side only: chunks {2u, 2u+1} are merged into one launch.
  *   atomic_gemm      0: one kernel launch per unit from a host loop on the compute
  *                    streams; 1: one kernel on the caller's stream whose workgroups walk
@@ -159,13 +161,10 @@ typedef enum { UB_OP_AG = 0, UB_OP_RS = 1 } ub_op_t;
  *                    tile to finish sums the tp partials ([TE#1344] "pipeline": the
  *                    GEMM chunks feed the reduce-scatter; here with no separate pass).  The
  *                    partials still go through the workspace, and out is bit-identical to
- *                    fuse_reduce 0 for either reduce_order.  The first fused call on a
- *                    handle (and one whose plan needs more tiles than any before) allocates
- *                    a small counter array, one 4-byte word per possible output tile
- *                    (tiles of 128 x 128), and zeroes it on `stream`; a larger array
- *                    replaces a smaller one after a device-wide wait.  It is freed by
- *                    ub_destroy.  Such a call must not be captured into a graph; later
- *                    calls may be. */
+ *                    fuse_reduce 0 for either reduce_order.  The tiles count their arrival
+ *                    in the workspace's counter region (see ub_required_bytes), which every
+ *                    launch leaves at zero; nothing is allocated or cleared on the call, so
+ *                    any fused call may be captured into a graph. */
 typedef enum { UB_REDUCE_ASCENDING = 0, UB_REDUCE_RING = 1 } ub_reduce_order_t;
 
 typedef struct {
@@ -208,9 +207,14 @@ UB_API void ub_overlap_cfg_default(ub_overlap_cfg_t* cfg);
 
 /* Bytes the caller must allocate for a registration of [capacity, hidden] over
  * tp_size ranks: the UB itself (capacity * hidden * element size: 2 for bf16, 1 for
- * fp8) and the reduce-scatter workspace of tp_size bf16 partial slots
- * (tp_size * capacity * hidden * 2; 0 for fp8, which has no reduce-scatter side).  Same
- * validation as ub_init.  Either output pointer may be NULL. */
+ * fp8) and the reduce-scatter workspace (0 for fp8, which has no reduce-scatter side).
+ * The workspace holds the tp_size bf16 partial slots (tp_size * capacity * hidden * 2
+ * bytes, [TE#3564] "Implementation approach": reduce-scatter keeps its per-rank chunks in
+ * its own capacity-sized allocation) and, from the next 256-byte boundary, the fused
+ * reduction's tile counters: 4 bytes per 128 x 128 output tile of a launch over up to
+ * capacity rows, one range per compute stream (UB_MAX_STREAMS of them), sized once here
+ * from the capacity (~129 KiB for capacity 16384, hidden 4096).  Same validation as
+ * ub_init.  Either output pointer may be NULL. */
 UB_API ub_status_t ub_required_bytes(int64_t capacity, int64_t hidden, int32_t tp_size,
                                      ub_dtype_t dtype, size_t* ub_bytes,
                                      size_t* rs_workspace_bytes);
@@ -224,12 +228,15 @@ UB_API ub_status_t ub_required_bytes(int64_t capacity, int64_t hidden, int32_t t
  *   dtype             UB_DTYPE_BF16 or UB_DTYPE_FP8_E4M3, else UB_ERR_DTYPE.
  *   ub_buf, ub_bytes  device memory of at least capacity*hidden*element-size bytes
  *                     (16-byte aligned), else UB_ERR_BUFFER_TOO_SMALL / UB_ERR_INVALID_ARG.
- *   rs_ws, rs_ws_bytes reduce-scatter workspace of at least tp_size*capacity*hidden*2
- *                     bytes, or NULL/0 when the reduce-scatter side is not used (always
- *                     NULL/0 for fp8, else UB_ERR_INVALID_ARG).
+ *   rs_ws, rs_ws_bytes reduce-scatter workspace of at least the size ub_required_bytes
+ *                     reports, or NULL/0 when the reduce-scatter side is not used (always
+ *                     NULL/0 for fp8, else UB_ERR_INVALID_ARG).  Its counter region (the
+ *                     bytes past the partial slots) must be zero at registration, e.g.
+ *                     allocated with torch.zeros; every call leaves it zero.
  * Records the pointers and sizes; allocates no device memory and makes no HIP call
- * (streams and events are created on the first GEMM call, on the device current then).
- * On success *out is a new handle whose active shape is [capacity, hidden]. */
+ * (streams and events are created by ub_prepare_streams or on the first GEMM call, on the
+ * device current then).  On success *out is a new handle whose active shape is
+ * [capacity, hidden]. */
 UB_API ub_status_t ub_init(ub_handle_t* out, int64_t capacity, int64_t hidden,
                            int32_t tp_size, ub_dtype_t dtype, void* ub_buf, size_t ub_bytes,
                            void* rs_ws, size_t rs_ws_bytes);
@@ -271,8 +278,9 @@ UB_API ub_status_t ub_copy_in(ub_handle_t h, const void* src, int64_t rows,
  * stride ldw >= n_cols, C [T, n_cols] with row stride ldc >= n_cols.  The rows are cut
  * into the plan's units; unit u is one GEMM reading the UB at byte offset
  * row0_u * hidden * 2.  Reads no UB byte beyond T*hidden elements; writes only C rows
- * [0, T).  n_cols, ldw, ldc multiples of 8; hidden a multiple of 64 (else
- * UB_ERR_UNSUPPORTED).  aggregate is honoured; W and C are caller memory.  Needs a bf16
+ * [0, T).  n_cols, ldw, ldc and hidden multiples of 8 (16-byte rows); a hidden that is not
+ * a multiple of the kernel's 32-deep k-step is handled by masking the last step's
+ * k-chunks past hidden.  aggregate is honoured; W and C are caller memory.  Needs a bf16
  * handle, as do ub_gemm_ag_arrival, ub_deliver_chunks, ub_gemm_rs_chunked and
  * ub_reduce_partials (else UB_ERR_DTYPE). */
 UB_API ub_status_t ub_gemm_ag_chunked(ub_handle_t h, const void* w, int64_t n_cols,
@@ -338,8 +346,9 @@ UB_API ub_status_t ub_gemm_ag_chunked_fp8(ub_handle_t h, const void* w, int64_t 
  *     - Deliveries must be SDMA copies: use_ce = 1 or a host source.  Otherwise
  *       UB_ERR_UNSUPPORTED, because the runtime's copy kernel would need CUs that waiting
  *       tiles hold.
- *     - A tile's wait is bounded (~0.5 s); past it the tile goes on, and the wait is
- *       counted (ub_arrival_timeouts).
+ *     - A tile's wait is bounded (~0.5 s); past it the tile stores bf16 NaN (0x7FC0)
+ *       over its whole output instead of computing from rows that may not have arrived,
+ *       and counts one timeout (ub_arrival_timeouts).
  *     - The flags live in a fixed device array of 64 slots, one per handle, taken on its
  *       first such call and returned by ub_destroy; a 65th handle gets
  *       UB_ERR_UNSUPPORTED.
@@ -357,12 +366,11 @@ UB_API ub_status_t ub_gemm_ag_arrival(ub_handle_t h, const void* src, int32_t sr
                                       int64_t ldc, const ub_overlap_cfg_t* cfg,
                                       ub_stream_t stream);
 
-/* Number of tile waits in the device-side chunk loop of ub_gemm_ag_arrival that hit the
+/* Number of tiles of the device-side chunk loop of ub_gemm_ag_arrival whose wait hit the
  * time bound on this handle's flag slot since the handle took the slot (0 if the handle
  * never gated on arrivals; ub_destroy clears the count, so a slot handed to a later handle
- * starts from zero).  A nonzero count means a chunk's flag never
- * came, and the results of that call are not to be trusted.  Synchronous (copies one word
- * from the device). */
+ * starts from zero).  A nonzero count means a chunk's flag never came; those tiles hold
+ * NaN.  Synchronous (copies one word from the device). */
 UB_API ub_status_t ub_arrival_timeouts(ub_handle_t h, uint32_t* count);
 
 /* The deliveries of ub_gemm_ag_arrival alone (same copies, order, stream and kind, no
@@ -382,7 +390,8 @@ UB_API ub_status_t ub_deliver_chunks(ub_handle_t h, const void* src, int32_t src
  * [r T/tp, (r+1) T/tp), contiguous.
  * A is [T, k] (row stride lda >= k), W is [k, hidden] (row stride ldw >= hidden), out is
  * [T, hidden] (row stride ldo >= hidden).  k % tp_size == 0 (else INVALID_ARG) and
- * Ks % 64 == 0 (else UNSUPPORTED).  Requires a registered workspace (else
+ * Ks % 8 == 0, so that every slice starts on a 16-byte boundary (else UNSUPPORTED).
+ * Requires a registered workspace (else
  * NOT_INITIALIZED).  aggregate is ignored (it is an all-gather option).  Writes nothing
  * beyond tp_size*T*hidden workspace elements or beyond T rows of out. */
 UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, int64_t lda,
@@ -440,8 +449,47 @@ UB_API ub_status_t ub_set_kernel_timing(ub_handle_t h, int32_t enable);
 UB_API ub_status_t ub_get_kernel_timing(ub_handle_t h, ub_kernel_stats_t* gemm,
                                         ub_kernel_stats_t* reduce);
 
+/* Create the handle's compute streams now, on the current device: the worker streams
+ * (and events) that calls with up to num_max_streams streams use (clamped to
+ * UB_MAX_STREAMS), and, when copy_stream is nonzero, the copy stream of
+ * ub_gemm_ag_arrival.  Optional: a call creates what it needs the first time; creating
+ * them right after registration gives them hardware queues of their own before the
+ * process's other streams take them (see num_max_streams).  num_max_streams < 1 ->
+ * UB_ERR_INVALID_ARG; a handle is bound to the device current at its first HIP call. */
+UB_API ub_status_t ub_prepare_streams(ub_handle_t h, int32_t num_max_streams,
+                                      int32_t copy_stream);
+
+/* Tile plan of the last GEMM launch group of a handle (ub_debug_last_plan). */
+typedef struct {
+  int32_t tile_m, tile_n;            /* tile of the (first) launch */
+  int64_t cut_row;                   /* -1: one launch; else the first row of a second launch */
+  int32_t tail_tile_m, tail_tile_n;  /* tile of the second launch (0 without one) */
+} ub_tile_plan_t;
+
+/* Debug and tuning settings of one handle, for tests and tile tuning; each starts at 0,
+ * which leaves every choice to the library.  No environment variable changes what the
+ * library computes.  Keys:
+ *   "tile_m", "tile_n"     force this tile shape for every GEMM launch of the handle (one
+ *                          launch per unit group, no cut).  Calls fail with
+ *                          UB_ERR_INVALID_ARG if their kernel has no such tile (bf16:
+ *                          320x256, 256x256, 128x256, 128x128; fp8: 256x256, 128x256).
+ *                          Results do not depend on the tile.
+ *   "cut_row"              > 0: a bf16 launch group whose rows span this row (a band
+ *                          boundary of its first tile) runs as two launches, the rows from
+ *                          cut_row on with the tile "tail_tile_m" x "tail_tile_n" (default
+ *                          128x128); the first launch takes the forced tile, or 256x256.
+ *                          Results do not depend on the cut.
+ *   "tile_group"           row tiles per group in the workgroup -> tile map (>= 1).
+ *   "arrival_wait_us"      bound of a gated tile's wait in ub_gemm_ag_arrival, in
+ *                          microseconds (0: ~0.5 s).
+ *   "arrival_drop_flags"   1: write no ready flag after the delivered chunks, so that the
+ *                          tiles that need them run into the bound (a test of that path).
+ * Unknown keys and out-of-range values -> UB_ERR_INVALID_ARG. */
+UB_API ub_status_t ub_debug_set(ub_handle_t h, const char* key, int64_t value);
+UB_API ub_status_t ub_debug_last_plan(ub_handle_t h, ub_tile_plan_t* out);
+
 /* Destroy a handle: waits for the handle's own streams, then releases its streams,
- * events, arrival-flag slot and fused-reduction counters.  The caller's streams are not waited for: work of this
+ * events and arrival-flag slot.  The caller's streams are not waited for: work of this
  * handle still queued there must have finished (the caller synchronises first), or a
  * device-side loop of a gated arrival could wait on a slot that another handle has taken
  * (it would end at its time bound, with wrong results).  Caller buffers are untouched.

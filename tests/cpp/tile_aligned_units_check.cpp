@@ -22,7 +22,7 @@ int main() {
     for (int i = 0; i < n; ++i) { r0[i] = r; r += sizes[i]; }
     int hi = r;
     for (int i = 0; i < n; ++i) { u.row0[i] = r0[perm[i]]; u.rows[i] = sizes[perm[i]]; }
-    int bm = (int[]){128, 192, 256}[rand() % 3];
+    int bm = (int[]){128, 256, 320}[rand() % 3];
     GemmUnits s = tile_aligned_units(u, bm);
     std::vector<int> cover(hi, 0);
     int prev_unit_pos = -1;

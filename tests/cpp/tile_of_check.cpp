@@ -22,7 +22,7 @@ int main() {
   long checks = 0;
   for (int it = 0; it < 20000; ++it) {
     P p{};
-    const int bm = (int[]){128, 192, 256}[rand() % 3];
+    const int bm = (int[]){128, 256, 320}[rand() % 3];
     p.group = (int[]){1, 2, 4, 8}[rand() % 4];
     p.tiles_n = 1 + rand() % 40;
     p.n_units = 1 + rand() % 64;

@@ -19,12 +19,36 @@ def host(t):
     return t.cpu().numpy().view(np.uint16)
 
 
+def force_tile(ub, h, tile):
+    """Force a tile shape ("MxN") on handle h through its debug settings, or None for the
+    library's own choice."""
+    m, n = (0, 0) if tile is None else map(int, tile.split("x"))
+    ub.ub_debug_set(h, "tile_m", m)
+    ub.ub_debug_set(h, "tile_n", n)
+
+
+BF16_TILES = ("320x256", "256x256", "128x256", "128x128")
+
+
 def canary(shape):
     return torch.full(shape, CANARY, dtype=torch.int16, device="cuda")
 
 
+def workspace(ub, capacity, hidden, tp, pad_rows=0):
+    """A reduce-scatter workspace of the size ub_required_bytes reports, plus pad_rows rows
+    of canary after it: the partial slots canary-filled, the counter region after them zero
+    (as ub_init requires).  Returns (whole allocation, view of the partial slots, bytes)."""
+    _, ws_bytes = ub.ub_required_bytes(capacity, hidden, tp)
+    parts = tp * capacity * hidden
+    whole = canary((ws_bytes // 2 + pad_rows * hidden,))
+    whole[parts: ws_bytes // 2].zero_()
+    return whole, whole[:parts], ws_bytes
+
+
 class Registration:
-    """A UB of [capacity, hidden] (+ workspace), canary-filled, registered with ub_init."""
+    """A UB of [capacity, hidden] (+ workspace), canary-filled, registered with ub_init.
+    ws_t views the workspace's partial slots; ws_counters its counter region, which every
+    call must leave zero; ws_pad the canary past the registered workspace."""
 
     def __init__(self, ub, capacity, hidden, tp, workspace=True, pad_rows=0):
         self.ub_mod = ub
@@ -32,9 +56,18 @@ class Registration:
         ub_bytes, ws_bytes = ub.ub_required_bytes(capacity, hidden, tp)
         # pad_rows extra canary rows after the registered region catch reads/writes past it
         self.ub_t = canary(((capacity + pad_rows) * hidden,))
-        self.ws_t = canary(((tp * capacity + pad_rows) * hidden,)) if workspace else None
+        self.ws_all = self.ws_t = None
+        if workspace:
+            self.ws_all, self.ws_t, _ = globals()["workspace"](ub, capacity, hidden, tp, pad_rows)
+            self.ws_counters = self.ws_all[tp * capacity * hidden: ws_bytes // 2]
+            self.ws_pad = self.ws_all[ws_bytes // 2:]
         self.h = ub.ub_init(capacity, hidden, tp, ub.UB_DTYPE_BF16, self.ub_t, ub_bytes,
-                            self.ws_t, ws_bytes if workspace else 0)
+                            self.ws_all, ws_bytes if workspace else 0)
+
+    def counters_clean(self):
+        """The counter region is back at zero and the canary past the workspace intact."""
+        torch.cuda.synchronize()
+        return bool((self.ws_counters == 0).all().item()) and bool((self.ws_pad == CANARY).all().item())
 
     def set_T(self, T):
         self.ub_mod.ub_set_active_shape(self.h, (T, self.hidden))

@@ -31,7 +31,7 @@ def main():
     src = torch.from_numpy(a.view(np.int16).ravel()).cuda()
     ub_bytes, ws_bytes = ub.ub_required_bytes(cap, H, tp)
     ub_t = torch.zeros(cap * H, dtype=torch.int16, device="cuda")
-    ws_t = torch.zeros(tp * cap * H, dtype=torch.int16, device="cuda")
+    ws_t = torch.zeros(ws_bytes // 2, dtype=torch.int16, device="cuda")
     h = ub.ub_init(cap, H, tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes, ws_t, ws_bytes)
     try:
         ub.ub_set_active_shape(h, (T, H))

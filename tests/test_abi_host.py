@@ -52,8 +52,20 @@ def _handle(capacity, hidden, tp, ws=True):
                       FAKE if ws else None, ws_bytes if ws else 0)
 
 
+def _ws_bytes(cap, hid, tp):
+    """The workspace the header describes: tp partial slots of [cap, hid] bf16, then, from the
+    next 256-byte boundary, 4-byte tile counters: UB_MAX_STREAMS ranges of (cap/128 + 1) x
+    (hid/128) words, or (cap/128 + 64) x (hid/128) for the device-side loop if larger."""
+    parts = tp * cap * hid * 2
+    rt, ct = -(-cap // 128), -(-hid // 128)
+    words = max(ub.UB_MAX_STREAMS * (rt + 1) * ct, (rt + 64) * ct)
+    return -(-parts // 256) * 256 + 4 * words
+
+
 def test_required_bytes_and_registration_errors():
-    assert ub.ub_required_bytes(8192, 4096, 8) == (8192 * 4096 * 2, 8 * 8192 * 4096 * 2)
+    assert ub.ub_required_bytes(8192, 4096, 8) == (8192 * 4096 * 2, _ws_bytes(8192, 4096, 8))
+    assert ub.ub_required_bytes(8192, 4096, 8)[1] == 8 * 8192 * 4096 * 2 + 4 * 8 * 65 * 32
+    assert ub.ub_required_bytes(200, 264, 2)[1] == _ws_bytes(200, 264, 2)
     assert ub.ub_required_bytes(512, 256, 2, ub.UB_DTYPE_FP8_E4M3) == (512 * 256, 0)
     for dt in (ub.UB_DTYPE_FP8_E5M2, ub.UB_DTYPE_FP16, 9):
         with pytest.raises(ub.UBError) as e:
@@ -178,7 +190,7 @@ def test_gemm_argument_errors_before_any_hip_call():
         # reduce-scatter
         assert st("ub_gemm_rs_chunked", h_nows, FAKE, 256, 256, FAKE, 256, FAKE, 256, cp, None) == "UB_ERR_NOT_INITIALIZED"
         assert st("ub_gemm_rs_chunked", h, FAKE, 255, 256, FAKE, 256, FAKE, 256, cp, None) == "UB_ERR_INVALID_ARG"
-        assert st("ub_gemm_rs_chunked", h, FAKE, 96, 96, FAKE, 256, FAKE, 256, cp, None) == "UB_ERR_UNSUPPORTED"
+        assert st("ub_gemm_rs_chunked", h, FAKE, 36, 40, FAKE, 256, FAKE, 256, cp, None) == "UB_ERR_UNSUPPORTED"
         assert st("ub_gemm_rs_chunked", h, FAKE, 256, 248, FAKE, 256, FAKE, 256, cp, None) == "UB_ERR_INVALID_ARG"
         assert st("ub_gemm_rs_chunked", h, FAKE, 256, 256, FAKE, 256, FAKE, 128, cp, None) == "UB_ERR_INVALID_ARG"
         bad = ub.make_cfg("ring_exchange", 2, reduce_order=2)
@@ -295,12 +307,28 @@ def test_fp8_handle_argument_errors_before_any_hip_call():
         ub.ub_destroy(h)
 
 
-def test_hidden_not_multiple_of_kstep_is_unsupported():
-    h = _handle(64, 72, 1)
+def test_debug_settings_checked_before_any_hip_call():
+    """ub_debug_set validates keys and ranges; a forced tile the kernel does not build is
+    rejected by the GEMM call before anything is launched; 0/0 restores the library's
+    choice.  Nothing but this entry point changes a handle's launches."""
+    h = _handle(512, 256, 2)
     try:
-        cfg = ub.make_cfg("bulk", 1)
-        st = ub.raw_call("ub_gemm_ag_chunked", h, FAKE, 8, 8, FAKE, 8, ctypes.byref(cfg), None)
-        assert ub.STATUS[st] == "UB_ERR_UNSUPPORTED"
+        for key, val in (("nope", 1), ("tile_m", -1), ("tile_group", -2),
+                         ("arrival_wait_us", -5), ("arrival_drop_flags", 2)):
+            with pytest.raises(ub.UBError) as e:
+                ub.ub_debug_set(h, key, val)
+            assert e.value.name == "UB_ERR_INVALID_ARG"
+        cfg = ub.make_cfg("ring_exchange", 2)
+        ub.ub_debug_set(h, "tile_m", 192)
+        ub.ub_debug_set(h, "tile_n", 256)
+        st = ub.raw_call("ub_gemm_ag_chunked", h, FAKE, 384, 384, FAKE, 384, ctypes.byref(cfg), None)
+        assert ub.STATUS[st] == "UB_ERR_INVALID_ARG" and "192x256" in ub.ub_last_error(h)
+        st = ub.raw_call("ub_gemm_rs_chunked", h, FAKE, 256, 256, FAKE, 256, FAKE, 256,
+                         ctypes.byref(cfg), None)
+        assert ub.STATUS[st] == "UB_ERR_INVALID_ARG"
+        ub.ub_debug_set(h, "tile_m", 0)
+        ub.ub_debug_set(h, "tile_n", 0)
+        assert ub.ub_debug_last_plan(h) == (0, 0, -1, 0, 0)  # no launch yet
     finally:
         ub.ub_destroy(h)
 

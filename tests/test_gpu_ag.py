@@ -124,11 +124,8 @@ def test_closed_forms(ub):
         reg.close()
 
 
-TILES = ("256x256", "192x256", "128x256", "256x128", "128x128")
-
-
-@pytest.mark.parametrize("tile", TILES)
-def test_every_tile_shape(ub, tile, monkeypatch):
+@pytest.mark.parametrize("tile", gu.BF16_TILES)
+def test_every_tile_shape(ub, tile):
     """Each GEMM tile shape, forced: bit-exact on integer inputs with ragged rows, a partial
     column tile and ragged chunks, and bit-identical to the automatic choice on random
     inputs (an output element's bits depend only on its A row and W column)."""
@@ -143,9 +140,8 @@ def test_every_tile_shape(ub, tile, monkeypatch):
     try:
         reg.set_T(T)
         reg.fill(a)
-        monkeypatch.delenv("UBX_GEMM_TILE", raising=False)
         ref = _run(ub, reg, w, N, ub.make_cfg("bulk", 1))[:T]
-        monkeypatch.setenv("UBX_GEMM_TILE", tile)
+        gu.force_tile(ub, reg.h, tile)
         for atomic in (False, True):
             got = _run(ub, reg, w, N, ub.make_cfg("ring_exchange", 8, atomic_gemm=atomic))
             assert np.array_equal(got[:T], ref), atomic
@@ -340,5 +336,42 @@ def test_kernel_timing_counts_launches(ub):
         assert g["total_ms"] > 0
         g2, _ = ub.ub_get_kernel_timing(reg.h)
         assert g2["launches"] == 0  # counters cleared by the read
+    finally:
+        reg.close()
+
+
+@pytest.mark.parametrize("H", (72, 200, 264))
+@pytest.mark.parametrize("tile", gu.BF16_TILES)
+def test_hidden_not_multiple_of_k_step(ub, H, tile):
+    """hidden a multiple of 8 but not of the kernel's 32-deep k-step: the last step's
+    k-chunks past hidden are masked (the next row's elements must not enter the sum).
+    Integer inputs bit-exact against the oracle for every tile shape, with the host loop
+    and the device-side loop; random inputs bit-identical to the automatic plan, within the
+    gate of the oracle; rows >= T untouched.  The UB rows after the active prefix hold
+    canary NaN patterns, which a read past hidden would carry into the last row's sums."""
+    rng = np.random.default_rng(140 + H)
+    cap, N, T, tp = 1024, 264, 600, 8
+    a_int = wl.integer_bits(rng, (T, H))
+    w_int = wl.integer_bits(rng, (H, N))
+    a = wl.normal_bits(rng, (T, H))
+    wr = wl.normal_bits(rng, (H, N), 0.02)
+    print(f"[k tail] H={H} tile={tile}", flush=True)
+    reg = gu.Registration(ub, cap, H, tp, workspace=False, pad_rows=8)
+    try:
+        reg.set_T(T)
+        reg.fill(a_int)
+        oref = _oracle_ag(cap, H, tp, a_int, w_int, _ocfg("pipeline", 3))
+        gu.force_tile(ub, reg.h, tile)
+        for atomic in (False, True):
+            got = _run(ub, reg, gu.dev(w_int), N, ub.make_cfg("pipeline", 3, atomic_gemm=atomic))
+            assert np.array_equal(got[:T], oref), atomic
+            assert np.all(got[T:] == gu.CANARY)
+        reg.fill(a)
+        gu.force_tile(ub, reg.h, None)
+        ref = _run(ub, reg, gu.dev(wr), N, ub.make_cfg("bulk", 1))[:T]
+        gu.check_close(ref, og.ag_rows(a, wr), a, wr, f"k tail H={H}")
+        gu.force_tile(ub, reg.h, tile)
+        got = _run(ub, reg, gu.dev(wr), N, ub.make_cfg("ring_exchange", 8, atomic_gemm=True))
+        assert np.array_equal(got[:T], ref)
     finally:
         reg.close()

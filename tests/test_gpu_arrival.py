@@ -221,19 +221,20 @@ def test_arrival_qkv_full_size(ub):
         reg.close()
 
 
-def test_arrival_device_loop_wait_bound(ub, monkeypatch):
-    """The failure path of the device-side loop's wait, forced from the host: no flag is
-    written for the delivered chunks (UBX_ARRIVAL_DROP_FLAGS=1) and the bound is 2 ms
-    (UBX_ARRIVAL_WAIT_US), so the tiles that need those chunks give up, count timeouts and
-    end: the call returns and nothing hangs.  The tiles of the local chunk, whose flag is
-    written, are still right.  A normal call afterwards is bit-identical to the
-    complete-buffer GEMM and adds no timeout."""
-    monkeypatch.setenv("UBX_GEMM_TILE", "256x256")  # the local chunk is exactly one tile row
+def test_arrival_device_loop_wait_bound(ub):
+    """The failure path of the device-side loop's wait, forced from the host through the
+    handle's debug settings: no flag is written for the delivered chunks
+    (arrival_drop_flags 1) and the bound is 2 ms (arrival_wait_us), so the tiles that need
+    those chunks give up, count one timeout each, store NaN over their output, and end: the
+    call returns and nothing hangs.  The tiles of the local chunk, whose flag is written,
+    are still right.  A normal call afterwards is bit-identical to the complete-buffer GEMM
+    and adds no timeout."""
     rng = np.random.default_rng(55)
     cap, H, N, T, tp, rank = 1024, 512, 264, 1024, 4, 1
     a = wl.normal_bits(rng, (T, H))
     w_t = gu.dev(wl.normal_bits(rng, (H, N), 0.02))
     reg = gu.Registration(ub, cap, H, tp, workspace=False, pad_rows=8)
+    gu.force_tile(ub, reg.h, "256x256")  # the local chunk is exactly one tile row
     try:
         reg.set_T(T)
         reg.fill(a)
@@ -244,17 +245,21 @@ def test_arrival_device_loop_wait_bound(ub, monkeypatch):
         lo, hi = rank * T // tp, (rank + 1) * T // tp
         cfg = ub.make_cfg("ring_exchange", rank=rank, atomic_gemm=True)
         before = ub.ub_arrival_timeouts(reg.h)
-        monkeypatch.setenv("UBX_ARRIVAL_WAIT_US", "2000")
-        monkeypatch.setenv("UBX_ARRIVAL_DROP_FLAGS", "1")
+        ub.ub_debug_set(reg.h, "arrival_wait_us", 2000)
+        ub.ub_debug_set(reg.h, "arrival_drop_flags", 1)
         print("[arrival wait bound] flags dropped, 2 ms bound", flush=True)
         c = gu.canary((T, N))
         ub.ub_gemm_ag_arrival(reg.h, gu.dev(a), w_t, N, N, c, N, cfg)
         torch.cuda.synchronize()
         after = ub.ub_arrival_timeouts(reg.h)
-        assert after > before
-        assert np.array_equal(gu.host(c)[lo:hi], ref[lo:hi])
-        monkeypatch.delenv("UBX_ARRIVAL_WAIT_US")
-        monkeypatch.delenv("UBX_ARRIVAL_DROP_FLAGS")
+        # 3 bands of 256 rows whose chunks never came, 2 column tiles each
+        assert after - before == 3 * 2
+        got = gu.host(c)
+        assert np.array_equal(got[lo:hi], ref[lo:hi])
+        late = np.concatenate([got[:lo], got[hi:]])
+        assert np.all(late == 0x7FC0)
+        ub.ub_debug_set(reg.h, "arrival_wait_us", 0)
+        ub.ub_debug_set(reg.h, "arrival_drop_flags", 0)
         print("[arrival wait bound] normal call", flush=True)
         _case(ub, reg, a, w_t, N, dict(method="ring_exchange", rank=rank, atomic_gemm=True), ref, T, tp)
         assert ub.ub_arrival_timeouts(reg.h) == after
@@ -270,19 +275,18 @@ def test_arrival_device_loop_wait_bound(ub, monkeypatch):
         reg.close()
 
 
-def test_arrival_device_loop_with_cut(ub, tmp_path, monkeypatch):
+def test_arrival_device_loop_with_cut(ub):
     """The device-side loop gated on arrivals when its tile plan is cut in two launches
-    (13216 rows x 1280 columns: 260 tiles of 256 x 256, the last 160 rows as 128 x 128
-    tiles): both launches wait on the flags of the chunks they read, no wait runs into its
-    bound, and the output equals the ungated GEMM over the complete buffer bit for bit.
-    The handle's timeout count starts at zero even when its flag slot was used (and timed
-    out on purpose) by a handle destroyed before it."""
+    (13216 rows x 1280 columns; a cut forced after 51 bands of 256 rows, the last 160 rows
+    as 128 x 128 tiles): both launches wait on the flags of the chunks they read, no wait
+    runs into its bound, and the output equals the ungated GEMM over the complete buffer
+    bit for bit.  The handle's timeout count starts at zero even when its flag slot was
+    used (and timed out on purpose) by a handle destroyed before it."""
     rng = np.random.default_rng(57)
     cap, H, N, T, tp = 13312, 256, 1280, 13216, 8
     a = wl.normal_bits(rng, (T, H))
     w_t = gu.dev(wl.normal_bits(rng, (H, N), 0.02))
     reg = gu.Registration(ub, cap, H, tp, workspace=False, pad_rows=8)
-    log = str(tmp_path / "plans.txt")
     try:
         reg.set_T(T)
         reg.fill(a)
@@ -290,14 +294,13 @@ def test_arrival_device_loop_with_cut(ub, tmp_path, monkeypatch):
         ub.ub_gemm_ag_chunked(reg.h, w_t, N, N, c, N, ub.make_cfg("bulk", 1, 1))
         torch.cuda.synchronize()
         ref = gu.host(c)
-        monkeypatch.setenv("UBX_GEMM_LOG", log)
+        gu.force_tile(ub, reg.h, "256x256")
+        ub.ub_debug_set(reg.h, "cut_row", 51 * 256)
         for rank, host_src in ((0, False), (5, False), (3, True)):
             print(f"[arrival cut] rank={rank} host_src={host_src}", flush=True)
             _case(ub, reg, a, w_t, N, dict(method="ring_exchange", rank=rank, atomic_gemm=True,
                                           use_ce=True), ref, T, tp, host_src=host_src)
-        with open(log) as f:
-            cuts = [int(dict(kv.split("=") for kv in line.split())["cut"]) for line in f if line.strip()]
-        assert cuts == [51 * 256] * 3, cuts
+            assert ub.ub_debug_last_plan(reg.h) == (256, 256, 51 * 256, 128, 128)
         assert ub.ub_arrival_timeouts(reg.h) == 0
     finally:
         reg.close()

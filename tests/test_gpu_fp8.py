@@ -96,17 +96,17 @@ def _gemm(ub, reg, w_codes, n, sa, sw, cfg, ldc=None):
 
 
 @pytest.mark.parametrize("tile", ["256x256", "128x256"])
-def test_gemm_integer_bit_exact_every_schedule(ub, tile, monkeypatch):
+def test_gemm_integer_bit_exact_every_schedule(ub, tile):
     """Small-integer codes, power-of-two scales: every partial sum is exact in fp32, so
     GPU == oracle bit for bit, for every chunking, stream count, rank, aggregate setting,
     the device-side loop, and both tile shapes."""
-    monkeypatch.setenv("UBX_GEMM_TILE", tile)
     rng = np.random.default_rng(72)
     cap, H, N, T, tp = 1024, 512, 264, 600, 8
     a = _int_codes(rng, (T, H))
     w = _int_codes(rng, (N, H))
     sa, sw = 2.0 ** -3, 2.0 ** -5
     reg = Fp8Reg(ub, cap, H, tp)
+    gu.force_tile(ub, reg.h, tile)
     try:
         ub.ub_set_active_shape(reg.h, (T, H))
         ub.ub_copy_in(reg.h, _dev8(a), T, 0)
@@ -269,12 +269,11 @@ def _as_bf16(codes, transpose=False):
 
 
 @pytest.mark.parametrize("tile", ["256x256", "128x256"])
-def test_rs_fp8_integer_bit_exact_every_schedule(ub, tile, monkeypatch):
+def test_rs_fp8_integer_bit_exact_every_schedule(ub, tile):
     """Small-integer codes, power-of-two scales: partials and sums are exact in fp32, so
     partials, ascending and ring-order outputs equal the oracle bit for bit, for every
     chunking, stream count, the device-side loop and both tile shapes; the workspace and
     output tails stay untouched."""
-    monkeypatch.setenv("UBX_GEMM_TILE", tile)
     rng = np.random.default_rng(75)
     cap, H, T, tp = 1024, 512, 600, 8
     K = tp * 128
@@ -282,6 +281,7 @@ def test_rs_fp8_integer_bit_exact_every_schedule(ub, tile, monkeypatch):
     w = _int_codes(rng, (H, K))
     sa, sw = 2.0 ** -3, 2.0 ** -5
     reg = gu.Registration(ub, cap, H, tp, pad_rows=8)
+    gu.force_tile(ub, reg.h, tile)
     try:
         reg.set_T(T)
         for order in ("ascending", "ring"):

@@ -35,8 +35,7 @@ def test_graph_replays_match_eager(ub):
             ub.make_cfg("ring_exchange", 1, 2, True, False, rank=6)]    # aggregate, 2 streams
     rs_cfgs = [ub.make_cfg("pipeline", 4, 3, atomic_gemm=True),
                ub.make_cfg("ring_exchange", 1, 3, reduce_order="ring", rank=1)]
-    # the same sums with the reduction fused into the slice-GEMM launch (bf16 only); the
-    # eager pass allocates their counters (largest T first), so capture allocates nothing
+    # the same sums with the reduction fused into the slice-GEMM launch (bf16 only)
     fused_cfgs = [ub.make_cfg("pipeline", 4, 3, fuse_reduce=True),
                   ub.make_cfg("ring_exchange", 1, 3, atomic_gemm=True, reduce_order="ring", rank=1,
                               fuse_reduce=True)]
@@ -100,5 +99,55 @@ def test_graph_replays_match_eager(ub):
             for k, o in enumerate(rs_outs):
                 assert np.array_equal(gu.host(o), eager_rs[k]), (rep, "rs", k)
             del scratch
+    finally:
+        reg.close()
+
+
+def test_graph_captures_first_fused_call(ub):
+    """The first fused reduce-scatter call of a handle goes straight into a graph: it needs
+    no allocation or clearing (its tile counters are the workspace's zeroed counter region),
+    so the capture holds only kernel launches.  Every replay equals the eager separate
+    reduction bit for bit, and leaves the counters at zero."""
+    rng = np.random.default_rng(92)
+    cap, H, tp, K = 2048, 264, 8, 1024
+    Ts = (2048, 1000)
+    a_rs = gu.dev(wl.normal_bits(rng, (cap, K)))
+    w_rs = gu.dev(wl.normal_bits(rng, (K, H), 0.02))
+    reg = gu.Registration(ub, cap, H, tp)
+    cfgs = [ub.make_cfg("pipeline", 4, 3, fuse_reduce=True),
+            ub.make_cfg("pipeline", 4, 3, atomic_gemm=True, fuse_reduce=True, reduce_order="ring")]
+    try:
+        s = torch.cuda.Stream()
+        ref = []
+        with torch.cuda.stream(s):  # eager, with the separate reduction only
+            for T in Ts:
+                ub.ub_set_active_shape(reg.h, (T, H))
+                for cfg in cfgs:
+                    sep = ub.make_cfg("pipeline", 4, 3, atomic_gemm=bool(cfg.atomic_gemm),
+                                      reduce_order="ring" if cfg.reduce_order else "ascending")
+                    o = gu.canary((cap, H))
+                    ub.ub_gemm_rs_chunked(reg.h, a_rs, K, K, w_rs, H, o, H, sep, s)
+                    ref.append(o)
+        torch.cuda.synchronize()
+        ref = [gu.host(o) for o in ref]
+        outs = [gu.canary((cap, H)) for _ in ref]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            i = 0
+            for T in Ts:
+                ub.ub_set_active_shape(reg.h, (T, H))
+                for cfg in cfgs:
+                    ub.ub_gemm_rs_chunked(reg.h, a_rs, K, K, w_rs, H, outs[i], H, cfg, s)
+                    i += 1
+        torch.cuda.synchronize()
+        for rep in range(3):
+            for o in outs:
+                o.fill_(gu.CANARY)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for k, o in enumerate(outs):
+                assert np.array_equal(gu.host(o), ref[k]), (rep, k)
+            assert reg.counters_clean(), rep
     finally:
         reg.close()

@@ -94,8 +94,8 @@ def test_integer_inputs_bit_exact(ub, cap, H, K, T, tp, method, ns):
         reg.close()
 
 
-@pytest.mark.parametrize("tile", ("256x256", "192x256", "128x256", "256x128", "128x128"))
-def test_every_tile_shape_rs(ub, tile, monkeypatch):
+@pytest.mark.parametrize("tile", gu.BF16_TILES)
+def test_every_tile_shape_rs(ub, tile):
     """Each GEMM tile shape, forced, on the slice GEMMs: integer inputs bit-exact against
     the oracle (partials and output), ragged rows and chunks."""
     rng = np.random.default_rng(22)
@@ -104,7 +104,7 @@ def test_every_tile_shape_rs(ub, tile, monkeypatch):
     wt = wl.integer_bits(rng, (K, H))
     print(f"[rs tile {tile}] cap={cap} H={H} K={K} T={T}", flush=True)
     reg = gu.Registration(ub, cap, H, tp, pad_rows=8)
-    monkeypatch.setenv("UBX_GEMM_TILE", tile)
+    gu.force_tile(ub, reg.h, tile)
     try:
         reg.set_T(T)
         ref, parts = _oracle_rs(cap, H, tp, a, wt, op.OverlapCfg(method="pipeline", num_splits=3))
@@ -377,5 +377,40 @@ def test_ring_reduce_fc2_full_size_sampled(ub):
             gu.check_close(parts[s], oparts[s], a_all[rows][:, s * ks:(s + 1) * ks],
                            wt[s * ks:(s + 1) * ks], f"fc2 ring partial {s}")
         assert np.all(oh[T:] == gu.CANARY)
+    finally:
+        reg.close()
+
+
+@pytest.mark.parametrize("ks", (40, 72))
+@pytest.mark.parametrize("fuse", (False, True))
+def test_slice_width_not_multiple_of_k_step(ub, ks, fuse):
+    """K / tp a multiple of 8 but not of the kernel's 32-deep k-step: each slice's last
+    step masks the A chunks that belong to the next slice.  Integer inputs: partials and
+    output bit-exact against the oracle for every tile shape, both schedules and both
+    summation orders; the counters of the fused sum end at zero."""
+    rng = np.random.default_rng(150 + ks)
+    cap, H, T, tp = 1024, 264, 600, 8
+    K = tp * ks
+    a = wl.integer_bits(rng, (T, K))
+    wt = wl.integer_bits(rng, (K, H))
+    reg = gu.Registration(ub, cap, H, tp, pad_rows=8)
+    try:
+        reg.set_T(T)
+        for order in ("ascending", "ring"):
+            ref, parts = _oracle_rs(cap, H, tp, a, wt, op.OverlapCfg(method="pipeline", num_splits=3,
+                                                                     reduce_order=order))
+            for tile in gu.BF16_TILES:
+                gu.force_tile(ub, reg.h, tile)
+                for atomic in (False, True):
+                    print(f"[slice tail] ks={ks} fuse={fuse} {order} {tile} atomic={atomic}", flush=True)
+                    reg.ws_t.fill_(gu.CANARY)
+                    out = _run_rs(ub, reg, gu.dev(a), K, gu.dev(wt),
+                                  ub.make_cfg("pipeline", 3, atomic_gemm=atomic, reduce_order=order,
+                                              fuse_reduce=fuse))
+                    assert np.array_equal(out[:T], ref), (order, tile, atomic)
+                    ws = gu.host(reg.ws_t)
+                    assert np.array_equal(ws[: tp * T * H].reshape(tp, T, H), parts)
+                    assert np.all(out[T:] == gu.CANARY)
+        assert reg.counters_clean()
     finally:
         reg.close()

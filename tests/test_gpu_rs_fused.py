@@ -75,8 +75,8 @@ def test_fused_integer_inputs_bit_exact(ub, cap, H, K, T, tp, method, ns):
         reg.close()
 
 
-@pytest.mark.parametrize("tile", ("256x256", "192x256", "128x256", "256x128", "128x128"))
-def test_fused_every_tile_shape(ub, tile, monkeypatch):
+@pytest.mark.parametrize("tile", gu.BF16_TILES)
+def test_fused_every_tile_shape(ub, tile):
     """Each GEMM tile shape, forced: the fused sum is bit-exact against the oracle on
     integer inputs (ragged rows, ragged last column tile, tp = 8) in both orders."""
     rng = np.random.default_rng(24)
@@ -85,7 +85,7 @@ def test_fused_every_tile_shape(ub, tile, monkeypatch):
     wt = wl.integer_bits(rng, (K, H))
     print(f"[fused tile {tile}] cap={cap} H={H} K={K} T={T}", flush=True)
     reg = gu.Registration(ub, cap, H, tp, pad_rows=8)
-    monkeypatch.setenv("UBX_GEMM_TILE", tile)
+    gu.force_tile(ub, reg.h, tile)
     try:
         reg.set_T(T)
         for order in ("ascending", "ring"):
@@ -125,6 +125,7 @@ def test_fused_equals_separate_reduction_every_schedule(ub):
                             got = _run(ub, reg, a, K, wt, cfg)
                             assert np.array_equal(got[:T], ref), (T, order, method, ns, atomic)
                             assert np.all(got[T:] == gu.CANARY)
+            assert reg.counters_clean(), T
     finally:
         reg.close()
 
@@ -187,5 +188,6 @@ def test_fused_fc2_full_size(ub):
             want, _ = og.rs_rows(a_all[rows], wt, tp)
             gu.check_rs_close(oh[rows], want, a_all[rows], wt, tp, f"fused fc2 T={T}")
             assert np.all(oh[T:] == gu.CANARY)
+        assert reg.counters_clean()
     finally:
         reg.close()
