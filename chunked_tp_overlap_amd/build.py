@@ -20,7 +20,7 @@ LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libub.so")
 
 SOURCES = ["ub_api.cpp", "ub_plan.cpp", "gemm_bf16.hip", "gemm_fp8.hip", "quantize_fp8.hip",
-           "reduce_partials.hip"]
+           "reduce_partials.hip", "static_scratch.hip"]
 
 ARCH = "gfx950"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")

@@ -383,10 +383,10 @@ ub_status_t check_ld(ub_ctx* h, const char* name, int64_t ld, int64_t cols) {
 // workspace prefix (slot s at element s*T*H) into out (row stride ldo), ascending or in ring
 // order (each row's shard T/tp decides its hop order).
 ubx::ReduceArgs reduce_args(const ub_ctx* h, int64_t row0, int64_t rows, void* out, int64_t ldo,
-                            bool ring) {
+                            bool ring, const uint16_t* ws = nullptr) {
   const int64_t H = h->hidden;
   ubx::ReduceArgs r{};
-  r.parts = h->ws + row0 * H;
+  r.parts = (ws ? ws : h->ws) + row0 * H;
   r.slot_stride = h->T * H;
   r.ldp = H;
   r.nslots = h->tp;
@@ -948,15 +948,27 @@ UB_API ub_status_t ub_gemm_ag_chunked_fp8(ub_handle_t h, const void* w, int64_t 
   return join_streams(h, caller, S);
 }
 
-UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, int64_t lda,
-                                      const void* w, int64_t ldw, void* out, int64_t ldo,
-                                      const ub_overlap_cfg_t* cfg, ub_stream_t stream) {
-  const TraceRange range("ub_gemm_rs_chunked");
-  if (!h) return UB_ERR_NOT_INITIALIZED;
+namespace {
+
+// Where a reduce-scatter call puts its partial slots (tp slots of T x hidden, packed from
+// the active T) and its fused-sum tile counters (all of them, and each compute stream's
+// range): the registered workspace, or the fixed scratch of ub_gemm_rs_chunked_noalloc.
+struct RsTarget {
+  uint16_t* ws;
+  uint32_t* counters;
+  int64_t counters_n;
+  int64_t stream_words;
+};
+
+// Checks of a bf16 reduce-scatter call, before any HIP call; builds the plan.
+ub_status_t check_rs_call(ub_ctx* h, const void* a, int64_t k, int64_t lda, const void* w,
+                          int64_t ldw, const void* out, int64_t ldo, const ub_overlap_cfg_t* cfg,
+                          bool need_ws) {
   ub_status_t st = need_dtype(h, UB_DTYPE_BF16, "the reduce-scatter GEMM");
   if (st != UB_OK) return st;
   if ((st = check_cfg_common(h, cfg)) != UB_OK) return st;
-  if (!h->ws) return fail(h, UB_ERR_NOT_INITIALIZED, "no reduce-scatter workspace registered");
+  if (need_ws && !h->ws)
+    return fail(h, UB_ERR_NOT_INITIALIZED, "no reduce-scatter workspace registered");
   if (!a || !w || !out) return fail(h, UB_ERR_INVALID_ARG, "a, w and out must be non-NULL");
   if (!aligned16(a) || !aligned16(w) || !aligned16(out))
     return fail(h, UB_ERR_INVALID_ARG, "a, w and out must be 16-byte aligned");
@@ -972,17 +984,23 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
   if ((st = check_ld(h, "lda", lda, k)) != UB_OK) return st;
   if ((st = check_ld(h, "ldw", ldw, H)) != UB_OK) return st;
   if ((st = check_ld(h, "ldo", ldo, H)) != UB_OK) return st;
-  st = ubx::build_plan(h->T, h->tp, *cfg, UB_OP_RS, &h->plan, &h->last_error);
-  if (st != UB_OK) return st;
+  return ubx::build_plan(h->T, h->tp, *cfg, UB_OP_RS, &h->plan, &h->last_error);
+}
+
+// Body of both bf16 reduce-scatter entry points, after check_rs_call.
+ub_status_t rs_call(ub_ctx* h, const RsTarget& tg, const void* a, int64_t k, int64_t lda,
+                    const void* w, int64_t ldw, void* out, int64_t ldo,
+                    const ub_overlap_cfg_t* cfg, hipStream_t caller) {
+  ub_status_t st;
+  const int64_t H = h->hidden;
+  const int64_t ks = k / h->tp;
   const int64_t T = h->T;
   const int32_t tp = h->tp;
-  hipStream_t caller = static_cast<hipStream_t>(stream);
   const bool ring = cfg->reduce_order == UB_REDUCE_RING;
   const bool fuse = cfg->fuse_reduce != 0;
-  // Fused reduction: the counters were sized at registration from the capacity.  The
-  // launches of one compute stream run one after another and leave their counters at zero,
-  // so each stream counts in its own range; the device-side loop uses the whole array.
-  const int64_t stream_words = ubx::fuse_counter_stream_words(h->capacity, H);
+  // Fused reduction: each compute stream's launches run one after another and leave
+  // their counters at zero, so each stream counts in its own range; the device-side loop
+  // uses the whole array.
   auto set_fuse = [&](ubx::GemmArgs& g, int64_t row0, int stream_index) {
     if (!fuse) return;
     g.fuse_out = static_cast<uint16_t*>(out) + row0 * ldo;
@@ -992,11 +1010,11 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
     g.fuse_row0 = row0;
     g.fuse_shard_rows = T / tp;
     if (stream_index < 0) {
-      g.counters = h->fuse_counters;
-      g.counters_n = h->fuse_counters_n;
+      g.counters = tg.counters;
+      g.counters_n = tg.counters_n;
     } else {
-      g.counters = h->fuse_counters + stream_index * stream_words;
-      g.counters_n = stream_words;
+      g.counters = tg.counters + stream_index * tg.stream_words;
+      g.counters_n = tg.stream_words;
     }
   };
   const double fused_flops = double(tp - 1) * H;  // per row: the reduction's adds
@@ -1017,7 +1035,7 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
     g.b = static_cast<const uint16_t*>(w);
     g.ldb = ldw;
     g.b_batch_stride = ks * ldw;
-    g.c = h->ws;
+    g.c = tg.ws;
     g.ldc = H;
     g.c_batch_stride = T * H;
     g.n = static_cast<int32_t>(H);
@@ -1030,7 +1048,7 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
                       [&] { return ubx::launch_gemm_bf16_units(g, units, caller); },
                       "slice GEMM launch");
     if (st != UB_OK || fuse) return st;
-    const ubx::ReduceArgs r = reduce_args(h, 0, T, out, ldo, ring);
+    const ubx::ReduceArgs r = reduce_args(h, 0, T, out, ldo, ring, tg.ws);
     return timed_launch(h, caller, 1, double(tp - 1) * T * H, 2.0 * (tp + 1) * T * H,
                         [&] { return ubx::launch_reduce_partials(r, caller); }, "reduce launch");
   }
@@ -1055,7 +1073,7 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
     g.b = static_cast<const uint16_t*>(w);
     g.ldb = ldw;
     g.b_batch_stride = ks * ldw;
-    g.c = h->ws + u.row0 * H;
+    g.c = tg.ws + u.row0 * H;
     g.ldc = H;
     g.c_batch_stride = T * H;
     g.m = static_cast<int32_t>(rows);
@@ -1071,13 +1089,61 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
     if (st != UB_OK) return st;
     if (fuse) continue;
     // the reduction of this chunk follows its GEMMs on the same stream
-    const ubx::ReduceArgs r = reduce_args(h, u.row0, rows, out, ldo, ring);
+    const ubx::ReduceArgs r = reduce_args(h, u.row0, rows, out, ldo, ring, tg.ws);
     const double rbytes = 2.0 * (tp + 1) * rows * H;
     st = timed_launch(h, s, 1, double(tp - 1) * rows * H, rbytes,
                       [&] { return ubx::launch_reduce_partials(r, s); }, "reduce launch");
     if (st != UB_OK) return st;
   }
   return join_streams(h, caller, S);
+}
+
+}  // namespace
+
+UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, int64_t lda,
+                                      const void* w, int64_t ldw, void* out, int64_t ldo,
+                                      const ub_overlap_cfg_t* cfg, ub_stream_t stream) {
+  const TraceRange range("ub_gemm_rs_chunked");
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  ub_status_t st = check_rs_call(h, a, k, lda, w, ldw, out, ldo, cfg, true);
+  if (st != UB_OK) return st;
+  const RsTarget tg{h->ws, h->fuse_counters, h->fuse_counters_n,
+                    ubx::fuse_counter_stream_words(h->capacity, h->hidden)};
+  return rs_call(h, tg, a, k, lda, w, ldw, out, ldo, cfg, static_cast<hipStream_t>(stream));
+}
+
+UB_API ub_status_t ub_gemm_rs_chunked_noalloc(ub_handle_t h, const void* a, int64_t k,
+                                              int64_t lda, const void* w, int64_t ldw, void* out,
+                                              int64_t ldo, const ub_overlap_cfg_t* cfg,
+                                              ub_stream_t stream) {
+  const TraceRange range("ub_gemm_rs_chunked_noalloc");
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  ub_status_t st = check_rs_call(h, a, k, lda, w, ldw, out, ldo, cfg, false);
+  if (st != UB_OK) return st;
+  // the workspace's layout, sized for the active T, in the fixed scratch
+  const int64_t T = h->T, H = h->hidden;
+  const size_t parts = static_cast<size_t>(h->tp) * static_cast<size_t>(T * H) * 2;
+  const size_t counter_off = (parts + 255) / 256 * 256;
+  const int64_t words = cfg->fuse_reduce ? ubx::fuse_counter_words(T, H) : 0;
+  const size_t need = counter_off + static_cast<size_t>(words) * sizeof(uint32_t);
+  if (need > ubx::kStaticScratchBytes)
+    return fail(h, UB_ERR_BUFFER_TOO_SMALL,
+                "this call needs %zu bytes of scratch (tp * T * hidden bf16 partials%s); the "
+                "fixed scratch holds %zu",
+                need, cfg->fuse_reduce ? " and fused-sum counters" : "", ubx::kStaticScratchBytes);
+  if ((st = ensure_device(h, 1)) != UB_OK) return st;
+  hipError_t e = hipSuccess;
+  unsigned char* base = ubx::static_scratch_base(&e);
+  if (!base) return hip_fail(h, e, "hipGetSymbolAddress(static scratch)");
+  hipStream_t caller = static_cast<hipStream_t>(stream);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(base + counter_off);
+  if (words > 0) {  // another call may have left the shared array in any state
+    e = ubx::launch_clear_words(counters, words, caller);
+    if (e != hipSuccess) return hip_fail(h, e, "scratch counter clear");
+  }
+  const RsTarget tg{reinterpret_cast<uint16_t*>(base), counters, words,
+                    ubx::fuse_counter_stream_words(T, H)};
+  return rs_call(h, tg, a, k, lda, w, ldw, out, ldo, cfg, caller);
 }
 
 UB_API ub_status_t ub_gemm_rs_chunked_fp8(ub_handle_t h, const void* a, int64_t k, int64_t lda,

@@ -184,4 +184,11 @@ struct ReduceArgs {
 };
 hipError_t launch_reduce_partials(const ReduceArgs& r, hipStream_t stream);
 
+// The fixed device scratch of ub_gemm_rs_chunked_noalloc (static_scratch.hip): its size, its
+// address on the current device (nullptr and *err set on failure), and a fill of n 32-bit
+// words with zeros on `stream` (a kernel, so that the call can be captured into a graph).
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+unsigned char* static_scratch_base(hipError_t* err);
+hipError_t launch_clear_words(uint32_t* p, int64_t n, hipStream_t stream);
+
 }  // namespace ubx

@@ -44,7 +44,8 @@ EXPORTS = (
     "ub_get_active_shape", "ub_get_capacity_shape", "ub_get_plan", "ub_copy_in",
     "ub_gemm_ag_chunked", "ub_gemm_ag_arrival", "ub_arrival_timeouts", "ub_deliver_chunks",
     "ub_quantize_in",
-    "ub_gemm_ag_chunked_fp8", "ub_gemm_rs_chunked", "ub_gemm_rs_chunked_fp8",
+    "ub_gemm_ag_chunked_fp8", "ub_gemm_rs_chunked", "ub_gemm_rs_chunked_noalloc",
+    "ub_gemm_rs_chunked_fp8",
     "ub_quantize_e4m3", "ub_reduce_partials",
     "ub_set_kernel_timing", "ub_get_kernel_timing", "ub_prepare_streams", "ub_debug_set",
     "ub_debug_last_plan", "ub_destroy", "ub_status_string", "ub_last_error",
@@ -103,6 +104,7 @@ _sig = {
     "ub_gemm_ag_chunked_fp8": (_I32, [_H, _P, _I64, _I64, ctypes.c_float, ctypes.c_float, _P,
                                       _I64, _CFGP, _P]),
     "ub_gemm_rs_chunked": (_I32, [_H, _P, _I64, _I64, _P, _I64, _P, _I64, _CFGP, _P]),
+    "ub_gemm_rs_chunked_noalloc": (_I32, [_H, _P, _I64, _I64, _P, _I64, _P, _I64, _CFGP, _P]),
     "ub_gemm_rs_chunked_fp8": (_I32, [_H, _P, _I64, _I64, _P, _I64, ctypes.c_float, ctypes.c_float,
                                       _P, _I64, _CFGP, _P]),
     "ub_quantize_e4m3": (_I32, [_P, _I64, _P, _I64, _I64, _I64, ctypes.c_float, _P]),
@@ -282,6 +284,11 @@ def ub_gemm_ag_chunked_fp8(h, w, n_cols, ldw, scale_inv_a, scale_inv_w, c, ldc, 
 
 def ub_gemm_rs_chunked(h, a, k, lda, w, ldw, out, ldo, cfg, stream=None):
     _check(_lib.ub_gemm_rs_chunked(h, _ptr(a), k, lda, _ptr(w), ldw, _ptr(out), ldo,
+                                   ctypes.byref(cfg), _stream(stream)), h)
+
+
+def ub_gemm_rs_chunked_noalloc(h, a, k, lda, w, ldw, out, ldo, cfg, stream=None):
+    _check(_lib.ub_gemm_rs_chunked_noalloc(h, _ptr(a), k, lda, _ptr(w), ldw, _ptr(out), ldo,
                                    ctypes.byref(cfg), _stream(stream)), h)
 
 

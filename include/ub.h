@@ -398,6 +398,24 @@ UB_API ub_status_t ub_gemm_rs_chunked(ub_handle_t h, const void* a, int64_t k, i
                                       const void* w, int64_t ldw, void* out, int64_t ldo,
                                       const ub_overlap_cfg_t* cfg, ub_stream_t stream);
 
+/* ub_gemm_rs_chunked for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation), also on a handle
+ * registered without a workspace: same arguments, checks, plan, kernels and results (bit
+ * for bit), but the tp partial slots ([tp, T, hidden] bf16, packed from the active T) and,
+ * with fuse_reduce, the tile counters live in the library's fixed device scratch of 32 MiB
+ * (kept by each GPU the library runs on until the process ends) instead of the registered
+ * workspace.  Calls needing more than 32 MiB (tp * T * hidden * 2 bytes of partials, plus
+ * the counters) return UB_ERR_BUFFER_TOO_SMALL before anything is enqueued.  Allocates
+ * nothing and calls no allocating routine; with fuse_reduce it first clears the counters
+ * with a fill kernel on `stream`.  Every call on one GPU shares the scratch: calls that
+ * overlap on a GPU (other streams, other handles, other threads) race and must be ordered
+ * by the caller.  The partials are not left in the handle's workspace, so
+ * ub_reduce_partials does not see them. */
+UB_API ub_status_t ub_gemm_rs_chunked_noalloc(ub_handle_t h, const void* a, int64_t k,
+                                              int64_t lda, const void* w, int64_t ldw, void* out,
+                                              int64_t ldo, const ub_overlap_cfg_t* cfg,
+                                              ub_stream_t stream);
+
 /* FP8 (E4M3) reduce-scatter GEMM: ub_gemm_rs_chunked with E4M3 operands and one
  * dequantization factor per tensor (the reading of [TE#3564]'s quantized buffers taken
  * for ub_gemm_ag_chunked_fp8).  The partials and the sum are bf16, as in

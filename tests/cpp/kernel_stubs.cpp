@@ -26,5 +26,10 @@ hipError_t launch_quantize_e4m3(const uint16_t*, int64_t, uint8_t*, int64_t, int
   return hipErrorNotSupported;
 }
 hipError_t launch_reduce_partials(const ReduceArgs&, hipStream_t) { return hipErrorNotSupported; }
+unsigned char* static_scratch_base(hipError_t* err) {
+  *err = hipErrorNotSupported;
+  return nullptr;
+}
+hipError_t launch_clear_words(uint32_t*, int64_t, hipStream_t) { return hipErrorNotSupported; }
 
 }  // namespace ubx
