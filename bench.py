@@ -48,6 +48,9 @@ def parse_args():
                    help="minimum CPU-oracle baseline work (seconds)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
+    p.add_argument("--points", default=None,
+                   help="with --profile-pass gqa: comma-separated T values of the sweep to run "
+                        "instead of all 32")
     p.add_argument("--profile-pass", default=None, choices=PROFILE_PASSES,
                    help="for rocprofv3: run only this workload's timed region (with the "
                         "library's per-launch events), then a 1 GiB copy that calibrates the "
@@ -663,11 +666,16 @@ def profile_ag(ub, wl, torch, np, dev, args):
     steps with the library's per-launch events."""
     make = {"gqa": gqa_sweep, "qkv": qkv_step, "fc1": fc1_step}[args.profile_pass]
     sw = make(ub, wl, torch, np, dev)
+    if args.points:
+        keep = [int(x) for x in args.points.split(",")]
+        sw.Ts = [T for T in keep if T <= sw.w.capacity]
+        sw.flops = sum(sw.flop(T) for T in sw.Ts)
     cfg = sw.cfg(True)
     per_step = _dispatches(ub, sw, cfg)  # one untimed step that records the plans
     sec, stats = sw.timed(cfg, args.steps, args.warmup, events=True)
     alg = sum(sw.alg_bytes(T) for T in sw.Ts)
-    out = {"profile_pass": args.profile_pass, "ms_per_step": round(sec * 1e3, 4),
+    out = {"profile_pass": args.profile_pass, "points": sw.Ts if args.points else "all",
+           "ms_per_step": round(sec * 1e3, 4),
            "calls_per_step": len(sw.Ts), "dispatches_per_step": per_step,
            "timed_calls": args.steps * len(sw.Ts), "timed_dispatches": args.steps * per_step,
            "timed_gflop": round(args.steps * sw.flops / 1e9, 3),
@@ -679,8 +687,9 @@ def profile_ag(ub, wl, torch, np, dev, args):
 
 
 def profile_fc2(ub, wl, torch, np, dev, args):
-    """The fc2 RS GEMM (device-side loop, then the pipeline on 3 streams) over its T sweep:
-    per call the slice-GEMM launch and the reduction launch."""
+    """The fc2 RS GEMM in the device-side loop over its T sweep: per call one slice-GEMM
+    launch (or two when its plan is cut) and one reduction launch; the timed region's GEMM
+    and reduction launches are reported apart (keys gemm and reduce)."""
     w = wl.fc2()
     ra, rw, _ = w.seeds()
     ub_bytes, ws_bytes = ub.ub_required_bytes(w.capacity, w.hidden, w.tp)
@@ -690,39 +699,45 @@ def profile_fc2(ub, wl, torch, np, dev, args):
     w_t = torch.from_numpy(wl.weights(w, rw).view(np.int16)).to(dev)
     o_t = torch.empty((w.capacity, w.hidden), dtype=torch.int16, device=dev)
     h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes, ws_t, ws_bytes)
-    ub.ub_prepare_streams(h, w.num_max_streams)
     stream = torch.cuda.current_stream()
-    out = {"profile_pass": "fc2", "T": list(wl.FC2_TOKENS), "modes": []}
-    for atomic in (True, False):
-        cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, False, atomic)
+    cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, False, True)
+    Ts = list(wl.FC2_TOKENS)
+    if args.points:
+        Ts = [int(x) for x in args.points.split(",")]
 
-        def step():
-            for T in wl.FC2_TOKENS:
-                ub.ub_set_active_shape(h, (T, w.hidden))
-                ub.ub_gemm_rs_chunked(h, a_t, w.k, w.k, w_t, w.hidden, o_t, w.hidden, cfg, stream)
+    def step():
+        for T in Ts:
+            ub.ub_set_active_shape(h, (T, w.hidden))
+            ub.ub_gemm_rs_chunked(h, a_t, w.k, w.k, w_t, w.hidden, o_t, w.hidden, cfg, stream)
 
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        ub.ub_set_kernel_timing(h, True)
-        ub.ub_get_kernel_timing(h)
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            step()
-        torch.cuda.synchronize()
-        sec = (time.perf_counter() - t0) / args.steps
-        gs, rs = ub.ub_get_kernel_timing(h)
-        ub.ub_set_kernel_timing(h, False)
-        flops = sum(2.0 * T * w.k * w.hidden for T in wl.FC2_TOKENS)
-        out["modes"].append({"mode": "atomic_gemm" if atomic else "pipeline_3_streams",
-                             "ms_per_step": round(sec * 1e3, 4), "tflops_step": round(flops / sec / 1e12, 2),
-                             "gemm_launches": gs["launches"], "gemm_event_ms": round(gs["total_ms"], 4),
-                             "reduce_launches": rs["launches"], "reduce_event_ms": round(rs["total_ms"], 4),
-                             "timed_gflop": round(args.steps * flops / 1e9, 3)})
-        torch.cuda.synchronize()
-        time.sleep(0.05)  # the two modes stand apart on the timeline
-    out["src_file"] = os.path.relpath(GEMM_SRC, ROOT)
-    out["src_hash"] = src_hash(GEMM_SRC)
+    dispatches = 0
+    for T in Ts:  # one untimed step that records the plans
+        ub.ub_set_active_shape(h, (T, w.hidden))
+        ub.ub_gemm_rs_chunked(h, a_t, w.k, w.k, w_t, w.hidden, o_t, w.hidden, cfg, stream)
+        dispatches += 2 if ub.ub_debug_last_plan(h)[2] >= 0 else 1
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ub.ub_set_kernel_timing(h, True)
+    ub.ub_get_kernel_timing(h)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / args.steps
+    gs, rs = ub.ub_get_kernel_timing(h)
+    ub.ub_set_kernel_timing(h, False)
+    flops = sum(2.0 * T * w.k * w.hidden for T in Ts)
+    out = {"profile_pass": "fc2", "T": Ts, "ms_per_step": round(sec * 1e3, 4),
+           "tflops_step": round(flops / sec / 1e12, 2),
+           "gemm": {"timed_calls": args.steps * len(Ts), "timed_dispatches": args.steps * dispatches,
+                    "timed_gflop": round(args.steps * flops / 1e9, 3),
+                    "timed_algorithmic_bytes": round(gs["bytes"]),
+                    "hip_event_total_ms": round(gs["total_ms"], 4)},
+           "reduce": {"timed_calls": args.steps * len(Ts), "timed_dispatches": args.steps * len(Ts),
+                      "timed_algorithmic_bytes": round(rs["bytes"]),
+                      "hip_event_total_ms": round(rs["total_ms"], 4)},
+           "src_file": os.path.relpath(GEMM_SRC, ROOT), "src_hash": src_hash(GEMM_SRC)}
     ub.ub_destroy(h)
     return out
 

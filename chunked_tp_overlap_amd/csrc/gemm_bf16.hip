@@ -55,6 +55,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -698,33 +699,35 @@ using PP128x256 = Cfg<128, 256, 32, 4, 2, 4>;   // 8 waves of 64x64
 using PL128x128 = Cfg<128, 128, 32, 4, 2, 2>;   // 4 waves of 64x64, 2 workgroups per CU
 constexpr int PP_D = 3;
 
-// Tile choice by a small cost model: a launch of `tiles` workgroups on the CUs left to it
-// (256 / concurrency, times the workgroups one CU holds) runs ceil(tiles / slots) rounds,
-// each as long as one tile takes at the tile's efficiency.  Efficiencies are relative to
-// the 256x256 ping-pong.  Measured on MI355X with rocprofv3 counters of the GEMM (GQA
-// shape, hidden 8192, 1280 columns): the 256x256 ping-pong keeps the matrix cores of its
-// busy CUs ~75% busy, the 128x256 one ~48% (a 64x64 wave tile reads more LDS bytes per
-// MFMA); the 128x128 kernel runs two workgroups per CU that share its MFMA pipes.  The
-// chip runs into its power limit under sustained MFMA load, so a launch that leaves CUs
-// idle runs the busy ones at a higher clock (2.25 GHz with ~145 busy CUs, 2.0 with ~217):
-// spreading the same work over more, smaller tiles gains much less than the tile count
-// suggests, and the efficiencies carry that.
+// Tile choice by a cost model fitted to measurements.  A launch of `tiles` workgroups on
+// the CUs left to it (share = 256 / concurrency; the 128 x 128 kernel holds two workgroups
+// per CU) runs in rounds; a round's time is one tile's work over the tile's speed and the
+// clock that the round's busy CUs allow:
+//   time(round) = BM * BN * K / (speed(tile) * boost(busy CUs)),
+//   boost(b) = min(1.476, (256 / b)^0.2245)
+// (the part runs into its power limit under MFMA load, so a launch that leaves CUs idle
+// runs the busy ones faster: counters of the GEMM show 2.25 GHz with ~145 busy CUs and 2.0
+// with ~217).  Tile speeds, relative to the 256x256 ping-pong at full occupancy: 320x256
+// 1.03, 128x256 0.75, 128x128 0.49 alone on a CU and 0.37 when two share one.  The five
+// constants are a least-squares fit of log time ratios to a forced-tile sweep on MI355X
+// over the workloads' own shapes (GQA 1280 x 8192 at 33 T, qkv 1536 x 4096, fc1 3584 x
+// 4096, fc2 4096 x 1792 in 8 slices; device-side loop and host loop; 78 points, including
+// forced cuts): the model's plan is within 2% of the best measured plan at 67 of them, at
+// 0.989 of the best on average.
 //
-// A launch whose last round would hold only a few tiles (say 260 tiles of 256 x 256 on
-// 256 CUs: the last 4 run alone, as long as all the others) is cut in two launches on the
-// same stream: the leading row bands that fill whole rounds with the large tile, then the
-// remaining rows with the tile that finishes them soonest.  Rows are cut at a band
-// boundary, so every row is still computed once, by one instruction sequence: the results
-// do not change.  The cut is taken only when the second launch fills at most about 60%
-// of its slots, and only for a launch that has the chip to itself (with several streams
-// the other streams' launches fill the idle CUs, and a cut measured 10% slower on fc1's
-// host loop).
-struct TileOpt { int kind, bm, bn, per_cu; double eff; };
+// Besides one tile shape for the whole launch, the model prices cuts: a launch that has the
+// chip to itself runs the leading row bands that fill whole rounds of a large tile, then
+// the remaining rows as a second launch on the same stream with the tile that finishes them
+// soonest.  Rows are cut at a band boundary, so every row is still computed once, by one
+// instruction sequence: the results do not change.  With several streams (the host loop)
+// the other streams' launches fill the idle CUs, and no cut is taken.
+struct TileOpt { int kind, bm, bn, per_cu; double speed, speed_alone; };
 enum TileKind { kTile128x128 = 0, kTile128x256 = 1, kTile256x256 = 2, kTile320x256 = 3 };
-const TileOpt kTileOpts[] = {{kTile320x256, 320, 256, 1, 1.00},
-                             {kTile256x256, 256, 256, 1, 1.00},
-                             {kTile128x256, 128, 256, 1, 0.62},
-                             {kTile128x128, 128, 128, 2, 0.75}};
+const TileOpt kTileOpts[] = {{kTile320x256, 320, 256, 1, 1.030, 1.030},
+                             {kTile256x256, 256, 256, 1, 1.000, 1.000},
+                             {kTile128x256, 128, 256, 1, 0.749, 0.749},
+                             {kTile128x128, 128, 128, 2, 0.373, 0.493}};
+constexpr double kBoostMax = 1.476, kBoostExp = 0.2245;
 
 const TileOpt* find_tile(int bm, int bn) {
   for (const TileOpt& o : kTileOpts)
@@ -753,11 +756,24 @@ GemmUnits clip_units(const GemmUnits& u, int64_t lo, int64_t hi) {
   return out;
 }
 
+// Predicted time (in units of one 256x256 tile's k-work at full occupancy) of one launch of
+// `row_tiles_` row tiles of `o` on `share` CUs.
 double tile_cost(const TileOpt& o, int64_t row_tiles_, const GemmArgs& g, int share) {
   const int64_t tiles = row_tiles_ * ((g.n + o.bn - 1) / o.bn) * g.batch;
-  const int64_t slots = (int64_t)(share > 0 ? share : 1) * o.per_cu;
-  const double rounds = (double)((tiles + slots - 1) / slots);
-  return rounds * o.bm * o.bn / (o.eff / o.per_cu);
+  const int64_t cus = share > 0 ? share : 1;
+  const int64_t slots = cus * o.per_cu;
+  const double area = (double)o.bm * o.bn / (256.0 * 256.0);
+  double t = 0.0;
+  for (int64_t left = tiles; left > 0;) {
+    const int64_t now = std::min(left, slots);
+    const bool alone = o.per_cu == 1 || now <= cus;
+    const int64_t busy_cus = alone ? now : cus;
+    const double busy = std::min(256.0, (double)busy_cus * 256.0 / (double)cus);
+    const double boost = std::min(kBoostMax, std::pow(256.0 / busy, kBoostExp));
+    t += area / ((alone ? o.speed_alone : o.speed) * boost);
+    left -= now;
+  }
+  return t;
 }
 
 // The cheapest single tile over the units; its cost in *cost.
@@ -807,13 +823,10 @@ TilePlan choose_plan(const GemmArgs& g, const GemmUnits& u) {
     const int64_t b1 = full * slots / band_tiles;             // bands inside them
     if (b1 <= 0 || b1 >= bands) continue;
     const int64_t cut = lo + b1 * o.bm;
-    const GemmUnits tail = clip_units(u, cut, hi);
     double tail_cost;
-    const TileOpt& t = best_single(g, tail, share, &tail_cost);
-    const int64_t tail_tiles = row_tiles(tail, t.bm) * ((g.n + t.bn - 1) / t.bn) * g.batch;
-    if (tail_tiles * 10 > (int64_t)share * t.per_cu * 6) continue;  // at most ~60% of the slots
+    const TileOpt& t = best_single(g, clip_units(u, cut, hi), share, &tail_cost);
     const double c = tile_cost(o, b1, g, share) + tail_cost;
-    if (c < best_cost * 0.97) {  // a second launch costs a little: cut only for a clear gain
+    if (c < best_cost * 0.98) {  // a second launch costs a little: cut only for a clear gain
       best_cost = c;
       plan = {o.kind, cut, t.kind};
     }
