@@ -72,6 +72,15 @@ def src_hash(path):
 
 # ---- workloads ---------------------------------------------------------------------------
 
+SCRATCH_BYTES = (64 << 20) + 256 * 1024  # partials of every split the library chooses + counters
+
+
+def register_scratch(ub, torch, dev, h):
+    t = torch.zeros(SCRATCH_BYTES // 2, dtype=torch.int16, device=dev)
+    ub.ub_register_scratch(h, t, SCRATCH_BYTES)
+    return t
+
+
 class AgSweep:
     """An all-gather-side workload on one registered UserBuffer: a list of active T values,
     one ub_gemm_ag_chunked call per T."""
@@ -89,6 +98,8 @@ class AgSweep:
         self.h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, self.ub_t, ub_bytes)
         # worker streams right after registration: they take hardware queues of their own
         ub.ub_prepare_streams(self.h, w.num_max_streams)
+        # split-K scratch: lets the library sum the rows of an underfilled launch in K segments
+        self.scratch = register_scratch(ub, torch, dev, self.h)
         self.stream = torch.cuda.current_stream()
         self.flops = sum(self.flop(T) for T in self.Ts)
 
@@ -145,11 +156,12 @@ class AgSweep:
         return out
 
     def plans(self, cfg):
-        """The tile plan of each point's call: (T, tile_m, tile_n, cut_row, tail_m, tail_n)."""
+        """The tile plan of each point's call: (T, tile_m, tile_n, cut_row, tail_m, tail_n,
+        seg_row, nseg, split, seg_tile_m, seg_tile_n)."""
         rows = []
         for T in self.Ts:
             self.call(T, cfg)
-            rows.append((T,) + tuple(self.ub.ub_debug_last_plan(self.h)))
+            rows.append((T,) + tuple(self.ub.ub_debug_last_plan(self.h, seg=True)))
         self.torch.cuda.synchronize()
         return rows
 
@@ -301,12 +313,13 @@ def main():
     per_pt = g.per_point(primary)
     result["per_point"] = {"columns": ["T", "tflops_median", "tflops_best", "plan"],
                            "note": "each point: 5 warm-up calls, 20 calls timed one by one (HIP events); "
-                                   "plan = tile_m x tile_n [cut row: tail tile]",
+                                   "plan = tile_m x tile_n [cut row: tail tile] [split-K from row r: "
+                                   "nseg segments on tile, summed in the kernel (r1) or by a second "
+                                   "launch (r2)]",
                            "rows": []}
     plans = {p[0]: p[1:] for p in g.plans(primary)}
     for T, med, best in per_pt:
-        tm, tn, cut, sm, sn = plans[T]
-        plan = f"{tm}x{tn}" + (f" cut {cut}: {sm}x{sn}" if cut >= 0 else "")
+        plan = describe_plan(plans[T])
         result["per_point"]["rows"].append([T, round(g.flop(T) / med / 1e9, 1),
                                             round(g.flop(T) / best / 1e9, 1), plan])
     result["per_point"]["tflops_sum_flops_over_sum_medians"] = round(
@@ -575,6 +588,7 @@ def arrival(ub, wl, torch, np, dev):
     c_t = torch.empty((w.capacity, w.n_cols), dtype=torch.int16, device=dev)
     h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes)
     ub.ub_prepare_streams(h, w.num_max_streams, copy_stream=True)
+    scratch = register_scratch(ub, torch, dev, h)  # noqa: F841 (held while h is used)
     stream = torch.cuda.current_stream()
     res = []
     for T in (4096, 6144, 8192):
@@ -656,9 +670,34 @@ def qkv_fp8(ub, wl, torch, np, dev):
 
 # ---- profile passes (for rocprofv3) ------------------------------------------------------
 
+def describe_plan(p):
+    """(tile_m, tile_n, cut_row, tail_m, tail_n, seg_row, nseg, split, seg_tile_m,
+    seg_tile_n) as text."""
+    tm, tn, cut, sm, sn, seg_row, nseg, split, gm, gn = p
+    out = []
+    if seg_row != 0:
+        out.append(f"{tm}x{tn}" + (f" cut {cut}: {sm}x{sn}" if cut >= 0 else ""))
+    if nseg > 1:
+        out.append(f"split-K from row {seg_row}: {nseg} x {gm}x{gn}" + (f" r{split}" if split else " fold"))
+    return "; ".join(out)
+
+
+def _call_dispatches(plan):
+    """Kernel dispatches of one call from its plan (T, tile_m, tile_n, cut_row, tail_m,
+    tail_n, seg_row, nseg, split, ...): the rows before seg_row launch once, or twice when
+    cut; K-segmented rows once, or twice when their split sum is a separate launch."""
+    cut, seg_row, nseg, split = plan[3], plan[6], plan[7], plan[8]
+    n = 0
+    if seg_row != 0:
+        n += 2 if cut >= 0 else 1
+    if nseg > 1:
+        n += 2 if split == 2 else 1
+    return n
+
+
 def _dispatches(ub, sw, cfg):
-    """Kernel dispatches of one step (a call whose plan is cut launches twice)."""
-    return sum(2 if p[3] >= 0 else 1 for p in sw.plans(cfg))
+    """Kernel dispatches of one step."""
+    return sum(_call_dispatches(p) for p in sw.plans(cfg))
 
 
 def profile_ag(ub, wl, torch, np, dev, args):
@@ -810,6 +849,7 @@ def profile_arrival(ub, wl, torch, np, dev, args):
     c_t = torch.empty((w.capacity, w.n_cols), dtype=torch.int16, device=dev)
     h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes)
     ub.ub_prepare_streams(h, w.num_max_streams, copy_stream=True)
+    scratch = register_scratch(ub, torch, dev, h)  # noqa: F841 (held while h is used)
     ub.ub_set_active_shape(h, (T, w.hidden))
     torch.cuda.synchronize()
     time.sleep(0.05)  # the uploads above stand apart from the first call on the timeline

@@ -61,6 +61,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <vector>
 
 #include "gemm_common.h"
 #include "ub_internal.h"
@@ -87,6 +88,12 @@ struct Params {
   uint32_t epoch;
   int32_t n_chunks;
   int32_t chunk_row0[kMaxGemmUnits + 1];
+  // K segmentation (seg kernel): nseg segments of the k-steps; split: one workgroup per
+  // (tile, segment), fp32 partials and per-tile counters in scratch
+  int32_t nseg;
+  int32_t split;
+  float* parts;
+  uint32_t* seg_counters;
   // fused reduction (GemmArgs): nslots == 0 = none
   uint16_t* out;
   int64_t ldo;
@@ -108,7 +115,7 @@ constexpr uint64_t kReadyTimeoutTicks = 50000000ull;  // 0.5 s of the 100 MHz s_
 // lines cached before they arrived.  The wait is bounded in time, so every wave ends.
 // Returns, to every wave of the workgroup alike, whether some wave ran past the bound; the
 // workgroup then counts one timeout and stores NaN instead of computing its tile.
-__device__ inline bool wait_ready(const Params& p, int r0, int r1) {
+__device__ inline bool wait_ready(const Params& p, int r0, int r1, bool count = true) {
   int c = 0;
   while (c + 1 < p.n_chunks && p.chunk_row0[c + 1] <= r0) ++c;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -123,7 +130,7 @@ __device__ inline bool wait_ready(const Params& p, int r0, int r1) {
     }
   }
   late = __syncthreads_or(late);
-  if (late && threadIdx.x == 0)
+  if (late && count && threadIdx.x == 0)
     __hip_atomic_fetch_add(p.timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
   return late != 0;
@@ -228,14 +235,14 @@ struct Tile {
   int a_rd_row, a_rd_c, a_rd_x, b_krow, b_col_chunk, b_x, b_in;
 
   // false: this workgroup has no tile (the whole workgroup returns before any barrier)
-  __device__ inline bool init(const Params& p, int tid) {
+  __device__ inline bool init(const Params& p, int tid, int tile_index = -1) {
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     group = wave >> 2;
     wm = wave / C::WGN;
     wn = wave % C::WGN;
     z = blockIdx.z;
-    tile = blockIdx.x;
+    tile = tile_index >= 0 ? tile_index : (int)blockIdx.x;
     int tn;
     if (!tile_of(p, tile, C::BM, m0, m_end, tn)) return false;
     n0 = tn * C::BN;
@@ -523,18 +530,132 @@ __device__ inline void wait_loads_barrier(bool full) {
   }
 }
 
-template <class C, int D>
+// ---- split-K meeting point ----------------------------------------------------------------
+// K-segmented rows: the nk k-steps of a tile form nseg segments, segment s holding steps
+// [s nk / nseg, (s+1) nk / nseg); each segment's products are accumulated from zero (MFMAs
+// in ascending k, as in every kernel here) into P_s, and the tile's result is
+//   C = bf16( ((P_0 + P_1) + P_2) + ... + P_{nseg-1} )   (fp32 adds, in that order).
+// Split: workgroup w computes segment w % nseg of tile w / nseg.  Here each segment writes
+// P_s (fp32, [i][j][thread] f32x4, coalesced) to its scratch slot, makes it visible at agent
+// scope (the tile's segments may run on different XCDs, each with its own L2) and counts
+// itself on the tile's counter (low 16 bits: segments arrived; a segment whose arrival wait
+// ran out adds 1 << 16 and writes nothing).  The last to arrive resets the counter, acquires
+// and returns true with the ordered sum in acc; if some segment ran late it counts one
+// timeout and stores NaN instead.  Every other workgroup returns false.
+template <class C>
+__device__ inline bool split_meet(unsigned char* smem, const Params& p, const Tile<C>& t,
+                                  int tid, int tile, int seg, int nseg, bool late,
+                                  f32x4 (&acc)[C::FM][C::FN]) {
+  constexpr int TILE = C::BM * C::BN;
+  if (!late) {
+    float* mine = p.parts + ((int64_t)tile * nseg + seg) * TILE;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+        *GLOBAL_PTR(f32x4, mine + ((i * C::FN + j) * C::THREADS + tid) * 4) = acc[i][j];
+  }
+  uint32_t* arrived = reinterpret_cast<uint32_t*>(smem);
+  uint32_t* counter = p.seg_counters + tile;
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t add = late ? 0x10001u : 1u;
+    const uint32_t now =
+        __hip_atomic_fetch_add(counter, add, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) + add;
+    if ((now & 0xFFFFu) == (uint32_t)nseg) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *LDS_PTR(uint32_t, arrived) = now;
+  }
+  __syncthreads();
+  const uint32_t now = *LDS_PTR(const uint32_t, arrived);
+  if ((now & 0xFFFFu) != (uint32_t)nseg) return false;
+  __syncthreads();  // every wave has read `arrived` before the epilogue reuses LDS
+  if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (now >> 16) {
+    if (tid == 0) __hip_atomic_fetch_add(p.timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    t.store_nan(p, tid);
+    return false;
+  }
+  const float* base = p.parts + (int64_t)tile * nseg * TILE;
+  for (int sg = 0; sg < nseg; ++sg) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        const f32x4 v = __builtin_nontemporal_load(
+            GLOBAL_PTR(const f32x4, base + (int64_t)sg * TILE + ((i * C::FN + j) * C::THREADS + tid) * 4));
+        acc[i][j] = sg == 0 ? v : acc[i][j] + v;
+      }
+  }
+  return true;
+}
+
+// The other split mode: every segment only writes P_s to its slot (a segment whose arrival
+// wait ran out writes quiet NaNs instead, which make the tile's sum NaN), and a separate
+// launch, gemm_bf16_split_reduce, sums the tile's partials in order over the whole chip.
+template <class C>
+__device__ inline void split_write(const Params& p, int tid, int tile, int seg, int nseg,
+                                   bool late, const f32x4 (&acc)[C::FM][C::FN]) {
+  float* mine = p.parts + ((int64_t)tile * nseg + seg) * (C::BM * C::BN);
+  const f32x4 nan4 = {__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+      *GLOBAL_PTR(f32x4, mine + ((i * C::FN + j) * C::THREADS + tid) * 4) = late ? nan4 : acc[i][j];
+}
+
+// Sum of the split partials of tiles of C, in segment order, rounded to bf16 and stored:
+// thread q of a tile's 256-thread group reads slot q (one f32x4: rows 4 (lane / 16) + e,
+// e < 4, of column lane % 16 of a 16 x 16 block of the producing wave) of every partial.
+template <class C>
+__global__ __launch_bounds__(256) void gemm_bf16_split_reduce(Params p) {
+  constexpr int TILE = C::BM * C::BN;
+  constexpr int GROUPS = TILE / 4 / 256;  // 256-slot groups per tile
+  const int tile = (int)blockIdx.x / GROUPS;
+  const int q = ((int)blockIdx.x % GROUPS) * 256 + (int)threadIdx.x;
+  int m0, m_end, tn;
+  if (!tile_of(p, tile, C::BM, m0, m_end, tn)) return;
+  const float* src = p.parts + (int64_t)tile * p.nseg * TILE + q * 4;
+  f32x4 sum = __builtin_nontemporal_load(GLOBAL_PTR(const f32x4, src));
+  for (int sg = 1; sg < p.nseg; ++sg)
+    sum = sum + __builtin_nontemporal_load(GLOBAL_PTR(const f32x4, src + (int64_t)sg * TILE));
+  const int t = q % C::THREADS, ij = q / C::THREADS;
+  const int i = ij / C::FN, j = ij % C::FN;
+  const int wave = t >> 6, lane = t & 63;
+  const int row = m0 + (wave / C::WGN) * C::WM + i * 16 + (lane >> 4) * 4;
+  const int col = tn * C::BN + (wave % C::WGN) * C::WN + j * 16 + (lane & 15);
+  if (col >= p.n) return;
+  uint16_t* c = p.c + (int64_t)row * p.ldc + col;
+#pragma unroll
+  for (int e = 0; e < 4; e += 2) {
+    const uint32_t v = pack_bf16x2(sum[e], sum[e + 1]);
+    if (row + e < m_end) c[(int64_t)e * p.ldc] = (uint16_t)(v & 0xFFFF);
+    if (row + e + 1 < m_end) c[(int64_t)(e + 1) * p.ldc] = (uint16_t)(v >> 16);
+  }
+}
+
+// SPLIT 1 or 2: workgroup w runs segment w % nseg of tile w / nseg; 1 meets the tile's
+// other segments in split_meet, 2 only writes its partial (split_write).
+template <class C, int D, int SPLIT = 0>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_pingpong(Params p) {
   static_assert(C::NW == 8, "ping-pong needs two waves per SIMD");
   static_assert(D >= 2 && D <= C::S - 1, "load distance");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x;
+  const int nseg = SPLIT ? p.nseg : 1;
+  const int tile = SPLIT ? (int)blockIdx.x / nseg : (int)blockIdx.x;
+  const int seg = SPLIT ? (int)blockIdx.x % nseg : 0;
   Tile<C> t;
-  if (!t.init(p, tid)) return;
-  if (p.ready && wait_ready(p, t.m0, min(t.m0 + C::BM, t.m_end))) {
-    t.store_nan(p, tid);
-    return;
+  if (!t.init(p, tid, tile)) return;
+  bool late = false;
+  if (p.ready) {
+    late = wait_ready(p, t.m0, min(t.m0 + C::BM, t.m_end), SPLIT != 1);
+    if (!SPLIT && late) {
+      t.store_nan(p, tid);
+      return;
+    }
   }
   const int group = t.group;
   const bool full = C::NFULL == C::NW || t.nl == C::LMAX;
@@ -546,20 +667,23 @@ void gemm_bf16_pingpong(Params p) {
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   bf16x8 af[C::SUBS][C::FM], bf[C::SUBS][C::FN];
   const int nk = (p.k + C::BK - 1) / C::BK;
+  // steps [k0, k1) of this workgroup (all of them unless split; none for a late segment)
+  const int k0 = SPLIT ? (int)((int64_t)seg * nk / nseg) : 0;
+  const int k1 = !SPLIT ? nk : late ? k0 : (int)((int64_t)(seg + 1) * nk / nseg);
 
 #pragma unroll
-  for (int s = 0; s < D; ++s) t.issue_loads(smem, s, nk);
+  for (int s = 0; s < D; ++s) t.issue_loads(smem, k0 + s, k1);
   __builtin_amdgcn_sched_barrier(0);
-  wait_loads_barrier<C, D, true>(full);  // b0: step 0 landed everywhere
+  wait_loads_barrier<C, D, true>(full);  // b0: step k0 landed everywhere
   __builtin_amdgcn_sched_barrier(0);
   if (group == 1) __asm__ volatile("s_barrier" ::: "memory");  // b1 for group 1
   __builtin_amdgcn_sched_barrier(0);
 
-  for (int ks = 0; ks < nk; ++ks) {
+  for (int ks = k0; ks < k1; ++ks) {
     // memory cluster
 #pragma unroll
     for (int sub = 0; sub < C::SUBS; ++sub) t.read_frags(smem, ks, sub * 32, af[sub], bf[sub]);
-    t.issue_loads(smem, ks + D, nk);
+    t.issue_loads(smem, ks + D, k1);
     __builtin_amdgcn_sched_barrier(0);
     if (group == 1) {
       wait_loads_barrier<C, D, true>(full);
@@ -580,8 +704,15 @@ void gemm_bf16_pingpong(Params p) {
   }
   if (group == 0) __asm__ volatile("s_barrier" ::: "memory");  // matches group 1's b1
   wait_vmcnt_and_barrier<0>();  // trailing out-of-range loads landed before LDS is reused
+  if constexpr (SPLIT == 2) {
+    split_write<C>(p, tid, tile, seg, nseg, late, acc);
+    return;
+  }
+  if constexpr (SPLIT == 1) {
+    if (!split_meet(smem, p, t, tid, tile, seg, nseg, late, acc)) return;
+  }
   t.store(smem, p, tid, acc);
-  if (p.nslots) t.fused_reduce(smem, p, tid);
+  if (!SPLIT && p.nslots) t.fused_reduce(smem, p, tid);
 }
 
 // ---- 4-wave, S-stage pipeline -----------------------------------------------------------
@@ -641,8 +772,91 @@ void gemm_bf16_pipelined(Params p) {
   if (p.nslots) t.fused_reduce(smem, p, tid);
 }
 
+// ---- K-segmented 4-wave kernel -----------------------------------------------------------
+// The segments of split_meet on 128 x 128 tiles.  SPLIT 1 or 2: one segment per workgroup,
+// as in the ping-pong kernel.  SPLIT 0: one workgroup per tile runs all steps and folds each
+// finished segment into the sum at the segment boundary, which gives the same bits without
+// scratch (the fallback when none is registered or it is too small).
+template <class C, int SPLIT>
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void gemm_bf16_seg(Params p) {
+  static_assert(C::S >= 2, "at least two stages");
+  static_assert(C::NW == 4 && C::NL % C::NW == 0, "one group of four waves, even load split");
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int tid = threadIdx.x;
+  const int nseg = p.nseg;
+  const int tile = SPLIT ? (int)blockIdx.x / nseg : (int)blockIdx.x;
+  const int seg = SPLIT ? (int)blockIdx.x % nseg : 0;
+  Tile<C> t;
+  if (!t.init(p, tid, tile)) return;
+  bool late = false;
+  if (p.ready) {
+    late = wait_ready(p, t.m0, min(t.m0 + C::BM, t.m_end), SPLIT != 1);
+    if (!SPLIT && late) {
+      t.store_nan(p, tid);
+      return;
+    }
+  }
+
+  f32x4 acc[C::FM][C::FN], sum[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      sum[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  bf16x8 af[2][C::FM], bf[2][C::FN];
+  const int nk = (p.k + C::BK - 1) / C::BK;
+  const int k0 = SPLIT ? (int)((int64_t)seg * nk / nseg) : 0;
+  const int k1 = !SPLIT ? nk : late ? k0 : (int)((int64_t)(seg + 1) * nk / nseg);
+  int done = 0;                                  // segments folded into sum
+  int boundary = (int)((int64_t)1 * nk / nseg);  // end of the current segment
+
+#pragma unroll
+  for (int s = 0; s < C::S; ++s) t.issue_loads(smem, k0 + s, k1);
+  wait_vmcnt_and_barrier<(C::S - 1) * C::LMAX>();
+  t.read_frags(smem, k0, 0, af[0], bf[0]);
+
+  for (int ks0 = k0; ks0 < k1; ks0 += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int ks = ks0 + u, b = u;
+      wait_vmcnt_and_barrier<(C::S - 2) * C::LMAX>();
+      t.issue_loads(smem, ks + C::S, k1);
+      t.read_frags(smem, ks + 1, 0, af[b ^ 1], bf[b ^ 1]);
+      if (ks < k1) {
+        mfma_block<C>(acc, af[b], bf[b]);
+        if (!SPLIT && ks + 1 == boundary) {  // a segment ends: fold it into the sum
+#pragma unroll
+          for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) {
+              sum[i][j] = done == 0 ? acc[i][j] : sum[i][j] + acc[i][j];
+              acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+          ++done;
+          boundary = (int)((int64_t)(done + 1) * nk / nseg);
+        }
+      }
+    }
+  }
+  wait_vmcnt_and_barrier<0>();  // trailing out-of-range loads landed before LDS is reused
+  if constexpr (SPLIT == 2) {
+    split_write<C>(p, tid, tile, seg, nseg, late, acc);
+  } else if constexpr (SPLIT == 1) {
+    if (!split_meet(smem, p, t, tid, tile, seg, nseg, late, acc)) return;
+    t.store(smem, p, tid, acc);
+  } else {
+    t.store(smem, p, tid, sum);
+  }
+}
+
+// seg_mode: 0 plain; 1 K-segmented in one workgroup per tile; 2 split, met in the kernel;
+// 3 split, summed by a gemm_bf16_split_reduce launch after it.
 template <class C, class K>
-hipError_t launch(K kernel, const GemmArgs& g, const GemmUnits& units, hipStream_t stream) {
+hipError_t launch(K kernel, const GemmArgs& g, const GemmUnits& units, hipStream_t stream,
+                  int seg_mode = 0, int nseg = 1) {
   const GemmUnits u = tile_aligned_units(units, C::BM);
   Params p{};
   p.a = g.a;
@@ -684,12 +898,30 @@ hipError_t launch(K kernel, const GemmArgs& g, const GemmUnits& units, hipStream
     p.row0 = g.fuse_row0;
     p.shard_rows = g.fuse_shard_rows;
   }
-  const int64_t grid = tiles;
+  int64_t grid = tiles;
+  if (seg_mode != 0) {  // K-segmented launch (batch 1, no fused sum)
+    if (g.batch != 1 || p.nslots) return hipErrorInvalidValue;
+    p.nseg = nseg;
+    p.split = seg_mode >= 2;
+    if (p.split) {
+      if ((seg_mode == 2 && tiles > g.split_counters_n) ||
+          tiles * nseg * C::BM * C::BN > g.split_parts_n)
+        return hipErrorInvalidValue;
+      p.parts = g.split_parts;
+      p.seg_counters = g.split_counters;
+      grid = tiles * nseg;
+    }
+  }
   if (grid > 0x7FFFFFFF || g.batch > 65535) return hipErrorInvalidValue;
   hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kernel), C::LDS_BYTES);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid, 1, g.batch), dim3(C::THREADS), C::LDS_BYTES,
                      stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess || seg_mode != 3) return e;
+  constexpr int GROUPS = C::BM * C::BN / 4 / 256;
+  if (tiles * GROUPS > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gemm_bf16_split_reduce<C>, dim3((unsigned)(tiles * GROUPS)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -758,11 +990,12 @@ GemmUnits clip_units(const GemmUnits& u, int64_t lo, int64_t hi) {
 
 // Predicted time (in units of one 256x256 tile's k-work at full occupancy) of one launch of
 // `row_tiles_` row tiles of `o` on `share` CUs.
-double tile_cost(const TileOpt& o, int64_t row_tiles_, const GemmArgs& g, int share) {
-  const int64_t tiles = row_tiles_ * ((g.n + o.bn - 1) / o.bn) * g.batch;
+// With nseg > 1, each tile is nseg split-K pieces of 1/nseg of its k-work.
+double tile_cost(const TileOpt& o, int64_t row_tiles_, const GemmArgs& g, int share, int nseg = 1) {
+  const int64_t tiles = row_tiles_ * ((g.n + o.bn - 1) / o.bn) * g.batch * nseg;
   const int64_t cus = share > 0 ? share : 1;
   const int64_t slots = cus * o.per_cu;
-  const double area = (double)o.bm * o.bn / (256.0 * 256.0);
+  const double area = (double)o.bm * o.bn / (256.0 * 256.0) / nseg;
   double t = 0.0;
   for (int64_t left = tiles; left > 0;) {
     const int64_t now = std::min(left, slots);
@@ -832,6 +1065,30 @@ TilePlan choose_plan(const GemmArgs& g, const GemmUnits& u) {
     }
   }
   return plan;
+}
+
+// The split-K launch of K-segmented rows on tiles of `kind`: reduce 1 meets the segments in
+// the kernel (split_meet), 2 sums them in a gemm_bf16_split_reduce launch after it.
+template <int R>
+hipError_t launch_split_r(int kind, const GemmArgs& g, const GemmUnits& u, hipStream_t stream,
+                          int nseg) {
+  constexpr int mode = R == 1 ? 2 : 3;
+  switch (kind) {
+    case kTile320x256:
+      return launch<PP320x256>(&gemm_bf16_pingpong<PP320x256, PP_D, R>, g, u, stream, mode, nseg);
+    case kTile256x256:
+      return launch<PP256x256>(&gemm_bf16_pingpong<PP256x256, PP_D, R>, g, u, stream, mode, nseg);
+    case kTile128x256:
+      return launch<PP128x256>(&gemm_bf16_pingpong<PP128x256, PP_D, R>, g, u, stream, mode, nseg);
+    default:
+      return launch<PL128x128>(&gemm_bf16_seg<PL128x128, R>, g, u, stream, mode, nseg);
+  }
+}
+
+hipError_t launch_split(int kind, const GemmArgs& g, const GemmUnits& u, hipStream_t stream,
+                        int nseg, int reduce) {
+  return reduce == 2 ? launch_split_r<2>(kind, g, u, stream, nseg)
+                     : launch_split_r<1>(kind, g, u, stream, nseg);
 }
 
 hipError_t launch_kind(int kind, const GemmArgs& g, const GemmUnits& u, hipStream_t stream) {
@@ -908,24 +1165,144 @@ hipError_t launch_gemm_bf16_units(const GemmArgs& g, const GemmUnits& u, hipStre
         return hipErrorInvalidValue;
     }
   }
-  const TilePlan plan = choose_plan(g, u);
-  if (g.plan_out) {
-    const TileOpt& a = opt_of(plan.kind);
-    g.plan_out->tile_m = a.bm;
-    g.plan_out->tile_n = a.bn;
-    g.plan_out->cut = plan.cut;
-    const TileOpt& b = opt_of(plan.tail_kind);
-    g.plan_out->tail_m = plan.cut >= 0 ? b.bm : 0;
-    g.plan_out->tail_n = plan.cut >= 0 ? b.bn : 0;
+  // K segmentation: rows at or after seg_row go to the segmented kernel (clamped so that no
+  // segment is empty); the rows before it follow the tile plan
+  const int nk = (g.k + PL128x128::BK - 1) / PL128x128::BK;
+  const int nseg = std::min(g.nseg, nk);
+  const bool seg = nseg > 1 && g.batch == 1 && g.fuse_nslots == 0;
+  const GemmUnits plain = seg ? clip_units(u, 0, g.seg_row) : u;
+  const GemmUnits segu = seg ? clip_units(u, g.seg_row, INT64_MAX) : GemmUnits{0, {}, {}};
+  if (g.plan_out) *g.plan_out = TilePlanRecord{};
+  hipError_t e = hipSuccess;
+  if (plain.n > 0) {
+    const TilePlan plan = choose_plan(g, plain);
+    if (g.plan_out) {
+      const TileOpt& a = opt_of(plan.kind);
+      g.plan_out->tile_m = a.bm;
+      g.plan_out->tile_n = a.bn;
+      g.plan_out->cut = plan.cut;
+      const TileOpt& b = opt_of(plan.tail_kind);
+      g.plan_out->tail_m = plan.cut >= 0 ? b.bm : 0;
+      g.plan_out->tail_n = plan.cut >= 0 ? b.bn : 0;
+    }
+    if (plan.cut < 0) {
+      e = launch_kind(plan.kind, g, plain, stream);
+    } else {
+      // two launches on one stream: the leading whole-round bands, then the rest (the fused
+      // reduction's counters are back at zero when the second starts)
+      int64_t lo = 0, hi = 0;
+      contiguous_rows(plain, &lo, &hi);
+      e = launch_kind(plan.kind, g, clip_units(plain, lo, plan.cut), stream);
+      if (e == hipSuccess) e = launch_kind(plan.tail_kind, g, clip_units(plain, plan.cut, hi), stream);
+    }
+    if (e != hipSuccess) return e;
   }
-  if (plan.cut < 0) return launch_kind(plan.kind, g, u, stream);
-  // two launches on one stream: the leading whole-round bands, then the rest (the fused
-  // reduction's counters are back at zero when the second starts)
-  int64_t lo = 0, hi = 0;
-  contiguous_rows(u, &lo, &hi);
-  hipError_t e = launch_kind(plan.kind, g, clip_units(u, lo, plan.cut), stream);
-  if (e != hipSuccess) return e;
-  return launch_kind(plan.tail_kind, g, clip_units(u, plan.cut, hi), stream);
+  if (segu.n > 0) {
+    // split pieces on the plan's tile (256 x 256 unless given); when the scratch cannot
+    // hold their partials, the 128 x 128 folding kernel (the same bits)
+    const TileOpt* o = g.seg_m > 0 ? find_tile(g.seg_m, g.seg_n) : find_tile(256, 256);
+    if (!o) return hipErrorInvalidValue;
+    const int64_t tiles = row_tiles(segu, o->bm) * ((g.n + o->bn - 1) / o->bn);
+    const int reduce = g.seg_reduce == 1 ? 1 : 2;
+    const bool split = g.split_parts && (reduce == 2 || (g.split_counters && tiles <= g.split_counters_n)) &&
+                       tiles * nseg * o->bm * o->bn <= g.split_parts_n;
+    if (!split) o = find_tile(128, 128);
+    if (g.plan_out) {
+      if (plain.n == 0) {
+        g.plan_out->tile_m = o->bm;
+        g.plan_out->tile_n = o->bn;
+      }
+      int64_t lo = 0, hi = 0;
+      g.plan_out->seg_row = contiguous_rows(segu, &lo, &hi) ? lo : segu.row0[0];
+      g.plan_out->nseg = nseg;
+      g.plan_out->split = split ? reduce : 0;
+      g.plan_out->seg_m = o->bm;
+      g.plan_out->seg_n = o->bn;
+    }
+    e = split ? launch_split(o->kind, g, segu, stream, nseg, reduce)
+              : launch<PL128x128>(&gemm_bf16_seg<PL128x128, 0>, g, segu, stream, 1, nseg);
+  }
+  return e;
+}
+
+namespace {
+
+// Predicted time of the split-K launch over `rows` rows on tiles `o`, nseg pieces per tile
+// (a piece does 1/nseg of the tile's k-steps), in the units of tile_cost (one 256 x 256
+// tile's k-work on a CU at full occupancy, ~0.0291 us per unit of k): the pieces' rounds
+// with the tile speeds and clock boost of tile_cost, plus the separate sum's launch gap and
+// the partials' round trip (each piece writes its fp32 tile, the sum reads it back).  The
+// two constants, 7.3 us per launch and 0.179 us per MB of partials written and read, are a
+// least-squares fit of log time ratios to a forced sweep on MI355X (tile x nseg x first
+// segmented row over the GQA, qkv and fc1 shapes at small T and at the tails of larger T;
+// 443 points): with them the choice below lands within 2% of the best measured
+// configuration at all but 4 of 44 token counts.
+constexpr double kUnitUsPerK = 0.0291, kSplitGapUs = 7.3, kSplitUsPerMB = 0.179;
+constexpr int64_t kSplitPartsMax = int64_t(16) << 20;  // floats: 64 MiB of partials
+
+double seg_cost(const TileOpt& o, int64_t rows, int64_t n, int64_t k, int nseg) {
+  GemmArgs g{};
+  g.n = (int32_t)n;
+  g.k = (int32_t)k;
+  g.batch = 1;
+  const int64_t row_t = (rows + o.bm - 1) / o.bm;
+  const int64_t pieces = row_t * ((n + o.bn - 1) / o.bn) * nseg;
+  if (pieces * o.bm * o.bn > kSplitPartsMax) return 1e30;
+  const double unit_us = kUnitUsPerK * (double)k;
+  const double mb = (double)pieces * o.bm * o.bn * 8.0 / 1e6;
+  return tile_cost(o, row_t, g, 256, nseg) + (kSplitGapUs + kSplitUsPerMB * mb) / unit_us;
+}
+
+}  // namespace
+
+// K segmentation of a call of T rows (device-side loop, the chip to itself): the best of no
+// segmentation (one tile, or whole rounds of a large tile and a tail launch, as choose_plan
+// prices them), all rows split, and whole rounds of a large tile followed by the remaining
+// rows split; each split option over the four tiles and nseg in {2, 3, 4, 6, 8, 12, 16}
+// (at most one segment per k-step).  Segmentation is taken only for a predicted gain of 3%.
+SegPlan choose_segmentation(int64_t T, int64_t n, int64_t k, int32_t batch) {
+  SegPlan none;
+  const int64_t nk = (k + PL128x128::BK - 1) / PL128x128::BK;
+  if (batch != 1 || T <= 0 || n <= 0 || nk < 4) return none;
+  GemmArgs g{};
+  g.n = (int32_t)n;
+  g.k = (int32_t)k;
+  g.batch = 1;
+  g.concurrency = 1;
+  GemmUnits u;
+  u.n = 1;
+  u.row0[0] = 0;
+  u.rows[0] = (int32_t)T;
+  double base;
+  best_single(g, u, 256, &base);
+  // leading whole rounds of each one-per-CU tile: (rows, cost), rows 0 for none
+  std::vector<std::pair<int64_t, double>> leads = {{0, 0.0}};
+  for (const TileOpt& o : kTileOpts) {
+    if (o.per_cu != 1) continue;
+    const int64_t bands = (T + o.bm - 1) / o.bm;
+    const int64_t band_tiles = (n + o.bn - 1) / o.bn;
+    const int64_t b1 = bands * band_tiles / 256 * 256 / band_tiles;
+    if (b1 <= 0 || b1 >= bands) continue;
+    const double lead = tile_cost(o, b1, g, 256);
+    double tail;
+    best_single(g, clip_units(u, b1 * o.bm, T), 256, &tail);
+    base = std::min(base, (lead + tail) / 0.98);
+    leads.push_back({b1 * o.bm, lead});
+  }
+  SegPlan best = none;
+  double best_cost = base * 0.97;
+  const int counts[] = {2, 3, 4, 6, 8, 12, 16};
+  for (const auto& lead : leads)
+    for (const TileOpt& o : kTileOpts)
+      for (int nseg : counts) {
+        if (nseg > nk) break;
+        const double c = lead.second + seg_cost(o, T - lead.first, n, k, nseg);
+        if (c < best_cost) {
+          best_cost = c;
+          best = {lead.first, nseg, o.bm, o.bn, 2};
+        }
+      }
+  return best;
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream) {

@@ -77,6 +77,12 @@ struct ub_ctx {
   // debug settings (ub_debug_set) and the tile plan of the last GEMM launch group
   ubx::DebugOpts dbg;
   ubx::TilePlanRecord last_plan;
+  // split-K scratch (ub_register_scratch): counter words (zero at registration, left zero)
+  // and fp32 partial tiles; one range of each per compute stream
+  uint32_t* split_counters = nullptr;
+  int64_t split_counters_n = 0;
+  float* split_parts = nullptr;
+  int64_t split_parts_n = 0;
   // scratch for plans
   ubx::Plan plan;
   std::string last_error;
@@ -339,6 +345,35 @@ ub_status_t check_cfg_common(ub_ctx* h, const ub_overlap_cfg_t* cfg) {
   return UB_OK;
 }
 
+// K segmentation of an all-gather-side call at the active T (a function of the call's shape
+// alone, or forced by the handle's debug settings), and the split scratch range of compute
+// stream `si` (of S streams; the device-side loop has the whole scratch).
+// Without a registered scratch nothing is segmented unless the debug settings force it.
+ubx::SegPlan ag_segmentation(const ub_ctx* h, int64_t n_cols) {
+  if (h->dbg.nseg == 1) return ubx::SegPlan{};
+  if (h->dbg.nseg >= 2)
+    return ubx::SegPlan{std::max<int64_t>(h->dbg.seg_row, 0), h->dbg.nseg, h->dbg.seg_m,
+                        h->dbg.seg_n, h->dbg.seg_reduce};
+  if (!h->split_parts) return ubx::SegPlan{};
+  return ubx::choose_segmentation(h->T, n_cols, h->hidden, 1);
+}
+
+void set_segmentation(const ub_ctx* h, ubx::GemmArgs& g, const ubx::SegPlan& sp, int64_t row0,
+                      int si, int S) {
+  if (sp.nseg <= 1) return;
+  g.seg_row = sp.seg_row - row0;
+  g.nseg = sp.nseg;
+  g.seg_m = sp.tile_m;
+  g.seg_n = sp.tile_n;
+  g.seg_reduce = sp.reduce;
+  if (!h->split_parts) return;
+  const int64_t cw = h->split_counters_n / S, pw = h->split_parts_n / S / 64 * 64;  // 256 B aligned
+  g.split_counters = h->split_counters + si * cw;
+  g.split_counters_n = cw;
+  g.split_parts = h->split_parts + si * pw;
+  g.split_parts_n = pw;
+}
+
 // Units of the plan, in execution order, for a device-side chunk loop.
 ub_status_t plan_units(ub_ctx* h, ubx::GemmUnits* u) {
   u->n = 0;
@@ -369,6 +404,9 @@ ub_status_t check_forced_tile(ub_ctx* h, bool fp8) {
   if (d.cut_row > 0 && (d.tail_m || d.tail_n) && !ok(d.tail_m, d.tail_n))
     return fail(h, UB_ERR_INVALID_ARG, "the bf16 GEMM has no %dx%d tile (debug tail_tile_m/n)",
                 d.tail_m, d.tail_n);
+  if (!fp8 && d.nseg >= 2 && (d.seg_m || d.seg_n) && !ok(d.seg_m, d.seg_n))
+    return fail(h, UB_ERR_INVALID_ARG, "the bf16 GEMM has no %dx%d tile (debug seg_tile_m/n)",
+                d.seg_m, d.seg_n);
   return UB_OK;
 }
 
@@ -730,6 +768,7 @@ ub_status_t ag_call(ub_ctx* h, const void* src, int src_on_host, const void* w, 
     g.k = static_cast<int32_t>(H);
     g.batch = 1;
     g.concurrency = 1;
+    set_segmentation(h, g, ag_segmentation(h, n_cols), 0, 0, 1);
     if (src) {
       const ChunkMap m = chunk_map(h, cfg);
       if ((st = ensure_ready_slot(h)) != UB_OK) return st;
@@ -757,6 +796,7 @@ ub_status_t ag_call(ub_ctx* h, const void* src, int src_on_host, const void* w, 
   const int S = h->plan.n_streams;
   if ((st = ensure_device(h, S)) != UB_OK) return st;
   const ChunkMap m = chunk_map(h, cfg);
+  const ubx::SegPlan sp = ag_segmentation(h, n_cols);
   if (src && (st = start_deliveries(h, m.n, caller)) != UB_OK) return st;
   if ((st = fork_streams(h, caller, S)) != UB_OK) return st;
   // With deliveries, each unit's copies are issued just before its GEMM, in plan order, so
@@ -791,6 +831,7 @@ ub_status_t ag_call(ub_ctx* h, const void* src, int src_on_host, const void* w, 
     g.k = static_cast<int32_t>(H);
     g.batch = 1;
     g.concurrency = S;
+    set_segmentation(h, g, sp, u.row0, u.stream, S);
     const double flops = 2.0 * rows * H * n_cols;
     const double bytes = 2.0 * (rows * H + H * n_cols + rows * n_cols);
     st = timed_launch(h, s, 0, flops, bytes, [&] { return ubx::launch_gemm_bf16(g, s); },
@@ -1322,6 +1363,26 @@ UB_API ub_status_t ub_debug_set(ub_handle_t h, const char* key, int64_t value) {
     (k == "tail_tile_m" ? d.tail_m : d.tail_n) = static_cast<int32_t>(value);
     return UB_OK;
   }
+  if (k == "seg_row") {
+    if (value < 0 || value > (int64_t(1) << 31)) return fail(h, UB_ERR_INVALID_ARG, "seg_row=%lld", (long long)value);
+    d.seg_row = value;
+    return UB_OK;
+  }
+  if (k == "nseg") {
+    if (value < 0 || value > 64) return fail(h, UB_ERR_INVALID_ARG, "nseg=%lld", (long long)value);
+    d.nseg = static_cast<int32_t>(value);
+    return UB_OK;
+  }
+  if (k == "seg_reduce") {
+    if (value < 0 || value > 2) return fail(h, UB_ERR_INVALID_ARG, "seg_reduce=%lld", (long long)value);
+    d.seg_reduce = static_cast<int32_t>(value);
+    return UB_OK;
+  }
+  if (k == "seg_tile_m" || k == "seg_tile_n") {
+    if (value < 0 || value > 1024) return fail(h, UB_ERR_INVALID_ARG, "%s=%lld", key, (long long)value);
+    (k == "seg_tile_m" ? d.seg_m : d.seg_n) = static_cast<int32_t>(value);
+    return UB_OK;
+  }
   if (k == "tile_group") {
     if (value < 0 || value > 4096) return fail(h, UB_ERR_INVALID_ARG, "tile_group=%lld", (long long)value);
     d.tile_group = static_cast<int32_t>(value);
@@ -1348,6 +1409,31 @@ UB_API ub_status_t ub_debug_last_plan(ub_handle_t h, ub_tile_plan_t* out) {
   out->cut_row = h->last_plan.cut;
   out->tail_tile_m = h->last_plan.tail_m;
   out->tail_tile_n = h->last_plan.tail_n;
+  out->seg_row = h->last_plan.seg_row;
+  out->nseg = h->last_plan.nseg;
+  out->split = h->last_plan.split;
+  out->seg_tile_m = h->last_plan.seg_m;
+  out->seg_tile_n = h->last_plan.seg_n;
+  return UB_OK;
+}
+
+UB_API ub_status_t ub_register_scratch(ub_handle_t h, void* buf, size_t bytes) {
+  if (!h) return UB_ERR_NOT_INITIALIZED;
+  if (!buf && bytes == 0) {  // unregister
+    h->split_counters = nullptr;
+    h->split_parts = nullptr;
+    h->split_counters_n = h->split_parts_n = 0;
+    return UB_OK;
+  }
+  if (!buf || !aligned16(buf)) return fail(h, UB_ERR_INVALID_ARG, "scratch must be 16-byte aligned");
+  if (bytes < UB_SCRATCH_MIN_BYTES)
+    return fail(h, UB_ERR_BUFFER_TOO_SMALL, "scratch of %zu bytes, at least %d needed", bytes,
+                UB_SCRATCH_MIN_BYTES);
+  unsigned char* b = static_cast<unsigned char*>(buf);
+  h->split_counters = reinterpret_cast<uint32_t*>(b);
+  h->split_counters_n = UB_SCRATCH_COUNTER_BYTES / 4;
+  h->split_parts = reinterpret_cast<float*>(b + UB_SCRATCH_COUNTER_BYTES);
+  h->split_parts_n = static_cast<int64_t>((bytes - UB_SCRATCH_COUNTER_BYTES) / sizeof(float));
   return UB_OK;
 }
 

@@ -45,6 +45,10 @@ struct DebugOpts {
   int64_t cut_row = 0;             // > 0: cut a launch group's rows there (see ub_debug_set)
   int32_t tail_m = 0, tail_n = 0;  // tile of the second launch of a forced cut
   int32_t tile_group = 0;          // force the row-tile group size of the workgroup map
+  int64_t seg_row = -1;            // >= 0: force K segmentation from this row (with nseg)
+  int32_t nseg = 0;                // forced segment count (>= 2 with seg_row >= 0)
+  int32_t seg_m = 0, seg_n = 0;    // tile of forced split pieces (0: the library's choice)
+  int32_t seg_reduce = 0;          // forced split sum: 1 in the kernel, 2 a separate launch
   int64_t arrival_wait_us = 0;     // bound of a gated tile's wait (0: ~0.5 s)
   int32_t arrival_drop_flags = 0;  // write no flag after delivered chunks
 };
@@ -54,7 +58,23 @@ struct TilePlanRecord {
   int32_t tile_m = 0, tile_n = 0;
   int64_t cut = -1;
   int32_t tail_m = 0, tail_n = 0;
+  int64_t seg_row = -1;  // first K-segmented row of the launch group, or -1
+  int32_t nseg = 0;
+  int32_t split = 0;     // the segments ran as separate workgroups (split-K), summed in the
+                         // kernel (1) or by a separate launch (2); 0: one workgroup per tile
+  int32_t seg_m = 0, seg_n = 0;  // tile of the segmented rows' launch
 };
+
+// K segmentation of an all-gather-side GEMM call: rows [seg_row, T) of the call are summed
+// in nseg K segments (see gemm_bf16.hip), the rows before seg_row in one.  A function of the
+// call's shape alone, so that every schedule computes the same bits.  nseg <= 1: none.
+struct SegPlan {
+  int64_t seg_row = -1;
+  int32_t nseg = 1;
+  int32_t tile_m = 0, tile_n = 0;  // tile of the split pieces (0: the library's choice)
+  int32_t reduce = 0;              // 1: sum in the split kernel; 2: a separate launch (0: 2)
+};
+SegPlan choose_segmentation(int64_t T, int64_t n, int64_t k, int32_t batch);
 
 struct GemmArgs {
   const uint16_t* a;
@@ -96,6 +116,19 @@ struct GemmArgs {
   // debug settings of the handle (nullptr: none) and where to record the plan taken
   const DebugOpts* dbg = nullptr;
   TilePlanRecord* plan_out = nullptr;
+  // K segmentation (batch 1 only): rows of this launch at or after seg_row (in the
+  // launch's own row coordinates) are summed in nseg K segments; nseg <= 1: none.  With a
+  // split scratch (fp32 partial tiles and one zero word per tile, left zero) the segments
+  // run as separate workgroups; without one, or when the launch needs more than it holds,
+  // one workgroup per tile sums them in the same order.
+  int64_t seg_row = 0;
+  int32_t nseg = 1;
+  int32_t seg_m = 0, seg_n = 0;  // tile of the split pieces (0: the library's choice)
+  int32_t seg_reduce = 0;        // 1: sum in the split kernel; 2 (or 0): a separate launch
+  float* split_parts = nullptr;
+  int64_t split_parts_n = 0;   // floats
+  uint32_t* split_counters = nullptr;
+  int64_t split_counters_n = 0;
 };
 // Counter words the fused reduction of a handle can need: one range per compute stream,
 // each large enough for one launch over up to `capacity` rows, and one for a device-side

@@ -48,7 +48,7 @@ EXPORTS = (
     "ub_gemm_rs_chunked_fp8",
     "ub_quantize_e4m3", "ub_reduce_partials",
     "ub_set_kernel_timing", "ub_get_kernel_timing", "ub_prepare_streams", "ub_debug_set",
-    "ub_debug_last_plan", "ub_destroy", "ub_status_string", "ub_last_error",
+    "ub_debug_last_plan", "ub_register_scratch", "ub_destroy", "ub_status_string", "ub_last_error",
 )
 
 
@@ -73,7 +73,13 @@ class ub_plan_unit_t(ctypes.Structure):
 
 class ub_tile_plan_t(ctypes.Structure):
     _fields_ = [("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("cut_row", ctypes.c_int64),
-                ("tail_tile_m", ctypes.c_int32), ("tail_tile_n", ctypes.c_int32)]
+                ("tail_tile_m", ctypes.c_int32), ("tail_tile_n", ctypes.c_int32),
+                ("seg_row", ctypes.c_int64), ("nseg", ctypes.c_int32), ("split", ctypes.c_int32),
+                ("seg_tile_m", ctypes.c_int32), ("seg_tile_n", ctypes.c_int32)]
+
+
+UB_SCRATCH_COUNTER_BYTES = 256 * 1024
+UB_SCRATCH_MIN_BYTES = UB_SCRATCH_COUNTER_BYTES + 64 * 1024
 
 
 class ub_kernel_stats_t(ctypes.Structure):
@@ -115,6 +121,7 @@ _sig = {
     "ub_prepare_streams": (_I32, [_H, _I32, _I32]),
     "ub_debug_set": (_I32, [_H, ctypes.c_char_p, _I64]),
     "ub_debug_last_plan": (_I32, [_H, ctypes.POINTER(ub_tile_plan_t)]),
+    "ub_register_scratch": (_I32, [_H, _P, _SZ]),
     "ub_destroy": (_I32, [_H]),
     "ub_status_string": (ctypes.c_char_p, [_I32]),
     "ub_last_error": (ctypes.c_char_p, [_H]),
@@ -332,11 +339,19 @@ def ub_debug_set(h, key, value):
     _check(_lib.ub_debug_set(h, key.encode(), int(value)), h)
 
 
-def ub_debug_last_plan(h):
-    """Returns (tile_m, tile_n, cut_row, tail_tile_m, tail_tile_n) of the last GEMM launch group."""
+def ub_debug_last_plan(h, seg=False):
+    """(tile_m, tile_n, cut_row, tail_tile_m, tail_tile_n) of the last GEMM launch group, and
+    with seg=True also (seg_row, nseg, split, seg_tile_m, seg_tile_n)."""
     p = ub_tile_plan_t()
     _check(_lib.ub_debug_last_plan(h, ctypes.byref(p)), h)
-    return p.tile_m, p.tile_n, p.cut_row, p.tail_tile_m, p.tail_tile_n
+    base = (p.tile_m, p.tile_n, p.cut_row, p.tail_tile_m, p.tail_tile_n)
+    return base + (p.seg_row, p.nseg, p.split, p.seg_tile_m, p.seg_tile_n) if seg else base
+
+
+def ub_register_scratch(h, buf, nbytes):
+    if buf is not None:
+        _fits(buf, nbytes, "scratch")
+    _check(_lib.ub_register_scratch(h, _ptr(buf), int(nbytes)), h)
 
 
 def ub_destroy(h):

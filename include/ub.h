@@ -369,8 +369,10 @@ UB_API ub_status_t ub_gemm_ag_arrival(ub_handle_t h, const void* src, int32_t sr
 /* Number of tiles of the device-side chunk loop of ub_gemm_ag_arrival whose wait hit the
  * time bound on this handle's flag slot since the handle took the slot (0 if the handle
  * never gated on arrivals; ub_destroy clears the count, so a slot handed to a later handle
- * starts from zero).  A nonzero count means a chunk's flag never came; those tiles hold
- * NaN.  Synchronous (copies one word from the device). */
+ * starts from zero).  Split-K rows (ub_register_scratch) summed by a second launch count
+ * once per K segment whose wait ran out; summed in the kernel, once per tile.  A nonzero
+ * count means a chunk's flag never came; those tiles hold NaN.  Synchronous (copies one
+ * word from the device). */
 UB_API ub_status_t ub_arrival_timeouts(ub_handle_t h, uint32_t* count);
 
 /* The deliveries of ub_gemm_ag_arrival alone (same copies, order, stream and kind, no
@@ -482,7 +484,36 @@ typedef struct {
   int32_t tile_m, tile_n;            /* tile of the (first) launch */
   int64_t cut_row;                   /* -1: one launch; else the first row of a second launch */
   int32_t tail_tile_m, tail_tile_n;  /* tile of the second launch (0 without one) */
+  int64_t seg_row;                   /* first K-segmented row of the launch group, or -1 */
+  int32_t nseg;                      /* K segments of those rows (0 or >= 2) */
+  int32_t split;                     /* the segments ran as separate workgroups (split-K),
+                                        summed in the kernel (1) or by a second launch (2);
+                                        0: one workgroup per tile */
+  int32_t seg_tile_m, seg_tile_n;    /* tile of the segmented rows' launch */
 } ub_tile_plan_t;
+
+/* Split-K scratch of a handle (optional; all-gather side).  When a call's shape leaves the
+ * chip underused -- few rows (small T), or a last round of tiles that would hold only a
+ * few -- the library sums the rows concerned in K segments: for those rows,
+ *   C = bf16( ((P_0 + P_1) + ...) + P_{nseg-1} )  in fp32,  P_s = the products of k-steps
+ *   [s nk / nseg, (s+1) nk / nseg) (32-deep steps) accumulated from zero,
+ * a choice made from (T, n_cols, hidden) alone while scratch is registered (nothing is
+ * segmented without it), so that every schedule (chunk count, stream count, order,
+ * atomic_gemm, arrivals) computes the same bits.  The segments run as separate workgroups
+ * that write fp32 partial tiles to the scratch; a launch that needs more partial space than
+ * it has (the host loop gives each of its streams an equal share) falls back to one
+ * workgroup per tile summing the segments in the same order: the same bits, slower.  The
+ * library segments at most 1024 tiles' worth of partials (64 MiB) in one call, so
+ * UB_SCRATCH_COUNTER_BYTES + 64 MiB covers every choice of the device-side chunk loop.
+ * Layout: the first UB_SCRATCH_COUNTER_BYTES hold 32-bit counters that must be zero at
+ * registration (e.g. torch.zeros) and are left zero; the rest holds partials.  The buffer
+ * is caller-owned and must outlive its registration; calls of the handle must not overlap
+ * on different streams (they share it).  buf NULL and bytes 0 unregisters; bytes <
+ * UB_SCRATCH_MIN_BYTES -> UB_ERR_BUFFER_TOO_SMALL; a buf not 16-byte aligned ->
+ * UB_ERR_INVALID_ARG. */
+#define UB_SCRATCH_COUNTER_BYTES (256 * 1024)
+#define UB_SCRATCH_MIN_BYTES (UB_SCRATCH_COUNTER_BYTES + 64 * 1024)
+UB_API ub_status_t ub_register_scratch(ub_handle_t h, void* buf, size_t bytes);
 
 /* Debug and tuning settings of one handle, for tests and tile tuning; each starts at 0,
  * which leaves every choice to the library.  No environment variable changes what the
@@ -497,6 +528,15 @@ typedef struct {
  *                          cut_row on with the tile "tail_tile_m" x "tail_tile_n" (default
  *                          128x128); the first launch takes the forced tile, or 256x256.
  *                          Results do not depend on the cut.
+ *   "nseg", "seg_row"      K segmentation of the all-gather side: nseg 0 (default) lets the
+ *                          shape decide (see ub_register_scratch); 1 turns it off; >= 2
+ *                          sums rows from seg_row on (call rows, default 0) in nseg
+ *                          segments (clamped to the number of 32-deep k-steps).
+ *   "seg_tile_m", "seg_tile_n"  tile of forced split pieces (default 256 x 256; any of the
+ *                          bf16 tiles).
+ *   "seg_reduce"           sum of forced split pieces: 1 the tile's last piece sums in the
+ *                          kernel (per-tile counters in the scratch); 2 (default) a second
+ *                          launch sums every tile over the whole chip.
  *   "tile_group"           row tiles per group in the workgroup -> tile map (>= 1).
  *   "arrival_wait_us"      bound of a gated tile's wait in ub_gemm_ag_arrival, in
  *                          microseconds (0: ~0.5 s).

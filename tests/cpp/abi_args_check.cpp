@@ -88,6 +88,14 @@ int main() {
   ub_tile_plan_t plan;
   CHECK(ub_debug_last_plan(h, &plan) == UB_OK && plan.cut_row == -1);
   CHECK(ub_prepare_streams(h, 0, 0) == UB_ERR_INVALID_ARG);
+  CHECK(ub_debug_set(h, "nseg", 65) == UB_ERR_INVALID_ARG && ub_debug_set(h, "seg_row", -1) == UB_ERR_INVALID_ARG);
+  CHECK(ub_debug_set(h, "nseg", 4) == UB_OK && ub_debug_set(h, "seg_row", 128) == UB_OK);
+  CHECK(ub_debug_set(h, "nseg", 0) == UB_OK && ub_debug_set(h, "seg_row", 0) == UB_OK);
+  CHECK(ub_register_scratch(h, fake(), UB_SCRATCH_MIN_BYTES - 16) == UB_ERR_BUFFER_TOO_SMALL);
+  CHECK(ub_register_scratch(h, nullptr, 1 << 26) == UB_ERR_INVALID_ARG);
+  CHECK(ub_register_scratch(h, fake(), 1 << 26) == UB_OK);
+  CHECK(ub_register_scratch(h, nullptr, 0) == UB_OK);
+  CHECK(ub_register_scratch(nullptr, fake(), 1 << 26) == UB_ERR_NOT_INITIALIZED);
   for (int s = 0; s <= 11; ++s) CHECK(ub_status_string(static_cast<ub_status_t>(s))[0] == 'U');
   CHECK(ub_destroy(h) == UB_OK);
   CHECK(ub_destroy(nullptr) == UB_OK);

@@ -31,5 +31,6 @@ unsigned char* static_scratch_base(hipError_t* err) {
   return nullptr;
 }
 hipError_t launch_clear_words(uint32_t*, int64_t, hipStream_t) { return hipErrorNotSupported; }
+SegPlan choose_segmentation(int64_t, int64_t, int64_t, int32_t) { return SegPlan{}; }
 
 }  // namespace ubx

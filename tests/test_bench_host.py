@@ -158,3 +158,22 @@ def test_timeline_summary_on_synthetic_trace(tmp_path):
     md = out.read_text()
     assert "| a | 2 | 250.0 | 200.0 | 200.0 | 150.0 | 400.0 |" in md
     assert "| b | 2 | 180.0 | 100.0 | 80.0 | 0.0 | 180.0 |" in md
+
+
+def test_call_dispatches_and_plan_text():
+    """Dispatch count of a call from its plan: plain rows once (twice when cut), split-K
+    rows once when summed in the kernel or folded, twice with the separate sum."""
+    import bench
+    plain = (1024, 256, 256, -1, 0, 0, -1, 0, 0, 0, 0)
+    cut = (1024, 320, 256, 6400, 128, 128, -1, 0, 0, 0, 0)
+    seg_only = (1024, 128, 256, -1, 0, 0, 0, 6, 2, 128, 256)
+    lead_seg = (13216, 320, 256, -1, 0, 0, 13056, 12, 2, 128, 128)
+    lead_cut_seg = (13216, 320, 256, 6400, 256, 256, 13056, 4, 1, 256, 256)
+    folded = (1024, 128, 128, -1, 0, 0, 0, 6, 0, 128, 128)
+    assert [bench._call_dispatches(p) for p in (plain, cut, seg_only, lead_seg, lead_cut_seg, folded)] == \
+        [1, 2, 2, 3, 3, 1]
+    assert bench.describe_plan(plain[1:]) == "256x256"
+    assert bench.describe_plan(cut[1:]) == "320x256 cut 6400: 128x128"
+    assert bench.describe_plan(seg_only[1:]) == "split-K from row 0: 6 x 128x256 r2"
+    assert bench.describe_plan(lead_seg[1:]) == "320x256; split-K from row 13056: 12 x 128x128 r2"
+    assert bench.describe_plan(folded[1:]) == "split-K from row 0: 6 x 128x128 fold"
