@@ -36,7 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 GEMM_SRC = os.path.join(ROOT, "chunked_tp_overlap_amd", "csrc", "gemm_bf16.hip")
 REDUCE_SRC = os.path.join(ROOT, "chunked_tp_overlap_amd", "csrc", "reduce_partials.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-PROFILE_PASSES = ("gqa", "qkv", "fc1", "fc2", "reduce", "fp8", "arrival")
+PROFILE_PASSES = ("gqa", "qkv", "fc1", "fc2", "reduce", "fp8", "arrival", "host")
 
 
 def parse_args():
@@ -57,7 +57,8 @@ def parse_args():
                         "byte counters, and print one JSON line (gqa: the headline sweep; qkv, "
                         "fc1: their microbatches; fc2: the slice GEMMs and reductions over its T "
                         "sweep; reduce: the fc2 reduction at T = 16384; fp8: the qkv step on an "
-                        "fp8 buffer; arrival: separated arrival-stand-in calls of every mode)")
+                        "fp8 buffer; arrival: separated arrival-stand-in calls of every mode; "
+                        "host: separated qkv host-loop and device-loop calls)")
     return p.parse_args()
 
 
@@ -236,7 +237,8 @@ def main():
     dev = torch.device("cuda:0")
     if args.profile_pass:
         fn = {"gqa": profile_ag, "qkv": profile_ag, "fc1": profile_ag, "fc2": profile_fc2,
-              "reduce": profile_reduce, "fp8": profile_fp8, "arrival": profile_arrival}[args.profile_pass]
+              "reduce": profile_reduce, "fp8": profile_fp8, "arrival": profile_arrival,
+              "host": profile_host}[args.profile_pass]
         res = fn(ub, wl, torch, np, dev, args)
         calibration_copy(torch, dev)
         print(json.dumps(res), flush=True)
@@ -265,13 +267,15 @@ def main():
         pass
     roofline = {
         "bound": "mfma",
-        "kernel": "gemm_bf16_pingpong / gemm_bf16_pipelined (device-side chunk loop; one call = "
-                  "one launch, or two when the plan cuts a nearly empty last round)",
+        "kernel": "gemm_bf16_* (device-side chunk loop; one call = one ping-pong/pipelined "
+                  "launch, two when the plan cuts a nearly empty last round, plus a split-K "
+                  "launch and its gemm_bf16_split_reduce for rows the plan sums in K segments)",
         "achieved": round(achieved, 2), "peak": MFMA_PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
         "frac": round(achieved / MFMA_PEAK_BF16_TFLOPS, 4),
         "traffic": traffic,
-        "traffic_note": (f"HBM bytes per call, mean over the sweep, from rocprofv3 FETCH_SIZE + "
-                         f"WRITE_SIZE passes of this kernel source ({traffic_src})" if traffic
+        "traffic_note": (f"HBM bytes per call, mean over the sweep, from an earlier rocprofv3 "
+                         f"FETCH_SIZE + WRITE_SIZE profile run of this same kernel source "
+                         f"({traffic_src}); not measured in this run" if traffic
                          else "no counter pass of this kernel source"),
         "calls": calls,
         "avg_call_us": round(stats["total_ms"] * 1e3 / max(1, calls), 3),
@@ -823,6 +827,42 @@ def profile_reduce(ub, wl, torch, np, dev, args):
     out["src_hash"] = src_hash(REDUCE_SRC)
     ub.ub_destroy(h)
     return out
+
+
+def profile_host(ub, wl, torch, np, dev, args):
+    """The pages' default schedule on qkv, for a rocprofv3 kernel trace: per T in (4096,
+    6912, 8192), `steps` host-loop calls (8 ring chunks, one launch each, on 3 streams),
+    then `steps` device-side-loop calls, each followed by a device synchronisation and a
+    20 ms pause, so that every call stands alone on the timeline.  Prints the modes in
+    trace order."""
+    w = wl.qkv()
+    ra, rw, _ = w.seeds()
+    ub_bytes, _ = ub.ub_required_bytes(w.capacity, w.hidden, w.tp)
+    ub_t = torch.from_numpy(wl.activations(w, w.capacity, ra).view(np.int16).ravel()).to(dev)
+    w_t = torch.from_numpy(wl.weights(w, rw).view(np.int16)).to(dev)
+    c_t = torch.empty((w.capacity, w.n_cols), dtype=torch.int16, device=dev)
+    h = ub.ub_init(w.capacity, w.hidden, w.tp, ub.UB_DTYPE_BF16, ub_t, ub_bytes)
+    ub.ub_prepare_streams(h, w.num_max_streams)
+    scratch = register_scratch(ub, torch, dev, h)  # noqa: F841 (held while h is used)
+    modes = []
+    for T in (4096, 6912, 8192):
+        ub.ub_set_active_shape(h, (T, w.hidden))
+        for label, atomic in (("host_loop", False), ("device_loop", True)):
+            cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, w.aggregate, atomic)
+            call = lambda: ub.ub_gemm_ag_chunked(h, w_t, w.n_cols, w.n_cols, c_t, w.n_cols, cfg)
+            call()  # untimed: first use of this shape
+            torch.cuda.synchronize()
+            time.sleep(0.02)
+            for _ in range(args.steps):
+                call()
+                torch.cuda.synchronize()
+                time.sleep(0.02)
+            modes.append({"mode": f"{label} T={T}", "calls": args.steps + 1,
+                          "gflop": round(2.0 * T * w.hidden * w.n_cols / 1e9, 3)})
+    ub.ub_destroy(h)
+    return {"profile_pass": "host", "workload": w.name, "chunks": w.tp,
+            "streams": w.num_max_streams, "modes": modes,
+            "gpu_max_hw_queues": os.environ.get("GPU_MAX_HW_QUEUES", "(runtime default)")}
 
 
 ARRIVAL_MODES = (("host_loop_pinned_host", True, True, False),

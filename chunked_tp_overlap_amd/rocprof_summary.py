@@ -21,6 +21,10 @@ over algorithmic bytes.
 arrival` under `rocprofv3 --kernel-trace --memory-copy-trace`: per delivery mode, the
 median call span, the time copies and GEMMs are active, and their overlap.
 
+--streams DIR --bench-json FILE --out FILE summarises `bench.py --profile-pass host` under
+`rocprofv3 --kernel-trace`: per mode, the median call span, the GEMM kernels' summed time,
+the time at least one runs, their mean and maximum concurrency and the busy time per stream.
+
 --util DIR adds a fourth run, --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES
 SQ_BUSY_CU_CYCLES, read per dispatch with that run's own timestamps:
   - GRBM_GUI_ACTIVE sums the busy cycles of the 8 XCDs' GRBMs, so /8 is the dispatch's
@@ -93,6 +97,8 @@ def counter_timed_dispatches(dirname, counters, kernel, n_timed):
 
 
 UTIL_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES")
+LDS_COUNTERS = ("SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS",
+                "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_INSTS_MFMA")
 
 
 def _union(iv):
@@ -176,7 +182,106 @@ def timeline(kt_dir, bench_json, out, title, command):
     print("\n".join(lines[:14 + len(top["modes"])]))
 
 
+def _groups(ev, gap_ns=5_000_000):
+    """Events (start, end, ...) sorted by start, split where a gap of more than gap_ns
+    follows every event so far."""
+    groups, cur, last_end = [], [], 0
+    for e in ev:
+        if cur and e[0] - last_end > gap_ns:
+            groups.append(cur)
+            cur = []
+        if not cur:
+            last_end = e[1]
+        cur.append(e)
+        last_end = max(last_end, e[1])
+    if cur:
+        groups.append(cur)
+    return groups
+
+
+def _max_concurrency(iv):
+    pts = sorted([(a, 1) for a, _ in iv] + [(b, -1) for _, b in iv], key=lambda x: (x[0], x[1]))
+    cur = best = 0
+    for _, d in pts:
+        cur += d
+        best = max(best, cur)
+    return best
+
+
+def streams(kt_dir, bench_json, out, title, command):
+    """Per-call stream timelines of `bench.py --profile-pass host` from a kernel trace: the
+    calls are the groups of GEMM kernels separated by the pass's 20 ms pauses, assigned to
+    the pass's modes in order.  Per call: span (first start to last end), the GEMM kernels'
+    summed durations, the time at least one runs (union), their mean concurrency (sum /
+    union), the most that run at once, the streams used, and the time each stream has a
+    kernel running."""
+    with open(bench_json) as f:
+        top = json.loads([ln for ln in f if ln.startswith("{")][-1])
+    ev = []
+    for r in _rows(_one(kt_dir, "_kernel_trace.csv")):
+        if "gemm_bf16" in r["Kernel_Name"]:
+            ev.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r.get("Stream_Id", ""),
+                       r["Kernel_Name"]))
+    ev.sort()
+    calls = _groups(ev)
+    want = sum(m["calls"] for m in top["modes"])
+    if len(calls) < want:
+        raise SystemExit(f"found {len(calls)} calls, expected {want}")
+    calls = calls[-want:]
+    lines = [f"# rocprofv3 summary: {title}", ""]
+    if command:
+        lines += ["Commands (from the repository root):", "", "```", command.strip(), "```", ""]
+    lines += [f"{top.get('workload')}: {top.get('chunks')} chunks on {top.get('streams')} streams "
+              f"(host loop), hardware queues {top.get('gpu_max_hw_queues')}.  Per mode, medians over "
+              f"its calls (the first call of each mode included):", "",
+              "| mode | calls | span us | TFLOP/s over span | kernels | kernel sum us | union us | "
+              "mean concurrency | max concurrency | streams | busy us per stream |",
+              "|---|---|---|---|---|---|---|---|---|---|---|"]
+    i = 0
+    details = []
+    for m in top["modes"]:
+        rows = []
+        for g in calls[i:i + m["calls"]]:
+            iv = [(a, b) for a, b, _, _ in g]
+            span = (max(b for _, b in iv) - g[0][0]) / 1e3
+            ksum = sum(b - a for a, b in iv) / 1e3
+            uni = _union(iv) / 1e3
+            per = {}
+            for a, b, st, _ in g:
+                per.setdefault(st, []).append((a, b))
+            busy = sorted((_union(v) / 1e3 for v in per.values()), reverse=True)
+            rows.append((span, len(g), ksum, uni, ksum / uni, _max_concurrency(iv), len(per), busy))
+        i += m["calls"]
+        med = [statistics.median(r[j] for r in rows) for j in range(7)]
+        busy = rows[len(rows) // 2][7]
+        tf = m["gflop"] / med[0] * 1e3 if m.get("gflop") else 0.0  # GFLOP / us -> TFLOP/s
+        lines.append(f"| {m['mode']} | {m['calls']} | {med[0]:.1f} | {tf:.0f} | {med[1]:.0f} | {med[2]:.1f} | "
+                     f"{med[3]:.1f} | {med[4]:.2f} | {med[5]:.0f} | {med[6]:.0f} | "
+                     f"{', '.join(f'{b:.1f}' for b in busy)} |")
+        g = calls[i - 1]
+        t0 = g[0][0]
+        details += ["", f"### {m['mode']}: its last call", "", "| stream | start us | end us | us | kernel |",
+                    "|---|---|---|---|---|"]
+        details += [f"| {st} | {(a - t0) / 1e3:.1f} | {(b - t0) / 1e3:.1f} | {(b - a) / 1e3:.1f} | `{n[:60]}` |"
+                    for a, b, st, n in g]
+    lines += ["", "`mean concurrency` = summed kernel time / time at least one GEMM kernel runs."]
+    lines += details
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines[:12 + len(top["modes"])]))
+
+
 def main():
+    if "--streams" in sys.argv:
+        p = argparse.ArgumentParser()
+        p.add_argument("--streams", required=True, help="rocprofv3 --kernel-trace directory")
+        p.add_argument("--bench-json", required=True)
+        p.add_argument("--title", default="host-loop stream timelines")
+        p.add_argument("--command", default="")
+        p.add_argument("--out", required=True)
+        a = p.parse_args()
+        streams(a.streams, a.bench_json, a.out, a.title, a.command)
+        return
     if "--timeline" in sys.argv:
         p = argparse.ArgumentParser()
         p.add_argument("--timeline", required=True, help="rocprofv3 --kernel-trace --memory-copy-trace directory")
@@ -200,6 +305,8 @@ def main():
     p.add_argument("--traffic", default=None, help="write the traffic figure here (JSON)")
     p.add_argument("--util", default=None,
                    help="rocprofv3 --pmc " + " ".join(UTIL_COUNTERS) + " output directory")
+    p.add_argument("--lds", default=None,
+                   help="rocprofv3 --pmc " + " ".join(LDS_COUNTERS) + " output directory")
     p.add_argument("--peak-flop-per-cu-cycle", type=float, default=4096.0,
                    help="dense MFMA FLOP per CU per cycle of the kernel's dtype (bf16 4096, fp8 8192)")
     a = p.parse_args()
@@ -294,6 +401,27 @@ def main():
             lines.append(f"- MFMA work issued: {mfma:.4g} SIMD-cycles, {util['mfma_issued_per_algorithmic']:.3f}x "
                          f"the algorithmic FLOPs at {a.peak_flop_per_cu_cycle / 4:.0f} FLOP per "
                          f"SIMD-cycle (the excess is padded rows of partial tiles)")
+    if a.lds:
+        ds = counter_timed_dispatches(a.lds, LDS_COUNTERS, a.kernel, n_timed)
+        tot = {c: sum(d[c] for d in ds) for c in LDS_COUNTERS}
+        ratio = lambda x, y: tot[x] / tot[y] if tot[y] else float("nan")
+        lines += ["", "## Where the waves wait (--pmc " + " ".join(LDS_COUNTERS) + ")", "",
+                  f"Sums over the last {len(ds)} dispatches of the counter run:", "",
+                  "| counter | total |", "|---|---|"]
+        lines += [f"| {c} | {tot[c]:.5g} |" for c in LDS_COUNTERS]
+        lines += ["",
+                  f"- LDS instructions per MFMA instruction: SQ_INSTS_LDS / SQ_INSTS_MFMA = "
+                  f"{ratio('SQ_INSTS_LDS', 'SQ_INSTS_MFMA'):.3f}",
+                  f"- bank conflicts: SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS = "
+                  f"{ratio('SQ_LDS_BANK_CONFLICT', 'SQ_ACTIVE_INST_LDS'):.4f} of the LDS-active cycles",
+                  f"- wave-cycles spent waiting to issue an LDS instruction: SQ_WAIT_INST_LDS / "
+                  f"SQ_WAVE_CYCLES = {ratio('SQ_WAIT_INST_LDS', 'SQ_WAVE_CYCLES'):.4f}",
+                  f"- wave-cycles spent waiting on any dependency or counter: SQ_WAIT_ANY / "
+                  f"SQ_WAVE_CYCLES = {ratio('SQ_WAIT_ANY', 'SQ_WAVE_CYCLES'):.4f}"]
+        if gflop:
+            lines.append(f"- MFMA math issued: SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 FLOP = "
+                         f"{tot['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9:.1f} GFLOP against "
+                         f"{gflop:.1f} algorithmic ({tot['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9 / gflop:.3f}x)")
     with open(a.out, "w") as f:
         f.write("\n".join(lines) + "\n")
     if a.traffic:

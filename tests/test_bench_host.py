@@ -177,3 +177,35 @@ def test_call_dispatches_and_plan_text():
     assert bench.describe_plan(seg_only[1:]) == "split-K from row 0: 6 x 128x256 r2"
     assert bench.describe_plan(lead_seg[1:]) == "320x256; split-K from row 13056: 12 x 128x128 r2"
     assert bench.describe_plan(folded[1:]) == "split-K from row 0: 6 x 128x128 fold"
+
+
+def test_streams_summary_on_synthetic_trace(tmp_path):
+    """Host-loop timelines: mode a runs three kernels on three streams, two of them at once
+    ([0, 100), [50, 150), [150, 200) us); mode b two kernels back to back on one stream."""
+    d = tmp_path / "kt"
+    d.mkdir()
+    kt = []
+    t = 50_000_000
+    for mode in ("a", "b"):
+        for _ in range(2):
+            if mode == "a":
+                kt += [[KERNEL, t, t + 100_000, 1], [KERNEL, t + 50_000, t + 150_000, 2],
+                       [KERNEL, t + 150_000, t + 200_000, 3]]
+            else:
+                kt += [[KERNEL, t, t + 60_000, 0], [KERNEL, t + 60_000, t + 100_000, 0]]
+            t += 20_000_000
+    kt.insert(0, ["void at::native::fill(int)", 1_000_000, 1_010_000, 0])
+    _write(d / "kt_kernel_trace.csv", ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Stream_Id"], kt)
+    bench = tmp_path / "b.json"
+    bench.write_text(json.dumps({"profile_pass": "host", "workload": "w", "chunks": 8, "streams": 3,
+                                 "modes": [{"mode": "a", "calls": 2, "gflop": 20.0},
+                                           {"mode": "b", "calls": 2, "gflop": 10.0}]}) + "\n")
+    out = tmp_path / "st.md"
+    r = subprocess.run([sys.executable, "-m", "chunked_tp_overlap_amd.rocprof_summary", "--streams", str(d),
+                        "--bench-json", str(bench), "--out", str(out)],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 0, r.stderr
+    md = out.read_text()
+    # span 200 us, 20 GFLOP -> 100 TFLOP/s; sum 250, union 200, mean 1.25, max 2, 3 streams
+    assert "| a | 2 | 200.0 | 100 | 3 | 250.0 | 200.0 | 1.25 | 2 | 3 | 100.0, 100.0, 50.0 |" in md
+    assert "| b | 2 | 100.0 | 100 | 2 | 100.0 | 100.0 | 1.00 | 1 | 1 | 100.0 |" in md
