@@ -1172,7 +1172,12 @@ hipError_t launch_gemm_bf16_units(const GemmArgs& g, const GemmUnits& u, hipStre
   const bool seg = nseg > 1 && g.batch == 1 && g.fuse_nslots == 0;
   const GemmUnits plain = seg ? clip_units(u, 0, g.seg_row) : u;
   const GemmUnits segu = seg ? clip_units(u, g.seg_row, INT64_MAX) : GemmUnits{0, {}, {}};
-  if (g.plan_out) *g.plan_out = TilePlanRecord{};
+  if (g.plan_out) {  // this launch group's plan; the call's dispatch count carries on
+    const int32_t d = g.plan_out->dispatches, pieces = g.plan_out->rs_pieces;
+    *g.plan_out = TilePlanRecord{};
+    g.plan_out->dispatches = d;
+    g.plan_out->rs_pieces = pieces;
+  }
   hipError_t e = hipSuccess;
   if (plain.n > 0) {
     const TilePlan plan = choose_plan(g, plain);
@@ -1185,6 +1190,7 @@ hipError_t launch_gemm_bf16_units(const GemmArgs& g, const GemmUnits& u, hipStre
       g.plan_out->tail_m = plan.cut >= 0 ? b.bm : 0;
       g.plan_out->tail_n = plan.cut >= 0 ? b.bn : 0;
     }
+    if (g.plan_out) g.plan_out->dispatches += plan.cut < 0 ? 1 : 2;
     if (plan.cut < 0) {
       e = launch_kind(plan.kind, g, plain, stream);
     } else {
@@ -1218,6 +1224,7 @@ hipError_t launch_gemm_bf16_units(const GemmArgs& g, const GemmUnits& u, hipStre
       g.plan_out->split = split ? reduce : 0;
       g.plan_out->seg_m = o->bm;
       g.plan_out->seg_n = o->bn;
+      g.plan_out->dispatches += split && reduce == 2 ? 2 : 1;
     }
     e = split ? launch_split(o->kind, g, segu, stream, nseg, reduce)
               : launch<PL128x128>(&gemm_bf16_seg<PL128x128, 0>, g, segu, stream, 1, nseg);

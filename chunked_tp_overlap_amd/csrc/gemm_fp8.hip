@@ -323,7 +323,9 @@ hipError_t launch_gemm_fp8_units(const GemmF8Args& g, const GemmUnits& u, hipStr
     if (u.rows[i] < 0 || u.row0[i] < 0) return hipErrorInvalidValue;
   const bool small = use_128(g, u);
   if (g.plan_out) {
+    const int32_t d = g.plan_out->dispatches;
     *g.plan_out = TilePlanRecord{};
+    g.plan_out->dispatches = d + 1;
     g.plan_out->tile_m = small ? 128 : 256;
     g.plan_out->tile_n = 256;
   }

@@ -32,6 +32,7 @@
 #include "ub_internal.h"
 
 constexpr int kMaxArrivalChunks = 64;
+constexpr int kMaxRsPieces = 8;
 
 struct ub_ctx {
   // registration
@@ -66,6 +67,7 @@ struct ub_ctx {
   // arrival stand-in: copy stream, one arrival event per chunk, its join event
   hipStream_t copy_stream = nullptr;
   hipEvent_t ev_arrive[kMaxArrivalChunks] = {};
+  hipEvent_t ev_piece[kMaxRsPieces] = {};  // pipelined device-side reduce-scatter
   hipEvent_t ev_copy_join = nullptr;
   // device-side arrival gating: this handle's slot of arrival flags (-1: none yet)
   int ready_slot = -1;
@@ -180,6 +182,10 @@ ub_status_t ensure_device(ub_ctx* h, int need_streams) {
     h->device = dev;
     e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
     if (e != hipSuccess) return hip_fail(h, e, "hipEventCreate");
+    for (hipEvent_t& ev : h->ev_piece) {
+      e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+      if (e != hipSuccess) return hip_fail(h, e, "hipEventCreate");
+    }
   } else if (h->device != dev) {
     return fail(h, UB_ERR_INVALID_ARG, "handle is bound to device %d but device %d is current",
                 h->device, dev);
@@ -749,6 +755,7 @@ ub_status_t ag_call(ub_ctx* h, const void* src, int src_on_host, const void* w, 
   if (src && (st = check_arrival(h, src, src_on_host, cfg)) != UB_OK) return st;
   const int64_t H = h->hidden;
   hipStream_t caller = static_cast<hipStream_t>(stream);
+  h->last_plan = ubx::TilePlanRecord{};
 
   if (cfg->atomic_gemm) {
     // One launch walks every unit in plan order on the caller's stream.
@@ -942,6 +949,7 @@ UB_API ub_status_t ub_gemm_ag_chunked_fp8(ub_handle_t h, const void* w, int64_t 
     return fail(h, UB_ERR_UNSUPPORTED, "hidden=%lld must be a multiple of %d", (long long)H,
                 ubx::kGemmF8KStep);
   if ((st = check_forced_tile(h, true)) != UB_OK) return st;
+  h->last_plan = ubx::TilePlanRecord{};
   ubx::GemmF8Args g{};
   g.dbg = &h->dbg;
   g.plan_out = &h->last_plan;
@@ -1029,6 +1037,44 @@ ub_status_t check_rs_call(ub_ctx* h, const void* a, int64_t k, int64_t lda, cons
 }
 
 // Body of both bf16 reduce-scatter entry points, after check_rs_call.
+// Rows [lo, hi) of the units, in the same order (empty pieces dropped).
+ubx::GemmUnits clip_rows(const ubx::GemmUnits& u, int64_t lo, int64_t hi) {
+  ubx::GemmUnits out;
+  out.n = 0;
+  for (int i = 0; i < u.n; ++i) {
+    const int64_t r0 = std::max<int64_t>(u.row0[i], lo);
+    const int64_t r1 = std::min<int64_t>((int64_t)u.row0[i] + u.rows[i], hi);
+    if (r1 <= r0) continue;
+    out.row0[out.n] = static_cast<int32_t>(r0);
+    out.rows[out.n] = static_cast<int32_t>(r1 - r0);
+    ++out.n;
+  }
+  return out;
+}
+
+// Row pieces of the pipelined device-side reduce-scatter: piece p's slice GEMMs run on the
+// caller's stream, then its reduction on worker stream 1 while the next piece's GEMMs run.
+// Cuts fall on multiples of 1280 rows (whole bands of the 256- and 320-row tiles), as near
+// to p T / P as that allows; returns the number of pieces (cuts[0] = 0, cuts[n] = T).
+int rs_cuts(int64_t T, int P, int64_t* cuts) {
+  constexpr int64_t kBand = 1280;
+  int n = 0;
+  cuts[0] = 0;
+  for (int p = 1; p < P; ++p) {
+    const int64_t c = (T * p / P + kBand / 2) / kBand * kBand;
+    if (c > cuts[n] && c < T) cuts[++n] = c;
+  }
+  cuts[++n] = T;
+  return n;
+}
+
+// Pieces of the device-side reduce-scatter at the active T: forced by the debug settings,
+// else 1 (one launch of every slice GEMM, then one reduction).
+int rs_pieces(const ub_ctx* h) {
+  if (h->dbg.rs_pieces > 0) return h->dbg.rs_pieces;
+  return 1;
+}
+
 ub_status_t rs_call(ub_ctx* h, const RsTarget& tg, const void* a, int64_t k, int64_t lda,
                     const void* w, int64_t ldw, void* out, int64_t ldo,
                     const ub_overlap_cfg_t* cfg, hipStream_t caller) {
@@ -1039,6 +1085,7 @@ ub_status_t rs_call(ub_ctx* h, const RsTarget& tg, const void* a, int64_t k, int
   const int32_t tp = h->tp;
   const bool ring = cfg->reduce_order == UB_REDUCE_RING;
   const bool fuse = cfg->fuse_reduce != 0;
+  h->last_plan = ubx::TilePlanRecord{};
   // Fused reduction: each compute stream's launches run one after another and leave
   // their counters at zero, so each stream counts in its own range; the device-side loop
   // uses the whole array.
@@ -1084,14 +1131,39 @@ ub_status_t rs_call(ub_ctx* h, const RsTarget& tg, const void* a, int64_t k, int
     g.batch = tp;
     g.concurrency = 1;
     set_fuse(g, 0, -1);
-    st = timed_launch(h, caller, 0, 2.0 * T * k * H + (fuse ? fused_flops * T : 0.0),
-                      2.0 * (T * k + k * H + tp * T * H) + (fuse ? fused_bytes * T : 0.0),
-                      [&] { return ubx::launch_gemm_bf16_units(g, units, caller); },
-                      "slice GEMM launch");
-    if (st != UB_OK || fuse) return st;
-    const ubx::ReduceArgs r = reduce_args(h, 0, T, out, ldo, ring, tg.ws);
-    return timed_launch(h, caller, 1, double(tp - 1) * T * H, 2.0 * (tp + 1) * T * H,
-                        [&] { return ubx::launch_reduce_partials(r, caller); }, "reduce launch");
+    int64_t cuts[kMaxRsPieces + 1];
+    const int np = fuse ? 1 : rs_cuts(T, rs_pieces(h), cuts);
+    if (np <= 1) {
+      st = timed_launch(h, caller, 0, 2.0 * T * k * H + (fuse ? fused_flops * T : 0.0),
+                        2.0 * (T * k + k * H + tp * T * H) + (fuse ? fused_bytes * T : 0.0),
+                        [&] { return ubx::launch_gemm_bf16_units(g, units, caller); },
+                        "slice GEMM launch");
+      if (st != UB_OK || fuse) return st;
+      const ubx::ReduceArgs r = reduce_args(h, 0, T, out, ldo, ring, tg.ws);
+      return timed_launch(h, caller, 1, double(tp - 1) * T * H, 2.0 * (tp + 1) * T * H,
+                          [&] { return ubx::launch_reduce_partials(r, caller); }, "reduce launch");
+    }
+    // pipelined: piece p's GEMMs on the caller's stream, its reduction on worker stream 1
+    // after an event, overlapping piece p + 1's GEMMs; the caller joins stream 1 at the end
+    if ((st = ensure_device(h, 2)) != UB_OK) return st;
+    hipStream_t rs = h->streams[1];
+    h->last_plan.rs_pieces = np;
+    for (int p = 0; p < np; ++p) {
+      const int64_t lo = cuts[p], rows = cuts[p + 1] - cuts[p];
+      const ubx::GemmUnits pu = clip_rows(units, lo, cuts[p + 1]);
+      st = timed_launch(h, caller, 0, 2.0 * rows * k * H, 2.0 * (rows * k + k * H + tp * rows * H),
+                        [&] { return ubx::launch_gemm_bf16_units(g, pu, caller); },
+                        "slice GEMM launch");
+      if (st != UB_OK) return st;
+      hipError_t e = hipEventRecord(h->ev_piece[p], caller);
+      if (e == hipSuccess) e = hipStreamWaitEvent(rs, h->ev_piece[p], 0);
+      if (e != hipSuccess) return hip_fail(h, e, "piece event");
+      const ubx::ReduceArgs r = reduce_args(h, lo, rows, out, ldo, ring, tg.ws);
+      st = timed_launch(h, rs, 1, double(tp - 1) * rows * H, 2.0 * (tp + 1) * rows * H,
+                        [&] { return ubx::launch_reduce_partials(r, rs); }, "reduce launch");
+      if (st != UB_OK) return st;
+    }
+    return join_streams(h, caller, 2);
   }
 
   const int S = h->plan.n_streams;
@@ -1224,6 +1296,7 @@ UB_API ub_status_t ub_gemm_rs_chunked_fp8(ub_handle_t h, const void* a, int64_t 
   const int32_t tp = h->tp;
   // slice s: columns [s*ks, (s+1)*ks) of A's rows and of W's rows; partial s at workspace
   // element s*T*H (offsets from the active T)
+  h->last_plan = ubx::TilePlanRecord{};
   ubx::GemmF8Args g{};
   g.dbg = &h->dbg;
   g.plan_out = &h->last_plan;
@@ -1373,6 +1446,12 @@ UB_API ub_status_t ub_debug_set(ub_handle_t h, const char* key, int64_t value) {
     d.nseg = static_cast<int32_t>(value);
     return UB_OK;
   }
+  if (k == "rs_pieces") {
+    if (value < 0 || value > kMaxRsPieces)
+      return fail(h, UB_ERR_INVALID_ARG, "rs_pieces=%lld", (long long)value);
+    d.rs_pieces = static_cast<int32_t>(value);
+    return UB_OK;
+  }
   if (k == "seg_reduce") {
     if (value < 0 || value > 2) return fail(h, UB_ERR_INVALID_ARG, "seg_reduce=%lld", (long long)value);
     d.seg_reduce = static_cast<int32_t>(value);
@@ -1414,6 +1493,8 @@ UB_API ub_status_t ub_debug_last_plan(ub_handle_t h, ub_tile_plan_t* out) {
   out->split = h->last_plan.split;
   out->seg_tile_m = h->last_plan.seg_m;
   out->seg_tile_n = h->last_plan.seg_n;
+  out->dispatches = h->last_plan.dispatches;
+  out->rs_pieces = h->last_plan.rs_pieces;
   return UB_OK;
 }
 
@@ -1456,6 +1537,8 @@ UB_API ub_status_t ub_destroy(ub_handle_t h) {
       (void)hipEventDestroy(h->ev_copy_join);
     }
     for (hipEvent_t ev : h->ev_arrive)
+      if (ev) (void)hipEventDestroy(ev);
+    for (hipEvent_t ev : h->ev_piece)
       if (ev) (void)hipEventDestroy(ev);
     for (hipEvent_t ev : h->free_events) (void)hipEventDestroy(ev);
     if (h->ready) {  // the next handle to take this slot starts with no counted timeouts

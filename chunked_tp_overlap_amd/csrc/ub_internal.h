@@ -49,6 +49,7 @@ struct DebugOpts {
   int32_t nseg = 0;                // forced segment count (>= 2 with seg_row >= 0)
   int32_t seg_m = 0, seg_n = 0;    // tile of forced split pieces (0: the library's choice)
   int32_t seg_reduce = 0;          // forced split sum: 1 in the kernel, 2 a separate launch
+  int32_t rs_pieces = 0;           // device-side reduce-scatter row pieces (0: the library's)
   int64_t arrival_wait_us = 0;     // bound of a gated tile's wait (0: ~0.5 s)
   int32_t arrival_drop_flags = 0;  // write no flag after delivered chunks
 };
@@ -63,6 +64,8 @@ struct TilePlanRecord {
   int32_t split = 0;     // the segments ran as separate workgroups (split-K), summed in the
                          // kernel (1) or by a separate launch (2); 0: one workgroup per tile
   int32_t seg_m = 0, seg_n = 0;  // tile of the segmented rows' launch
+  int32_t dispatches = 0;        // GEMM kernels the call launched (all its launch groups)
+  int32_t rs_pieces = 0;         // row pieces of a pipelined device-side reduce-scatter
 };
 
 // K segmentation of an all-gather-side GEMM call: rows [seg_row, T) of the call are summed

@@ -75,7 +75,8 @@ class ub_tile_plan_t(ctypes.Structure):
     _fields_ = [("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("cut_row", ctypes.c_int64),
                 ("tail_tile_m", ctypes.c_int32), ("tail_tile_n", ctypes.c_int32),
                 ("seg_row", ctypes.c_int64), ("nseg", ctypes.c_int32), ("split", ctypes.c_int32),
-                ("seg_tile_m", ctypes.c_int32), ("seg_tile_n", ctypes.c_int32)]
+                ("seg_tile_m", ctypes.c_int32), ("seg_tile_n", ctypes.c_int32),
+                ("dispatches", ctypes.c_int32), ("rs_pieces", ctypes.c_int32)]
 
 
 UB_SCRATCH_COUNTER_BYTES = 256 * 1024
@@ -346,6 +347,13 @@ def ub_debug_last_plan(h, seg=False):
     _check(_lib.ub_debug_last_plan(h, ctypes.byref(p)), h)
     base = (p.tile_m, p.tile_n, p.cut_row, p.tail_tile_m, p.tail_tile_n)
     return base + (p.seg_row, p.nseg, p.split, p.seg_tile_m, p.seg_tile_n) if seg else base
+
+
+def ub_debug_plan(h):
+    """Every field of the last call's plan record as a dict."""
+    p = ub_tile_plan_t()
+    _check(_lib.ub_debug_last_plan(h, ctypes.byref(p)), h)
+    return {name: getattr(p, name) for name, _ in ub_tile_plan_t._fields_}
 
 
 def ub_register_scratch(h, buf, nbytes):

@@ -490,6 +490,10 @@ typedef struct {
                                         summed in the kernel (1) or by a second launch (2);
                                         0: one workgroup per tile */
   int32_t seg_tile_m, seg_tile_n;    /* tile of the segmented rows' launch */
+  int32_t dispatches;                /* GEMM kernels the last call launched, every launch
+                                        group counted (reductions not counted) */
+  int32_t rs_pieces;                 /* row pieces of a pipelined device-side
+                                        reduce-scatter (0: not pipelined) */
 } ub_tile_plan_t;
 
 /* Split-K scratch of a handle (optional; all-gather side).  When a call's shape leaves the
@@ -534,6 +538,11 @@ UB_API ub_status_t ub_register_scratch(ub_handle_t h, void* buf, size_t bytes);
  *                          segments (clamped to the number of 32-deep k-steps).
  *   "seg_tile_m", "seg_tile_n"  tile of forced split pieces (default 256 x 256; any of the
  *                          bf16 tiles).
+ *   "rs_pieces"            device-side reduce-scatter (atomic_gemm, fuse_reduce 0) in P row
+ *                          pieces: piece p's slice GEMMs on the caller's stream, its
+ *                          reduction on a worker stream overlapping piece p + 1's GEMMs;
+ *                          0 (default) the library's choice, 1..8 forced.  The results do
+ *                          not change.
  *   "seg_reduce"           sum of forced split pieces: 1 the tile's last piece sums in the
  *                          kernel (per-tile counters in the scratch); 2 (default) a second
  *                          launch sums every tile over the whole chip.

@@ -81,9 +81,9 @@ int main() {
   // debug settings
   CHECK(ub_debug_set(h, "nope", 1) == UB_ERR_INVALID_ARG);
   CHECK(ub_debug_set(h, nullptr, 1) == UB_ERR_INVALID_ARG);
-  CHECK(ub_debug_set(h, "tile_m", 192) == UB_OK && ub_debug_set(h, "tile_n", 256) == UB_OK);
+  CHECK(ub_debug_set(h, "tile_m", 192) == UB_OK && ub_debug_set(h, "tile_n", 128) == UB_OK);
   CHECK(ub_gemm_ag_chunked(h, fake(), 384, 384, fake(), 384, &cfg, nullptr) == UB_ERR_INVALID_ARG);
-  CHECK(std::strstr(ub_last_error(h), "192x256") != nullptr);
+  CHECK(std::strstr(ub_last_error(h), "192x128") != nullptr);
   CHECK(ub_debug_set(h, "tile_m", 0) == UB_OK && ub_debug_set(h, "tile_n", 0) == UB_OK);
   ub_tile_plan_t plan;
   CHECK(ub_debug_last_plan(h, &plan) == UB_OK && plan.cut_row == -1);

@@ -320,9 +320,9 @@ def test_debug_settings_checked_before_any_hip_call():
             assert e.value.name == "UB_ERR_INVALID_ARG"
         cfg = ub.make_cfg("ring_exchange", 2)
         ub.ub_debug_set(h, "tile_m", 192)
-        ub.ub_debug_set(h, "tile_n", 256)
+        ub.ub_debug_set(h, "tile_n", 128)
         st = ub.raw_call("ub_gemm_ag_chunked", h, FAKE, 384, 384, FAKE, 384, ctypes.byref(cfg), None)
-        assert ub.STATUS[st] == "UB_ERR_INVALID_ARG" and "192x256" in ub.ub_last_error(h)
+        assert ub.STATUS[st] == "UB_ERR_INVALID_ARG" and "192x128" in ub.ub_last_error(h)
         st = ub.raw_call("ub_gemm_rs_chunked", h, FAKE, 256, 256, FAKE, 256, FAKE, 256,
                          ctypes.byref(cfg), None)
         assert ub.STATUS[st] == "UB_ERR_INVALID_ARG"

@@ -414,3 +414,92 @@ def test_slice_width_not_multiple_of_k_step(ub, ks, fuse):
         assert reg.counters_clean()
     finally:
         reg.close()
+
+
+# ---- pipelined device-side reduce-scatter (rs_pieces) ------------------------------------
+
+def _rs_piece_count(T, P):
+    """Pieces the library cuts T rows into for P requested: cuts on multiples of 1280 rows
+    nearest to p T / P, strictly increasing and inside (0, T)."""
+    cuts = [0]
+    for p in range(1, P):
+        c = (T * p // P + 640) // 1280 * 1280
+        if cuts[-1] < c < T:
+            cuts.append(c)
+    return len(cuts)
+
+
+@pytest.mark.parametrize("ring", (False, True))
+def test_pipelined_device_loop_pieces_bit_identical(ub, ring):
+    """The device-side loop in 1..8 row pieces (each piece's reduction on a worker stream,
+    overlapping the next piece's GEMMs): output bit-identical to one launch + one
+    reduction and to the host loop; integer inputs equal the oracle bit for bit; plan
+    record counts the pieces and the GEMM dispatches."""
+    rng = np.random.default_rng(61 + ring)
+    cap, H, K, tp = 8192, 512, 2048, 8
+    for T, ints in ((7680, True), (6136, False)):
+        a = (wl.integer_bits if ints else wl.normal_bits)(rng, (T, K))
+        wt = wl.integer_bits(rng, (K, H)) if ints else wl.normal_bits(rng, (K, H), 0.02)
+        a_t, w_t = gu.dev(a), gu.dev(wt)
+        reg = gu.Registration(ub, cap, H, tp, pad_rows=8)
+        try:
+            reg.set_T(T)
+            order = "ring" if ring else "ascending"
+            base = ub.make_cfg("pipeline", 4, atomic_gemm=True, reduce_order=order)
+            ub.ub_debug_set(reg.h, "rs_pieces", 1)
+            ref = _run_rs(ub, reg, a_t, K, w_t, base)
+            assert ub.ub_debug_plan(reg.h)["rs_pieces"] == 0
+            if ints:
+                o, _ = _oracle_rs(cap, H, tp, a, wt, op.OverlapCfg(method="pipeline", num_splits=4,
+                                                                   reduce_order=order))
+                assert np.array_equal(ref[:T], o)
+            for pieces in (2, 3, 4, 8):
+                print(f"[rs pieces] T={T} ring={ring} pieces={pieces}", flush=True)
+                ub.ub_debug_set(reg.h, "rs_pieces", pieces)
+                got = _run_rs(ub, reg, a_t, K, w_t, base)
+                assert np.array_equal(got, ref), pieces
+                plan = ub.ub_debug_plan(reg.h)
+                assert plan["rs_pieces"] == _rs_piece_count(T, pieces), plan
+                assert plan["dispatches"] >= plan["rs_pieces"]
+            ub.ub_debug_set(reg.h, "rs_pieces", 0)
+            host = _run_rs(ub, reg, a_t, K, w_t, ub.make_cfg("pipeline", 4, reduce_order=order))
+            assert np.array_equal(host, ref)
+            assert reg.counters_clean()
+        finally:
+            reg.close()
+
+
+def test_pipelined_fc2_full_size_sampled(ub):
+    """fc2 (capacity 16384, hidden 4096, K 14336 in 8 slices) in the device-side loop with
+    4 row pieces at T = 16384 and 12280: bit-identical to the unpipelined call, sampled
+    rows against the oracle."""
+    w = wl.fc2()
+    ra, rw, _ = w.seeds()
+    a_all = wl.activations(w, w.capacity, ra)
+    wt = wl.weights(w, rw)
+    a_t, w_t = gu.dev(a_all), gu.dev(wt)
+    H, tp = w.hidden, w.tp
+    reg = gu.Registration(ub, w.capacity, H, tp, pad_rows=8)
+    rng = np.random.default_rng(17)
+    cfg = ub.make_cfg(w.method, w.num_splits, w.num_max_streams, atomic_gemm=True)
+    try:
+        out = gu.canary((w.capacity + 8, H))
+        for T in (16384, 12280):
+            print(f"[fc2 pieces] T={T}", flush=True)
+            reg.set_T(T)
+            outs = []
+            for pieces in (1, 4):
+                ub.ub_debug_set(reg.h, "rs_pieces", pieces)
+                out.fill_(gu.CANARY)
+                ub.ub_gemm_rs_chunked(reg.h, a_t, w.k, w.k, w_t, H, out, H, cfg)
+                torch.cuda.synchronize()
+                outs.append(gu.host(out))
+            assert np.array_equal(outs[0], outs[1])
+            rows = np.array(sorted(set(rng.integers(0, T, size=24).tolist()) |
+                                   {0, T - 1, 3839, 3840, 7679, 7680, 11519, 11520} - {r for r in range(T, 16384)}))
+            ref, _ = og.rs_rows(a_all[rows], wt, tp)
+            gu.check_rs_close(outs[1][rows], ref, a_all[rows], wt, tp, f"fc2 pieces T={T}")
+            assert np.all(outs[1][T:] == gu.CANARY)
+    finally:
+        ub.ub_debug_set(reg.h, "rs_pieces", 0)
+        reg.close()
