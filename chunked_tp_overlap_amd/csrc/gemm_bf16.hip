@@ -617,9 +617,22 @@ __global__ __launch_bounds__(256) void gemm_bf16_split_reduce(Params p) {
   int m0, m_end, tn;
   if (!tile_of(p, tile, C::BM, m0, m_end, tn)) return;
   const float* src = p.parts + (int64_t)tile * p.nseg * TILE + q * 4;
-  f32x4 sum = __builtin_nontemporal_load(GLOBAL_PTR(const f32x4, src));
-  for (int sg = 1; sg < p.nseg; ++sg)
-    sum = sum + __builtin_nontemporal_load(GLOBAL_PTR(const f32x4, src + (int64_t)sg * TILE));
+  // four partials' loads in flight (past the last segment the last is read again, an L2
+  // hit that no add uses), then their adds in segment order
+  const int ns = p.nseg;
+  f32x4 sum = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s0 = 0; s0 < ns; s0 += 4) {
+    f32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = __builtin_nontemporal_load(
+          GLOBAL_PTR(const f32x4, src + (int64_t)min(s0 + i, ns - 1) * TILE));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 t = s0 + i == 0 ? v[i] : sum + v[i];
+      if (s0 + i < ns) sum = t;
+    }
+  }
   const int t = q % C::THREADS, ij = q / C::THREADS;
   const int i = ij / C::FN, j = ij % C::FN;
   const int wave = t >> 6, lane = t & 63;
