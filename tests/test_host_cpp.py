@@ -59,6 +59,19 @@ def test_tile_of(tmp_path):
 
 
 @pytest.mark.skipif(_cxx() is None, reason="clang++ not available")
+def test_segmentation_choice(tmp_path):
+    """choose_segmentation over the workloads' shapes and random ones: deterministic, from
+    the priced segment counts, inside the row range on 64-row boundaries, on a built tile,
+    within the 64 MiB of partials the scratch sizing promises; none for batched launches."""
+    out = _build_and_run(tmp_path, "segmentation_check",
+                         [os.path.join(CPP, "segmentation_check.cpp"), os.path.join(CSRC, "gemm_bf16.hip"),
+                          os.path.join(CSRC, "ub_plan.cpp")],
+                         libs=("-lamdhip64",), hip=True, timeout=600)
+    checks, segmented = map(int, out.split()[1:3])
+    assert checks == 6000 and segmented > 100
+
+
+@pytest.mark.skipif(_cxx() is None, reason="clang++ not available")
 def test_abi_argument_paths_under_sanitizers(tmp_path):
     """The C ABI's argument checks, state handling and messages, and a randomized sweep of
     arguments through every entry point, with no sanitizer report (the device launchers
