@@ -894,7 +894,7 @@ hipError_t launch(K kernel, const GemmArgs& g, const GemmUnits& units, hipStream
   }
   p.unit_tile0[u.n] = (int32_t)tiles;
   if (tiles == 0) return hipSuccess;
-  p.group = tile_group(tiles, C::NW == 8 ? 1 : 2, g.dbg ? g.dbg->tile_group : 0);
+  p.group = tile_group(tiles, p.tiles_n, C::NW == 8 ? 1 : 2, g.dbg ? g.dbg->tile_group : 0);
   p.ready = g.ready;
   p.timeouts = g.timeouts;
   p.wait_ticks = g.wait_ticks ? g.wait_ticks : kReadyTimeoutTicks;

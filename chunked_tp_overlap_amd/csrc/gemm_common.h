@@ -82,12 +82,15 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
 //
 // Group size: a launch whose tiles all run at once (no more tiles than workgroup slots)
 // gains nothing from column groups and lists its tiles row by row (group 1), which keeps
-// each XCD's block on the fewest A rows; larger launches use groups of 4 (measured on
-// MI355X: qkv shapes ~1-2% faster with 1, 8192^3 and 16384 x 3584 x 4096 3-5% faster with 4).
-// forced > 0 (a handle's debug setting) overrides the choice.
-inline int tile_group(int64_t tiles, int per_cu, int forced) {
+// each XCD's block on the fewest A rows; so does a launch with few tile columns (at most
+// 8); other larger launches use groups of 4.  Measured on MI355X, interleaved per point:
+// the GQA shape (5 tile columns) at T = 23376 ... 32520 runs 2-4% faster with 1 than with
+// 4; qkv shapes ~1-2% faster with 1; fc2's batched slices (16 columns) 3-10% and 8192^3 and
+// 16384 x 3584 x 4096 3-5% faster with 4.  forced > 0 (a handle's debug setting) overrides
+// the choice.
+inline int tile_group(int64_t tiles, int tiles_n, int per_cu, int forced) {
   if (forced >= 1) return forced;
-  return tiles <= 256 * (int64_t)per_cu ? 1 : 4;
+  return tiles <= 256 * (int64_t)per_cu || tiles_n <= 8 ? 1 : 4;
 }
 
 // Sets a kernel's dynamic-LDS limit on the current device, once per (device, kernel):

@@ -283,7 +283,7 @@ hipError_t launch(const GemmF8Args& g, const GemmUnits& units, hipStream_t strea
   }
   p.unit_tile0[u.n] = (int32_t)tiles;
   if (tiles == 0) return hipSuccess;
-  p.group = tile_group(tiles, 1, g.dbg ? g.dbg->tile_group : 0);
+  p.group = tile_group(tiles, p.tiles_n, 1, g.dbg ? g.dbg->tile_group : 0);
   const int64_t grid = tiles;
   if (grid > 0x7FFFFFFF || g.batch < 1 || g.batch > 65535) return hipErrorInvalidValue;
   auto kernel = &gemm_fp8_pingpong<C, F8_D>;
