@@ -290,7 +290,7 @@ struct Tile {
     a_rd_x = a_swz<C::A_CPR>(lane & 15);
     b_krow = (lane >> 4) * 8 + ((lane >> 2) & 3);
     b_col_chunk = (wn * C::WN + (lane & 3) * 4) >> 3;
-    b_x = b_swz((lane >> 2) & 3);
+    b_x = b_swz(b_krow);  // bits 0, 1 and 3 of the k-row; the second read's +4 leaves them
     b_in = (lane & 1) * 8;
 
     return true;

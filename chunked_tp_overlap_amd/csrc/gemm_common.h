@@ -31,7 +31,9 @@ template <int CPR>
 __device__ constexpr int a_swz(int R) {
   return CPR == 8 ? ((R ^ (R >> 1)) & 7) : (((R >> 1) ^ (R >> 2)) & 3);
 }
-__device__ constexpr int b_swz(int r) { return (2 * (r & 3)) ^ (4 * (r & 3)); }
+// B: k-rows r and r + 8 (read by the two 16-lane halves of one 32-lane LDS cycle of the
+// transposing reads) get column-chunk sets that differ by XOR 2, disjoint banks.
+__device__ constexpr int b_swz(int r) { return ((2 * (r & 3)) ^ (4 * (r & 3))) ^ (((r >> 3) & 1) << 1); }
 
 // Raw buffer resource (base, num_records bytes) in scalar registers.
 __device__ inline i32x4 make_rsrc(const void* base, uint32_t num_records) {
