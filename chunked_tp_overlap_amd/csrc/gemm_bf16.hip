@@ -169,9 +169,13 @@ __device__ inline u32x4 pack8(const float (&acc)[8]) {
                pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
 }
 
-template <int BM_, int BN_, int BK_, int S_, int WGM_, int WGN_>
+// BNL: columns of a B k-row in LDS.  A tile narrower than 256 columns (BN 192 or 160) keeps
+// the 256-column row, so that the direct loads still cover whole rows and the B swizzle
+// stays a permutation of the row; its loads of chunks past BN are out of range (zeros in
+// LDS, no memory access) and no read uses them.
+template <int BM_, int BN_, int BK_, int S_, int WGM_, int WGN_, int BNL_ = BN_>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, BNL = BNL_;
   static constexpr int WGM = WGM_, WGN = WGN_;      // wave grid
   static constexpr int NW = WGM * WGN;              // waves per workgroup
   static constexpr int THREADS = 64 * NW;
@@ -183,8 +187,8 @@ struct Cfg {
   static constexpr int A_ROW = BK * 2;              // bytes per A row in a stage
   static constexpr int A_CPR = BK / 8;              // 16-byte chunks per A row
   static constexpr int A_BYTES = BM * A_ROW;
-  static constexpr int B_ROW = BN * 2;              // bytes per B k-row
-  static constexpr int B_CPR = BN / 8;
+  static constexpr int B_ROW = BNL * 2;             // bytes per B k-row in LDS
+  static constexpr int B_CPR = BNL / 8;
   static constexpr int B_BYTES = BK * B_ROW;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int NA_ALL = A_BYTES / 1024;     // 1 KB direct loads per step, A
@@ -210,6 +214,7 @@ struct Cfg {
   static_assert(WM % 16 == 0 && WN % 16 == 0 && BK % 32 == 0, "whole 16x16x32 blocks");
   static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "whole 1 KB loads");
   static_assert(1024 % A_ROW == 0 && 1024 % B_ROW == 0, "a load covers whole rows");
+  static_assert(BN <= BNL && BN % 16 == 0, "the tile's columns within the LDS row");
   static_assert(S * LMAX <= 63, "vmcnt is a 6-bit count");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS is 160 KiB per CU");
 };
@@ -276,7 +281,8 @@ struct Tile {
         const int krow = C::B_ROWS_PER_LOAD * idx + lane / C::B_CPR;
         const int chunk = (lane % C::B_CPR) ^ b_swz(krow);
         lds_off[j] = (uint32_t)(C::A_BYTES + idx * 1024);
-        off[j] = n0 + chunk * 8 < p.n ? (uint32_t)((krow * p.ldb + chunk * 8) * 2) : OOB;
+        off[j] = chunk * 8 < C::BN && n0 + chunk * 8 < p.n
+                     ? (uint32_t)((krow * p.ldb + chunk * 8) * 2) : OOB;
       }
       if (j >= nl) off[j] = OOB;
     }
@@ -941,6 +947,8 @@ hipError_t launch(K kernel, const GemmArgs& g, const GemmUnits& units, hipStream
 using PP320x256 = Cfg<320, 256, 32, 4, 2, 4>;   // 8 waves of 160x64
 using PP256x256 = Cfg<256, 256, 32, 4, 2, 4>;   // 8 waves of 128x64
 using PP128x256 = Cfg<128, 256, 32, 4, 2, 4>;   // 8 waves of 64x64
+using PP256x192 = Cfg<256, 192, 32, 4, 4, 2, 256>;  // 8 waves of 64x96 (B rows 256 wide in LDS)
+using PP256x160 = Cfg<256, 160, 32, 4, 4, 2, 256>;  // 8 waves of 64x80
 using PL128x128 = Cfg<128, 128, 32, 4, 2, 2>;   // 4 waves of 64x64, 2 workgroups per CU
 constexpr int PP_D = 3;
 
@@ -958,7 +966,13 @@ constexpr int PP_D = 3;
 // over the workloads' own shapes (GQA 1280 x 8192 at 33 T, qkv 1536 x 4096, fc1 3584 x
 // 4096, fc2 4096 x 1792 in 8 slices; device-side loop and host loop; 78 points, including
 // forced cuts): the model's plan is within 2% of the best measured plan at 67 of them, at
-// 0.989 of the best on average.
+// 0.989 of the best on average.  The narrow tiles 256x192 and 256x160 (eight and ten
+// column tiles on N = 1536, eight on N = 1280) fill one round where 256x256 leaves a third
+// of the CUs idle; their speeds, 0.80 and 0.76, are the same ratio fitted to forced
+// one-round launches of the three shapes at 21 T against 256x256 (within 4% at each).
+// A one-round launch's time barely follows the tile's area (a 128x256 or 256x160 tile
+// takes 0.78 or 0.92 of a 256x256 tile's time): the narrow tiles pay only where they fill
+// CUs that a wider tile leaves idle.
 //
 // Besides one tile shape for the whole launch, the model prices cuts: a launch that has the
 // chip to itself runs the leading row bands that fill whole rounds of a large tile, then
@@ -967,11 +981,14 @@ constexpr int PP_D = 3;
 // instruction sequence: the results do not change.  With several streams (the host loop)
 // the other streams' launches fill the idle CUs, and no cut is taken.
 struct TileOpt { int kind, bm, bn, per_cu; double speed, speed_alone; };
-enum TileKind { kTile128x128 = 0, kTile128x256 = 1, kTile256x256 = 2, kTile320x256 = 3 };
+enum TileKind { kTile128x128 = 0, kTile128x256 = 1, kTile256x256 = 2, kTile320x256 = 3,
+                kTile256x192 = 4, kTile256x160 = 5 };
 const TileOpt kTileOpts[] = {{kTile320x256, 320, 256, 1, 1.030, 1.030},
                              {kTile256x256, 256, 256, 1, 1.000, 1.000},
                              {kTile128x256, 128, 256, 1, 0.749, 0.749},
-                             {kTile128x128, 128, 128, 2, 0.373, 0.493}};
+                             {kTile128x128, 128, 128, 2, 0.373, 0.493},
+                             {kTile256x192, 256, 192, 1, 0.800, 0.800},
+                             {kTile256x160, 256, 160, 1, 0.760, 0.760}};
 constexpr double kBoostMax = 1.476, kBoostExp = 0.2245;
 
 const TileOpt* find_tile(int bm, int bn) {
@@ -1093,6 +1110,10 @@ hipError_t launch_split_r(int kind, const GemmArgs& g, const GemmUnits& u, hipSt
       return launch<PP256x256>(&gemm_bf16_pingpong<PP256x256, PP_D, R>, g, u, stream, mode, nseg);
     case kTile128x256:
       return launch<PP128x256>(&gemm_bf16_pingpong<PP128x256, PP_D, R>, g, u, stream, mode, nseg);
+    case kTile256x192:
+      return launch<PP256x192>(&gemm_bf16_pingpong<PP256x192, PP_D, R>, g, u, stream, mode, nseg);
+    case kTile256x160:
+      return launch<PP256x160>(&gemm_bf16_pingpong<PP256x160, PP_D, R>, g, u, stream, mode, nseg);
     default:
       return launch<PL128x128>(&gemm_bf16_seg<PL128x128, R>, g, u, stream, mode, nseg);
   }
@@ -1113,6 +1134,10 @@ hipError_t launch_kind(int kind, const GemmArgs& g, const GemmUnits& u, hipStrea
       return launch<PP256x256>(&gemm_bf16_pingpong<PP256x256, PP_D>, g, u, stream);
     case kTile128x256:
       return launch<PP128x256>(&gemm_bf16_pingpong<PP128x256, PP_D>, g, u, stream);
+    case kTile256x192:
+      return launch<PP256x192>(&gemm_bf16_pingpong<PP256x192, PP_D>, g, u, stream);
+    case kTile256x160:
+      return launch<PP256x160>(&gemm_bf16_pingpong<PP256x160, PP_D>, g, u, stream);
     default:
       return launch<PL128x128>(&gemm_bf16_pipelined<PL128x128>, g, u, stream);
   }

@@ -27,7 +27,7 @@ def force_tile(ub, h, tile):
     ub.ub_debug_set(h, "tile_n", n)
 
 
-BF16_TILES = ("320x256", "256x256", "128x256", "128x128")
+BF16_TILES = ("320x256", "256x256", "128x256", "128x128", "256x192", "256x160")
 
 
 def canary(shape):

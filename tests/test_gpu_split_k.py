@@ -93,11 +93,15 @@ def test_integer_inputs_bit_exact(ub, H, nseg, seg_row):
                     assert np.array_equal(c[:T], ref), (reduce, tile, kw)
                     assert np.all(c[T:cap] == gu.CANARY)
                 assert _counters_zero(ub, scr)
-                # the device-side loop ran split on that tile, with the clamped segment count
+                # the device-side loop ran split on that tile, with the clamped segment
+                # count, or the folding kernel when the tile's partials exceed the scratch
                 _run(ub, reg, w_t, N, ub.make_cfg(**SCHEDULES[0]))
                 plan = ub.ub_debug_last_plan(reg.h, seg=True)
-                assert plan[5:] == (seg_row, min(nseg, (H + 31) // 32), reduce,
-                                    *map(int, tile.split("x"))), plan
+                ns = min(nseg, (H + 31) // 32)
+                bm, bn = map(int, tile.split("x"))
+                parts = -(-(T - seg_row) // bm) * -(-N // bn) * ns * bm * bn * 4
+                want = (seg_row, ns, reduce, bm, bn) if parts <= 64 * MiB else (seg_row, ns, 0, 128, 128)
+                assert plan[5:] == want, plan
         ub.ub_register_scratch(reg.h, None, 0)  # the folding kernel
         for kw in SCHEDULES:
             c = _run(ub, reg, w_t, N, ub.make_cfg(**kw))
