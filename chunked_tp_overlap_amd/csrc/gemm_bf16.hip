@@ -1018,6 +1018,16 @@ GemmUnits clip_units(const GemmUnits& u, int64_t lo, int64_t hi) {
   return out;
 }
 
+// At short K the 320x256 tile gains on the others: its launch has a fifth fewer tiles, and
+// each tile's fixed part (the loads before the first MFMA, the epilogue) weighs more.  Forced
+// launches of the fc2 slices (K = 1792) give it 1.10 against 256x256 (the right choice at
+// all six T from 2048 to 16384); K >= 4096 keeps the fitted 1.03.  Linear in between.
+double short_k_gain(const TileOpt& o, int64_t k) {
+  if (o.kind != kTile320x256 || k >= 4096) return 1.0;
+  const double f = k <= 1792 ? 1.0 : (4096.0 - (double)k) / (4096.0 - 1792.0);
+  return 1.0 + f * (1.10 / 1.03 - 1.0);
+}
+
 // Predicted time (in units of one 256x256 tile's k-work at full occupancy) of one launch of
 // `row_tiles_` row tiles of `o` on `share` CUs.
 // With nseg > 1, each tile is nseg split-K pieces of 1/nseg of its k-work.
@@ -1033,7 +1043,7 @@ double tile_cost(const TileOpt& o, int64_t row_tiles_, const GemmArgs& g, int sh
     const int64_t busy_cus = alone ? now : cus;
     const double busy = std::min(256.0, (double)busy_cus * 256.0 / (double)cus);
     const double boost = std::min(kBoostMax, std::pow(256.0 / busy, kBoostExp));
-    t += area / ((alone ? o.speed_alone : o.speed) * boost);
+    t += area / ((alone ? o.speed_alone : o.speed) * short_k_gain(o, g.k) * boost);
     left -= now;
   }
   return t;
