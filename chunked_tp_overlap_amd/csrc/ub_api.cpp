@@ -54,8 +54,9 @@ struct ub_ctx {
   int n_streams_created = 1;
   hipEvent_t ev_fork = nullptr;
   hipEvent_t ev_join[UB_MAX_STREAMS] = {};
-  // kernel timing
-  bool timing = false;
+  // kernel timing: 0 off, 1 an event pair per launch, 2 chained (a launch starts at the
+  // end event of the previous timed launch on its stream)
+  int32_t timing = 0;
   struct TimedLaunch {
     hipEvent_t start, stop;
     int kind;  // 0 gemm, 1 reduce
@@ -63,6 +64,7 @@ struct ub_ctx {
   };
   std::vector<hipEvent_t> free_events;
   std::vector<TimedLaunch> pending;
+  std::vector<std::pair<hipStream_t, hipEvent_t>> chain;  // last end event per stream (mode 2)
   ub_kernel_stats_t stats[2] = {};
   // arrival stand-in: copy stream, one arrival event per chunk, its join event
   hipStream_t copy_stream = nullptr;
@@ -260,6 +262,15 @@ void release_ready_slot(ub_ctx* h) {
 }
 
 // ---- per-launch timing ----------------------------------------------------------------
+bool in_chain(const ub_ctx* h, hipEvent_t ev) {
+  for (const auto& c : h->chain)
+    if (c.second == ev) return true;
+  return false;
+}
+
+// Waits for every pending timed launch and adds it to the stats.  Its events go back to
+// the pool, except the chain's current end events, which later launches start from (a
+// chained launch's start event is the previous launch's stop event: each is freed once).
 ub_status_t harvest(ub_ctx* h) {
   for (auto& t : h->pending) {
     hipError_t e = hipEventSynchronize(t.stop);
@@ -272,11 +283,31 @@ ub_status_t harvest(ub_ctx* h) {
     s.total_ms += ms;
     s.flops += t.flops;
     s.bytes += t.bytes;
-    h->free_events.push_back(t.start);
-    h->free_events.push_back(t.stop);
   }
+  std::vector<hipEvent_t> done;
+  for (auto& t : h->pending) {
+    done.push_back(t.start);
+    done.push_back(t.stop);
+  }
+  std::sort(done.begin(), done.end());
+  done.erase(std::unique(done.begin(), done.end()), done.end());
+  for (hipEvent_t ev : done)
+    if (!in_chain(h, ev)) h->free_events.push_back(ev);
   h->pending.clear();
   return UB_OK;
+}
+
+// Ends every chain: the next timed launch on each stream records a start event of its own.
+// A chain head that no pending launch holds goes back to the pool now; the others go back
+// when harvest takes their launch.
+void clear_chain(ub_ctx* h) {
+  std::vector<std::pair<hipStream_t, hipEvent_t>> heads;
+  heads.swap(h->chain);
+  for (const auto& c : heads) {
+    bool held = false;
+    for (const auto& t : h->pending) held = held || t.start == c.second || t.stop == c.second;
+    if (!held) h->free_events.push_back(c.second);
+  }
 }
 
 hipEvent_t take_event(ub_ctx* h) {
@@ -303,13 +334,25 @@ ub_status_t timed_launch(ub_ctx* h, hipStream_t s, int kind, double flops, doubl
     ub_status_t st = harvest(h);  // oldest launches finished long ago: no real stall
     if (st != UB_OK) return st;
   }
-  hipEvent_t a = take_event(h), b = take_event(h);
+  hipEvent_t a = nullptr;
+  size_t link = h->chain.size();
+  if (h->timing == 2)
+    for (size_t i = 0; i < h->chain.size(); ++i)
+      if (h->chain[i].first == s) link = i;
+  if (link < h->chain.size()) a = h->chain[link].second;
+  const bool own_a = a == nullptr;
+  if (own_a) a = take_event(h);
+  hipEvent_t b = take_event(h);
   if (!a || !b) return fail(h, UB_ERR_HIP, "hipEventCreate failed for kernel timing");
-  hipError_t e = hipEventRecord(a, s);
+  hipError_t e = own_a ? hipEventRecord(a, s) : hipSuccess;
   if (e == hipSuccess) e = launch();
   if (e == hipSuccess) e = hipEventRecord(b, s);
   if (e != hipSuccess) return hip_fail(h, e, what);
   h->pending.push_back({a, b, kind, flops, bytes});
+  if (h->timing == 2) {
+    if (link < h->chain.size()) h->chain[link].second = b;
+    else h->chain.push_back({s, b});
+  }
   return UB_OK;
 }
 
@@ -1380,7 +1423,11 @@ UB_API ub_status_t ub_reduce_partials(ub_handle_t h, void* out, int64_t ldo,
 
 UB_API ub_status_t ub_set_kernel_timing(ub_handle_t h, int32_t enable) {
   if (!h) return UB_ERR_NOT_INITIALIZED;
-  h->timing = enable != 0;
+  if (enable < 0 || enable > 2)
+    return fail(h, UB_ERR_INVALID_ARG, "enable=%d must be 0 (off), 1 (per launch) or 2 (chained)",
+                enable);
+  clear_chain(h);
+  h->timing = enable;
   return UB_OK;
 }
 
@@ -1389,6 +1436,7 @@ UB_API ub_status_t ub_get_kernel_timing(ub_handle_t h, ub_kernel_stats_t* gemm,
   if (!h) return UB_ERR_NOT_INITIALIZED;
   ub_status_t st = harvest(h);
   if (st != UB_OK) return st;
+  clear_chain(h);
   if (gemm) *gemm = h->stats[0];
   if (reduce) *reduce = h->stats[1];
   h->stats[0] = ub_kernel_stats_t{};
@@ -1525,6 +1573,7 @@ UB_API ub_status_t ub_destroy(ub_handle_t h) {
     (void)hipGetDevice(&cur);
     if (cur != h->device) (void)hipSetDevice(h->device);
     harvest(h);
+    clear_chain(h);
     for (int i = 1; i < h->n_streams_created; ++i) {
       (void)hipStreamSynchronize(h->streams[i]);
       (void)hipStreamDestroy(h->streams[i]);

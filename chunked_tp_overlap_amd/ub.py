@@ -321,7 +321,8 @@ def ub_reduce_partials(h, out, ldo, reduce_order="ascending", stream=None):
 
 
 def ub_set_kernel_timing(h, enable):
-    _check(_lib.ub_set_kernel_timing(h, int(bool(enable))), h)
+    """enable: False/0 off, True/1 an event pair per launch, 2 chained (one event per launch)."""
+    _check(_lib.ub_set_kernel_timing(h, int(enable)), h)
 
 
 def ub_get_kernel_timing(h):

@@ -460,11 +460,17 @@ UB_API ub_status_t ub_quantize_e4m3(const void* src, int64_t lds, void* dst, int
 UB_API ub_status_t ub_reduce_partials(ub_handle_t h, void* out, int64_t ldo,
                                       int32_t reduce_order, ub_stream_t stream);
 
-/* Per-launch kernel timing.  While enabled, every GEMM and reduction launch is bracketed
- * by HIP events recorded on the stream it is launched on; ub_get_kernel_timing waits for
- * them and returns the accumulated durations with the algorithmic FLOPs and bytes of the
- * measured launches, then clears the counters.  Disabled by default; enabling it adds two
- * event records per launch. */
+/* Per-launch kernel timing.  enable 1: every GEMM and reduction launch is bracketed by HIP
+ * events recorded on the stream it is launched on (two event records per launch).
+ * enable 2, chained: a launch's start is the end event of the previous launch timed on
+ * the same stream since the last ub_get_kernel_timing or ub_set_kernel_timing, so one
+ * record per launch (each record costs a few microseconds of GPU time); the caller
+ * promises that nothing else runs on that stream between the calls it measures, or that
+ * work counts as the next launch's time (back-to-back calls on one stream; not the host
+ * loop's worker streams, whose launches wait for the caller's).  enable 0 (the default):
+ * off.  ub_get_kernel_timing waits for the measured launches and returns the accumulated
+ * durations with their algorithmic FLOPs and bytes, then clears the counters and ends the
+ * chains.  Other values of enable -> UB_ERR_INVALID_ARG. */
 UB_API ub_status_t ub_set_kernel_timing(ub_handle_t h, int32_t enable);
 UB_API ub_status_t ub_get_kernel_timing(ub_handle_t h, ub_kernel_stats_t* gemm,
                                         ub_kernel_stats_t* reduce);

@@ -333,6 +333,21 @@ def test_debug_settings_checked_before_any_hip_call():
         ub.ub_destroy(h)
 
 
+def test_kernel_timing_modes_checked_before_any_hip_call():
+    """ub_set_kernel_timing takes 0 (off), 1 (an event pair per launch) or 2 (chained);
+    anything else is rejected and leaves the mode as it was."""
+    h = _handle(512, 256, 2)
+    try:
+        for mode in (0, 1, 2, 0):
+            ub.ub_set_kernel_timing(h, mode)
+        for bad in (3, -1, 100):
+            with pytest.raises(ub.UBError) as e:
+                ub.ub_set_kernel_timing(h, bad)
+            assert e.value.name == "UB_ERR_INVALID_ARG" and "chained" in ub.ub_last_error(h)
+    finally:
+        ub.ub_destroy(h)
+
+
 def test_atomic_gemm_unit_limit_checked_before_any_hip_call():
     h = _handle(1024, 256, 1)
     try:

@@ -5,6 +5,8 @@ and across every scheduling knob, capacity and buffer offset; sampled rows at th
 sizes of the QKV, fc1 and GQA-bulk workloads in the launch configuration the bench uses.
 """
 
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -336,6 +338,44 @@ def test_kernel_timing_counts_launches(ub):
         assert g["total_ms"] > 0
         g2, _ = ub.ub_get_kernel_timing(reg.h)
         assert g2["launches"] == 0  # counters cleared by the read
+    finally:
+        reg.close()
+
+
+def test_chained_kernel_timing(ub):
+    """Chained timing (one event record per launch): back-to-back device-side-loop calls on
+    one stream count every launch, and their durations add up to the span between the
+    first call's start and the last call's end, which an outer event pair on the same stream
+    brackets.  Reading the counters ends the chain: a host-side pause before the next
+    batch is not counted as that batch's time."""
+    H, N, T = 2048, 1280, 4096
+    rng = np.random.default_rng(5)
+    reg = gu.Registration(ub, 4096, H, 8, workspace=False)
+    try:
+        reg.set_T(T)
+        reg.fill(wl.normal_bits(rng, (T, H)))
+        wt = gu.dev(wl.normal_bits(rng, (H, N), 0.02))
+        cfg = ub.make_cfg("bulk", 8, atomic_gemm=True)
+        stream = torch.cuda.current_stream()
+        c = gu.canary((4096, N))
+        _run(ub, reg, wt, N, cfg)  # warm
+        ub.ub_set_kernel_timing(reg.h, 2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(6):
+            ub.ub_gemm_ag_chunked(reg.h, wt, N, N, c, N, cfg, stream)
+        e1.record(stream)
+        g, _ = ub.ub_get_kernel_timing(reg.h)
+        outer = e0.elapsed_time(e1)
+        assert g["launches"] == 6 and g["flops"] == pytest.approx(6 * 2.0 * T * H * N)
+        assert 0 < g["total_ms"] <= outer * 1.01 + 0.005 and g["total_ms"] >= 0.8 * outer, (g, outer)
+        time.sleep(0.05)  # the GPU idles; the next batch starts a new chain
+        for _ in range(2):
+            ub.ub_gemm_ag_chunked(reg.h, wt, N, N, c, N, cfg, stream)
+        g2, _ = ub.ub_get_kernel_timing(reg.h)
+        assert g2["launches"] == 2 and g2["total_ms"] < 0.5 * g["total_ms"] + 5.0, (g, g2)
+        assert g2["total_ms"] < 40.0
+        ub.ub_set_kernel_timing(reg.h, 0)
     finally:
         reg.close()
 
