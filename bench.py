@@ -321,7 +321,7 @@ def main():
     }
     per_pt = g.per_point(primary)
     result["per_point"] = {"columns": ["T", "tflops_median", "tflops_best", "plan"],
-                           "note": "each point: 5 warm-up calls, 20 calls timed one by one (HIP events); "
+                           "note": "each point: 5 warm-up calls, 20 calls back to back, each timed between HIP events (one event per call); "
                                    "plan = tile_m x tile_n [cut row: tail tile] [split-K from row r: "
                                    "nseg segments on tile, summed in the kernel (r1) or by a second "
                                    "launch (r2)]",
@@ -401,17 +401,19 @@ def calibration_copy(torch, dev):
 
 
 def _call_stats(fn, torch, stream, reps=20, warmup=5):
-    """Per-call times (ms) of fn() with HIP events around each call on `stream`: `warmup`
-    untimed calls, then `reps` timed ones.  Returns (median, minimum, mean)."""
+    """Per-call times (ms) of fn() from HIP events on `stream`: `warmup` untimed calls, then
+    `reps` timed ones back to back, one event before the first and one after each (call i
+    runs from event i to event i + 1; an event record costs a few us of GPU time, so one per
+    call rather than a pair).  Returns (median, minimum, mean)."""
     for _ in range(warmup):
         fn()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for e0, e1 in ev:
-        e0.record(stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for e in ev[1:]:
         fn()
-        e1.record(stream)
+        e.record(stream)
     torch.cuda.synchronize()
-    t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
     return t[len(t) // 2], t[0], sum(t) / len(t)
 
 
@@ -467,7 +469,7 @@ def secondary(ub, wl, torch, np, dev):
     # QKV: 32 THD microbatches of one step
     q = qkv_step(ub, wl, torch, np, dev)
     log("secondary qkv_ag")
-    sec, qst = q.timed(q.cfg(True), 20, 5, events=True)
+    sec, qst = q.timed(q.cfg(True), 20, 5, events=2)
     sec_h, _ = q.timed(q.cfg(False), 10, 2)
     hl_ev = q.timed(q.cfg(False), 2, 0, events=True)[1]
     res = {"atomic_gemm": {"tflops_step": round(q.flops / sec / 1e12, 2), "ms_per_step": round(sec * 1e3, 4),
