@@ -1313,7 +1313,8 @@ double seg_cost(const TileOpt& o, int64_t rows, int64_t n, int64_t k, int nseg) 
 // K segmentation of a call of T rows (device-side loop, the chip to itself): the best of no
 // segmentation (one tile, or whole rounds of a large tile and a tail launch, as choose_plan
 // prices them), all rows split, and whole rounds of a large tile followed by the remaining
-// rows split; each split option over the four tiles and nseg in {2, 3, 4, 6, 8, 12, 16}
+// rows split; each split option over the four tiles the split costs were fitted on (not the
+// narrow 256x192 and 256x160) and nseg in {2, 3, 4, 6, 8, 12, 16}
 // (at most one segment per k-step).  Segmentation is taken only for a predicted gain of 3%.
 SegPlan choose_segmentation(int64_t T, int64_t n, int64_t k, int32_t batch) {
   SegPlan none;
@@ -1348,7 +1349,8 @@ SegPlan choose_segmentation(int64_t T, int64_t n, int64_t k, int32_t batch) {
   double best_cost = base * 0.97;
   const int counts[] = {2, 3, 4, 6, 8, 12, 16};
   for (const auto& lead : leads)
-    for (const TileOpt& o : kTileOpts)
+    for (const TileOpt& o : kTileOpts) {
+      if (o.kind == kTile256x192 || o.kind == kTile256x160) continue;  // split cost not fitted
       for (int nseg : counts) {
         if (nseg > nk) break;
         const double c = lead.second + seg_cost(o, T - lead.first, n, k, nseg);
@@ -1357,6 +1359,7 @@ SegPlan choose_segmentation(int64_t T, int64_t n, int64_t k, int32_t batch) {
           best = {lead.first, nseg, o.bm, o.bn, 2};
         }
       }
+    }
   return best;
 }
 
