@@ -312,12 +312,13 @@ def test_fc1_full_size_sampled(ub, atomic):
 
 def test_gqa_bulk_sweep_sampled(ub):
     """One capacity buffer, never reallocated, swept over a declared subset of the T grid
-    (first, every 4th, last on the 1016-step grid, and the capacity 32768)."""
+    (first, every 4th, last on the 1016-step grid, and the capacity 32768); the device-side
+    loop also at T = 7120 and 8136, where its plan is one round of 256x160 tiles."""
     w = wl.gqa_bulk()
     Ts = wl.gqa_tokens(include_capacity=False)
     subset = sorted(set(Ts[::4]) | {Ts[0], Ts[-1], 32768})
     _full_size_ag(ub, w, subset, "gqa_bulk")
-    _full_size_ag(ub, w, [Ts[0], Ts[13], 32768], "gqa_bulk", atomic=True)
+    _full_size_ag(ub, w, [Ts[0], Ts[6], Ts[7], Ts[13], 32768], "gqa_bulk", atomic=True)
 
 
 def test_kernel_timing_counts_launches(ub):

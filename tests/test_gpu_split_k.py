@@ -237,8 +237,8 @@ def test_arrival_timeout_in_split_tiles(ub):
 def test_gqa_automatic_segmentation_sampled(ub, atomic):
     """GQA sizes (hidden 8192, 1280 columns, one 32768-row buffer) with scratch registered:
     sampled rows against the oracle at T where the library segments all rows, only the
-    last round's rows, or nothing, and the device-side loop's bits equal to the host
-    loop's."""
+    last round's rows, or nothing (T = 8136: one round of the narrow 256x160 tile), and the
+    device-side loop's bits equal to the host loop's."""
     w = wl.gqa_bulk()
     ra, rw, _ = w.seeds()
     a_all = wl.activations(w, w.capacity, ra)
@@ -251,7 +251,7 @@ def test_gqa_automatic_segmentation_sampled(ub, atomic):
         scr = _scratch(ub, reg.h)
         c = gu.canary((w.capacity + 4, w.n_cols))
         seen = set()
-        for T in (1024, 4072, 13216, 20328, 32520):
+        for T in (1024, 4072, 8136, 13216, 20328, 32520):
             reg.set_T(T)
             outs = []
             for at in (atomic, not atomic):
@@ -263,6 +263,8 @@ def test_gqa_automatic_segmentation_sampled(ub, atomic):
                 if at:
                     plan = ub.ub_debug_last_plan(reg.h, seg=True)
                     seen.add("all" if plan[6] > 1 and plan[5] == 0 else "tail" if plan[6] > 1 else "none")
+                    if plan[1] in (192, 160):
+                        seen.add("narrow")
             print(f"[gqa split_k] T={T} atomic={atomic} plan={plan}", flush=True)
             ch = outs[0]
             assert np.array_equal(ch[:T], outs[1][:T])
@@ -270,6 +272,6 @@ def test_gqa_automatic_segmentation_sampled(ub, atomic):
             gu.check_close(ch[rows], og.ag_rows(a_all[rows], wt), a_all[rows], wt, f"gqa T={T}")
             assert np.all(ch[T:] == gu.CANARY)
         assert _counters_zero(ub, scr)
-        assert {"all", "tail"} <= seen, seen
+        assert {"all", "tail", "narrow"} <= seen, seen
     finally:
         reg.close()
