@@ -951,6 +951,9 @@ using PP256x192 = Cfg<256, 192, 32, 4, 4, 2, 256>;  // 8 waves of 64x96 (B rows 
 using PP256x160 = Cfg<256, 160, 32, 4, 4, 2, 256>;  // 8 waves of 64x80
 using PL128x128 = Cfg<128, 128, 32, 4, 2, 2>;   // 4 waves of 64x64, 2 workgroups per CU
 constexpr int PP_D = 3;
+// The narrow tiles load two steps ahead: 1-3% faster than three at every one-round point
+// where the plans take them (GQA T = 7120, 8136; qkv T = 5536 ... 6392), in-process A/B.
+constexpr int PP_D_NARROW = 2;
 
 // Tile choice by a cost model fitted to measurements.  A launch of `tiles` workgroups on
 // the CUs left to it (share = 256 / concurrency; the 128 x 128 kernel holds two workgroups
@@ -1121,9 +1124,9 @@ hipError_t launch_split_r(int kind, const GemmArgs& g, const GemmUnits& u, hipSt
     case kTile128x256:
       return launch<PP128x256>(&gemm_bf16_pingpong<PP128x256, PP_D, R>, g, u, stream, mode, nseg);
     case kTile256x192:
-      return launch<PP256x192>(&gemm_bf16_pingpong<PP256x192, PP_D, R>, g, u, stream, mode, nseg);
+      return launch<PP256x192>(&gemm_bf16_pingpong<PP256x192, PP_D_NARROW, R>, g, u, stream, mode, nseg);
     case kTile256x160:
-      return launch<PP256x160>(&gemm_bf16_pingpong<PP256x160, PP_D, R>, g, u, stream, mode, nseg);
+      return launch<PP256x160>(&gemm_bf16_pingpong<PP256x160, PP_D_NARROW, R>, g, u, stream, mode, nseg);
     default:
       return launch<PL128x128>(&gemm_bf16_seg<PL128x128, R>, g, u, stream, mode, nseg);
   }
@@ -1145,9 +1148,9 @@ hipError_t launch_kind(int kind, const GemmArgs& g, const GemmUnits& u, hipStrea
     case kTile128x256:
       return launch<PP128x256>(&gemm_bf16_pingpong<PP128x256, PP_D>, g, u, stream);
     case kTile256x192:
-      return launch<PP256x192>(&gemm_bf16_pingpong<PP256x192, PP_D>, g, u, stream);
+      return launch<PP256x192>(&gemm_bf16_pingpong<PP256x192, PP_D_NARROW>, g, u, stream);
     case kTile256x160:
-      return launch<PP256x160>(&gemm_bf16_pingpong<PP256x160, PP_D>, g, u, stream);
+      return launch<PP256x160>(&gemm_bf16_pingpong<PP256x160, PP_D_NARROW>, g, u, stream);
     default:
       return launch<PL128x128>(&gemm_bf16_pipelined<PL128x128>, g, u, stream);
   }
