@@ -1368,13 +1368,38 @@ UB_API ub_status_t ub_gemm_rs_chunked_fp8(ub_handle_t h, const void* a, int64_t 
     if ((st = plan_units(h, &units)) != UB_OK) return st;
     if ((st = ensure_device(h, 1)) != UB_OK) return st;
     g.concurrency = 1;
-    st = timed_launch(h, caller, 0, 2.0 * T * k * H, double(T * k + k * H + 2 * tp * T * H),
-                      [&] { return ubx::launch_gemm_fp8_units(g, units, caller); },
-                      "fp8 slice GEMM launch");
-    if (st != UB_OK) return st;
-    const ubx::ReduceArgs r = reduce_args(h, 0, T, out, ldo, ring);
-    return timed_launch(h, caller, 1, double(tp - 1) * T * H, 2.0 * (tp + 1) * T * H,
-                        [&] { return ubx::launch_reduce_partials(r, caller); }, "reduce launch");
+    int64_t cuts[kMaxRsPieces + 1];
+    const int np = rs_cuts(T, rs_pieces(h), cuts);
+    if (np <= 1) {
+      st = timed_launch(h, caller, 0, 2.0 * T * k * H, double(T * k + k * H + 2 * tp * T * H),
+                        [&] { return ubx::launch_gemm_fp8_units(g, units, caller); },
+                        "fp8 slice GEMM launch");
+      if (st != UB_OK) return st;
+      const ubx::ReduceArgs r = reduce_args(h, 0, T, out, ldo, ring);
+      return timed_launch(h, caller, 1, double(tp - 1) * T * H, 2.0 * (tp + 1) * T * H,
+                          [&] { return ubx::launch_reduce_partials(r, caller); }, "reduce launch");
+    }
+    // pipelined as the bf16 call: piece p's slice GEMMs on the caller's stream, its
+    // reduction on worker stream 1 after an event, overlapping piece p + 1's GEMMs
+    if ((st = ensure_device(h, 2)) != UB_OK) return st;
+    hipStream_t rs = h->streams[1];
+    for (int p = 0; p < np; ++p) {
+      const int64_t lo = cuts[p], rows = cuts[p + 1] - cuts[p];
+      const ubx::GemmUnits pu = clip_rows(units, lo, cuts[p + 1]);
+      st = timed_launch(h, caller, 0, 2.0 * rows * k * H, double(rows * k + k * H + 2 * tp * rows * H),
+                        [&] { return ubx::launch_gemm_fp8_units(g, pu, caller); },
+                        "fp8 slice GEMM launch");
+      if (st != UB_OK) return st;
+      hipError_t e = hipEventRecord(h->ev_piece[p], caller);
+      if (e == hipSuccess) e = hipStreamWaitEvent(rs, h->ev_piece[p], 0);
+      if (e != hipSuccess) return hip_fail(h, e, "piece event");
+      const ubx::ReduceArgs r = reduce_args(h, lo, rows, out, ldo, ring);
+      st = timed_launch(h, rs, 1, double(tp - 1) * rows * H, 2.0 * (tp + 1) * rows * H,
+                        [&] { return ubx::launch_reduce_partials(r, rs); }, "reduce launch");
+      if (st != UB_OK) return st;
+    }
+    h->last_plan.rs_pieces = np;
+    return join_streams(h, caller, 2);
   }
 
   const int S = h->plan.n_streams;

@@ -544,8 +544,8 @@ UB_API ub_status_t ub_register_scratch(ub_handle_t h, void* buf, size_t bytes);
  *                          segments (clamped to the number of 32-deep k-steps).
  *   "seg_tile_m", "seg_tile_n"  tile of forced split pieces (default 256 x 256; any of the
  *                          bf16 tiles).
- *   "rs_pieces"            device-side reduce-scatter (atomic_gemm, fuse_reduce 0) in P row
- *                          pieces: piece p's slice GEMMs on the caller's stream, its
+ *   "rs_pieces"            device-side reduce-scatter (atomic_gemm; bf16 with fuse_reduce 0,
+ *                          and fp8) in P row pieces: piece p's slice GEMMs on the caller's stream, its
  *                          reduction on a worker stream overlapping piece p + 1's GEMMs;
  *                          0 (default) the library's choice, 1..8 forced.  The results do
  *                          not change.

@@ -303,6 +303,39 @@ def test_rs_fp8_integer_bit_exact_every_schedule(ub, tile):
         reg.close()
 
 
+def test_rs_fp8_pipelined_pieces_bit_exact(ub):
+    """The device-side FP8 reduce-scatter cut into row pieces (debug rs_pieces, each piece's
+    reduction on a worker stream after its slice GEMMs): integer codes equal the oracle bit
+    for bit in both reduce orders, workspace included, whatever the piece count; the plan
+    record reports the pieces taken (cuts on multiples of 1280 rows)."""
+    rng = np.random.default_rng(77)
+    cap, H, T, tp = 4096, 256, 3000, 4
+    K = tp * 64
+    a = _int_codes(rng, (T, K))
+    w = _int_codes(rng, (H, K))
+    sa, sw = 2.0 ** -4, 2.0 ** -3
+    reg = gu.Registration(ub, cap, H, tp, pad_rows=8)
+    try:
+        reg.set_T(T)
+        for order in ("ascending", "ring"):
+            want, want_ws = _oracle_rs8(cap, H, tp, a, w, sa, sw,
+                                        op.OverlapCfg(method="pipeline", num_splits=4, reduce_order=order))
+            for pieces, taken in ((1, 0), (2, 2), (3, 3), (8, 3)):
+                print(f"[rs fp8 pieces] {order} {pieces}", flush=True)
+                ub.ub_debug_set(reg.h, "rs_pieces", pieces)
+                reg.ws_t.fill_(gu.CANARY)
+                got = _rs8(ub, reg, a, w, sa, sw, ub.make_cfg("pipeline", 4, 3, atomic_gemm=True,
+                                                              reduce_order=order))
+                assert np.array_equal(got[:T], want), (order, pieces)
+                assert np.all(got[T:] == gu.CANARY)
+                ws = gu.host(reg.ws_t)
+                assert np.array_equal(ws[: tp * T * H].reshape(tp, T, H), want_ws)
+                assert ub.ub_debug_plan(reg.h)["rs_pieces"] == taken, (pieces, ub.ub_debug_plan(reg.h))
+        ub.ub_debug_set(reg.h, "rs_pieces", 0)
+    finally:
+        reg.close()
+
+
 def test_rs_fp8_random_codes_within_tolerance_and_schedule_identical(ub):
     """Codes over every binade, a scale pair whose fp32 product is not a power of two:
     within the bounds of the oracle, and bit-identical across schedules."""
