@@ -325,6 +325,19 @@ struct Tile {
     }
   }
 
+  // Load slot j alone (the same load issue_loads makes for it).
+  __device__ inline void issue_load_slot(unsigned char* smem, int ks, int nk, int j) const {
+    if (j + 1 == C::LMAX && C::LMAX * C::NW != C::NL && j >= nl) return;
+    const uint32_t st = lds_addr(smem) + (uint32_t)((ks % C::S) * C::STAGE);
+    const uint32_t dead = ks < nk ? 0u : OOB;
+    if (slot_is_a(j)) {
+      const uint32_t tail = ks == k_tail_step ? ~0u : 0u;
+      dma16(ra, st + lds_off[j], ((off[j] + (uint32_t)ks * a_kstep) | dead) | (tail_mask[j] & tail));
+    } else {
+      dma16(rb, st + lds_off[j], (off[j] + (uint32_t)ks * b_kstep) | dead);
+    }
+  }
+
   __device__ inline void read_frags(const unsigned char* smem, int ks, int kk, bf16x8* af,
                                     bf16x8* bf) const {
     const unsigned char* sa = smem + (ks % C::S) * C::STAGE;
@@ -504,6 +517,33 @@ __device__ inline void mfma_block(f32x4 (&acc)[C::FM][C::FN], const bf16x8* af, 
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
 }
 
+// The MFMAs of one step with this wave's direct loads of step ks_load dealt between them:
+// load slot j after MFMA (j + 1) NM / (LMAX + 1) of the NM.  The loads' issue leaves the
+// memory cluster, which is the longer of the two clusters on the tiles that use this.
+template <class C>
+__device__ inline void mfma_block_loads(f32x4 (&acc)[C::FM][C::FN],
+                                        const bf16x8 (&af)[C::SUBS][C::FM],
+                                        const bf16x8 (&bf)[C::SUBS][C::FN], const Tile<C>& t,
+                                        unsigned char* smem, int ks_load, int k1) {
+  constexpr int NM = C::SUBS * C::FM * C::FN;
+  int m = 0, j = 0;
+#pragma unroll
+  for (int sub = 0; sub < C::SUBS; ++sub)
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int n = 0; n < C::FN; ++n) {
+        acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[sub][i], bf[sub][n], acc[i][n], 0, 0, 0);
+        ++m;
+        if (j < C::LMAX && m == (j + 1) * NM / (C::LMAX + 1)) {
+          __builtin_amdgcn_sched_barrier(0);
+          t.issue_load_slot(smem, ks_load, k1, j);
+          __builtin_amdgcn_sched_barrier(0);
+          ++j;
+        }
+      }
+}
+
 // ---- 8-wave ping-pong ------------------------------------------------------------------
 // Waves 0-3 (group 0) and 4-7 (group 1) hold one SIMD each.  Each wave alternates a memory
 // cluster (all fragments of step ks from LDS; its share of the direct loads of step ks+D)
@@ -517,6 +557,14 @@ __device__ inline void mfma_block(f32x4 (&acc)[C::FM][C::FN], const bf16x8* af, 
 //    loads per step): group 1 at the end of its memory cluster, group 0 at the end of its
 //    compute cluster;
 //  - every wave executes the same number of barriers (2*nk + 4).
+// LIC (loads in the compute cluster): a wave issues its loads of step ks+D between the MFMAs
+// of step ks instead of in its memory cluster.  Those loads come after b(2ks+1), later than
+// the stage-reuse bound needs; group 1's wait at the end of its memory cluster of step ks
+// then has only steps ks+2 ... ks+D-1 issued after ks+1, so (D-2)*L may stay in flight,
+// while group 0's wait, after its compute cluster, is unchanged.  Where the memory cluster
+// is the longer one (the narrow tiles and 128x256, whose waves hold 16-24 MFMAs per step)
+// this measured 2-11% faster; where the MFMA cluster is (256x256, 320x256: 32 and 40),
+// 3-7% slower, and 10% slower with all loads at the cluster's start.
 
 // s_waitcnt for this wave's loads: at most (D-1) steps' worth (LMAX or LMAX-1 per step) in
 // flight, optionally with the LDS reads drained, then the workgroup barrier.
@@ -656,7 +704,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_split_reduce(Params p) {
 
 // SPLIT 1 or 2: workgroup w runs segment w % nseg of tile w / nseg; 1 meets the tile's
 // other segments in split_meet, 2 only writes its partial (split_write).
-template <class C, int D, int SPLIT = 0>
+template <class C, int D, int SPLIT = 0, bool LIC = false>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_pingpong(Params p) {
   static_assert(C::NW == 8, "ping-pong needs two waves per SIMD");
@@ -702,17 +750,21 @@ void gemm_bf16_pingpong(Params p) {
     // memory cluster
 #pragma unroll
     for (int sub = 0; sub < C::SUBS; ++sub) t.read_frags(smem, ks, sub * 32, af[sub], bf[sub]);
-    t.issue_loads(smem, ks + D, k1);
+    if constexpr (!LIC) t.issue_loads(smem, ks + D, k1);
     __builtin_amdgcn_sched_barrier(0);
     if (group == 1) {
-      wait_loads_barrier<C, D, true>(full);
+      wait_loads_barrier<C, LIC ? D - 1 : D, true>(full);
     } else {
       __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     __builtin_amdgcn_sched_barrier(0);
     // compute cluster
+    if constexpr (LIC) {
+      mfma_block_loads<C>(acc, af, bf, t, smem, ks + D, k1);
+    } else {
 #pragma unroll
-    for (int sub = 0; sub < C::SUBS; ++sub) mfma_block<C>(acc, af[sub], bf[sub]);
+      for (int sub = 0; sub < C::SUBS; ++sub) mfma_block<C>(acc, af[sub], bf[sub]);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (group == 0) {
       wait_loads_barrier<C, D, false>(full);
@@ -951,9 +1003,11 @@ using PP256x192 = Cfg<256, 192, 32, 4, 4, 2, 256>;  // 8 waves of 64x96 (B rows 
 using PP256x160 = Cfg<256, 160, 32, 4, 4, 2, 256>;  // 8 waves of 64x80
 using PL128x128 = Cfg<128, 128, 32, 4, 2, 2>;   // 4 waves of 64x64, 2 workgroups per CU
 constexpr int PP_D = 3;
-// The narrow tiles load two steps ahead: 1-3% faster than three at every one-round point
-// where the plans take them (GQA T = 7120, 8136; qkv T = 5536 ... 6392), in-process A/B.
-constexpr int PP_D_NARROW = 2;
+// Tiles whose direct loads issue between the MFMAs (see the ping-pong kernel): the narrow
+// tiles and 128x256.  At load distance 3 they measured 2-11% faster than with the loads in
+// the memory cluster at distance 2 (the narrow tiles' best before) on the GQA, qkv and fc1
+// points where the plans take them; at distance 2 the gain was a third of that.
+template <class C> constexpr bool kLoadsInCompute = C::BN < 256 || C::BM < 256;
 
 // Tile choice by a cost model fitted to measurements.  A launch of `tiles` workgroups on
 // the CUs left to it (share = 256 / concurrency; the 128 x 128 kernel holds two workgroups
@@ -971,10 +1025,16 @@ constexpr int PP_D_NARROW = 2;
 // forced cuts): the model's plan is within 2% of the best measured plan at 67 of them, at
 // 0.989 of the best on average.  The narrow tiles 256x192 and 256x160 (eight and ten
 // column tiles on N = 1536, eight on N = 1280) fill one round where 256x256 leaves a third
-// of the CUs idle; their speeds, 0.80 and 0.76, are the same ratio fitted to forced
-// one-round launches of the three shapes at 21 T against 256x256 (within 4% at each).
+// of the CUs idle; their speeds, 0.883 and 0.835 (with their loads between the MFMAs), are
+// the same ratio fitted to forced one-round launches of the three shapes at 19 and 15 T
+// against 256x256 (within 10% at each; the fit overrates them a little next to full
+// occupancy, where the clock falls faster than the boost curve has it).  With these the
+// plans moved to 256x192 at GQA T = 9152, qkv 6656 ... 8192 and fc1 3072 and measured
+// 2-10% faster there (in-process A/B against 0.80 and 0.76); raising 128x256 to the
+// 0.78 its one-round points give as well lost 6-10% at GQA T = 2040 and qkv T = 2048,
+// where it displaces split-K plans, so 128x256 keeps the joint fit's 0.749.
 // A one-round launch's time barely follows the tile's area (a 128x256 or 256x160 tile
-// takes 0.78 or 0.92 of a 256x256 tile's time): the narrow tiles pay only where they fill
+// takes 0.72 or 0.81 of a 256x256 tile's time): the narrow tiles pay only where they fill
 // CUs that a wider tile leaves idle.
 //
 // Besides one tile shape for the whole launch, the model prices cuts: a launch that has the
@@ -990,8 +1050,8 @@ const TileOpt kTileOpts[] = {{kTile320x256, 320, 256, 1, 1.030, 1.030},
                              {kTile256x256, 256, 256, 1, 1.000, 1.000},
                              {kTile128x256, 128, 256, 1, 0.749, 0.749},
                              {kTile128x128, 128, 128, 2, 0.373, 0.493},
-                             {kTile256x192, 256, 192, 1, 0.800, 0.800},
-                             {kTile256x160, 256, 160, 1, 0.760, 0.760}};
+                             {kTile256x192, 256, 192, 1, 0.883, 0.883},
+                             {kTile256x160, 256, 160, 1, 0.835, 0.835}};
 constexpr double kBoostMax = 1.476, kBoostExp = 0.2245;
 
 const TileOpt* find_tile(int bm, int bn) {
@@ -1118,15 +1178,15 @@ hipError_t launch_split_r(int kind, const GemmArgs& g, const GemmUnits& u, hipSt
   constexpr int mode = R == 1 ? 2 : 3;
   switch (kind) {
     case kTile320x256:
-      return launch<PP320x256>(&gemm_bf16_pingpong<PP320x256, PP_D, R>, g, u, stream, mode, nseg);
+      return launch<PP320x256>(&gemm_bf16_pingpong<PP320x256, PP_D, R, kLoadsInCompute<PP320x256>>, g, u, stream, mode, nseg);
     case kTile256x256:
-      return launch<PP256x256>(&gemm_bf16_pingpong<PP256x256, PP_D, R>, g, u, stream, mode, nseg);
+      return launch<PP256x256>(&gemm_bf16_pingpong<PP256x256, PP_D, R, kLoadsInCompute<PP256x256>>, g, u, stream, mode, nseg);
     case kTile128x256:
-      return launch<PP128x256>(&gemm_bf16_pingpong<PP128x256, PP_D, R>, g, u, stream, mode, nseg);
+      return launch<PP128x256>(&gemm_bf16_pingpong<PP128x256, PP_D, R, kLoadsInCompute<PP128x256>>, g, u, stream, mode, nseg);
     case kTile256x192:
-      return launch<PP256x192>(&gemm_bf16_pingpong<PP256x192, PP_D_NARROW, R>, g, u, stream, mode, nseg);
+      return launch<PP256x192>(&gemm_bf16_pingpong<PP256x192, PP_D, R, kLoadsInCompute<PP256x192>>, g, u, stream, mode, nseg);
     case kTile256x160:
-      return launch<PP256x160>(&gemm_bf16_pingpong<PP256x160, PP_D_NARROW, R>, g, u, stream, mode, nseg);
+      return launch<PP256x160>(&gemm_bf16_pingpong<PP256x160, PP_D, R, kLoadsInCompute<PP256x160>>, g, u, stream, mode, nseg);
     default:
       return launch<PL128x128>(&gemm_bf16_seg<PL128x128, R>, g, u, stream, mode, nseg);
   }
@@ -1142,15 +1202,15 @@ hipError_t launch_kind(int kind, const GemmArgs& g, const GemmUnits& u, hipStrea
   if (u.n <= 0) return hipSuccess;
   switch (kind) {
     case kTile320x256:
-      return launch<PP320x256>(&gemm_bf16_pingpong<PP320x256, PP_D>, g, u, stream);
+      return launch<PP320x256>(&gemm_bf16_pingpong<PP320x256, PP_D, 0, kLoadsInCompute<PP320x256>>, g, u, stream);
     case kTile256x256:
-      return launch<PP256x256>(&gemm_bf16_pingpong<PP256x256, PP_D>, g, u, stream);
+      return launch<PP256x256>(&gemm_bf16_pingpong<PP256x256, PP_D, 0, kLoadsInCompute<PP256x256>>, g, u, stream);
     case kTile128x256:
-      return launch<PP128x256>(&gemm_bf16_pingpong<PP128x256, PP_D>, g, u, stream);
+      return launch<PP128x256>(&gemm_bf16_pingpong<PP128x256, PP_D, 0, kLoadsInCompute<PP128x256>>, g, u, stream);
     case kTile256x192:
-      return launch<PP256x192>(&gemm_bf16_pingpong<PP256x192, PP_D_NARROW>, g, u, stream);
+      return launch<PP256x192>(&gemm_bf16_pingpong<PP256x192, PP_D, 0, kLoadsInCompute<PP256x192>>, g, u, stream);
     case kTile256x160:
-      return launch<PP256x160>(&gemm_bf16_pingpong<PP256x160, PP_D_NARROW>, g, u, stream);
+      return launch<PP256x160>(&gemm_bf16_pingpong<PP256x160, PP_D, 0, kLoadsInCompute<PP256x160>>, g, u, stream);
     default:
       return launch<PL128x128>(&gemm_bf16_pipelined<PL128x128>, g, u, stream);
   }
