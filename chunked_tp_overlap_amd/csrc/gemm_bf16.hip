@@ -77,6 +77,7 @@ struct Params {
   int32_t n, k;
   int32_t tiles_n;                       // tile columns
   int32_t group;                         // row tiles per group (tile_of)
+  int32_t tiles_total;                   // unit_tile0[n_units]: the launch's tiles
   int32_t n_units;                       // row units, in processing order
   int32_t unit_row0[kMaxGemmUnits];
   int32_t unit_rows[kMaxGemmUnits];
@@ -238,9 +239,11 @@ struct Tile {
   uint32_t a_kstep, b_kstep;
   int k_tail_step;                       // the step whose A chunks past k are masked, or -1
   int a_rd_row, a_rd_c, a_rd_x, b_krow, b_col_chunk, b_x, b_in;
+  const uint32_t* ready;                 // the launch's arrival flags (nullptr: none)
+  int nslots;                            // fused reduction's slices (0: none)
 
-  // false: this workgroup has no tile (the whole workgroup returns before any barrier)
-  __device__ inline bool init(const Params& p, int tid, int tile_index = -1) {
+  // (a workgroup past the launch's last tile ends in tile_of_lanes, before any barrier)
+  __device__ inline void init(const Params& p, int tid, int tile_index = -1) {
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     group = wave >> 2;
@@ -248,24 +251,36 @@ struct Tile {
     wn = wave % C::WGN;
     z = blockIdx.z;
     tile = tile_index >= 0 ? tile_index : (int)blockIdx.x;
+    // every kernel argument the prologue needs, loaded before the first branch (args_here)
+    const UnitLanes ul = unit_lanes(p);
+    const uint16_t* const pa = p.a;
+    const uint16_t* const pb = p.b;
+    uint16_t* const pc = p.c;
+    const int64_t lda = p.lda, sa = p.sa, ldb = p.ldb, sb = p.sb, sc = p.sc;
+    const int kk = p.k, nn = p.n;
+    ready = p.ready;
+    nslots = p.nslots;
+    lanes_here(ul);
+    const int nu = p.n_units, tc = p.tiles_n, tg = p.group, tt = p.tiles_total;
+    args_here(pa, pb, pc, lda, sa, ldb, sb, sc, kk, nn, ready, nslots, nu, tc, tg, tt);
     int tn;
-    if (!tile_of(p, tile, C::BM, m0, m_end, tn)) return false;
+    tile_of_lanes(ul, nu, tc, tg, tt, tile, C::BM, m0, m_end, tn);
     n0 = tn * C::BN;
-    const uint16_t* A = p.a + z * p.sa + (int64_t)m0 * p.lda;
-    const uint16_t* B = p.b + z * p.sb + n0;
-    cg = p.c + z * p.sc;
+    const uint16_t* A = pa + z * sa + (int64_t)m0 * lda;
+    const uint16_t* B = pb + z * sb + n0;
+    cg = pc + z * sc;
     // A from this tile's first row, valid rows only; B from column n0 of the batch entry,
     // k rows only (rows past k read zeros)
     const int rows_valid = min(C::BM, m_end - m0);
-    ra = make_rsrc(A, (uint32_t)(rows_valid * p.lda * 2));
-    rb = make_rsrc(B, (uint32_t)(((int64_t)p.k * p.ldb - n0) * 2));
+    ra = make_rsrc(A, (uint32_t)(rows_valid * lda * 2));
+    rb = make_rsrc(B, (uint32_t)(((int64_t)kk * ldb - n0) * 2));
     // Direct loads: A load i covers rows A_ROWS_PER_LOAD*i + lane/A_CPR, slot lane%A_CPR
     // holding k-chunk slot ^ a_swz(row); B load i covers k-rows B_ROWS_PER_LOAD*i +
     // lane/B_CPR, slot lane%B_CPR holding column chunk slot ^ b_swz(krow).  Load i of an
     // operand lands at byte 1024*i of that operand's part of the stage.
     nl = wave < C::NFULL ? C::LMAX : C::LMAX - 1;
-    k_tail_step = p.k % C::BK ? p.k / C::BK : -1;
-    const int k_tail = p.k - (p.k / C::BK) * C::BK;  // valid k of the last step (if partial)
+    k_tail_step = kk % C::BK ? kk / C::BK : -1;
+    const int k_tail = kk - (kk / C::BK) * C::BK;  // valid k of the last step (if partial)
 #pragma unroll
     for (int j = 0; j < C::LMAX; ++j) {
       const int li = wave + C::NW * j;
@@ -275,19 +290,19 @@ struct Tile {
         const int row = C::A_ROWS_PER_LOAD * idx + lane / C::A_CPR;
         const int chunk = (lane % C::A_CPR) ^ a_swz<C::A_CPR>(row);
         lds_off[j] = (uint32_t)idx * 1024;
-        off[j] = (uint32_t)((row * p.lda + chunk * 8) * 2);
+        off[j] = (uint32_t)((row * lda + chunk * 8) * 2);
         if (k_tail_step >= 0 && chunk * 8 >= k_tail) tail_mask[j] = OOB;
       } else {
         const int krow = C::B_ROWS_PER_LOAD * idx + lane / C::B_CPR;
         const int chunk = (lane % C::B_CPR) ^ b_swz(krow);
         lds_off[j] = (uint32_t)(C::A_BYTES + idx * 1024);
-        off[j] = chunk * 8 < C::BN && n0 + chunk * 8 < p.n
-                     ? (uint32_t)((krow * p.ldb + chunk * 8) * 2) : OOB;
+        off[j] = chunk * 8 < C::BN && n0 + chunk * 8 < nn
+                     ? (uint32_t)((krow * ldb + chunk * 8) * 2) : OOB;
       }
       if (j >= nl) off[j] = OOB;
     }
     a_kstep = C::BK * 2;
-    b_kstep = (uint32_t)(C::BK * p.ldb * 2);
+    b_kstep = (uint32_t)(C::BK * ldb * 2);
     // Fragment reads.  A: row R = wm*WM + i*16 + (lane&15), k-chunk (kk/8 + lane/16) in
     // slot ^ a_swz(R) (a function of lane&15 only).  B: k-row kk + (lane/16)*8 + (lane>>2)&3
     // (+4 for the second read), column wn*WN + j*16 + (lane&3)*4.
@@ -298,8 +313,6 @@ struct Tile {
     b_col_chunk = (wn * C::WN + (lane & 3) * 4) >> 3;
     b_x = b_swz(b_krow);  // bits 0, 1 and 3 of the k-row; the second read's +4 leaves them
     b_in = (lane & 1) * 8;
-
-    return true;
   }
 
   // This wave's direct loads of step ks into stage ks % S.  Steps past the end are issued
@@ -449,7 +462,7 @@ struct Tile {
     constexpr int VPR = C::BN / 8;
     constexpr int NV = C::BM * VPR / C::THREADS;  // 16-byte vectors per lane
     // G vectors per round with all their slices' loads in flight (16 loads per lane)
-    constexpr int G0 = NS > 0 && NS <= 16 ? 16 / NS : 1;
+    constexpr int G0 = NS > 0 && NS <= 16 ? 16 / (NS > 0 ? NS : 1) : 1;
     constexpr int G = NV % G0 == 0 ? G0 : (NV % 4 == 0 ? 4 : (NV % 2 == 0 ? 2 : 1));
     static_assert(NV % G == 0, "vectors per lane split into rounds");
     constexpr int NL = NS > 0 ? NS : 1;
@@ -669,7 +682,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_split_reduce(Params p) {
   const int tile = (int)blockIdx.x / GROUPS;
   const int q = ((int)blockIdx.x % GROUPS) * 256 + (int)threadIdx.x;
   int m0, m_end, tn;
-  if (!tile_of(p, tile, C::BM, m0, m_end, tn)) return;
+  tile_of_wave(p, tile, C::BM, m0, m_end, tn);
   const float* src = p.parts + (int64_t)tile * p.nseg * TILE + q * 4;
   // four partials' loads in flight (past the last segment the last is read again, an L2
   // hit that no add uses), then their adds in segment order
@@ -715,9 +728,9 @@ void gemm_bf16_pingpong(Params p) {
   const int tile = SPLIT ? (int)blockIdx.x / nseg : (int)blockIdx.x;
   const int seg = SPLIT ? (int)blockIdx.x % nseg : 0;
   Tile<C> t;
-  if (!t.init(p, tid, tile)) return;
+  t.init(p, tid, tile);
   bool late = false;
-  if (p.ready) {
+  if (t.ready) {
     late = wait_ready(p, t.m0, min(t.m0 + C::BM, t.m_end), SPLIT != 1);
     if (!SPLIT && late) {
       t.store_nan(p, tid);
@@ -783,7 +796,7 @@ void gemm_bf16_pingpong(Params p) {
     if (!split_meet(smem, p, t, tid, tile, seg, nseg, late, acc)) return;
   }
   t.store(smem, p, tid, acc);
-  if (!SPLIT && p.nslots) t.fused_reduce(smem, p, tid);
+  if (!SPLIT && t.nslots) t.fused_reduce(smem, p, tid);
 }
 
 // ---- 4-wave, S-stage pipeline -----------------------------------------------------------
@@ -798,8 +811,8 @@ void gemm_bf16_pipelined(Params p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x;
   Tile<C> t;
-  if (!t.init(p, tid)) return;
-  if (p.ready && wait_ready(p, t.m0, min(t.m0 + C::BM, t.m_end))) {
+  t.init(p, tid);
+  if (t.ready && wait_ready(p, t.m0, min(t.m0 + C::BM, t.m_end))) {
     t.store_nan(p, tid);
     return;
   }
@@ -840,7 +853,7 @@ void gemm_bf16_pipelined(Params p) {
   }
   wait_vmcnt_and_barrier<0>();  // trailing out-of-range loads landed before LDS is reused
   t.store(smem, p, tid, acc);
-  if (p.nslots) t.fused_reduce(smem, p, tid);
+  if (t.nslots) t.fused_reduce(smem, p, tid);
 }
 
 // ---- K-segmented 4-wave kernel -----------------------------------------------------------
@@ -859,9 +872,9 @@ void gemm_bf16_seg(Params p) {
   const int tile = SPLIT ? (int)blockIdx.x / nseg : (int)blockIdx.x;
   const int seg = SPLIT ? (int)blockIdx.x % nseg : 0;
   Tile<C> t;
-  if (!t.init(p, tid, tile)) return;
+  t.init(p, tid, tile);
   bool late = false;
-  if (p.ready) {
+  if (t.ready) {
     late = wait_ready(p, t.m0, min(t.m0 + C::BM, t.m_end), SPLIT != 1);
     if (!SPLIT && late) {
       t.store_nan(p, tid);
@@ -951,6 +964,7 @@ hipError_t launch(K kernel, const GemmArgs& g, const GemmUnits& units, hipStream
     tiles += (int64_t)((u.rows[i] + C::BM - 1) / C::BM) * p.tiles_n;
   }
   p.unit_tile0[u.n] = (int32_t)tiles;
+  p.tiles_total = (int32_t)tiles;
   if (tiles == 0) return hipSuccess;
   p.group = tile_group(tiles, p.tiles_n, C::NW == 8 ? 1 : 2, g.dbg ? g.dbg->tile_group : 0);
   p.ready = g.ready;

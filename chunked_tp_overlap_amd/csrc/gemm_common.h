@@ -111,27 +111,91 @@ inline hipError_t ensure_lds_attr(const void* kernel, int bytes) {
   return e;
 }
 
-template <class P>
-__host__ __device__ inline bool tile_of(const P& p, int wg, int bm, int& m0, int& m_end, int& tn) {
-  const int C = p.tiles_n;
-  const int total = p.unit_tile0[p.n_units];
+// Workgroup wg's place in that order: its row tile (in the list of all units' row tiles)
+// and its tile column, for `total` tiles of C columns listed in groups of G row tiles.
+__host__ __device__ __attribute__((always_inline)) inline void tile_position(int wg, int total, int C, int G, int& row_tile,
+                                              int& tn) {
   const int R = total / C;
-  if (wg >= total) return false;
   const int q = total / NUM_XCD, rem = total % NUM_XCD;
   const int x = wg % NUM_XCD, k = wg / NUM_XCD;
   const int t = x * q + (x < rem ? x : rem) + k;  // XCD x holds [x q + min(x, rem), ...)
-  const int G = p.group;
   const int group = t / (G * C);
   const int first = group * G;
   const int gm = G < R - first ? G : R - first;
   const int r = t - group * G * C;
-  const int row_tile = first + r % gm;
+  row_tile = first + r % gm;
   tn = r / gm;
+}
+
+template <class P>
+__host__ __device__ __attribute__((always_inline)) inline bool tile_of(const P& p, int wg, int bm, int& m0, int& m_end, int& tn) {
+  const int C = p.tiles_n;
+  const int total = p.unit_tile0[p.n_units];
+  if (wg >= total) return false;
+  int row_tile;
+  tile_position(wg, total, C, p.group, row_tile, tn);
   int u = 0;
   while (u + 1 < p.n_units && p.unit_tile0[u + 1] / C <= row_tile) ++u;
   m0 = p.unit_row0[u] + (row_tile - p.unit_tile0[u] / C) * bm;
   m_end = p.unit_row0[u] + p.unit_rows[u];
   return true;
+}
+
+// tile_of as a wave computes it in a kernel: the same tile, with the unit table read by one
+// load per lane (lane j: unit j) and the unit found by a ballot, instead of a scan whose
+// every step waits on a scalar load.  unit_tile0 is non-decreasing and a multiple of C, so
+// the units that start at or before the row tile are a prefix of the lanes, and its length
+// is the scan's answer.  At the start of a launch every workgroup reads the table at once;
+// there the scan's chain of dependent loads took most of a ~6k-cycle prologue.
+struct UnitLanes {
+  int t0, t1, r0, nr;  // lane j: unit j's first tile, unit j + 1's, unit j's first row, rows
+};
+
+template <class P>
+__device__ __attribute__((always_inline)) inline UnitLanes unit_lanes(const P& p) {
+  static_assert(sizeof(p.unit_row0) == 64 * sizeof(p.unit_row0[0]), "one lane per unit");
+  const int lane = __lane_id();
+  return UnitLanes{p.unit_tile0[lane], p.unit_tile0[lane + 1], p.unit_row0[lane], p.unit_rows[lane]};
+}
+
+// nu units, C tile columns, G row tiles per group, total tiles: the launch's n_units,
+// tiles_n, group and unit_tile0[n_units].  A workgroup past the last tile (none is launched)
+// ends here; an early return instead, after the lanes' loads, makes the compiler treat the
+// kernel's exit as divergent and keep the tile's addresses in VGPRs.
+__device__ __attribute__((always_inline)) inline void tile_of_lanes(const UnitLanes& l, int nu,
+                                                                     int C, int G, int total,
+                                                                     int wg, int bm, int& m0,
+                                                                     int& m_end, int& tn) {
+  if (wg >= total) __builtin_amdgcn_endpgm();
+  int row_tile;
+  tile_position(wg, total, C, G, row_tile, tn);
+  const int lane = __lane_id();
+  const int u = __popcll(__ballot(lane + 1 < nu && l.t1 <= row_tile * C));
+  const int r0 = __builtin_amdgcn_readlane(l.r0, u);
+  m0 = r0 + (row_tile - __builtin_amdgcn_readlane(l.t0, u) / C) * bm;
+  m_end = r0 + __builtin_amdgcn_readlane(l.nr, u);
+}
+
+template <class P>
+__device__ __attribute__((always_inline)) inline void tile_of_wave(const P& p, int wg, int bm,
+                                                                    int& m0, int& m_end, int& tn) {
+  tile_of_lanes(unit_lanes(p), p.n_units, p.tiles_n, p.group, p.tiles_total, wg, bm, m0, m_end,
+                tn);
+}
+
+// Marks values loaded from the kernel arguments as needed here: their loads issue before
+// this point, together, and are waited for once (the compiler otherwise places each load
+// at its first use, behind the branches before it, one round trip each).
+template <class T>
+__device__ inline void arg_here(const T& v) {
+  __asm__ volatile("" ::"s"(v));
+}
+template <class... T>
+__device__ inline void args_here(const T&... v) {
+  (arg_here(v), ...);
+}
+__device__ inline void lanes_here(const UnitLanes& l) {
+  __asm__ volatile("" ::"v"(l.t0), "v"(l.t1), "v"(l.r0), "v"(l.nr));
 }
 
 }  // namespace

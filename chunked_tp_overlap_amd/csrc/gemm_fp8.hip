@@ -48,6 +48,7 @@ struct F8Params {
   float scale;
   int32_t tiles_n;
   int32_t group;                         // row tiles per group (tile_of)
+  int32_t tiles_total;                   // unit_tile0[n_units]: the launch's tiles
   int32_t n_units;
   int32_t unit_row0[kMaxGemmUnits];
   int32_t unit_rows[kMaxGemmUnits];
@@ -91,34 +92,44 @@ struct F8Tile {
   uint32_t rd_a, rd_b;  // byte offset of this lane's first A / B fragment row in a stage
   int rd_c0, rd_c1;     // the two 16-byte chunk slots (swizzled) this lane reads
 
-  // false: this workgroup has no tile (the whole workgroup returns before any barrier)
-  __device__ inline bool init(const F8Params& p, int tid) {
+  // (a workgroup past the launch's last tile ends in tile_of_lanes, before any barrier)
+  __device__ inline void init(const F8Params& p, int tid) {
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     group = wave >> 2;
     wm = wave / C::WGN;
     wn = wave % C::WGN;
+    // every kernel argument the prologue needs, loaded before the first branch (args_here)
+    const UnitLanes ul = unit_lanes(p);
+    const auto pa = p.a;
+    const auto pb = p.b;
+    const auto pc = p.c;
+    const int64_t lda = p.lda, sa = p.sa, ldb = p.ldb, sb = p.sb, sc = p.sc;
+    const int nn = p.n;
+    lanes_here(ul);
+    const int nu = p.n_units, tc = p.tiles_n, tg = p.group, tt = p.tiles_total;
+    args_here(pa, pb, pc, lda, sa, ldb, sb, sc, nn, nu, tc, tg, tt);
     int tn;
-    if (!tile_of(p, blockIdx.x, C::BM, m0, m_end, tn)) return false;
+    tile_of_lanes(ul, nu, tc, tg, tt, (int)blockIdx.x, C::BM, m0, m_end, tn);
     n0 = tn * C::BN;
     const int rows_a = min(C::BM, m_end - m0);
-    const int rows_b = min(C::BN, p.n - n0);
+    const int rows_b = min(C::BN, nn - n0);
     // batch entry blockIdx.z: A and B start sa / sb bytes further (a K slice), C sc elements
-    ra = make_rsrc(p.a + blockIdx.z * p.sa + (int64_t)m0 * p.lda, (uint32_t)(rows_a * p.lda));
-    rb = make_rsrc(p.b + blockIdx.z * p.sb + (int64_t)n0 * p.ldb, (uint32_t)(rows_b * p.ldb));
-    cg = p.c + blockIdx.z * p.sc;
+    ra = make_rsrc(pa + blockIdx.z * sa + (int64_t)m0 * lda, (uint32_t)(rows_a * lda));
+    rb = make_rsrc(pb + blockIdx.z * sb + (int64_t)n0 * ldb, (uint32_t)(rows_b * ldb));
+    cg = pc + blockIdx.z * sc;
     // Direct load t of this wave covers operand rows 16 (wave * N + t) + lane / 4; lane
     // slot lane % 4 holds k-chunk slot ^ a_swz(row).  Rows past the operand's valid rows
     // are beyond the resource's size and read as zeros.
 #pragma unroll
     for (int t = 0; t < C::NA; ++t) {
       const int row = C::ROWS_PER_LOAD * (wave * C::NA + t) + lane / C::CPR;
-      a_off[t] = (uint32_t)(row * p.lda + ((lane % C::CPR) ^ a_swz<C::CPR>(row)) * 16);
+      a_off[t] = (uint32_t)(row * lda + ((lane % C::CPR) ^ a_swz<C::CPR>(row)) * 16);
     }
 #pragma unroll
     for (int t = 0; t < C::NB; ++t) {
       const int row = C::ROWS_PER_LOAD * (wave * C::NB + t) + lane / C::CPR;
-      b_off[t] = (uint32_t)(row * p.ldb + ((lane % C::CPR) ^ a_swz<C::CPR>(row)) * 16);
+      b_off[t] = (uint32_t)(row * ldb + ((lane % C::CPR) ^ a_swz<C::CPR>(row)) * 16);
     }
     // Fragments: A row wm*WM + i*32 + (lane&31), B row wn*WN + j*32 + (lane&31); the
     // swizzle of a row depends only on its low bits, i.e. on lane & 31.
@@ -127,8 +138,6 @@ struct F8Tile {
     const int x = a_swz<C::CPR>(lane & 31);
     rd_c0 = ((2 * (lane >> 5)) ^ x) * 16;
     rd_c1 = ((2 * (lane >> 5) + 1) ^ x) * 16;
-
-    return true;
   }
 
   // Steps past the end are issued with out-of-range offsets (zeros, no memory touched) so
@@ -201,7 +210,7 @@ void gemm_fp8_pingpong(F8Params p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x;
   F8Tile<C> t;
-  if (!t.init(p, tid)) return;
+  t.init(p, tid);
   const int group = t.group;
 
   f32x16 acc[C::FM][C::FN];
@@ -282,6 +291,7 @@ hipError_t launch(const GemmF8Args& g, const GemmUnits& units, hipStream_t strea
     tiles += (int64_t)((u.rows[i] + C::BM - 1) / C::BM) * p.tiles_n;
   }
   p.unit_tile0[u.n] = (int32_t)tiles;
+  p.tiles_total = (int32_t)tiles;
   if (tiles == 0) return hipSuccess;
   p.group = tile_group(tiles, p.tiles_n, 1, g.dbg ? g.dbg->tile_group : 0);
   const int64_t grid = tiles;
