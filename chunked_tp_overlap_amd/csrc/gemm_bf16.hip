@@ -116,7 +116,22 @@ constexpr uint64_t kReadyTimeoutTicks = 50000000ull;  // 0.5 s of the 100 MHz s_
 // lines cached before they arrived.  The wait is bounded in time, so every wave ends.
 // Returns, to every wave of the workgroup alike, whether some wave ran past the bound; the
 // workgroup then counts one timeout and stores NaN instead of computing its tile.
-__device__ inline bool wait_ready(const Params& p, int r0, int r1, bool count = true) {
+// The workgroup's OR of v, through the first words of the kernel's LDS (called before any
+// load writes there; the kernels then need no LDS of their own, which leaves all 160 KiB to
+// the stages).
+__device__ inline int workgroup_or(unsigned char* smem, int v) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
+  const bool any = __ballot(v != 0) != 0;
+  if (lane == 0) *LDS_PTR(uint32_t, smem + 4 * wave) = any ? 1u : 0u;
+  __syncthreads();
+  uint32_t r = 0;
+  for (int i = 0; i < waves; ++i) r |= *LDS_PTR(const uint32_t, smem + 4 * i);
+  __syncthreads();  // every wave has read the words before LDS is reused
+  return (int)r;
+}
+
+__device__ inline bool wait_ready(const Params& p, unsigned char* smem, int r0, int r1,
+                                  bool count = true) {
   int c = 0;
   while (c + 1 < p.n_chunks && p.chunk_row0[c + 1] <= r0) ++c;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -130,7 +145,7 @@ __device__ inline bool wait_ready(const Params& p, int r0, int r1, bool count = 
       __builtin_amdgcn_s_sleep(8);
     }
   }
-  late = __syncthreads_or(late);
+  late = workgroup_or(smem, late);
   if (late && count && threadIdx.x == 0)
     __hip_atomic_fetch_add(p.timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
@@ -731,7 +746,7 @@ void gemm_bf16_pingpong(Params p) {
   t.init(p, tid, tile);
   bool late = false;
   if (t.ready) {
-    late = wait_ready(p, t.m0, min(t.m0 + C::BM, t.m_end), SPLIT != 1);
+    late = wait_ready(p, smem, t.m0, min(t.m0 + C::BM, t.m_end), SPLIT != 1);
     if (!SPLIT && late) {
       t.store_nan(p, tid);
       return;
@@ -812,7 +827,7 @@ void gemm_bf16_pipelined(Params p) {
   const int tid = threadIdx.x;
   Tile<C> t;
   t.init(p, tid);
-  if (t.ready && wait_ready(p, t.m0, min(t.m0 + C::BM, t.m_end))) {
+  if (t.ready && wait_ready(p, smem, t.m0, min(t.m0 + C::BM, t.m_end))) {
     t.store_nan(p, tid);
     return;
   }
@@ -875,7 +890,7 @@ void gemm_bf16_seg(Params p) {
   t.init(p, tid, tile);
   bool late = false;
   if (t.ready) {
-    late = wait_ready(p, t.m0, min(t.m0 + C::BM, t.m_end), SPLIT != 1);
+    late = wait_ready(p, smem, t.m0, min(t.m0 + C::BM, t.m_end), SPLIT != 1);
     if (!SPLIT && late) {
       t.store_nan(p, tid);
       return;
@@ -1017,6 +1032,8 @@ using PP256x192 = Cfg<256, 192, 32, 4, 4, 2, 256>;  // 8 waves of 64x96 (B rows 
 using PP256x160 = Cfg<256, 160, 32, 4, 4, 2, 256>;  // 8 waves of 64x80
 using PL128x128 = Cfg<128, 128, 32, 4, 2, 2>;   // 4 waves of 64x64, 2 workgroups per CU
 constexpr int PP_D = 3;
+// load distance of a ping-pong tile: one step less than its stages
+template <class C> constexpr int kDist = C::S - 1;
 // Tiles whose direct loads issue between the MFMAs (see the ping-pong kernel): the narrow
 // tiles and 128x256.  At load distance 3 they measured 2-11% faster than with the loads in
 // the memory cluster at distance 2 (the narrow tiles' best before) on the GQA, qkv and fc1
@@ -1192,15 +1209,15 @@ hipError_t launch_split_r(int kind, const GemmArgs& g, const GemmUnits& u, hipSt
   constexpr int mode = R == 1 ? 2 : 3;
   switch (kind) {
     case kTile320x256:
-      return launch<PP320x256>(&gemm_bf16_pingpong<PP320x256, PP_D, R, kLoadsInCompute<PP320x256>>, g, u, stream, mode, nseg);
+      return launch<PP320x256>(&gemm_bf16_pingpong<PP320x256, kDist<PP320x256>, R, kLoadsInCompute<PP320x256>>, g, u, stream, mode, nseg);
     case kTile256x256:
-      return launch<PP256x256>(&gemm_bf16_pingpong<PP256x256, PP_D, R, kLoadsInCompute<PP256x256>>, g, u, stream, mode, nseg);
+      return launch<PP256x256>(&gemm_bf16_pingpong<PP256x256, kDist<PP256x256>, R, kLoadsInCompute<PP256x256>>, g, u, stream, mode, nseg);
     case kTile128x256:
-      return launch<PP128x256>(&gemm_bf16_pingpong<PP128x256, PP_D, R, kLoadsInCompute<PP128x256>>, g, u, stream, mode, nseg);
+      return launch<PP128x256>(&gemm_bf16_pingpong<PP128x256, kDist<PP128x256>, R, kLoadsInCompute<PP128x256>>, g, u, stream, mode, nseg);
     case kTile256x192:
-      return launch<PP256x192>(&gemm_bf16_pingpong<PP256x192, PP_D, R, kLoadsInCompute<PP256x192>>, g, u, stream, mode, nseg);
+      return launch<PP256x192>(&gemm_bf16_pingpong<PP256x192, kDist<PP256x192>, R, kLoadsInCompute<PP256x192>>, g, u, stream, mode, nseg);
     case kTile256x160:
-      return launch<PP256x160>(&gemm_bf16_pingpong<PP256x160, PP_D, R, kLoadsInCompute<PP256x160>>, g, u, stream, mode, nseg);
+      return launch<PP256x160>(&gemm_bf16_pingpong<PP256x160, kDist<PP256x160>, R, kLoadsInCompute<PP256x160>>, g, u, stream, mode, nseg);
     default:
       return launch<PL128x128>(&gemm_bf16_seg<PL128x128, R>, g, u, stream, mode, nseg);
   }
@@ -1216,15 +1233,15 @@ hipError_t launch_kind(int kind, const GemmArgs& g, const GemmUnits& u, hipStrea
   if (u.n <= 0) return hipSuccess;
   switch (kind) {
     case kTile320x256:
-      return launch<PP320x256>(&gemm_bf16_pingpong<PP320x256, PP_D, 0, kLoadsInCompute<PP320x256>>, g, u, stream);
+      return launch<PP320x256>(&gemm_bf16_pingpong<PP320x256, kDist<PP320x256>, 0, kLoadsInCompute<PP320x256>>, g, u, stream);
     case kTile256x256:
-      return launch<PP256x256>(&gemm_bf16_pingpong<PP256x256, PP_D, 0, kLoadsInCompute<PP256x256>>, g, u, stream);
+      return launch<PP256x256>(&gemm_bf16_pingpong<PP256x256, kDist<PP256x256>, 0, kLoadsInCompute<PP256x256>>, g, u, stream);
     case kTile128x256:
-      return launch<PP128x256>(&gemm_bf16_pingpong<PP128x256, PP_D, 0, kLoadsInCompute<PP128x256>>, g, u, stream);
+      return launch<PP128x256>(&gemm_bf16_pingpong<PP128x256, kDist<PP128x256>, 0, kLoadsInCompute<PP128x256>>, g, u, stream);
     case kTile256x192:
-      return launch<PP256x192>(&gemm_bf16_pingpong<PP256x192, PP_D, 0, kLoadsInCompute<PP256x192>>, g, u, stream);
+      return launch<PP256x192>(&gemm_bf16_pingpong<PP256x192, kDist<PP256x192>, 0, kLoadsInCompute<PP256x192>>, g, u, stream);
     case kTile256x160:
-      return launch<PP256x160>(&gemm_bf16_pingpong<PP256x160, PP_D, 0, kLoadsInCompute<PP256x160>>, g, u, stream);
+      return launch<PP256x160>(&gemm_bf16_pingpong<PP256x160, kDist<PP256x160>, 0, kLoadsInCompute<PP256x160>>, g, u, stream);
     default:
       return launch<PL128x128>(&gemm_bf16_pipelined<PL128x128>, g, u, stream);
   }
