@@ -1015,14 +1015,11 @@ hipError_t launch(K kernel, const GemmArgs& g, const GemmUnits& units, hipStream
   if (grid > 0x7FFFFFFF || g.batch > 65535) return hipErrorInvalidValue;
   hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kernel), C::LDS_BYTES);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid, 1, g.batch), dim3(C::THREADS), C::LDS_BYTES,
-                     stream, p);
-  e = hipGetLastError();
+  e = launch_k(kernel, dim3((unsigned)grid, 1, g.batch), dim3(C::THREADS), C::LDS_BYTES, stream, p);
   if (e != hipSuccess || seg_mode != 3) return e;
   constexpr int GROUPS = C::BM * C::BN / 4 / 256;
   if (tiles * GROUPS > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemm_bf16_split_reduce<C>, dim3((unsigned)(tiles * GROUPS)), dim3(256), 0, stream, p);
-  return hipGetLastError();
+  return launch_k(&gemm_bf16_split_reduce<C>, dim3((unsigned)(tiles * GROUPS)), dim3(256), 0, stream, p);
 }
 
 using PP320x256 = Cfg<320, 256, 32, 4, 2, 4>;   // 8 waves of 160x64

@@ -299,9 +299,7 @@ hipError_t launch(const GemmF8Args& g, const GemmUnits& units, hipStream_t strea
   auto kernel = &gemm_fp8_pingpong<C, F8_D>;
   hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kernel), C::LDS_BYTES);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid, 1, g.batch), dim3(C::THREADS), C::LDS_BYTES,
-                     stream, p);
-  return hipGetLastError();
+  return launch_k(kernel, dim3((unsigned)grid, 1, g.batch), dim3(C::THREADS), C::LDS_BYTES, stream, p);
 }
 
 // Tile choice as for bf16 (rounds of a launch x tile area / efficiency); a handle's debug

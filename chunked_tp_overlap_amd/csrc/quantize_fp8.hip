@@ -92,9 +92,8 @@ hipError_t launch_quantize_e4m3(const uint16_t* src, int64_t lds, uint8_t* dst, 
   if (cols % 8 != 0 || lds % 8 != 0 || ldd % 8 != 0) return hipErrorInvalidValue;
   const int64_t blocks = (rows * (cols / 8) + V * THREADS - 1) / (V * THREADS);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(quantize_rows, dim3((unsigned)blocks), dim3(THREADS), 0, stream, src, lds,
-                     dst, ldd, rows, cols, scale);
-  return hipGetLastError();
+  return launch_k(&quantize_rows, dim3((unsigned)blocks), dim3(THREADS), 0, stream, src, lds, dst,
+                  ldd, rows, cols, scale);
 }
 
 }  // namespace ubx

@@ -165,18 +165,11 @@ hipError_t launch_nsv(const ReduceArgs& r, int64_t nvec, int64_t vpr, hipStream_
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const bool packed = r.ldp == r.cols && r.ldo == r.cols;
   const dim3 grid((unsigned)blocks), block(THREADS);
-  if (r.ring) {
-    if (packed)
-      hipLaunchKernelGGL((reduce_chunks<NS, true, true, V>), grid, block, 0, stream, r, nvec, vpr);
-    else
-      hipLaunchKernelGGL((reduce_chunks<NS, false, true, V>), grid, block, 0, stream, r, nvec, vpr);
-  } else {
-    if (packed)
-      hipLaunchKernelGGL((reduce_chunks<NS, true, false, V>), grid, block, 0, stream, r, nvec, vpr);
-    else
-      hipLaunchKernelGGL((reduce_chunks<NS, false, false, V>), grid, block, 0, stream, r, nvec, vpr);
-  }
-  return hipGetLastError();
+  if (r.ring)
+    return packed ? launch_k(&reduce_chunks<NS, true, true, V>, grid, block, 0, stream, r, nvec, vpr)
+                  : launch_k(&reduce_chunks<NS, false, true, V>, grid, block, 0, stream, r, nvec, vpr);
+  return packed ? launch_k(&reduce_chunks<NS, true, false, V>, grid, block, 0, stream, r, nvec, vpr)
+                : launch_k(&reduce_chunks<NS, false, false, V>, grid, block, 0, stream, r, nvec, vpr);
 }
 
 constexpr int64_t kSmallSumVectors = int64_t(1) << 21;

@@ -54,8 +54,7 @@ hipError_t launch_clear_words(uint32_t* p, int64_t n, hipStream_t stream) {
   constexpr int kThreads = 256;
   const int64_t blocks = (n + kThreads - 1) / kThreads;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(clear_words, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, n);
-  return hipGetLastError();
+  return launch_k(&clear_words, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, n);
 }
 
 }  // namespace ubx

@@ -345,8 +345,15 @@ ub_status_t timed_launch(ub_ctx* h, hipStream_t s, int kind, double flops, doubl
   hipEvent_t b = take_event(h);
   if (!a || !b) return fail(h, UB_ERR_HIP, "hipEventCreate failed for kernel timing");
   hipError_t e = own_a ? hipEventRecord(a, s) : hipSuccess;
-  if (e == hipSuccess) e = launch();
-  if (e == hipSuccess) e = hipEventRecord(b, s);
+  if (e == hipSuccess) {
+    // the call's kernels record b at their end (launch_k); a call that launched none
+    // records it here
+    ubx::g_launch_stop = b;
+    ubx::g_launch_stop_used = false;
+    e = launch();
+    ubx::g_launch_stop = nullptr;
+    if (e == hipSuccess && !ubx::g_launch_stop_used) e = hipEventRecord(b, s);
+  }
   if (e != hipSuccess) return hip_fail(h, e, what);
   h->pending.push_back({a, b, kind, flops, bytes});
   if (h->timing == 2) {

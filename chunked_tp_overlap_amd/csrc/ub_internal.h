@@ -1,6 +1,7 @@
 // Internal declarations shared by the library's translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -10,6 +11,30 @@
 #include "ub.h"
 
 namespace ubx {
+
+// Kernel timing hook.  While a timed call runs (timed_launch in ub_api.cpp) this is the
+// call's stop event, and every kernel the library launches in it records the event at its
+// own end: hipExtLaunchKernel's stop event uses the dispatch's completion timestamp, where a
+// separate hipEventRecord adds a marker packet of its own (~3 us of GPU time per record,
+// measured on a back-to-back sweep).  Launches in order on the call's stream, so the event
+// ends with the call's last kernel.  nullptr: no call is timed on this thread.
+inline thread_local hipEvent_t g_launch_stop = nullptr;
+inline thread_local bool g_launch_stop_used = false;
+
+template <class T>
+struct same_type { using type = T; };
+
+// Every kernel launch of the library.
+template <class... KA>
+hipError_t launch_k(void (*kernel)(KA...), dim3 grid, dim3 block, size_t shmem, hipStream_t s,
+                    typename same_type<KA>::type... args) {
+  void* argv[sizeof...(KA) > 0 ? sizeof...(KA) : 1] = {(void*)&args...};
+  const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block,
+                                          argv, shmem, s, nullptr, g_launch_stop, 0);
+  if (g_launch_stop && e == hipSuccess) g_launch_stop_used = true;
+  return e;
+}
+
 
 // ---- chunk plan (host only; ub_plan.cpp) ------------------------------------------------
 struct Plan {
