@@ -16,9 +16,9 @@ when the plan cuts a nearly empty last round, whose workgroups walk the 8 chunks
 order); the host loop of per-chunk launches on min(8, 3) streams is measured as a secondary
 row, as are the QKV, fc1 and fc2 workloads, the reduction, FP8 and the arrival stand-in.
 
-Per-call HIP events (the library's kernel timing, chained: one record on the launch stream
-after every call, each call timed from the previous call's end) are taken inside the
-headline's timed region itself, so the roofline's kernel time is part of the timed step.  Prints one JSON line.  --profile-pass runs only one workload's
+Per-call HIP events (the library's kernel timing, chained: each call's end event taken by
+its last kernel launch on the launch stream, each call timed from the previous call's end)
+are taken inside the headline's timed region itself, so the roofline's kernel time is part of the timed step.  Prints one JSON line.  --profile-pass runs only one workload's
 timed region (and a copy of known size that calibrates rocprofv3's byte counters).
 """
 
@@ -248,8 +248,8 @@ def main():
     g = gqa_sweep(ub, wl, torch, np, dev)
     primary = g.cfg(atomic=True)
     log(f"warmup {args.warmup}, timed {args.steps} steps of {len(g.Ts)} GQA points (atomic_gemm)")
-    # chained kernel timing: one event per call on the launch stream, each call's time runs
-    # from the previous call's end event (an event record costs a few us of GPU time)
+    # chained kernel timing: one event per call, taken by the call's last kernel launch on the
+    # launch stream; each call's time runs from the previous call's end event
     sec, stats = g.timed(primary, args.steps, args.warmup, events=2)
     tflops = g.flops / sec / 1e12
     log(f"primary: {sec * 1e3:.3f} ms/step, {tflops:.1f} TFLOP/s (chained per-call events on)")
@@ -285,10 +285,10 @@ def main():
         "avg_call_gflop": round(stats["flops"] / max(1, calls) / 1e9, 4),
         "algorithmic_bytes_per_call": round(stats["bytes"] / max(1, calls)),
         "kernel_ms_per_step": round(kernel_ms_per_step, 4),
-        "timing": "HIP events on the launch stream inside the timed region, chained: one "
-                  "record after every GEMM call, each call's time from the previous call's "
-                  "end event (the first from an event of its own); kernel_ms_per_step <= "
-                  "ms_per_step",
+        "timing": "HIP events on the launch stream inside the timed region, chained: each "
+                  "GEMM call's end event recorded by its last kernel launch, each call's "
+                  "time from the previous call's end event (the first from an event of its "
+                  "own); kernel_ms_per_step <= ms_per_step",
     }
 
     w = g.w

@@ -461,10 +461,13 @@ UB_API ub_status_t ub_reduce_partials(ub_handle_t h, void* out, int64_t ldo,
                                       int32_t reduce_order, ub_stream_t stream);
 
 /* Per-launch kernel timing.  enable 1: every GEMM and reduction launch is bracketed by HIP
- * events recorded on the stream it is launched on (two event records per launch).
+ * events on the stream it is launched on: a start event recorded before it, and an end
+ * event that the call's last kernel launch takes (hipExtLaunchKernel's stop event, the
+ * kernel's own completion time, no separate event record).
  * enable 2, chained: a launch's start is the end event of the previous launch timed on
- * the same stream since the last ub_get_kernel_timing or ub_set_kernel_timing, so one
- * record per launch (each record costs a few microseconds of GPU time); the caller
+ * the same stream since the last ub_get_kernel_timing or ub_set_kernel_timing, so no
+ * event record of its own after the first (a record costs a few microseconds of GPU
+ * time); the caller
  * promises that nothing else runs on that stream between the calls it measures, or that
  * work counts as the next launch's time (back-to-back calls on one stream; not the host
  * loop's worker streams, whose launches wait for the caller's).  enable 0 (the default):
