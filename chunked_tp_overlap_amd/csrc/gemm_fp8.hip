@@ -55,9 +55,12 @@ struct F8Params {
   int32_t unit_tile0[kMaxGemmUnits + 1];
 };
 
-template <int BM_, int BN_, int S_, int WGM_, int WGN_>
+// BNL: B rows in LDS.  A tile narrower than 256 columns keeps 256 B rows in its stage, so
+// that its direct loads still split evenly over the waves; the loads of rows past BN fall
+// outside B's resource (zeros in LDS, no memory access) and no fragment read uses them.
+template <int BM_, int BN_, int S_, int WGM_, int WGN_, int BNL_ = BN_>
 struct F8Cfg {
-  static constexpr int BM = BM_, BN = BN_, BK = 64, S = S_;
+  static constexpr int BM = BM_, BN = BN_, BK = 64, S = S_, BNL = BNL_;
   static constexpr int WGM = WGM_, WGN = WGN_;
   static constexpr int NW = WGM * WGN;
   static constexpr int THREADS = 64 * NW;
@@ -67,7 +70,7 @@ struct F8Cfg {
   static constexpr int CPR = 4;             // 16-byte chunks per row
   static constexpr int ROWS_PER_LOAD = 16;  // a 1 KiB direct load covers 16 rows
   static constexpr int A_BYTES = BM * ROW;
-  static constexpr int B_BYTES = BN * ROW;
+  static constexpr int B_BYTES = BNL * ROW;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int NA = A_BYTES / 1024 / NW;  // direct loads per wave per step
   static constexpr int NB = B_BYTES / 1024 / NW;
@@ -80,6 +83,7 @@ struct F8Cfg {
                 "direct loads do not split over the waves");
   static_assert(WM % 32 == 0 && WN % 32 == 0 && FM >= 1 && FN >= 1, "32x32 blocks");
   static_assert(S * L <= 63, "vmcnt is a 6-bit count");
+  static_assert(BN <= BNL, "the tile's B rows within the stage");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS is 160 KiB per CU");
 };
 
@@ -154,6 +158,18 @@ struct F8Tile {
       dma16(rb, lds_addr(st + C::A_BYTES + (wave * C::NB + t) * 1024), live ? b_off[t] + kk : OOB);
   }
 
+  // Load slot j alone (A's NA slots, then B's), the same load issue_loads makes for it.
+  __device__ inline void issue_load_slot(unsigned char* smem, int ks, int nk, int j) const {
+    unsigned char* st = smem + (ks % C::S) * C::STAGE;
+    const bool live = ks < nk;
+    const uint32_t kk = (uint32_t)ks * C::BK;
+    if (j < C::NA)
+      dma16(ra, lds_addr(st + (wave * C::NA + j) * 1024), live ? a_off[j] + kk : OOB);
+    else
+      dma16(rb, lds_addr(st + C::A_BYTES + (wave * C::NB + j - C::NA) * 1024),
+            live ? b_off[j - C::NA] + kk : OOB);
+  }
+
   __device__ inline i32x8 frag(const unsigned char* row) const {
     const u32x4 lo = *LDS_PTR(const u32x4, row + rd_c0);
     const u32x4 hi = *LDS_PTR(const u32x4, row + rd_c1);
@@ -203,7 +219,10 @@ struct F8Tile {
 
 // The ping-pong of gemm_bf16_pingpong (same barriers, same landing argument) with one
 // 64-deep MFMA step per stage.
-template <class C, int D>
+// LIC: the loads of step ks + D issue between the MFMAs of step ks instead of in the memory
+// cluster (as in the bf16 ping-pong: group 1's wait at the end of its memory cluster then
+// allows (D - 2) steps in flight).
+template <class C, int D, bool LIC = false>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_fp8_pingpong(F8Params p) {
   static_assert(D >= 2 && D <= C::S - 1, "load distance");
@@ -233,20 +252,36 @@ void gemm_fp8_pingpong(F8Params p) {
 
   for (int ks = 0; ks < nk; ++ks) {
     t.read_frags(smem, ks, af, bf);  // memory cluster
-    t.issue_loads(smem, ks + D, nk);
+    if constexpr (!LIC) t.issue_loads(smem, ks + D, nk);
     __builtin_amdgcn_sched_barrier(0);
     if (group == 1) {
-      __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((D - 1) * C::L) : "memory");
+      __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((LIC ? D - 2 : D - 1) * C::L) : "memory");
     } else {
       __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     __builtin_amdgcn_sched_barrier(0);
+    {
+      constexpr int NM = C::FM * C::FN;
+      int m = 0, jl = 0;
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)  // compute cluster
+      for (int i = 0; i < C::FM; ++i)  // compute cluster
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j],
-                                                                    0, 0, 0, 127, 0, 127);
+        for (int j = 0; j < C::FN; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j],
+                                                                      0, 0, 0, 127, 0, 127);
+          ++m;
+          if (LIC && jl < C::L && m == (jl + 1) * NM / (C::L + 1)) {
+            __builtin_amdgcn_sched_barrier(0);
+            t.issue_load_slot(smem, ks + D, nk, jl);
+            __builtin_amdgcn_sched_barrier(0);
+            ++jl;
+          }
+        }
+      if constexpr (LIC) {  // slots the MFMA count left over (NM <= L)
+#pragma unroll
+        for (; jl < C::L; ++jl) t.issue_load_slot(smem, ks + D, nk, jl);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
     // Both groups take the same wait and barrier here: group 1 has issued no loads since
     // its own wait at the end of its memory cluster, so the wait costs it nothing.  With
@@ -263,7 +298,12 @@ void gemm_fp8_pingpong(F8Params p) {
 
 using F8_256x256 = F8Cfg<256, 256, 4, 2, 4>;  // 8 waves of 128x64
 using F8_128x256 = F8Cfg<128, 256, 4, 2, 4>;  // 8 waves of 64x64
+using F8_256x192 = F8Cfg<256, 192, 4, 4, 2, 256>;  // 8 waves of 64x96 (B rows 256 deep in LDS)
 constexpr int F8_D = 3;
+// The narrow tile and 128x256 issue their loads between the MFMAs (their memory cluster is
+// the longer one): on the qkv shape, forced tiles, bit-identical, 256x192 ran 1.5-1.8 PFLOP/s
+// at T = 5536 ... 8192 with it and 1.46-1.86 without (256x256: 1.44-1.91), 128x256 +1-4%.
+template <class C> constexpr bool kF8LoadsInCompute = C::BN < 256 || C::BM < 256;
 
 template <class C>
 hipError_t launch(const GemmF8Args& g, const GemmUnits& units, hipStream_t stream) {
@@ -296,7 +336,7 @@ hipError_t launch(const GemmF8Args& g, const GemmUnits& units, hipStream_t strea
   p.group = tile_group(tiles, p.tiles_n, 1, g.dbg ? g.dbg->tile_group : 0);
   const int64_t grid = tiles;
   if (grid > 0x7FFFFFFF || g.batch < 1 || g.batch > 65535) return hipErrorInvalidValue;
-  auto kernel = &gemm_fp8_pingpong<C, F8_D>;
+  auto kernel = &gemm_fp8_pingpong<C, F8_D, kF8LoadsInCompute<C>>;
   hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kernel), C::LDS_BYTES);
   if (e != hipSuccess) return e;
   return launch_k(kernel, dim3((unsigned)grid, 1, g.batch), dim3(C::THREADS), C::LDS_BYTES, stream, p);
@@ -304,15 +344,20 @@ hipError_t launch(const GemmF8Args& g, const GemmUnits& units, hipStream_t strea
 
 // Tile choice as for bf16 (rounds of a launch x tile area / efficiency); a handle's debug
 // setting can force one of the two shapes.
-bool use_128(const GemmF8Args& g, const GemmUnits& u) {
-  if (g.dbg && g.dbg->tile_m > 0) return g.dbg->tile_m == 128;
+// 0: 256x256, 1: 128x256, 2: 256x192.  Efficiencies against 256x256: 128x256 0.62; 256x192
+// 0.82, the ratio of forced one-round launches on the qkv shape (0.77 at T = 8192 ... 0.86 at
+// 4096), which takes it at every qkv pack (5536 ... 8176 rows, 2-11% faster than 256x256
+// there) and leaves 128x256 at T = 4096, where it measured fastest.
+int f8_tile(const GemmF8Args& g, const GemmUnits& u) {
+  if (g.dbg && g.dbg->tile_m > 0) return g.dbg->tile_m == 128 ? 1 : g.dbg->tile_n == 192 ? 2 : 0;
   const int share = 256 / (g.concurrency > 1 ? g.concurrency : 1);
-  auto cost = [&](int bm, double eff) {
-    const int64_t tiles = row_tiles(u, bm) * ((g.n + 255) / 256) * g.batch;
+  auto cost = [&](int bm, int bn, double eff) {
+    const int64_t tiles = row_tiles(u, bm) * ((g.n + bn - 1) / bn) * g.batch;
     const int64_t slots = share > 0 ? share : 1;
-    return (double)((tiles + slots - 1) / slots) * bm * 256 / eff;
+    return (double)((tiles + slots - 1) / slots) * bm * bn / eff;
   };
-  return cost(128, 0.62) < cost(256, 1.0);
+  const double c0 = cost(256, 256, 1.0), c1 = cost(128, 256, 0.62), c2 = cost(256, 192, 0.82);
+  return c1 < c0 && c1 < c2 ? 1 : c2 < c0 ? 2 : 0;
 }
 
 }  // namespace
@@ -329,19 +374,20 @@ hipError_t launch_gemm_fp8_units(const GemmF8Args& g, const GemmUnits& u, hipStr
     return hipErrorInvalidValue;
   for (int i = 0; i < u.n; ++i)
     if (u.rows[i] < 0 || u.row0[i] < 0) return hipErrorInvalidValue;
-  const bool small = use_128(g, u);
+  const int kind = f8_tile(g, u);
   if (g.plan_out) {
     const int32_t d = g.plan_out->dispatches;
     *g.plan_out = TilePlanRecord{};
     g.plan_out->dispatches = d + 1;
-    g.plan_out->tile_m = small ? 128 : 256;
-    g.plan_out->tile_n = 256;
+    g.plan_out->tile_m = kind == 1 ? 128 : 256;
+    g.plan_out->tile_n = kind == 2 ? 192 : 256;
   }
-  return small ? launch<F8_128x256>(g, u, stream) : launch<F8_256x256>(g, u, stream);
+  return kind == 1 ? launch<F8_128x256>(g, u, stream)
+                   : kind == 2 ? launch<F8_256x192>(g, u, stream) : launch<F8_256x256>(g, u, stream);
 }
 
 bool gemm_fp8_tile_supported(int tile_m, int tile_n) {
-  return tile_n == 256 && (tile_m == 128 || tile_m == 256);
+  return (tile_n == 256 && (tile_m == 128 || tile_m == 256)) || (tile_m == 256 && tile_n == 192);
 }
 
 }  // namespace ubx

@@ -95,11 +95,11 @@ def _gemm(ub, reg, w_codes, n, sa, sw, cfg, ldc=None):
     return gu.host(c)
 
 
-@pytest.mark.parametrize("tile", ["256x256", "128x256"])
+@pytest.mark.parametrize("tile", ["256x256", "128x256", "256x192"])
 def test_gemm_integer_bit_exact_every_schedule(ub, tile):
     """Small-integer codes, power-of-two scales: every partial sum is exact in fp32, so
     GPU == oracle bit for bit, for every chunking, stream count, rank, aggregate setting,
-    the device-side loop, and both tile shapes."""
+    the device-side loop, and every tile shape."""
     rng = np.random.default_rng(72)
     cap, H, N, T, tp = 1024, 512, 264, 600, 8
     a = _int_codes(rng, (T, H))
@@ -268,11 +268,11 @@ def _as_bf16(codes, transpose=False):
     return ob.encode_rne(v.T.copy() if transpose else v)
 
 
-@pytest.mark.parametrize("tile", ["256x256", "128x256"])
+@pytest.mark.parametrize("tile", ["256x256", "128x256", "256x192"])
 def test_rs_fp8_integer_bit_exact_every_schedule(ub, tile):
     """Small-integer codes, power-of-two scales: partials and sums are exact in fp32, so
     partials, ascending and ring-order outputs equal the oracle bit for bit, for every
-    chunking, stream count, the device-side loop and both tile shapes; the workspace and
+    chunking, stream count, the device-side loop and every tile shape; the workspace and
     output tails stay untouched."""
     rng = np.random.default_rng(75)
     cap, H, T, tp = 1024, 512, 600, 8
