@@ -197,6 +197,29 @@ def test_bit_identical_across_schedules_capacity_and_offset(ub):
             ub.ub_destroy(h)
 
 
+def test_device_loop_unit_table_up_to_64_units(ub):
+    """The device-side loop's tile lookup (lane j of each wave reads unit j, a ballot finds a
+    tile's unit) over unit tables of 33, 63 and 64 units, on every tile shape: bit-identical
+    to one host-loop chunk."""
+    rng = np.random.default_rng(11)
+    H, N, T, tp = 256, 320, 3000, 8
+    a = wl.normal_bits(rng, (T, H))
+    wt = gu.dev(wl.normal_bits(rng, (H, N), 0.02))
+    reg = gu.Registration(ub, 4096, H, tp, workspace=False)
+    try:
+        reg.set_T(T)
+        reg.fill(a)
+        ref = _run(ub, reg, wt, N, ub.make_cfg("bulk", 1))[:T]
+        for tile in gu.BF16_TILES:
+            gu.force_tile(ub, reg.h, tile)
+            for method, ns in (("pipeline", 33), ("bulk", 63), ("pipeline", 64)):
+                got = _run(ub, reg, wt, N, ub.make_cfg(method, ns, 3, False, True))[:T]
+                assert np.array_equal(got, ref), (tile, method, ns)
+        gu.force_tile(ub, reg.h, None)
+    finally:
+        reg.close()
+
+
 def test_strided_weights_and_output(ub):
     """ldw > n_cols and ldc > n_cols: only the first n_cols columns are read / written."""
     rng = np.random.default_rng(12)
