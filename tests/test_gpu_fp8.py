@@ -98,8 +98,8 @@ def _gemm(ub, reg, w_codes, n, sa, sw, cfg, ldc=None):
 @pytest.mark.parametrize("tile", ["256x256", "128x256", "256x192"])
 def test_gemm_integer_bit_exact_every_schedule(ub, tile):
     """Small-integer codes, power-of-two scales: every partial sum is exact in fp32, so
-    GPU == oracle bit for bit, for every chunking, stream count, rank, aggregate setting,
-    the device-side loop, and every tile shape."""
+    GPU == oracle bit for bit, for every chunking (up to a 64-unit device-side loop), stream
+    count, rank, aggregate setting, and every tile shape."""
     rng = np.random.default_rng(72)
     cap, H, N, T, tp = 1024, 512, 264, 600, 8
     a = _int_codes(rng, (T, H))
@@ -116,7 +116,8 @@ def test_gemm_integer_bit_exact_every_schedule(ub, tile):
                                                   ("ring_exchange", 1, 3, False, 5, True),
                                                   ("ring_exchange", 1, 2, True, 3, True),
                                                   ("pipeline", 7, 3, False, 0, False),
-                                                  ("bulk", 3, 1, True, 0, True)]:
+                                                  ("bulk", 3, 1, True, 0, True),
+                                                  ("pipeline", 64, 3, False, 0, True)]:
             cfg = ub.make_cfg(method, ns, nms, agg, atomic, rank=rank)
             got = _gemm(ub, reg, w, N, sa, sw, cfg)
             assert np.array_equal(got[:T], want), (tile, method, ns, nms, agg, rank, atomic)
